@@ -1,0 +1,362 @@
+"""CPU oracle for query-aware sparse decode (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this module.  The HIP library never calls it, and it imports
+nothing from the HIP package: the two share only the seeded input generators
+in ``synthetic/``.
+
+Everything is plain numpy in float64 on values that are exactly the stored
+(bf16 or fp32) inputs, and each stored result is rounded once, to nearest
+even, into its storage type.  Sources, cited by page title and section:
+
+* "Meta-Llama-3.1-8B-Instruct-Butler" model card (TokenButler), section
+  *Method*: producer layers 0, G, 2G, ... read LN(H) and emit
+  Q_imp = f_theta(LN(H)) with G slots; K_imp = K . W_K for every layer;
+  a consumer at layer l uses slot (l - 1) mod G, scores every cached token,
+  keeps a top-x subset under a fixed budget and adds a sink prefix and a
+  recent window.  Section *Memory requirements*: default 50% per layer,
+  layer 0 dense, ``fixed_<N>pc`` retains (100 - N)%, knobs
+  ``min_sparse_index`` (sink) and ``sliding_window`` (window).
+* "TokenButler: Token Importance is Predictable" (arXiv abstract page):
+  selection is per token under a fixed budget, the full KV cache is kept.
+* TokenSelect README, first highlights: per-head Q.K criticality, per-head
+  softmax, summed over heads ("soft voting").
+
+Readings where the pages are silent (each listed in the design notes):
+GQA head h belongs to KV head h // R; the raw scorer of a GQA group is the
+group's summed Q_imp dotted with K_imp; LN is LayerNorm without affine,
+eps given, biased variance; f_theta is Linear -> ReLU -> Linear without
+biases, output laid out head-major, then slot, then d'; ties in the top-x go
+to the lower token index; -0 counts as +0 and NaN as -inf; the budget is
+x = floor(L_r * num / den) taken over all L_r tokens, then unioned with the
+sink [0, s) and the window [L_r - w, L_r); attention uses scale 1/sqrt(D).
+
+Parity pins for every function live in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# storage rounding
+# ---------------------------------------------------------------------------
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float64 values once, to nearest even, onto the bfloat16 grid.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range: the
+    spacing at a value whose leading bit is 2^(e-1) is 2^(e-8), floored at
+    the subnormal spacing 2^-133; a rounded magnitude of 2^128 or more
+    overflows to infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    fin = np.isfinite(x) & (x != 0.0)
+    xf = x[fin]
+    _, e = np.frexp(xf)                      # |xf| = m * 2^e, m in [0.5, 1)
+    ulp_exp = np.maximum(e - 8, -133)
+    scaled = np.ldexp(xf, -ulp_exp)          # exact: power-of-two scaling
+    r = np.ldexp(np.rint(scaled), ulp_exp)   # rint: round half to even
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, r), r)
+    out[fin] = r
+    return out
+
+
+def round_to_f32(x) -> np.ndarray:
+    """Round float64 values once, to nearest even, onto the float32 grid."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def round_storage(x, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f32":
+        return round_to_f32(x)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# producer and slot map (model card, Method)
+# ---------------------------------------------------------------------------
+
+def producer_of(layer: int, G: int) -> int:
+    """Producer layer whose Q_imp serves ``layer``: itself when layer % G == 0,
+    otherwise the nearest producer below (producers sit at 0, G, 2G, ...)."""
+    return G * (layer // G)
+
+
+def slot_of(layer: int, G: int) -> int:
+    """Slot of the producer's Q_imp that ``layer`` reads: (layer - 1) mod G."""
+    return (layer - 1) % G
+
+
+def layer_norm(h, eps: float) -> np.ndarray:
+    """LN over the last axis: (h - mean) / sqrt(biased var + eps), no affine."""
+    h = np.asarray(h, dtype=np.float64)
+    mu = h.mean(axis=-1, keepdims=True)
+    var = ((h - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (h - mu) / np.sqrt(var + eps)
+
+
+def produce_queries(h, w1, w2, Hq: int, G: int, dprime: int, eps: float = 1e-5,
+                    dtype: str = "bf16") -> np.ndarray:
+    """Q_imp = f_theta(LN(H)) as [B, Hq, G, Lq, d'].
+
+    h: [B, Lq, E]; w1: [E, F]; w2: [F, Hq*G*d'].  f_theta is
+    relu(x . W1) . W2; the normalised input, the hidden activation and the
+    output are each rounded to the storage type, as a bf16 pipeline stores
+    them.  Output column (head*G + slot)*d' + i is Q_imp[b, head, slot, t, i].
+    """
+    h = np.asarray(h, dtype=np.float64)
+    B, Lq, E = h.shape
+    x = round_storage(layer_norm(h, eps), dtype)
+    a = round_storage(np.maximum(x @ np.asarray(w1, np.float64), 0.0), dtype)
+    y = round_storage(a @ np.asarray(w2, np.float64), dtype)
+    assert y.shape[-1] == Hq * G * dprime
+    return y.reshape(B, Lq, Hq, G, dprime).transpose(0, 2, 3, 1, 4).copy()
+
+
+# ---------------------------------------------------------------------------
+# key projection (model card, Method: K_imp = K . W_K)
+# ---------------------------------------------------------------------------
+
+def project_keys(k, w_k, dtype: str) -> np.ndarray:
+    """K_imp = K . W_K for key rows k [..., D] and W_K [D, d'], rounded once."""
+    return round_storage(np.asarray(k, np.float64) @ np.asarray(w_k, np.float64), dtype)
+
+
+# ---------------------------------------------------------------------------
+# scoring
+# ---------------------------------------------------------------------------
+
+def _causal_lengths(Lq: int, L: int, q_pos0: int, causal: bool) -> np.ndarray:
+    if not causal:
+        return np.full(Lq, L, dtype=np.int64)
+    return np.minimum(q_pos0 + np.arange(Lq) + 1, L)
+
+
+def score_raw(q_imp_slot, kimp, Hkv: int, causal: bool = False, q_pos0: int = 0) -> np.ndarray:
+    """Raw importance scores [B, Hkv, Lq, L], float32 values in float64.
+
+    q_imp_slot: [B, Hq, Lq, d'] (the consumer's slot); kimp: [B, Hkv, L, d'].
+    Score of token t for KV head g is (sum of Q_imp over g's query heads)
+    . K_imp[t], summed in float64 and rounded once to float32.  For a causal
+    row i (absolute position q_pos0 + i) tokens after it score -inf.
+    """
+    q = np.asarray(q_imp_slot, np.float64)
+    k = np.asarray(kimp, np.float64)
+    B, Hq, Lq, dp = q.shape
+    R = Hq // Hkv
+    qbar = q.reshape(B, Hkv, R, Lq, dp).sum(axis=2)            # [B, Hkv, Lq, d']
+    s = round_to_f32(np.einsum("bgqi,bgti->bgqt", qbar, k))
+    lens = _causal_lengths(Lq, k.shape[2], q_pos0, causal)
+    t = np.arange(k.shape[2])
+    s[:, :, t[None, :] >= lens[:, None]] = -np.inf
+    return s
+
+
+def softmax_last(z) -> np.ndarray:
+    z = np.asarray(z, np.float64)
+    m = np.max(z, axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(z - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def score_softvote(q, k, Hkv: int, scale: float, causal: bool = False,
+                   q_pos0: int = 0) -> np.ndarray:
+    """Soft-voting scores [B, Hkv, Lq, L] (TokenSelect README, highlights).
+
+    q: [B, Hq, Lq, D]; k: [B, Hkv, L, D].  For each query head h the
+    criticality of token t is its logit q_h . k_t * scale; each head's
+    criticalities are normalised by a softmax over all cached tokens (the
+    causal prefix for a causal row); the score of t for KV head g is the sum
+    of those probabilities over g's query heads, rounded to float32.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    B, Hq, Lq, D = q.shape
+    R = Hq // Hkv
+    L = k.shape[2]
+    kk = np.repeat(k, R, axis=1)                                 # [B, Hq, L, D]
+    z = np.einsum("bhqd,bhtd->bhqt", q, kk) * scale
+    lens = _causal_lengths(Lq, L, q_pos0, causal)
+    t = np.arange(L)
+    z[:, :, t[None, :] >= lens[:, None]] = -np.inf
+    p = softmax_last(z)
+    s = round_to_f32(p.reshape(B, Hkv, R, Lq, L).sum(axis=2))
+    s[:, :, t[None, :] >= lens[:, None]] = -np.inf
+    return s
+
+
+# ---------------------------------------------------------------------------
+# selection (model card, Method and Memory requirements)
+# ---------------------------------------------------------------------------
+
+def budget(L_r: int, num: int, den: int) -> int:
+    """Fixed budget x = floor(L_r * num / den); fixed_<N>pc is num/den = (100-N)/100."""
+    return (L_r * num) // den
+
+
+def fixed_pc_fraction(policy: str):
+    """'fixed_70pc' -> (30, 100): the retained fraction as num/den."""
+    assert policy.startswith("fixed_") and policy.endswith("pc")
+    n = int(policy[len("fixed_"):-2])
+    return (100 - n, 100)
+
+
+def select(scores_row, x: int, n_sink: int, n_window: int) -> np.ndarray:
+    """Selected token set of one row, ascending int64.
+
+    Top-x tokens by (score descending, index ascending) over the row's L_r
+    tokens, unioned with the sink [0, n_sink) and the window
+    [L_r - n_window, L_r).  -0 is +0 and NaN is -inf for the ordering.
+    """
+    s = np.array(scores_row, dtype=np.float64)
+    s[np.isnan(s)] = -np.inf
+    s[s == 0.0] = 0.0
+    L_r = s.shape[0]
+    order = np.lexsort((np.arange(L_r), -s))       # last key is primary
+    top = order[:min(max(x, 0), L_r)]
+    sink = np.arange(min(n_sink, L_r))
+    window = np.arange(max(0, L_r - n_window), L_r)
+    return np.unique(np.concatenate([top, sink, window]).astype(np.int64))
+
+
+def select_rows(scores, num: int, den: int, n_sink: int, n_window: int,
+                causal: bool = False, q_pos0: int = 0):
+    """Apply ``select`` to every row of scores [B, Hkv, Lq, L]; returns a
+    nested list [B][Hkv][Lq] of index arrays."""
+    B, Hkv, Lq, L = scores.shape
+    lens = _causal_lengths(Lq, L, q_pos0, causal)
+    out = []
+    for b in range(B):
+        rows_b = []
+        for g in range(Hkv):
+            rows_g = []
+            for i in range(Lq):
+                L_r = int(lens[i])
+                rows_g.append(select(scores[b, g, i, :L_r], budget(L_r, num, den),
+                                     n_sink, n_window))
+            rows_b.append(rows_g)
+        out.append(rows_b)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# attention over the selected set (model card, intro and Method)
+# ---------------------------------------------------------------------------
+
+def attend(q_heads, k_rows, v_rows, scale: float) -> np.ndarray:
+    """Softmax attention of query heads [R, D] over the selected rows [n, D].
+
+    o_h = sum_t softmax_t(q_h . k_t * scale) v_t, all in float64.
+    """
+    q = np.asarray(q_heads, np.float64)
+    k = np.asarray(k_rows, np.float64)
+    v = np.asarray(v_rows, np.float64)
+    z = (q @ k.T) * scale                                        # [R, n]
+    p = softmax_last(z)
+    return p @ v
+
+
+def sparse_decode_attn(q, k_cache, v_cache, sel, scale: float) -> np.ndarray:
+    """Decode attention [B, Hq, D] for one query token per head.
+
+    q: [B, Hq, D]; caches [B, Hkv, L_cap, D]; sel[b][g] is the ascending
+    selected index array of KV head g.  Query head h reads KV head h // R.
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    R = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        for g in range(Hkv):
+            idx = np.asarray(sel[b][g], np.int64)
+            out[b, g * R:(g + 1) * R] = attend(q[b, g * R:(g + 1) * R],
+                                               np.asarray(k_cache[b, g])[idx],
+                                               np.asarray(v_cache[b, g])[idx], scale)
+    return out
+
+
+def masked_attention_rows(q, k_cache, v_cache, sel_rows, scale: float,
+                          rows: Optional[list] = None) -> dict:
+    """Prefill attention for selected query rows.
+
+    q: [B, Hq, Lq, D]; sel_rows[b][g][i] is row i's selected set.  Returns
+    {(b, h, i): o[D]} for every (b, h, i) in ``rows`` (all rows if None).
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, Lq, D = q.shape
+    Hkv = k_cache.shape[1]
+    R = Hq // Hkv
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(Lq)]
+    out = {}
+    for (b, h, i) in rows:
+        g = h // R
+        idx = np.asarray(sel_rows[b][g][i], np.int64)
+        out[(b, h, i)] = attend(q[b, h, i][None, :], np.asarray(k_cache[b, g])[idx],
+                                np.asarray(v_cache[b, g])[idx], scale)[0]
+    return out
+
+
+def dense_decode_attn(q, k_cache, v_cache, L: int, scale: float) -> np.ndarray:
+    """Dense decode attention over tokens [0, L) (layer 0 of the model card)."""
+    B, Hkv = k_cache.shape[:2]
+    sel = [[np.arange(L) for _ in range(Hkv)] for _ in range(B)]
+    return sparse_decode_attn(q, k_cache, v_cache, sel, scale)
+
+
+# ---------------------------------------------------------------------------
+# one decode step of one layer, chained
+# ---------------------------------------------------------------------------
+
+def decode_layer_step(*, q, k_cache, v_cache, L: int, num: int, den: int,
+                      n_sink: int, n_window: int, scale: float, Hkv: int,
+                      mode: str = "raw", q_imp_slot=None, kimp=None,
+                      dense: bool = False) -> dict:
+    """Score -> select -> attend for one decode layer at context L.
+
+    q: [B, Hq, D]; raw mode needs q_imp_slot [B, Hq, d'] and kimp
+    [B, Hkv, >=L, d']; softvote mode scores with q against the keys.
+    Returns scores [B, Hkv, L], the selected sets and the output [B, Hq, D].
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, D = q.shape
+    kc = np.asarray(k_cache, np.float64)[:, :, :L]
+    vc = np.asarray(v_cache, np.float64)[:, :, :L]
+    if dense:
+        sel = [[np.arange(L) for _ in range(Hkv)] for _ in range(B)]
+        return {"scores": None, "sel": sel,
+                "out": sparse_decode_attn(q, kc, vc, sel, scale)}
+    if mode == "raw":
+        s = score_raw(np.asarray(q_imp_slot, np.float64)[:, :, None, :],
+                      np.asarray(kimp, np.float64)[:, :, :L], Hkv)[:, :, 0]
+    else:
+        s = score_softvote(q[:, :, None, :], kc, Hkv, scale)[:, :, 0]
+    x = budget(L, num, den)
+    sel = [[select(s[b, g], x, n_sink, n_window) for g in range(Hkv)] for b in range(B)]
+    return {"scores": s, "sel": sel, "out": sparse_decode_attn(q, kc, vc, sel, scale)}
+
+
+def ulps_bf16(a, b) -> np.ndarray:
+    """Distance in bf16 units in the last place between two bf16-valued arrays."""
+    def ordered(x):
+        x = np.asarray(x, np.float64).astype(np.float32)
+        u = x.view(np.uint32).astype(np.int64) >> 16
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def mean_abs(x) -> float:
+    return float(np.mean(np.abs(np.asarray(x, np.float64))))
+
+
+__all__ = [n for n in dir() if not n.startswith("_") and n not in ("math", "np", "Optional",
+                                                                   "annotations")]

@@ -1,0 +1,479 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks one oracle function against an independent fact: exact
+rational arithmetic (``fractions.Fraction``) with its own round-to-nearest-
+even, brute-force enumeration of subsets, a library routine that the oracle
+does not call (torch's layer_norm / softmax / scaled_dot_product_attention,
+torch's float32 -> bfloat16 conversion), a golden table derived from the
+pages, or an invariant of the definition.  The mutation tests at the end
+plant plausible mistakes in the oracle and check that these pins catch them.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import reference as ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# independent exact rounding (Fraction based)
+# ---------------------------------------------------------------------------
+
+def frac_rne(fr: Fraction, p: int, emin: int = -126) -> float:
+    """Round an exact rational to the binary format with p significant bits
+    and minimum normal exponent emin, ties to even (no overflow handling)."""
+    if fr == 0:
+        return 0.0
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, emin) - (p - 1))
+    q = a / ulp
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(n * ulp)
+
+
+def bf16_grid(rng, shape, scale=1.0):
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+
+
+# ---------------------------------------------------------------------------
+# storage rounding
+# ---------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch_on_structured_float32_patterns():
+    """All 2^16 upper halves x the lower halves that decide the rounding."""
+    hi = np.arange(1 << 16, dtype=np.uint64) << np.uint64(16)
+    lows = np.array([0x0000, 0x0001, 0x3FFF, 0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xFFFF,
+                     0x1234, 0x9ABC], dtype=np.uint64)
+    bits = (hi[:, None] | lows[None, :]).ravel().astype(np.uint32)
+    f = bits.view(np.float32)
+    ours = ref.round_to_bf16(f.astype(np.float64))
+    theirs = torch.from_numpy(f.copy()).to(torch.bfloat16).double().numpy()
+    both_nan = np.isnan(ours) & np.isnan(theirs)
+    assert np.all((ours == theirs) | both_nan)
+    # sign of zero is kept
+    z = np.signbit(ours[(ours == 0)]) == np.signbit(theirs[(theirs == 0)])
+    assert z.all()
+
+
+def test_bf16_rounding_random_float32_sample():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 1 << 32, size=1 << 21, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    ours = ref.round_to_bf16(f.astype(np.float64))
+    theirs = torch.from_numpy(f.copy()).to(torch.bfloat16).double().numpy()
+    assert np.all((ours == theirs) | (np.isnan(ours) & np.isnan(theirs)))
+
+
+def test_bf16_single_rounding_golden():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "bf16_single_rounding.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    assert len(rows) >= 10
+    for src, want, note in rows:
+        got = ref.round_to_bf16(np.array([float.fromhex(src)]))[0]
+        assert got == float.fromhex(want), (src, want, note, got.hex())
+
+
+def test_bf16_rounding_of_float64_matches_exact_rationals():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(3000) * np.exp2(rng.integers(-20, 20, 3000))
+    # plant exact ties and near-ties in float64 (below float32 resolution)
+    base = ref.round_to_bf16(x[:1000])
+    ulp = np.exp2(np.frexp(base)[1] - 8)
+    x[:1000] = base + ulp / 2 * np.sign(base) + rng.choice([-1, 0, 1], 1000) * np.abs(base) * 2.0 ** -45
+    got = ref.round_to_bf16(x)
+    for xi, gi in zip(x, got):
+        assert gi == frac_rne(Fraction(float(xi)), 8), (xi.hex(), gi)
+
+
+def test_f32_rounding_matches_exact_rationals():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(2000) * np.exp2(rng.integers(-30, 30, 2000))
+    got = ref.round_to_f32(x)
+    for xi, gi in zip(x, got):
+        assert gi == frac_rne(Fraction(float(xi)), 24), xi.hex()
+
+
+# ---------------------------------------------------------------------------
+# layer norm and producer
+# ---------------------------------------------------------------------------
+
+def test_layer_norm_matches_torch():
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal((3, 7, 64)) * 3 + 1.5
+    ours = ref.layer_norm(h, 1e-5)
+    theirs = torch.nn.functional.layer_norm(torch.from_numpy(h), (64,), eps=1e-5).numpy()
+    np.testing.assert_allclose(ours, theirs, rtol=0, atol=1e-12)
+
+
+def test_produce_queries_matches_exact_mlp_and_layout():
+    """f_theta = relu(x W1) W2 with bf16 storage of x, a and y, checked with
+    exact rationals; the output layout is checked element by element."""
+    rng = np.random.default_rng(6)
+    B, Lq, E, F, Hq, G, dp = 2, 3, 8, 5, 3, 2, 2
+    h = bf16_grid(rng, (B, Lq, E), 2.0)
+    w1 = bf16_grid(rng, (E, F), 0.3)
+    w2 = bf16_grid(rng, (F, Hq * G * dp), 0.3)
+    got = ref.produce_queries(h, w1, w2, Hq, G, dp, eps=1e-5)
+    assert got.shape == (B, Hq, G, Lq, dp)
+    xhat = torch.nn.functional.layer_norm(torch.from_numpy(h), (E,), eps=1e-5).numpy()
+    for b in range(B):
+        for t in range(Lq):
+            x = [frac_rne(Fraction(float(v)), 8) for v in xhat[b, t]]
+            a = []
+            for f in range(F):
+                acc = sum(Fraction(x[e]) * Fraction(float(w1[e, f])) for e in range(E))
+                a.append(frac_rne(max(acc, Fraction(0)), 8))
+            for col in range(Hq * G * dp):
+                y = frac_rne(sum(Fraction(a[f]) * Fraction(float(w2[f, col])) for f in range(F)), 8)
+                head, rem = divmod(col, G * dp)
+                slot, i = divmod(rem, dp)
+                assert got[b, head, slot, t, i] == y, (b, t, col)
+
+
+def test_slot_map_golden():
+    rows = [list(map(int, ln.split())) for ln in open(os.path.join(GOLDEN, "slot_map_g4.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 32
+    for layer, producer, slot, dense in rows:
+        assert ref.producer_of(layer, 4) == producer
+        assert ref.slot_of(layer, 4) == slot
+        assert (layer == 0) == bool(dense)
+
+
+def test_fixed_pc_policy_golden():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "fixed_pc_policy.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    for policy, num, den, L, x in rows:
+        assert ref.fixed_pc_fraction(policy) == (int(num), int(den))
+        assert ref.budget(int(L), int(num), int(den)) == int(x)
+
+
+# ---------------------------------------------------------------------------
+# projection and scores
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,p", [("bf16", 8), ("f32", 24)])
+def test_project_keys_matches_exact_rationals(dtype, p):
+    rng = np.random.default_rng(8)
+    D, dp, n = 16, 5, 7                      # non-square: a transposed W_K fails
+    if dtype == "bf16":
+        k = bf16_grid(rng, (n, D)); w = bf16_grid(rng, (D, dp), 0.25)
+    else:
+        k = rng.standard_normal((n, D)).astype(np.float32).astype(np.float64)
+        w = (rng.standard_normal((D, dp)) * 0.25).astype(np.float32).astype(np.float64)
+    got = ref.project_keys(k, w, dtype)
+    for t in range(n):
+        for j in range(dp):
+            exact = sum(Fraction(float(k[t, d])) * Fraction(float(w[d, j])) for d in range(D))
+            assert got[t, j] == frac_rne(exact, p), (t, j)
+
+
+def test_score_raw_matches_exact_group_sums_and_causal_mask():
+    rng = np.random.default_rng(9)
+    B, Hkv, R, Lq, L, dp = 2, 3, 2, 3, 9, 4
+    Hq = Hkv * R
+    q = bf16_grid(rng, (B, Hq, Lq, dp))
+    k = bf16_grid(rng, (B, Hkv, L, dp))
+    got = ref.score_raw(q, k, Hkv, causal=True, q_pos0=4)
+    for b in range(B):
+        for g in range(Hkv):
+            for i in range(Lq):
+                for t in range(L):
+                    if t > 4 + i:
+                        assert got[b, g, i, t] == -np.inf
+                        continue
+                    exact = sum(Fraction(float(q[b, h, i, j])) * Fraction(float(k[b, g, t, j]))
+                                for h in range(g * R, (g + 1) * R) for j in range(dp))
+                    assert got[b, g, i, t] == frac_rne(exact, 24), (b, g, i, t)
+    nc = ref.score_raw(q, k, Hkv)
+    assert np.isfinite(nc).all()
+
+
+def test_score_raw_bf16_sum_is_order_independent():
+    """For bf16 inputs every partial sum is exact in float64, so any order of
+    summation gives the same float64 value (the score is exactly rounded)."""
+    rng = np.random.default_rng(10)
+    q = bf16_grid(rng, (4, 32))
+    k = bf16_grid(rng, (20000, 32))
+    qbar = q.sum(axis=0)
+    a = k @ qbar
+    b = np.zeros(20000)
+    for j in reversed(range(32)):
+        b += k[:, j] * qbar[j]
+    assert np.array_equal(a, b)
+
+
+def test_softvote_reduces_to_softmax_and_sums_to_group_size():
+    rng = np.random.default_rng(11)
+    B, Hkv, R, Lq, L, D = 1, 2, 2, 2, 50, 16
+    q = bf16_grid(rng, (B, Hkv * R, Lq, D))
+    q[:, 0:R] = 0.0                            # group 0: all-zero queries -> uniform
+    k = bf16_grid(rng, (B, Hkv, L, D))
+    s = ref.score_softvote(q, k, Hkv, 0.25)
+    np.testing.assert_allclose(s.sum(axis=-1), R, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(s[0, 0], R / L, rtol=1e-7)
+    # R = 1 is a plain softmax of the scaled logits (torch)
+    s1 = ref.score_softvote(q[:, 2:3], k[:, 1:2], 1, 0.25)
+    z = torch.from_numpy(q[0, 2] @ k[0, 1].T * 0.25)
+    want = torch.softmax(z, dim=-1).float().double().numpy()
+    np.testing.assert_array_equal(s1[0, 0], want)
+    # group 1 = sum of its two heads' softmaxes
+    z2 = torch.from_numpy(q[0, 3] @ k[0, 1].T * 0.25)
+    want2 = (torch.softmax(z, -1) + torch.softmax(z2, -1)).float().double().numpy()
+    np.testing.assert_array_equal(s[0, 1], want2)
+
+
+def test_softvote_causal_rows_normalise_over_prefix():
+    rng = np.random.default_rng(12)
+    q = bf16_grid(rng, (1, 2, 4, 8))
+    k = bf16_grid(rng, (1, 1, 10, 8))
+    s = ref.score_softvote(q, k, 1, 0.3, causal=True, q_pos0=3)
+    for i in range(4):
+        n = 3 + i + 1
+        assert np.all(s[0, 0, i, n:] == -np.inf)
+        assert abs(s[0, 0, i, :n].sum() - 2.0) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def _dominates(s, t, u):
+    a, b = s[t], s[u]
+    a = -np.inf if np.isnan(a) else a
+    b = -np.inf if np.isnan(b) else b
+    return a > b or (a == b and t < u)
+
+
+def brute_select(s, x, n_sink, n_window):
+    L = len(s)
+    k = min(x, L)
+    winners = []
+    for T in itertools.combinations(range(L), k):
+        Ts = set(T)
+        if all(_dominates(s, t, u) for t in Ts for u in range(L) if u not in Ts):
+            winners.append(Ts)
+    assert len(winners) == 1
+    S = winners[0] | set(range(min(n_sink, L))) | set(range(max(0, L - n_window), L))
+    return sorted(S)
+
+
+def brute_max_sum(s, x):
+    """Top-x as the max-sum subset, lexicographically smallest on ties."""
+    best = None
+    for T in itertools.combinations(range(len(s)), x):
+        key = (-sum(s[t] for t in T), T)
+        if best is None or key < best:
+            best = key
+    return sorted(best[1])
+
+
+def test_select_matches_brute_force_enumeration():
+    rng = np.random.default_rng(13)
+    vals = np.array([-2.0, -1.0, -0.0, 0.0, 0.5, 1.0, 3.0, np.inf, -np.inf, np.nan])
+    for trial in range(250):
+        L = int(rng.integers(1, 12))
+        s = vals[rng.integers(0, len(vals), L)] if trial % 2 else rng.standard_normal(L)
+        x = int(rng.integers(0, L + 2))
+        ns, nw = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        got = ref.select(s, x, ns, nw).tolist()
+        assert got == brute_select(s, x, ns, nw), (s, x, ns, nw)
+        if trial % 2 == 0 and 0 < x <= L:
+            assert ref.select(s, x, 0, 0).tolist() == brute_max_sum(s, x)
+
+
+def test_select_invariants():
+    rng = np.random.default_rng(14)
+    L = 500
+    s = rng.standard_normal(L)
+    for x in (0, 1, 10, 250, 499):
+        S = set(ref.select(s, x, 4, 16).tolist())
+        assert set(range(4)) <= S and set(range(L - 16, L)) <= S
+        assert max(x, 20) <= len(S) <= min(L, x + 20)
+        assert set(ref.select(s, x, 4, 16)) <= set(ref.select(s, x + 1, 4, 16))
+    assert ref.select(s, L, 4, 16).tolist() == list(range(L))
+    assert ref.select(s, 10 * L, 0, 0).tolist() == list(range(L))
+    eq = np.full(L, 0.25)
+    assert ref.select(eq, 30, 4, 16).tolist() == sorted(set(range(30)) | set(range(L - 16, L)))
+    # positive scaling of the scores never changes the set
+    assert ref.select(s * 3.5, 123, 4, 16).tolist() == ref.select(s, 123, 4, 16).tolist()
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def test_attend_matches_sdpa_dense_and_masked():
+    rng = np.random.default_rng(15)
+    R, n, D = 4, 37, 32
+    q = rng.standard_normal((R, D)); k = rng.standard_normal((n, D)); v = rng.standard_normal((n, D))
+    scale = 1 / math.sqrt(D)
+    got = ref.attend(q, k, v, scale)
+    Q, K, V = (torch.from_numpy(a)[None, None] for a in (q, k, v))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        Q[0].unsqueeze(0), K.expand(1, 1, n, D), V.expand(1, 1, n, D), scale=scale)[0, 0].numpy()
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    mask = rng.random(n) < 0.4
+    mask[0] = True
+    idx = np.nonzero(mask)[0]
+    got_m = ref.attend(q, k[idx], v[idx], scale)
+    want_m = torch.nn.functional.scaled_dot_product_attention(
+        Q[0].unsqueeze(0), K, V, attn_mask=torch.from_numpy(mask)[None, None, None, :],
+        scale=scale)[0, 0].numpy()
+    np.testing.assert_allclose(got_m, want_m, rtol=0, atol=1e-12)
+
+
+def test_attend_special_cases():
+    rng = np.random.default_rng(16)
+    k = rng.standard_normal((9, 8)); v = rng.standard_normal((9, 8))
+    q = rng.standard_normal((2, 8))
+    assert np.array_equal(ref.attend(q, k[3:4], v[3:4], 0.5), np.repeat(v[3:4], 2, axis=0))
+    np.testing.assert_allclose(ref.attend(np.zeros((1, 8)), k, v, 0.5)[0], v.mean(axis=0),
+                               rtol=0, atol=1e-15)
+
+
+def test_gqa_head_to_kv_head_map():
+    """Query head h reads KV head h // R (consecutive groups)."""
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, L, D = 1, 4, 2, 6, 4
+    k = rng.standard_normal((B, Hkv, L, D)); v = rng.standard_normal((B, Hkv, L, D))
+    q = rng.standard_normal((B, Hq, D))
+    sel = [[np.array([2]), np.array([5])]]
+    out = ref.sparse_decode_attn(q, k, v, sel, 0.5)
+    for h in range(Hq):
+        g = h // 2
+        assert np.array_equal(out[0, h], v[0, g, sel[0][g][0]])
+
+
+# ---------------------------------------------------------------------------
+# whole decode step: invariants the method's definition fixes
+# ---------------------------------------------------------------------------
+
+def _tiny_layer(seed=18, L=40, Hq=4, Hkv=2, D=16, dp=8):
+    rng = np.random.default_rng(seed)
+    return dict(q=bf16_grid(rng, (1, Hq, D)), k=bf16_grid(rng, (1, Hkv, L, D)),
+                v=bf16_grid(rng, (1, Hkv, L, D)), qi=bf16_grid(rng, (1, Hq, dp)),
+                wk=bf16_grid(rng, (D, dp), 0.25), L=L, Hkv=Hkv, D=D)
+
+
+def _sdpa_dense(q, k, v, Hkv, scale):
+    R = q.shape[1] // Hkv
+    Q = torch.from_numpy(q)[:, :, None, :]
+    K = torch.from_numpy(np.repeat(k, R, axis=1)); V = torch.from_numpy(np.repeat(v, R, axis=1))
+    return torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)[:, :, 0].numpy()
+
+
+@pytest.mark.parametrize("mode", ["raw", "softvote"])
+def test_full_budget_equals_dense_attention(mode):
+    d = _tiny_layer()
+    kimp = ref.project_keys(d["k"], d["wk"], "bf16")
+    scale = 1 / math.sqrt(d["D"])
+    for num, den in ((1, 1), (3, 2)):
+        r = ref.decode_layer_step(q=d["q"], k_cache=d["k"], v_cache=d["v"], L=d["L"], num=num,
+                                  den=den, n_sink=2, n_window=3, scale=scale, Hkv=d["Hkv"],
+                                  mode=mode, q_imp_slot=d["qi"], kimp=kimp)
+        np.testing.assert_allclose(r["out"], _sdpa_dense(d["q"], d["k"], d["v"], d["Hkv"], scale),
+                                   rtol=0, atol=1e-12)
+
+
+def test_sink_and_window_always_selected():
+    d = _tiny_layer(L=64)
+    kimp = ref.project_keys(d["k"], d["wk"], "bf16")
+    r = ref.decode_layer_step(q=d["q"], k_cache=d["k"], v_cache=d["v"], L=64, num=1, den=8,
+                              n_sink=4, n_window=8, scale=0.25, Hkv=d["Hkv"], mode="raw",
+                              q_imp_slot=d["qi"], kimp=kimp)
+    for g in range(d["Hkv"]):
+        S = set(r["sel"][0][g].tolist())
+        assert set(range(4)) | set(range(56, 64)) <= S
+        assert 8 <= len(S) <= 20
+
+
+# ---------------------------------------------------------------------------
+# mutation checks: plausible mistakes in the oracle must fail a pin
+# ---------------------------------------------------------------------------
+
+def _pins_fail(monkeypatch, name, bad, test):
+    monkeypatch.setattr(ref, name, bad)
+    with pytest.raises(AssertionError):
+        test()
+
+
+def test_mutations_are_caught(monkeypatch):
+    good_select = ref.select
+
+    def select_ties_high(s, x, ns, nw):      # ties to the higher index
+        s = np.asarray(s, np.float64)
+        L = len(s)
+        order = np.lexsort((-np.arange(L), -np.nan_to_num(s, nan=-np.inf)))[:min(x, L)]
+        return np.unique(np.concatenate([order, np.arange(min(ns, L)),
+                                         np.arange(max(0, L - nw), L)]))
+    _pins_fail(monkeypatch, "select", select_ties_high, test_select_matches_brute_force_enumeration)
+    monkeypatch.setattr(ref, "select", good_select)
+
+    def select_no_window(s, x, ns, nw):
+        return good_select(s, x, ns, 0)
+    _pins_fail(monkeypatch, "select", select_no_window, test_select_invariants)
+    monkeypatch.setattr(ref, "select", good_select)
+
+    good_rb = ref.round_to_bf16
+    _pins_fail(monkeypatch, "round_to_bf16",
+               lambda x: np.asarray(x, np.float64).astype(np.float32).view(np.uint32)
+               .__and__(np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64),
+               test_bf16_rounding_random_float32_sample)          # truncation
+    monkeypatch.setattr(ref, "round_to_bf16", good_rb)
+
+    good_proj = ref.project_keys
+    _pins_fail(monkeypatch, "project_keys",
+               lambda k, w, dt: ref.round_storage(np.asarray(k) @ np.asarray(w)[::-1], dt),
+               lambda: test_project_keys_matches_exact_rationals("bf16", 8))
+    monkeypatch.setattr(ref, "project_keys", good_proj)
+
+    good_ln = ref.layer_norm
+    _pins_fail(monkeypatch, "layer_norm",
+               lambda h, eps: (np.asarray(h) - np.mean(h, -1, keepdims=True))
+               / np.sqrt(np.var(h, -1, ddof=1, keepdims=True) + eps),          # unbiased var
+               test_layer_norm_matches_torch)
+    monkeypatch.setattr(ref, "layer_norm", good_ln)
+
+    good_sr = ref.score_raw
+
+    def score_first_head_only(q, k, Hkv, causal=False, q_pos0=0):
+        q = np.asarray(q, np.float64)
+        R = q.shape[1] // Hkv
+        return good_sr(q[:, ::R].repeat(R, axis=1) / R, k, Hkv, causal, q_pos0)
+    _pins_fail(monkeypatch, "score_raw", score_first_head_only,
+               test_score_raw_matches_exact_group_sums_and_causal_mask)
+    monkeypatch.setattr(ref, "score_raw", good_sr)
+
+    good_att = ref.attend
+    _pins_fail(monkeypatch, "attend",
+               lambda q, k, v, scale: good_att(q, k, v, 1.0),              # scale dropped
+               test_attend_matches_sdpa_dense_and_masked)
+    monkeypatch.setattr(ref, "attend", good_att)
+
+    good_slot = ref.slot_of
+    _pins_fail(monkeypatch, "slot_of", lambda layer, G: layer % G, test_slot_map_golden)
+    monkeypatch.setattr(ref, "slot_of", good_slot)
+
+    good_prod = ref.producer_of
+    _pins_fail(monkeypatch, "producer_of", lambda layer, G: G * ((layer - 1) // G) if layer else 0,
+               test_slot_map_golden)
+    monkeypatch.setattr(ref, "producer_of", good_prod)
