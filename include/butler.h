@@ -1,0 +1,187 @@
+/*
+ * butler.h -- C ABI of libbutler, query-aware sparse decode for AMD MI355X (gfx950).
+ *
+ * The method (TokenButler, "Meta-Llama-3.1-8B-Instruct-Butler" model card, section
+ * Method; TokenSelect README, highlights):
+ *   producer layers 0, G, 2G, ... turn LN(H) into low-dimensional importance queries
+ *   Q_imp = f_theta(LN(H)); every layer projects its cached post-RoPE keys to
+ *   K_imp = K . W_K; a consumer layer scores every cached token with its slot of Q_imp
+ *   against K_imp (or, TokenSelect style, with per-head softmax-normalised Q.K summed
+ *   over the heads of a GQA group), keeps a fixed budget of top-x tokens plus a sink
+ *   prefix and a recent window, and attends over that set only.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library never
+ *     allocates or frees device memory, keeps no pointer after returning and never
+ *     synchronises: all work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream).  Buffers must stay alive until the stream has passed the enqueued work.
+ *   - Tensors are dense, row-major, innermost dimension contiguous, with the shapes
+ *     given below.  Cache tensors are allocated with a token capacity L_cap >= L.
+ *     Every tensor pointer must be 16-byte aligned.
+ *   - dtype is BUTLER_BF16 or BUTLER_F32 for the key, query and value tensors; scores
+ *     and attention outputs are always float32; indices, counts are int32.
+ *   - Arguments are validated on the host before anything is enqueued.  On an error
+ *     return nothing has been enqueued and no output has been touched.
+ *   - Workspace (where an entry point has one) follows a two-phase query: call with
+ *     workspace == NULL and ws_bytes != NULL, the required size is written to *ws_bytes
+ *     and BUTLER_OK is returned without enqueueing anything.  Then call with a buffer of
+ *     at least that size and *ws_bytes set to its size.  A workspace buffer must be
+ *     zero-filled before its first use; every call leaves the counters in it zero again,
+ *     so the same buffer can be reused call after call on one stream.  Two calls that
+ *     share one workspace must not run concurrently.
+ *   - Results are deterministic: the same inputs give bitwise identical outputs.
+ */
+#ifndef BUTLER_H
+#define BUTLER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum butler_status {
+  BUTLER_OK = 0,
+  BUTLER_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned pointer, ...   */
+  BUTLER_ERR_UNSUPPORTED = -2,  /* dtype / head dim / d' / group size not built      */
+  BUTLER_ERR_WORKSPACE = -3,    /* workspace smaller than the queried size           */
+  BUTLER_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError)          */
+};
+
+enum butler_dtype { BUTLER_F32 = 0, BUTLER_BF16 = 1 };
+
+enum butler_score_mode { BUTLER_SCORE_RAW = 0, BUTLER_SCORE_SOFTVOTE = 1 };
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* butler_status_string(int status);
+
+/* ABI version, currently 1. */
+int butler_abi_version(void);
+
+/*
+ * butler_project_keys -- K_imp = K . W_K for the tokens [pos0, pos0 + n_new).
+ * Model card, Method: "the real (post-RoPE) cached keys are projected into the same
+ * d'-dimensional space via a learned matrix W_K of shape D x d'", appended once per
+ * generated token (n_new = 1 in decode, n_new = L when a prompt is first cached).
+ *
+ *   k_cache [B, Hkv, L_cap, D]      dtype   cached keys (read)
+ *   w_k     [D, d']                 dtype   projection of this layer, shared by all KV heads
+ *   kimp    [B, Hkv, L_cap, d']     dtype   rows pos0 .. pos0+n_new-1 written, others untouched
+ * Each output is accumulated in float32 and rounded to nearest even into dtype.
+ * D in {64, 128}; d' in {16, 32}; 0 <= pos0, n_new >= 1, pos0 + n_new <= L_cap.
+ */
+int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
+                        void* kimp, int B, int Hkv, int L_cap, int D, int dprime,
+                        int pos0, int n_new);
+
+/*
+ * butler_produce_queries -- Q_imp = f_theta(LN(H)) at a producer layer.
+ * Model card, Method: a producer reads the hidden states H [B, Lq, E] and predicts
+ * importance queries for itself and the next G-1 layers, (B*Hq) x G x Lq x d'.
+ * f_theta is the two-layer MLP  y = relu(LN(h) . W1) . W2  without biases; LN is a
+ * LayerNorm without affine parameters (biased variance, ln_eps).  The normalised row,
+ * the hidden activation and y are stored as bf16 between the steps.  Column
+ * (head*G + slot)*d' + i of y is Q_imp[b, head, slot, t, i].
+ *
+ *   h      [B, Lq, E]         bf16
+ *   w1     [E, F]             bf16
+ *   w2     [F, Hq*G*d']       bf16
+ *   q_imp  [B, Hq, G, Lq, d'] bf16 (written)
+ * dtype must be BUTLER_BF16.  E, F multiples of 64; Hq*G*d' a multiple of 64.
+ * workspace: normalised rows and hidden activations, split-K partial sums.
+ */
+int butler_produce_queries(void* stream, int dtype, const void* h, const void* w1,
+                           const void* w2, void* q_imp, int B, int Lq, int E, int F, int Hq,
+                           int G, int dprime, float ln_eps, void* workspace, size_t* ws_bytes);
+
+/*
+ * butler_score -- importance score of every cached token, per KV head and query row.
+ *
+ * BUTLER_SCORE_RAW (model card, Method: the consumer scores every cached token with its
+ * slot of Q_imp against K_imp):
+ *   q     = q_imp [B, Hq, G, Lq, d'], the consumer reads slot `slot`
+ *   keys  = kimp  [B, Hkv, L_cap, d']
+ *   score[b, g, i, t] = (sum over the R = Hq/Hkv query heads h of group g of
+ *                        Q_imp[b, h, slot, i, :]) . K_imp[b, g, t, :]
+ *   computed exactly (float64 products and sums of the stored values) and rounded once
+ *   to float32.  dk = d'.
+ * BUTLER_SCORE_SOFTVOTE (TokenSelect README, highlights: per-head Q.K criticality,
+ * normalised by a softmax per head, summed over heads):
+ *   q     = [B, Hq, Lq, D] attention queries, keys = k_cache [B, Hkv, L_cap, D]
+ *   score[b, g, i, t] = sum_{h in g} softmax_t(softmax_scale * q_h . k_t)
+ *   float32 arithmetic; the softmax runs over all scored tokens of the row.  dk = D,
+ *   G and slot are ignored.
+ * Causal rows (causal != 0): query row i sits at absolute position q_pos0 + i and scores
+ * only the tokens t <= q_pos0 + i; the others are written as -inf.  Non-causal rows score
+ * tokens [0, L).
+ *
+ *   scores [B, Hkv, Lq, L] float32 (written)
+ * RAW: d' in {16, 32}; SOFTVOTE: D in {64, 128}, Lq == 1 (decode); R in {1, 2, 4, 8}.
+ * workspace: SOFTVOTE keeps per-token logits and per-block softmax partials.
+ */
+int butler_score(void* stream, int mode, int dtype, const void* q, const void* keys,
+                 float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq, int L,
+                 int L_cap, int dk, int q_pos0, int causal, float softmax_scale,
+                 void* workspace, size_t* ws_bytes);
+
+/*
+ * butler_select_topk -- fixed-budget top-x + sink + window, per KV head and query row.
+ * Model card, Method and Memory requirements: keep the top-x tokens under a fixed
+ * budget (fixed_<N>pc keeps (100-N)% of the tokens), augmented by a sink prefix of
+ * n_sink tokens (min_sparse_index) and a recent window of n_window tokens
+ * (sliding_window).  For a row of length L_r (L, or q_pos0+i+1 for causal row i):
+ *   x   = floor(L_r * budget_num / budget_den)
+ *   T   = the first min(x, L_r) tokens ordered by (score descending, index ascending);
+ *         -0 equals +0, NaN ranks as -inf
+ *   S   = T  U  [0, min(n_sink, L_r))  U  [max(0, L_r - n_window), L_r)
+ * Output: `idx` (when non-NULL) holds S in ascending order in the first count[row]
+ * entries of its row, entries beyond that are left as they were; `bitmask` (when
+ * non-NULL) holds bit (t % 32) of word t / 32 set iff t in S, for every word of the row;
+ * count[row] = |S|.  At least one of idx, bitmask must be non-NULL.
+ *
+ *   scores  [B, Hkv, Lq, L]          float32 (read)
+ *   idx     [B, Hkv, Lq, cap]        int32   (written) -- cap >= min(L, x + n_sink + n_window)
+ *   bitmask [B, Hkv, Lq, ceil(L/32)] uint32  (written)
+ *   count   [B, Hkv, Lq]             int32   (written)
+ * 0 <= budget_num, 1 <= budget_den, n_sink >= 0, n_window >= 0.
+ * workspace: radix histograms, the threshold state and per-block counts.
+ */
+int butler_select_topk(void* stream, const float* scores, int budget_num, int budget_den,
+                       int n_sink, int n_window, int32_t* idx, uint32_t* bitmask,
+                       int32_t* count, int B, int Hkv, int Lq, int L, int cap, int q_pos0,
+                       int causal, void* workspace, size_t* ws_bytes);
+
+/*
+ * butler_sparse_decode_attn -- attention over the selected tokens only.
+ * Model card, intro and Method: attention reads only the selected subset of the full
+ * (never evicted) KV cache.  For query head h (KV head g = h / R) of row i:
+ *   o[b, h, i, :] = sum_{t in S} softmax_t(softmax_scale * q . k_t) v_t
+ * with float32 logits, float32 online softmax and float32 accumulation.
+ *
+ * Lq == 1 (decode): S comes from idx [B, Hkv, 1, cap] / count [B, Hkv, 1] as written by
+ *   butler_select_topk; split over the selected list, partial results merged in a fixed
+ *   order by the last block of each KV head.
+ * Lq > 1 (chunked prefill): S of row i comes from bitmask [B, Hkv, Lq, ceil(L/32)];
+ *   query row i sits at absolute position q_pos0 + i; only tokens t <= q_pos0 + i may
+ *   be selected.
+ *
+ *   q       [B, Hq, Lq, D]      dtype
+ *   k_cache [B, Hkv, L_cap, D]  dtype
+ *   v_cache [B, Hkv, L_cap, D]  dtype
+ *   out     [B, Hq, Lq, D]      float32 (written)
+ * An empty selected set is an error of the caller (the window always holds the newest
+ * token); its output row is written as zeros.  Selected indices must be < L <= L_cap.
+ * workspace: per-block softmax partials and merge tickets.
+ */
+int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* idx, const int32_t* count,
+                              const uint32_t* bitmask, float* out, int B, int Hq, int Hkv,
+                              int D, int Lq, int L, int L_cap, int cap, int q_pos0,
+                              float softmax_scale, void* workspace, size_t* ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BUTLER_H */

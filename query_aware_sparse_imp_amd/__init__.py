@@ -1,0 +1,235 @@
+"""Python binding of libbutler: query-aware sparse decode on AMD MI355X (gfx950).
+
+Argument marshalling only.  Every function here takes torch tensors that already
+live on the GPU, checks their shapes, dtypes and contiguity, and calls the C entry
+point of the same name in ``libbutler.so`` with raw device pointers, sizes and the
+current HIP stream.  All compute happens in the library's HIP kernels; there is no
+fallback.  Importing this package fails loudly if the library has not been built
+(``python -m query_aware_sparse_imp_amd.csrc.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Dict, Optional, Tuple
+
+import torch
+
+__all__ = [
+    "BUTLER_OK", "BUTLER_SCORE_RAW", "BUTLER_SCORE_SOFTVOTE", "ButlerError", "lib", "LIB_PATH",
+    "butler_project_keys", "butler_produce_queries", "butler_score", "butler_select_topk",
+    "butler_sparse_decode_attn", "butler_status_string", "butler_abi_version",
+    "declared_symbols", "workspace_bytes",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbutler.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "butler.h")
+
+BUTLER_OK = 0
+BUTLER_F32, BUTLER_BF16 = 0, 1
+BUTLER_SCORE_RAW, BUTLER_SCORE_SOFTVOTE = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m query_aware_sparse_imp_amd.csrc.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)
+_SIGS = {
+    "butler_status_string": ([_i], ctypes.c_char_p),
+    "butler_abi_version": ([], _i),
+    "butler_project_keys": ([_vp, _i, _vp, _vp, _vp] + [_i] * 7, _i),
+    "butler_produce_queries": ([_vp, _i, _vp, _vp, _vp, _vp] + [_i] * 7 + [_f, _vp, _sz], _i),
+    "butler_score": ([_vp, _i, _i, _vp, _vp, _vp] + [_i] * 11 + [_f, _vp, _sz], _i),
+    "butler_select_topk": ([_vp, _vp] + [_i] * 4 + [_vp, _vp, _vp] + [_i] * 7 + [_vp, _sz], _i),
+    "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 9 + [_f, _vp, _sz], _i),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+class ButlerError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {butler_status_string(status)} ({status})")
+        self.status = status
+
+
+def butler_status_string(status: int) -> str:
+    return lib.butler_status_string(status).decode()
+
+
+def butler_abi_version() -> int:
+    return lib.butler_abi_version()
+
+
+def declared_symbols() -> list:
+    """Function names declared in include/butler.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(butler_\w+)\s*\(", text)))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != BUTLER_OK:
+        raise ButlerError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BUTLER_BF16
+    if t.dtype == torch.float32:
+        return BUTLER_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# Workspaces: one zero-initialised buffer per (entry point, device), grown on demand.
+# The library leaves the counters inside a workspace zero after every call, so a buffer
+# can be reused call after call on one stream.
+_WS: Dict[Tuple[str, int], torch.Tensor] = {}
+
+
+def _workspace(name: str, nbytes: int, device: torch.device) -> Tuple[Optional[int], ctypes.c_size_t]:
+    if nbytes == 0:
+        return None, ctypes.c_size_t(0)
+    key = (name, device.index if device.index is not None else torch.cuda.current_device())
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf.data_ptr(), ctypes.c_size_t(buf.numel())
+
+
+def workspace_bytes(query) -> int:
+    """Runs a size query: ``query(ws_ptr, ws_bytes_ptr)`` with ws = NULL."""
+    n = ctypes.c_size_t(0)
+    _check("workspace query", query(None, ctypes.byref(n)))
+    return n.value
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def butler_project_keys(k_cache: torch.Tensor, w_k: torch.Tensor, kimp: torch.Tensor,
+                        pos0: int, n_new: int, stream=None) -> None:
+    """kimp[:, :, pos0:pos0+n_new] = k_cache[:, :, pos0:pos0+n_new] @ w_k (see butler.h)."""
+    B, Hkv, L_cap, D = k_cache.shape
+    dp = w_k.shape[1]
+    if w_k.shape != (D, dp) or kimp.shape != (B, Hkv, L_cap, dp):
+        raise ValueError("shape mismatch")
+    if not (k_cache.dtype == w_k.dtype == kimp.dtype):
+        raise TypeError("k_cache, w_k and kimp must share a dtype")
+    _check("butler_project_keys", lib.butler_project_keys(
+        _stream(stream), _dtype_code(k_cache), _ptr(k_cache), _ptr(w_k), _ptr(kimp),
+        B, Hkv, L_cap, D, dp, pos0, n_new))
+
+
+def butler_produce_queries(h: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+                           q_imp: torch.Tensor, ln_eps: float = 1e-5, stream=None) -> None:
+    """q_imp [B, Hq, G, Lq, d'] = reshape(relu(LN(h) @ w1) @ w2) (see butler.h)."""
+    B, Lq, E = h.shape
+    F = w1.shape[1]
+    _, Hq, G, Lq2, dp = q_imp.shape
+    if w1.shape != (E, F) or w2.shape != (F, Hq * G * dp) or Lq2 != Lq or q_imp.shape[0] != B:
+        raise ValueError("shape mismatch")
+    dt = _dtype_code(h)
+    args = (dt, _ptr(h), _ptr(w1), _ptr(w2), _ptr(q_imp), B, Lq, E, F, Hq, G, dp, ln_eps)
+    need = workspace_bytes(lambda ws, n: lib.butler_produce_queries(_stream(stream), *args, ws, n))
+    ws, n = _workspace("produce", need, h.device)
+    _check("butler_produce_queries",
+           lib.butler_produce_queries(_stream(stream), *args, ws, ctypes.byref(n)))
+
+
+def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.Tensor, *,
+                 Hkv: int, L: int, slot: int = 0, q_pos0: int = 0, causal: bool = False,
+                 softmax_scale: float = 1.0, stream=None) -> None:
+    """Importance scores [B, Hkv, Lq, L] (see butler.h).
+
+    RAW: q = q_imp [B, Hq, G, Lq, d'], keys = kimp [B, Hkv, L_cap, d'].
+    SOFTVOTE: q = [B, Hq, Lq, D], keys = k_cache [B, Hkv, L_cap, D].
+    """
+    if mode == BUTLER_SCORE_RAW:
+        B, Hq, G, Lq, dk = q.shape
+    else:
+        B, Hq, Lq, dk = q.shape
+        G = 1
+    Bk, Hk, L_cap, dk2 = keys.shape
+    if (Bk, Hk, dk2) != (B, Hkv, dk) or scores.shape != (B, Hkv, Lq, L):
+        raise ValueError("shape mismatch")
+    if q.dtype != keys.dtype or scores.dtype != torch.float32:
+        raise TypeError("dtype mismatch")
+    args = (mode, _dtype_code(q), _ptr(q), _ptr(keys), _ptr(scores), B, Hq, Hkv, G, slot, Lq, L,
+            L_cap, dk, q_pos0, int(causal), softmax_scale)
+    need = workspace_bytes(lambda ws, n: lib.butler_score(_stream(stream), *args, ws, n))
+    ws, n = _workspace("score", need, q.device)
+    _check("butler_score", lib.butler_score(_stream(stream), *args, ws, ctypes.byref(n)))
+
+
+def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n_sink: int,
+                       n_window: int, count: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                       bitmask: Optional[torch.Tensor] = None, *, q_pos0: int = 0,
+                       causal: bool = False, stream=None) -> None:
+    """Top-x + sink + window per row of scores [B, Hkv, Lq, L] (see butler.h)."""
+    B, Hkv, Lq, L = scores.shape
+    cap = 0
+    if idx is not None:
+        if idx.shape[:3] != (B, Hkv, Lq) or idx.dtype != torch.int32:
+            raise ValueError("idx must be int32 [B, Hkv, Lq, cap]")
+        cap = idx.shape[3]
+    if bitmask is not None:
+        if bitmask.shape != (B, Hkv, Lq, (L + 31) // 32) or bitmask.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("bitmask must be 32-bit [B, Hkv, Lq, ceil(L/32)]")
+    if count.shape != (B, Hkv, Lq) or count.dtype != torch.int32:
+        raise ValueError("count must be int32 [B, Hkv, Lq]")
+    args = (_ptr(scores), budget_num, budget_den, n_sink, n_window, _ptr(idx), _ptr(bitmask),
+            _ptr(count), B, Hkv, Lq, L, cap, q_pos0, int(causal))
+    need = workspace_bytes(lambda ws, n: lib.butler_select_topk(_stream(stream), *args, ws, n))
+    ws, n = _workspace("select", need, scores.device)
+    _check("butler_select_topk",
+           lib.butler_select_topk(_stream(stream), *args, ws, ctypes.byref(n)))
+
+
+def butler_sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              out: torch.Tensor, *, L: int, idx: Optional[torch.Tensor] = None,
+                              count: Optional[torch.Tensor] = None,
+                              bitmask: Optional[torch.Tensor] = None, q_pos0: int = 0,
+                              softmax_scale: float, stream=None) -> None:
+    """Attention of q [B, Hq, Lq, D] over the selected tokens (see butler.h)."""
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, L_cap, D2 = k_cache.shape
+    if (Bk, D2) != (B, D) or v_cache.shape != k_cache.shape or out.shape != (B, Hq, Lq, D):
+        raise ValueError("shape mismatch")
+    if out.dtype != torch.float32 or not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    cap = 0
+    if idx is not None:
+        if idx.shape[:3] != (B, Hkv, Lq) or count is None or count.shape != (B, Hkv, Lq):
+            raise ValueError("idx [B, Hkv, Lq, cap] and count [B, Hkv, Lq] required")
+        cap = idx.shape[3]
+    args = (_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(idx), _ptr(count),
+            _ptr(bitmask), _ptr(out), B, Hq, Hkv, D, Lq, L, L_cap, cap, q_pos0, softmax_scale)
+    need = workspace_bytes(
+        lambda ws, n: lib.butler_sparse_decode_attn(_stream(stream), *args, ws, n))
+    ws, n = _workspace("attn", need, q.device)
+    _check("butler_sparse_decode_attn",
+           lib.butler_sparse_decode_attn(_stream(stream), *args, ws, ctypes.byref(n)))

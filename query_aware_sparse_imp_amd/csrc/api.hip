@@ -1,0 +1,196 @@
+// C ABI of libbutler (declared in include/butler.h): host-side argument checks, the
+// two-phase workspace query and the kernel launches.  Every check runs before anything
+// is enqueued, and none of them touches the HIP runtime, so argument errors are
+// reported identically with or without a GPU.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/butler.h"
+#include "kernels.h"
+
+using namespace butler;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int from_hip(hipError_t e) { return e == hipSuccess ? BUTLER_OK : BUTLER_ERR_HIP; }
+
+inline bool debug_sync() {
+  static const bool on = [] {
+    const char* v = getenv("BUTLER_DEBUG_SYNC");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+inline int finish(hipStream_t s, hipError_t e) {
+  if (e != hipSuccess) return BUTLER_ERR_HIP;
+  if (debug_sync() && hipStreamSynchronize(s) != hipSuccess) return BUTLER_ERR_HIP;
+  return BUTLER_OK;
+}
+
+// Two-phase workspace protocol.  Returns 1 when the caller only asked for the size
+// (and *rc holds the status to return), 0 when the call should proceed.
+inline int workspace_phase(void* ws, size_t* ws_bytes, size_t need, int* rc) {
+  if (ws == nullptr) {
+    if (need == 0) return 0;
+    if (ws_bytes == nullptr) { *rc = BUTLER_ERR_INVALID_ARG; return 1; }
+    *ws_bytes = need;
+    *rc = BUTLER_OK;
+    return 1;
+  }
+  if (ws_bytes == nullptr || *ws_bytes < need) { *rc = BUTLER_ERR_WORKSPACE; return 1; }
+  if (!aligned16(ws)) { *rc = BUTLER_ERR_INVALID_ARG; return 1; }
+  return 0;
+}
+
+inline bool valid_dtype(int d) { return d == BUTLER_F32 || d == BUTLER_BF16; }
+inline bool pow2_group(int R) { return R == 1 || R == 2 || R == 4 || R == 8; }
+
+}  // namespace
+
+extern "C" {
+
+const char* butler_status_string(int status) {
+  switch (status) {
+    case BUTLER_OK: return "BUTLER_OK";
+    case BUTLER_ERR_INVALID_ARG: return "BUTLER_ERR_INVALID_ARG";
+    case BUTLER_ERR_UNSUPPORTED: return "BUTLER_ERR_UNSUPPORTED";
+    case BUTLER_ERR_WORKSPACE: return "BUTLER_ERR_WORKSPACE";
+    case BUTLER_ERR_HIP: return "BUTLER_ERR_HIP";
+    default: return "BUTLER_ERR_UNKNOWN";
+  }
+}
+
+int butler_abi_version(void) { return 1; }
+
+int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
+                        void* kimp, int B, int Hkv, int L_cap, int D, int dprime, int pos0,
+                        int n_new) {
+  if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
+  if (!k_cache || !w_k || !kimp) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(w_k) || !aligned16(kimp)) return BUTLER_ERR_INVALID_ARG;
+  if (B <= 0 || Hkv <= 0 || L_cap <= 0 || n_new <= 0 || pos0 < 0) return BUTLER_ERR_INVALID_ARG;
+  if ((long long)pos0 + n_new > L_cap) return BUTLER_ERR_INVALID_ARG;
+  if (!(D == 64 || D == 128) || !(dprime == 16 || dprime == 32)) return BUTLER_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(s, launch_project_keys(s, dtype, k_cache, w_k, kimp, B, Hkv, L_cap, D, dprime,
+                                       pos0, n_new));
+}
+
+int butler_produce_queries(void* stream, int dtype, const void* h, const void* w1,
+                           const void* w2, void* q_imp, int B, int Lq, int E, int F, int Hq,
+                           int G, int dprime, float ln_eps, void* workspace,
+                           size_t* ws_bytes) {
+  if (dtype != BUTLER_BF16) return BUTLER_ERR_UNSUPPORTED;
+  if (B <= 0 || Lq <= 0 || E <= 0 || F <= 0 || Hq <= 0 || G <= 0 || dprime <= 0)
+    return BUTLER_ERR_INVALID_ARG;
+  if (!(ln_eps > 0.f)) return BUTLER_ERR_INVALID_ARG;
+  const long long N2 = (long long)Hq * G * dprime;
+  if (E % 64 || F % 64 || N2 % 64 || N2 > (1 << 24)) return BUTLER_ERR_UNSUPPORTED;
+  if ((long long)B * Lq > (1 << 24)) return BUTLER_ERR_UNSUPPORTED;
+  int rc;
+  if (workspace_phase(workspace, ws_bytes, produce_workspace(B * Lq, E, F, (int)N2), &rc))
+    return rc;
+  if (!h || !w1 || !w2 || !q_imp) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w1) || !aligned16(w2) || !aligned16(q_imp))
+    return BUTLER_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(s, launch_produce(s, h, w1, w2, q_imp, B, Lq, E, F, Hq, G, dprime, ln_eps,
+                                  workspace));
+}
+
+int butler_score(void* stream, int mode, int dtype, const void* q, const void* keys,
+                 float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq, int L,
+                 int L_cap, int dk, int q_pos0, int causal, float softmax_scale,
+                 void* workspace, size_t* ws_bytes) {
+  if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
+  if (mode != BUTLER_SCORE_RAW && mode != BUTLER_SCORE_SOFTVOTE) return BUTLER_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || L <= 0 || L_cap < L || q_pos0 < 0)
+    return BUTLER_ERR_INVALID_ARG;
+  if (Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
+  if (!pow2_group(Hq / Hkv)) return BUTLER_ERR_UNSUPPORTED;
+  if ((long long)B * Hkv * Lq > 65535LL * 65535LL) return BUTLER_ERR_UNSUPPORTED;
+  size_t need = 0;
+  if (mode == BUTLER_SCORE_RAW) {
+    if (G <= 0 || slot < 0 || slot >= G) return BUTLER_ERR_INVALID_ARG;
+    if (!(dk == 16 || dk == 32)) return BUTLER_ERR_UNSUPPORTED;
+    if (Lq > 65535 || B * Hkv > 65535) return BUTLER_ERR_UNSUPPORTED;
+  } else {
+    if (!(dk == 64 || dk == 128)) return BUTLER_ERR_UNSUPPORTED;
+    if (Lq != 1 || causal) return BUTLER_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f)) return BUTLER_ERR_INVALID_ARG;
+    need = softvote_workspace(B, Hq, Hkv, L);
+  }
+  int rc;
+  if (workspace_phase(workspace, ws_bytes, need, &rc)) return rc;
+  if (!q || !keys || !scores) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(keys) || !aligned16(scores)) return BUTLER_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (mode == BUTLER_SCORE_RAW)
+    return finish(s, launch_score_raw(s, dtype, q, keys, scores, B, Hq, Hkv, G, slot, Lq, L,
+                                      L_cap, dk, q_pos0, causal));
+  return finish(s, launch_score_softvote(s, dtype, q, keys, scores, B, Hq, Hkv, L, L_cap, dk,
+                                         softmax_scale, workspace));
+}
+
+int butler_select_topk(void* stream, const float* scores, int budget_num, int budget_den,
+                       int n_sink, int n_window, int32_t* idx, uint32_t* bitmask,
+                       int32_t* count, int B, int Hkv, int Lq, int L, int cap, int q_pos0,
+                       int causal, void* workspace, size_t* ws_bytes) {
+  if (B <= 0 || Hkv <= 0 || Lq <= 0 || L <= 0 || q_pos0 < 0) return BUTLER_ERR_INVALID_ARG;
+  if (budget_num < 0 || budget_den <= 0 || n_sink < 0 || n_window < 0)
+    return BUTLER_ERR_INVALID_ARG;
+  const long long rows = (long long)B * Hkv * Lq;
+  if (rows > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
+  if (idx) {
+    const long long x = (long long)L * budget_num / budget_den;
+    long long need_cap = x + n_sink + n_window;
+    if (need_cap > L) need_cap = L;
+    if (cap < need_cap) return BUTLER_ERR_INVALID_ARG;
+  }
+  int rc;
+  if (workspace_phase(workspace, ws_bytes, select_workspace((int)rows, L, Lq), &rc)) return rc;
+  if (!scores || !count || (!idx && !bitmask)) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(scores)) return BUTLER_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(s, launch_select(s, scores, budget_num, budget_den, n_sink, n_window, idx,
+                                 bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, workspace));
+}
+
+int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* idx, const int32_t* count,
+                              const uint32_t* bitmask, float* out, int B, int Hq, int Hkv,
+                              int D, int Lq, int L, int L_cap, int cap, int q_pos0,
+                              float softmax_scale, void* workspace, size_t* ws_bytes) {
+  if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || L <= 0 || L_cap < L || q_pos0 < 0)
+    return BUTLER_ERR_INVALID_ARG;
+  if (Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
+  if (!pow2_group(Hq / Hkv) || !(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.f)) return BUTLER_ERR_INVALID_ARG;
+  const bool use_idx = idx != nullptr;
+  if (!use_idx && !bitmask) return BUTLER_ERR_INVALID_ARG;
+  const long long rows = (long long)B * Hkv * Lq;
+  if (use_idx) {
+    if (cap <= 0 || !count) return BUTLER_ERR_INVALID_ARG;
+    if (rows > 65535) return BUTLER_ERR_UNSUPPORTED;
+  } else {
+    if (L > 16384 || rows > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
+  }
+  const size_t need = use_idx ? attn_workspace(B, Hq, Hkv, D, Lq, L, cap) : 0;
+  int rc;
+  if (workspace_phase(workspace, ws_bytes, need, &rc)) return rc;
+  if (!q || !k_cache || !v_cache || !out) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return BUTLER_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (use_idx)
+    return finish(s, launch_attn_idx(s, dtype, q, k_cache, v_cache, idx, count, out, B, Hq, Hkv,
+                                     D, Lq, L_cap, cap, softmax_scale, workspace));
+  return finish(s, launch_attn_bitmask(s, dtype, q, k_cache, v_cache, bitmask, out, B, Hq, Hkv,
+                                       D, Lq, L, L_cap, q_pos0, softmax_scale, workspace));
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Device helpers shared by the libbutler kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define BUTLER_WAVE 64
+
+typedef uint16_t bf16_t;
+
+// bf16 <-> fp32.  bf16 is the upper half of an IEEE fp32; the narrowing rounds
+// to nearest, ties to even, and keeps NaN a (quiet) NaN.
+__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Element loaders: 16 bytes -> 8 (bf16) or 4 (fp32) floats.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const bf16_t* p, float* out) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[2 * j] = __uint_as_float(w[j] << 16);
+      out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void load_raw(const bf16_t* p, uint4& v) {
+    v = *reinterpret_cast<const uint4*>(p);
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float* out) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+};
+
+__device__ __forceinline__ float load_elem(const bf16_t* p) { return bf2f(*p); }
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+
+// Monotone key of a score: larger key <=> larger score.  NaN ranks as -inf and
+// -0 as +0, so equal scores always give equal keys.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// exp2 on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Inclusive wave-wide prefix sum (wave64).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive block-wide prefix sum over NT threads; `tmp` holds NT/64 ints of
+// LDS.  Returns this thread's exclusive prefix and the block total.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_sum(int v, int& total, int* tmp) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int inc = wave_inclusive_sum(v);
+  if (lane == 63) tmp[wid] = inc;
+  __syncthreads();
+  if (wid == 0) {
+    int w = (lane < NW) ? tmp[lane] : 0;
+    w = wave_inclusive_sum(w);
+    if (lane < NW) tmp[lane] = w;
+  }
+  __syncthreads();
+  const int before = wid ? tmp[wid - 1] : 0;
+  total = tmp[NW - 1];
+  __syncthreads();
+  return before + inc - v;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_sum_f(float v, float* tmp) {
+  constexpr int NW = NT / 64;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += tmp[w];
+  __syncthreads();
+  return s;
+}
+
+__device__ __forceinline__ float neg_inf() { return __uint_as_float(0xff800000u); }

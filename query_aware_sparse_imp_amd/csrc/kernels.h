@@ -1,0 +1,48 @@
+// Host-side launchers of the libbutler kernels.  Each returns a hipError_t
+// from the launch; arguments are validated by the C ABI layer (api.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace butler {
+
+// ---- key projection -------------------------------------------------------
+hipError_t launch_project_keys(hipStream_t s, int dtype, const void* k, const void* w,
+                               void* kimp, int B, int Hkv, int L_cap, int D, int dp,
+                               int pos0, int n_new);
+
+// ---- producer -------------------------------------------------------------
+size_t produce_workspace(int M, int E, int F, int N2);
+hipError_t launch_produce(hipStream_t s, const void* h, const void* w1, const void* w2,
+                          void* q_imp, int B, int Lq, int E, int F, int Hq, int G, int dp,
+                          float eps, void* ws);
+
+// ---- scoring --------------------------------------------------------------
+hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
+                            float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
+                            int L, int L_cap, int dp, int q_pos0, int causal);
+size_t softvote_workspace(int B, int Hq, int Hkv, int L);
+hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const void* k,
+                                 float* scores, int B, int Hq, int Hkv, int L, int L_cap,
+                                 int D, float scale, void* ws);
+
+// ---- selection ------------------------------------------------------------
+size_t select_workspace(int rows, int L, int Lq);
+hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
+                         int n_window, int32_t* idx, uint32_t* bitmask, int32_t* count,
+                         int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
+                         void* ws);
+
+// ---- attention ------------------------------------------------------------
+size_t attn_workspace(int B, int Hq, int Hkv, int D, int Lq, int L, int cap);
+hipError_t launch_attn_idx(hipStream_t s, int dtype, const void* q, const void* k,
+                           const void* v, const int32_t* idx, const int32_t* count,
+                           float* out, int B, int Hq, int Hkv, int D, int Lq, int L_cap,
+                           int cap, float scale, void* ws);
+hipError_t launch_attn_bitmask(hipStream_t s, int dtype, const void* q, const void* k,
+                               const void* v, const uint32_t* bitmask, float* out, int B,
+                               int Hq, int Hkv, int D, int Lq, int L, int L_cap, int q_pos0,
+                               float scale, void* ws);
+
+}  // namespace butler

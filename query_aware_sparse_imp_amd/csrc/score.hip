@@ -1,0 +1,263 @@
+// Importance scores of every cached token.
+//
+// RAW (TokenButler model card, Method): score(t) = (sum of the group's Q_imp) . K_imp[t].
+//   The K_imp stream is read with 16-byte loads, DP/8 lanes per token (4 lanes at
+//   d' = 32, so one wave instruction covers 16 consecutive 64-byte rows = 1 KiB);
+//   products and sums run in float64, where every partial sum of bf16 products is
+//   exact, and the result is rounded once to float32 -- the score is the exactly
+//   rounded dot product whatever the reduction order.
+//
+// SOFTVOTE (TokenSelect README, highlights): per-head logits z_h(t) = scale * q_h . k_t,
+//   a softmax over t for every head, summed over the heads of the GQA group.
+//   Pass 1 streams the keys once (D/8 lanes per 256-byte key row), writes the
+//   base-2 logits of the R heads and a per-block (max, sum of exp2) pair per head.
+//   Pass 2 merges the block pairs in block order (every block computes the same
+//   merge) and turns the stored logits into the summed probabilities.
+#include "common.h"
+#include "kernels.h"
+
+namespace butler {
+namespace {
+
+constexpr int kRawThreads = 256;
+constexpr int kRawUnroll = 4;
+
+template <typename T, int DP>
+__global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
+    const T* __restrict__ q_imp, const T* __restrict__ kimp, float* __restrict__ scores,
+    int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal,
+    int tpb) {
+  constexpr int EPL = Vec16<T>::N;
+  constexpr int LPT = DP / EPL;           // lanes per token
+  constexpr int TPI = kRawThreads / LPT;  // tokens per block-wide step
+  const int bg = blockIdx.z, i = blockIdx.y;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int R = Hq / Hkv;
+  __shared__ double qbar[DP];
+  if (threadIdx.x < DP) {
+    double a = 0.0;
+    for (int r = 0; r < R; ++r)
+      a += (double)load_elem(
+          q_imp + ((((size_t)b * Hq + g * R + r) * G + slot) * Lq + i) * DP + threadIdx.x);
+    qbar[threadIdx.x] = a;
+  }
+  __syncthreads();
+  const int part = threadIdx.x % LPT, sub = threadIdx.x / LPT;
+  double qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = qbar[part * EPL + e];
+  const int L_r = causal ? min(q_pos0 + i + 1, L) : L;
+  const int t0 = blockIdx.x * tpb;
+  const int t1 = min(t0 + tpb, L);
+  const int tv = min(t1, L_r);
+  const T* kb = kimp + (size_t)bg * L_cap * DP + part * EPL;
+  float* srow = scores + ((size_t)bg * Lq + i) * L;
+  for (int t = t0 + sub; t < t1; t += TPI * kRawUnroll) {
+    float kv[kRawUnroll][EPL];
+#pragma unroll
+    for (int u = 0; u < kRawUnroll; ++u) {
+      const int tu = t + u * TPI;
+      if (tu < tv) {
+        Vec16<T>::load(kb + (size_t)tu * DP, kv[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) kv[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRawUnroll; ++u) {
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc = fma(qv[e], (double)kv[u][e], acc);
+#pragma unroll
+      for (int o = 1; o < LPT; o <<= 1) acc += __shfl_xor(acc, o, 64);
+      const int tu = t + u * TPI;
+      if (part == 0 && tu < t1) srow[tu] = (tu < L_r) ? (float)acc : neg_inf();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// soft voting
+// ---------------------------------------------------------------------------
+
+constexpr int kSvThreads = 256;
+constexpr int kSvTokensPerBlock = 256;
+
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
+  if (m2 == neg_inf()) return;
+  if (m == neg_inf()) { m = m2; l = l2; return; }
+  const float mn = fmaxf(m, m2);
+  l = l * fast_exp2(m - mn) + l2 * fast_exp2(m2 - mn);
+  m = mn;
+}
+
+template <typename T, int D, int R>
+__global__ __launch_bounds__(kSvThreads) void softvote_logits_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ logits,
+    float2* __restrict__ part, int Hq, int Hkv, int L, int L_cap, float scale_log2,
+    int nblk) {
+  constexpr int EPL = Vec16<T>::N;
+  constexpr int LPR = D / EPL;
+  constexpr int TPW = 64 / LPR;
+  constexpr int ITERS = 64 / TPW;
+  const int bg = blockIdx.y, blk = blockIdx.x;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int sub = lane / LPR, pe = lane % LPR;
+  float qr[R][EPL];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float tmp[EPL];
+    Vec16<T>::load(q + ((size_t)b * Hq + g * R + r) * D + pe * EPL, tmp);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qr[r][e] = tmp[e] * scale_log2;
+  }
+  float m[R], l[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) { m[r] = neg_inf(); l[r] = 0.f; }
+  const int tbase = blk * kSvTokensPerBlock + wid * 64 + sub;
+  const T* kb = k + (size_t)bg * L_cap * D + pe * EPL;
+  float* zb = logits + (size_t)bg * R * L;
+#pragma unroll 4
+  for (int it = 0; it < ITERS; ++it) {
+    const int t = tbase + it * TPW;
+    float kv[EPL];
+    if (t < L) {
+      Vec16<T>::load(kb + (size_t)t * D, kv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kv[e] = 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a = fmaf(qr[r][e], kv[e], a);
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) a += __shfl_xor(a, o, 64);
+      if (t < L) {
+        if (pe == 0) zb[(size_t)r * L + t] = a;
+        merge_ml(m[r], l[r], a, 1.f);
+      }
+    }
+  }
+  // lane groups of the wave -> one pair per head
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) {
+      const float m2 = __shfl_xor(m[r], o, 64);
+      const float l2 = __shfl_xor(l[r], o, 64);
+      merge_ml(m[r], l[r], m2, l2);
+    }
+  }
+  __shared__ float sm[4][R], sl[4][R];
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) { sm[wid][r] = m[r]; sl[wid][r] = l[r]; }
+  }
+  __syncthreads();
+  if (threadIdx.x < R) {
+    const int r = threadIdx.x;
+    float mm = sm[0][r], ll = sl[0][r];
+    for (int w = 1; w < 4; ++w) merge_ml(mm, ll, sm[w][r], sl[w][r]);
+    part[((size_t)bg * nblk + blk) * R + r] = make_float2(mm, ll);
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
+    const float* __restrict__ logits, const float2* __restrict__ part,
+    float* __restrict__ scores, int L, int nblk) {
+  const int bg = blockIdx.y, blk = blockIdx.x;
+  __shared__ float Ms[R], Ls[R];
+  if (threadIdx.x < R) {
+    const int r = threadIdx.x;
+    float mm = neg_inf(), ll = 0.f;
+    for (int j = 0; j < nblk; ++j) {
+      const float2 p = part[((size_t)bg * nblk + j) * R + r];
+      merge_ml(mm, ll, p.x, p.y);
+    }
+    Ms[r] = mm;
+    Ls[r] = ll;
+  }
+  __syncthreads();
+  const float* zb = logits + (size_t)bg * R * L;
+  const int t0 = blk * kSvTokensPerBlock;
+  for (int t = t0 + threadIdx.x; t < min(t0 + kSvTokensPerBlock, L); t += kSvThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) s += fast_exp2(zb[(size_t)r * L + t] - Ms[r]) / Ls[r];
+    scores[(size_t)bg * L + t] = s;
+  }
+}
+
+template <typename T, int DP>
+hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scores, int B,
+                 int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
+                 int causal) {
+  constexpr int LPT = DP / Vec16<T>::N;
+  const int tpb = (kRawThreads / LPT) * kRawUnroll * 2;
+  dim3 grid((L + tpb - 1) / tpb, Lq, B * Hkv);
+  hipLaunchKernelGGL((score_raw_kernel<T, DP>), grid, dim3(kRawThreads), 0, s, (const T*)q_imp,
+                     (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal,
+                     tpb);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int R>
+hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int B, int Hq,
+                int Hkv, int L, int L_cap, float scale, void* ws) {
+  const int nblk = (L + kSvTokensPerBlock - 1) / kSvTokensPerBlock;
+  float* logits = (float*)ws;
+  float2* part = (float2*)(logits + (size_t)B * Hkv * R * L);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  dim3 grid(nblk, B * Hkv);
+  hipLaunchKernelGGL((softvote_logits_kernel<T, D, R>), grid, dim3(kSvThreads), 0, s,
+                     (const T*)q, (const T*)k, logits, part, Hq, Hkv, L, L_cap, scale_log2,
+                     nblk);
+  hipLaunchKernelGGL((softvote_combine_kernel<R>), grid, dim3(kSvThreads), 0, s, logits, part,
+                     scores, L, nblk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
+                            float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
+                            int L, int L_cap, int dp, int q_pos0, int causal) {
+  if (dtype == 1) {
+    if (dp == 32) return raw_t<bf16_t, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
+    if (dp == 16) return raw_t<bf16_t, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
+  } else {
+    if (dp == 32) return raw_t<float, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
+    if (dp == 16) return raw_t<float, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t softvote_workspace(int B, int Hq, int Hkv, int L) {
+  const int R = Hq / Hkv;
+  const size_t nblk = (L + kSvTokensPerBlock - 1) / kSvTokensPerBlock;
+  return (size_t)B * Hkv * R * L * sizeof(float) + (size_t)B * Hkv * nblk * R * sizeof(float2);
+}
+
+hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const void* k,
+                                 float* scores, int B, int Hq, int Hkv, int L, int L_cap,
+                                 int D, float scale, void* ws) {
+  const int R = Hq / Hkv;
+#define BUTLER_SV(T, DD, RR)                                                       \
+  if (D == DD && R == RR) return sv_t<T, DD, RR>(s, q, k, scores, B, Hq, Hkv, L, L_cap, scale, ws);
+  if (dtype == 1) {
+    BUTLER_SV(bf16_t, 128, 1) BUTLER_SV(bf16_t, 128, 2) BUTLER_SV(bf16_t, 128, 4) BUTLER_SV(bf16_t, 128, 8)
+    BUTLER_SV(bf16_t, 64, 1) BUTLER_SV(bf16_t, 64, 2) BUTLER_SV(bf16_t, 64, 4) BUTLER_SV(bf16_t, 64, 8)
+  } else {
+    BUTLER_SV(float, 128, 1) BUTLER_SV(float, 128, 2) BUTLER_SV(float, 128, 4) BUTLER_SV(float, 128, 8)
+    BUTLER_SV(float, 64, 1) BUTLER_SV(float, 64, 2) BUTLER_SV(float, 64, 4) BUTLER_SV(float, 64, 8)
+  }
+#undef BUTLER_SV
+  return hipErrorInvalidValue;
+}
+
+}  // namespace butler

@@ -1,0 +1,111 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/butler.h declares, answers workspace queries, and rejects bad arguments with
+the documented status before anything is enqueued (no HIP call is made on these paths).
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import query_aware_sparse_imp_amd as qa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = qa.lib
+OK, INV, UNS, WSE = 0, -1, -2, -3
+FAKE = 0x10000          # a 16-byte aligned non-null address; never dereferenced here
+MIS = 0x10004           # misaligned
+
+
+def test_every_declared_symbol_is_exported():
+    names = qa.declared_symbols()
+    assert {"butler_project_keys", "butler_produce_queries", "butler_score",
+            "butler_select_topk", "butler_sparse_decode_attn"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", qa.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+
+
+def test_status_strings_and_version():
+    assert qa.butler_abi_version() == 1
+    assert qa.butler_status_string(0) == "BUTLER_OK"
+    assert qa.butler_status_string(-3) == "BUTLER_ERR_WORKSPACE"
+    assert qa.butler_status_string(123) == "BUTLER_ERR_UNKNOWN"
+
+
+def test_project_keys_validation():
+    f = L.butler_project_keys
+    assert f(None, 1, None, FAKE, FAKE, 1, 8, 100, 128, 32, 0, 1) == INV      # null
+    assert f(None, 1, MIS, FAKE, FAKE, 1, 8, 100, 128, 32, 0, 1) == INV       # misaligned
+    assert f(None, 1, FAKE, FAKE, FAKE, 1, 8, 100, 128, 32, 99, 2) == INV     # past L_cap
+    assert f(None, 1, FAKE, FAKE, FAKE, 1, 8, 100, 96, 32, 0, 1) == UNS       # D
+    assert f(None, 1, FAKE, FAKE, FAKE, 1, 8, 100, 128, 24, 0, 1) == UNS      # d'
+    assert f(None, 7, FAKE, FAKE, FAKE, 1, 8, 100, 128, 32, 0, 1) == UNS      # dtype
+    assert f(None, 1, FAKE, FAKE, FAKE, 0, 8, 100, 128, 32, 0, 1) == INV      # B
+
+
+def _score(mode=0, dtype=1, q=FAKE, keys=FAKE, scores=FAKE, B=1, Hq=32, Hkv=8, G=1, slot=0,
+           Lq=1, Lk=1000, L_cap=1000, dk=32, q_pos0=0, causal=0, scale=0.1, ws=None, n=None):
+    return L.butler_score(None, mode, dtype, q, keys, scores, B, Hq, Hkv, G, slot, Lq, Lk,
+                          L_cap, dk, q_pos0, causal, scale, ws, n)
+
+
+def test_score_validation_and_workspace_query():
+    assert _score(Hq=30) == INV                         # Hq % Hkv
+    assert _score(Hq=24, Hkv=8) == UNS                  # group of 3
+    assert _score(Lk=1001) == INV                       # L > L_cap
+    assert _score(slot=1, G=1) == INV
+    assert _score(dk=64) == UNS                         # raw d'
+    assert _score(mode=1, dk=128, Lq=2) == UNS          # softvote decode only
+    n = ctypes.c_size_t(0)
+    assert _score(mode=1, dk=128, n=ctypes.byref(n)) == OK
+    R, Lk = 4, 1000
+    assert n.value >= 8 * R * Lk * 4
+    small = ctypes.c_size_t(16)
+    assert _score(mode=1, dk=128, ws=FAKE, n=ctypes.byref(small)) == WSE
+    assert _score(q=None) == INV
+
+
+def test_select_validation():
+    f = L.butler_select_topk
+    # cap smaller than min(L, x + sink + window)
+    assert f(None, FAKE, 1, 2, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 567, 0, 0, None,
+             None) == INV
+    assert f(None, FAKE, 1, 0, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
+             None) == INV                                                  # den = 0
+    assert f(None, FAKE, 1, 2, -1, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
+             None) == INV                                                  # negative sink
+    assert f(None, FAKE, 1, 2, 4, 64, None, None, FAKE, 1, 8, 1, 1000, 0, 0, 0, None,
+             None) == INV                                                  # no output
+
+
+def test_attention_validation_and_workspace_query():
+    f = L.butler_sparse_decode_attn
+    n = ctypes.c_size_t(0)
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 128, 1, 32768, 32768,
+             16452, 0, 0.088, None, ctypes.byref(n)) == OK
+    nsplit = (16452 + 255) // 256
+    assert n.value >= 8 * nsplit * 4 * 130 * 4
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, 32, 8, 128, 1, 32768, 32768,
+             16452, 0, 0.088, None, None) == INV                            # idx without count
+    assert f(None, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1, 32, 8, 128, 4, 20000, 20000,
+             0, 0, 0.088, None, None) == UNS                                # bitmask L too long
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 96, 1, 100, 100,
+             100, 0, 0.088, None, None) == UNS                              # D
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 128, 1, 100, 100,
+             100, 0, -1.0, None, None) == INV                               # scale
+
+
+def test_produce_validation_and_workspace_query():
+    f = L.butler_produce_queries
+    n = ctypes.c_size_t(0)
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, 1, 1, 4096, 1024, 32, 4, 32, 1e-5, None,
+             ctypes.byref(n)) == OK
+    assert n.value >= 4096 * 2 + 1024 * 2
+    assert f(None, 0, FAKE, FAKE, FAKE, FAKE, 1, 1, 4096, 1024, 32, 4, 32, 1e-5, None,
+             ctypes.byref(n)) == UNS                                        # fp32 producer
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, 1, 1, 4000, 1024, 32, 4, 32, 1e-5, None,
+             ctypes.byref(n)) == UNS                                        # E % 64

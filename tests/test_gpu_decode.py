@@ -1,0 +1,145 @@
+"""GPU parity of the decode path (raw scorer): project -> score -> select -> attend.
+
+Workloads: the tiny fp32 decode step (B=1, one head, D=64, L=256, d'=16) and the
+Llama-3.1-8B-shaped bf16 layer (32/8 heads, D=128, d'=32, 50% + sink 4 + window 64)
+at a ragged size that spans several tiles and at the full L=32768, each over a few
+decode steps that append one token.  Every stage is gated on the GPU's own upstream
+result (see tests/parity.py); the independent oracle chain is reported.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from parity import (ATOL, check_attend, check_project, check_select_exact, decode_step_gpu,
+                    np64, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import query_aware_sparse_imp_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _run_decode(w, L, steps, layer=0, report=None):
+    import query_aware_sparse_imp_amd as qa
+    print(f"[decode] cfg={w.cfg} L={L} steps={steps} layer={layer}", flush=True)
+    inp = to_device(synthetic.decode_layer(w, layer, L=L, extra=steps))
+    dev = "cuda"
+    L_cap = inp["L_cap"]
+    kimp = torch.zeros(w.B, w.Hkv, L_cap, w.dprime, dtype=w.dtype, device=dev)
+    qa.butler_project_keys(inp["k_cache_d"], inp["w_k_d"], kimp, 0, L)
+    torch.cuda.synchronize()
+    check_project(kimp, inp["k_cache"], inp["w_k"], 0, L)
+    q_imp_slot = np64(inp["q_imp"])[:, :, 0, 0, :]                 # [B, Hq, d']
+    for s in range(steps + 1):
+        Lc = L + s
+        if s > 0:
+            qa.butler_project_keys(inp["k_cache_d"], inp["w_k_d"], kimp, Lc - 1, 1)
+        r = decode_step_gpu(inp, kimp, Lc, qa.BUTLER_SCORE_RAW, q_imp=inp["q_imp_d"])
+        torch.cuda.synchronize()
+        if s > 0:
+            check_project(kimp, inp["k_cache"], inp["w_k"], Lc - 1, Lc)
+        kimp_np = np64(kimp[:, :, :Lc])
+        want_s = oracle.score_raw(q_imp_slot[:, :, None, :], kimp_np, w.Hkv)
+        got_s = np64(r["scores"])
+        if w.dtype == torch.bfloat16:
+            assert np.array_equal(got_s, want_s), "raw scores must be bit-exact"
+        else:
+            qbar = np.abs(q_imp_slot.reshape(w.B, w.Hkv, w.R, -1)).sum(2)
+            mag = np.einsum("bgi,bgti->bgt", qbar, np.abs(kimp_np))[:, :, None, :]
+            diff = got_s != want_s
+            assert (np.abs(got_s - want_s) <= 1e-5 * mag)[diff].all()
+        check_select_exact(r["idx"], r["count"], got_s, r["num"], r["den"], w.n_sink,
+                           w.n_window)
+        idx, cnt = r["idx"].cpu().numpy(), r["count"].cpu().numpy()
+        check_attend(r["out"], inp["q"], inp["k_cache"], inp["v_cache"],
+                     lambda b, g, i: idx[b, g, i, :cnt[b, g, i]], w.scale, w.dtype)
+        # independent oracle chain (reported, not gated)
+        kimp_or = oracle.project_keys(np64(inp["k_cache"][:, :, :Lc]), np64(inp["w_k"]),
+                                      "bf16" if w.dtype == torch.bfloat16 else "f32")
+        ind = oracle.decode_layer_step(q=np64(inp["q"])[:, :, 0], k_cache=np64(inp["k_cache"]),
+                                       v_cache=np64(inp["v_cache"]), L=Lc, num=w.budget_num,
+                                       den=w.budget_den, n_sink=w.n_sink, n_window=w.n_window,
+                                       scale=w.scale, Hkv=w.Hkv, mode="raw",
+                                       q_imp_slot=q_imp_slot, kimp=kimp_or)
+        jac = []
+        for b in range(w.B):
+            for g in range(w.Hkv):
+                a = set(idx[b, g, 0, :cnt[b, g, 0]].tolist())
+                o = set(ind["sel"][b][g].tolist())
+                jac.append(len(a & o) / len(a | o))
+        err = float(np.abs(r["out"].cpu().double().numpy()[:, :, 0] - ind["out"]).max())
+        print(f"  step {s}: L={Lc} independent chain: min Jaccard {min(jac):.6f}, "
+              f"max-abs {err:.3e}", flush=True)
+        if report is not None:
+            report.append((Lc, min(jac), err))
+
+
+def test_tiny_fp32_decode():
+    w = synthetic.WORKLOADS[1]
+    _run_decode(w, w.L, steps=2)
+
+
+def test_layer_bf16_ragged_decode():
+    w = synthetic.WORKLOADS[2]
+    _run_decode(w, 4133, steps=3, layer=1)
+
+
+def test_layer_bf16_full_size_decode():
+    w = synthetic.WORKLOADS[2]
+    rep = []
+    _run_decode(w, w.L, steps=2, layer=0, report=rep)
+    assert min(j for _, j, _ in rep) > 0.95
+
+
+def test_decode_is_deterministic():
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[2]
+    inp = to_device(synthetic.decode_layer(w, 2, L=9000))
+    kimp = torch.zeros(w.B, w.Hkv, 9000, w.dprime, dtype=w.dtype, device="cuda")
+    qa.butler_project_keys(inp["k_cache_d"], inp["w_k_d"], kimp, 0, 9000)
+    outs = [decode_step_gpu(inp, kimp, 9000, qa.BUTLER_SCORE_RAW, q_imp=inp["q_imp_d"])
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for key in ("scores", "idx", "count", "out"):
+            assert torch.equal(o[key], outs[0][key]), key
+
+
+def test_full_budget_is_dense_attention():
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[2]
+    L = 3000
+    inp = to_device(synthetic.decode_layer(w, 3, L=L))
+    kimp = torch.zeros(w.B, w.Hkv, L, w.dprime, dtype=w.dtype, device="cuda")
+    qa.butler_project_keys(inp["k_cache_d"], inp["w_k_d"], kimp, 0, L)
+    r = decode_step_gpu(inp, kimp, L, qa.BUTLER_SCORE_RAW, q_imp=inp["q_imp_d"], dense=True)
+    torch.cuda.synchronize()
+    assert (r["count"].cpu() == L).all()
+    dense = oracle.dense_decode_attn(np64(inp["q"])[:, :, 0], np64(inp["k_cache"]),
+                                     np64(inp["v_cache"]), L, w.scale)
+    assert np.abs(r["out"].cpu().double().numpy()[:, :, 0] - dense).max() <= ATOL[w.dtype]
+
+
+def test_zero_importance_queries_tie_to_lowest_indices():
+    """Q_imp = 0 makes every raw score +0: the budget takes the lowest indices."""
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[2]
+    L = 2500
+    inp = to_device(synthetic.decode_layer(w, 4, L=L))
+    inp["q_imp_d"] = torch.zeros_like(inp["q_imp_d"])
+    kimp = torch.zeros(w.B, w.Hkv, L, w.dprime, dtype=w.dtype, device="cuda")
+    qa.butler_project_keys(inp["k_cache_d"], inp["w_k_d"], kimp, 0, L)
+    r = decode_step_gpu(inp, kimp, L, qa.BUTLER_SCORE_RAW, q_imp=inp["q_imp_d"])
+    torch.cuda.synchronize()
+    x = L // 2
+    want = sorted(set(range(x)) | set(range(L - w.n_window, L)))
+    cnt = r["count"].cpu().numpy()
+    idx = r["idx"].cpu().numpy()
+    for g in range(w.Hkv):
+        assert idx[0, g, 0, :cnt[0, g, 0]].tolist() == want

@@ -1,0 +1,83 @@
+"""GPU selection against the oracle on hand-made score rows (bit-exact sets).
+
+Covers ties (small-integer scores), -0 versus +0, NaN, +-inf, ragged lengths, budgets of
+0, of exactly L and above L, sinks and windows longer than the row, and causal rows whose
+length grows with the query position, with both index-list and bitmask outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import bitmask_to_sets
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+SPECIAL = np.array([np.nan, -0.0, 0.0, np.inf, -np.inf, 1.0, -1.0], np.float32)
+
+
+def _scores(rng, shape, kind):
+    if kind == "normal":
+        return rng.standard_normal(shape).astype(np.float32)
+    if kind == "ties":
+        return rng.integers(-3, 4, shape).astype(np.float32)
+    if kind == "special":
+        s = rng.standard_normal(shape).astype(np.float32)
+        m = rng.random(shape) < 0.3
+        s[m] = SPECIAL[rng.integers(0, len(SPECIAL), int(m.sum()))]
+        return s
+    if kind == "equal":
+        return np.full(shape, 0.5, np.float32)
+    raise ValueError(kind)
+
+
+def _run(scores_np, num, den, ns, nw, causal=False, q_pos0=0):
+    import query_aware_sparse_imp_amd as qa
+    B, Hkv, Lq, L = scores_np.shape
+    x = (L * num) // den
+    cap = max(1, min(L, x + ns + nw))
+    s = torch.from_numpy(scores_np).cuda()
+    idx = torch.full((B, Hkv, Lq, cap), -7, dtype=torch.int32, device="cuda")
+    bm = torch.zeros((B, Hkv, Lq, (L + 31) // 32), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((B, Hkv, Lq), dtype=torch.int32, device="cuda")
+    qa.butler_select_topk(s, num, den, ns, nw, cnt, idx=idx, bitmask=bm, q_pos0=q_pos0,
+                          causal=causal)
+    torch.cuda.synchronize()
+    sets = bitmask_to_sets(bm, L)
+    cnt_np, idx_np = cnt.cpu().numpy(), idx.cpu().numpy()
+    for b in range(B):
+        for g in range(Hkv):
+            for i in range(Lq):
+                L_r = min(q_pos0 + i + 1, L) if causal else L
+                want = oracle.select(scores_np[b, g, i, :L_r].astype(np.float64),
+                                     oracle.budget(L_r, num, den), ns, nw)
+                got = idx_np[b, g, i, :cnt_np[b, g, i]]
+                assert cnt_np[b, g, i] == len(want), (L, num, den, ns, nw, b, g, i)
+                assert np.array_equal(got, want), (L, num, den, ns, nw, b, g, i)
+                assert np.array_equal(np.nonzero(sets[b, g, i])[0], want)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "special", "equal"])
+def test_select_rows_match_oracle(kind):
+    rng = np.random.default_rng({"normal": 1, "ties": 2, "special": 3, "equal": 4}[kind])
+    cases = [(1, 1, 2, 0, 0), (2, 1, 2, 1, 1), (31, 1, 2, 4, 16), (32, 3, 10, 4, 64),
+             (33, 1, 16, 4, 128), (100, 0, 1, 3, 5), (257, 1, 1, 4, 16), (1000, 5, 4, 0, 0),
+             (4097, 1, 2, 4, 64), (20011, 1, 16, 4, 128), (40000, 3, 10, 4, 64)]
+    for (L, num, den, ns, nw) in cases:
+        print(f"[select] kind={kind} L={L} budget={num}/{den} sink={ns} window={nw}", flush=True)
+        _run(_scores(rng, (1, 3, 1, L), kind), num, den, ns, nw)
+
+
+def test_select_causal_rows():
+    rng = np.random.default_rng(5)
+    for (Lq, q_pos0, L) in ((37, 100, 137), (64, 0, 64), (129, 1000, 1129)):
+        print(f"[select-causal] Lq={Lq} q_pos0={q_pos0} L={L}", flush=True)
+        _run(_scores(rng, (2, 2, Lq, L), "ties"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0)
+        _run(_scores(rng, (1, 2, Lq, L), "normal"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0)
