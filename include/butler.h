@@ -22,13 +22,16 @@
  *     and attention outputs are always float32; indices, counts are int32.
  *   - Arguments are validated on the host before anything is enqueued.  On an error
  *     return nothing has been enqueued and no output has been touched.
- *   - Workspace (where an entry point has one) follows a two-phase query: call with
- *     workspace == NULL and ws_bytes != NULL, the required size is written to *ws_bytes
- *     and BUTLER_OK is returned without enqueueing anything.  Then call with a buffer of
- *     at least that size and *ws_bytes set to its size.  A workspace buffer must be
- *     zero-filled before its first use; every call leaves the counters in it zero again,
- *     so the same buffer can be reused call after call on one stream.  Two calls that
- *     share one workspace must not run concurrently.
+ *   - Workspace follows a two-phase query.  workspace == NULL with ws_bytes != NULL is
+ *     a size query: the required size (0 when none is needed) is written to *ws_bytes,
+ *     BUTLER_OK is returned and nothing is enqueued.  The real call passes a buffer of at
+ *     least that size with *ws_bytes set to its size, or workspace == NULL and
+ *     ws_bytes == NULL when the required size is 0 (BUTLER_ERR_WORKSPACE otherwise).  A
+ *     workspace must be zero-filled before its first use; every call leaves the
+ *     accumulators in it zero again, so one buffer serves every later call with the same
+ *     size arguments on one stream.  A call with other sizes may lay the workspace out
+ *     differently: give it its own buffer, or zero-fill the shared one first.  Two calls
+ *     that share a workspace must not run concurrently.
  *   - Results are deterministic: the same inputs give bitwise identical outputs.
  */
 #ifndef BUTLER_H
@@ -68,7 +71,8 @@ int butler_abi_version(void);
  *   k_cache [B, Hkv, L_cap, D]      dtype   cached keys (read)
  *   w_k     [D, d']                 dtype   projection of this layer, shared by all KV heads
  *   kimp    [B, Hkv, L_cap, d']     dtype   rows pos0 .. pos0+n_new-1 written, others untouched
- * Each output is accumulated in float32 and rounded to nearest even into dtype.
+ * Each output is the exact dot product (float64 accumulation) rounded once, to nearest
+ * even, into dtype.
  * D in {64, 128}; d' in {16, 32}; 0 <= pos0, n_new >= 1, pos0 + n_new <= L_cap.
  */
 int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
@@ -144,8 +148,10 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
  *   idx     [B, Hkv, Lq, cap]        int32   (written) -- cap >= min(L, x + n_sink + n_window)
  *   bitmask [B, Hkv, Lq, ceil(L/32)] uint32  (written)
  *   count   [B, Hkv, Lq]             int32   (written)
- * 0 <= budget_num, 1 <= budget_den, n_sink >= 0, n_window >= 0.
- * workspace: radix histograms, the threshold state and per-block counts.
+ * 0 <= budget_num, 1 <= budget_den, n_sink >= 0, n_window >= 0.  Rows of a causal or
+ * multi-row (Lq > 1) call hold at most 65536 tokens; single-row decode calls up to 2^23.
+ * workspace: none up to 65536 tokens; beyond, radix histograms, candidate keys, per-chunk
+ * counts and offsets (about 8 bytes per token per row).
  */
 int butler_select_topk(void* stream, const float* scores, int budget_num, int budget_den,
                        int n_sink, int n_window, int32_t* idx, uint32_t* bitmask,

@@ -102,21 +102,28 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-# Workspaces: one zero-initialised buffer per (entry point, device), grown on demand.
-# The library leaves the counters inside a workspace zero after every call, so a buffer
-# can be reused call after call on one stream.
-_WS: Dict[Tuple[str, int], torch.Tensor] = {}
+# Workspaces: one zero-initialised buffer per (entry point, device, call shape).  The
+# library leaves the accumulators inside a workspace zero after every call, so a buffer is
+# reused by every later call of the same shape on one stream; a call of another shape may
+# lay the workspace out differently and gets its own buffer.
+_WS: Dict[tuple, torch.Tensor] = {}
 
 
-def _workspace(name: str, nbytes: int, device: torch.device) -> Tuple[Optional[int], ctypes.c_size_t]:
+def _workspace(name: str, nbytes: int, device: torch.device, shape: tuple):
+    """(pointer, size cell) of the workspace to pass; (None, None) when none is needed."""
     if nbytes == 0:
-        return None, ctypes.c_size_t(0)
-    key = (name, device.index if device.index is not None else torch.cuda.current_device())
+        return None, None
+    key = (name, device.index if device.index is not None else torch.cuda.current_device(),
+           shape)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = buf
     return buf.data_ptr(), ctypes.c_size_t(buf.numel())
+
+
+def _byref(n):
+    return None if n is None else ctypes.byref(n)
 
 
 def workspace_bytes(query) -> int:
@@ -155,9 +162,9 @@ def butler_produce_queries(h: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
     dt = _dtype_code(h)
     args = (dt, _ptr(h), _ptr(w1), _ptr(w2), _ptr(q_imp), B, Lq, E, F, Hq, G, dp, ln_eps)
     need = workspace_bytes(lambda ws, n: lib.butler_produce_queries(_stream(stream), *args, ws, n))
-    ws, n = _workspace("produce", need, h.device)
+    ws, n = _workspace("produce", need, h.device, (B, Lq, E, F, Hq, G, dp))
     _check("butler_produce_queries",
-           lib.butler_produce_queries(_stream(stream), *args, ws, ctypes.byref(n)))
+           lib.butler_produce_queries(_stream(stream), *args, ws, _byref(n)))
 
 
 def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.Tensor, *,
@@ -181,8 +188,8 @@ def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.T
     args = (mode, _dtype_code(q), _ptr(q), _ptr(keys), _ptr(scores), B, Hq, Hkv, G, slot, Lq, L,
             L_cap, dk, q_pos0, int(causal), softmax_scale)
     need = workspace_bytes(lambda ws, n: lib.butler_score(_stream(stream), *args, ws, n))
-    ws, n = _workspace("score", need, q.device)
-    _check("butler_score", lib.butler_score(_stream(stream), *args, ws, ctypes.byref(n)))
+    ws, n = _workspace("score", need, q.device, tuple(args[5:]))
+    _check("butler_score", lib.butler_score(_stream(stream), *args, ws, _byref(n)))
 
 
 def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n_sink: int,
@@ -204,9 +211,9 @@ def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n
     args = (_ptr(scores), budget_num, budget_den, n_sink, n_window, _ptr(idx), _ptr(bitmask),
             _ptr(count), B, Hkv, Lq, L, cap, q_pos0, int(causal))
     need = workspace_bytes(lambda ws, n: lib.butler_select_topk(_stream(stream), *args, ws, n))
-    ws, n = _workspace("select", need, scores.device)
+    ws, n = _workspace("select", need, scores.device, (budget_num, budget_den, B, Hkv, Lq, L, cap, q_pos0, int(causal)))
     _check("butler_select_topk",
-           lib.butler_select_topk(_stream(stream), *args, ws, ctypes.byref(n)))
+           lib.butler_select_topk(_stream(stream), *args, ws, _byref(n)))
 
 
 def butler_sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -230,6 +237,6 @@ def butler_sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
             _ptr(bitmask), _ptr(out), B, Hq, Hkv, D, Lq, L, L_cap, cap, q_pos0, softmax_scale)
     need = workspace_bytes(
         lambda ws, n: lib.butler_sparse_decode_attn(_stream(stream), *args, ws, n))
-    ws, n = _workspace("attn", need, q.device)
+    ws, n = _workspace("attn", need, q.device, tuple(args[8:]))
     _check("butler_sparse_decode_attn",
-           lib.butler_sparse_decode_attn(_stream(stream), *args, ws, ctypes.byref(n)))
+           lib.butler_sparse_decode_attn(_stream(stream), *args, ws, _byref(n)))

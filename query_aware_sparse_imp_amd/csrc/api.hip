@@ -30,14 +30,15 @@ inline int finish(hipStream_t s, hipError_t e) {
   return BUTLER_OK;
 }
 
-// Two-phase workspace protocol.  Returns 1 when the caller only asked for the size
-// (and *rc holds the status to return), 0 when the call should proceed.
+// Two-phase workspace protocol.  workspace == NULL with ws_bytes != NULL is always a
+// size query: *ws_bytes = need, nothing is enqueued.  workspace == NULL with
+// ws_bytes == NULL is a call without workspace, allowed when need == 0.  Returns 1 when
+// the call must return *rc now, 0 when it should proceed.
 inline int workspace_phase(void* ws, size_t* ws_bytes, size_t need, int* rc) {
   if (ws == nullptr) {
+    if (ws_bytes != nullptr) { *ws_bytes = need; *rc = BUTLER_OK; return 1; }
     if (need == 0) return 0;
-    if (ws_bytes == nullptr) { *rc = BUTLER_ERR_INVALID_ARG; return 1; }
-    *ws_bytes = need;
-    *rc = BUTLER_OK;
+    *rc = BUTLER_ERR_WORKSPACE;
     return 1;
   }
   if (ws_bytes == nullptr || *ws_bytes < need) { *rc = BUTLER_ERR_WORKSPACE; return 1; }
@@ -144,6 +145,10 @@ int butler_select_topk(void* stream, const float* scores, int budget_num, int bu
     return BUTLER_ERR_INVALID_ARG;
   const long long rows = (long long)B * Hkv * Lq;
   if (rows > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
+  // one workgroup per row holds at most 64K keys; long rows use the chunked decode
+  // schedule (one query row per KV head, no causal mask), up to 8M tokens
+  if ((causal || Lq > 1) && L > 65536) return BUTLER_ERR_UNSUPPORTED;
+  if (L > 8388608) return BUTLER_ERR_UNSUPPORTED;
   if (idx) {
     const long long x = (long long)L * budget_num / budget_den;
     long long need_cap = x + n_sink + n_window;
@@ -151,7 +156,7 @@ int butler_select_topk(void* stream, const float* scores, int budget_num, int bu
     if (cap < need_cap) return BUTLER_ERR_INVALID_ARG;
   }
   int rc;
-  if (workspace_phase(workspace, ws_bytes, select_workspace((int)rows, L, Lq), &rc)) return rc;
+  if (workspace_phase(workspace, ws_bytes, select_workspace((int)rows, L, Lq, causal), &rc)) return rc;
   if (!scores || !count || (!idx && !bitmask)) return BUTLER_ERR_INVALID_ARG;
   if (!aligned16(scores)) return BUTLER_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
@@ -175,11 +180,11 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
   const long long rows = (long long)B * Hkv * Lq;
   if (use_idx) {
     if (cap <= 0 || !count) return BUTLER_ERR_INVALID_ARG;
-    if (rows > 65535) return BUTLER_ERR_UNSUPPORTED;
+    if (rows * ((cap + 255) / 256) > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
   } else {
     if (L > 16384 || rows > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
   }
-  const size_t need = use_idx ? attn_workspace(B, Hq, Hkv, D, Lq, L, cap) : 0;
+  const size_t need = use_idx ? attn_workspace(dtype, B, Hq, Hkv, D, Lq, L, cap) : 0;
   int rc;
   if (workspace_phase(workspace, ws_bytes, need, &rc)) return rc;
   if (!q || !k_cache || !v_cache || !out) return BUTLER_ERR_INVALID_ARG;

@@ -1,37 +1,46 @@
 // Attention over the selected tokens only (TokenButler model card, intro and Method:
 // the full KV cache is kept, each step attends to the selected subset).
 //
-// Decode (index lists): split-K flash decoding.  The selected list of one (b, KV
-// head, query row) is cut into slices of kTokensPerSplit positions, one workgroup per
-// slice.  Inside a workgroup D/8 lanes cover one 2*D-byte key row (16 bytes each), so
-// a wave gathers 64/(D/8) selected rows per load instruction, straight into VGPRs;
-// all R query heads of the GQA group are served by the same gathered rows.  Logits,
-// the online softmax (base 2) and the P.V accumulation run in float32.  Each slice
-// writes (max, sum, acc[D]) per head; the workgroup that finishes last (an atomic
-// ticket per row) merges the slices in slice order and writes the output, then resets
-// its ticket to zero for the next call.
+// Decode (index lists) -- split-K flash decoding.  The selected list of one (b, KV head,
+// query row) is cut into splits; a split is a 512-thread workgroup that takes 256 list
+// positions per round.  The split's indices are staged once in LDS; each wave owns 32
+// positions and D/8 lanes cover one key row (16 bytes each), so every lane issues the
+// loads of 8 rows' K and V slices back to back before any arithmetic -- 32 KiB of
+// gathers in flight per wave, straight into VGPRs.  All R query heads of the GQA group
+// use the same gathered rows.  Logits (DPP row reductions), the base-2 online softmax and
+// P.V run in float32.  A wave's lane groups merge by shuffles, the waves through LDS, and
+// each split writes (max, sum, acc[D]) per head.  A second kernel merges the splits of
+// every (row, head, 32-wide slice of D) in split order: its 256 threads load all the
+// partials of the slice at once (8 split groups x 32 columns), so the merge costs one
+// memory round trip.  (Workgroups do not hand work to each other inside a kernel: the
+// device-wide release that would need writes back the XCD's L2.)
 //
-// Prefill (bitmask rows): one workgroup per query row expands the row's bitmask into
-// an ascending LDS index list and runs the same gather loop over it.
+// Prefill (bitmask rows) -- one workgroup per query row walks the row's bitmask 2048
+// tokens at a time, compacts the set bits into an LDS index list and runs the same wave
+// routine over it.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace butler {
 namespace {
 
-constexpr int kAttnThreads = 256;
-constexpr int kTokensPerSplit = 256;
-constexpr int kAttnUnroll = 4;
-constexpr int kMaxBitmaskL = 16384;
+constexpr int kAttnThreads = 512;
+constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kRoundTokens = 256;     // list positions per workgroup round (32 per wave)
+constexpr int kMaxSplits = 512;          // splits per row (more -> several rounds per split)
+constexpr int kBmChunkWords = 64;     // bitmask words compacted per prefill round
 
 template <typename T, int D, int R>
 struct Geo {
-  static constexpr int EPL = Vec16<T>::N;   // elements per lane
-  static constexpr int LPR = D / EPL;       // lanes per key row
-  static constexpr int TPW = 64 / LPR;      // rows per wave step
+  static constexpr int EPL = Vec16<T>::N;          // elements per lane
+  static constexpr int LPR = D / EPL;              // lanes per key row
+  static constexpr int TPW = 64 / LPR;             // rows per wave step
+  static constexpr int STEPS = 32 / TPW;           // steps per wave per round
+  static constexpr int UB = STEPS < 8 ? STEPS : 8; // rows per lane group per batch
 };
 
-// Online-softmax state of R heads for this lane's slice of D.
 template <int R, int EPL>
 struct SoftState {
   float m[R], l[R], acc[R][EPL];
@@ -44,134 +53,151 @@ struct SoftState {
       for (int e = 0; e < EPL; ++e) acc[r][e] = 0.f;
     }
   }
-  // merge another state (m2, l2, a2) into this one
-  __device__ __forceinline__ void merge(int r, float m2, float l2, const float* a2) {
-    if (m2 == neg_inf()) return;
-    const float mn = fmaxf(m[r], m2);
-    const float a = (m[r] == neg_inf()) ? 0.f : fast_exp2(m[r] - mn);
-    const float b = fast_exp2(m2 - mn);
-    l[r] = l[r] * a + l2 * b;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[r][e] = acc[r][e] * a + a2[e] * b;
-    m[r] = mn;
-  }
 };
 
-// Processes list positions p = p0, p0 + stride, ... < p1 (this lane group's share).
-template <typename T, int D, int R, typename ListT>
-__device__ __forceinline__ void gather_attend(const T* __restrict__ kb, const T* __restrict__ vb,
-                                              ListT list, int L_cap, int p0, int p1, int stride,
-                                              const float (&qr)[R][Geo<T, D, R>::EPL],
-                                              SoftState<R, Geo<T, D, R>::EPL>& st) {
+// One batch: this lane group attends to rows toks[0..UB) (-1 = no row).
+template <typename T, int D, int R>
+__device__ __forceinline__ void attend_batch(const T* __restrict__ kb, const T* __restrict__ vb,
+                                             const int (&toks)[Geo<T, D, R>::UB],
+                                             const float (&qr)[R][Geo<T, D, R>::EPL],
+                                             SoftState<R, Geo<T, D, R>::EPL>& st) {
   using G = Geo<T, D, R>;
-  constexpr int EPL = G::EPL, LPR = G::LPR, U = kAttnUnroll;
-  for (int p = p0; p < p1; p += stride * U) {
-    float kv[U][EPL], vv[U][EPL];
-    bool ok[U];
+  constexpr int EPL = G::EPL, LPR = G::LPR, UB = G::UB;
+  Raw16 kr[UB], vr[UB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int pu = p + u * stride;
-      ok[u] = pu < p1;
-      if (ok[u]) {
-        // indices outside [0, L_cap) never leave the cache (they read row L_cap - 1)
-        const long long t = (long long)min((unsigned)list[pu], (unsigned)(L_cap - 1));
-        Vec16<T>::load(kb + t * D, kv[u]);
-        Vec16<T>::load(vb + t * D, vv[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) { kv[u][e] = 0.f; vv[u][e] = 0.f; }
-      }
+  for (int u = 0; u < UB; ++u) {
+    if (toks[u] >= 0) {
+      kr[u].load(kb + (long long)toks[u] * D);
+      vr[u].load(vb + (long long)toks[u] * D);
+    } else {
+      kr[u].v = make_uint4(0, 0, 0, 0);
+      vr[u].v = make_uint4(0, 0, 0, 0);
     }
+  }
+  float z[R][UB];
+#pragma unroll
+  for (int u = 0; u < UB; ++u) {
+    float kf[EPL];
+    unpack16<T>(kr[u], kf);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float z[U];
-      float mx = st.m[r];
+      float a = 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float a = 0.f;
+      for (int e = 0; e < EPL; ++e) a = fmaf(qr[r][e], kf[e], a);
+      a = group_sum<LPR>(a);
+      z[r][u] = (toks[u] >= 0) ? a : neg_inf();
+    }
+  }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) a = fmaf(qr[r][e], kv[u][e], a);
+  for (int r = 0; r < R; ++r) {
+    float mx = st.m[r];
 #pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) a += __shfl_xor(a, o, 64);
-        z[u] = ok[u] ? a : neg_inf();
-        mx = fmaxf(mx, z[u]);
-      }
-      const float alpha = (st.m[r] == neg_inf()) ? 0.f : fast_exp2(st.m[r] - mx);
-      st.l[r] *= alpha;
+    for (int u = 0; u < UB; ++u) mx = fmaxf(mx, z[r][u]);
+    if (mx == neg_inf()) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) st.acc[r][e] *= alpha;
+      for (int u = 0; u < UB; ++u) z[r][u] = 0.f;
+      continue;
+    }
+    const float alpha = (st.m[r] == neg_inf()) ? 0.f : fast_exp2(st.m[r] - mx);
+    float lsum = st.l[r] * alpha;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float pz = ok[u] ? fast_exp2(z[u] - mx) : 0.f;
-        st.l[r] += pz;
+    for (int e = 0; e < EPL; ++e) st.acc[r][e] *= alpha;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) st.acc[r][e] = fmaf(pz, vv[u][e], st.acc[r][e]);
-      }
-      st.m[r] = (mx == neg_inf()) ? st.m[r] : mx;
+    for (int u = 0; u < UB; ++u) {
+      const float p = (toks[u] >= 0) ? fast_exp2(z[r][u] - mx) : 0.f;
+      z[r][u] = p;
+      lsum += p;
+    }
+    st.l[r] = lsum;
+    st.m[r] = mx;
+  }
+#pragma unroll
+  for (int u = 0; u < UB; ++u) {
+    float vf[EPL];
+    unpack16<T>(vr[u], vf);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) st.acc[r][e] = fmaf(z[r][u], vf[e], st.acc[r][e]);
     }
   }
 }
 
-// Reduces the states of all lane groups of the block into LDS arrays
-// red_m/red_l [R], red_acc [R][D] (valid after return, all threads synced).
-template <typename T, int D, int R>
-__device__ __forceinline__ void block_reduce_state(SoftState<R, Geo<T, D, R>::EPL>& st,
-                                                   float* sm, float* sl, float* sacc,
-                                                   float* red_m, float* red_l,
-                                                   float* red_acc) {
+// lo <- merge(lo, hi) for one head
+template <int EPL>
+__device__ __forceinline__ void merge_pair(float& m, float& l, float* acc, float m2, float l2,
+                                           const float* a2) {
+  if (m2 == neg_inf()) return;
+  if (m == neg_inf()) {
+    m = m2; l = l2;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = a2[e];
+    return;
+  }
+  const float mn = fmaxf(m, m2);
+  const float fa = fast_exp2(m - mn), fb = fast_exp2(m2 - mn);
+  l = l * fa + l2 * fb;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * fa + a2[e] * fb;
+  m = mn;
+}
+
+// Merges the lane groups of each wave (fixed order, identical in both lanes of a pair),
+// then the waves through LDS.  On return, red_m/red_l [R] and red_acc [R*D] hold the
+// workgroup's state; all threads have synchronised.
+template <typename T, int D, int R, int NT = kAttnThreads>
+__device__ __forceinline__ void block_reduce(SoftState<R, Geo<T, D, R>::EPL>& st, float* s_m,
+                                             float* s_l, float* s_acc, float* red_m,
+                                             float* red_l, float* red_acc) {
   using G = Geo<T, D, R>;
   constexpr int EPL = G::EPL, LPR = G::LPR;
-  constexpr int NW = kAttnThreads / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int pe = lane % LPR;
-  // lane groups within the wave (same pe, different rows)
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int o = LPR; o < 64; o <<= 1) {
+    const bool low = (lane & o) == 0;
 #pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) {
+    for (int r = 0; r < R; ++r) {
       const float m2 = __shfl_xor(st.m[r], o, 64);
       const float l2 = __shfl_xor(st.l[r], o, 64);
       float a2[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(st.acc[r][e], o, 64);
-      // merge in a fixed order regardless of which lane holds which side
-      SoftState<1, EPL> lo, hi;
-      const bool mine_low = (lane & o) == 0;
-      lo.m[0] = mine_low ? st.m[r] : m2;  lo.l[0] = mine_low ? st.l[r] : l2;
-      hi.m[0] = mine_low ? m2 : st.m[r];  hi.l[0] = mine_low ? l2 : st.l[r];
+      if (low) {
+        merge_pair<EPL>(st.m[r], st.l[r], st.acc[r], m2, l2, a2);
+      } else {
+        float m = m2, l = l2, acc[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        lo.acc[0][e] = mine_low ? st.acc[r][e] : a2[e];
-        hi.acc[0][e] = mine_low ? a2[e] : st.acc[r][e];
+        for (int e = 0; e < EPL; ++e) acc[e] = a2[e];
+        merge_pair<EPL>(m, l, acc, st.m[r], st.l[r], st.acc[r]);
+        st.m[r] = m; st.l[r] = l;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) st.acc[r][e] = acc[e];
       }
-      lo.merge(0, hi.m[0], hi.l[0], hi.acc[0]);
-      st.m[r] = lo.m[0];
-      st.l[r] = lo.l[0];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) st.acc[r][e] = lo.acc[0][e];
     }
   }
   if (lane < LPR) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (pe == 0) { sm[wid * R + r] = st.m[r]; sl[wid * R + r] = st.l[r]; }
+      if (pe == 0) { s_m[wid * R + r] = st.m[r]; s_l[wid * R + r] = st.l[r]; }
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sacc[(wid * R + r) * D + pe * EPL + e] = st.acc[r][e];
+      for (int e = 0; e < EPL; ++e) s_acc[(wid * R + r) * D + pe * EPL + e] = st.acc[r][e];
     }
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < R * D; j += kAttnThreads) {
-    const int r = j / D, d = j % D;
+  constexpr int NWV = NT / 64;
+  for (int j = threadIdx.x; j < R * D; j += NT) {
+    const int r = j / D, d = j - r * D;
     float M = neg_inf();
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * R + r]);
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_m[w * R + r]);
     float lsum = 0.f, a = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = sm[w * R + r];
+    for (int w = 0; w < NWV; ++w) {
+      const float mw = s_m[w * R + r];
       const float f = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
-      lsum += sl[w * R + r] * f;
-      a += sacc[(w * R + r) * D + d] * f;
+      lsum += s_l[w * R + r] * f;
+      a += s_acc[(w * R + r) * D + d] * f;
     }
     red_acc[j] = a;
     if (d == 0) { red_m[r] = M; red_l[r] = lsum; }
@@ -180,83 +206,341 @@ __device__ __forceinline__ void block_reduce_state(SoftState<R, Geo<T, D, R>::EP
 }
 
 template <typename T, int D, int R>
-__device__ __forceinline__ void load_q(const T* q, long long qoff_head0, long long head_stride,
+__device__ __forceinline__ void load_q(const T* q, long long head0, long long head_stride,
                                        int pe, float scale_log2,
                                        float (&qr)[R][Geo<T, D, R>::EPL]) {
   constexpr int EPL = Geo<T, D, R>::EPL;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float tmp[EPL];
-    Vec16<T>::load(q + qoff_head0 + r * head_stride + pe * EPL, tmp);
+    Vec16<T>::load(q + head0 + r * head_stride + pe * EPL, tmp);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qr[r][e] = tmp[e] * scale_log2;
+  }
+}
+
+// Runs this wave's share of one round: LDS list positions [wid*32, wid*32 + 32).
+template <typename T, int D, int R>
+__device__ __forceinline__ void wave_round(const T* kb, const T* vb, const int* s_list,
+                                           const float (&qr)[R][Geo<T, D, R>::EPL],
+                                           SoftState<R, Geo<T, D, R>::EPL>& st) {
+  using G = Geo<T, D, R>;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int sub = lane / G::LPR;
+#pragma unroll
+  for (int s0 = 0; s0 < G::STEPS; s0 += G::UB) {
+    int toks[G::UB];
+#pragma unroll
+    for (int u = 0; u < G::UB; ++u) toks[u] = s_list[wid * 32 + (s0 + u) * G::TPW + sub];
+    attend_batch<T, D, R>(kb, vb, toks, qr, st);
   }
 }
 
 template <typename T, int D, int R>
 __global__ __launch_bounds__(kAttnThreads) void attn_idx_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ out,
-    float* __restrict__ part, int* __restrict__ tickets, int Hq, int Hkv, int Lq, int L_cap,
-    int cap, float scale_log2, int nsplit) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+    float* __restrict__ part, int Hq, int Hkv, int Lq, int L_cap, int cap, float scale_log2,
+    int nsplit, int rounds, int rows) {
   using G = Geo<T, D, R>;
-  constexpr int EPL = G::EPL, LPR = G::LPR, TPW = G::TPW;
-  constexpr int NW = kAttnThreads / 64;
-  const int row = blockIdx.y, split = blockIdx.x;
+  constexpr int EPL = G::EPL;
+  constexpr int PS = D + 4;  // floats per (split, head) partial: m, l, pad, pad, acc[D]
+  const int row = blockIdx.x % rows, split = blockIdx.x / rows;
   const int bg = row / Lq, i = row - bg * Lq;
   const int b = bg / Hkv, g = bg - b * Hkv;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int sub = lane / LPR, pe = lane % LPR;
+  const int lane = threadIdx.x & 63;
+  const int pe = lane % G::LPR;
+
+  __shared__ int s_list[kRoundTokens];
+  __shared__ float s_m[kAttnWaves * R], s_l[kAttnWaves * R], red_m[R], red_l[R];
+  __shared__ float s_acc[kAttnWaves * R * D];
+  __shared__ float red_acc[R * D];
 
   float qr[R][EPL];
   load_q<T, D, R>(q, (((long long)b * Hq + g * R) * Lq + i) * D, (long long)Lq * D, pe,
                   scale_log2, qr);
   const int n = min(count[row], cap);
-  const int p_start = split * kTokensPerSplit;
-  const int p_end = min(p_start + kTokensPerSplit, n);
+  const int p_split = split * kRoundTokens * rounds;
   SoftState<R, EPL> st;
   st.init();
   const T* kb = k + (long long)bg * L_cap * D + pe * EPL;
   const T* vb = v + (long long)bg * L_cap * D + pe * EPL;
-  gather_attend<T, D, R>(kb, vb, idx + (long long)row * cap, L_cap, p_start + wid * TPW + sub, p_end,
-                         NW * TPW, qr, st);
-
-  __shared__ float sm[NW * R], sl[NW * R], sacc[NW * R * D];
-  __shared__ float red_m[R], red_l[R], red_acc[R * D];
-  block_reduce_state<T, D, R>(st, sm, sl, sacc, red_m, red_l, red_acc);
-
-  float* my = part + ((long long)row * nsplit + split) * R * (D + 2);
-  for (int j = threadIdx.x; j < R * D; j += kAttnThreads) my[(j / D) * (D + 2) + 2 + j % D] = red_acc[j];
-  if (threadIdx.x < R) {
-    my[threadIdx.x * (D + 2)] = red_m[threadIdx.x];
-    my[threadIdx.x * (D + 2) + 1] = red_l[threadIdx.x];
-  }
-  __threadfence();
-  __syncthreads();
-  __shared__ int sh_last;
-  if (threadIdx.x == 0) {
-    const int t = __hip_atomic_fetch_add(&tickets[row], 1, __ATOMIC_ACQ_REL,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = (t == nsplit - 1);
-  }
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
-  const float* base = part + (long long)row * nsplit * R * (D + 2);
-  for (int j = threadIdx.x; j < R * D; j += kAttnThreads) {
-    const int r = j / D, d = j % D;
-    float M = neg_inf();
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[((long long)s * R + r) * (D + 2)]);
-    float lsum = 0.f, a = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* ps = base + ((long long)s * R + r) * (D + 2);
-      const float f = (ps[0] == neg_inf()) ? 0.f : fast_exp2(ps[0] - M);
-      lsum += ps[1] * f;
-      a += ps[2 + d] * f;
+  const int32_t* irow = idx + (long long)row * cap;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int p0 = p_split + rd * kRoundTokens;
+    if (p0 >= n) break;
+    __syncthreads();
+    if (threadIdx.x < kRoundTokens) {
+      const int p = p0 + threadIdx.x;
+      // indices outside [0, L_cap) are clamped so a bad list never reads past the cache
+      s_list[threadIdx.x] = (p < n) ? (int)min((unsigned)irow[p], (unsigned)(L_cap - 1)) : -1;
     }
-    out[(((long long)b * Hq + g * R + r) * Lq + i) * D + d] = (lsum > 0.f) ? a / lsum : 0.f;
+    __syncthreads();
+    wave_round<T, D, R>(kb, vb, s_list, qr, st);
   }
-  if (threadIdx.x == 0) tickets[row] = 0;
+  block_reduce<T, D, R>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
+  float* my = part + ((long long)row * nsplit + split) * R * PS;
+  for (int j = threadIdx.x; j < R * D; j += kAttnThreads) my[(j / D) * PS + 4 + j % D] = red_acc[j];
+  if (threadIdx.x < R) {
+    my[threadIdx.x * PS] = red_m[threadIdx.x];
+    my[threadIdx.x * PS + 1] = red_l[threadIdx.x];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16, D = 128: logits on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// A wave takes 16 selected rows at a time.  v_mfma_f32_16x16x32_bf16 computes
+// S[t][h] = sum_d K[t][d] q[h][d] for the 16 rows (A operand: lane l holds 8 consecutive
+// d of row l%16, so 4 loads of 16 bytes per lane bring the tile's 16 key rows) and up to
+// 16 query-head columns (B operand: the group's R heads, zero beyond).  Four MFMAs cover
+// D = 128.  The result leaves the logits of rows 4q..4q+3 and head h in lane 16q + h:
+// every 16-lane row q runs its own online softmax for its 4 rows per tile, one lane per
+// head, and broadcasts the rescale factor and the 4 probabilities of each head across the
+// row with DPP row_newbcast.  P.V stays on the VALU in float32: lane p of row q owns
+// columns 8p..8p+7 of D and accumulates its row's 4 value rows (16-byte loads) for the R
+// heads.  Each wave takes 2 tiles per round with all 16 row loads in flight; rows and
+// waves merge with the same reduction as the VALU kernel.
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+template <int H>
+__device__ __forceinline__ float row_bcast(float x) { return dpp_f<0x150 + H>(x); }
+
+__device__ __forceinline__ float row_bcast_rt(float x, int h) {
+  switch (h) {
+    case 0: return row_bcast<0>(x);
+    case 1: return row_bcast<1>(x);
+    case 2: return row_bcast<2>(x);
+    case 3: return row_bcast<3>(x);
+    case 4: return row_bcast<4>(x);
+    case 5: return row_bcast<5>(x);
+    case 6: return row_bcast<6>(x);
+    default: return row_bcast<7>(x);
+  }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+constexpr int kMfThreads = 256;           // 4 waves
+constexpr int kMfWaves = kMfThreads / 64;
+constexpr int kMfRound = kMfWaves * 16;    // list positions per block round (a tile per wave)
+constexpr int kMfStage = 4096;             // list positions staged in LDS at a time
+constexpr int kMfTargetBlocks = 768;       // about what the GPU keeps resident (3 per CU)
+
+struct MfTile {
+  uint4 k[4], v[4];
+  int tv[4];
+};
+
+__device__ __forceinline__ void mf_load(MfTile& tl, const int* s_list, int base,
+                                        const bf16_t* kb, const bf16_t* vb, int quad, int pe) {
+  constexpr int D = 128;
+  const int tk = s_list[base + pe];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    tl.k[kk] = (tk >= 0) ? *reinterpret_cast<const uint4*>(kb + (long long)tk * D + kk * 32 + 8 * quad)
+                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    tl.tv[r] = s_list[base + 4 * quad + r];
+    tl.v[r] = (tl.tv[r] >= 0) ? *reinterpret_cast<const uint4*>(vb + (long long)tl.tv[r] * D + 8 * pe)
+                              : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void mf_compute(const MfTile& tl, const bf16x8_t (&qf)[4],
+                                           float scale_log2, float& m, float& l,
+                                           float (&acc)[R][8]) {
+  f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[kk]), qf[kk], c, 0, 0, 0);
+  // lane (quad, pe): logits of rows 4*quad + r for head pe
+  float z[4], mt = neg_inf();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    z[r] = (tl.tv[r] >= 0) ? c[r] * scale_log2 : neg_inf();
+    mt = fmaxf(mt, z[r]);
+  }
+  const float mn = fmaxf(m, mt);
+  const float alpha = (mn == neg_inf()) ? 1.f : fast_exp2(m - mn);
+  float pz[4], ps = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pz[r] = (tl.tv[r] >= 0) ? fast_exp2(z[r] - mn) : 0.f;
+    ps += pz[r];
+  }
+  l = l * alpha + ps;
+  m = mn;
+  float vv[4][8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    Raw16 rv;
+    rv.v = tl.v[r];
+    unpack16<bf16_t>(rv, vv[r]);
+  }
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    const float a = row_bcast_rt(alpha, h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] *= a;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = row_bcast_rt(pz[r], h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vv[r][e], acc[h][e]);
+    }
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+    float* __restrict__ part, int Hq, int Hkv, int Lq, int L_cap, int cap, float scale_log2,
+    int nsplit, int split_len, int rows) {
+  constexpr int D = 128;
+  constexpr int PS = D + 4;
+  static_assert(R <= 8, "at most 8 query heads per KV head");
+  const int row = blockIdx.x % rows, split = blockIdx.x / rows;
+  const int bg = row / Lq, i = row - bg * Lq;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int quad = lane >> 4, pe = lane & 15;
+
+  __shared__ int s_list[kMfStage];
+  __shared__ float s_m[kMfWaves * R], s_l[kMfWaves * R], red_m[R], red_l[R];
+  __shared__ float s_acc[kMfWaves * R * D];
+  __shared__ float red_acc[R * D];
+
+  // B operand: q[h = pe][kk*32 + 8*quad .. +8], zero for columns pe >= R
+  bf16x8_t qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (pe < R)
+      raw = *reinterpret_cast<const uint4*>(q + (((long long)b * Hq + g * R + pe) * Lq + i) * D +
+                                            kk * 32 + 8 * quad);
+    qf[kk] = as_bf16x8(raw);
+  }
+  const int n = min(count[row], cap);
+  const int p_begin = split * split_len;
+  const int p_end = min(p_begin + split_len, n);
+  const bf16_t* kb = k + (long long)bg * L_cap * D;
+  const bf16_t* vb = v + (long long)bg * L_cap * D;
+  const int32_t* irow = idx + (long long)row * cap;
+
+  float m = neg_inf(), l = 0.f;   // softmax state of head pe for this row's stream
+  float acc[R][8];
+#pragma unroll
+  for (int h = 0; h < R; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  for (int cs = p_begin; cs < p_end; cs += kMfStage) {
+    const int len = min(kMfStage, p_end - cs);
+    const int nr = (len + kMfRound - 1) / kMfRound;
+    __syncthreads();
+    for (int j = threadIdx.x; j < nr * kMfRound; j += kMfThreads)
+      // indices outside [0, L_cap) are clamped so a bad list never reads past the cache
+      s_list[j] = (j < len) ? (int)min((unsigned)irow[cs + j], (unsigned)(L_cap - 1)) : -1;
+    __syncthreads();
+    // one tile per wave per round; the next tile's rows are in flight during the compute
+    MfTile ta, tb;
+    mf_load(ta, s_list, wid * 16, kb, vb, quad, pe);
+    for (int r = 0; r < nr; r += 2) {
+      if (r + 1 < nr) mf_load(tb, s_list, (r + 1) * kMfRound + wid * 16, kb, vb, quad, pe);
+      mf_compute<R>(ta, qf, scale_log2, m, l, acc);
+      if (r + 2 < nr) mf_load(ta, s_list, (r + 2) * kMfRound + wid * 16, kb, vb, quad, pe);
+      if (r + 1 < nr) mf_compute<R>(tb, qf, scale_log2, m, l, acc);
+    }
+  }
+  // hand the per-row streams to the shared reduction: every lane of a row needs the
+  // (m, l) of every head, which live in lane h of the row
+  SoftState<R, 8> st;
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    st.m[h] = row_bcast_rt(m, h);
+    st.l[h] = row_bcast_rt(l, h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[h][e] = acc[h][e];
+  }
+  block_reduce<bf16_t, D, R, kMfThreads>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
+  float* my = part + ((long long)row * nsplit + split) * R * PS;
+  for (int j = threadIdx.x; j < R * D; j += kMfThreads) my[(j / D) * PS + 4 + j % D] = red_acc[j];
+  if (threadIdx.x < R) {
+    my[threadIdx.x * PS] = red_m[threadIdx.x];
+    my[threadIdx.x * PS + 1] = red_l[threadIdx.x];
+  }
+}
+
+// Merge of the splits: one workgroup per (row, head, 32 columns of D).  Thread
+// (group gs, column c) loads the column of splits gs, gs + 8, ... up front; the weights
+// exp2(m_s - M) and the normaliser come from one wave over the (m, l) pairs.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeGroups = kMergeThreads / 32;
+constexpr int kMergeMaxPer = kMaxSplits / kMergeGroups;
+
+template <int D, int R>
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
+    const float* __restrict__ part, float* __restrict__ out, int Hq, int Hkv, int Lq,
+    int nsplit) {
+  constexpr int PS = D + 4;
+  constexpr int NSL = D / 32;
+  const int slice = blockIdx.x % NSL;
+  const int r = (blockIdx.x / NSL) % R;
+  const int row = blockIdx.x / (NSL * R);
+  const int bg = row / Lq, i = row - bg * Lq;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int c = threadIdx.x & 31, gs = threadIdx.x >> 5;
+  const float* base = part + (long long)row * nsplit * R * PS + (long long)r * PS;
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_part[kMergeGroups][32];
+  __shared__ float s_inv;
+  float av[kMergeMaxPer];
+#pragma unroll
+  for (int j = 0; j < kMergeMaxPer; ++j) {
+    const int s = gs + j * kMergeGroups;
+    av[j] = (s < nsplit) ? base[(long long)s * R * PS + 4 + slice * 32 + c] : 0.f;
+  }
+  if (threadIdx.x < 64) {
+    // one wave: max of m, then weights and their l-weighted sum, in split order per lane
+    float M = neg_inf();
+    for (int s = threadIdx.x; s < nsplit; s += 64) M = fmaxf(M, base[(long long)s * R * PS]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float lsum = 0.f;
+    for (int s = threadIdx.x; s < nsplit; s += 64) {
+      const float m = base[(long long)s * R * PS];
+      const float wgt = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
+      s_w[s] = wgt;
+      lsum += wgt * base[(long long)s * R * PS + 1];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+    if (threadIdx.x == 0) s_inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+  }
+  __syncthreads();
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMergeMaxPer; ++j) {
+    const int s = gs + j * kMergeGroups;
+    if (s < nsplit) a = fmaf(s_w[s], av[j], a);
+  }
+  s_part[gs][c] = a;
+  __syncthreads();
+  if (gs == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMergeGroups; ++j) t += s_part[j][c];
+    out[(((long long)b * Hq + g * R + r) * Lq + i) * D + slice * 32 + c] = t * s_inv;
+  }
 }
 
 // Bitmask rows: one workgroup per (b, KV head, query row).
@@ -266,34 +550,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bitmask_kernel(
     const uint32_t* __restrict__ bitmask, float* __restrict__ out, int Hq, int Hkv, int Lq,
     int L, int L_cap, int q_pos0, float scale_log2) {
   using G = Geo<T, D, R>;
-  constexpr int EPL = G::EPL, LPR = G::LPR, TPW = G::TPW;
-  constexpr int NW = kAttnThreads / 64;
+  constexpr int EPL = G::EPL;
   const int row = blockIdx.x;
   const int bg = row / Lq, i = row - bg * Lq;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int sub = lane / LPR, pe = lane % LPR;
+  const int pe = lane % G::LPR;
   const int nwords = (L + 31) / 32;
   const int L_r = min(q_pos0 + i + 1, L);
   const int nwords_act = (L_r + 31) / 32;
-  __shared__ int list[kMaxBitmaskL];
-  __shared__ int tmp[NW];
-  const uint32_t* brow = bitmask + (long long)row * nwords;
-  int carry = 0;
-  for (int w0 = 0; w0 < nwords_act; w0 += kAttnThreads) {
-    const int w = w0 + threadIdx.x;
-    uint32_t bits = 0;
-    if (w < nwords_act) {
-      bits = brow[w];
-      const int lim = L_r - w * 32;  // tokens after the row's own position never count
-      if (lim < 32) bits &= (lim <= 0) ? 0u : ((1u << lim) - 1u);
-    }
-    int tot;
-    int pos = carry + block_exclusive_sum<kAttnThreads>(__popc(bits), tot, tmp);
-    for (uint32_t e = bits; e; e &= e - 1) list[pos++] = w * 32 + (__ffs(e) - 1);
-    carry += tot;
-  }
-  __syncthreads();
+  __shared__ int s_list[kBmChunkWords * 32 + kRoundTokens];
+  __shared__ int s_cnt;
+  __shared__ float s_m[kAttnWaves * R], s_l[kAttnWaves * R], red_m[R], red_l[R];
+  __shared__ float s_acc[kAttnWaves * R * D];
+  __shared__ float red_acc[R * D];
+
   float qr[R][EPL];
   load_q<T, D, R>(q, (((long long)b * Hq + g * R) * Lq + i) * D, (long long)Lq * D, pe,
                   scale_log2, qr);
@@ -301,31 +572,95 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bitmask_kernel(
   st.init();
   const T* kb = k + (long long)bg * L_cap * D + pe * EPL;
   const T* vb = v + (long long)bg * L_cap * D + pe * EPL;
-  gather_attend<T, D, R>(kb, vb, (const int*)list, L_cap, wid * TPW + sub, carry, NW * TPW, qr, st);
-  __shared__ float sm[NW * R], sl[NW * R], sacc[NW * R * D];
-  __shared__ float red_m[R], red_l[R], red_acc[R * D];
-  block_reduce_state<T, D, R>(st, sm, sl, sacc, red_m, red_l, red_acc);
+  const uint32_t* brow = bitmask + (long long)row * nwords;
+  for (int w0 = 0; w0 < nwords_act; w0 += kBmChunkWords) {
+    __syncthreads();
+    if (wid == 0) {
+      const int w = w0 + lane;
+      uint32_t bits = 0;
+      if (lane < kBmChunkWords && w < nwords_act) {
+        bits = brow[w];
+        const int lim = L_r - w * 32;  // tokens after the row's own position never count
+        if (lim < 32) bits &= (1u << lim) - 1u;
+      }
+      const int c = __popc(bits);
+      int pos = wave_inclusive_sum(c) - c;
+      for (uint32_t e = bits; e; e &= e - 1) s_list[pos++] = w * 32 + (__ffs(e) - 1);
+      if (lane == 63) s_cnt = pos;
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    for (int p0 = 0; p0 < cnt; p0 += kRoundTokens) {
+      // pad the tail of the list with "no row" entries
+      __syncthreads();
+      if (threadIdx.x < kRoundTokens && p0 + threadIdx.x >= cnt) s_list[p0 + threadIdx.x] = -1;
+      __syncthreads();
+      wave_round<T, D, R>(kb, vb, s_list + p0, qr, st);
+    }
+  }
+  block_reduce<T, D, R>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
   for (int j = threadIdx.x; j < R * D; j += kAttnThreads) {
-    const int r = j / D, d = j % D;
+    const int r = j / D, d = j - r * D;
     out[(((long long)b * Hq + g * R + r) * Lq + i) * D + d] =
         (red_l[r] > 0.f) ? red_acc[j] / red_l[r] : 0.f;
   }
 }
 
-int nsplit_for(int cap) { return (cap + kTokensPerSplit - 1) / kTokensPerSplit; }
+struct SplitPlan {
+  int nsplit, rounds;
+};
+
+// The matrix-core kernel sizes its splits so the grid is about what stays resident: a
+// split of split_len list positions (a multiple of the 64-position block round).
+struct MfPlan {
+  int nsplit, split_len;
+};
+
+MfPlan plan_mfma(long long rows, int cap) {
+  long long per_row = kMfTargetBlocks / rows;
+  if (per_row < 1) per_row = 1;
+  long long len = (cap + per_row - 1) / per_row;
+  len = (len + kMfRound - 1) / kMfRound * kMfRound;
+  if (len < kMfRound) len = kMfRound;
+  long long ns = (cap + len - 1) / len;
+  while (ns > kMaxSplits) {
+    len += kMfRound;
+    ns = (cap + len - 1) / len;
+  }
+  return {(int)ns, (int)len};
+}
+
+SplitPlan plan_for(int cap) {
+  const int raw = (cap + kRoundTokens - 1) / kRoundTokens;
+  const int rounds = (raw + kMaxSplits - 1) / kMaxSplits;
+  const int per = kRoundTokens * rounds;
+  return {(cap + per - 1) / per, rounds};
+}
 
 template <typename T, int D, int R>
 hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
                  const int32_t* idx, const int32_t* count, float* out, int B, int Hq, int Hkv,
                  int Lq, int L_cap, int cap, float scale, void* ws) {
-  const int nsplit = nsplit_for(cap);
   const long long rows = (long long)B * Hkv * Lq;
-  int* tickets = (int*)ws;
-  float* part = (float*)((char*)ws + ((rows * sizeof(int) + 255) / 256) * 256);
-  hipLaunchKernelGGL((attn_idx_kernel<T, D, R>), dim3(nsplit, (unsigned)rows),
-                     dim3(kAttnThreads), 0, s, (const T*)q, (const T*)k, (const T*)v, idx,
-                     count, out, part, tickets, Hq, Hkv, Lq, L_cap, cap,
-                     scale * 1.4426950408889634f, nsplit);
+  float* part = (float*)ws;
+  int nsplit;
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
+    const MfPlan sp = plan_mfma(rows, cap);
+    nsplit = sp.nsplit;
+    hipLaunchKernelGGL((attn_mfma_kernel<R>), dim3((unsigned)(sp.nsplit * rows)),
+                       dim3(kMfThreads), 0, s, (const bf16_t*)q, (const bf16_t*)k,
+                       (const bf16_t*)v, idx, count, part, Hq, Hkv, Lq, L_cap, cap,
+                       scale * 1.4426950408889634f, sp.nsplit, sp.split_len, (int)rows);
+  } else {
+    const SplitPlan sp = plan_for(cap);
+    nsplit = sp.nsplit;
+    hipLaunchKernelGGL((attn_idx_kernel<T, D, R>), dim3((unsigned)(sp.nsplit * rows)),
+                       dim3(kAttnThreads), 0, s, (const T*)q, (const T*)k, (const T*)v, idx,
+                       count, part, Hq, Hkv, Lq, L_cap, cap, scale * 1.4426950408889634f,
+                       sp.nsplit, sp.rounds, (int)rows);
+  }
+  hipLaunchKernelGGL((attn_merge_kernel<D, R>), dim3((unsigned)(rows * R * (D / 32))),
+                     dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
   return hipGetLastError();
 }
 
@@ -342,12 +677,12 @@ hipError_t bm_t(hipStream_t s, const void* q, const void* k, const void* v,
 
 }  // namespace
 
-size_t attn_workspace(int B, int Hq, int Hkv, int D, int Lq, int L, int cap) {
+size_t attn_workspace(int dtype, int B, int Hq, int Hkv, int D, int Lq, int L, int cap) {
   (void)L;
   const long long rows = (long long)B * Hkv * Lq;
   const int R = Hq / Hkv;
-  const size_t tick = ((rows * sizeof(int) + 255) / 256) * 256;
-  return tick + (size_t)rows * nsplit_for(cap) * R * (D + 2) * sizeof(float);
+  const int nsplit = (dtype == 1 && D == 128) ? plan_mfma(rows, cap).nsplit : plan_for(cap).nsplit;
+  return (size_t)rows * nsplit * R * (D + 4) * sizeof(float);
 }
 
 #define BUTLER_ATTN_DISPATCH(FN, ...)                                              \

@@ -18,6 +18,17 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// float64 -> bf16 rounded once to nearest even.  The double is first rounded to odd
+// into float32 (truncate, then set the last bit when anything was dropped); a
+// round-to-nearest-even from there to bf16 is then the correctly rounded result,
+// because float32 keeps at least two more bits than bf16.
+__device__ __forceinline__ uint16_t d2bf(double d) {
+  const float t = __double2float_rz(d);
+  uint32_t u = __float_as_uint(t);
+  if ((double)t != d && (u & 0x7fffffffu) < 0x7f800000u) u |= 1u;
+  return f2bf(__uint_as_float(u));
+}
+
 // Element loaders: 16 bytes -> 8 (bf16) or 4 (fp32) floats.
 template <typename T> struct Vec16;
 template <> struct Vec16<bf16_t> {
@@ -105,3 +116,48 @@ __device__ __forceinline__ float block_sum_f(float v, float* tmp) {
 }
 
 __device__ __forceinline__ float neg_inf() { return __uint_as_float(0xff800000u); }
+
+// Cross-lane moves inside a row of 16 lanes (DPP), as floats.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N consecutive lanes (N in 1..64, a power of two).  Every
+// step adds the same two partial sums in both lanes of a pair, so all lanes of a group
+// end with bitwise the same total.  Within 16 lanes the steps are DPP moves (quad
+// permutations, then the half-row and row mirrors); wider groups add LDS permutes.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp_f<0x141>(x);   // row_half_mirror
+  if constexpr (N >= 16) x += dpp_f<0x140>(x);  // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// 16 raw bytes of a row.
+struct Raw16 {
+  uint4 v;
+  __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const uint4*>(p); }
+};
+template <typename T> __device__ __forceinline__ void unpack16(const Raw16& r, float* out);
+template <> __device__ __forceinline__ void unpack16<bf16_t>(const Raw16& r, float* out) {
+  const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[2 * j] = __uint_as_float(w[j] << 16);
+    out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+template <> __device__ __forceinline__ void unpack16<float>(const Raw16& r, float* out) {
+  out[0] = __uint_as_float(r.v.x); out[1] = __uint_as_float(r.v.y);
+  out[2] = __uint_as_float(r.v.z); out[3] = __uint_as_float(r.v.w);
+}
+
+// Atomic ticket at agent scope: returns the previous value.
+__device__ __forceinline__ int ticket_take(int* t) {
+  return __hip_atomic_fetch_add(t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}

@@ -28,14 +28,14 @@ hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const 
                                  int D, float scale, void* ws);
 
 // ---- selection ------------------------------------------------------------
-size_t select_workspace(int rows, int L, int Lq);
+size_t select_workspace(int rows, int L, int Lq, int causal);
 hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
                          int n_window, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
                          void* ws);
 
 // ---- attention ------------------------------------------------------------
-size_t attn_workspace(int B, int Hq, int Hkv, int D, int Lq, int L, int cap);
+size_t attn_workspace(int dtype, int B, int Hq, int Hkv, int D, int Lq, int L, int cap);
 hipError_t launch_attn_idx(hipStream_t s, int dtype, const void* q, const void* k,
                            const void* v, const int32_t* idx, const int32_t* count,
                            float* out, int B, int Hq, int Hkv, int D, int Lq, int L_cap,

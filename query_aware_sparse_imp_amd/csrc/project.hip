@@ -4,19 +4,18 @@
 //
 // One thread per output element (row, j).  W_K (at most 128 x 32) lives in LDS as
 // float; a key row is read in 16-byte chunks that the DP threads of a row share
-// (same address -> one request).  bf16 rows accumulate in float32 (the products of
-// two bf16 values are exact in float32), float32 rows in float64; the result is
-// rounded once into the storage type.
+// (same address -> one request).  Products and sums run in float64, where every
+// partial sum of bf16 x bf16 products is exact, and the result is rounded once into
+// the storage type -- K_imp is the correctly rounded K . W_K.
 #include "common.h"
 #include "kernels.h"
 
 namespace butler {
 namespace {
 
-template <typename T> struct Acc { using type = float; };
-template <> struct Acc<float> { using type = double; };
+template <typename T> struct Acc { using type = double; };
 
-__device__ __forceinline__ void store_elem(bf16_t* p, float v) { *p = f2bf(v); }
+__device__ __forceinline__ void store_elem(bf16_t* p, double v) { *p = d2bf(v); }
 __device__ __forceinline__ void store_elem(float* p, double v) { *p = (float)v; }
 
 template <typename T, int D, int DP>
@@ -29,24 +28,36 @@ __global__ __launch_bounds__(256) void project_keys_kernel(const T* __restrict__
   constexpr int EPL = Vec16<T>::N;
   constexpr int RPB = 256 / DP;
   __shared__ float wsh[D * DP];
-  for (int i = threadIdx.x; i < D * DP; i += 256) wsh[i] = load_elem(w + i);
-  __syncthreads();
   const int j = threadIdx.x % DP;
   const int rsub = threadIdx.x / DP;
-  for (long long row = (long long)blockIdx.x * RPB + rsub; row < rows_total;
-       row += (long long)gridDim.x * RPB) {
-    const long long bg = row / n_new;
-    const long long t = pos0 + row % n_new;
+  const long long stride = (long long)gridDim.x * RPB;
+  long long row = (long long)blockIdx.x * RPB + rsub;
+  // the first key row is requested before W_K is staged, so both round trips overlap
+  float kv[D / EPL][EPL];
+  auto load_row = [&](long long rw) {
+    const long long bg = rw / n_new, t = pos0 + rw % n_new;
     const T* kr = k + (bg * L_cap + t) * D;
-    A acc = 0;
-#pragma unroll 4
-    for (int c = 0; c < D / EPL; ++c) {
-      float kv[EPL];
-      Vec16<T>::load(kr + c * EPL, kv);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc += (A)kv[e] * (A)wsh[(c * EPL + e) * DP + j];
+    for (int c = 0; c < D / EPL; ++c) Vec16<T>::load(kr + c * EPL, kv[c]);
+  };
+  if (row < rows_total) load_row(row);
+  for (int i = threadIdx.x; i < D * DP; i += 256) wsh[i] = load_elem(w + i);
+  __syncthreads();
+  while (row < rows_total) {
+    // four independent float64 sums (every partial sum is exact, so their order does not
+    // change the result)
+    A acc4[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < D / EPL; ++c) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        acc4[c & 3] = fma((A)kv[c][e], (A)wsh[(c * EPL + e) * DP + j], acc4[c & 3]);
     }
+    const A acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    const long long bg = row / n_new, t = pos0 + row % n_new;
     store_elem(kimp + (bg * L_cap + t) * DP + j, acc);
+    row += stride;
+    if (row < rows_total) load_row(row);
   }
 }
 

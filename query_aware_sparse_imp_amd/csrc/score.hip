@@ -20,7 +20,7 @@ namespace butler {
 namespace {
 
 constexpr int kRawThreads = 256;
-constexpr int kRawUnroll = 4;
+constexpr int kRawUnroll = 8;
 
 template <typename T, int DP>
 __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
@@ -33,27 +33,15 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   const int bg = blockIdx.z, i = blockIdx.y;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int R = Hq / Hkv;
-  __shared__ double qbar[DP];
-  if (threadIdx.x < DP) {
-    double a = 0.0;
-    for (int r = 0; r < R; ++r)
-      a += (double)load_elem(
-          q_imp + ((((size_t)b * Hq + g * R + r) * G + slot) * Lq + i) * DP + threadIdx.x);
-    qbar[threadIdx.x] = a;
-  }
-  __syncthreads();
   const int part = threadIdx.x % LPT, sub = threadIdx.x / LPT;
-  double qv[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) qv[e] = qbar[part * EPL + e];
   const int L_r = causal ? min(q_pos0 + i + 1, L) : L;
   const int t0 = blockIdx.x * tpb;
   const int t1 = min(t0 + tpb, L);
   const int tv = min(t1, L_r);
   const T* kb = kimp + (size_t)bg * L_cap * DP + part * EPL;
   float* srow = scores + ((size_t)bg * Lq + i) * L;
-  for (int t = t0 + sub; t < t1; t += TPI * kRawUnroll) {
-    float kv[kRawUnroll][EPL];
+  float kv[kRawUnroll][EPL];
+  auto load_batch = [&](int t) {
 #pragma unroll
     for (int u = 0; u < kRawUnroll; ++u) {
       const int tu = t + u * TPI;
@@ -64,6 +52,23 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
         for (int e = 0; e < EPL; ++e) kv[u][e] = 0.f;
       }
     }
+  };
+  // the first batch of K_imp rows is requested before the group query is summed
+  int t = t0 + sub;
+  if (t < t1) load_batch(t);
+  __shared__ double qbar[DP];
+  if (threadIdx.x < DP) {
+    double a = 0.0;
+    for (int r = 0; r < R; ++r)
+      a += (double)load_elem(
+          q_imp + ((((size_t)b * Hq + g * R + r) * G + slot) * Lq + i) * DP + threadIdx.x);
+    qbar[threadIdx.x] = a;
+  }
+  __syncthreads();
+  double qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = qbar[part * EPL + e];
+  while (t < t1) {
 #pragma unroll
     for (int u = 0; u < kRawUnroll; ++u) {
       double acc = 0.0;
@@ -74,6 +79,8 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
       const int tu = t + u * TPI;
       if (part == 0 && tu < t1) srow[tu] = (tu < L_r) ? (float)acc : neg_inf();
     }
+    t += TPI * kRawUnroll;
+    if (t < t1) load_batch(t);
   }
 }
 
@@ -198,7 +205,7 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
                  int causal) {
   constexpr int LPT = DP / Vec16<T>::N;
-  const int tpb = (kRawThreads / LPT) * kRawUnroll * 2;
+  const int tpb = (kRawThreads / LPT) * kRawUnroll;
   dim3 grid((L + tpb - 1) / tpb, Lq, B * Hkv);
   hipLaunchKernelGGL((score_raw_kernel<T, DP>), grid, dim3(kRawThreads), 0, s, (const T*)q_imp,
                      (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal,

@@ -1,39 +1,60 @@
 // Fixed-budget top-x + sink + window selection (TokenButler model card, Method and
 // Memory requirements).
 //
-// Scores become order-preserving uint32 keys (score_key).  The x-th largest key tau
-// is found exactly by a most-significant-digit radix select over digits of 11, 11 and
-// 10 bits: each pass histograms, in LDS, the next digit of the keys that share the
-// prefix found so far, and a block-wide scan from the top bin finds the bin that holds
-// the x-th largest key.  After the third pass tau is known together with the number of
-// keys equal to tau that the budget still takes; those are the lowest-index ones.
-// The emit pass walks the row in index order, 32 tokens (one bitmask word) per thread:
-// a block scan ranks the keys equal to tau, a second one places the selected tokens,
-// so the index list comes out ascending and the result does not depend on timing.
+// Scores become order-preserving uint32 keys (score_key: NaN ranks as -inf, -0 as +0).
+// The x-th largest key tau is found exactly by a most-significant-digit radix select
+// over digits of 11, 11 and 10 bits: a pass histograms the next digit of the keys that
+// share the prefix found so far, and a scan from the top bin finds the bin that holds the
+// x-th largest key.  After the third digit tau is exact, together with the number of keys
+// equal to tau that the budget still takes; the lowest-index ones are taken.  The emit
+// walks the row in index order, so the index list comes out ascending.
 //
-// One workgroup handles one row (a (b, KV head, query row) triple); rows are
-// independent, so a prefill chunk launches thousands of workgroups while a decode step
-// launches B * Hkv of them.
+// Workgroups never wait on one another inside a kernel (a device-wide release on this
+// GPU writes back the XCD's L2, far too slow for a per-workgroup handshake), so there are
+// two schedules:
+//
+// Rows of at most 64K tokens (decode rows up to 64K, every causal prefill row): one
+//   workgroup per row holds the row's keys in VGPRs (up to 64 per thread, strided so that
+//   a wave's ballot covers 64 consecutive tokens), builds the digit histograms in LDS, and
+//   emits through 64-token ballot words with two block-wide scans over the words (tie
+//   ranks, then output positions).  The first digit's histogram sees every key, and
+//   in one workgroup its LDS atomics pile onto the few hot bins; for decode rows longer
+//   than 4096 tokens it is built first by many workgroups (2048 tokens each, LDS then
+//   global atomics) and the row kernel starts from it (and clears it), so the row kernel
+//   only histograms the keys inside the chosen first-digit bin.
+//
+// Longer decode rows: five kernels over 2048-token chunks, no scratch shared inside a
+//   kernel except by atomics:
+//     1  histogram of key bits 31..21 (LDS, then global atomics)
+//     2  each workgroup derives the bin b1; histogram of bits 20..10 of the keys in b1
+//     3  each workgroup derives b1:b2; per-chunk count of the tokens surely selected (key
+//        above the 22-bit prefix, or a sink / window token); keys sharing the prefix are
+//        appended to a candidate list
+//     4  one workgroup per row resolves the last 10 bits, the tie quota and the
+//        lowest-index tie cut from the candidates, then every chunk's output offset and the
+//        row count; it clears the histograms and the candidate counter for the next call
+//     5  every chunk emits its bitmask words and its indices at its offset.
 #include "common.h"
 #include "kernels.h"
 
 namespace butler {
 namespace {
 
-constexpr int kSelThreads = 512;
+enum { kModeNormal = 0, kModeNone = 1, kModeAll = 2 };
 
-struct RadixState {
-  uint32_t tau;  // key of the x-th largest score
-  int need;      // keys equal to tau that belong to the top x (lowest indices first)
-};
+__device__ __forceinline__ int row_mode(int L_r, int num, int den, int& k) {
+  const long long x = (long long)L_r * num / den;
+  k = (int)min<long long>(x, (long long)L_r);
+  return k <= 0 ? kModeNone : (k >= L_r ? kModeAll : kModeNormal);
+}
 
-// Finds, among hist[0..nbins) scanned from the top bin down, the bin holding the
-// need-th largest key.  Returns (bin, need - keys in higher bins) via LDS.
+// Among hist[0..nbins), scanned from the top bin down, the bin that holds the need-th
+// largest key, and the rank left inside it.  All NT threads call it.
 template <int NT>
 __device__ void find_bin_from_top(const uint32_t* hist, int nbins, int need, int* tmp,
                                   int* out_bin, int* out_need) {
-  const int per = nbins / NT;  // bins per thread (nbins is a multiple of NT)
-  const int hi = nbins - threadIdx.x * per;  // this thread covers bins [hi-per, hi)
+  const int per = nbins / NT;
+  const int hi = nbins - threadIdx.x * per;  // this thread covers bins [hi - per, hi)
   int local = 0;
   for (int j = 1; j <= per; ++j) local += (int)hist[hi - j];
   int total;
@@ -52,44 +73,108 @@ __device__ void find_bin_from_top(const uint32_t* hist, int nbins, int need, int
   __syncthreads();
 }
 
+// Same from the bottom: the bin holding the need-th smallest value.
 template <int NT>
-__global__ __launch_bounds__(NT) void select_rows_kernel(
+__device__ void find_bin_from_bottom(const uint32_t* hist, int nbins, int need, int* tmp,
+                                     int* out_bin, int* out_need) {
+  const int per = nbins / NT;
+  const int lo = threadIdx.x * per;
+  int local = 0;
+  for (int j = 0; j < per; ++j) local += (int)hist[lo + j];
+  int total;
+  int below = block_exclusive_sum<NT>(local, total, tmp);
+  if (below < need && need <= below + local) {
+    for (int j = 0; j < per; ++j) {
+      const int c = (int)hist[lo + j];
+      if (below + c >= need) {
+        *out_bin = lo + j;
+        *out_need = need - below;
+        break;
+      }
+      below += c;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// one workgroup per row, keys in VGPRs
+// ---------------------------------------------------------------------------
+
+// In-place exclusive scan of a[0..n) (LDS) by NT threads; returns the total.
+template <int NT>
+__device__ __forceinline__ int block_scan_array(int* a, int n, int* tmp) {
+  const int per = (n + NT - 1) / NT;
+  const int lo = threadIdx.x * per;
+  int local = 0;
+  for (int j = 0; j < per; ++j)
+    if (lo + j < n) local += a[lo + j];
+  int total;
+  int run = block_exclusive_sum<NT>(local, total, tmp);
+  for (int j = 0; j < per; ++j) {
+    if (lo + j < n) {
+      const int v = a[lo + j];
+      a[lo + j] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
+// Thread tid owns tokens tid + NT*j (j < KPT): for a fixed j the 64 lanes of a wave hold
+// 64 consecutive tokens, so a ballot is one 64-token word of the row in index order
+// (word j*NW + wave).
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void select_row_kernel(
     const float* __restrict__ scores, int num, int den, int n_sink, int n_window,
     int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask, int32_t* __restrict__ count,
-    int Lq, int L, int cap, int q_pos0, int causal) {
-  const long long row = blockIdx.x + (long long)blockIdx.y * gridDim.x;
+    int Lq, int L, int cap, int q_pos0, int causal, uint32_t* __restrict__ ghist) {
+  constexpr int NW = NT / 64;
+  constexpr int MAXW = NT * KPT / 64;
+  const long long row = blockIdx.x;
   const int i = (int)(row % Lq);
   const int L_r = causal ? min(q_pos0 + i + 1, L) : L;
-  const long long x = (long long)L_r * num / den;
-  const int k = (int)min<long long>(x, (long long)L_r);
+  int k;
+  const int mode = row_mode(L_r, num, den, k);
   const float* s = scores + row * (long long)L;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
 
   __shared__ uint32_t hist[2048];
-  __shared__ int tmp[NT / 64];
+  __shared__ int tmp[NW];
   __shared__ int sh_bin, sh_need;
+  __shared__ int wtie[MAXW], wcnt[MAXW];
+  __shared__ uint64_t wsel[MAXW];
 
-  uint32_t tau;
-  int need;
-  if (k <= 0) {
-    tau = 0xffffffffu;  // no key exceeds or equals it (NaN keys never reach 0xffffffff)
-    need = 0;
-  } else if (k >= L_r) {
-    tau = 0u;           // every real key is above it
-    need = 0;
-  } else {
+  // all loads at once, from clamped addresses (no control flow around them)
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = score_key(s[min((int)threadIdx.x + NT * j, L_r - 1)]);
+  auto valid = [&](int j) { return (int)threadIdx.x + NT * j < L_r; };
+
+  uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;
+  int need = 0;
+  if (mode == kModeNormal) {
     uint32_t prefix = 0, pmask = 0;
     need = k;
     const int shifts[3] = {21, 10, 0};
     const int bins[3] = {2048, 2048, 1024};
+#pragma unroll
     for (int p = 0; p < 3; ++p) {
       const int sh = shifts[p], nb = bins[p];
-      for (int j = threadIdx.x; j < nb; j += NT) hist[j] = 0;
-      __syncthreads();
-      for (int t = threadIdx.x; t < L_r; t += NT) {
-        const uint32_t key = score_key(s[t]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
+      if (p == 0 && ghist) {
+        uint32_t* gh = ghist + row * 2048;
+        for (int j = threadIdx.x; j < 2048; j += NT) { hist[j] = gh[j]; gh[j] = 0u; }
+        __syncthreads();
+      } else {
+        for (int j = threadIdx.x; j < nb; j += NT) hist[j] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          if (valid(j) && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> sh) & (nb - 1)], 1u);
+        __syncthreads();
       }
-      __syncthreads();
       find_bin_from_top<NT>(hist, nb, need, tmp, &sh_bin, &sh_need);
       prefix |= (uint32_t)sh_bin << sh;
       pmask |= (uint32_t)(nb - 1) << sh;
@@ -99,59 +184,392 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(
     tau = prefix;
   }
 
-  // ---- emit in index order, one 32-token word per thread per step ----------
-  const int nwords_row = (L + 31) / 32;
-  const int nwords_act = (L_r + 31) / 32;
+  // ---- emit in index order -------------------------------------------------------
   const int w_lo = max(0, L_r - n_window);
-  int32_t* irow = idx ? idx + row * (long long)cap : nullptr;
-  uint32_t* brow = bitmask ? bitmask + row * (long long)nwords_row : nullptr;
-  int tie_carry = 0, pos_carry = 0;
-  for (int w0 = 0; w0 < nwords_row; w0 += NT) {
-    const int w = w0 + threadIdx.x;
-    uint32_t gt = 0, eq = 0, forced = 0;
-    if (w < nwords_act) {
-      const int tb = w * 32;
-      const int n = min(32, L_r - tb);
-      for (int j = 0; j < n; ++j) {
-        const int t = tb + j;
-        const uint32_t key = score_key(s[t]);
-        gt |= (uint32_t)(key > tau) << j;
-        eq |= (uint32_t)(key == tau) << j;
-        forced |= (uint32_t)(t < n_sink || t >= w_lo) << j;
-      }
-    }
-    int ties_total;
-    const int tie_before = block_exclusive_sum<NT>(__popc(eq), ties_total, tmp);
-    uint32_t take = 0;
-    int rank = tie_carry + tie_before;
-    for (uint32_t e = eq; e; e &= e - 1) {
-      const int j = __ffs(e) - 1;
-      if (rank < need) take |= 1u << j;
-      ++rank;
-    }
-    const uint32_t sel = gt | take | forced;
-    int sel_total;
-    const int pos_before = block_exclusive_sum<NT>(__popc(sel), sel_total, tmp);
-    if (w < nwords_row) {
-      if (brow) brow[w] = sel;
-      if (irow) {
-        int pos = pos_carry + pos_before;
-        for (uint32_t e = sel; e; e &= e - 1) {
-          if (pos < cap) irow[pos] = w * 32 + (__ffs(e) - 1);
-          ++pos;
-        }
-      }
-    }
-    tie_carry += ties_total;
-    pos_carry += sel_total;
+  // rank of every key equal to tau among the row's equal keys, in index order
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t e = __ballot(valid(j) && key[j] == tau);
+    if (lane == 0) wtie[j * NW + wid] = __popcll(e);
   }
-  if (threadIdx.x == 0) count[row] = pos_carry;
+  __syncthreads();
+  block_scan_array<NT>(wtie, MAXW, tmp);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int t = (int)threadIdx.x + NT * j;
+    const bool v = valid(j);
+    const bool eq = v && key[j] == tau;
+    const uint64_t e = __ballot(eq);
+    const int rank = wtie[j * NW + wid] + __popcll(e & lt);
+    bool sel = v && (t < n_sink || t >= w_lo || key[j] > tau);
+    if (eq) sel = sel || mode == kModeAll || (mode == kModeNormal && rank < need);
+    const uint64_t b = __ballot(sel);
+    if (lane == 0) { wsel[j * NW + wid] = b; wcnt[j * NW + wid] = __popcll(b); }
+  }
+  __syncthreads();
+  const int total = block_scan_array<NT>(wcnt, MAXW, tmp);
+  if (idx) {
+    int32_t* irow = idx + row * (long long)cap;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int w = j * NW + wid;
+      const uint64_t b = wsel[w];
+      if ((b >> lane) & 1ull) {
+        const int pos = wcnt[w] + __popcll(b & lt);
+        if (pos < cap) irow[pos] = (int)threadIdx.x + NT * j;
+      }
+    }
+  }
+  if (bitmask) {
+    const int nwords = (L + 31) / 32;
+    uint32_t* brow = bitmask + row * (long long)nwords;
+    for (int j = threadIdx.x; j < nwords; j += NT) {
+      const int w = j >> 1;
+      brow[j] = (w < MAXW) ? (uint32_t)(wsel[w] >> (32 * (j & 1))) : 0u;
+    }
+  }
+  if (threadIdx.x == 0) count[row] = total;
+}
+
+// ---------------------------------------------------------------------------
+// long decode rows: five kernels over 2048-token chunks
+// ---------------------------------------------------------------------------
+
+constexpr int kMbThreads = 256;
+constexpr int kMbChunk = 2048;           // tokens per workgroup, 8 per thread
+constexpr int kMbMaxChunks = 4096;       // rows of up to 8M tokens
+constexpr int kRowMaxL = 65536;          // longest row of the one-workgroup schedule
+
+struct RowState {
+  uint32_t tau;
+  int tie_cut;
+};
+
+struct MbWs {
+  uint32_t* hist1;   // [rows][2048]   zero between calls
+  uint32_t* hist2;   // [rows][2048]   zero between calls
+  uint32_t* ccount;  // [rows]         zero between calls
+  RowState* state;   // [rows]
+  int* defcnt;       // [rows][nchunk]
+  int* offs;         // [rows][nchunk]
+  uint2* cand;       // [rows][L]  (key, index | sink/window flag << 31)
+};
+
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t mb_bytes(long long rows, int L) {
+  const long long nchunk = (L + kMbChunk - 1) / kMbChunk;
+  return 2 * al256(rows * 2048 * 4) + al256(rows * 4) + al256(rows * sizeof(RowState)) +
+         2 * al256(rows * nchunk * 4) + al256((size_t)rows * L * sizeof(uint2));
+}
+
+MbWs carve(void* ws, long long rows, int L) {
+  const long long nchunk = (L + kMbChunk - 1) / kMbChunk;
+  char* p = (char*)ws;
+  MbWs w;
+  w.hist1 = (uint32_t*)p;     p += al256(rows * 2048 * sizeof(uint32_t));
+  w.hist2 = (uint32_t*)p;     p += al256(rows * 2048 * sizeof(uint32_t));
+  w.ccount = (uint32_t*)p;    p += al256(rows * sizeof(uint32_t));
+  w.state = (RowState*)p;     p += al256(rows * sizeof(RowState));
+  w.defcnt = (int*)p;         p += al256(rows * nchunk * sizeof(int));
+  w.offs = (int*)p;           p += al256(rows * nchunk * sizeof(int));
+  w.cand = (uint2*)p;
+  return w;
+}
+
+// The 8 keys of tokens t0 .. t0+7; returns how many exist (t < L).
+__device__ __forceinline__ int load_keys8(const float* s, int t0, int L, uint32_t (&key)[8]) {
+  const int nv = max(0, min(8, L - t0));
+  if (nv == 8 && ((((uintptr_t)(s + t0)) & 15u) == 0)) {
+    const float4 a = *reinterpret_cast<const float4*>(s + t0);
+    const float4 b = *reinterpret_cast<const float4*>(s + t0 + 4);
+    key[0] = score_key(a.x); key[1] = score_key(a.y); key[2] = score_key(a.z);
+    key[3] = score_key(a.w); key[4] = score_key(b.x); key[5] = score_key(b.y);
+    key[6] = score_key(b.z); key[7] = score_key(b.w);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) key[j] = (j < nv) ? score_key(s[t0 + j]) : 0u;
+  }
+  return nv;
+}
+
+// Derives (bin, rank left) from a row's global histogram; all threads call it.
+__device__ __forceinline__ void bin_from_global(const uint32_t* gh, int need, uint32_t* h,
+                                                int* tmp, int* sh_bin, int* sh_need) {
+  for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = gh[j];
+  __syncthreads();
+  find_bin_from_top<kMbThreads>(h, 2048, need, tmp, sh_bin, sh_need);
+}
+
+__device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* gh) {
+  for (int j = threadIdx.x; j < 2048; j += kMbThreads)
+    if (h[j]) atomicAdd(&gh[j], h[j]);
+}
+
+__global__ __launch_bounds__(kMbThreads) void mb_hist1_kernel(const float* __restrict__ scores,
+                                                              int num, int den, int L, int rows,
+                                                              MbWs w) {
+  const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
+  int k;
+  if (row_mode(L, num, den, k) != kModeNormal) return;
+  __shared__ uint32_t h[2048];
+  for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
+  __syncthreads();
+  uint32_t key[8];
+  const int nv = load_keys8(scores + (long long)row * L, chunk * kMbChunk + threadIdx.x * 8, L, key);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < nv) atomicAdd(&h[key[j] >> 21], 1u);
+  __syncthreads();
+  flush_hist(h, w.hist1 + (long long)row * 2048);
+}
+
+__global__ __launch_bounds__(kMbThreads) void mb_hist2_kernel(const float* __restrict__ scores,
+                                                              int num, int den, int L, int rows,
+                                                              MbWs w) {
+  const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
+  int k;
+  if (row_mode(L, num, den, k) != kModeNormal) return;
+  __shared__ uint32_t h[2048];
+  __shared__ int tmp[kMbThreads / 64];
+  __shared__ int sh_bin, sh_need;
+  uint32_t key[8];
+  const int nv = load_keys8(scores + (long long)row * L, chunk * kMbChunk + threadIdx.x * 8, L, key);
+  bin_from_global(w.hist1 + (long long)row * 2048, k, h, tmp, &sh_bin, &sh_need);
+  const uint32_t b1 = (uint32_t)sh_bin;
+  for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < nv && (key[j] >> 21) == b1) atomicAdd(&h[(key[j] >> 10) & 2047u], 1u);
+  __syncthreads();
+  flush_hist(h, w.hist2 + (long long)row * 2048);
+}
+
+__global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __restrict__ scores,
+                                                             int num, int den, int n_sink,
+                                                             int n_window, int L, int rows,
+                                                             MbWs w) {
+  const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
+  const int nchunk = gridDim.x / rows;
+  int k;
+  const int mode = row_mode(L, num, den, k);
+  __shared__ uint32_t h[2048];
+  __shared__ int tmp[kMbThreads / 64];
+  __shared__ int sh_bin, sh_need, sh_base;
+  const int t0 = chunk * kMbChunk + threadIdx.x * 8;
+  uint32_t key[8];
+  const int nv = load_keys8(scores + (long long)row * L, t0, L, key);
+  uint32_t hi22 = 0;
+  if (mode == kModeNormal) {
+    bin_from_global(w.hist1 + (long long)row * 2048, k, h, tmp, &sh_bin, &sh_need);
+    const uint32_t b1 = (uint32_t)sh_bin;
+    const int need1 = sh_need;
+    __syncthreads();
+    bin_from_global(w.hist2 + (long long)row * 2048, need1, h, tmp, &sh_bin, &sh_need);
+    hi22 = (b1 << 11) | (uint32_t)sh_bin;
+  }
+  const int w_lo = max(0, L - n_window);
+  int ndef = 0, ncand = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= nv) continue;
+    const int t = t0 + j;
+    const bool forced = t < n_sink || t >= w_lo;
+    if (mode == kModeNormal) {
+      const uint32_t top = key[j] >> 10;
+      ndef += (forced || top > hi22) ? 1 : 0;
+      ncand += (top == hi22) ? 1 : 0;
+    } else {
+      ndef += (forced || mode == kModeAll) ? 1 : 0;
+    }
+  }
+  int tot_def, tot_cand;
+  block_exclusive_sum<kMbThreads>(ndef, tot_def, tmp);
+  const int cpos = block_exclusive_sum<kMbThreads>(ncand, tot_cand, tmp);
+  if (threadIdx.x == 0) {
+    w.defcnt[(long long)row * nchunk + chunk] = tot_def;
+    sh_base = tot_cand ? (int)atomicAdd(&w.ccount[row], (uint32_t)tot_cand) : 0;
+  }
+  __syncthreads();
+  if (ncand) {
+    uint2* crow = w.cand + (long long)row * L;
+    int pos = sh_base + cpos;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= nv || (key[j] >> 10) != hi22) continue;
+      const int t = t0 + j;
+      const uint32_t flag = (t < n_sink || t >= w_lo) ? 0x80000000u : 0u;
+      crow[pos++] = make_uint2(key[j], (uint32_t)t | flag);
+    }
+  }
+}
+
+constexpr int kResThreads = 1024;
+
+__global__ __launch_bounds__(kResThreads) void mb_resolve_kernel(int num, int den, int L,
+                                                                 int nchunk,
+                                                                 int32_t* __restrict__ count,
+                                                                 MbWs w) {
+  const int row = blockIdx.x;
+  int k;
+  const int mode = row_mode(L, num, den, k);
+  __shared__ uint32_t h[2048];
+  __shared__ int cnt[kMbMaxChunks];
+  __shared__ int tmp[kResThreads / 64];
+  __shared__ int sh_bin, sh_need, sh_ties;
+  uint32_t* gh1 = w.hist1 + (long long)row * 2048;
+  uint32_t* gh2 = w.hist2 + (long long)row * 2048;
+  const int n = (int)w.ccount[row];
+  const uint2* crow = w.cand + (long long)row * L;
+  uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;
+  int tie_cut = -1;
+  if (mode == kModeNormal) {
+    for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = gh1[j];
+    __syncthreads();
+    find_bin_from_top<kResThreads>(h, 2048, k, tmp, &sh_bin, &sh_need);
+    const uint32_t b1 = (uint32_t)sh_bin;
+    const int need1 = sh_need;
+    __syncthreads();
+    for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = gh2[j];
+    __syncthreads();
+    find_bin_from_top<kResThreads>(h, 2048, need1, tmp, &sh_bin, &sh_need);
+    const uint32_t hi22 = (b1 << 11) | (uint32_t)sh_bin;
+    const int need2 = sh_need;
+    __syncthreads();
+    // last 10 bits
+    for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = 0u;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n; j += kResThreads) atomicAdd(&h[crow[j].x & 1023u], 1u);
+    __syncthreads();
+    find_bin_from_top<kResThreads>(h, 1024, need2, tmp, &sh_bin, &sh_need);
+    tau = (hi22 << 10) | (uint32_t)sh_bin;
+    const int need3 = sh_need;
+    if (threadIdx.x == 0) sh_ties = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int j = threadIdx.x; j < n; j += kResThreads) mine += (crow[j].x == tau) ? 1 : 0;
+    if (mine) atomicAdd(&sh_ties, mine);
+    __syncthreads();
+    if (need3 >= sh_ties) {
+      tie_cut = 0x7fffffff;
+    } else {
+      // the need3-th smallest index among the keys equal to tau: bits 30..20, 19..10, 9..0
+      uint32_t pre = 0u, pmask = 0u;
+      int need = need3;
+      const int shifts[3] = {20, 10, 0};
+      const uint32_t widths[3] = {2048u, 1024u, 1024u};
+      for (int p = 0; p < 3; ++p) {
+        __syncthreads();
+        for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = 0u;
+        __syncthreads();
+        for (int j = threadIdx.x; j < n; j += kResThreads) {
+          const uint2 c = crow[j];
+          const uint32_t t = c.y & 0x7fffffffu;
+          if (c.x == tau && (t & pmask) == pre) atomicAdd(&h[(t >> shifts[p]) & (widths[p] - 1u)], 1u);
+        }
+        __syncthreads();
+        find_bin_from_bottom<kResThreads>(h, 2048, need, tmp, &sh_bin, &sh_need);
+        pre |= (uint32_t)sh_bin << shifts[p];
+        pmask |= (widths[p] - 1u) << shifts[p];
+        need = sh_need;
+      }
+      tie_cut = (int)pre;
+    }
+  }
+  // per-chunk selected counts -> offsets, row count
+  for (int c = threadIdx.x; c < nchunk; c += kResThreads) cnt[c] = w.defcnt[(long long)row * nchunk + c];
+  __syncthreads();
+  if (mode == kModeNormal) {
+    for (int j = threadIdx.x; j < n; j += kResThreads) {
+      const uint2 c = crow[j];
+      if (c.y & 0x80000000u) continue;  // sink / window tokens are already counted
+      const int t = (int)c.y;
+      if (c.x > tau || (c.x == tau && t <= tie_cut)) atomicAdd(&cnt[t / kMbChunk], 1);
+    }
+  }
+  __syncthreads();
+  int carry = 0;
+  for (int c0 = 0; c0 < nchunk; c0 += kResThreads) {
+    const int c = c0 + threadIdx.x;
+    const int v = (c < nchunk) ? cnt[c] : 0;
+    int tot;
+    const int ex = block_exclusive_sum<kResThreads>(v, tot, tmp);
+    if (c < nchunk) w.offs[(long long)row * nchunk + c] = carry + ex;
+    carry += tot;
+  }
+  // clear the accumulators for the next call
+  for (int j = threadIdx.x; j < 2048; j += kResThreads) { gh1[j] = 0u; gh2[j] = 0u; }
+  if (threadIdx.x == 0) {
+    count[row] = carry;
+    w.state[row].tau = tau;
+    w.state[row].tie_cut = tie_cut;
+    w.ccount[row] = 0u;
+  }
+}
+
+__global__ __launch_bounds__(kMbThreads) void mb_emit_kernel(
+    const float* __restrict__ scores, int num, int den, int n_sink, int n_window, int L,
+    int rows, int cap, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask, MbWs w) {
+  const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
+  const int nchunk = gridDim.x / rows;
+  int k;
+  const int mode = row_mode(L, num, den, k);
+  __shared__ int tmp[kMbThreads / 64];
+  __shared__ uint8_t bytes[kMbThreads];
+  const uint32_t tau = w.state[row].tau;
+  const int tie_cut = w.state[row].tie_cut;
+  const int w_lo = max(0, L - n_window);
+  const int t0 = chunk * kMbChunk + threadIdx.x * 8;
+  uint32_t key[8];
+  const int nv = load_keys8(scores + (long long)row * L, t0, L, key);
+  uint32_t sel = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= nv) continue;
+    const int t = t0 + j;
+    bool s = t < n_sink || t >= w_lo;
+    if (mode == kModeAll) s = true;
+    else if (mode == kModeNormal) s = s || key[j] > tau || (key[j] == tau && t <= tie_cut);
+    sel |= (uint32_t)s << j;
+  }
+  int tot;
+  const int ex = block_exclusive_sum<kMbThreads>(__popc(sel), tot, tmp);
+  if (idx) {
+    int pos = w.offs[(long long)row * nchunk + chunk] + ex;
+    int32_t* irow = idx + (long long)row * cap;
+    for (uint32_t e = sel; e; e &= e - 1) {
+      if (pos < cap) irow[pos] = t0 + (__ffs(e) - 1);
+      ++pos;
+    }
+  }
+  if (bitmask) {
+    bytes[threadIdx.x] = (uint8_t)sel;
+    __syncthreads();
+    const int nwords = (L + 31) / 32;
+    const int wd = chunk * (kMbChunk / 32) + threadIdx.x;
+    if (threadIdx.x < kMbChunk / 32 && wd < nwords) {
+      const int b0 = threadIdx.x * 4;
+      bitmask[(long long)row * nwords + wd] = (uint32_t)bytes[b0] | ((uint32_t)bytes[b0 + 1] << 8) |
+                                              ((uint32_t)bytes[b0 + 2] << 16) |
+                                              ((uint32_t)bytes[b0 + 3] << 24);
+    }
+  }
+}
+
+bool use_chunked(int Lq, int L, int causal) {
+  return !causal && Lq == 1 && L > kRowMaxL;
+}
+
+bool use_ghist(int Lq, int L, int causal) {
+  return !causal && Lq == 1 && L > 4096 && L <= kRowMaxL;
 }
 
 }  // namespace
 
-size_t select_workspace(int rows, int L, int Lq) {
-  (void)rows; (void)L; (void)Lq;
+size_t select_workspace(int rows, int L, int Lq, int causal) {
+  if (use_chunked(Lq, L, causal)) return mb_bytes(rows, L);
+  if (use_ghist(Lq, L, causal)) return al256((size_t)rows * 2048 * sizeof(uint32_t));
   return 0;
 }
 
@@ -159,18 +577,51 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
                          int n_window, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
                          void* ws) {
-  (void)ws;
   const long long rows = (long long)B * Hkv * Lq;
-  unsigned gx = (unsigned)(rows < 65536 ? rows : 65536);
-  unsigned gy = (unsigned)((rows + gx - 1) / gx);
-  if ((long long)gx * gy != rows) {
-    // rows is not a multiple of 65536: fall back to a 1-D grid when it fits
-    gx = (unsigned)rows;
-    gy = 1;
+  if (use_chunked(Lq, L, causal)) {
+    const MbWs w = carve(ws, rows, L);
+    const int nchunk = (L + kMbChunk - 1) / kMbChunk;
+    const dim3 grid((unsigned)(rows * nchunk));
+    hipLaunchKernelGGL(mb_hist1_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, L,
+                       (int)rows, w);
+    hipLaunchKernelGGL(mb_hist2_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, L,
+                       (int)rows, w);
+    hipLaunchKernelGGL(mb_cand_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, n_sink,
+                       n_window, L, (int)rows, w);
+    hipLaunchKernelGGL(mb_resolve_kernel, dim3((unsigned)rows), dim3(kResThreads), 0, s, num,
+                       den, L, nchunk, count, w);
+    hipLaunchKernelGGL(mb_emit_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, n_sink,
+                       n_window, L, (int)rows, cap, idx, bitmask, w);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((select_rows_kernel<kSelThreads>), dim3(gx, gy), dim3(kSelThreads), 0, s,
-                     scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
-                     q_pos0, causal);
+  // one workgroup per row; the widest rows get 1024 threads x 64 keys.  Decode rows
+  // longer than 4096 tokens get their first-digit histogram from many workgroups.
+  uint32_t* gh = nullptr;
+  if (use_ghist(Lq, L, causal)) {
+    gh = (uint32_t*)ws;
+    const int nchunk = (L + kMbChunk - 1) / kMbChunk;
+    MbWs w{};
+    w.hist1 = gh;
+    hipLaunchKernelGGL(mb_hist1_kernel, dim3((unsigned)(rows * nchunk)), dim3(kMbThreads), 0, s,
+                       scores, num, den, L, (int)rows, w);
+  }
+  if (L <= 4096) {
+    hipLaunchKernelGGL((select_row_kernel<256, 16>), dim3((unsigned)rows), dim3(256), 0, s,
+                       scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
+                       q_pos0, causal, gh);
+  } else if (L <= 16384) {
+    hipLaunchKernelGGL((select_row_kernel<512, 32>), dim3((unsigned)rows), dim3(512), 0, s,
+                       scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
+                       q_pos0, causal, gh);
+  } else if (L <= 32768) {
+    hipLaunchKernelGGL((select_row_kernel<1024, 32>), dim3((unsigned)rows), dim3(1024), 0, s,
+                       scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
+                       q_pos0, causal, gh);
+  } else {
+    hipLaunchKernelGGL((select_row_kernel<1024, 64>), dim3((unsigned)rows), dim3(1024), 0, s,
+                       scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
+                       q_pos0, causal, gh);
+  }
   return hipGetLastError();
 }
 
