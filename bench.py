@@ -11,10 +11,13 @@ selected set.  Eight independent layer replicas (1.15 GiB of K/V/K_imp) are cycl
 that the 256 MB Infinity Cache cannot serve a step from the previous one.
 
 Timing: W warm-up steps, then exactly K steps replayed from one captured HIP graph,
-bracketed by torch.cuda.synchronize().  Inside the graph each kernel is bracketed by
-external HIP event-record nodes on the launch stream, which gives the average duration
-of every kernel over the timed region; the roofline object uses the attention kernel
-(the dominant one: it moves ~79% of a step's algorithmic bytes).
+bracketed by torch.cuda.synchronize().  Per-call durations: where the runtime accepts
+event-record nodes inside a captured graph, every call of the timed graph is bracketed by
+them; ROCm refuses those, and then each call kind is timed with events on the launch
+stream around a graph of K back-to-back calls of that kind (score and select as a pair,
+since they hand over the first-digit histogram).  The roofline object uses the attention
+call (split kernel + merge kernel), the dominant one: it moves ~79% of a step's
+algorithmic bytes.
 
 Extra fields: the same step at L = 128K and 256K (2 replicas each), and the CPU oracle
 timed on a bounded sample of the same workload (one thread).  Inputs are seeded and
@@ -64,6 +67,8 @@ class Layer:
         self.scores = torch.empty(w.B, w.Hkv, 1, L, dtype=torch.float32, device=device)
         self.idx = torch.empty(w.B, w.Hkv, 1, self.cap, dtype=torch.int32, device=device)
         self.count = torch.empty(w.B, w.Hkv, 1, dtype=torch.int32, device=device)
+        # first-digit histogram handed from the scorer to the selection (kept zeroed by it)
+        self.hist = torch.zeros(w.B, w.Hkv, 1, 2048, dtype=torch.int32, device=device)
         self.out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
         log(f"  layer replica {layer} at L={L} ready in {time.time() - t0:.1f}s")
 
@@ -72,10 +77,11 @@ class Layer:
         return [
             ("project", lambda: qa.butler_project_keys(self.k, self.wk, self.kimp, L - 1, 1)),
             ("score", lambda: qa.butler_score(qa.BUTLER_SCORE_RAW, self.qi, self.kimp,
-                                              self.scores, Hkv=w.Hkv, L=L)),
+                                              self.scores, Hkv=w.Hkv, L=L,
+                                              radix_hist=self.hist)),
             ("select", lambda: qa.butler_select_topk(self.scores, w.budget_num, w.budget_den,
                                                      w.n_sink, w.n_window, self.count,
-                                                     idx=self.idx)),
+                                                     idx=self.idx, radix_hist=self.hist)),
             ("attn", lambda: qa.butler_sparse_decode_attn(self.q, self.k, self.v, self.out,
                                                           L=L, idx=self.idx, count=self.count,
                                                           softmax_scale=w.scale)),
@@ -129,9 +135,9 @@ def run_config(w, L, replicas, steps, warmup, device):
     try:
         g_warm, _ = capture(max(warmup, 1), False)
         g_timed, evs = capture(steps, True)
-    except Exception as exc:  # event nodes not capturable: time kernels by a second graph
+    except Exception as exc:  # event nodes not capturable: time kernels by further graphs
         log(f"  external events in capture failed ({exc}); timing kernels per graph")
-        method = "per-kernel-graphs"
+        method = "per-call-graphs"
         g_warm, _ = capture(max(warmup, 1), False)
         g_timed, evs = capture(steps, False)
 
@@ -142,25 +148,31 @@ def run_config(w, L, replicas, steps, warmup, device):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    ab = [lay.algorithmic_bytes() for lay in layers]   # counts of the last timed steps
 
     per_kernel = {}
     if method == "graph-events":
         for name, e0, e1 in evs:
             per_kernel.setdefault(name, []).append(e0.elapsed_time(e1) * 1e3)   # us
     else:
-        for name in names:
+        # Events around a graph of `steps` back-to-back calls of one kind.  The scorer and
+        # the selection share the first-digit histogram (the scorer fills it, the selection
+        # empties it), so they are timed together as one pair.
+        groups = {"project": ["project"], "score+select": ["score", "select"], "attn": ["attn"]}
+        for gname, members in groups.items():
             gk = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gk):
                 for s in range(steps):
-                    dict(layers[s % replicas].calls())[name]()
+                    calls = dict(layers[s % replicas].calls())
+                    for m in members:
+                        calls[m]()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             gk.replay()
             b.record()
             torch.cuda.synchronize()
-            per_kernel[name] = [a.elapsed_time(b) * 1e3 / steps]
+            per_kernel[gname] = [a.elapsed_time(b) * 1e3 / steps]
     avg_us = {k: sum(v) / len(v) for k, v in per_kernel.items()}
-    ab = [lay.algorithmic_bytes() for lay in layers]
     step_bytes = sum(a["step"] for a in ab) / len(ab)
     attn_bytes = sum(a["attn"] for a in ab) / len(ab)
     n_sel = sum(a["n_sel"] for a in ab) / len(ab)

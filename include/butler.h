@@ -120,12 +120,20 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
  * only the tokens t <= q_pos0 + i; the others are written as -inf.  Non-causal rows score
  * tokens [0, L).
  *
- *   scores [B, Hkv, Lq, L] float32 (written)
+ *   scores     [B, Hkv, Lq, L]     float32 (written)
+ *   radix_hist [B, Hkv, Lq, 2048]  uint32, optional (NULL = none).  When given, the count
+ *              of every written score (t < row length) is added to bin key >> 21, where
+ *              key is the score's order-preserving 32-bit key (bits of the float with
+ *              -0 taken as +0 and NaN as -inf; sign set: all bits flipped, else the sign
+ *              bit set).  The caller zero-fills it before its first use; passing it on to
+ *              butler_select_topk spares the selection one pass over the scores, and
+ *              butler_select_topk leaves it zero-filled again.
  * RAW: d' in {16, 32}; SOFTVOTE: D in {64, 128}, Lq == 1 (decode); R in {1, 2, 4, 8}.
  * workspace: SOFTVOTE keeps per-token logits and per-block softmax partials.
  */
 int butler_score(void* stream, int mode, int dtype, const void* q, const void* keys,
-                 float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq, int L,
+                 float* scores, uint32_t* radix_hist, int B, int Hq, int Hkv, int G, int slot,
+                 int Lq, int L,
                  int L_cap, int dk, int q_pos0, int causal, float softmax_scale,
                  void* workspace, size_t* ws_bytes);
 
@@ -145,15 +153,21 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
  * count[row] = |S|.  At least one of idx, bitmask must be non-NULL.
  *
  *   scores  [B, Hkv, Lq, L]          float32 (read)
+ *   radix_hist [B, Hkv, Lq, 2048]    uint32, optional: the histogram butler_score built for
+ *                                    exactly these scores (see butler_score); it is used
+ *                                    instead of a counting pass and zero-filled again.  NULL:
+ *                                    the selection counts by itself.
  *   idx     [B, Hkv, Lq, cap]        int32   (written) -- cap >= min(L, x + n_sink + n_window)
  *   bitmask [B, Hkv, Lq, ceil(L/32)] uint32  (written)
  *   count   [B, Hkv, Lq]             int32   (written)
  * 0 <= budget_num, 1 <= budget_den, n_sink >= 0, n_window >= 0.  Rows of a causal or
  * multi-row (Lq > 1) call hold at most 65536 tokens; single-row decode calls up to 2^23.
- * workspace: none up to 65536 tokens; beyond, radix histograms, candidate keys, per-chunk
- * counts and offsets (about 8 bytes per token per row).
+ * workspace: none for causal / multi-row calls and rows up to 4096 tokens; otherwise a
+ * radix histogram, candidate keys, per-chunk counts and offsets (about 8 bytes per token
+ * per row).
  */
-int butler_select_topk(void* stream, const float* scores, int budget_num, int budget_den,
+int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist, int budget_num,
+                       int budget_den,
                        int n_sink, int n_window, int32_t* idx, uint32_t* bitmask,
                        int32_t* count, int B, int Hkv, int Lq, int L, int cap, int q_pos0,
                        int causal, void* workspace, size_t* ws_bytes);

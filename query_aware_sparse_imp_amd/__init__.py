@@ -43,8 +43,9 @@ _SIGS = {
     "butler_abi_version": ([], _i),
     "butler_project_keys": ([_vp, _i, _vp, _vp, _vp] + [_i] * 7, _i),
     "butler_produce_queries": ([_vp, _i, _vp, _vp, _vp, _vp] + [_i] * 7 + [_f, _vp, _sz], _i),
-    "butler_score": ([_vp, _i, _i, _vp, _vp, _vp] + [_i] * 11 + [_f, _vp, _sz], _i),
-    "butler_select_topk": ([_vp, _vp] + [_i] * 4 + [_vp, _vp, _vp] + [_i] * 7 + [_vp, _sz], _i),
+    "butler_score": ([_vp, _i, _i, _vp, _vp, _vp, _vp] + [_i] * 11 + [_f, _vp, _sz], _i),
+    "butler_select_topk": ([_vp, _vp, _vp] + [_i] * 4 + [_vp, _vp, _vp] + [_i] * 7 + [_vp, _sz],
+                           _i),
     "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 9 + [_f, _vp, _sz], _i),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -71,6 +72,11 @@ def declared_symbols() -> list:
     """Function names declared in include/butler.h."""
     text = open(HEADER).read()
     return sorted(set(re.findall(r"\b(butler_\w+)\s*\(", text)))
+
+
+def _check_hist(h: Optional[torch.Tensor], rows: tuple) -> None:
+    if h is not None and (tuple(h.shape) != (*rows, 2048) or h.element_size() != 4):
+        raise ValueError("radix_hist must be 32-bit [B, Hkv, Lq, 2048]")
 
 
 def _check(fn: str, status: int) -> None:
@@ -169,11 +175,14 @@ def butler_produce_queries(h: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
 
 def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.Tensor, *,
                  Hkv: int, L: int, slot: int = 0, q_pos0: int = 0, causal: bool = False,
-                 softmax_scale: float = 1.0, stream=None) -> None:
+                 softmax_scale: float = 1.0, radix_hist: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
     """Importance scores [B, Hkv, Lq, L] (see butler.h).
 
     RAW: q = q_imp [B, Hq, G, Lq, d'], keys = kimp [B, Hkv, L_cap, d'].
     SOFTVOTE: q = [B, Hq, Lq, D], keys = k_cache [B, Hkv, L_cap, D].
+    radix_hist: optional zero-filled int32/uint32 [B, Hkv, Lq, 2048] that collects the
+    first radix digit of every score for butler_select_topk.
     """
     if mode == BUTLER_SCORE_RAW:
         B, Hq, G, Lq, dk = q.shape
@@ -185,17 +194,19 @@ def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.T
         raise ValueError("shape mismatch")
     if q.dtype != keys.dtype or scores.dtype != torch.float32:
         raise TypeError("dtype mismatch")
-    args = (mode, _dtype_code(q), _ptr(q), _ptr(keys), _ptr(scores), B, Hq, Hkv, G, slot, Lq, L,
-            L_cap, dk, q_pos0, int(causal), softmax_scale)
+    _check_hist(radix_hist, (B, Hkv, Lq))
+    args = (mode, _dtype_code(q), _ptr(q), _ptr(keys), _ptr(scores), _ptr(radix_hist), B, Hq,
+            Hkv, G, slot, Lq, L, L_cap, dk, q_pos0, int(causal), softmax_scale)
     need = workspace_bytes(lambda ws, n: lib.butler_score(_stream(stream), *args, ws, n))
-    ws, n = _workspace("score", need, q.device, tuple(args[5:]))
+    ws, n = _workspace("score", need, q.device, tuple(args[6:]))
     _check("butler_score", lib.butler_score(_stream(stream), *args, ws, _byref(n)))
 
 
 def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n_sink: int,
                        n_window: int, count: torch.Tensor, idx: Optional[torch.Tensor] = None,
                        bitmask: Optional[torch.Tensor] = None, *, q_pos0: int = 0,
-                       causal: bool = False, stream=None) -> None:
+                       causal: bool = False, radix_hist: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
     """Top-x + sink + window per row of scores [B, Hkv, Lq, L] (see butler.h)."""
     B, Hkv, Lq, L = scores.shape
     cap = 0
@@ -208,8 +219,9 @@ def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n
             raise ValueError("bitmask must be 32-bit [B, Hkv, Lq, ceil(L/32)]")
     if count.shape != (B, Hkv, Lq) or count.dtype != torch.int32:
         raise ValueError("count must be int32 [B, Hkv, Lq]")
-    args = (_ptr(scores), budget_num, budget_den, n_sink, n_window, _ptr(idx), _ptr(bitmask),
-            _ptr(count), B, Hkv, Lq, L, cap, q_pos0, int(causal))
+    _check_hist(radix_hist, (B, Hkv, Lq))
+    args = (_ptr(scores), _ptr(radix_hist), budget_num, budget_den, n_sink, n_window, _ptr(idx),
+            _ptr(bitmask), _ptr(count), B, Hkv, Lq, L, cap, q_pos0, int(causal))
     need = workspace_bytes(lambda ws, n: lib.butler_select_topk(_stream(stream), *args, ws, n))
     ws, n = _workspace("select", need, scores.device, (budget_num, budget_den, B, Hkv, Lq, L, cap, q_pos0, int(causal)))
     _check("butler_select_topk",

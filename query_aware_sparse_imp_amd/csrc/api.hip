@@ -103,7 +103,8 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
 }
 
 int butler_score(void* stream, int mode, int dtype, const void* q, const void* keys,
-                 float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq, int L,
+                 float* scores, uint32_t* radix_hist, int B, int Hq, int Hkv, int G, int slot,
+                 int Lq, int L,
                  int L_cap, int dk, int q_pos0, int causal, float softmax_scale,
                  void* workspace, size_t* ws_bytes) {
   if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
@@ -128,15 +129,17 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
   if (workspace_phase(workspace, ws_bytes, need, &rc)) return rc;
   if (!q || !keys || !scores) return BUTLER_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(keys) || !aligned16(scores)) return BUTLER_ERR_INVALID_ARG;
+  if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (mode == BUTLER_SCORE_RAW)
     return finish(s, launch_score_raw(s, dtype, q, keys, scores, B, Hq, Hkv, G, slot, Lq, L,
-                                      L_cap, dk, q_pos0, causal));
+                                      L_cap, dk, q_pos0, causal, radix_hist));
   return finish(s, launch_score_softvote(s, dtype, q, keys, scores, B, Hq, Hkv, L, L_cap, dk,
-                                         softmax_scale, workspace));
+                                         softmax_scale, workspace, radix_hist));
 }
 
-int butler_select_topk(void* stream, const float* scores, int budget_num, int budget_den,
+int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist, int budget_num,
+                       int budget_den,
                        int n_sink, int n_window, int32_t* idx, uint32_t* bitmask,
                        int32_t* count, int B, int Hkv, int Lq, int L, int cap, int q_pos0,
                        int causal, void* workspace, size_t* ws_bytes) {
@@ -159,9 +162,11 @@ int butler_select_topk(void* stream, const float* scores, int budget_num, int bu
   if (workspace_phase(workspace, ws_bytes, select_workspace((int)rows, L, Lq, causal), &rc)) return rc;
   if (!scores || !count || (!idx && !bitmask)) return BUTLER_ERR_INVALID_ARG;
   if (!aligned16(scores)) return BUTLER_ERR_INVALID_ARG;
+  if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   return finish(s, launch_select(s, scores, budget_num, budget_den, n_sink, n_window, idx,
-                                 bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, workspace));
+                                 bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, radix_hist,
+                                 workspace));
 }
 
 int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void* k_cache,

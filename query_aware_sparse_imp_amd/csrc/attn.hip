@@ -485,9 +485,8 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
 // exp2(m_s - M) and the normaliser come from one wave over the (m, l) pairs.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = kMergeThreads / 32;
-constexpr int kMergeMaxPer = kMaxSplits / kMergeGroups;
 
-template <int D, int R>
+template <int D, int R, int PER>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     const float* __restrict__ part, float* __restrict__ out, int Hq, int Hkv, int Lq,
     int nsplit) {
@@ -500,46 +499,48 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int c = threadIdx.x & 31, gs = threadIdx.x >> 5;
   const float* base = part + (long long)row * nsplit * R * PS + (long long)r * PS;
-  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[kMergeThreads / 64];
   __shared__ float s_part[kMergeGroups][32];
-  __shared__ float s_inv;
-  float av[kMergeMaxPer];
+  // every load of the slice at once (addresses clamped, values masked afterwards)
+  float av[PER], mv[PER], lv[PER];
 #pragma unroll
-  for (int j = 0; j < kMergeMaxPer; ++j) {
-    const int s = gs + j * kMergeGroups;
-    av[j] = (s < nsplit) ? base[(long long)s * R * PS + 4 + slice * 32 + c] : 0.f;
+  for (int j = 0; j < PER; ++j) {
+    const int s = min(gs + j * kMergeGroups, nsplit - 1);
+    const float* ps = base + (long long)s * R * PS;
+    av[j] = ps[4 + slice * 32 + c];
+    mv[j] = ps[0];
+    lv[j] = ps[1];
   }
-  if (threadIdx.x < 64) {
-    // one wave: max of m, then weights and their l-weighted sum, in split order per lane
-    float M = neg_inf();
-    for (int s = threadIdx.x; s < nsplit; s += 64) M = fmaxf(M, base[(long long)s * R * PS]);
+  float M = neg_inf();
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float lsum = 0.f;
-    for (int s = threadIdx.x; s < nsplit; s += 64) {
-      const float m = base[(long long)s * R * PS];
-      const float wgt = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
-      s_w[s] = wgt;
-      lsum += wgt * base[(long long)s * R * PS + 1];
-    }
+  for (int j = 0; j < PER; ++j)
+    if (gs + j * kMergeGroups < nsplit) M = fmaxf(M, mv[j]);
+  // block max (max is exact, any order)
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
-    if (threadIdx.x == 0) s_inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
-  }
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = M;
   __syncthreads();
-  float a = 0.f;
+  M = s_red[0];
 #pragma unroll
-  for (int j = 0; j < kMergeMaxPer; ++j) {
-    const int s = gs + j * kMergeGroups;
-    if (s < nsplit) a = fmaf(s_w[s], av[j], a);
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
+  float a = 0.f, lsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (gs + j * kMergeGroups < nsplit && mv[j] != neg_inf()) {
+      const float wgt = fast_exp2(mv[j] - M);
+      a = fmaf(wgt, av[j], a);
+      lsum = fmaf(wgt, lv[j], lsum);
+    }
   }
+  __shared__ float s_l[kMergeGroups];
   s_part[gs][c] = a;
+  if (c == 0) s_l[gs] = lsum;
   __syncthreads();
   if (gs == 0) {
-    float t = 0.f;
+    float t = 0.f, L = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMergeGroups; ++j) t += s_part[j][c];
-    out[(((long long)b * Hq + g * R + r) * Lq + i) * D + slice * 32 + c] = t * s_inv;
+    for (int j = 0; j < kMergeGroups; ++j) { t += s_part[j][c]; L += s_l[j]; }
+    out[(((long long)b * Hq + g * R + r) * Lq + i) * D + slice * 32 + c] = (L > 0.f) ? t / L : 0.f;
   }
 }
 
@@ -659,8 +660,19 @@ hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
                        count, part, Hq, Hkv, Lq, L_cap, cap, scale * 1.4426950408889634f,
                        sp.nsplit, sp.rounds, (int)rows);
   }
-  hipLaunchKernelGGL((attn_merge_kernel<D, R>), dim3((unsigned)(rows * R * (D / 32))),
-                     dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  // splits per thread of the merge: the smallest power of two >= nsplit / 8
+  const dim3 mgrid((unsigned)(rows * R * (D / 32)));
+  const int per = (nsplit + kMergeGroups - 1) / kMergeGroups;
+  if (per <= 4)
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 4>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  else if (per <= 8)
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 8>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  else if (per <= 16)
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 16>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  else if (per <= 32)
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 32>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 64>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
   return hipGetLastError();
 }
 

@@ -21,18 +21,18 @@ hipError_t launch_produce(hipStream_t s, const void* h, const void* w1, const vo
 // ---- scoring --------------------------------------------------------------
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
-                            int L, int L_cap, int dp, int q_pos0, int causal);
+                            int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist);
 size_t softvote_workspace(int B, int Hq, int Hkv, int L);
 hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const void* k,
                                  float* scores, int B, int Hq, int Hkv, int L, int L_cap,
-                                 int D, float scale, void* ws);
+                                 int D, float scale, void* ws, uint32_t* hist);
 
 // ---- selection ------------------------------------------------------------
 size_t select_workspace(int rows, int L, int Lq, int causal);
 hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
                          int n_window, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
-                         void* ws);
+                         uint32_t* hist, void* ws);
 
 // ---- attention ------------------------------------------------------------
 size_t attn_workspace(int dtype, int B, int Hq, int Hkv, int D, int Lq, int L, int cap);

@@ -41,7 +41,26 @@ __global__ __launch_bounds__(256) void project_keys_kernel(const T* __restrict__
     for (int c = 0; c < D / EPL; ++c) Vec16<T>::load(kr + c * EPL, kv[c]);
   };
   if (row < rows_total) load_row(row);
-  for (int i = threadIdx.x; i < D * DP; i += 256) wsh[i] = load_elem(w + i);
+  // W_K in 16-byte pieces, all issued before any is used
+  {
+    constexpr int EPL16 = Vec16<T>::N;
+    constexpr int NPIECE = D * DP / EPL16;
+    constexpr int PER = (NPIECE + 255) / 256;
+    float wv[PER][EPL16];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int pc = threadIdx.x + u * 256;
+      if (pc < NPIECE) Vec16<T>::load(w + pc * EPL16, wv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int pc = threadIdx.x + u * 256;
+      if (pc < NPIECE) {
+#pragma unroll
+        for (int e = 0; e < EPL16; ++e) wsh[pc * EPL16 + e] = wv[u][e];
+      }
+    }
+  }
   __syncthreads();
   while (row < rows_total) {
     // four independent float64 sums (every partial sum is exact, so their order does not

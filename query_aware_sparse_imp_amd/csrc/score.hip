@@ -7,6 +7,11 @@
 //   exact, and the result is rounded once to float32 -- the score is the exactly
 //   rounded dot product whatever the reduction order.
 //
+// Both scorers can also add each score's first radix digit (the top 11 bits of the
+// order-preserving key that the selection uses) into a per-row global histogram, counted
+// in LDS per workgroup and flushed with atomics, so the selection that follows starts from
+// it instead of reading every score once more.
+//
 // SOFTVOTE (TokenSelect README, highlights): per-head logits z_h(t) = scale * q_h . k_t,
 //   a softmax over t for every head, summed over the heads of the GQA group.
 //   Pass 1 streams the keys once (D/8 lanes per 256-byte key row), writes the
@@ -26,7 +31,7 @@ template <typename T, int DP>
 __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
     const T* __restrict__ q_imp, const T* __restrict__ kimp, float* __restrict__ scores,
     int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal,
-    int tpb) {
+    int tpb, uint32_t* __restrict__ radix_hist) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPT = DP / EPL;           // lanes per token
   constexpr int TPI = kRawThreads / LPT;  // tokens per block-wide step
@@ -57,11 +62,20 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   int t = t0 + sub;
   if (t < t1) load_batch(t);
   __shared__ double qbar[DP];
+  __shared__ uint32_t hist[2048];
+  if (radix_hist)
+    for (int j = threadIdx.x; j < 2048; j += kRawThreads) hist[j] = 0u;
   if (threadIdx.x < DP) {
+    // the group's R <= 8 values are loaded together, then summed in head order
+    float qh[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      qh[r] = (r < R) ? load_elem(q_imp + ((((size_t)b * Hq + g * R + min(r, R - 1)) * G + slot) *
+                                               Lq + i) * DP + threadIdx.x)
+                      : 0.f;
     double a = 0.0;
-    for (int r = 0; r < R; ++r)
-      a += (double)load_elem(
-          q_imp + ((((size_t)b * Hq + g * R + r) * G + slot) * Lq + i) * DP + threadIdx.x);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) a += (double)qh[r];
     qbar[threadIdx.x] = a;
   }
   __syncthreads();
@@ -77,10 +91,20 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
 #pragma unroll
       for (int o = 1; o < LPT; o <<= 1) acc += __shfl_xor(acc, o, 64);
       const int tu = t + u * TPI;
-      if (part == 0 && tu < t1) srow[tu] = (tu < L_r) ? (float)acc : neg_inf();
+      if (part == 0 && tu < t1) {
+        const float sc = (tu < L_r) ? (float)acc : neg_inf();
+        srow[tu] = sc;
+        if (radix_hist && tu < L_r) atomicAdd(&hist[score_key(sc) >> 21], 1u);
+      }
     }
     t += TPI * kRawUnroll;
     if (t < t1) load_batch(t);
+  }
+  if (radix_hist) {
+    __syncthreads();
+    uint32_t* gh = radix_hist + ((size_t)bg * Lq + i) * 2048;
+    for (int j = threadIdx.x; j < 2048; j += kRawThreads)
+      if (hist[j]) atomicAdd(&gh[j], hist[j]);
   }
 }
 
@@ -176,9 +200,12 @@ __global__ __launch_bounds__(kSvThreads) void softvote_logits_kernel(
 template <int R>
 __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
     const float* __restrict__ logits, const float2* __restrict__ part,
-    float* __restrict__ scores, int L, int nblk) {
+    float* __restrict__ scores, int L, int nblk, uint32_t* __restrict__ radix_hist) {
   const int bg = blockIdx.y, blk = blockIdx.x;
   __shared__ float Ms[R], Ls[R];
+  __shared__ uint32_t hist[2048];
+  if (radix_hist)
+    for (int j = threadIdx.x; j < 2048; j += kSvThreads) hist[j] = 0u;
   if (threadIdx.x < R) {
     const int r = threadIdx.x;
     float mm = neg_inf(), ll = 0.f;
@@ -197,25 +224,32 @@ __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) s += fast_exp2(zb[(size_t)r * L + t] - Ms[r]) / Ls[r];
     scores[(size_t)bg * L + t] = s;
+    if (radix_hist) atomicAdd(&hist[score_key(s) >> 21], 1u);
+  }
+  if (radix_hist) {
+    __syncthreads();
+    uint32_t* gh = radix_hist + (size_t)bg * 2048;
+    for (int j = threadIdx.x; j < 2048; j += kSvThreads)
+      if (hist[j]) atomicAdd(&gh[j], hist[j]);
   }
 }
 
 template <typename T, int DP>
 hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scores, int B,
                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
-                 int causal) {
+                 int causal, uint32_t* hist) {
   constexpr int LPT = DP / Vec16<T>::N;
   const int tpb = (kRawThreads / LPT) * kRawUnroll;
   dim3 grid((L + tpb - 1) / tpb, Lq, B * Hkv);
   hipLaunchKernelGGL((score_raw_kernel<T, DP>), grid, dim3(kRawThreads), 0, s, (const T*)q_imp,
                      (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal,
-                     tpb);
+                     tpb, hist);
   return hipGetLastError();
 }
 
 template <typename T, int D, int R>
 hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int B, int Hq,
-                int Hkv, int L, int L_cap, float scale, void* ws) {
+                int Hkv, int L, int L_cap, float scale, void* ws, uint32_t* hist) {
   const int nblk = (L + kSvTokensPerBlock - 1) / kSvTokensPerBlock;
   float* logits = (float*)ws;
   float2* part = (float2*)(logits + (size_t)B * Hkv * R * L);
@@ -225,7 +259,7 @@ hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int 
                      (const T*)q, (const T*)k, logits, part, Hq, Hkv, L, L_cap, scale_log2,
                      nblk);
   hipLaunchKernelGGL((softvote_combine_kernel<R>), grid, dim3(kSvThreads), 0, s, logits, part,
-                     scores, L, nblk);
+                     scores, L, nblk, hist);
   return hipGetLastError();
 }
 
@@ -233,13 +267,13 @@ hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int 
 
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
-                            int L, int L_cap, int dp, int q_pos0, int causal) {
+                            int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist) {
   if (dtype == 1) {
-    if (dp == 32) return raw_t<bf16_t, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
-    if (dp == 16) return raw_t<bf16_t, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
+    if (dp == 32) return raw_t<bf16_t, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);
+    if (dp == 16) return raw_t<bf16_t, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);
   } else {
-    if (dp == 32) return raw_t<float, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
-    if (dp == 16) return raw_t<float, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
+    if (dp == 32) return raw_t<float, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);
+    if (dp == 16) return raw_t<float, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);
   }
   return hipErrorInvalidValue;
 }
@@ -252,10 +286,10 @@ size_t softvote_workspace(int B, int Hq, int Hkv, int L) {
 
 hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const void* k,
                                  float* scores, int B, int Hq, int Hkv, int L, int L_cap,
-                                 int D, float scale, void* ws) {
+                                 int D, float scale, void* ws, uint32_t* hist) {
   const int R = Hq / Hkv;
 #define BUTLER_SV(T, DD, RR)                                                       \
-  if (D == DD && R == RR) return sv_t<T, DD, RR>(s, q, k, scores, B, Hq, Hkv, L, L_cap, scale, ws);
+  if (D == DD && R == RR) return sv_t<T, DD, RR>(s, q, k, scores, B, Hq, Hkv, L, L_cap, scale, ws, hist);
   if (dtype == 1) {
     BUTLER_SV(bf16_t, 128, 1) BUTLER_SV(bf16_t, 128, 2) BUTLER_SV(bf16_t, 128, 4) BUTLER_SV(bf16_t, 128, 8)
     BUTLER_SV(bf16_t, 64, 1) BUTLER_SV(bf16_t, 64, 2) BUTLER_SV(bf16_t, 64, 4) BUTLER_SV(bf16_t, 64, 8)

@@ -10,30 +10,27 @@
 // walks the row in index order, so the index list comes out ascending.
 //
 // Workgroups never wait on one another inside a kernel (a device-wide release on this
-// GPU writes back the XCD's L2, far too slow for a per-workgroup handshake), so there are
-// two schedules:
+// GPU writes back the XCD's L2, far too slow for a per-workgroup handshake); every
+// hand-off between workgroups goes through a kernel boundary.  The first radix digit can
+// come from the scorer (an optional per-row histogram of the top 11 key bits, see
+// butler_score), which saves one pass over the scores.  Two schedules:
 //
-// Rows of at most 64K tokens (decode rows up to 64K, every causal prefill row): one
-//   workgroup per row holds the row's keys in VGPRs (up to 64 per thread, strided so that
-//   a wave's ballot covers 64 consecutive tokens), builds the digit histograms in LDS, and
-//   emits through 64-token ballot words with two block-wide scans over the words (tie
-//   ranks, then output positions).  The first digit's histogram sees every key, and
-//   in one workgroup its LDS atomics pile onto the few hot bins; for decode rows longer
-//   than 4096 tokens it is built first by many workgroups (2048 tokens each, LDS then
-//   global atomics) and the row kernel starts from it (and clears it), so the row kernel
-//   only histograms the keys inside the chosen first-digit bin.
+// Decode rows longer than 4096 tokens: kernels over 2048-token chunks
+//   0  (only without the scorer's histogram) histogram of key bits 31..21
+//   1  every chunk derives the first-digit bin b1, counts its tokens that are surely
+//      selected (digit above b1, or a sink / window token) and appends the keys whose
+//      digit is b1 to a candidate list -- for scores of any spread only a sliver of the
+//      row
+//   2  one workgroup per row resolves bits 20..0 of tau over the candidates (in LDS when
+//      they fit), the tie quota and the lowest-index tie cut, then every chunk's output
+//      offset and the row count, and clears the histogram and the candidate counter
+//   3  every chunk emits its bitmask words and its indices at its offset.
 //
-// Longer decode rows: five kernels over 2048-token chunks, no scratch shared inside a
-//   kernel except by atomics:
-//     1  histogram of key bits 31..21 (LDS, then global atomics)
-//     2  each workgroup derives the bin b1; histogram of bits 20..10 of the keys in b1
-//     3  each workgroup derives b1:b2; per-chunk count of the tokens surely selected (key
-//        above the 22-bit prefix, or a sink / window token); keys sharing the prefix are
-//        appended to a candidate list
-//     4  one workgroup per row resolves the last 10 bits, the tie quota and the
-//        lowest-index tie cut from the candidates, then every chunk's output offset and the
-//        row count; it clears the histograms and the candidate counter for the next call
-//     5  every chunk emits its bitmask words and its indices at its offset.
+// Other rows (short decode rows, every causal prefill row): one workgroup per row holds
+//   the row's keys in VGPRs (up to 64 per thread, strided so that a wave's ballot covers
+//   64 consecutive tokens), builds the digit histograms in LDS (the first from the
+//   scorer's histogram when given), and emits through 64-token ballot words with two
+//   block-wide scans over the words (tie ranks, then output positions).
 #include "common.h"
 #include "kernels.h"
 
@@ -155,6 +152,11 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
 
   uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;
   int need = 0;
+  if (ghist && mode != kModeNormal) {
+    // the scorer's histogram is not needed, but it must be left zero-filled
+    uint32_t* gh = ghist + row * 2048;
+    for (int j = threadIdx.x; j < 2048; j += NT) gh[j] = 0u;
+  }
   if (mode == kModeNormal) {
     uint32_t prefix = 0, pmask = 0;
     need = k;
@@ -232,13 +234,14 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// long decode rows: five kernels over 2048-token chunks
+// decode rows longer than 4096 tokens: three (or four) kernels over 2048-token chunks
 // ---------------------------------------------------------------------------
 
 constexpr int kMbThreads = 256;
 constexpr int kMbChunk = 2048;           // tokens per workgroup, 8 per thread
 constexpr int kMbMaxChunks = 4096;       // rows of up to 8M tokens
-constexpr int kRowMaxL = 65536;          // longest row of the one-workgroup schedule
+constexpr int kResThreads = 1024;
+constexpr int kResStage = 12288;         // candidates staged in LDS (more: read from memory)
 
 struct RowState {
   uint32_t tau;
@@ -246,9 +249,8 @@ struct RowState {
 };
 
 struct MbWs {
-  uint32_t* hist1;   // [rows][2048]   zero between calls
-  uint32_t* hist2;   // [rows][2048]   zero between calls
-  uint32_t* ccount;  // [rows]         zero between calls
+  uint32_t* hist1;   // [rows][2048]   first-digit counts, zero between calls
+  uint32_t* ccount;  // [rows]         candidate counter, zero between calls
   RowState* state;   // [rows]
   int* defcnt;       // [rows][nchunk]
   int* offs;         // [rows][nchunk]
@@ -259,7 +261,7 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t mb_bytes(long long rows, int L) {
   const long long nchunk = (L + kMbChunk - 1) / kMbChunk;
-  return 2 * al256(rows * 2048 * 4) + al256(rows * 4) + al256(rows * sizeof(RowState)) +
+  return al256(rows * 2048 * 4) + al256(rows * 4) + al256(rows * sizeof(RowState)) +
          2 * al256(rows * nchunk * 4) + al256((size_t)rows * L * sizeof(uint2));
 }
 
@@ -268,7 +270,6 @@ MbWs carve(void* ws, long long rows, int L) {
   char* p = (char*)ws;
   MbWs w;
   w.hist1 = (uint32_t*)p;     p += al256(rows * 2048 * sizeof(uint32_t));
-  w.hist2 = (uint32_t*)p;     p += al256(rows * 2048 * sizeof(uint32_t));
   w.ccount = (uint32_t*)p;    p += al256(rows * sizeof(uint32_t));
   w.state = (RowState*)p;     p += al256(rows * sizeof(RowState));
   w.defcnt = (int*)p;         p += al256(rows * nchunk * sizeof(int));
@@ -288,27 +289,15 @@ __device__ __forceinline__ int load_keys8(const float* s, int t0, int L, uint32_
     key[6] = score_key(b.z); key[7] = score_key(b.w);
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) key[j] = (j < nv) ? score_key(s[t0 + j]) : 0u;
+    for (int j = 0; j < 8; ++j) key[j] = score_key(s[min(t0 + j, L - 1)]);
   }
   return nv;
 }
 
-// Derives (bin, rank left) from a row's global histogram; all threads call it.
-__device__ __forceinline__ void bin_from_global(const uint32_t* gh, int need, uint32_t* h,
-                                                int* tmp, int* sh_bin, int* sh_need) {
-  for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = gh[j];
-  __syncthreads();
-  find_bin_from_top<kMbThreads>(h, 2048, need, tmp, sh_bin, sh_need);
-}
-
-__device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* gh) {
-  for (int j = threadIdx.x; j < 2048; j += kMbThreads)
-    if (h[j]) atomicAdd(&gh[j], h[j]);
-}
-
+// first-digit histogram, when the scorer did not produce it
 __global__ __launch_bounds__(kMbThreads) void mb_hist1_kernel(const float* __restrict__ scores,
                                                               int num, int den, int L, int rows,
-                                                              MbWs w) {
+                                                              uint32_t* __restrict__ ghist) {
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
   int k;
   if (row_mode(L, num, den, k) != kModeNormal) return;
@@ -321,34 +310,18 @@ __global__ __launch_bounds__(kMbThreads) void mb_hist1_kernel(const float* __res
   for (int j = 0; j < 8; ++j)
     if (j < nv) atomicAdd(&h[key[j] >> 21], 1u);
   __syncthreads();
-  flush_hist(h, w.hist1 + (long long)row * 2048);
+  uint32_t* gh = ghist + (long long)row * 2048;
+  for (int j = threadIdx.x; j < 2048; j += kMbThreads)
+    if (h[j]) atomicAdd(&gh[j], h[j]);
 }
 
-__global__ __launch_bounds__(kMbThreads) void mb_hist2_kernel(const float* __restrict__ scores,
-                                                              int num, int den, int L, int rows,
-                                                              MbWs w) {
-  const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
-  int k;
-  if (row_mode(L, num, den, k) != kModeNormal) return;
-  __shared__ uint32_t h[2048];
-  __shared__ int tmp[kMbThreads / 64];
-  __shared__ int sh_bin, sh_need;
-  uint32_t key[8];
-  const int nv = load_keys8(scores + (long long)row * L, chunk * kMbChunk + threadIdx.x * 8, L, key);
-  bin_from_global(w.hist1 + (long long)row * 2048, k, h, tmp, &sh_bin, &sh_need);
-  const uint32_t b1 = (uint32_t)sh_bin;
-  for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < nv && (key[j] >> 21) == b1) atomicAdd(&h[(key[j] >> 10) & 2047u], 1u);
-  __syncthreads();
-  flush_hist(h, w.hist2 + (long long)row * 2048);
-}
-
+// Chunk pass: every workgroup derives the first-digit bin b1 from the row's histogram,
+// counts its tokens that are surely selected (digit above b1, or sink / window) and
+// appends the keys whose first digit is b1 to the row's candidate list.
 __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __restrict__ scores,
                                                              int num, int den, int n_sink,
                                                              int n_window, int L, int rows,
+                                                             const uint32_t* __restrict__ ghist,
                                                              MbWs w) {
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
   const int nchunk = gridDim.x / rows;
@@ -360,14 +333,13 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
   const int t0 = chunk * kMbChunk + threadIdx.x * 8;
   uint32_t key[8];
   const int nv = load_keys8(scores + (long long)row * L, t0, L, key);
-  uint32_t hi22 = 0;
+  uint32_t b1 = 0;
   if (mode == kModeNormal) {
-    bin_from_global(w.hist1 + (long long)row * 2048, k, h, tmp, &sh_bin, &sh_need);
-    const uint32_t b1 = (uint32_t)sh_bin;
-    const int need1 = sh_need;
+    const uint32_t* gh = ghist + (long long)row * 2048;
+    for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = gh[j];
     __syncthreads();
-    bin_from_global(w.hist2 + (long long)row * 2048, need1, h, tmp, &sh_bin, &sh_need);
-    hi22 = (b1 << 11) | (uint32_t)sh_bin;
+    find_bin_from_top<kMbThreads>(h, 2048, k, tmp, &sh_bin, &sh_need);
+    b1 = (uint32_t)sh_bin;
   }
   const int w_lo = max(0, L - n_window);
   int ndef = 0, ncand = 0;
@@ -377,9 +349,9 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
     const int t = t0 + j;
     const bool forced = t < n_sink || t >= w_lo;
     if (mode == kModeNormal) {
-      const uint32_t top = key[j] >> 10;
-      ndef += (forced || top > hi22) ? 1 : 0;
-      ncand += (top == hi22) ? 1 : 0;
+      const uint32_t top = key[j] >> 21;
+      ndef += (forced || top > b1) ? 1 : 0;
+      ncand += (top == b1) ? 1 : 0;
     } else {
       ndef += (forced || mode == kModeAll) ? 1 : 0;
     }
@@ -397,7 +369,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
     int pos = sh_base + cpos;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (j >= nv || (key[j] >> 10) != hi22) continue;
+      if (j >= nv || (key[j] >> 21) != b1) continue;
       const int t = t0 + j;
       const uint32_t flag = (t < n_sink || t >= w_lo) ? 0x80000000u : 0u;
       crow[pos++] = make_uint2(key[j], (uint32_t)t | flag);
@@ -405,74 +377,90 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
   }
 }
 
-constexpr int kResThreads = 1024;
-
+// Row pass (one workgroup per row): the remaining 21 bits of tau and the tie cut from the
+// candidates (staged in LDS when they fit), then every chunk's output offset and the row
+// count; clears the histogram and the candidate counter for the next call.
 __global__ __launch_bounds__(kResThreads) void mb_resolve_kernel(int num, int den, int L,
                                                                  int nchunk,
                                                                  int32_t* __restrict__ count,
+                                                                 uint32_t* __restrict__ ghist,
                                                                  MbWs w) {
   const int row = blockIdx.x;
   int k;
   const int mode = row_mode(L, num, den, k);
   __shared__ uint32_t h[2048];
   __shared__ int cnt[kMbMaxChunks];
+  __shared__ uint32_t s_key[kResStage], s_id[kResStage];
   __shared__ int tmp[kResThreads / 64];
   __shared__ int sh_bin, sh_need, sh_ties;
-  uint32_t* gh1 = w.hist1 + (long long)row * 2048;
-  uint32_t* gh2 = w.hist2 + (long long)row * 2048;
+  uint32_t* gh = ghist + (long long)row * 2048;
   const int n = (int)w.ccount[row];
   const uint2* crow = w.cand + (long long)row * L;
+  const bool staged = n <= kResStage;
+  if (staged) {
+    for (int j = threadIdx.x; j < n; j += kResThreads) {
+      const uint2 c = crow[j];
+      s_key[j] = c.x;
+      s_id[j] = c.y;
+    }
+  }
+  auto ckey = [&](int j) { return staged ? s_key[j] : crow[j].x; };
+  auto cid = [&](int j) { return staged ? s_id[j] : crow[j].y; };
   uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;
   int tie_cut = -1;
   if (mode == kModeNormal) {
-    for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = gh1[j];
+    for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = gh[j];
     __syncthreads();
     find_bin_from_top<kResThreads>(h, 2048, k, tmp, &sh_bin, &sh_need);
     const uint32_t b1 = (uint32_t)sh_bin;
-    const int need1 = sh_need;
-    __syncthreads();
-    for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = gh2[j];
-    __syncthreads();
-    find_bin_from_top<kResThreads>(h, 2048, need1, tmp, &sh_bin, &sh_need);
-    const uint32_t hi22 = (b1 << 11) | (uint32_t)sh_bin;
-    const int need2 = sh_need;
-    __syncthreads();
-    // last 10 bits
-    for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = 0u;
-    __syncthreads();
-    for (int j = threadIdx.x; j < n; j += kResThreads) atomicAdd(&h[crow[j].x & 1023u], 1u);
-    __syncthreads();
-    find_bin_from_top<kResThreads>(h, 1024, need2, tmp, &sh_bin, &sh_need);
-    tau = (hi22 << 10) | (uint32_t)sh_bin;
-    const int need3 = sh_need;
+    int need = sh_need;
+    // bits 20..10, then 9..0, over the candidates (all have first digit b1)
+    uint32_t prefix = b1 << 21, pmask = 0xffe00000u;
+    const int shifts[2] = {10, 0};
+    const int bins[2] = {2048, 1024};
+    for (int p = 0; p < 2; ++p) {
+      __syncthreads();
+      for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = 0u;
+      __syncthreads();
+      for (int j = threadIdx.x; j < n; j += kResThreads) {
+        const uint32_t key = ckey(j);
+        if ((key & pmask) == prefix) atomicAdd(&h[(key >> shifts[p]) & (uint32_t)(bins[p] - 1)], 1u);
+      }
+      __syncthreads();
+      find_bin_from_top<kResThreads>(h, bins[p], need, tmp, &sh_bin, &sh_need);
+      prefix |= (uint32_t)sh_bin << shifts[p];
+      pmask |= (uint32_t)(bins[p] - 1) << shifts[p];
+      need = sh_need;
+    }
+    tau = prefix;
+    const int need3 = need;   // keys equal to tau that the budget takes
     if (threadIdx.x == 0) sh_ties = 0;
     __syncthreads();
     int mine = 0;
-    for (int j = threadIdx.x; j < n; j += kResThreads) mine += (crow[j].x == tau) ? 1 : 0;
+    for (int j = threadIdx.x; j < n; j += kResThreads) mine += (ckey(j) == tau) ? 1 : 0;
     if (mine) atomicAdd(&sh_ties, mine);
     __syncthreads();
     if (need3 >= sh_ties) {
       tie_cut = 0x7fffffff;
     } else {
       // the need3-th smallest index among the keys equal to tau: bits 30..20, 19..10, 9..0
-      uint32_t pre = 0u, pmask = 0u;
-      int need = need3;
-      const int shifts[3] = {20, 10, 0};
-      const uint32_t widths[3] = {2048u, 1024u, 1024u};
+      uint32_t pre = 0u, pm = 0u;
+      int nd = need3;
+      const int ish[3] = {20, 10, 0};
+      const uint32_t iw[3] = {2048u, 1024u, 1024u};
       for (int p = 0; p < 3; ++p) {
         __syncthreads();
         for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = 0u;
         __syncthreads();
         for (int j = threadIdx.x; j < n; j += kResThreads) {
-          const uint2 c = crow[j];
-          const uint32_t t = c.y & 0x7fffffffu;
-          if (c.x == tau && (t & pmask) == pre) atomicAdd(&h[(t >> shifts[p]) & (widths[p] - 1u)], 1u);
+          const uint32_t t = cid(j) & 0x7fffffffu;
+          if (ckey(j) == tau && (t & pm) == pre) atomicAdd(&h[(t >> ish[p]) & (iw[p] - 1u)], 1u);
         }
         __syncthreads();
-        find_bin_from_bottom<kResThreads>(h, 2048, need, tmp, &sh_bin, &sh_need);
-        pre |= (uint32_t)sh_bin << shifts[p];
-        pmask |= (widths[p] - 1u) << shifts[p];
-        need = sh_need;
+        find_bin_from_bottom<kResThreads>(h, 2048, nd, tmp, &sh_bin, &sh_need);
+        pre |= (uint32_t)sh_bin << ish[p];
+        pm |= (iw[p] - 1u) << ish[p];
+        nd = sh_need;
       }
       tie_cut = (int)pre;
     }
@@ -482,10 +470,11 @@ __global__ __launch_bounds__(kResThreads) void mb_resolve_kernel(int num, int de
   __syncthreads();
   if (mode == kModeNormal) {
     for (int j = threadIdx.x; j < n; j += kResThreads) {
-      const uint2 c = crow[j];
-      if (c.y & 0x80000000u) continue;  // sink / window tokens are already counted
-      const int t = (int)c.y;
-      if (c.x > tau || (c.x == tau && t <= tie_cut)) atomicAdd(&cnt[t / kMbChunk], 1);
+      const uint32_t id = cid(j);
+      if (id & 0x80000000u) continue;  // sink / window tokens are already counted
+      const uint32_t key = ckey(j);
+      const int t = (int)id;
+      if (key > tau || (key == tau && t <= tie_cut)) atomicAdd(&cnt[t / kMbChunk], 1);
     }
   }
   __syncthreads();
@@ -499,7 +488,7 @@ __global__ __launch_bounds__(kResThreads) void mb_resolve_kernel(int num, int de
     carry += tot;
   }
   // clear the accumulators for the next call
-  for (int j = threadIdx.x; j < 2048; j += kResThreads) { gh1[j] = 0u; gh2[j] = 0u; }
+  for (int j = threadIdx.x; j < 2048; j += kResThreads) gh[j] = 0u;
   if (threadIdx.x == 0) {
     count[row] = carry;
     w.state[row].tau = tau;
@@ -558,69 +547,55 @@ __global__ __launch_bounds__(kMbThreads) void mb_emit_kernel(
 }
 
 bool use_chunked(int Lq, int L, int causal) {
-  return !causal && Lq == 1 && L > kRowMaxL;
-}
-
-bool use_ghist(int Lq, int L, int causal) {
-  return !causal && Lq == 1 && L > 4096 && L <= kRowMaxL;
+  return !causal && Lq == 1 && L > 4096;
 }
 
 }  // namespace
 
 size_t select_workspace(int rows, int L, int Lq, int causal) {
-  if (use_chunked(Lq, L, causal)) return mb_bytes(rows, L);
-  if (use_ghist(Lq, L, causal)) return al256((size_t)rows * 2048 * sizeof(uint32_t));
-  return 0;
+  return use_chunked(Lq, L, causal) ? mb_bytes(rows, L) : 0;
 }
 
 hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
                          int n_window, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
-                         void* ws) {
+                         uint32_t* hist, void* ws) {
   const long long rows = (long long)B * Hkv * Lq;
   if (use_chunked(Lq, L, causal)) {
     const MbWs w = carve(ws, rows, L);
     const int nchunk = (L + kMbChunk - 1) / kMbChunk;
     const dim3 grid((unsigned)(rows * nchunk));
-    hipLaunchKernelGGL(mb_hist1_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, L,
-                       (int)rows, w);
-    hipLaunchKernelGGL(mb_hist2_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, L,
-                       (int)rows, w);
+    uint32_t* gh = hist;
+    if (!gh) {
+      gh = w.hist1;
+      hipLaunchKernelGGL(mb_hist1_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, L,
+                         (int)rows, gh);
+    }
     hipLaunchKernelGGL(mb_cand_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, n_sink,
-                       n_window, L, (int)rows, w);
+                       n_window, L, (int)rows, (const uint32_t*)gh, w);
     hipLaunchKernelGGL(mb_resolve_kernel, dim3((unsigned)rows), dim3(kResThreads), 0, s, num,
-                       den, L, nchunk, count, w);
+                       den, L, nchunk, count, gh, w);
     hipLaunchKernelGGL(mb_emit_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, n_sink,
                        n_window, L, (int)rows, cap, idx, bitmask, w);
     return hipGetLastError();
   }
-  // one workgroup per row; the widest rows get 1024 threads x 64 keys.  Decode rows
-  // longer than 4096 tokens get their first-digit histogram from many workgroups.
-  uint32_t* gh = nullptr;
-  if (use_ghist(Lq, L, causal)) {
-    gh = (uint32_t*)ws;
-    const int nchunk = (L + kMbChunk - 1) / kMbChunk;
-    MbWs w{};
-    w.hist1 = gh;
-    hipLaunchKernelGGL(mb_hist1_kernel, dim3((unsigned)(rows * nchunk)), dim3(kMbThreads), 0, s,
-                       scores, num, den, L, (int)rows, w);
-  }
+  // one workgroup per row; the widest rows get 1024 threads x 64 keys
   if (L <= 4096) {
     hipLaunchKernelGGL((select_row_kernel<256, 16>), dim3((unsigned)rows), dim3(256), 0, s,
                        scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
-                       q_pos0, causal, gh);
+                       q_pos0, causal, hist);
   } else if (L <= 16384) {
     hipLaunchKernelGGL((select_row_kernel<512, 32>), dim3((unsigned)rows), dim3(512), 0, s,
                        scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
-                       q_pos0, causal, gh);
+                       q_pos0, causal, hist);
   } else if (L <= 32768) {
     hipLaunchKernelGGL((select_row_kernel<1024, 32>), dim3((unsigned)rows), dim3(1024), 0, s,
                        scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
-                       q_pos0, causal, gh);
+                       q_pos0, causal, hist);
   } else {
     hipLaunchKernelGGL((select_row_kernel<1024, 64>), dim3((unsigned)rows), dim3(1024), 0, s,
                        scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
-                       q_pos0, causal, gh);
+                       q_pos0, causal, hist);
   }
   return hipGetLastError();
 }

@@ -108,8 +108,9 @@ def check_attend(out_gpu, q, k_cache, v_cache, sets, scale, dtype, heads=None) -
 
 
 def decode_step_gpu(inp: dict, kimp: torch.Tensor, L: int, mode: int, q_imp=None, slot=0,
-                    dense=False) -> dict:
-    """score -> select -> attend on the GPU for one decode layer at context L."""
+                    dense=False, use_hist=True) -> dict:
+    """score -> select -> attend on the GPU for one decode layer at context L (with the
+    scorer's first-digit histogram handed to the selection unless use_hist is False)."""
     w = inp["workload"]
     dev = kimp.device if kimp is not None else inp["k_cache_d"].device
     B, Hkv = w.B, w.Hkv
@@ -120,13 +121,19 @@ def decode_step_gpu(inp: dict, kimp: torch.Tensor, L: int, mode: int, q_imp=None
     else:
         num, den = w.budget_num, w.budget_den
     cap = min(L, (L * num) // den + w.n_sink + w.n_window)
+    hist = torch.zeros(B, Hkv, 1, 2048, dtype=torch.int32, device=dev) if use_hist else None
     if mode == qa.BUTLER_SCORE_RAW:
-        qa.butler_score(mode, q_imp, kimp, scores, Hkv=Hkv, L=L, slot=slot)
+        qa.butler_score(mode, q_imp, kimp, scores, Hkv=Hkv, L=L, slot=slot, radix_hist=hist)
     else:
-        qa.butler_score(mode, q_d, k_d, scores, Hkv=Hkv, L=L, softmax_scale=w.scale)
+        qa.butler_score(mode, q_d, k_d, scores, Hkv=Hkv, L=L, softmax_scale=w.scale,
+                        radix_hist=hist)
     idx = torch.full((B, Hkv, 1, cap), -1, dtype=torch.int32, device=dev)
     count = torch.zeros(B, Hkv, 1, dtype=torch.int32, device=dev)
-    qa.butler_select_topk(scores, num, den, w.n_sink, w.n_window, count, idx=idx)
+    qa.butler_select_topk(scores, num, den, w.n_sink, w.n_window, count, idx=idx,
+                          radix_hist=hist)
+    if hist is not None:
+        torch.cuda.synchronize()
+        assert int(hist.abs().sum()) == 0, "the selection must leave the histogram zeroed"
     out = torch.empty(B, w.Hq, 1, w.D, dtype=torch.float32, device=dev)
     qa.butler_sparse_decode_attn(q_d, k_d, v_d, out, L=L, idx=idx, count=count,
                                  softmax_scale=w.scale)

@@ -49,7 +49,7 @@ def test_project_keys_validation():
 
 def _score(mode=0, dtype=1, q=FAKE, keys=FAKE, scores=FAKE, B=1, Hq=32, Hkv=8, G=1, slot=0,
            Lq=1, Lk=1000, L_cap=1000, dk=32, q_pos0=0, causal=0, scale=0.1, ws=None, n=None):
-    return L.butler_score(None, mode, dtype, q, keys, scores, B, Hq, Hkv, G, slot, Lq, Lk,
+    return L.butler_score(None, mode, dtype, q, keys, scores, None, B, Hq, Hkv, G, slot, Lq, Lk,
                           L_cap, dk, q_pos0, causal, scale, ws, n)
 
 
@@ -72,13 +72,13 @@ def test_score_validation_and_workspace_query():
 def test_select_validation():
     f = L.butler_select_topk
     # cap smaller than min(L, x + sink + window)
-    assert f(None, FAKE, 1, 2, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 567, 0, 0, None,
+    assert f(None, FAKE, None, 1, 2, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 567, 0, 0, None,
              None) == INV
-    assert f(None, FAKE, 1, 0, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
+    assert f(None, FAKE, None, 1, 0, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
              None) == INV                                                  # den = 0
-    assert f(None, FAKE, 1, 2, -1, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
+    assert f(None, FAKE, None, 1, 2, -1, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
              None) == INV                                                  # negative sink
-    assert f(None, FAKE, 1, 2, 4, 64, None, None, FAKE, 1, 8, 1, 1000, 0, 0, 0, None,
+    assert f(None, FAKE, None, 1, 2, 4, 64, None, None, FAKE, 1, 8, 1, 1000, 0, 0, 0, None,
              None) == INV                                                  # no output
 
 

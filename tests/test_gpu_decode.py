@@ -143,3 +143,22 @@ def test_zero_importance_queries_tie_to_lowest_indices():
     idx = r["idx"].cpu().numpy()
     for g in range(w.Hkv):
         assert idx[0, g, 0, :cnt[0, g, 0]].tolist() == want
+
+
+def test_scorer_histogram_matches_selection_without_it():
+    """The selection gives bitwise the same result from the scorer's first-digit
+    histogram as from its own counting pass, on short, mid and long rows."""
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[2]
+    for L in (3000, 9000, 70001):
+        print(f"[hist] L={L}", flush=True)
+        inp = to_device(synthetic.decode_layer(w, 5, L=L))
+        kimp = torch.zeros(w.B, w.Hkv, L, w.dprime, dtype=w.dtype, device="cuda")
+        qa.butler_project_keys(inp["k_cache_d"], inp["w_k_d"], kimp, 0, L)
+        a = decode_step_gpu(inp, kimp, L, qa.BUTLER_SCORE_RAW, q_imp=inp["q_imp_d"], use_hist=True)
+        b = decode_step_gpu(inp, kimp, L, qa.BUTLER_SCORE_RAW, q_imp=inp["q_imp_d"], use_hist=False)
+        torch.cuda.synchronize()
+        for key in ("scores", "idx", "count", "out"):
+            assert torch.equal(a[key], b[key]), (L, key)
+        check_select_exact(a["idx"], a["count"], np64(a["scores"]), w.budget_num, w.budget_den,
+                           w.n_sink, w.n_window)

@@ -75,12 +75,14 @@ def _prefill_case(w, L, chunk):
         Lq = min(chunk, L - c0)
         Lk = c0 + Lq
         scores = torch.empty(w.B, w.Hkv, Lq, Lk, dtype=torch.float32, device=dev)
+        hist = torch.zeros(w.B, w.Hkv, Lq, 2048, dtype=torch.int32, device=dev)
         qa.butler_score(qa.BUTLER_SCORE_RAW, q_imp[:, :, :, c0:c0 + Lq].contiguous(), kimp,
-                        scores, Hkv=w.Hkv, L=Lk, slot=0, q_pos0=c0, causal=True)
+                        scores, Hkv=w.Hkv, L=Lk, slot=0, q_pos0=c0, causal=True,
+                        radix_hist=hist)
         bm = torch.zeros(w.B, w.Hkv, Lq, (Lk + 31) // 32, dtype=torch.int32, device=dev)
         cnt = torch.zeros(w.B, w.Hkv, Lq, dtype=torch.int32, device=dev)
         qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink, w.n_window, cnt,
-                              bitmask=bm, q_pos0=c0, causal=True)
+                              bitmask=bm, q_pos0=c0, causal=True, radix_hist=hist)
         out = torch.empty(w.B, w.Hq, Lq, w.D, dtype=torch.float32, device=dev)
         qa.butler_sparse_decode_attn(q_d[:, :, c0:c0 + Lq].contiguous(), k_d, v_d, out, L=Lk,
                                      bitmask=bm, q_pos0=c0, softmax_scale=w.scale)
