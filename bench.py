@@ -72,6 +72,11 @@ class Layer:
         self.out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
         log(f"  layer replica {layer} at L={L} ready in {time.time() - t0:.1f}s")
 
+    def free(self):
+        """Drop the device buffers (the host copy of the inputs stays)."""
+        for name in ("k", "v", "q", "wk", "qi", "kimp", "scores", "idx", "count", "hist", "out"):
+            setattr(self, name, None)
+
     def calls(self):
         qa, w, L = self.qa, self.w, self.L
         return [
@@ -240,6 +245,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--L", type=int, default=None)
+    ap.add_argument("--copy-cal", action="store_true",
+                    help="run a 256 MiB device copy first (HBM counter calibration)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -252,14 +259,27 @@ def main(argv=None) -> int:
     dev = "cuda:0"
     w = synthetic.WORKLOADS[2]
     L = a.L or w.L
+    if a.copy_cal:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters scale the
+        # counters of the attention kernel to bytes
+        src = torch.randn(64 * 1024 * 1024, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"[bench] {w.name}: L={L}, 8 replicas, steps={a.steps}, warmup={a.warmup}")
     head, layers = run_config(w, L, 8, a.steps, a.warmup, dev)
+    host0 = layers[0]
     log(f"[bench] headline: {json.dumps(head)}")
 
     sweep = []
     if not a.no_sweep:
         for Ls in (131072, 262144):
-            del layers
+            for lay in layers:
+                if lay is not host0:
+                    lay.free()
+            layers = []
             torch.cuda.empty_cache()
             log(f"[bench] sweep L={Ls}")
             r, layers = run_config(w, Ls, 2, max(a.steps // 4, 20), max(a.warmup // 4, 4), dev)
@@ -267,14 +287,14 @@ def main(argv=None) -> int:
                                             "attn_GBps", "kernel_us", "timing")})
             sweep[-1]["step_frac_of_hbm_peak"] = r["step_GBps"] / HBM_PEAK_GBS
             log(f"[bench] sweep result: {json.dumps(sweep[-1])}")
-        del layers
+        for lay in layers:
+            lay.free()
         layers = None
 
     cpu = None
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
-        lay0 = Layer(w, 0, L, dev)
-        cpu = cpu_baseline(lay0)
+        cpu = cpu_baseline(host0)
         log(f"[bench] cpu baseline: {json.dumps(cpu)}")
 
     attn_us = head["kernel_us"]["attn"]
@@ -298,7 +318,7 @@ def main(argv=None) -> int:
                    "L": L, "scorer": "raw", "budget": f"{w.budget_num}/{w.budget_den}",
                    "sink": w.n_sink, "window": w.n_window, "layer_replicas": 8,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "attn_idx_kernel (sparse decode attention)",
+        "roofline": {"bound": "hbm", "kernel": "sparse decode attention call: attn_mfma_kernel + attn_merge_kernel",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": head["attn_bytes"],

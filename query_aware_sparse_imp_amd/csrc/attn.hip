@@ -329,8 +329,14 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
 constexpr int kMfThreads = 256;           // 4 waves
 constexpr int kMfWaves = kMfThreads / 64;
 constexpr int kMfRound = kMfWaves * 16;    // list positions per block round (a tile per wave)
-constexpr int kMfStage = 4096;             // list positions staged in LDS at a time
-constexpr int kMfTargetBlocks = 768;       // about what the GPU keeps resident (3 per CU)
+#ifndef BUTLER_MF_STAGE
+#define BUTLER_MF_STAGE 4096
+#endif
+#ifndef BUTLER_MF_TARGET_BLOCKS
+#define BUTLER_MF_TARGET_BLOCKS 512
+#endif
+constexpr int kMfStage = BUTLER_MF_STAGE;  // list positions staged in LDS at a time
+constexpr int kMfTargetBlocks = BUTLER_MF_TARGET_BLOCKS;  // grid size aimed at (2 per CU)
 
 struct MfTile {
   uint4 k[4], v[4];

@@ -239,7 +239,13 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
                  int causal, uint32_t* hist) {
   constexpr int LPT = DP / Vec16<T>::N;
-  const int tpb = (kRawThreads / LPT) * kRawUnroll;
+  // a tile is what one block-wide step covers (8 loads per thread); a workgroup loops
+  // over enough tiles that a row has at most 64 workgroups -- this bounds the atomics
+  // that the workgroups' histograms send to the same hot bins of a row
+  const int tile = (kRawThreads / LPT) * kRawUnroll;
+  const int tiles = (L + tile - 1) / tile;
+  const int per = (tiles + 63) / 64;
+  const int tpb = tile * per;
   dim3 grid((L + tpb - 1) / tpb, Lq, B * Hkv);
   hipLaunchKernelGGL((score_raw_kernel<T, DP>), grid, dim3(kRawThreads), 0, s, (const T*)q_imp,
                      (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal,
