@@ -161,3 +161,23 @@ template <> __device__ __forceinline__ void unpack16<float>(const Raw16& r, floa
 __device__ __forceinline__ int ticket_take(int* t) {
   return __hip_atomic_fetch_add(t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Sum of a double over aligned groups of N lanes (N in {1, 2, 4, 8}): quad-permute DPP
+// moves of both 32-bit halves, then one xor-4 shuffle for N = 8; every lane of a group
+// ends with the same bits.
+template <int N>
+__device__ __forceinline__ double quad_sum_d(double x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "group of 1, 2, 4 or 8 lanes");
+  if constexpr (N >= 2) {
+    const int lo = __double2loint(x), hi = __double2hiint(x);
+    x += __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false),
+                          __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false));
+  }
+  if constexpr (N >= 4) {
+    const int lo = __double2loint(x), hi = __double2hiint(x);
+    x += __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false),
+                          __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false));
+  }
+  if constexpr (N >= 8) x += __shfl_xor(x, 4);
+  return x;
+}

@@ -25,7 +25,20 @@ namespace butler {
 namespace {
 
 constexpr int kRawThreads = 256;
-constexpr int kRawUnroll = 8;
+#ifndef BUTLER_SCORE_UNROLL
+#define BUTLER_SCORE_UNROLL 8
+#endif
+#ifndef BUTLER_SCORE_ROW_WG
+#define BUTLER_SCORE_ROW_WG 64
+#endif
+constexpr int kRawUnroll = BUTLER_SCORE_UNROLL;
+constexpr int kRawRowWg = BUTLER_SCORE_ROW_WG;
+
+// Raw bytes of one 16-byte piece of every token of a batch.
+template <int U>
+struct RawBatch {
+  uint4 v[U];
+};
 
 template <typename T, int DP>
 __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
@@ -35,6 +48,7 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPT = DP / EPL;           // lanes per token
   constexpr int TPI = kRawThreads / LPT;  // tokens per block-wide step
+  constexpr int U = kRawUnroll;
   const int bg = blockIdx.z, i = blockIdx.y;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int R = Hq / Hkv;
@@ -45,24 +59,21 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   const int tv = min(t1, L_r);
   const T* kb = kimp + (size_t)bg * L_cap * DP + part * EPL;
   float* srow = scores + ((size_t)bg * Lq + i) * L;
-  float kv[kRawUnroll][EPL];
-  auto load_batch = [&](int t) {
+  // batch loads at clamped addresses: no control flow around them
+  auto load_batch = [&](RawBatch<U>& rb, int t) {
 #pragma unroll
-    for (int u = 0; u < kRawUnroll; ++u) {
-      const int tu = t + u * TPI;
-      if (tu < tv) {
-        Vec16<T>::load(kb + (size_t)tu * DP, kv[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) kv[u][e] = 0.f;
-      }
+    for (int u = 0; u < U; ++u) {
+      const int tu = min(t + u * TPI, max(tv - 1, 0));
+      rb.v[u] = *reinterpret_cast<const uint4*>(kb + (size_t)tu * DP);
     }
   };
-  // the first batch of K_imp rows is requested before the group query is summed
-  int t = t0 + sub;
-  if (t < t1) load_batch(t);
   __shared__ double qbar[DP];
   __shared__ uint32_t hist[2048];
+  RawBatch<U> ba, bb;
+  int t = t0 + sub;
+  // the first two batches of K_imp rows are requested before the group query is summed
+  if (t < t1) load_batch(ba, t);
+  if (t + TPI * U < t1) load_batch(bb, t + TPI * U);
   if (radix_hist)
     for (int j = threadIdx.x; j < 2048; j += kRawThreads) hist[j] = 0u;
   if (threadIdx.x < DP) {
@@ -82,23 +93,34 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   double qv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = qbar[part * EPL + e];
-  while (t < t1) {
+  auto consume = [&](const RawBatch<U>& rb, int tb) {
 #pragma unroll
-    for (int u = 0; u < kRawUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
+      Raw16 r16;
+      r16.v = rb.v[u];
+      float kf[EPL];
+      unpack16<T>(r16, kf);
       double acc = 0.0;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc = fma(qv[e], (double)kv[u][e], acc);
-#pragma unroll
-      for (int o = 1; o < LPT; o <<= 1) acc += __shfl_xor(acc, o, 64);
-      const int tu = t + u * TPI;
+      for (int e = 0; e < EPL; ++e) acc = fma(qv[e], (double)kf[e], acc);
+      acc = quad_sum_d<LPT>(acc);
+      const int tu = tb + u * TPI;
       if (part == 0 && tu < t1) {
         const float sc = (tu < L_r) ? (float)acc : neg_inf();
         srow[tu] = sc;
         if (radix_hist && tu < L_r) atomicAdd(&hist[score_key(sc) >> 21], 1u);
       }
     }
-    t += TPI * kRawUnroll;
-    if (t < t1) load_batch(t);
+  };
+  // two batches in flight: the one after next is requested before this one is consumed
+  while (t < t1) {
+    consume(ba, t);
+    t += TPI * U;
+    if (t + TPI * U < t1) load_batch(ba, t + TPI * U);
+    if (t >= t1) break;
+    consume(bb, t);
+    t += TPI * U;
+    if (t + TPI * U < t1) load_batch(bb, t + TPI * U);
   }
   if (radix_hist) {
     __syncthreads();
@@ -239,12 +261,12 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
                  int causal, uint32_t* hist) {
   constexpr int LPT = DP / Vec16<T>::N;
-  // a tile is what one block-wide step covers (8 loads per thread); a workgroup loops
-  // over enough tiles that a row has at most 64 workgroups -- this bounds the atomics
-  // that the workgroups' histograms send to the same hot bins of a row
+  // a tile is what one block-wide step covers (kRawUnroll loads per thread); a workgroup
+  // loops over enough tiles that a row has at most kRawRowWg workgroups -- this bounds the
+  // atomics that the workgroups' histograms send to the same hot bins of a row
   const int tile = (kRawThreads / LPT) * kRawUnroll;
   const int tiles = (L + tile - 1) / tile;
-  const int per = (tiles + 63) / 64;
+  const int per = (tiles + kRawRowWg - 1) / kRawRowWg;
   const int tpb = tile * per;
   dim3 grid((L + tpb - 1) / tpb, Lq, B * Hkv);
   hipLaunchKernelGGL((score_raw_kernel<T, DP>), grid, dim3(kRawThreads), 0, s, (const T*)q_imp,
