@@ -326,41 +326,52 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-constexpr int kMfThreads = 256;           // 4 waves
-constexpr int kMfWaves = kMfThreads / 64;
-constexpr int kMfRound = kMfWaves * 16;    // list positions per block round (a tile per wave)
+#ifndef BUTLER_MF_THREADS
+#define BUTLER_MF_THREADS 512
+#endif
+#ifndef BUTLER_MF_BUF
+#define BUTLER_MF_BUF 2
+#endif
 #ifndef BUTLER_MF_STAGE
 #define BUTLER_MF_STAGE 4096
 #endif
 #ifndef BUTLER_MF_TARGET_BLOCKS
-#define BUTLER_MF_TARGET_BLOCKS 512
+#define BUTLER_MF_TARGET_BLOCKS 256
 #endif
+constexpr int kMfThreads = BUTLER_MF_THREADS;
+constexpr int kMfWaves = kMfThreads / 64;
+constexpr int kMfRound = kMfWaves * 16;    // list positions per block round (a tile per wave)
+constexpr int kMfBuf = BUTLER_MF_BUF;      // tiles per wave in the load ring
 constexpr int kMfStage = BUTLER_MF_STAGE;  // list positions staged in LDS at a time
+constexpr int kMfPad = (2 * kMfBuf - 2) * kMfRound;  // ring prefetch past the stage end
 constexpr int kMfTargetBlocks = BUTLER_MF_TARGET_BLOCKS;  // grid size aimed at (2 per CU)
+static_assert(kMfStage % kMfThreads == 0, "stage is a whole number of block-wide loads");
 
 struct MfTile {
   uint4 k[4], v[4];
-  int tv[4];
 };
 
+// Rows of the tile at list positions base .. base+15: lane (quad, pe) takes K columns
+// kk*32 + 8*quad of row pe, and V columns 8*pe of rows 4*quad + r.  Every position of the
+// staged list holds a valid cache row (past the end: a selected row, masked out of the
+// softmax), so the loads need no guard and the compiler can count them exactly.
 __device__ __forceinline__ void mf_load(MfTile& tl, const int* s_list, int base,
                                         const bf16_t* kb, const bf16_t* vb, int quad, int pe) {
   constexpr int D = 128;
   const int tk = s_list[base + pe];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
-    tl.k[kk] = (tk >= 0) ? *reinterpret_cast<const uint4*>(kb + (long long)tk * D + kk * 32 + 8 * quad)
-                         : make_uint4(0, 0, 0, 0);
+    tl.k[kk] = *reinterpret_cast<const uint4*>(kb + (long long)tk * D + kk * 32 + 8 * quad);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    tl.tv[r] = s_list[base + 4 * quad + r];
-    tl.v[r] = (tl.tv[r] >= 0) ? *reinterpret_cast<const uint4*>(vb + (long long)tl.tv[r] * D + 8 * pe)
-                              : make_uint4(0, 0, 0, 0);
+    const int tv = s_list[base + 4 * quad + r];
+    tl.v[r] = *reinterpret_cast<const uint4*>(vb + (long long)tv * D + 8 * pe);
   }
 }
 
+// lim = how many of rows 4*quad .. 4*quad+3 of the tile are real list entries
 template <int R>
-__device__ __forceinline__ void mf_compute(const MfTile& tl, const bf16x8_t (&qf)[4],
+__device__ __forceinline__ void mf_compute(const MfTile& tl, const bf16x8_t (&qf)[4], int lim,
                                            float scale_log2, float& m, float& l,
                                            float (&acc)[R][8]) {
   f32x4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -371,7 +382,7 @@ __device__ __forceinline__ void mf_compute(const MfTile& tl, const bf16x8_t (&qf
   float z[4], mt = neg_inf();
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    z[r] = (tl.tv[r] >= 0) ? c[r] * scale_log2 : neg_inf();
+    z[r] = (r < lim) ? c[r] * scale_log2 : neg_inf();
     mt = fmaxf(mt, z[r]);
   }
   const float mn = fmaxf(m, mt);
@@ -379,7 +390,7 @@ __device__ __forceinline__ void mf_compute(const MfTile& tl, const bf16x8_t (&qf
   float pz[4], ps = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    pz[r] = (tl.tv[r] >= 0) ? fast_exp2(z[r] - mn) : 0.f;
+    pz[r] = (r < lim) ? fast_exp2(z[r] - mn) : 0.f;
     ps += pz[r];
   }
   l = l * alpha + ps;
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int quad = lane >> 4, pe = lane & 15;
 
-  __shared__ int s_list[kMfStage];
+  __shared__ int s_list[kMfStage + kMfPad];
   __shared__ float s_m[kMfWaves * R], s_l[kMfWaves * R], red_m[R], red_l[R];
   __shared__ float s_acc[kMfWaves * R * D];
   __shared__ float red_acc[R * D];
@@ -453,19 +464,39 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
     const int len = min(kMfStage, p_end - cs);
     const int nr = (len + kMfRound - 1) / kMfRound;
     __syncthreads();
-    for (int j = threadIdx.x; j < nr * kMfRound; j += kMfThreads)
-      // indices outside [0, L_cap) are clamped so a bad list never reads past the cache
-      s_list[j] = (j < len) ? (int)min((unsigned)irow[cs + j], (unsigned)(L_cap - 1)) : -1;
+    // the whole stage of indices is requested at once; positions past its end repeat its
+    // last entry, and indices outside [0, L_cap) are clamped so a bad list never reads
+    // past the cache
+    constexpr int U = kMfStage / kMfThreads;
+    const int last = (int)min((unsigned)irow[cs + len - 1], (unsigned)(L_cap - 1));
+    int iv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) iv[u] = irow[cs + min((int)threadIdx.x + u * kMfThreads, len - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      s_list[threadIdx.x + u * kMfThreads] = (int)min((unsigned)iv[u], (unsigned)(L_cap - 1));
+    for (int j = threadIdx.x; j < kMfPad; j += kMfThreads) s_list[kMfStage + j] = last;
     __syncthreads();
-    // one tile per wave per round; the next tile's rows are in flight during the compute
-    MfTile ta, tb;
-    mf_load(ta, s_list, wid * 16, kb, vb, quad, pe);
-    for (int r = 0; r < nr; r += 2) {
-      if (r + 1 < nr) mf_load(tb, s_list, (r + 1) * kMfRound + wid * 16, kb, vb, quad, pe);
-      mf_compute<R>(ta, qf, scale_log2, m, l, acc);
-      if (r + 2 < nr) mf_load(ta, s_list, (r + 2) * kMfRound + wid * 16, kb, vb, quad, pe);
-      if (r + 1 < nr) mf_compute<R>(tb, qf, scale_log2, m, l, acc);
+    // a ring of kMfBuf tiles per wave: kMfBuf - 1 tiles are in flight during each compute.
+    // Round rho lives in t[rho % kMfBuf]; the main loop has no branch, so every wait is for
+    // exactly one tile, and the last nr % kMfBuf rounds are already loaded when it ends.
+    MfTile t[kMfBuf];
+    const int w0 = wid * 16;
+    const int lim0 = len - w0 - 4 * quad;
+#pragma unroll
+    for (int b = 0; b < kMfBuf - 1; ++b) mf_load(t[b], s_list, b * kMfRound + w0, kb, vb, quad, pe);
+    const int nmain = nr - nr % kMfBuf;
+    for (int r = 0; r < nmain; r += kMfBuf) {
+#pragma unroll
+      for (int b = 0; b < kMfBuf; ++b) {
+        mf_load(t[(b + kMfBuf - 1) % kMfBuf], s_list, (r + b + kMfBuf - 1) * kMfRound + w0, kb, vb,
+                quad, pe);
+        mf_compute<R>(t[b], qf, lim0 - (r + b) * kMfRound, scale_log2, m, l, acc);
+      }
     }
+#pragma unroll
+    for (int b = 0; b < kMfBuf - 1; ++b)
+      if (nmain + b < nr) mf_compute<R>(t[b], qf, lim0 - (nmain + b) * kMfRound, scale_log2, m, l, acc);
   }
   // hand the per-row streams to the shared reduction: every lane of a row needs the
   // (m, l) of every head, which live in lane h of the row

@@ -19,12 +19,13 @@
 //   0  (only without the scorer's histogram) histogram of key bits 31..21
 //   1  every chunk derives the first-digit bin b1, counts its tokens that are surely
 //      selected (digit above b1, or a sink / window token) and appends the keys whose
-//      digit is b1 to a candidate list -- for scores of any spread only a sliver of the
-//      row
-//   2  one workgroup per row resolves bits 20..0 of tau over the candidates (in LDS when
-//      they fit), the tie quota and the lowest-index tie cut, then every chunk's output
-//      offset and the row count, and clears the histogram and the candidate counter
-//   3  every chunk emits its bitmask words and its indices at its offset.
+//      digit is b1 to the row's candidate ring -- for scores of any spread only a sliver
+//      of the row
+//   2  every chunk resolves tau and the tie cut from the row's candidates (the same work
+//      in every workgroup of the row: cheaper than a kernel boundary while the candidates
+//      are few), derives its output offset from the per-chunk counts and emits its
+//      bitmask words and indices; the chunk-0 workgroup writes the row count and clears
+//      the histogram.
 //
 // Other rows (short decode rows, every causal prefill row): one workgroup per row holds
 //   the row's keys in VGPRs (up to 64 per thread, strided so that a wave's ballot covers
@@ -240,28 +241,27 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
 constexpr int kMbThreads = 256;
 constexpr int kMbChunk = 2048;           // tokens per workgroup, 8 per thread
 constexpr int kMbMaxChunks = 4096;       // rows of up to 8M tokens
-constexpr int kResThreads = 1024;
-constexpr int kResStage = 12288;         // candidates staged in LDS (more: read from memory)
+constexpr int kFinStage = 2048;          // candidates staged in LDS (more: read from memory)
 
 struct RowState {
-  uint32_t tau;
-  int tie_cut;
+  uint32_t b1;  // first-digit bin of the x-th largest key
+  int need;     // rank of the x-th largest key inside that bin (1-based)
 };
 
 struct MbWs {
-  uint32_t* hist1;   // [rows][2048]   first-digit counts, zero between calls
-  uint32_t* ccount;  // [rows]         candidate counter, zero between calls
-  RowState* state;   // [rows]
-  int* defcnt;       // [rows][nchunk]
-  int* offs;         // [rows][nchunk]
-  uint2* cand;       // [rows][L]  (key, index | sink/window flag << 31)
+  uint32_t* hist1;               // [rows][2048]   first-digit counts, zero between calls
+  unsigned long long* ccount;    // [rows]         running candidate counter (never reset)
+  RowState* state;               // [rows]
+  int* defcnt;                   // [rows][nchunk] tokens of the chunk that are surely selected
+  int* ncand;                    // [rows][nchunk] candidates the chunk appended
+  uint2* cand;                   // [rows][L]      ring of (key, index | sink/window flag << 31)
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t mb_bytes(long long rows, int L) {
   const long long nchunk = (L + kMbChunk - 1) / kMbChunk;
-  return al256(rows * 2048 * 4) + al256(rows * 4) + al256(rows * sizeof(RowState)) +
+  return al256(rows * 2048 * 4) + al256(rows * 8) + al256(rows * sizeof(RowState)) +
          2 * al256(rows * nchunk * 4) + al256((size_t)rows * L * sizeof(uint2));
 }
 
@@ -269,11 +269,11 @@ MbWs carve(void* ws, long long rows, int L) {
   const long long nchunk = (L + kMbChunk - 1) / kMbChunk;
   char* p = (char*)ws;
   MbWs w;
-  w.hist1 = (uint32_t*)p;     p += al256(rows * 2048 * sizeof(uint32_t));
-  w.ccount = (uint32_t*)p;    p += al256(rows * sizeof(uint32_t));
-  w.state = (RowState*)p;     p += al256(rows * sizeof(RowState));
-  w.defcnt = (int*)p;         p += al256(rows * nchunk * sizeof(int));
-  w.offs = (int*)p;           p += al256(rows * nchunk * sizeof(int));
+  w.hist1 = (uint32_t*)p;                 p += al256(rows * 2048 * sizeof(uint32_t));
+  w.ccount = (unsigned long long*)p;      p += al256(rows * 8);
+  w.state = (RowState*)p;                 p += al256(rows * sizeof(RowState));
+  w.defcnt = (int*)p;                     p += al256(rows * nchunk * sizeof(int));
+  w.ncand = (int*)p;                      p += al256(rows * nchunk * sizeof(int));
   w.cand = (uint2*)p;
   return w;
 }
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_hist1_kernel(const float* __res
 
 // Chunk pass: every workgroup derives the first-digit bin b1 from the row's histogram,
 // counts its tokens that are surely selected (digit above b1, or sink / window) and
-// appends the keys whose first digit is b1 to the row's candidate list.
+// appends the keys whose first digit is b1 to the row's candidate ring.
 __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __restrict__ scores,
                                                              int num, int den, int n_sink,
                                                              int n_window, int L, int rows,
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
   const int mode = row_mode(L, num, den, k);
   __shared__ uint32_t h[2048];
   __shared__ int tmp[kMbThreads / 64];
-  __shared__ int sh_bin, sh_need, sh_base;
+  __shared__ int sh_bin, sh_need, sh_start;
   const int t0 = chunk * kMbChunk + threadIdx.x * 8;
   uint32_t key[8];
   const int nv = load_keys8(scores + (long long)row * L, t0, L, key);
@@ -340,6 +340,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
     __syncthreads();
     find_bin_from_top<kMbThreads>(h, 2048, k, tmp, &sh_bin, &sh_need);
     b1 = (uint32_t)sh_bin;
+    if (chunk == 0 && threadIdx.x == 0) w.state[row] = RowState{b1, sh_need};
   }
   const int w_lo = max(0, L - n_window);
   int ndef = 0, ncand = 0;
@@ -361,157 +362,204 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
   const int cpos = block_exclusive_sum<kMbThreads>(ncand, tot_cand, tmp);
   if (threadIdx.x == 0) {
     w.defcnt[(long long)row * nchunk + chunk] = tot_def;
-    sh_base = tot_cand ? (int)atomicAdd(&w.ccount[row], (uint32_t)tot_cand) : 0;
+    w.ncand[(long long)row * nchunk + chunk] = tot_cand;
+    sh_start = tot_cand ? (int)(atomicAdd(&w.ccount[row], (unsigned long long)tot_cand) %
+                                (unsigned long long)L)
+                        : 0;
   }
   __syncthreads();
   if (ncand) {
     uint2* crow = w.cand + (long long)row * L;
-    int pos = sh_base + cpos;
+    int pos = sh_start + cpos;
+    if (pos >= L) pos -= L;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j >= nv || (key[j] >> 21) != b1) continue;
       const int t = t0 + j;
       const uint32_t flag = (t < n_sink || t >= w_lo) ? 0x80000000u : 0u;
-      crow[pos++] = make_uint2(key[j], (uint32_t)t | flag);
+      crow[pos] = make_uint2(key[j], (uint32_t)t | flag);
+      if (++pos == L) pos = 0;
     }
   }
 }
 
-// Row pass (one workgroup per row): the remaining 21 bits of tau and the tie cut from the
-// candidates (staged in LDS when they fit), then every chunk's output offset and the row
-// count; clears the histogram and the candidate counter for the next call.
-__global__ __launch_bounds__(kResThreads) void mb_resolve_kernel(int num, int den, int L,
-                                                                 int nchunk,
-                                                                 int32_t* __restrict__ count,
-                                                                 uint32_t* __restrict__ ghist,
-                                                                 MbWs w) {
-  const int row = blockIdx.x;
-  int k;
-  const int mode = row_mode(L, num, den, k);
-  __shared__ uint32_t h[2048];
-  __shared__ int cnt[kMbMaxChunks];
-  __shared__ uint32_t s_key[kResStage], s_id[kResStage];
-  __shared__ int tmp[kResThreads / 64];
-  __shared__ int sh_bin, sh_need, sh_ties;
-  uint32_t* gh = ghist + (long long)row * 2048;
-  const int n = (int)w.ccount[row];
-  const uint2* crow = w.cand + (long long)row * L;
-  const bool staged = n <= kResStage;
-  if (staged) {
-    for (int j = threadIdx.x; j < n; j += kResThreads) {
-      const uint2 c = crow[j];
-      s_key[j] = c.x;
-      s_id[j] = c.y;
-    }
+// Block-wide sums of three ints over the kMbThreads threads; every thread gets the totals.
+__device__ __forceinline__ int3 block_sum3(int a, int b, int c, int3* tmp) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o);
+    b += __shfl_xor(b, o);
+    c += __shfl_xor(c, o);
   }
-  auto ckey = [&](int j) { return staged ? s_key[j] : crow[j].x; };
-  auto cid = [&](int j) { return staged ? s_id[j] : crow[j].y; };
-  uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;
-  int tie_cut = -1;
-  if (mode == kModeNormal) {
-    for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = gh[j];
-    __syncthreads();
-    find_bin_from_top<kResThreads>(h, 2048, k, tmp, &sh_bin, &sh_need);
-    const uint32_t b1 = (uint32_t)sh_bin;
-    int need = sh_need;
-    // bits 20..10, then 9..0, over the candidates (all have first digit b1)
-    uint32_t prefix = b1 << 21, pmask = 0xffe00000u;
-    const int shifts[2] = {10, 0};
-    const int bins[2] = {2048, 1024};
-    for (int p = 0; p < 2; ++p) {
-      __syncthreads();
-      for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = 0u;
-      __syncthreads();
-      for (int j = threadIdx.x; j < n; j += kResThreads) {
-        const uint32_t key = ckey(j);
-        if ((key & pmask) == prefix) atomicAdd(&h[(key >> shifts[p]) & (uint32_t)(bins[p] - 1)], 1u);
-      }
-      __syncthreads();
-      find_bin_from_top<kResThreads>(h, bins[p], need, tmp, &sh_bin, &sh_need);
-      prefix |= (uint32_t)sh_bin << shifts[p];
-      pmask |= (uint32_t)(bins[p] - 1) << shifts[p];
-      need = sh_need;
-    }
-    tau = prefix;
-    const int need3 = need;   // keys equal to tau that the budget takes
-    if (threadIdx.x == 0) sh_ties = 0;
-    __syncthreads();
-    int mine = 0;
-    for (int j = threadIdx.x; j < n; j += kResThreads) mine += (ckey(j) == tau) ? 1 : 0;
-    if (mine) atomicAdd(&sh_ties, mine);
-    __syncthreads();
-    if (need3 >= sh_ties) {
-      tie_cut = 0x7fffffff;
-    } else {
-      // the need3-th smallest index among the keys equal to tau: bits 30..20, 19..10, 9..0
-      uint32_t pre = 0u, pm = 0u;
-      int nd = need3;
-      const int ish[3] = {20, 10, 0};
-      const uint32_t iw[3] = {2048u, 1024u, 1024u};
-      for (int p = 0; p < 3; ++p) {
-        __syncthreads();
-        for (int j = threadIdx.x; j < 2048; j += kResThreads) h[j] = 0u;
-        __syncthreads();
-        for (int j = threadIdx.x; j < n; j += kResThreads) {
-          const uint32_t t = cid(j) & 0x7fffffffu;
-          if (ckey(j) == tau && (t & pm) == pre) atomicAdd(&h[(t >> ish[p]) & (iw[p] - 1u)], 1u);
-        }
-        __syncthreads();
-        find_bin_from_bottom<kResThreads>(h, 2048, nd, tmp, &sh_bin, &sh_need);
-        pre |= (uint32_t)sh_bin << ish[p];
-        pm |= (iw[p] - 1u) << ish[p];
-        nd = sh_need;
-      }
-      tie_cut = (int)pre;
-    }
-  }
-  // per-chunk selected counts -> offsets, row count
-  for (int c = threadIdx.x; c < nchunk; c += kResThreads) cnt[c] = w.defcnt[(long long)row * nchunk + c];
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = make_int3(a, b, c);
   __syncthreads();
-  if (mode == kModeNormal) {
-    for (int j = threadIdx.x; j < n; j += kResThreads) {
-      const uint32_t id = cid(j);
-      if (id & 0x80000000u) continue;  // sink / window tokens are already counted
-      const uint32_t key = ckey(j);
-      const int t = (int)id;
-      if (key > tau || (key == tau && t <= tie_cut)) atomicAdd(&cnt[t / kMbChunk], 1);
-    }
+  int3 r = make_int3(0, 0, 0);
+#pragma unroll
+  for (int w = 0; w < kMbThreads / 64; ++w) {
+    r.x += tmp[w].x;
+    r.y += tmp[w].y;
+    r.z += tmp[w].z;
   }
   __syncthreads();
-  int carry = 0;
-  for (int c0 = 0; c0 < nchunk; c0 += kResThreads) {
-    const int c = c0 + threadIdx.x;
-    const int v = (c < nchunk) ? cnt[c] : 0;
-    int tot;
-    const int ex = block_exclusive_sum<kResThreads>(v, tot, tmp);
-    if (c < nchunk) w.offs[(long long)row * nchunk + c] = carry + ex;
-    carry += tot;
-  }
-  // clear the accumulators for the next call
-  for (int j = threadIdx.x; j < 2048; j += kResThreads) gh[j] = 0u;
-  if (threadIdx.x == 0) {
-    count[row] = carry;
-    w.state[row].tau = tau;
-    w.state[row].tie_cut = tie_cut;
-    w.ccount[row] = 0u;
-  }
+  return r;
 }
 
-__global__ __launch_bounds__(kMbThreads) void mb_emit_kernel(
+// Whether candidate c comes before (key kj, index ij) in (key desc, index asc) order.
+__device__ __forceinline__ int precedes(uint2 c, uint32_t kj, uint32_t ij) {
+  const uint32_t ii = c.y & 0x7fffffffu;
+  return (c.x > kj || (c.x == kj && ii < ij)) ? 1 : 0;
+}
+
+// Finishing pass, one workgroup per chunk: every workgroup of a row resolves the same tau
+// and tie cut from the row's candidates (a rank count when they are few, else the radix
+// over bits 20..0 and the index radix of the ties), sums the sure and the selected
+// candidate counts of the chunks before its own into its output offset, and emits its
+// tokens.  The chunk-0 workgroup writes the row count and clears the row's histogram
+// (nothing in this kernel reads it).
+__global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
     const float* __restrict__ scores, int num, int den, int n_sink, int n_window, int L,
-    int rows, int cap, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask, MbWs w) {
+    int rows, int cap, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask,
+    int32_t* __restrict__ count, uint32_t* __restrict__ ghist, MbWs w) {
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
   const int nchunk = gridDim.x / rows;
   int k;
   const int mode = row_mode(L, num, den, k);
+  __shared__ uint32_t h[2048];
+  __shared__ uint2 s_c[kFinStage];
   __shared__ int tmp[kMbThreads / 64];
+  __shared__ int3 tmp3[kMbThreads / 64];
+  __shared__ int sh_bin, sh_need, sh_tie;
+  __shared__ uint32_t sh_tau;
   __shared__ uint8_t bytes[kMbThreads];
-  const uint32_t tau = w.state[row].tau;
-  const int tie_cut = w.state[row].tie_cut;
   const int w_lo = max(0, L - n_window);
-  const int t0 = chunk * kMbChunk + threadIdx.x * 8;
+  const int c_lo = chunk * kMbChunk;
+  const int t0 = c_lo + threadIdx.x * 8;
   uint32_t key[8];
   const int nv = load_keys8(scores + (long long)row * L, t0, L, key);
+  // the row's state and candidate counter are requested with the per-chunk counts
+  RowState st = {0u, 0};
+  unsigned long long end = 0ull;
+  if (mode == kModeNormal) {
+    st = w.state[row];
+    end = w.ccount[row];
+  }
+  int n_loc = 0, def_all = 0, def_before = 0;
+  for (int c = threadIdx.x; c < nchunk; c += kMbThreads) {
+    const int d = w.defcnt[(long long)row * nchunk + c];
+    def_all += d;
+    def_before += (c < chunk) ? d : 0;
+    n_loc += w.ncand[(long long)row * nchunk + c];
+  }
+  const int3 sums = block_sum3(n_loc, def_all, def_before, tmp3);
+  const int n = sums.x;
+  def_all = sums.y;
+  def_before = sums.z;
+  int tot;
+  if (chunk == 0) {
+    uint32_t* gh = ghist + (long long)row * 2048;
+    for (int j = threadIdx.x; j < 2048; j += kMbThreads) gh[j] = 0u;
+  }
+  uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;
+  int tie_cut = -1;
+  int sel_all = 0, sel_before = 0;   // selected candidates that are not sink / window
+  if (mode == kModeNormal && n > 0) {
+    const int base = (int)((end - (unsigned long long)n) % (unsigned long long)L);
+    const uint2* crow = w.cand + (long long)row * L;
+    auto at = [&](int j) {
+      const int p = base + j;
+      return crow[p >= L ? p - L : p];
+    };
+    const bool staged = n <= kFinStage;
+    if (staged) {
+      for (int j = threadIdx.x; j < n; j += kMbThreads) s_c[j] = at(j);
+    }
+    __syncthreads();
+    auto ckey = [&](int j) { return staged ? s_c[j].x : at(j).x; };
+    auto cid = [&](int j) { return staged ? s_c[j].y : at(j).y; };
+    if (n <= kMbThreads) {
+      // rank of each candidate in (key desc, index asc) order; the one of rank need-1 is
+      // the last token the budget takes
+      if ((int)threadIdx.x < n) {
+        const uint2 me = s_c[threadIdx.x];
+        const uint32_t kj = me.x, ij = me.y & 0x7fffffffu;
+        int rank = 0, i = 0;
+        for (; i + 4 <= n; i += 4) {
+          const uint2 c0 = s_c[i], c1 = s_c[i + 1], c2 = s_c[i + 2], c3 = s_c[i + 3];
+          rank += precedes(c0, kj, ij) + precedes(c1, kj, ij) + precedes(c2, kj, ij) +
+                  precedes(c3, kj, ij);
+        }
+        for (; i < n; ++i) rank += precedes(s_c[i], kj, ij);
+        if (rank == st.need - 1) {
+          sh_tau = kj;
+          sh_tie = (int)ij;
+        }
+      }
+      __syncthreads();
+      tau = sh_tau;
+      tie_cut = sh_tie;
+    } else {
+      // bits 20..10, then 9..0, over the candidates (all have first digit b1)
+      uint32_t prefix = st.b1 << 21, pmask = 0xffe00000u;
+      int need = st.need;
+      const int shifts[2] = {10, 0};
+      const int bins[2] = {2048, 1024};
+      for (int p = 0; p < 2; ++p) {
+        for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
+        __syncthreads();
+        for (int j = threadIdx.x; j < n; j += kMbThreads) {
+          const uint32_t kk = ckey(j);
+          if ((kk & pmask) == prefix) atomicAdd(&h[(kk >> shifts[p]) & (uint32_t)(bins[p] - 1)], 1u);
+        }
+        __syncthreads();
+        find_bin_from_top<kMbThreads>(h, bins[p], need, tmp, &sh_bin, &sh_need);
+        prefix |= (uint32_t)sh_bin << shifts[p];
+        pmask |= (uint32_t)(bins[p] - 1) << shifts[p];
+        need = sh_need;
+      }
+      tau = prefix;
+      int mine = 0;
+      for (int j = threadIdx.x; j < n; j += kMbThreads) mine += (ckey(j) == tau) ? 1 : 0;
+      int ties;
+      block_exclusive_sum<kMbThreads>(mine, ties, tmp);
+      if (need >= ties) {
+        tie_cut = 0x7fffffff;
+      } else {
+        // the need-th smallest index among the keys equal to tau: bits 30..20, 19..10, 9..0
+        uint32_t pre = 0u, pm = 0u;
+        int nd = need;
+        const int ish[3] = {20, 10, 0};
+        const uint32_t iw[3] = {2048u, 1024u, 1024u};
+        for (int p = 0; p < 3; ++p) {
+          for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
+          __syncthreads();
+          for (int j = threadIdx.x; j < n; j += kMbThreads) {
+            const uint32_t t = cid(j) & 0x7fffffffu;
+            if (ckey(j) == tau && (t & pm) == pre) atomicAdd(&h[(t >> ish[p]) & (iw[p] - 1u)], 1u);
+          }
+          __syncthreads();
+          find_bin_from_bottom<kMbThreads>(h, 2048, nd, tmp, &sh_bin, &sh_need);
+          pre |= (uint32_t)sh_bin << ish[p];
+          pm |= (iw[p] - 1u) << ish[p];
+          nd = sh_need;
+        }
+        tie_cut = (int)pre;
+      }
+    }
+    for (int j = threadIdx.x; j < n; j += kMbThreads) {
+      const uint32_t id = cid(j);
+      if (id & 0x80000000u) continue;  // sink / window tokens are counted as sure
+      const uint32_t kk = ckey(j);
+      const int t = (int)id;
+      if (kk > tau || (kk == tau && t <= tie_cut)) {
+        ++sel_all;
+        sel_before += (t < c_lo) ? 1 : 0;
+      }
+    }
+    const int3 ss = block_sum3(sel_all, sel_before, 0, tmp3);
+    sel_all = ss.x;
+    sel_before = ss.y;
+  }
+  if (chunk == 0 && threadIdx.x == 0) count[row] = def_all + sel_all;
   uint32_t sel = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -522,10 +570,9 @@ __global__ __launch_bounds__(kMbThreads) void mb_emit_kernel(
     else if (mode == kModeNormal) s = s || key[j] > tau || (key[j] == tau && t <= tie_cut);
     sel |= (uint32_t)s << j;
   }
-  int tot;
   const int ex = block_exclusive_sum<kMbThreads>(__popc(sel), tot, tmp);
   if (idx) {
-    int pos = w.offs[(long long)row * nchunk + chunk] + ex;
+    int pos = def_before + sel_before + ex;
     int32_t* irow = idx + (long long)row * cap;
     for (uint32_t e = sel; e; e &= e - 1) {
       if (pos < cap) irow[pos] = t0 + (__ffs(e) - 1);
@@ -573,10 +620,8 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
     }
     hipLaunchKernelGGL(mb_cand_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, n_sink,
                        n_window, L, (int)rows, (const uint32_t*)gh, w);
-    hipLaunchKernelGGL(mb_resolve_kernel, dim3((unsigned)rows), dim3(kResThreads), 0, s, num,
-                       den, L, nchunk, count, gh, w);
-    hipLaunchKernelGGL(mb_emit_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, n_sink,
-                       n_window, L, (int)rows, cap, idx, bitmask, w);
+    hipLaunchKernelGGL(mb_finish_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, n_sink,
+                       n_window, L, (int)rows, cap, idx, bitmask, count, gh, w);
     return hipGetLastError();
   }
   // one workgroup per row; the widest rows get 1024 threads x 64 keys
