@@ -15,17 +15,18 @@
 // come from the scorer (an optional per-row histogram of the top 11 key bits, see
 // butler_score), which saves one pass over the scores.  Two schedules:
 //
-// Decode rows longer than 4096 tokens: kernels over 2048-token chunks
+// Decode rows longer than 4096 tokens: kernels over chunks of 256 threads x 8 or 16 keys
 //   0  (only without the scorer's histogram) histogram of key bits 31..21
 //   1  every chunk derives the first-digit bin b1, counts its tokens that are surely
 //      selected (digit above b1, or a sink / window token) and appends the keys whose
 //      digit is b1 to the row's candidate ring -- for scores of any spread only a sliver
 //      of the row
-//   2  every chunk resolves tau and the tie cut from the row's candidates (the same work
-//      in every workgroup of the row: cheaper than a kernel boundary while the candidates
-//      are few), derives its output offset from the per-chunk counts and emits its
-//      bitmask words and indices; the chunk-0 workgroup writes the row count and clears
-//      the histogram.
+//   2  every wave of every chunk resolves tau and the tie cut from the row's candidates
+//      on its own with ballot counts, bit by bit (the same work everywhere: cheaper than
+//      a kernel boundary while the candidates are few; past 2048 candidates the whole
+//      workgroup runs radix passes), derives its output offset from the per-chunk counts
+//      and emits its bitmask words and indices through 64-token ballot words; the chunk-0
+//      workgroup writes the row count and clears the histogram.
 //
 // Other rows (short decode rows, every causal prefill row): one workgroup per row holds
 //   the row's keys in VGPRs (up to 64 per thread, strided so that a wave's ballot covers
@@ -34,6 +35,8 @@
 //   block-wide scans over the words (tie ranks, then output positions).
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace butler {
 namespace {
@@ -235,153 +238,11 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// decode rows longer than 4096 tokens: three (or four) kernels over 2048-token chunks
+// decode rows longer than 4096 tokens: two (or three) kernels over token chunks
 // ---------------------------------------------------------------------------
 
 constexpr int kMbThreads = 256;
-constexpr int kMbChunk = 2048;           // tokens per workgroup, 8 per thread
-constexpr int kMbMaxChunks = 4096;       // rows of up to 8M tokens
-constexpr int kFinStage = 2048;          // candidates staged in LDS (more: read from memory)
-
-struct RowState {
-  uint32_t b1;  // first-digit bin of the x-th largest key
-  int need;     // rank of the x-th largest key inside that bin (1-based)
-};
-
-struct MbWs {
-  uint32_t* hist1;               // [rows][2048]   first-digit counts, zero between calls
-  unsigned long long* ccount;    // [rows]         running candidate counter (never reset)
-  RowState* state;               // [rows]
-  int* defcnt;                   // [rows][nchunk] tokens of the chunk that are surely selected
-  int* ncand;                    // [rows][nchunk] candidates the chunk appended
-  uint2* cand;                   // [rows][L]      ring of (key, index | sink/window flag << 31)
-};
-
-size_t al256(size_t x) { return (x + 255) / 256 * 256; }
-
-size_t mb_bytes(long long rows, int L) {
-  const long long nchunk = (L + kMbChunk - 1) / kMbChunk;
-  return al256(rows * 2048 * 4) + al256(rows * 8) + al256(rows * sizeof(RowState)) +
-         2 * al256(rows * nchunk * 4) + al256((size_t)rows * L * sizeof(uint2));
-}
-
-MbWs carve(void* ws, long long rows, int L) {
-  const long long nchunk = (L + kMbChunk - 1) / kMbChunk;
-  char* p = (char*)ws;
-  MbWs w;
-  w.hist1 = (uint32_t*)p;                 p += al256(rows * 2048 * sizeof(uint32_t));
-  w.ccount = (unsigned long long*)p;      p += al256(rows * 8);
-  w.state = (RowState*)p;                 p += al256(rows * sizeof(RowState));
-  w.defcnt = (int*)p;                     p += al256(rows * nchunk * sizeof(int));
-  w.ncand = (int*)p;                      p += al256(rows * nchunk * sizeof(int));
-  w.cand = (uint2*)p;
-  return w;
-}
-
-// The 8 keys of tokens t0 .. t0+7; returns how many exist (t < L).
-__device__ __forceinline__ int load_keys8(const float* s, int t0, int L, uint32_t (&key)[8]) {
-  const int nv = max(0, min(8, L - t0));
-  if (nv == 8 && ((((uintptr_t)(s + t0)) & 15u) == 0)) {
-    const float4 a = *reinterpret_cast<const float4*>(s + t0);
-    const float4 b = *reinterpret_cast<const float4*>(s + t0 + 4);
-    key[0] = score_key(a.x); key[1] = score_key(a.y); key[2] = score_key(a.z);
-    key[3] = score_key(a.w); key[4] = score_key(b.x); key[5] = score_key(b.y);
-    key[6] = score_key(b.z); key[7] = score_key(b.w);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) key[j] = score_key(s[min(t0 + j, L - 1)]);
-  }
-  return nv;
-}
-
-// first-digit histogram, when the scorer did not produce it
-__global__ __launch_bounds__(kMbThreads) void mb_hist1_kernel(const float* __restrict__ scores,
-                                                              int num, int den, int L, int rows,
-                                                              uint32_t* __restrict__ ghist) {
-  const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
-  int k;
-  if (row_mode(L, num, den, k) != kModeNormal) return;
-  __shared__ uint32_t h[2048];
-  for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
-  __syncthreads();
-  uint32_t key[8];
-  const int nv = load_keys8(scores + (long long)row * L, chunk * kMbChunk + threadIdx.x * 8, L, key);
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < nv) atomicAdd(&h[key[j] >> 21], 1u);
-  __syncthreads();
-  uint32_t* gh = ghist + (long long)row * 2048;
-  for (int j = threadIdx.x; j < 2048; j += kMbThreads)
-    if (h[j]) atomicAdd(&gh[j], h[j]);
-}
-
-// Chunk pass: every workgroup derives the first-digit bin b1 from the row's histogram,
-// counts its tokens that are surely selected (digit above b1, or sink / window) and
-// appends the keys whose first digit is b1 to the row's candidate ring.
-__global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __restrict__ scores,
-                                                             int num, int den, int n_sink,
-                                                             int n_window, int L, int rows,
-                                                             const uint32_t* __restrict__ ghist,
-                                                             MbWs w) {
-  const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
-  const int nchunk = gridDim.x / rows;
-  int k;
-  const int mode = row_mode(L, num, den, k);
-  __shared__ uint32_t h[2048];
-  __shared__ int tmp[kMbThreads / 64];
-  __shared__ int sh_bin, sh_need, sh_start;
-  const int t0 = chunk * kMbChunk + threadIdx.x * 8;
-  uint32_t key[8];
-  const int nv = load_keys8(scores + (long long)row * L, t0, L, key);
-  uint32_t b1 = 0;
-  if (mode == kModeNormal) {
-    const uint32_t* gh = ghist + (long long)row * 2048;
-    for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = gh[j];
-    __syncthreads();
-    find_bin_from_top<kMbThreads>(h, 2048, k, tmp, &sh_bin, &sh_need);
-    b1 = (uint32_t)sh_bin;
-    if (chunk == 0 && threadIdx.x == 0) w.state[row] = RowState{b1, sh_need};
-  }
-  const int w_lo = max(0, L - n_window);
-  int ndef = 0, ncand = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= nv) continue;
-    const int t = t0 + j;
-    const bool forced = t < n_sink || t >= w_lo;
-    if (mode == kModeNormal) {
-      const uint32_t top = key[j] >> 21;
-      ndef += (forced || top > b1) ? 1 : 0;
-      ncand += (top == b1) ? 1 : 0;
-    } else {
-      ndef += (forced || mode == kModeAll) ? 1 : 0;
-    }
-  }
-  int tot_def, tot_cand;
-  block_exclusive_sum<kMbThreads>(ndef, tot_def, tmp);
-  const int cpos = block_exclusive_sum<kMbThreads>(ncand, tot_cand, tmp);
-  if (threadIdx.x == 0) {
-    w.defcnt[(long long)row * nchunk + chunk] = tot_def;
-    w.ncand[(long long)row * nchunk + chunk] = tot_cand;
-    sh_start = tot_cand ? (int)(atomicAdd(&w.ccount[row], (unsigned long long)tot_cand) %
-                                (unsigned long long)L)
-                        : 0;
-  }
-  __syncthreads();
-  if (ncand) {
-    uint2* crow = w.cand + (long long)row * L;
-    int pos = sh_start + cpos;
-    if (pos >= L) pos -= L;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= nv || (key[j] >> 21) != b1) continue;
-      const int t = t0 + j;
-      const uint32_t flag = (t < n_sink || t >= w_lo) ? 0x80000000u : 0u;
-      crow[pos] = make_uint2(key[j], (uint32_t)t | flag);
-      if (++pos == L) pos = 0;
-    }
-  }
-}
+constexpr int kMbWaves = kMbThreads / 64;
 
 // Block-wide sums of three ints over the kMbThreads threads; every thread gets the totals.
 __device__ __forceinline__ int3 block_sum3(int a, int b, int c, int3* tmp) {
@@ -404,57 +265,439 @@ __device__ __forceinline__ int3 block_sum3(int a, int b, int c, int3* tmp) {
   return r;
 }
 
-// Whether candidate c comes before (key kj, index ij) in (key desc, index asc) order.
-__device__ __forceinline__ int precedes(uint2 c, uint32_t kj, uint32_t ij) {
-  const uint32_t ii = c.y & 0x7fffffffu;
-  return (c.x > kj || (c.x == kj && ii < ij)) ? 1 : 0;
+#ifndef BUTLER_SEL_KPT_LO
+#define BUTLER_SEL_KPT_LO 8
+#endif
+#ifndef BUTLER_SEL_KPT_HI
+#define BUTLER_SEL_KPT_HI 16
+#endif
+#ifndef BUTLER_SEL_KPT_SPLIT
+#define BUTLER_SEL_KPT_SPLIT 131072
+#endif
+
+// Keys per thread of the chunk kernels: a chunk is kMbThreads * kpt tokens.  Longer rows
+// take longer chunks, so the per-workgroup fixed work (the first-digit search, the
+// candidate resolution) is shared by more tokens.
+int kpt_for(int L) { return L <= BUTLER_SEL_KPT_SPLIT ? BUTLER_SEL_KPT_LO : BUTLER_SEL_KPT_HI; }
+
+struct RowState {
+  uint32_t b1;  // first-digit bin of the x-th largest key
+  int need;     // rank of the x-th largest key inside that bin (1-based)
+};
+
+struct MbWs {
+  uint32_t* hist1;               // [rows][2048]   first-digit counts, zero between calls
+  unsigned long long* ccount;    // [rows]         running candidate counter (never reset)
+  RowState* state;               // [rows]
+  int* defcnt;                   // [rows][nchunk] tokens of the chunk that are surely selected
+  int* ncand;                    // [rows][nchunk] candidates the chunk appended
+  uint2* cand;                   // [rows][L]      ring of (key, index | sink/window flag << 31)
+};
+
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+long long nchunk_for(int L) {
+  const int chunk = kMbThreads * kpt_for(L);
+  return (L + chunk - 1) / chunk;
 }
 
-// Finishing pass, one workgroup per chunk: every workgroup of a row resolves the same tau
-// and tie cut from the row's candidates (a rank count when they are few, else the radix
-// over bits 20..0 and the index radix of the ties), sums the sure and the selected
-// candidate counts of the chunks before its own into its output offset, and emits its
-// tokens.  The chunk-0 workgroup writes the row count and clears the row's histogram
-// (nothing in this kernel reads it).
+size_t mb_bytes(long long rows, int L) {
+  const long long nchunk = nchunk_for(L);
+  return al256(rows * 2048 * 4) + al256(rows * 8) + al256(rows * sizeof(RowState)) +
+         2 * al256(rows * nchunk * 4) + al256((size_t)rows * L * sizeof(uint2));
+}
+
+MbWs carve(void* ws, long long rows, int L) {
+  const long long nchunk = nchunk_for(L);
+  char* p = (char*)ws;
+  MbWs w;
+  w.hist1 = (uint32_t*)p;                 p += al256(rows * 2048 * sizeof(uint32_t));
+  w.ccount = (unsigned long long*)p;      p += al256(rows * 8);
+  w.state = (RowState*)p;                 p += al256(rows * sizeof(RowState));
+  w.defcnt = (int*)p;                     p += al256(rows * nchunk * sizeof(int));
+  w.ncand = (int*)p;                      p += al256(rows * nchunk * sizeof(int));
+  w.cand = (uint2*)p;
+  return w;
+}
+
+// The KPT keys of tokens t0 .. t0+KPT-1 (all requested at once); returns how many exist.
+template <int KPT>
+__device__ __forceinline__ int load_keys(const float* s, int t0, int L, uint32_t (&key)[KPT]) {
+  const int nv = max(0, min(KPT, L - t0));
+  if (nv == KPT && ((((uintptr_t)(s + t0)) & 15u) == 0)) {
+    float4 a[KPT / 4];
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q) a[q] = *reinterpret_cast<const float4*>(s + t0 + 4 * q);
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q) {
+      key[4 * q] = score_key(a[q].x);
+      key[4 * q + 1] = score_key(a[q].y);
+      key[4 * q + 2] = score_key(a[q].z);
+      key[4 * q + 3] = score_key(a[q].w);
+    }
+  } else {
+    float f[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) f[j] = s[min(t0 + j, L - 1)];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = score_key(f[j]);
+  }
+  return nv;
+}
+
+// first-digit histogram, when the scorer did not produce it
+template <int KPT>
+__global__ __launch_bounds__(kMbThreads) void mb_hist1_kernel(const float* __restrict__ scores,
+                                                              int num, int den, int L, int rows,
+                                                              uint32_t* __restrict__ ghist) {
+  const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
+  int k;
+  if (row_mode(L, num, den, k) != kModeNormal) return;
+  __shared__ uint32_t h[2048];
+  for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
+  __syncthreads();
+  uint32_t key[KPT];
+  const int nv = load_keys<KPT>(scores + (long long)row * L,
+                                (chunk * kMbThreads + threadIdx.x) * KPT, L, key);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (j < nv) atomicAdd(&h[key[j] >> 21], 1u);
+  __syncthreads();
+  uint32_t* gh = ghist + (long long)row * 2048;
+  for (int j = threadIdx.x; j < 2048; j += kMbThreads)
+    if (h[j]) atomicAdd(&gh[j], h[j]);
+}
+
+// ---- wave-level pieces: every wave works on its own, no barrier ----
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int ballot_count(bool p) { return __popcll(__ballot(p)); }
+
+// The bin of a 2048-bin histogram (global, 16-byte aligned) that holds the need-th largest
+// key, and the rank left inside it.  Lane l sums bins [2048 - 32(l+1), 2048 - 32l), the
+// lanes scan from the top, and the lane whose range holds the rank walks its 32 bins.
+__device__ __forceinline__ void wave_find_top(const uint32_t* __restrict__ gh, int need,
+                                              uint32_t& bin, int& rest) {
+  const int lane = threadIdx.x & 63;
+  const int lo = 2048 - 32 * (lane + 1);
+  uint32_t c[32];
+  const uint4* p = reinterpret_cast<const uint4*>(gh + lo);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint4 v = p[q];
+    c[4 * q] = v.x;
+    c[4 * q + 1] = v.y;
+    c[4 * q + 2] = v.z;
+    c[4 * q + 3] = v.w;
+  }
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) local += (int)c[i];
+  const int incl = wave_inclusive_sum(local);
+  const int excl = incl - local;
+  const unsigned long long m = __ballot(excl < need && need <= incl);
+  const int src = m ? (int)__ffsll((unsigned long long)m) - 1 : 0;
+  int above = excl, b = lo, r = 1;
+  bool found = false;
+#pragma unroll
+  for (int i = 31; i >= 0; --i) {
+    if (!found && above + (int)c[i] >= need) {
+      b = lo + i;
+      r = need - above;
+      found = true;
+    }
+    if (!found) above += (int)c[i];
+  }
+  bin = (uint32_t)__shfl(b, src);
+  rest = __shfl(r, src);
+}
+
+// One wave resolves, from the row's n <= 64*Q candidates (every one has first digit b1,
+// and the need-th largest of them is the x-th largest key of the row), tau bit by bit from
+// bit 20 down -- a ballot count of the candidates that carry the trial bit -- then, when
+// the budget splits the keys equal to tau, the tie cut bit by bit over their indices
+// (lowest indices first), and the counts of the selected candidates that are not sink /
+// window tokens: all of them, and those before index c_lo.
+template <int Q>
+__device__ void wave_resolve(const uint2* __restrict__ crow, int base, int n, int L,
+                             uint32_t b1, int need, int c_lo, uint32_t& tau, int& tie_cut,
+                             int& sel_all, int& sel_before) {
+  const int lane = threadIdx.x & 63;
+  uint32_t ck[Q], ci[Q];
+  bool cv[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    cv[q] = lane + 64 * q < n;
+    int p = base + min(lane + 64 * q, n - 1);
+    if (p >= L) p -= L;
+    const uint2 c = crow[p];
+    ck[q] = c.x;
+    ci[q] = c.y;
+  }
+  uint32_t P = b1 << 21;
+  int kk = need;
+  for (int bit = 20; bit >= 0; --bit) {
+    const uint32_t hi = 0xffffffffu << (bit + 1);
+    int c1 = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      c1 += ballot_count(cv[q] && (ck[q] & hi) == P && ((ck[q] >> bit) & 1u));
+    if (c1 >= kk) P |= 1u << bit;
+    else kk -= c1;
+  }
+  tau = P;
+  int ties = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) ties += ballot_count(cv[q] && ck[q] == tau);
+  if (kk >= ties) {
+    tie_cut = 0x7fffffff;
+  } else {
+    uint32_t I = 0u;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t hi = (0x7fffffffu << (bit + 1)) & 0x7fffffffu;
+      int c0 = 0;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const uint32_t t = ci[q] & 0x7fffffffu;
+        c0 += ballot_count(cv[q] && ck[q] == tau && (t & hi) == I && !((t >> bit) & 1u));
+      }
+      if (c0 < kk) {
+        kk -= c0;
+        I |= 1u << bit;
+      }
+    }
+    tie_cut = (int)I;
+  }
+  sel_all = 0;
+  sel_before = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int t = (int)(ci[q] & 0x7fffffffu);
+    const bool s = cv[q] && !(ci[q] >> 31) && (ck[q] > tau || (ck[q] == tau && t <= tie_cut));
+    sel_all += ballot_count(s);
+    sel_before += ballot_count(s && t < c_lo);
+  }
+}
+
+// The same for rows with many candidates, by the whole workgroup: radix passes over bits
+// 20..10 and 9..0 of the candidates (LDS histograms, read from the ring in memory), the
+// tie quota, the index radix of the ties, then the two counts.
+__device__ void block_resolve(const uint2* __restrict__ crow, int base, int n, int L,
+                              uint32_t b1, int need, int c_lo, uint32_t* h, int* tmp, int3* tmp3,
+                              int* sh, uint32_t& tau, int& tie_cut, int& sel_all,
+                              int& sel_before) {
+  auto at = [&](int j) {
+    const int p = base + j;
+    return crow[p >= L ? p - L : p];
+  };
+  uint32_t prefix = b1 << 21, pmask = 0xffe00000u;
+  const int shifts[2] = {10, 0};
+  const int bins[2] = {2048, 1024};
+  for (int p = 0; p < 2; ++p) {
+    for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n; j += kMbThreads) {
+      const uint32_t kk = at(j).x;
+      if ((kk & pmask) == prefix) atomicAdd(&h[(kk >> shifts[p]) & (uint32_t)(bins[p] - 1)], 1u);
+    }
+    __syncthreads();
+    find_bin_from_top<kMbThreads>(h, bins[p], need, tmp, &sh[0], &sh[1]);
+    prefix |= (uint32_t)sh[0] << shifts[p];
+    pmask |= (uint32_t)(bins[p] - 1) << shifts[p];
+    need = sh[1];
+  }
+  tau = prefix;
+  int mine = 0;
+  for (int j = threadIdx.x; j < n; j += kMbThreads) mine += (at(j).x == tau) ? 1 : 0;
+  int ties;
+  block_exclusive_sum<kMbThreads>(mine, ties, tmp);
+  if (need >= ties) {
+    tie_cut = 0x7fffffff;
+  } else {
+    // the need-th smallest index among the keys equal to tau: bits 30..20, 19..10, 9..0
+    uint32_t pre = 0u, pm = 0u;
+    int nd = need;
+    const int ish[3] = {20, 10, 0};
+    const uint32_t iw[3] = {2048u, 1024u, 1024u};
+    for (int p = 0; p < 3; ++p) {
+      for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
+      __syncthreads();
+      for (int j = threadIdx.x; j < n; j += kMbThreads) {
+        const uint2 c = at(j);
+        const uint32_t t = c.y & 0x7fffffffu;
+        if (c.x == tau && (t & pm) == pre) atomicAdd(&h[(t >> ish[p]) & (iw[p] - 1u)], 1u);
+      }
+      __syncthreads();
+      find_bin_from_bottom<kMbThreads>(h, 2048, nd, tmp, &sh[0], &sh[1]);
+      pre |= (uint32_t)sh[0] << ish[p];
+      pm |= (iw[p] - 1u) << ish[p];
+      nd = sh[1];
+    }
+    tie_cut = (int)pre;
+  }
+  int sa = 0, sb = 0;
+  for (int j = threadIdx.x; j < n; j += kMbThreads) {
+    const uint2 c = at(j);
+    if (c.y & 0x80000000u) continue;  // sink / window tokens are counted as sure
+    const int t = (int)c.y;
+    if (c.x > tau || (c.x == tau && t <= tie_cut)) {
+      ++sa;
+      sb += (t < c_lo) ? 1 : 0;
+    }
+  }
+  const int3 ss = block_sum3(sa, sb, 0, tmp3);
+  sel_all = ss.x;
+  sel_before = ss.y;
+}
+
+// Chunk pass.  Thread i of the workgroup holds tokens c_lo + i + 256 j (j < KPT), so a
+// wave's ballot covers 64 consecutive tokens.  Every wave derives the first-digit bin b1
+// from the row's histogram on its own, counts its tokens that are surely selected (digit
+// above b1, or sink / window) and appends the keys whose first digit is b1 to the row's
+// candidate ring, at positions the workgroup takes with one atomic.
+template <int KPT>
+__global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __restrict__ scores,
+                                                             int num, int den, int n_sink,
+                                                             int n_window, int L, int rows,
+                                                             const uint32_t* __restrict__ ghist,
+                                                             MbWs w) {
+  const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
+  const int nchunk = gridDim.x / rows;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int k;
+  const int mode = row_mode(L, num, den, k);
+  const int c_lo = chunk * kMbThreads * KPT;
+  const float* srow = scores + (long long)row * L;
+  float f[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) f[j] = srow[min(c_lo + (int)threadIdx.x + kMbThreads * j, L - 1)];
+  uint32_t b1 = 0u;
+  int need = 0;
+  if (mode == kModeNormal) {
+    wave_find_top(ghist + (long long)row * 2048, k, b1, need);
+    if (chunk == 0 && threadIdx.x == 0) w.state[row] = RowState{b1, need};
+  }
+  const int w_lo = max(0, L - n_window);
+  int ndef = 0, ncw = 0;
+  unsigned long long cm[KPT];
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
+    key[j] = score_key(f[j]);
+    const bool valid = t < L;
+    const bool forced = t < n_sink || t >= w_lo;
+    bool def, cand;
+    if (mode == kModeNormal) {
+      const uint32_t top = key[j] >> 21;
+      def = valid && (forced || top > b1);
+      cand = valid && top == b1;
+    } else {
+      def = valid && (forced || mode == kModeAll);
+      cand = false;
+    }
+    ndef += def ? 1 : 0;
+    cm[j] = __ballot(cand);
+    ncw += __popcll(cm[j]);
+  }
+  ndef = wave_sum_i(ndef);
+  // one atomic per workgroup (same-address atomics serialise): the waves' counts meet in LDS
+  __shared__ int s_n[kMbWaves], s_d[kMbWaves];
+  __shared__ int s_start;
+  if (lane == 0) {
+    s_n[wid] = ncw;
+    s_d[wid] = ndef;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tn = 0, td = 0;
+#pragma unroll
+    for (int v = 0; v < kMbWaves; ++v) {
+      tn += s_n[v];
+      td += s_d[v];
+    }
+    const long long e = (long long)row * nchunk + chunk;
+    w.defcnt[e] = td;
+    w.ncand[e] = tn;
+    s_start = tn ? (int)(atomicAdd(&w.ccount[row], (unsigned long long)tn) % (unsigned long long)L)
+                 : 0;
+  }
+  __syncthreads();
+  int start = s_start;
+#pragma unroll
+  for (int v = 0; v < kMbWaves; ++v) start += (v < wid) ? s_n[v] : 0;
+  if (start >= L) start -= L;
+  if (ncw) {
+    uint2* crow = w.cand + (long long)row * L;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int pos = start;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if ((cm[j] >> lane) & 1ull) {
+        int p = pos + __popcll(cm[j] & lt);
+        if (p >= L) p -= L;
+        const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
+        const uint32_t flag = (t < n_sink || t >= w_lo) ? 0x80000000u : 0u;
+        crow[p] = make_uint2(key[j], (uint32_t)t | flag);
+      }
+      pos += __popcll(cm[j]);
+      if (pos >= L) pos -= L;
+    }
+  }
+}
+
+// Finishing pass, one workgroup per chunk, tokens held as in the chunk pass.  Every wave
+// sums the row's per-chunk counts and resolves tau and the tie cut from the candidate ring
+// on its own (the whole workgroup only when the candidates exceed 2048), so nothing waits
+// on another wave until the output positions: the 64-token ballot words of the chunk are
+// prefix-summed once through LDS, and each wave writes its words' indices coalesced and
+// their bitmask words.  The chunk-0 workgroup writes the row count and clears the row's
+// histogram (nothing in this kernel reads it).
+template <int KPT>
 __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
     const float* __restrict__ scores, int num, int den, int n_sink, int n_window, int L,
     int rows, int cap, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask,
     int32_t* __restrict__ count, uint32_t* __restrict__ ghist, MbWs w) {
+  constexpr int NWD = kMbWaves * KPT;   // 64-token words per chunk
+  static_assert(NWD <= 128, "two words per lane in the prefix scan");
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
   const int nchunk = gridDim.x / rows;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int k;
   const int mode = row_mode(L, num, den, k);
   __shared__ uint32_t h[2048];
-  __shared__ uint2 s_c[kFinStage];
-  __shared__ int tmp[kMbThreads / 64];
-  __shared__ int3 tmp3[kMbThreads / 64];
-  __shared__ int sh_bin, sh_need, sh_tie;
-  __shared__ uint32_t sh_tau;
-  __shared__ uint8_t bytes[kMbThreads];
-  const int w_lo = max(0, L - n_window);
-  const int c_lo = chunk * kMbChunk;
-  const int t0 = c_lo + threadIdx.x * 8;
-  uint32_t key[8];
-  const int nv = load_keys8(scores + (long long)row * L, t0, L, key);
-  // the row's state and candidate counter are requested with the per-chunk counts
+  __shared__ int tmp[kMbWaves];
+  __shared__ int3 tmp3[kMbWaves];
+  __shared__ int sh[2];
+  __shared__ int s_wc[NWD];
+  const int c_lo = chunk * kMbThreads * KPT;
+  const float* srow = scores + (long long)row * L;
+  float f[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) f[j] = srow[min(c_lo + (int)threadIdx.x + kMbThreads * j, L - 1)];
+  // the row's state and candidate counter are requested with the per-wave counts
   RowState st = {0u, 0};
   unsigned long long end = 0ull;
   if (mode == kModeNormal) {
     st = w.state[row];
     end = w.ccount[row];
   }
-  int n_loc = 0, def_all = 0, def_before = 0;
-  for (int c = threadIdx.x; c < nchunk; c += kMbThreads) {
-    const int d = w.defcnt[(long long)row * nchunk + c];
+  const long long e0 = (long long)row * nchunk;
+  int n = 0, def_all = 0, def_before = 0;
+  for (int e = lane; e < nchunk; e += 64) {
+    const int d = w.defcnt[e0 + e];
     def_all += d;
-    def_before += (c < chunk) ? d : 0;
-    n_loc += w.ncand[(long long)row * nchunk + c];
+    def_before += (e < chunk) ? d : 0;
+    n += w.ncand[e0 + e];
   }
-  const int3 sums = block_sum3(n_loc, def_all, def_before, tmp3);
-  const int n = sums.x;
-  def_all = sums.y;
-  def_before = sums.z;
-  int tot;
+  n = wave_sum_i(n);
+  def_all = wave_sum_i(def_all);
+  def_before = wave_sum_i(def_before);
   if (chunk == 0) {
     uint32_t* gh = ghist + (long long)row * 2048;
     for (int j = threadIdx.x; j < 2048; j += kMbThreads) gh[j] = 0u;
@@ -465,130 +708,54 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
   if (mode == kModeNormal && n > 0) {
     const int base = (int)((end - (unsigned long long)n) % (unsigned long long)L);
     const uint2* crow = w.cand + (long long)row * L;
-    auto at = [&](int j) {
-      const int p = base + j;
-      return crow[p >= L ? p - L : p];
-    };
-    const bool staged = n <= kFinStage;
-    if (staged) {
-      for (int j = threadIdx.x; j < n; j += kMbThreads) s_c[j] = at(j);
-    }
-    __syncthreads();
-    auto ckey = [&](int j) { return staged ? s_c[j].x : at(j).x; };
-    auto cid = [&](int j) { return staged ? s_c[j].y : at(j).y; };
-    if (n <= kMbThreads) {
-      // rank of each candidate in (key desc, index asc) order; the one of rank need-1 is
-      // the last token the budget takes
-      if ((int)threadIdx.x < n) {
-        const uint2 me = s_c[threadIdx.x];
-        const uint32_t kj = me.x, ij = me.y & 0x7fffffffu;
-        int rank = 0, i = 0;
-        for (; i + 4 <= n; i += 4) {
-          const uint2 c0 = s_c[i], c1 = s_c[i + 1], c2 = s_c[i + 2], c3 = s_c[i + 3];
-          rank += precedes(c0, kj, ij) + precedes(c1, kj, ij) + precedes(c2, kj, ij) +
-                  precedes(c3, kj, ij);
-        }
-        for (; i < n; ++i) rank += precedes(s_c[i], kj, ij);
-        if (rank == st.need - 1) {
-          sh_tau = kj;
-          sh_tie = (int)ij;
-        }
-      }
-      __syncthreads();
-      tau = sh_tau;
-      tie_cut = sh_tie;
-    } else {
-      // bits 20..10, then 9..0, over the candidates (all have first digit b1)
-      uint32_t prefix = st.b1 << 21, pmask = 0xffe00000u;
-      int need = st.need;
-      const int shifts[2] = {10, 0};
-      const int bins[2] = {2048, 1024};
-      for (int p = 0; p < 2; ++p) {
-        for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
-        __syncthreads();
-        for (int j = threadIdx.x; j < n; j += kMbThreads) {
-          const uint32_t kk = ckey(j);
-          if ((kk & pmask) == prefix) atomicAdd(&h[(kk >> shifts[p]) & (uint32_t)(bins[p] - 1)], 1u);
-        }
-        __syncthreads();
-        find_bin_from_top<kMbThreads>(h, bins[p], need, tmp, &sh_bin, &sh_need);
-        prefix |= (uint32_t)sh_bin << shifts[p];
-        pmask |= (uint32_t)(bins[p] - 1) << shifts[p];
-        need = sh_need;
-      }
-      tau = prefix;
-      int mine = 0;
-      for (int j = threadIdx.x; j < n; j += kMbThreads) mine += (ckey(j) == tau) ? 1 : 0;
-      int ties;
-      block_exclusive_sum<kMbThreads>(mine, ties, tmp);
-      if (need >= ties) {
-        tie_cut = 0x7fffffff;
-      } else {
-        // the need-th smallest index among the keys equal to tau: bits 30..20, 19..10, 9..0
-        uint32_t pre = 0u, pm = 0u;
-        int nd = need;
-        const int ish[3] = {20, 10, 0};
-        const uint32_t iw[3] = {2048u, 1024u, 1024u};
-        for (int p = 0; p < 3; ++p) {
-          for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
-          __syncthreads();
-          for (int j = threadIdx.x; j < n; j += kMbThreads) {
-            const uint32_t t = cid(j) & 0x7fffffffu;
-            if (ckey(j) == tau && (t & pm) == pre) atomicAdd(&h[(t >> ish[p]) & (iw[p] - 1u)], 1u);
-          }
-          __syncthreads();
-          find_bin_from_bottom<kMbThreads>(h, 2048, nd, tmp, &sh_bin, &sh_need);
-          pre |= (uint32_t)sh_bin << ish[p];
-          pm |= (iw[p] - 1u) << ish[p];
-          nd = sh_need;
-        }
-        tie_cut = (int)pre;
-      }
-    }
-    for (int j = threadIdx.x; j < n; j += kMbThreads) {
-      const uint32_t id = cid(j);
-      if (id & 0x80000000u) continue;  // sink / window tokens are counted as sure
-      const uint32_t kk = ckey(j);
-      const int t = (int)id;
-      if (kk > tau || (kk == tau && t <= tie_cut)) {
-        ++sel_all;
-        sel_before += (t < c_lo) ? 1 : 0;
-      }
-    }
-    const int3 ss = block_sum3(sel_all, sel_before, 0, tmp3);
-    sel_all = ss.x;
-    sel_before = ss.y;
+#define BUTLER_RESOLVE(QQ) \
+  wave_resolve<QQ>(crow, base, n, L, st.b1, st.need, c_lo, tau, tie_cut, sel_all, sel_before)
+    if (n <= 64) BUTLER_RESOLVE(1);
+    else if (n <= 128) BUTLER_RESOLVE(2);
+    else if (n <= 256) BUTLER_RESOLVE(4);
+    else if (n <= 512) BUTLER_RESOLVE(8);
+    else if (n <= 1024) BUTLER_RESOLVE(16);
+    else if (n <= 2048) BUTLER_RESOLVE(32);
+    else
+      block_resolve(crow, base, n, L, st.b1, st.need, c_lo, h, tmp, tmp3, sh, tau, tie_cut,
+                    sel_all, sel_before);
+#undef BUTLER_RESOLVE
   }
   if (chunk == 0 && threadIdx.x == 0) count[row] = def_all + sel_all;
-  uint32_t sel = 0;
+  const int w_lo = max(0, L - n_window);
+  unsigned long long sm[KPT];
+  int my = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= nv) continue;
-    const int t = t0 + j;
-    bool s = t < n_sink || t >= w_lo;
-    if (mode == kModeAll) s = true;
-    else if (mode == kModeNormal) s = s || key[j] > tau || (key[j] == tau && t <= tie_cut);
-    sel |= (uint32_t)s << j;
+  for (int j = 0; j < KPT; ++j) {
+    const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
+    const uint32_t key = score_key(f[j]);
+    bool s = t < n_sink || t >= w_lo || mode == kModeAll;
+    if (mode == kModeNormal) s = s || key > tau || (key == tau && t <= tie_cut);
+    sm[j] = __ballot(s && t < L);
+    if (lane == j) my = __popcll(sm[j]);
   }
-  const int ex = block_exclusive_sum<kMbThreads>(__popc(sel), tot, tmp);
-  if (idx) {
-    int pos = def_before + sel_before + ex;
-    int32_t* irow = idx + (long long)row * cap;
-    for (uint32_t e = sel; e; e &= e - 1) {
-      if (pos < cap) irow[pos] = t0 + (__ffs(e) - 1);
-      ++pos;
+  // word u = j * waves + wave covers tokens c_lo + 256 j + 64 wave .. +63
+  if (lane < KPT) s_wc[lane * kMbWaves + wid] = my;
+  __syncthreads();
+  const int v0 = (2 * lane < NWD) ? s_wc[2 * lane] : 0;
+  const int v1 = (2 * lane + 1 < NWD) ? s_wc[2 * lane + 1] : 0;
+  const int ex = wave_inclusive_sum(v0 + v1) - (v0 + v1);
+  const int out0 = def_before + sel_before;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int nwords = (L + 31) / 32;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int u = j * kMbWaves + wid;
+    const int pe = __shfl(ex, u >> 1), pv = __shfl(v0, u >> 1);
+    const int pref = pe + ((u & 1) ? pv : 0);
+    const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
+    if (idx && ((sm[j] >> lane) & 1ull)) {
+      const int pos = out0 + pref + __popcll(sm[j] & lt);
+      if (pos < cap) idx[(long long)row * cap + pos] = t;
     }
-  }
-  if (bitmask) {
-    bytes[threadIdx.x] = (uint8_t)sel;
-    __syncthreads();
-    const int nwords = (L + 31) / 32;
-    const int wd = chunk * (kMbChunk / 32) + threadIdx.x;
-    if (threadIdx.x < kMbChunk / 32 && wd < nwords) {
-      const int b0 = threadIdx.x * 4;
-      bitmask[(long long)row * nwords + wd] = (uint32_t)bytes[b0] | ((uint32_t)bytes[b0 + 1] << 8) |
-                                              ((uint32_t)bytes[b0 + 2] << 16) |
-                                              ((uint32_t)bytes[b0 + 3] << 24);
+    if (bitmask && lane < 2) {
+      const int wd = (c_lo + kMbThreads * j + 64 * wid) / 32 + lane;
+      if (wd < nwords) bitmask[(long long)row * nwords + wd] = (uint32_t)(sm[j] >> (32 * lane));
     }
   }
 }
@@ -610,18 +777,24 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
   const long long rows = (long long)B * Hkv * Lq;
   if (use_chunked(Lq, L, causal)) {
     const MbWs w = carve(ws, rows, L);
-    const int nchunk = (L + kMbChunk - 1) / kMbChunk;
+    const int nchunk = (int)nchunk_for(L);
     const dim3 grid((unsigned)(rows * nchunk));
-    uint32_t* gh = hist;
-    if (!gh) {
-      gh = w.hist1;
-      hipLaunchKernelGGL(mb_hist1_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, L,
-                         (int)rows, gh);
+    uint32_t* gh = hist ? hist : w.hist1;
+    auto run = [&](auto kpt_c) {
+      constexpr int KPT = decltype(kpt_c)::value;
+      if (!hist)
+        hipLaunchKernelGGL(mb_hist1_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
+                           L, (int)rows, gh);
+      hipLaunchKernelGGL(mb_cand_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
+                         n_sink, n_window, L, (int)rows, (const uint32_t*)gh, w);
+      hipLaunchKernelGGL(mb_finish_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
+                         n_sink, n_window, L, (int)rows, cap, idx, bitmask, count, gh, w);
+    };
+    switch (kpt_for(L)) {
+      case 8: run(std::integral_constant<int, 8>()); break;
+      case 16: run(std::integral_constant<int, 16>()); break;
+      default: run(std::integral_constant<int, 32>()); break;
     }
-    hipLaunchKernelGGL(mb_cand_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, n_sink,
-                       n_window, L, (int)rows, (const uint32_t*)gh, w);
-    hipLaunchKernelGGL(mb_finish_kernel, grid, dim3(kMbThreads), 0, s, scores, num, den, n_sink,
-                       n_window, L, (int)rows, cap, idx, bitmask, count, gh, w);
     return hipGetLastError();
   }
   // one workgroup per row; the widest rows get 1024 threads x 64 keys
