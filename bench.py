@@ -237,6 +237,229 @@ def cpu_baseline(layer, budget_s: float = 12.0):
                       f"{el:.1f} s"}
 
 
+# ---------------------------------------------------------------------------
+# the other workloads: soft-voting batched decode, full-depth long-context decode,
+# chunked causal prefill (reported in "configs"; the headline stays the layer decode)
+# ---------------------------------------------------------------------------
+
+def graph_time(fns, reps):
+    """Seconds per replay of a graph holding `reps` passes over `fns` (after one eager
+    pass and one warm-up replay)."""
+    import torch
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            for f in fns:
+                f()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps
+
+
+def run_softvote(device):
+    """Batched decode with the soft-voting scorer: B=16, L=16384, 30% + 4 + 64, the 64
+    steps of the query walk, each step = score (TokenSelect soft votes over all L keys),
+    select, attend.  One graph holds the 64 steps."""
+    import torch
+    import synthetic
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[3]
+    t0 = time.time()
+    cache = synthetic.softvote_cache(w)
+    qs = [q.to(device) for q in synthetic.softvote_queries(w, w.steps)]
+    k, v = cache["k_cache"].to(device), cache["v_cache"].to(device)
+    del cache
+    log(f"  softvote inputs ready in {time.time() - t0:.1f}s")
+    cap = w.cap(w.L)
+    scores = torch.empty(w.B, w.Hkv, 1, w.L, dtype=torch.float32, device=device)
+    hist = torch.zeros(w.B, w.Hkv, 1, 2048, dtype=torch.int32, device=device)
+    idx = torch.empty(w.B, w.Hkv, 1, cap, dtype=torch.int32, device=device)
+    cnt = torch.empty(w.B, w.Hkv, 1, dtype=torch.int32, device=device)
+    out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
+
+    def step(q):
+        return [lambda: qa.butler_score(qa.BUTLER_SCORE_SOFTVOTE, q, k, scores, Hkv=w.Hkv,
+                                        L=w.L, softmax_scale=w.scale, radix_hist=hist),
+                lambda: qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink,
+                                              w.n_window, cnt, idx=idx, radix_hist=hist),
+                lambda: qa.butler_sparse_decode_attn(q, k, v, out, L=w.L, idx=idx, count=cnt,
+                                                     softmax_scale=w.scale)]
+    fns = [f for q in qs for f in step(q)]
+    sec = graph_time(fns, 1) / len(qs)
+    n_sel = int(cnt.sum())
+    elt = 2
+    byts = w.B * w.Hkv * w.L * w.D * elt + n_sel * (2 * w.D * elt + 8) + w.B * w.Hq * w.D * (elt + 4)
+    del k, v
+    return {"workload": w.name, "steps": len(qs), "steps_per_s": 1.0 / sec,
+            "ms_per_step": sec * 1e3, "algorithmic_bytes": byts,
+            "GB/s": byts / sec / 1e9, "frac_of_hbm_peak": byts / sec / 1e9 / HBM_PEAK_GBS}
+
+
+def _rope_t(x, base=500000.0):
+    """Rotate-half RoPE over the last dim of x [..., T, D] (positions 0..T-1), float32."""
+    import torch
+    T, D = x.shape[-2], x.shape[-1]
+    half = D // 2
+    inv = base ** (-torch.arange(half, dtype=torch.float64, device=x.device) * 2.0 / D)
+    ang = torch.arange(T, dtype=torch.float64, device=x.device)[:, None] * inv[None, :]
+    c, s = torch.cos(ang).float(), torch.sin(ang).float()
+    a, b = x[..., :half], x[..., half:]
+    return torch.cat([a * c - b * s, b * c + a * s], dim=-1)
+
+
+def run_full_depth(steps, device):
+    """Long-context full-depth decode: B=1, L=262144, 32 layers, producers at layers
+    0, 4, ..., 28 (f_theta on LN(H), G=4 slots), layer 0 dense, the others 1/16 + 4 + 128.
+    Inputs are drawn on the GPU (seeded torch generator, same distributions as the
+    workload: N(0,1) K/V/q with 1% heavy-hitter keys, N(0, 0.02) weights), since 38.6 GB
+    of host-side draws would dominate the run.  One graph holds `steps` whole steps."""
+    import torch
+    import synthetic
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[4]
+    L, dt = w.L, w.dtype
+    gen = torch.Generator(device=device)
+    gen.manual_seed(20260404)
+    rn = lambda *shape, std=1.0: (torch.randn(*shape, generator=gen, device=device) * std)
+    t0 = time.time()
+    lay = []
+    n_heavy = int(round(w.heavy_frac * L))
+    for l in range(w.layers):
+        q = rn(w.B, w.Hq, 1, w.D).to(dt)
+        k = rn(w.B, w.Hkv, L, w.D)
+        u = q.float().reshape(w.B, w.Hkv, w.R, w.D).sum(2)
+        u = u / u.norm(dim=-1, keepdim=True)
+        for g in range(w.Hkv):
+            pos = torch.randperm(L, generator=gen, device=device)[:n_heavy]
+            k[0, g, pos] += 3.0 * u[0, g]
+        d = {"q": q, "k": k.to(dt), "v": rn(w.B, w.Hkv, L, w.D).to(dt),
+             "wk": rn(w.D, w.dprime, std=0.02).to(dt)}
+        del k
+        d["kimp"] = torch.empty(w.B, w.Hkv, L, w.dprime, dtype=dt, device=device)
+        qa.butler_project_keys(d["k"], d["wk"], d["kimp"], 0, L)
+        if l % w.G == 0:
+            d["h"] = rn(w.B, 1, w.E).to(dt)
+            d["w1"] = rn(w.E, w.F, std=0.02).to(dt)
+            d["w2"] = rn(w.F, w.Hq * w.G * w.dprime, std=0.02).to(dt)
+            d["qimp"] = torch.empty(w.B, w.Hq, w.G, 1, w.dprime, dtype=dt, device=device)
+        lay.append(d)
+    torch.cuda.synchronize()
+    log(f"  full-depth inputs ready in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB on the device)")
+    cap = w.cap(L)
+    scores = torch.empty(w.B, w.Hkv, 1, L, dtype=torch.float32, device=device)
+    hist = torch.zeros(w.B, w.Hkv, 1, 2048, dtype=torch.int32, device=device)
+    idx = torch.empty(w.B, w.Hkv, 1, cap, dtype=torch.int32, device=device)
+    idx_dense = torch.empty(w.B, w.Hkv, 1, L, dtype=torch.int32, device=device)
+    cnt = torch.empty(w.B, w.Hkv, 1, dtype=torch.int32, device=device)
+    out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
+    fns = []
+    for l, d in enumerate(lay):
+        if l % w.G == 0:
+            fns.append(lambda d=d: qa.butler_produce_queries(d["h"], d["w1"], d["w2"], d["qimp"]))
+        fns.append(lambda d=d: qa.butler_project_keys(d["k"], d["wk"], d["kimp"], L - 1, 1))
+        if l == 0:   # dense layer: the budget takes every token
+            fns.append(lambda: qa.butler_select_topk(scores, 1, 1, w.n_sink, w.n_window, cnt,
+                                                     idx=idx_dense))
+            fns.append(lambda d=d: qa.butler_sparse_decode_attn(d["q"], d["k"], d["v"], out, L=L,
+                                                                idx=idx_dense, count=cnt,
+                                                                softmax_scale=w.scale))
+            continue
+        prod = lay[w.G * (l // w.G)]
+        slot = (l - 1) % w.G
+        fns.append(lambda d=d, prod=prod, slot=slot: qa.butler_score(
+            qa.BUTLER_SCORE_RAW, prod["qimp"], d["kimp"], scores, Hkv=w.Hkv, L=L, slot=slot,
+            radix_hist=hist))
+        fns.append(lambda: qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink,
+                                                 w.n_window, cnt, idx=idx, radix_hist=hist))
+        fns.append(lambda d=d: qa.butler_sparse_decode_attn(d["q"], d["k"], d["v"], out, L=L,
+                                                            idx=idx, count=cnt,
+                                                            softmax_scale=w.scale))
+    sec = graph_time(fns, steps)
+    n_sel = int(cnt.sum())              # last consumer layer's selection
+    elt = 2
+    consumer = w.B * w.Hkv * (L * w.dprime * elt + n_sel // w.Hkv * (2 * w.D * elt + 8))
+    dense = w.B * w.Hkv * L * 2 * w.D * elt
+    producer = (w.E * w.F + w.F * w.Hq * w.G * w.dprime) * elt
+    byts = dense + (w.layers - 1) * consumer + (w.layers // w.G) * producer
+    lay.clear()
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "steps": steps, "steps_per_s": 1.0 / sec,
+            "ms_per_step": sec * 1e3, "layer_steps_per_s": w.layers / sec,
+            "algorithmic_bytes": byts, "GB/s": byts / sec / 1e9,
+            "frac_of_hbm_peak": byts / sec / 1e9 / HBM_PEAK_GBS,
+            "inputs": "seeded torch generator on the GPU"}
+
+
+def run_prefill(device):
+    """Chunked causal prefill: B=2, L=8192 in query chunks of 1024.  Per chunk: f_theta
+    on the chunk's hidden rows (Q_imp, slot 0 scored), K_imp of the chunk's keys, causal
+    raw scores of the chunk against its prefix, per-row top-50% + sink 4 + window 64 into
+    a bitmask, masked attention of every row.  Q / H arrive chunk-major (the layout a
+    chunked prefill produces them in); inputs are drawn on the GPU from a seeded torch
+    generator with the workload's distributions (H ~ N(0,1), weights N(0, 0.02), RoPE at
+    base 500000)."""
+    import torch
+    import synthetic
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[5]
+    L, C, dt = w.L, w.chunk, w.dtype
+    nc = L // C
+    gen = torch.Generator(device=device)
+    gen.manual_seed(20260505)
+    rn = lambda *shape, std=1.0: (torch.randn(*shape, generator=gen, device=device) * std)
+    H = rn(w.B, L, w.E).to(dt)
+    proj = {}
+    for name, heads in (("q", w.Hq), ("k", w.Hkv), ("v", w.Hkv)):
+        W = rn(w.E, heads * w.D, std=0.02).to(dt)
+        x = (H.float().reshape(-1, w.E) @ W.float()).reshape(w.B, L, heads, w.D).transpose(1, 2)
+        proj[name] = (_rope_t(x) if name != "v" else x).to(dt).contiguous()
+    k, v = proj["k"], proj["v"]
+    Qc = [proj["q"][:, :, c * C:(c + 1) * C].contiguous() for c in range(nc)]
+    Hc = [H[:, c * C:(c + 1) * C].contiguous() for c in range(nc)]
+    del proj, H
+    w1, w2 = rn(w.E, w.F, std=0.02).to(dt), rn(w.F, w.Hq * w.G * w.dprime, std=0.02).to(dt)
+    wk = rn(w.D, w.dprime, std=0.02).to(dt)
+    kimp = torch.empty(w.B, w.Hkv, L, w.dprime, dtype=dt, device=device)
+    qimp = [torch.empty(w.B, w.Hq, w.G, C, w.dprime, dtype=dt, device=device) for _ in range(nc)]
+    scores = [torch.empty(w.B, w.Hkv, C, (c + 1) * C, dtype=torch.float32, device=device)
+              for c in range(nc)]
+    hist = [torch.zeros(w.B, w.Hkv, C, 2048, dtype=torch.int32, device=device) for _ in range(nc)]
+    bms = [torch.empty(w.B, w.Hkv, C, ((c + 1) * C + 31) // 32, dtype=torch.int32, device=device)
+           for c in range(nc)]
+    cnt = torch.empty(w.B, w.Hkv, C, dtype=torch.int32, device=device)
+    outs = [torch.empty(w.B, w.Hq, C, w.D, dtype=torch.float32, device=device) for _ in range(nc)]
+    groups = {"produce": [], "project": [], "score+select": [], "attn": []}
+    for c in range(nc):
+        c0, Lc = c * C, (c + 1) * C
+        groups["produce"].append(lambda c=c: qa.butler_produce_queries(Hc[c], w1, w2, qimp[c]))
+        groups["project"].append(lambda c0=c0: qa.butler_project_keys(k, wk, kimp, c0, C))
+        groups["score+select"].append(lambda c=c, c0=c0, Lc=Lc: (
+            qa.butler_score(qa.BUTLER_SCORE_RAW, qimp[c], kimp, scores[c], Hkv=w.Hkv, L=Lc,
+                            slot=0, q_pos0=c0, causal=True, radix_hist=hist[c]),
+            qa.butler_select_topk(scores[c], w.budget_num, w.budget_den, w.n_sink, w.n_window,
+                                  cnt, bitmask=bms[c], q_pos0=c0, causal=True,
+                                  radix_hist=hist[c])))
+        groups["attn"].append(lambda c=c, c0=c0, Lc=Lc: qa.butler_sparse_decode_attn(
+            Qc[c], k, v, outs[c], L=Lc, bitmask=bms[c], q_pos0=c0, softmax_scale=w.scale))
+    order = [f for c in range(nc) for f in (groups["produce"][c], groups["project"][c],
+                                           groups["score+select"][c], groups["attn"][c])]
+    sec = graph_time(order, 1)
+    part = {name: graph_time(fs, 1) * 1e6 for name, fs in groups.items()}
+    prod_flops = 2.0 * w.B * L * (w.E * w.F + w.F * w.Hq * w.G * w.dprime)
+    return {"workload": w.name, "prefill_s": sec, "tokens_per_s": w.B * L / sec,
+            "phase_us": {kk: round(vv, 1) for kk, vv in part.items()},
+            "producer_TFLOPs": prod_flops / (part["produce"] * 1e-6) / 1e12,
+            "producer_frac_of_bf16_mfma_peak": prod_flops / (part["produce"] * 1e-6) / 2.5e15,
+            "inputs": "seeded torch generator on the GPU"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +468,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--L", type=int, default=None)
+    ap.add_argument("--configs", default="3,4,5",
+                    help="other workloads to measure: 3 soft-voting, 4 full depth, 5 prefill")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run a 256 MiB device copy first (HBM counter calibration)")
     a = ap.parse_args(argv)
@@ -291,6 +516,18 @@ def main(argv=None) -> int:
             lay.free()
         layers = None
 
+    others = {}
+    for c in [x for x in a.configs.split(",") if x]:
+        torch.cuda.empty_cache()
+        log(f"[bench] workload {c}")
+        if c == "3":
+            others["softvote_decode"] = run_softvote(dev)
+        elif c == "4":
+            others["full_depth_decode"] = run_full_depth(max(a.steps // 40, 3), dev)
+        elif c == "5":
+            others["chunked_prefill"] = run_prefill(dev)
+        log(f"[bench] workload {c}: {json.dumps(others)}")
+
     cpu = None
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
@@ -327,6 +564,7 @@ def main(argv=None) -> int:
                      "frac": head["step_GBps"] / HBM_PEAK_GBS},
         "kernel_us": head["kernel_us"],
         "sweep": sweep,
+        "configs": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
