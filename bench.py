@@ -293,11 +293,15 @@ def run_softvote(device):
     fns = [f for q in qs for f in step(q)]
     sec = graph_time(fns, 1) / len(qs)
     n_sel = int(cnt.sum())
+    st = [step(q) for q in qs]
+    phase = {"score+select": graph_time([f for s3 in st for f in s3[:2]], 1) / len(qs),
+             "attn": graph_time([s3[2] for s3 in st], 1) / len(qs)}
     elt = 2
     byts = w.B * w.Hkv * w.L * w.D * elt + n_sel * (2 * w.D * elt + 8) + w.B * w.Hq * w.D * (elt + 4)
     del k, v
     return {"workload": w.name, "steps": len(qs), "steps_per_s": 1.0 / sec,
-            "ms_per_step": sec * 1e3, "algorithmic_bytes": byts,
+            "ms_per_step": sec * 1e3, "phase_us": {kk: round(vv * 1e6, 1) for kk, vv in phase.items()},
+            "algorithmic_bytes": byts,
             "GB/s": byts / sec / 1e9, "frac_of_hbm_peak": byts / sec / 1e9 / HBM_PEAK_GBS}
 
 
@@ -360,28 +364,38 @@ def run_full_depth(steps, device):
     cnt = torch.empty(w.B, w.Hkv, 1, dtype=torch.int32, device=device)
     out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
     fns = []
+    groups = {"produce": [], "project": [], "dense layer 0": [], "score+select": [], "attn": []}
+
+    def add(group, *fs):
+        fns.extend(fs)
+        groups[group].extend(fs)
     for l, d in enumerate(lay):
         if l % w.G == 0:
-            fns.append(lambda d=d: qa.butler_produce_queries(d["h"], d["w1"], d["w2"], d["qimp"]))
-        fns.append(lambda d=d: qa.butler_project_keys(d["k"], d["wk"], d["kimp"], L - 1, 1))
+            add("produce", lambda d=d: qa.butler_produce_queries(d["h"], d["w1"], d["w2"], d["qimp"]))
+        add("project", lambda d=d: qa.butler_project_keys(d["k"], d["wk"], d["kimp"], L - 1, 1))
         if l == 0:   # dense layer: the budget takes every token
-            fns.append(lambda: qa.butler_select_topk(scores, 1, 1, w.n_sink, w.n_window, cnt,
-                                                     idx=idx_dense))
-            fns.append(lambda d=d: qa.butler_sparse_decode_attn(d["q"], d["k"], d["v"], out, L=L,
-                                                                idx=idx_dense, count=cnt,
-                                                                softmax_scale=w.scale))
+            add("dense layer 0",
+                lambda: qa.butler_select_topk(scores, 1, 1, w.n_sink, w.n_window, cnt,
+                                              idx=idx_dense),
+                lambda d=d: qa.butler_sparse_decode_attn(d["q"], d["k"], d["v"], out, L=L,
+                                                         idx=idx_dense, count=cnt,
+                                                         softmax_scale=w.scale))
             continue
         prod = lay[w.G * (l // w.G)]
         slot = (l - 1) % w.G
-        fns.append(lambda d=d, prod=prod, slot=slot: qa.butler_score(
-            qa.BUTLER_SCORE_RAW, prod["qimp"], d["kimp"], scores, Hkv=w.Hkv, L=L, slot=slot,
-            radix_hist=hist))
-        fns.append(lambda: qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink,
-                                                 w.n_window, cnt, idx=idx, radix_hist=hist))
-        fns.append(lambda d=d: qa.butler_sparse_decode_attn(d["q"], d["k"], d["v"], out, L=L,
-                                                            idx=idx, count=cnt,
-                                                            softmax_scale=w.scale))
+        add("score+select",
+            lambda d=d, prod=prod, slot=slot: qa.butler_score(
+                qa.BUTLER_SCORE_RAW, prod["qimp"], d["kimp"], scores, Hkv=w.Hkv, L=L,
+                slot=slot, radix_hist=hist),
+            lambda: qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink,
+                                          w.n_window, cnt, idx=idx, radix_hist=hist))
+        add("attn", lambda d=d: qa.butler_sparse_decode_attn(d["q"], d["k"], d["v"], out, L=L,
+                                                             idx=idx, count=cnt,
+                                                             softmax_scale=w.scale))
     sec = graph_time(fns, steps)
+    phase = {name: graph_time(fs, 1) * 1e6 for name, fs in groups.items() if name != "attn"}
+    # the consumer attention reads the last consumer layer's index list in this timing
+    phase["attn"] = graph_time(groups["attn"], 1) * 1e6
     n_sel = int(cnt.sum())              # last consumer layer's selection
     elt = 2
     consumer = w.B * w.Hkv * (L * w.dprime * elt + n_sel // w.Hkv * (2 * w.D * elt + 8))
@@ -392,6 +406,7 @@ def run_full_depth(steps, device):
     torch.cuda.empty_cache()
     return {"workload": w.name, "steps": steps, "steps_per_s": 1.0 / sec,
             "ms_per_step": sec * 1e3, "layer_steps_per_s": w.layers / sec,
+            "phase_us": {kk: round(vv, 1) for kk, vv in phase.items()},
             "algorithmic_bytes": byts, "GB/s": byts / sec / 1e9,
             "frac_of_hbm_peak": byts / sec / 1e9 / HBM_PEAK_GBS,
             "inputs": "seeded torch generator on the GPU"}

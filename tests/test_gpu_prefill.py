@@ -56,6 +56,12 @@ def test_producer_prefill_rows():
     _producer_case(w, 77, layer=0)
 
 
+def test_producer_prefill_chunk():
+    """One 1024-row prefill chunk of both sequences (the matrix-core GEMM, split over K)."""
+    w = synthetic.WORKLOADS[5]
+    _producer_case(w, 1024, layer=1)
+
+
 def _prefill_case(w, L, chunk):
     import query_aware_sparse_imp_amd as qa
     print(f"[prefill] B={w.B} L={L} chunk={chunk}", flush=True)
