@@ -713,11 +713,180 @@ hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Prefill on the matrix cores (bf16, D = 128, R = 4): one workgroup per (b, KV head, 32
+// query rows), one wave per query head of the group.  Key tiles of 32 tokens run from 0
+// to the block's causal end; each tile is staged in LDS once for the four heads -- K as
+// [token][d], V transposed to [d][token] (two tokens packed per 32-bit word).
+//   S^T = K . Q^T        A = K rows (tokens), B = the wave's 32 queries (kept in VGPRs)
+//   O^T += V^T . P^T      A = V^T rows (d), B = P^T straight from the S^T accumulators
+// In the 32x32 accumulator layout lane l holds query l%32 and tokens 8(r/4) + 4(l/32) +
+// r%4: ordered by r, that is exactly the MFMA B operand of a 16-token K step if the K
+// order is permuted the same way on the V^T side (tokens {0-3, 8-11} for lanes 0-31,
+// {4-7, 12-15} for lanes 32-63: two 8-byte LDS reads).  The query is the lane in both
+// S^T and O^T, so the online softmax (max, rescale, sum) needs only the partner lane
+// l ^ 32.  Masking comes from the row's bitmask word of the tile.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+
+constexpr int kPfThreads = 256;
+constexpr int kPfKS = 128 + 8;   // LDS row stride (bf16) of the K tile
+constexpr int kPfVS = 32 + 4;    // LDS row stride (bf16) of the transposed V tile
+
+__global__ __launch_bounds__(kPfThreads) void attn_prefill_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const uint32_t* __restrict__ bitmask, float* __restrict__ out, int Hq, int Hkv, int Lq,
+    int L, int L_cap, int q_pos0, float scale_log2) {
+  constexpr int D = 128, R = 4;
+  const int nrb = (Lq + 31) / 32;
+  const int rb = blockIdx.x % nrb, bg = blockIdx.x / nrb;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int h = g * R + wid;
+  const int i0 = rb * 32;
+  const int ql = lane & 31, hi = lane >> 5;
+  const int qi = min(i0 + ql, Lq - 1);
+  const bool qvalid = i0 + ql < Lq;
+  const int nwords = (L + 31) / 32;
+  // the wave's 32 queries as the B operand: lane l: query l%32, d = 16s + 8(l/32) .. +8
+  bf16x8_t qf[8];
+  {
+    const bf16_t* qr = q + (((long long)b * Hq + h) * Lq + qi) * D + 8 * hi;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) qf[s8] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * s8));
+  }
+  const uint32_t* brow = bitmask + ((long long)bg * Lq + qi) * nwords;
+  const bf16_t* kb = k + (long long)bg * L_cap * D;
+  const bf16_t* vb = v + (long long)bg * L_cap * D;
+  // causal end of the block: its last row sees tokens < q_pos0 + last + 1
+  const int t_end = min(L, q_pos0 + min(i0 + 32, Lq));
+  __shared__ __align__(16) bf16_t Ks[32 * kPfKS];
+  __shared__ __align__(16) bf16_t Vt[D * kPfVS];
+  // staging roles: K chunks c = tid, tid + 256 (token c/16, d 8*(c%16)); V token pair
+  // tp = tid/16 (tokens 2tp, 2tp+1), d group dg = tid%16 (d 8dg .. 8dg+7)
+  const int kc0 = tid, kc1 = tid + kPfThreads;
+  const int tp = tid >> 4, dg = tid & 15;
+  uint4 rk0, rk1, rv0, rv1;
+  uint32_t wd_next;
+  auto gload = [&](int t0) {
+    const int a0 = min(t0 + (kc0 >> 4), L - 1), a1 = min(t0 + (kc1 >> 4), L - 1);
+    rk0 = *reinterpret_cast<const uint4*>(kb + (long long)a0 * D + (kc0 & 15) * 8);
+    rk1 = *reinterpret_cast<const uint4*>(kb + (long long)a1 * D + (kc1 & 15) * 8);
+    const int v0 = min(t0 + 2 * tp, L - 1), v1 = min(t0 + 2 * tp + 1, L - 1);
+    rv0 = *reinterpret_cast<const uint4*>(vb + (long long)v0 * D + dg * 8);
+    rv1 = *reinterpret_cast<const uint4*>(vb + (long long)v1 * D + dg * 8);
+    wd_next = brow[min(t0 >> 5, nwords - 1)];
+  };
+  float m = neg_inf(), l = 0.f;
+  f32x16_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  gload(0);
+  for (int t0 = 0; t0 < t_end; t0 += 32) {
+    const uint32_t wd = qvalid ? wd_next : 0u;
+    __syncthreads();   // the previous tile's readers are done
+    *reinterpret_cast<uint4*>(&Ks[(kc0 >> 4) * kPfKS + (kc0 & 15) * 8]) = rk0;
+    *reinterpret_cast<uint4*>(&Ks[(kc1 >> 4) * kPfKS + (kc1 & 15) * 8]) = rk1;
+    {
+      uint32_t* vw = reinterpret_cast<uint32_t*>(Vt);
+      const uint32_t x0[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
+      const uint32_t x1[4] = {rv1.x, rv1.y, rv1.z, rv1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vw[(8 * dg + 2 * j) * (kPfVS / 2) + tp] = (x0[j] & 0xffffu) | (x1[j] << 16);
+        vw[(8 * dg + 2 * j + 1) * (kPfVS / 2) + tp] = (x0[j] >> 16) | (x1[j] & 0xffff0000u);
+      }
+    }
+    __syncthreads();
+    gload(min(t0 + 32, t_end - 1));   // next tile in flight during this one
+    // S^T tile: 32 tokens x 32 queries
+    f32x16_t c;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[r] = 0.f;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[ql * kPfKS + 16 * s8 + 8 * hi]);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s8], c, 0, 0, 0);
+    }
+    // mask, online softmax of query ql (partner lane l ^ 32 holds the other 16 tokens)
+    float z[16], mt = neg_inf();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tt = 8 * (r >> 2) + 4 * hi + (r & 3);
+      z[r] = ((wd >> tt) & 1u) ? c[r] * scale_log2 : neg_inf();
+      mt = fmaxf(mt, z[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float alpha = (mn == neg_inf()) ? 1.f : fast_exp2(m - mn);
+    float pr[16], ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = (z[r] == neg_inf()) ? 0.f : fast_exp2(z[r] - mn);
+      ps += pr[r];
+    }
+    ps += __shfl_xor(ps, 32);
+    l = l * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    // P^T as the B operand of the two 16-token K steps
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)pr[8 * ks + e];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const bf16_t* vrow = &Vt[(db * 32 + ql) * kPfVS];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * ks + 4 * hi);
+        const bf16x4_t hi4 = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * ks + 8 + 4 * hi);
+        const bf16x8_t a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[db], 0, 0, 0);
+      }
+    }
+  }
+  // O^T: lane l holds query ql, d = 32 db + 8(r/4) + 4(l/32) + r%4
+  if (qvalid) {
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    float* orow = out + (((long long)b * Hq + h) * Lq + i0 + ql) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4 v4;
+        v4.x = o[db][4 * r4] * inv;
+        v4.y = o[db][4 * r4 + 1] * inv;
+        v4.z = o[db][4 * r4 + 2] * inv;
+        v4.w = o[db][4 * r4 + 3] * inv;
+        *reinterpret_cast<float4*>(orow + 32 * db + 8 * r4 + 4 * hi) = v4;
+      }
+  }
+}
+
 template <typename T, int D, int R>
 hipError_t bm_t(hipStream_t s, const void* q, const void* k, const void* v,
                 const uint32_t* bitmask, float* out, int B, int Hq, int Hkv, int Lq, int L,
                 int L_cap, int q_pos0, float scale) {
   const long long rows = (long long)B * Hkv * Lq;
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128 && R == 4) {
+    if (Lq >= 32) {
+      const long long blocks = (long long)B * Hkv * ((Lq + 31) / 32);
+      hipLaunchKernelGGL(attn_prefill_mfma_kernel, dim3((unsigned)blocks), dim3(kPfThreads), 0, s,
+                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, bitmask, out, Hq,
+                         Hkv, Lq, L, L_cap, q_pos0, scale * 1.4426950408889634f);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_bitmask_kernel<T, D, R>), dim3((unsigned)rows), dim3(kAttnThreads),
                      0, s, (const T*)q, (const T*)k, (const T*)v, bitmask, out, Hq, Hkv, Lq,
                      L, L_cap, q_pos0, scale * 1.4426950408889634f);
