@@ -368,14 +368,35 @@ __global__ __launch_bounds__(kGvThreads) void gemv_ln_w1_kernel(const bf16_t* __
   __shared__ float red[8 * kGvCols];
   __shared__ float tmp[kGvThreads / 64];
   for (int m = 0; m < M; ++m) {
+    // the row is held in registers: 16-byte pieces, all requested before the reductions
     const bf16_t* hr = h + (long long)m * K;
+    constexpr int kPieces = 4;   // rows up to 256 * 8 * 4 = 8192 elements
+    float hv[kPieces][8];
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+      const int e0 = (threadIdx.x + kGvThreads * u) * 8;
+      if (e0 < K) {
+        Vec16<bf16_t>::load(hr + e0, hv[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[u][e] = 0.f;
+      }
+    }
     float sum = 0.f;
-    for (int j = threadIdx.x; j < K; j += kGvThreads) sum += bf2f(hr[j]);
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += hv[u][e];
     const float mean = block_sum_f<kGvThreads>(sum, tmp) / (float)K;
     float v = 0.f;
-    for (int j = threadIdx.x; j < K; j += kGvThreads) {
-      const float d = bf2f(hr[j]) - mean;
-      v = fmaf(d, d, v);
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+      if ((threadIdx.x + kGvThreads * u) * 8 >= K) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = hv[u][e] - mean;
+        v = fmaf(d, d, v);
+      }
     }
     const float rstd = 1.0f / sqrtf(block_sum_f<kGvThreads>(v, tmp) / (float)K + eps);
     if (threadIdx.x < kGvK) xs[m][threadIdx.x] = bf2f(f2bf((bf2f(hr[k0 + threadIdx.x]) - mean) * rstd));
@@ -401,7 +422,14 @@ __global__ __launch_bounds__(kGvThreads) void gemv_relu_w2_kernel(const float* _
   const int m = threadIdx.x / kGvK, kk = threadIdx.x % kGvK;
   if (m < M) {
     float a = 0.f;
-    for (int s1 = 0; s1 < nslice1; ++s1) a += part1[((long long)s1 * M + m) * K + k0 + kk];
+    for (int s0 = 0; s0 < nslice1; s0 += 16) {
+      float pv[16];   // sixteen slices requested at once, summed in slice order
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        pv[u] = part1[((long long)min(s0 + u, nslice1 - 1) * M + m) * K + k0 + kk];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) a += (s0 + u < nslice1) ? pv[u] : 0.f;
+    }
     xs[m][kk] = bf2f(f2bf(fmaxf(a, 0.f)));
   }
   __syncthreads();
@@ -414,12 +442,18 @@ __global__ void gemv_out_kernel(const float* __restrict__ part2, int nslice2, bf
   if (e >= (long long)M * N) return;
   const int m = (int)(e / N), n = (int)(e % N);
   float a = 0.f;
-  for (int s2 = 0; s2 < nslice2; ++s2) a += part2[((long long)s2 * M + m) * N + n];
+  for (int s0 = 0; s0 < nslice2; s0 += 16) {
+    float pv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) pv[u] = part2[((long long)min(s0 + u, nslice2 - 1) * M + m) * N + n];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) a += (s0 + u < nslice2) ? pv[u] : 0.f;
+  }
   store_out(ep, q_imp, M, N, m, n, a);
 }
 
 bool use_gemv(int M, int E, int F, int N2) {
-  return M <= kGvMaxM && E % kGvK == 0 && F % kGvK == 0 && F % kGvCols == 0 &&
+  return M <= kGvMaxM && E <= kGvThreads * 8 * 4 && E % 8 == 0 && E % kGvK == 0 && F % kGvK == 0 && F % kGvCols == 0 &&
          N2 % kGvCols == 0;
 }
 

@@ -243,6 +243,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
 
 constexpr int kMbThreads = 256;
 constexpr int kMbWaves = kMbThreads / 64;
+constexpr int kFinStage = 2048;   // second-digit candidates gathered in LDS
 
 // Block-wide sums of three ints over the kMbThreads threads; every thread gets the totals.
 __device__ __forceinline__ int3 block_sum3(int a, int b, int c, int3* tmp) {
@@ -281,8 +282,10 @@ __device__ __forceinline__ int3 block_sum3(int a, int b, int c, int3* tmp) {
 int kpt_for(int L) { return L <= BUTLER_SEL_KPT_SPLIT ? BUTLER_SEL_KPT_LO : BUTLER_SEL_KPT_HI; }
 
 struct RowState {
-  uint32_t b1;  // first-digit bin of the x-th largest key
-  int need;     // rank of the x-th largest key inside that bin (1-based)
+  uint32_t b1;     // first-digit bin of the x-th largest key
+  int need;        // rank of the x-th largest key inside that bin (1-based)
+  uint32_t epoch;  // this call's number: which second-digit histogram is live
+  uint32_t pad;
 };
 
 struct MbWs {
@@ -291,6 +294,10 @@ struct MbWs {
   RowState* state;               // [rows]
   int* defcnt;                   // [rows][nchunk] tokens of the chunk that are surely selected
   int* ncand;                    // [rows][nchunk] candidates the chunk appended
+  uint32_t* epoch;               // [rows]         calls made so far (never reset)
+  uint32_t* hist2;               // [2][rows][2048] second-digit (key bits 20..10) counts of
+                                 //                the candidates; buffer epoch % 2 is filled,
+                                 //                the other one is zero
   uint2* cand;                   // [rows][L]      ring of (key, index | sink/window flag << 31)
 };
 
@@ -304,7 +311,8 @@ long long nchunk_for(int L) {
 size_t mb_bytes(long long rows, int L) {
   const long long nchunk = nchunk_for(L);
   return al256(rows * 2048 * 4) + al256(rows * 8) + al256(rows * sizeof(RowState)) +
-         2 * al256(rows * nchunk * 4) + al256((size_t)rows * L * sizeof(uint2));
+         2 * al256(rows * nchunk * 4) + al256(rows * 4) + al256(2 * rows * 2048 * 4) +
+         al256((size_t)rows * L * sizeof(uint2));
 }
 
 MbWs carve(void* ws, long long rows, int L) {
@@ -316,6 +324,8 @@ MbWs carve(void* ws, long long rows, int L) {
   w.state = (RowState*)p;                 p += al256(rows * sizeof(RowState));
   w.defcnt = (int*)p;                     p += al256(rows * nchunk * sizeof(int));
   w.ncand = (int*)p;                      p += al256(rows * nchunk * sizeof(int));
+  w.epoch = (uint32_t*)p;                 p += al256(rows * 4);
+  w.hist2 = (uint32_t*)p;                 p += al256(2 * rows * 2048 * 4);
   w.cand = (uint2*)p;
   return w;
 }
@@ -417,15 +427,16 @@ __device__ __forceinline__ void wave_find_top(const uint32_t* __restrict__ gh, i
   rest = __shfl(r, src);
 }
 
-// One wave resolves, from the row's n <= 64*Q candidates (every one has first digit b1,
-// and the need-th largest of them is the x-th largest key of the row), tau bit by bit from
-// bit 20 down -- a ballot count of the candidates that carry the trial bit -- then, when
+// One wave resolves, from n <= 64*Q candidates (all share the key bits above top_bit,
+// given in prefix, and the need-th largest of them is the x-th largest key of the row;
+// crow[(base + j) mod L] is candidate j, in global memory or LDS), tau bit by bit from
+// top_bit down -- a ballot count of the candidates that carry the trial bit -- then, when
 // the budget splits the keys equal to tau, the tie cut bit by bit over their indices
 // (lowest indices first), and the counts of the selected candidates that are not sink /
 // window tokens: all of them, and those before index c_lo.
 template <int Q>
-__device__ void wave_resolve(const uint2* __restrict__ crow, int base, int n, int L,
-                             uint32_t b1, int need, int c_lo, uint32_t& tau, int& tie_cut,
+__device__ void wave_resolve(const uint2* crow, int base, int n, int L, uint32_t prefix,
+                             int top_bit, int need, int c_lo, uint32_t& tau, int& tie_cut,
                              int& sel_all, int& sel_before) {
   const int lane = threadIdx.x & 63;
   uint32_t ck[Q], ci[Q];
@@ -439,9 +450,9 @@ __device__ void wave_resolve(const uint2* __restrict__ crow, int base, int n, in
     ck[q] = c.x;
     ci[q] = c.y;
   }
-  uint32_t P = b1 << 21;
+  uint32_t P = prefix;
   int kk = need;
-  for (int bit = 20; bit >= 0; --bit) {
+  for (int bit = top_bit; bit >= 0; --bit) {
     const uint32_t hi = 0xffffffffu << (bit + 1);
     int c1 = 0;
 #pragma unroll
@@ -578,10 +589,12 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
   for (int j = 0; j < KPT; ++j) f[j] = srow[min(c_lo + (int)threadIdx.x + kMbThreads * j, L - 1)];
   uint32_t b1 = 0u;
   int need = 0;
+  const uint32_t epoch = w.epoch[row];
   if (mode == kModeNormal) {
     wave_find_top(ghist + (long long)row * 2048, k, b1, need);
-    if (chunk == 0 && threadIdx.x == 0) w.state[row] = RowState{b1, need};
+    if (chunk == 0 && threadIdx.x == 0) w.state[row] = RowState{b1, need, epoch, 0u};
   }
+  uint32_t* h2 = w.hist2 + ((long long)(epoch & 1u) * rows + row) * 2048;
   const int w_lo = max(0, L - n_window);
   int ndef = 0, ncw = 0;
   unsigned long long cm[KPT];
@@ -604,6 +617,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
     ndef += def ? 1 : 0;
     cm[j] = __ballot(cand);
     ncw += __popcll(cm[j]);
+    if (cand) atomicAdd(&h2[(key[j] >> 10) & 2047u], 1u);
   }
   ndef = wave_sum_i(ndef);
   // one atomic per workgroup (same-address atomics serialise): the waves' counts meet in LDS
@@ -675,6 +689,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
   __shared__ int3 tmp3[kMbWaves];
   __shared__ int sh[2];
   __shared__ int s_wc[NWD];
+  __shared__ uint2 s_c[kFinStage];
   const int c_lo = chunk * kMbThreads * KPT;
   const float* srow = scores + (long long)row * L;
   float f[KPT];
@@ -698,9 +713,15 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
   n = wave_sum_i(n);
   def_all = wave_sum_i(def_all);
   def_before = wave_sum_i(def_before);
+  const uint32_t epoch = w.epoch[row];   // not advanced before this kernel ends
   if (chunk == 0) {
+    // clear the first-digit histogram and the second-digit one the next call fills
     uint32_t* gh = ghist + (long long)row * 2048;
-    for (int j = threadIdx.x; j < 2048; j += kMbThreads) gh[j] = 0u;
+    uint32_t* h2n = w.hist2 + ((long long)((epoch + 1u) & 1u) * rows + row) * 2048;
+    for (int j = threadIdx.x; j < 2048; j += kMbThreads) {
+      gh[j] = 0u;
+      h2n[j] = 0u;
+    }
   }
   uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;
   int tie_cut = -1;
@@ -708,19 +729,67 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
   if (mode == kModeNormal && n > 0) {
     const int base = (int)((end - (unsigned long long)n) % (unsigned long long)L);
     const uint2* crow = w.cand + (long long)row * L;
-#define BUTLER_RESOLVE(QQ) \
-  wave_resolve<QQ>(crow, base, n, L, st.b1, st.need, c_lo, tau, tie_cut, sel_all, sel_before)
-    if (n <= 64) BUTLER_RESOLVE(1);
-    else if (n <= 128) BUTLER_RESOLVE(2);
-    else if (n <= 256) BUTLER_RESOLVE(4);
-    else if (n <= 512) BUTLER_RESOLVE(8);
-    else if (n <= 1024) BUTLER_RESOLVE(16);
-    else if (n <= 2048) BUTLER_RESOLVE(32);
-    else
-      block_resolve(crow, base, n, L, st.b1, st.need, c_lo, h, tmp, tmp3, sh, tau, tie_cut,
-                    sel_all, sel_before);
+#define BUTLER_RESOLVE(QQ, SRC, BASE, NN, LL, PRE, BIT, NEED, SA, SB) \
+  wave_resolve<QQ>(SRC, BASE, NN, LL, PRE, BIT, NEED, c_lo, tau, tie_cut, SA, SB)
+    if (n <= 256) {
+      const uint32_t pre = st.b1 << 21;
+      if (n <= 64) BUTLER_RESOLVE(1, crow, base, n, L, pre, 20, st.need, sel_all, sel_before);
+      else if (n <= 128) BUTLER_RESOLVE(2, crow, base, n, L, pre, 20, st.need, sel_all, sel_before);
+      else BUTLER_RESOLVE(4, crow, base, n, L, pre, 20, st.need, sel_all, sel_before);
+    } else {
+      // many candidates: the second digit from the chunk pass's histogram, then one scan
+      // that counts the selected candidates above it and gathers the ones inside it
+      uint32_t b2;
+      int need2;
+      wave_find_top(w.hist2 + ((long long)(st.epoch & 1u) * rows + row) * 2048, st.need, b2,
+                    need2);
+      const uint32_t p22 = (st.b1 << 11) | b2;
+      if (threadIdx.x == 0) sh[0] = 0;
+      __syncthreads();
+      int a_all = 0, a_before = 0;
+      for (int j0 = 0; j0 < n; j0 += kMbThreads * 8) {
+        uint2 cc[8];   // eight candidates per thread requested at once
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int pj = base + min(j0 + (int)threadIdx.x + kMbThreads * u, n - 1);
+          cc[u] = crow[pj >= L ? pj - L : pj];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (j0 + (int)threadIdx.x + kMbThreads * u >= n) continue;
+          const uint2 c = cc[u];
+          const uint32_t k22 = c.x >> 10;
+          if (k22 > p22) {
+            if (!(c.y & 0x80000000u)) {
+              ++a_all;
+              a_before += ((int)c.y < c_lo) ? 1 : 0;
+            }
+          } else if (k22 == p22) {
+            const int slot = atomicAdd(&sh[0], 1);
+            if (slot < kFinStage) s_c[slot] = c;
+          }
+        }
+      }
+      const int3 ab = block_sum3(a_all, a_before, 0, tmp3);
+      const int m2 = sh[0];
+      if (m2 <= kFinStage) {
+        int s2a = 0, s2b = 0;
+        const uint32_t pre = p22 << 10;
+        if (m2 <= 64) BUTLER_RESOLVE(1, s_c, 0, m2, kFinStage, pre, 9, need2, s2a, s2b);
+        else if (m2 <= 256) BUTLER_RESOLVE(4, s_c, 0, m2, kFinStage, pre, 9, need2, s2a, s2b);
+        else if (m2 <= 1024) BUTLER_RESOLVE(16, s_c, 0, m2, kFinStage, pre, 9, need2, s2a, s2b);
+        else BUTLER_RESOLVE(32, s_c, 0, m2, kFinStage, pre, 9, need2, s2a, s2b);
+        sel_all = ab.x + s2a;
+        sel_before = ab.y + s2b;
+      } else {
+        // a flood of equal keys: the whole workgroup runs radix passes over the ring
+        block_resolve(crow, base, n, L, st.b1, st.need, c_lo, h, tmp, tmp3, sh, tau, tie_cut,
+                      sel_all, sel_before);
+      }
+    }
 #undef BUTLER_RESOLVE
   }
+  if (chunk == 0 && threadIdx.x == 0) w.epoch[row] = epoch + 1u;
   if (chunk == 0 && threadIdx.x == 0) count[row] = def_all + sel_all;
   const int w_lo = max(0, L - n_window);
   unsigned long long sm[KPT];
