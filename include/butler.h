@@ -121,12 +121,13 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
  * tokens [0, L).
  *
  *   scores     [B, Hkv, Lq, L]     float32 (written)
- *   radix_hist [B, Hkv, Lq, 2048]  uint32, optional (NULL = none).  When given, the count
- *              of every written score (t < row length) is added to bin key >> 21, where
- *              key is the score's order-preserving 32-bit key (bits of the float with
- *              -0 taken as +0 and NaN as -inf; sign set: all bits flipped, else the sign
- *              bit set).  The caller zero-fills it before its first use; passing it on to
- *              butler_select_topk spares the selection one pass over the scores, and
+ *   radix_hist [B, Hkv, Lq, 2048]  uint32, optional (NULL = none), used by single-row
+ *              (Lq == 1) calls only; multi-row calls leave it untouched.  When used, the
+ *              count of every written score (t < row length) is added to bin key >> 21,
+ *              where key is the score's order-preserving 32-bit key (bits of the float
+ *              with -0 taken as +0 and NaN as -inf; sign set: all bits flipped, else the
+ *              sign bit set).  The caller zero-fills it before its first use; passing it
+ *              on to butler_select_topk spares the selection one pass over the scores, and
  *              butler_select_topk leaves it zero-filled again.
  * RAW: d' in {16, 32}; SOFTVOTE: D in {64, 128}, Lq == 1 (decode); R in {1, 2, 4, 8}.
  * workspace: SOFTVOTE keeps per-token logits and per-block softmax partials.
@@ -156,7 +157,8 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
  *   radix_hist [B, Hkv, Lq, 2048]    uint32, optional: the histogram butler_score built for
  *                                    exactly these scores (see butler_score); it is used
  *                                    instead of a counting pass and zero-filled again.  NULL:
- *                                    the selection counts by itself.
+ *                                    the selection counts by itself.  Multi-row (Lq > 1)
+ *                                    calls ignore it, as butler_score does.
  *   idx     [B, Hkv, Lq, cap]        int32   (written) -- cap >= min(L, x + n_sink + n_window)
  *   bitmask [B, Hkv, Lq, ceil(L/32)] uint32  (written)
  *   count   [B, Hkv, Lq]             int32   (written)

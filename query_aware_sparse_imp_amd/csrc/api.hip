@@ -131,11 +131,13 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
   if (!aligned16(q) || !aligned16(keys) || !aligned16(scores)) return BUTLER_ERR_INVALID_ARG;
   if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
+  // the first-digit histogram is a decode-row hand-off; multi-row calls leave it untouched
+  uint32_t* hist = (Lq > 1) ? nullptr : radix_hist;
   if (mode == BUTLER_SCORE_RAW)
     return finish(s, launch_score_raw(s, dtype, q, keys, scores, B, Hq, Hkv, G, slot, Lq, L,
-                                      L_cap, dk, q_pos0, causal, radix_hist));
+                                      L_cap, dk, q_pos0, causal, hist));
   return finish(s, launch_score_softvote(s, dtype, q, keys, scores, B, Hq, Hkv, L, L_cap, dk,
-                                         softmax_scale, workspace, radix_hist));
+                                         softmax_scale, workspace, hist));
 }
 
 int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist, int budget_num,
@@ -164,8 +166,9 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist, 
   if (!aligned16(scores)) return BUTLER_ERR_INVALID_ARG;
   if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
+  uint32_t* hist = (Lq > 1) ? nullptr : radix_hist;   // see butler_score
   return finish(s, launch_select(s, scores, budget_num, budget_den, n_sink, n_window, idx,
-                                 bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, radix_hist,
+                                 bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, hist,
                                  workspace));
 }
 

@@ -256,6 +256,133 @@ __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// multi-row raw scores (prefill chunks) on the matrix cores, still exact
+// ---------------------------------------------------------------------------
+// S[i][t] = qbar[i] . K_imp[t] for a block of query rows against every token is a dense
+// contraction over d'.  v_mfma_f64_16x16x4f64 keeps it exact: the operands are exact in
+// float64 (qbar is a float64 sum of R bf16 values, K_imp is bf16), every product and
+// partial sum is exact, so the accumulation order does not matter and the one rounding
+// to float32 gives the same bits as the decode kernel and the oracle.
+// Layout of the f64 MFMA (checked on the device): A lane l = A[l%16][l/16], B lane l =
+// B[l/16][l%16], accumulator r of lane l = C[4r + l/16][l%16].  The d' index is permuted
+// so that lane group g4 = l/16 feeds d' = KG*g4 + s at step s (KG = d'/4): each lane then
+// reads KG consecutive K_imp elements of its token with one load.
+// A workgroup holds 64 query rows (qbar in VGPRs, 16 x 16 tiles of 4 x 4 per wave) and
+// its 4 waves sweep 1024 tokens, 64 per wave step; tiles past every row's causal end are
+// written as -inf without arithmetic.
+
+constexpr int kCsThreads = 256;
+constexpr int kCsRows = 64;
+constexpr int kCsTokBlk = 1024;
+
+typedef __attribute__((ext_vector_type(4))) double f64x4_t;
+
+template <int DP>
+__global__ __launch_bounds__(kCsThreads) void score_rows_mfma_kernel(
+    const bf16_t* __restrict__ q_imp, const bf16_t* __restrict__ kimp, float* __restrict__ scores,
+    int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal) {
+  constexpr int KG = DP / 4;   // d' values per lane group
+  const int bg = blockIdx.z, i0 = blockIdx.y * kCsRows;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int R = Hq / Hkv;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int ql = lane & 15, g4 = lane >> 4;
+  // qbar[qb][s] = sum over the group's heads of Q_imp[row i0 + 16qb + ql][KG*g4 + s]
+  double qa[4][KG];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    const int i = min(i0 + 16 * qb + ql, Lq - 1);
+    float hv[8][KG];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const int hh = min(h, R - 1);
+      const bf16_t* src = q_imp + ((((long long)b * Hq + g * R + hh) * G + slot) * Lq + i) * DP + KG * g4;
+      if constexpr (KG == 8) {
+        Vec16<bf16_t>::load(src, hv[h]);
+      } else {
+        const uint2 raw = *reinterpret_cast<const uint2*>(src);
+        hv[h][0] = bf2f((bf16_t)(raw.x & 0xffffu));
+        hv[h][1] = bf2f((bf16_t)(raw.x >> 16));
+        hv[h][2] = bf2f((bf16_t)(raw.y & 0xffffu));
+        hv[h][3] = bf2f((bf16_t)(raw.y >> 16));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < KG; ++e) {
+      double a = 0.0;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) a += (h < R) ? (double)hv[h][e] : 0.0;
+      qa[qb][e] = a;
+    }
+  }
+  const bf16_t* kb = kimp + (long long)bg * L_cap * DP + KG * g4;
+  float* srow0 = scores + ((long long)bg * Lq) * L;
+  const int i_last = min(i0 + kCsRows, Lq) - 1;
+  const int t_vis = causal ? min(L, q_pos0 + i_last + 1) : L;   // tokens any row sees
+  for (int it = 0; it < kCsTokBlk / (64 * 4); ++it) {
+    const int t0 = blockIdx.x * kCsTokBlk + (it * 4 + wid) * 64;
+    if (t0 >= L) break;
+    const bool live = t0 < t_vis;
+    f64x4_t acc[4][4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[qb][tb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    if (live) {
+      float kv[4][KG];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const bf16_t* src = kb + (long long)min(t0 + 16 * tb + ql, L - 1) * DP;
+        if constexpr (KG == 8) {
+          Vec16<bf16_t>::load(src, kv[tb]);
+        } else {
+          const uint2 raw = *reinterpret_cast<const uint2*>(src);
+          kv[tb][0] = bf2f((bf16_t)(raw.x & 0xffffu));
+          kv[tb][1] = bf2f((bf16_t)(raw.x >> 16));
+          kv[tb][2] = bf2f((bf16_t)(raw.y & 0xffffu));
+          kv[tb][3] = bf2f((bf16_t)(raw.y >> 16));
+        }
+      }
+#pragma unroll
+      for (int s8 = 0; s8 < KG; ++s8)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+            acc[qb][tb] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[qb][s8], (double)kv[tb][s8],
+                                                               acc[qb][tb], 0, 0, 0);
+    }
+    // accumulator r of tile (qb, tb): row i0 + 16qb + 4r + g4, token t0 + 16tb + ql
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 16 * qb + 4 * r + g4;
+        if (i >= Lq) continue;
+        const int lim = causal ? min(L, q_pos0 + i + 1) : L;
+        float* srow = srow0 + (long long)i * L;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const int t = t0 + 16 * tb + ql;
+          if (t < L) srow[t] = (t < lim) ? (float)acc[qb][tb][r] : neg_inf();
+        }
+      }
+  }
+}
+
+template <int DP>
+hipError_t rows_t(hipStream_t s, const void* q_imp, const void* kimp, float* scores, int B,
+                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
+                  int causal) {
+  dim3 grid((L + kCsTokBlk - 1) / kCsTokBlk, (Lq + kCsRows - 1) / kCsRows, B * Hkv);
+  hipLaunchKernelGGL((score_rows_mfma_kernel<DP>), grid, dim3(kCsThreads), 0, s,
+                     (const bf16_t*)q_imp, (const bf16_t*)kimp, scores, Hq, Hkv, G, slot, Lq, L,
+                     L_cap, q_pos0, causal);
+  return hipGetLastError();
+}
+
 template <typename T, int DP>
 hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scores, int B,
                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
@@ -291,11 +418,18 @@ hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int 
   return hipGetLastError();
 }
 
+bool R_ok(int Hq, int Hkv) { return Hq % Hkv == 0 && Hq / Hkv <= 8; }
+
 }  // namespace
 
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
                             int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist) {
+  if (dtype == 1 && Lq > 1 && R_ok(Hq, Hkv)) {
+    // several query rows: the matrix-core kernel (it builds no first-digit histogram)
+    if (dp == 32) return rows_t<32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
+    if (dp == 16) return rows_t<16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
+  }
   if (dtype == 1) {
     if (dp == 32) return raw_t<bf16_t, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);
     if (dp == 16) return raw_t<bf16_t, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);

@@ -93,6 +93,7 @@ def _prefill_case(w, L, chunk):
         qa.butler_sparse_decode_attn(q_d[:, :, c0:c0 + Lq].contiguous(), k_d, v_d, out, L=Lk,
                                      bitmask=bm, q_pos0=c0, softmax_scale=w.scale)
         torch.cuda.synchronize()
+        assert int(hist.abs().sum()) == 0, "multi-row calls leave the histogram untouched"
         got_s = np64(scores)
         want_s = oracle.score_raw(qi[:, :, c0:c0 + Lq], kn[:, :, :Lk], w.Hkv, causal=True,
                                   q_pos0=c0)
