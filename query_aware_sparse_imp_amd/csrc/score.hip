@@ -18,6 +18,8 @@
 //   base-2 logits of the R heads and a per-block (max, sum of exp2) pair per head.
 //   Pass 2 merges the block pairs in block order (every block computes the same
 //   merge) and turns the stored logits into the summed probabilities.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -219,6 +221,88 @@ __global__ __launch_bounds__(kSvThreads) void softvote_logits_kernel(
   }
 }
 
+
+// bf16, D = 128: logits on the matrix cores.  v_mfma_f32_16x16x32_bf16 with 16 key rows as
+// A and the group's R query heads as the B columns (columns >= R are zero); lane
+// (quad, pe) then holds the logits of tokens 4*quad + r of the tile for head pe.  A wave
+// takes 64 tokens (4 tiles), all 16 of its 16-byte key loads issued first.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8s_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4s_t;
+
+template <int R>
+__global__ __launch_bounds__(kSvThreads) void softvote_logits_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, float* __restrict__ logits,
+    float2* __restrict__ part, int Hq, int Hkv, int L, int L_cap, float scale_log2, int nblk) {
+  constexpr int D = 128;
+  const int bg = blockIdx.y, blk = blockIdx.x;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int quad = lane >> 4, pe = lane & 15;
+  const int tw = blk * kSvTokensPerBlock + wid * 64;
+  const bf16_t* kb = k + (size_t)bg * L_cap * D + 8 * quad;
+  uint4 kr[4][4];
+#pragma unroll
+  for (int tile = 0; tile < 4; ++tile) {
+    const int t = min(tw + tile * 16 + pe, L - 1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      kr[tile][kk] = *reinterpret_cast<const uint4*>(kb + (size_t)t * D + kk * 32);
+  }
+  bf16x8s_t qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (pe < R)
+      raw = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + g * R + pe) * D + kk * 32 + 8 * quad);
+    qf[kk] = __builtin_bit_cast(bf16x8s_t, raw);
+  }
+  float z[4][4];
+  float mloc = neg_inf();
+#pragma unroll
+  for (int tile = 0; tile < 4; ++tile) {
+    f32x4s_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8s_t, kr[tile][kk]),
+                                                   qf[kk], c, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tw + tile * 16 + 4 * quad + r;
+      z[tile][r] = (t < L) ? c[r] * scale_log2 : neg_inf();
+      mloc = fmaxf(mloc, z[tile][r]);
+    }
+  }
+  float* zb = logits + ((size_t)bg * R + min(pe, R - 1)) * L;
+  float lloc = 0.f;
+#pragma unroll
+  for (int tile = 0; tile < 4; ++tile)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tw + tile * 16 + 4 * quad + r;
+      if (pe < R && t < L) zb[t] = z[tile][r];
+      lloc += (z[tile][r] == neg_inf()) ? 0.f : fast_exp2(z[tile][r] - mloc);
+    }
+  // the four quads of a head, then the waves
+  float m = mloc, l = lloc;
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) {
+    const float m2 = __shfl_xor(m, o, 64), l2 = __shfl_xor(l, o, 64);
+    merge_ml(m, l, m2, l2);
+  }
+  __shared__ float sm[kSvThreads / 64][16], sl[kSvThreads / 64][16];
+  if (quad == 0) {
+    sm[wid][pe] = m;
+    sl[wid][pe] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x < R) {
+    const int r = threadIdx.x;
+    float mm = sm[0][r], ll = sl[0][r];
+    for (int w = 1; w < kSvThreads / 64; ++w) merge_ml(mm, ll, sm[w][r], sl[w][r]);
+    part[((size_t)bg * nblk + blk) * R + r] = make_float2(mm, ll);
+  }
+}
+
 template <int R>
 __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
     const float* __restrict__ logits, const float2* __restrict__ part,
@@ -228,15 +312,40 @@ __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
   __shared__ uint32_t hist[2048];
   if (radix_hist)
     for (int j = threadIdx.x; j < 2048; j += kSvThreads) hist[j] = 0u;
-  if (threadIdx.x < R) {
-    const int r = threadIdx.x;
-    float mm = neg_inf(), ll = 0.f;
-    for (int j = 0; j < nblk; ++j) {
-      const float2 p = part[((size_t)bg * nblk + j) * R + r];
-      merge_ml(mm, ll, p.x, p.y);
+  // the row's per-block (max, sum) pairs of every head: thread j merges blocks j, j+256,
+  // ... in order, then a butterfly over the wave and the waves in order (deterministic)
+  {
+    float mm[R], ll[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) { mm[r] = neg_inf(); ll[r] = 0.f; }
+    for (int j = threadIdx.x; j < nblk; j += kSvThreads) {
+      float2 p[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) p[r] = part[((size_t)bg * nblk + j) * R + r];
+#pragma unroll
+      for (int r = 0; r < R; ++r) merge_ml(mm[r], ll[r], p[r].x, p[r].y);
     }
-    Ms[r] = mm;
-    Ls[r] = ll;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(mm[r], o, 64), l2 = __shfl_xor(ll[r], o, 64);
+        merge_ml(mm[r], ll[r], m2, l2);
+      }
+    }
+    __shared__ float wm[kSvThreads / 64][R], wl[kSvThreads / 64][R];
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) { wm[threadIdx.x >> 6][r] = mm[r]; wl[threadIdx.x >> 6][r] = ll[r]; }
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+      const int r = threadIdx.x;
+      float m0 = wm[0][r], l0 = wl[0][r];
+      for (int w = 1; w < kSvThreads / 64; ++w) merge_ml(m0, l0, wm[w][r], wl[w][r]);
+      Ms[r] = m0;
+      Ls[r] = l0;
+    }
   }
   __syncthreads();
   const float* zb = logits + (size_t)bg * R * L;
@@ -410,9 +519,15 @@ hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int 
   float2* part = (float2*)(logits + (size_t)B * Hkv * R * L);
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid(nblk, B * Hkv);
-  hipLaunchKernelGGL((softvote_logits_kernel<T, D, R>), grid, dim3(kSvThreads), 0, s,
-                     (const T*)q, (const T*)k, logits, part, Hq, Hkv, L, L_cap, scale_log2,
-                     nblk);
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
+    hipLaunchKernelGGL((softvote_logits_mfma_kernel<R>), grid, dim3(kSvThreads), 0, s,
+                       (const bf16_t*)q, (const bf16_t*)k, logits, part, Hq, Hkv, L, L_cap,
+                       scale_log2, nblk);
+  } else {
+    hipLaunchKernelGGL((softvote_logits_kernel<T, D, R>), grid, dim3(kSvThreads), 0, s,
+                       (const T*)q, (const T*)k, logits, part, Hq, Hkv, L, L_cap, scale_log2,
+                       nblk);
+  }
   hipLaunchKernelGGL((softvote_combine_kernel<R>), grid, dim3(kSvThreads), 0, s, logits, part,
                      scores, L, nblk, hist);
   return hipGetLastError();
