@@ -829,6 +829,8 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
   }
 }
 
+
+
 bool use_chunked(int Lq, int L, int causal) {
   return !causal && Lq == 1 && L > 4096;
 }
@@ -866,24 +868,19 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
     }
     return hipGetLastError();
   }
-  // one workgroup per row; the widest rows get 1024 threads x 64 keys
-  if (L <= 4096) {
-    hipLaunchKernelGGL((select_row_kernel<256, 16>), dim3((unsigned)rows), dim3(256), 0, s,
-                       scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
-                       q_pos0, causal, hist);
-  } else if (L <= 16384) {
-    hipLaunchKernelGGL((select_row_kernel<512, 32>), dim3((unsigned)rows), dim3(512), 0, s,
-                       scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
-                       q_pos0, causal, hist);
-  } else if (L <= 32768) {
-    hipLaunchKernelGGL((select_row_kernel<1024, 32>), dim3((unsigned)rows), dim3(1024), 0, s,
-                       scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
-                       q_pos0, causal, hist);
-  } else {
-    hipLaunchKernelGGL((select_row_kernel<1024, 64>), dim3((unsigned)rows), dim3(1024), 0, s,
-                       scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,
-                       q_pos0, causal, hist);
-  }
+  // one workgroup per row, sized to the row: 16 or 32 keys per thread, 64 to 1024 threads
+#define BUTLER_SR(NT, KPT)                                                                 \
+  hipLaunchKernelGGL((select_row_kernel<NT, KPT>), dim3((unsigned)rows), dim3(NT), 0, s,   \
+                     scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,   \
+                     q_pos0, causal, hist)
+  if (L <= 1024) BUTLER_SR(64, 16);
+  else if (L <= 2048) BUTLER_SR(128, 16);
+  else if (L <= 4096) BUTLER_SR(256, 16);
+  else if (L <= 8192) BUTLER_SR(256, 32);
+  else if (L <= 16384) BUTLER_SR(512, 32);
+  else if (L <= 32768) BUTLER_SR(1024, 32);
+  else BUTLER_SR(1024, 64);
+#undef BUTLER_SR
   return hipGetLastError();
 }
 
