@@ -262,10 +262,13 @@ def graph_time(fns, reps):
     return (time.perf_counter() - t0) / reps
 
 
-def run_softvote(device):
+def run_softvote(device, cache_threshold=None):
     """Batched decode with the soft-voting scorer: B=16, L=16384, 30% + 4 + 64, the 64
     steps of the query walk, each step = score (TokenSelect soft votes over all L keys),
-    select, attend.  One graph holds the 64 steps."""
+    select, attend.  One graph holds the 64 steps.  With cache_threshold, every step first
+    runs the selection cache (TokenSelect's Selection Cache; the threshold is not on the
+    pages), and score and select skip the (b, KV head) rows whose cached selection stands;
+    the reference queries start from zero at the first step of every replay."""
     import torch
     import synthetic
     import query_aware_sparse_imp_amd as qa
@@ -282,27 +285,52 @@ def run_softvote(device):
     idx = torch.empty(w.B, w.Hkv, 1, cap, dtype=torch.int32, device=device)
     cnt = torch.empty(w.B, w.Hkv, 1, dtype=torch.int32, device=device)
     out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
+    cached = cache_threshold is not None
+    q_ref = torch.zeros_like(qs[0]) if cached else None
+    keep = torch.zeros(w.B, w.Hkv, dtype=torch.int32, device=device) if cached else None
 
     def step(q):
-        return [lambda: qa.butler_score(qa.BUTLER_SCORE_SOFTVOTE, q, k, scores, Hkv=w.Hkv,
-                                        L=w.L, softmax_scale=w.scale, radix_hist=hist),
-                lambda: qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink,
-                                              w.n_window, cnt, idx=idx, radix_hist=hist),
-                lambda: qa.butler_sparse_decode_attn(q, k, v, out, L=w.L, idx=idx, count=cnt,
-                                                     softmax_scale=w.scale)]
-    fns = [f for q in qs for f in step(q)]
+        fs = [lambda: qa.butler_score(qa.BUTLER_SCORE_SOFTVOTE, q, k, scores, Hkv=w.Hkv,
+                                      L=w.L, softmax_scale=w.scale, radix_hist=hist,
+                                      keep=keep),
+              lambda: qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink,
+                                            w.n_window, cnt, idx=idx, radix_hist=hist,
+                                            keep=keep),
+              lambda: qa.butler_sparse_decode_attn(q, k, v, out, L=w.L, idx=idx, count=cnt,
+                                                   softmax_scale=w.scale)]
+        if cached:
+            fs.insert(0, lambda: qa.butler_selection_cache(q, q_ref, keep, Hkv=w.Hkv,
+                                                           threshold=cache_threshold))
+        return fs
+    res = {"workload": w.name, "steps": len(qs)}
+    if cached:
+        # the fraction of (step, b, KV head) rows whose selection was reused (eager pass)
+        q_ref.zero_()
+        kept = 0
+        for q in qs:
+            for f in step(q):
+                f()
+            kept += int(keep.sum())
+        res["selection_cache"] = {"threshold": cache_threshold,
+                                  "kept_fraction": kept / (len(qs) * w.B * w.Hkv)}
+        fns = [lambda: q_ref.zero_()] + [f for q in qs for f in step(q)]
+    else:
+        fns = [f for q in qs for f in step(q)]
     sec = graph_time(fns, 1) / len(qs)
     n_sel = int(cnt.sum())
-    st = [step(q) for q in qs]
-    phase = {"score+select": graph_time([f for s3 in st for f in s3[:2]], 1) / len(qs),
-             "attn": graph_time([s3[2] for s3 in st], 1) / len(qs)}
+    if not cached:
+        st = [step(q) for q in qs]
+        phase = {"score+select": graph_time([f for s3 in st for f in s3[:2]], 1) / len(qs),
+                 "attn": graph_time([s3[2] for s3 in st], 1) / len(qs)}
+        res["phase_us"] = {kk: round(vv * 1e6, 1) for kk, vv in phase.items()}
     elt = 2
     byts = w.B * w.Hkv * w.L * w.D * elt + n_sel * (2 * w.D * elt + 8) + w.B * w.Hq * w.D * (elt + 4)
     del k, v
-    return {"workload": w.name, "steps": len(qs), "steps_per_s": 1.0 / sec,
-            "ms_per_step": sec * 1e3, "phase_us": {kk: round(vv * 1e6, 1) for kk, vv in phase.items()},
-            "algorithmic_bytes": byts,
-            "GB/s": byts / sec / 1e9, "frac_of_hbm_peak": byts / sec / 1e9 / HBM_PEAK_GBS}
+    res.update({"steps_per_s": 1.0 / sec, "ms_per_step": sec * 1e3})
+    if not cached:
+        res.update({"algorithmic_bytes": byts, "GB/s": byts / sec / 1e9,
+                    "frac_of_hbm_peak": byts / sec / 1e9 / HBM_PEAK_GBS})
+    return res
 
 
 def _rope_t(x, base=500000.0):
@@ -537,6 +565,7 @@ def main(argv=None) -> int:
         log(f"[bench] workload {c}")
         if c == "3":
             others["softvote_decode"] = run_softvote(dev)
+            others["softvote_decode_selection_cache"] = run_softvote(dev, cache_threshold=0.98)
         elif c == "4":
             others["full_depth_decode"] = run_full_depth(max(a.steps // 40, 3), dev)
         elif c == "5":

@@ -129,11 +129,15 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
  *              sign bit set).  The caller zero-fills it before its first use; passing it
  *              on to butler_select_topk spares the selection one pass over the scores, and
  *              butler_select_topk leaves it zero-filled again.
+ *   keep       [B, Hkv]            int32, optional (NULL = none), single-row calls only:
+ *              rows of a (b, KV head) with keep != 0 are skipped -- their scores (and
+ *              radix_hist) are left as they were (see butler_selection_cache).
  * RAW: d' in {16, 32}; SOFTVOTE: D in {64, 128}, Lq == 1 (decode); R in {1, 2, 4, 8}.
  * workspace: SOFTVOTE keeps per-token logits and per-block softmax partials.
  */
 int butler_score(void* stream, int mode, int dtype, const void* q, const void* keys,
-                 float* scores, uint32_t* radix_hist, int B, int Hq, int Hkv, int G, int slot,
+                 float* scores, uint32_t* radix_hist, const int32_t* keep, int B, int Hq,
+                 int Hkv, int G, int slot,
                  int Lq, int L,
                  int L_cap, int dk, int q_pos0, int causal, float softmax_scale,
                  void* workspace, size_t* ws_bytes);
@@ -154,6 +158,9 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
  * count[row] = |S|.  At least one of idx, bitmask must be non-NULL.
  *
  *   scores  [B, Hkv, Lq, L]          float32 (read)
+ *   keep    [B, Hkv]                 int32, optional (NULL = none), single-row calls only:
+ *                                    rows with keep != 0 are skipped; their idx, bitmask
+ *                                    and count keep the previous selection.
  *   radix_hist [B, Hkv, Lq, 2048]    uint32, optional: the histogram butler_score built for
  *                                    exactly these scores (see butler_score); it is used
  *                                    instead of a counting pass and zero-filled again.  NULL:
@@ -168,7 +175,8 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
  * radix histogram, candidate keys, per-chunk counts and offsets (about 8 bytes per token
  * per row).
  */
-int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist, int budget_num,
+int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
+                       const int32_t* keep, int budget_num,
                        int budget_den,
                        int n_sink, int n_window, int32_t* idx, uint32_t* bitmask,
                        int32_t* count, int B, int Hkv, int Lq, int L, int cap, int q_pos0,
@@ -201,6 +209,28 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
                               const uint32_t* bitmask, float* out, int B, int Hq, int Hkv,
                               int D, int Lq, int L, int L_cap, int cap, int q_pos0,
                               float softmax_scale, void* workspace, size_t* ws_bytes);
+
+/*
+ * butler_selection_cache -- TokenSelect README, highlights, Selection Cache: consecutive
+ * similar queries share one token selection, so selection runs less often.  For every
+ * (b, KV head) of a decode step, the cosine similarity between the group's current query
+ * (its R heads' D-vectors stacked into one vector of R*D) and the reference query the
+ * cached selection was made for:
+ *   cos >= threshold  ->  keep[b, g] = 1: score and select skip the (b, g) rows and the
+ *                         previous index list / bitmask / count stand;
+ *   otherwise         ->  keep[b, g] = 0 and q_ref[b, g] = q[b, g]: the next score and
+ *                         select recompute the selection for this query.
+ * A zero vector on either side gives cos = 0.  The similarity is accumulated in float32
+ * (products of the stored values, one sum per (b, g) in lane order, then a fixed tree).
+ *
+ *   q      [B, Hq, 1, D]   dtype (read)
+ *   q_ref  [B, Hq, 1, D]   dtype (read, rows refreshed) -- caller-owned state; a first call
+ *                          with threshold > 1 (or a zero-filled q_ref) refreshes every row
+ *   keep   [B, Hkv]        int32 (written)
+ * D in {64, 128}, R = Hq / Hkv in {1, 2, 4, 8}.  No workspace.
+ */
+int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, int32_t* keep,
+                           int B, int Hq, int Hkv, int D, float threshold);
 
 #ifdef __cplusplus
 }

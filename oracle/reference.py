@@ -20,7 +20,8 @@ even, into its storage type.  Sources, cited by page title and section:
 * "TokenButler: Token Importance is Predictable" (arXiv abstract page):
   selection is per token under a fixed budget, the full KV cache is kept.
 * TokenSelect README, first highlights: per-head Q.K criticality, per-head
-  softmax, summed over heads ("soft voting").
+  softmax, summed over heads ("soft voting"); Selection Cache: consecutive
+  similar queries share one token selection.
 
 Readings where the pages are silent (each listed in the design notes):
 GQA head h belongs to KV head h // R; the raw scorer of a GQA group is the
@@ -343,6 +344,29 @@ def decode_layer_step(*, q, k_cache, v_cache, L: int, num: int, den: int,
     x = budget(L, num, den)
     sel = [[select(s[b, g], x, n_sink, n_window) for g in range(Hkv)] for b in range(B)]
     return {"scores": s, "sel": sel, "out": sparse_decode_attn(q, kc, vc, sel, scale)}
+
+
+def selection_cache(q, q_ref, Hkv: int, threshold: float):
+    """TokenSelect README, highlights, Selection Cache: consecutive similar queries share
+    one token selection.  q, q_ref: [B, Hq, D] (one decode step).  Per (b, KV head), the
+    cosine similarity of the group's R query heads stacked into one vector (float64; 0
+    when either vector is zero) with the reference the cached selection was made for.
+    Returns (keep [B, Hkv] bool: cos >= threshold, new q_ref: q where not kept, cos)."""
+    q = np.asarray(q, dtype=np.float64)
+    ref = np.asarray(q_ref, dtype=np.float64)
+    B, Hq, D = q.shape
+    R = Hq // Hkv
+    a = q.reshape(B, Hkv, R * D)
+    c = ref.reshape(B, Hkv, R * D)
+    na = np.sqrt((a * a).sum(-1))
+    nc = np.sqrt((c * c).sum(-1))
+    dot = (a * c).sum(-1)
+    den = na * nc
+    cos = np.where(den > 0, dot / np.where(den > 0, den, 1.0), 0.0)
+    keep = cos >= threshold
+    new_ref = np.where(keep[:, :, None, None], c.reshape(B, Hkv, R, D),
+                       a.reshape(B, Hkv, R, D)).reshape(B, Hq, D)
+    return keep, new_ref, cos
 
 
 def ulps_bf16(a, b) -> np.ndarray:

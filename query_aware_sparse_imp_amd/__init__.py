@@ -19,8 +19,8 @@ import torch
 __all__ = [
     "BUTLER_OK", "BUTLER_SCORE_RAW", "BUTLER_SCORE_SOFTVOTE", "ButlerError", "lib", "LIB_PATH",
     "butler_project_keys", "butler_produce_queries", "butler_score", "butler_select_topk",
-    "butler_sparse_decode_attn", "butler_status_string", "butler_abi_version",
-    "declared_symbols", "workspace_bytes",
+    "butler_sparse_decode_attn", "butler_selection_cache", "butler_status_string",
+    "butler_abi_version", "declared_symbols", "workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbutler.so")
@@ -43,9 +43,10 @@ _SIGS = {
     "butler_abi_version": ([], _i),
     "butler_project_keys": ([_vp, _i, _vp, _vp, _vp] + [_i] * 7, _i),
     "butler_produce_queries": ([_vp, _i, _vp, _vp, _vp, _vp] + [_i] * 7 + [_f, _vp, _sz], _i),
-    "butler_score": ([_vp, _i, _i, _vp, _vp, _vp, _vp] + [_i] * 11 + [_f, _vp, _sz], _i),
-    "butler_select_topk": ([_vp, _vp, _vp] + [_i] * 4 + [_vp, _vp, _vp] + [_i] * 7 + [_vp, _sz],
-                           _i),
+    "butler_score": ([_vp, _i, _i, _vp, _vp, _vp, _vp, _vp] + [_i] * 11 + [_f, _vp, _sz], _i),
+    "butler_select_topk": ([_vp, _vp, _vp, _vp] + [_i] * 4 + [_vp, _vp, _vp] + [_i] * 7 +
+                           [_vp, _sz], _i),
+    "butler_selection_cache": ([_vp, _i, _vp, _vp, _vp] + [_i] * 4 + [_f], _i),
     "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 9 + [_f, _vp, _sz], _i),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -77,6 +78,11 @@ def declared_symbols() -> list:
 def _check_hist(h: Optional[torch.Tensor], rows: tuple) -> None:
     if h is not None and (tuple(h.shape) != (*rows, 2048) or h.element_size() != 4):
         raise ValueError("radix_hist must be 32-bit [B, Hkv, Lq, 2048]")
+
+
+def _check_keep(k: Optional[torch.Tensor], shape: tuple) -> None:
+    if k is not None and (tuple(k.shape) != shape or k.dtype != torch.int32):
+        raise ValueError("keep must be int32 [B, Hkv]")
 
 
 def _check(fn: str, status: int) -> None:
@@ -176,13 +182,15 @@ def butler_produce_queries(h: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
 def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.Tensor, *,
                  Hkv: int, L: int, slot: int = 0, q_pos0: int = 0, causal: bool = False,
                  softmax_scale: float = 1.0, radix_hist: Optional[torch.Tensor] = None,
-                 stream=None) -> None:
+                 keep: Optional[torch.Tensor] = None, stream=None) -> None:
     """Importance scores [B, Hkv, Lq, L] (see butler.h).
 
     RAW: q = q_imp [B, Hq, G, Lq, d'], keys = kimp [B, Hkv, L_cap, d'].
     SOFTVOTE: q = [B, Hq, Lq, D], keys = k_cache [B, Hkv, L_cap, D].
     radix_hist: optional zero-filled int32/uint32 [B, Hkv, Lq, 2048] that collects the
     first radix digit of every score for butler_select_topk.
+    keep: optional int32 [B, Hkv] from butler_selection_cache; rows with keep != 0 are
+    skipped (single-row calls).
     """
     if mode == BUTLER_SCORE_RAW:
         B, Hq, G, Lq, dk = q.shape
@@ -195,10 +203,12 @@ def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.T
     if q.dtype != keys.dtype or scores.dtype != torch.float32:
         raise TypeError("dtype mismatch")
     _check_hist(radix_hist, (B, Hkv, Lq))
-    args = (mode, _dtype_code(q), _ptr(q), _ptr(keys), _ptr(scores), _ptr(radix_hist), B, Hq,
-            Hkv, G, slot, Lq, L, L_cap, dk, q_pos0, int(causal), softmax_scale)
+    _check_keep(keep, (B, Hkv))
+    args = (mode, _dtype_code(q), _ptr(q), _ptr(keys), _ptr(scores), _ptr(radix_hist),
+            _ptr(keep), B, Hq, Hkv, G, slot, Lq, L, L_cap, dk, q_pos0, int(causal),
+            softmax_scale)
     need = workspace_bytes(lambda ws, n: lib.butler_score(_stream(stream), *args, ws, n))
-    ws, n = _workspace("score", need, q.device, tuple(args[6:]))
+    ws, n = _workspace("score", need, q.device, tuple(args[7:]))
     _check("butler_score", lib.butler_score(_stream(stream), *args, ws, _byref(n)))
 
 
@@ -206,8 +216,9 @@ def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n
                        n_window: int, count: torch.Tensor, idx: Optional[torch.Tensor] = None,
                        bitmask: Optional[torch.Tensor] = None, *, q_pos0: int = 0,
                        causal: bool = False, radix_hist: Optional[torch.Tensor] = None,
-                       stream=None) -> None:
-    """Top-x + sink + window per row of scores [B, Hkv, Lq, L] (see butler.h)."""
+                       keep: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Top-x + sink + window per row of scores [B, Hkv, Lq, L] (see butler.h).  keep: as in
+    butler_score; kept rows leave idx, bitmask and count as they were."""
     B, Hkv, Lq, L = scores.shape
     cap = 0
     if idx is not None:
@@ -220,7 +231,9 @@ def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n
     if count.shape != (B, Hkv, Lq) or count.dtype != torch.int32:
         raise ValueError("count must be int32 [B, Hkv, Lq]")
     _check_hist(radix_hist, (B, Hkv, Lq))
-    args = (_ptr(scores), _ptr(radix_hist), budget_num, budget_den, n_sink, n_window, _ptr(idx),
+    _check_keep(keep, (B, Hkv))
+    args = (_ptr(scores), _ptr(radix_hist), _ptr(keep), budget_num, budget_den, n_sink, n_window,
+            _ptr(idx),
             _ptr(bitmask), _ptr(count), B, Hkv, Lq, L, cap, q_pos0, int(causal))
     need = workspace_bytes(lambda ws, n: lib.butler_select_topk(_stream(stream), *args, ws, n))
     ws, n = _workspace("select", need, scores.device, (budget_num, budget_den, B, Hkv, Lq, L, cap, q_pos0, int(causal)))
@@ -252,3 +265,17 @@ def butler_sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     ws, n = _workspace("attn", need, q.device, tuple(args[8:]))
     _check("butler_sparse_decode_attn",
            lib.butler_sparse_decode_attn(_stream(stream), *args, ws, _byref(n)))
+
+
+def butler_selection_cache(q: torch.Tensor, q_ref: torch.Tensor, keep: torch.Tensor, *,
+                           Hkv: int, threshold: float, stream=None) -> None:
+    """keep[b, g] = cos(q group, q_ref group) >= threshold; refreshes q_ref where not
+    (see butler.h).  q, q_ref: [B, Hq, 1, D]; keep: int32 [B, Hkv]."""
+    B, Hq, Lq, D = q.shape
+    if q_ref.shape != q.shape or Lq != 1 or keep.shape != (B, Hkv) or keep.dtype != torch.int32:
+        raise ValueError("shape mismatch")
+    if q_ref.dtype != q.dtype:
+        raise TypeError("dtype mismatch")
+    _check("butler_selection_cache", lib.butler_selection_cache(
+        _stream(stream), _dtype_code(q), _ptr(q), _ptr(q_ref), _ptr(keep), B, Hq, Hkv, D,
+        float(threshold)))

@@ -64,7 +64,7 @@ const char* butler_status_string(int status) {
   }
 }
 
-int butler_abi_version(void) { return 1; }
+int butler_abi_version(void) { return 2; }
 
 int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
                         void* kimp, int B, int Hkv, int L_cap, int D, int dprime, int pos0,
@@ -103,7 +103,8 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
 }
 
 int butler_score(void* stream, int mode, int dtype, const void* q, const void* keys,
-                 float* scores, uint32_t* radix_hist, int B, int Hq, int Hkv, int G, int slot,
+                 float* scores, uint32_t* radix_hist, const int32_t* keep, int B, int Hq,
+                 int Hkv, int G, int slot,
                  int Lq, int L,
                  int L_cap, int dk, int q_pos0, int causal, float softmax_scale,
                  void* workspace, size_t* ws_bytes) {
@@ -131,16 +132,19 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
   if (!aligned16(q) || !aligned16(keys) || !aligned16(scores)) return BUTLER_ERR_INVALID_ARG;
   if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  // the first-digit histogram is a decode-row hand-off; multi-row calls leave it untouched
+  // the first-digit histogram and the selection-cache flags are decode-row hand-offs;
+  // multi-row calls ignore them
   uint32_t* hist = (Lq > 1) ? nullptr : radix_hist;
+  const int32_t* kp = (Lq > 1) ? nullptr : keep;
   if (mode == BUTLER_SCORE_RAW)
     return finish(s, launch_score_raw(s, dtype, q, keys, scores, B, Hq, Hkv, G, slot, Lq, L,
-                                      L_cap, dk, q_pos0, causal, hist));
+                                      L_cap, dk, q_pos0, causal, hist, kp));
   return finish(s, launch_score_softvote(s, dtype, q, keys, scores, B, Hq, Hkv, L, L_cap, dk,
-                                         softmax_scale, workspace, hist));
+                                         softmax_scale, workspace, hist, kp));
 }
 
-int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist, int budget_num,
+int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
+                       const int32_t* keep, int budget_num,
                        int budget_den,
                        int n_sink, int n_window, int32_t* idx, uint32_t* bitmask,
                        int32_t* count, int B, int Hkv, int Lq, int L, int cap, int q_pos0,
@@ -167,8 +171,9 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist, 
   if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* hist = (Lq > 1) ? nullptr : radix_hist;   // see butler_score
+  const int32_t* kp = (Lq > 1) ? nullptr : keep;
   return finish(s, launch_select(s, scores, budget_num, budget_den, n_sink, n_window, idx,
-                                 bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, hist,
+                                 bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, hist, kp,
                                  workspace));
 }
 
@@ -204,6 +209,19 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
                                      D, Lq, L_cap, cap, softmax_scale, workspace));
   return finish(s, launch_attn_bitmask(s, dtype, q, k_cache, v_cache, bitmask, out, B, Hq, Hkv,
                                        D, Lq, L, L_cap, q_pos0, softmax_scale, workspace));
+}
+
+int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, int32_t* keep,
+                           int B, int Hq, int Hkv, int D, float threshold) {
+  if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
+  if (!pow2_group(Hq / Hkv) || !(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
+  if ((long long)B * Hkv > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
+  if (threshold != threshold) return BUTLER_ERR_INVALID_ARG;   // NaN
+  if (!q || !q_ref || !keep) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(q_ref) || !aligned16(keep)) return BUTLER_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(s, launch_selection_cache(s, dtype, q, q_ref, keep, B, Hq, Hkv, D, threshold));
 }
 
 }  // extern "C"

@@ -21,18 +21,20 @@ hipError_t launch_produce(hipStream_t s, const void* h, const void* w1, const vo
 // ---- scoring --------------------------------------------------------------
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
-                            int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist);
+                            int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist,
+                            const int32_t* keep);
 size_t softvote_workspace(int B, int Hq, int Hkv, int L);
 hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const void* k,
                                  float* scores, int B, int Hq, int Hkv, int L, int L_cap,
-                                 int D, float scale, void* ws, uint32_t* hist);
+                                 int D, float scale, void* ws, uint32_t* hist,
+                                 const int32_t* keep);
 
 // ---- selection ------------------------------------------------------------
 size_t select_workspace(int rows, int L, int Lq, int causal);
 hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
                          int n_window, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
-                         uint32_t* hist, void* ws);
+                         uint32_t* hist, const int32_t* keep, void* ws);
 
 // ---- attention ------------------------------------------------------------
 size_t attn_workspace(int dtype, int B, int Hq, int Hkv, int D, int Lq, int L, int cap);
@@ -44,5 +46,8 @@ hipError_t launch_attn_bitmask(hipStream_t s, int dtype, const void* q, const vo
                                const void* v, const uint32_t* bitmask, float* out, int B,
                                int Hq, int Hkv, int D, int Lq, int L, int L_cap, int q_pos0,
                                float scale, void* ws);
+
+hipError_t launch_selection_cache(hipStream_t s, int dtype, const void* q, void* q_ref,
+                                  int32_t* keep, int B, int Hq, int Hkv, int D, float threshold);
 
 }  // namespace butler

@@ -46,12 +46,13 @@ template <typename T, int DP>
 __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
     const T* __restrict__ q_imp, const T* __restrict__ kimp, float* __restrict__ scores,
     int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal,
-    int tpb, uint32_t* __restrict__ radix_hist) {
+    int tpb, uint32_t* __restrict__ radix_hist, const int32_t* __restrict__ keep) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPT = DP / EPL;           // lanes per token
   constexpr int TPI = kRawThreads / LPT;  // tokens per block-wide step
   constexpr int U = kRawUnroll;
   const int bg = blockIdx.z, i = blockIdx.y;
+  if (keep && keep[bg]) return;   // the cached selection stands (single-row calls)
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int R = Hq / Hkv;
   const int part = threadIdx.x % LPT, sub = threadIdx.x / LPT;
@@ -151,7 +152,8 @@ template <typename T, int D, int R>
 __global__ __launch_bounds__(kSvThreads) void softvote_logits_kernel(
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ logits,
     float2* __restrict__ part, int Hq, int Hkv, int L, int L_cap, float scale_log2,
-    int nblk) {
+    int nblk, const int32_t* __restrict__ keep) {
+  if (keep && keep[blockIdx.y]) return;
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPR = D / EPL;
   constexpr int TPW = 64 / LPR;
@@ -232,7 +234,9 @@ typedef __attribute__((ext_vector_type(4))) float f32x4s_t;
 template <int R>
 __global__ __launch_bounds__(kSvThreads) void softvote_logits_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, float* __restrict__ logits,
-    float2* __restrict__ part, int Hq, int Hkv, int L, int L_cap, float scale_log2, int nblk) {
+    float2* __restrict__ part, int Hq, int Hkv, int L, int L_cap, float scale_log2, int nblk,
+    const int32_t* __restrict__ keep) {
+  if (keep && keep[blockIdx.y]) return;
   constexpr int D = 128;
   const int bg = blockIdx.y, blk = blockIdx.x;
   const int b = bg / Hkv, g = bg - b * Hkv;
@@ -306,8 +310,10 @@ __global__ __launch_bounds__(kSvThreads) void softvote_logits_mfma_kernel(
 template <int R>
 __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
     const float* __restrict__ logits, const float2* __restrict__ part,
-    float* __restrict__ scores, int L, int nblk, uint32_t* __restrict__ radix_hist) {
+    float* __restrict__ scores, int L, int nblk, uint32_t* __restrict__ radix_hist,
+    const int32_t* __restrict__ keep) {
   const int bg = blockIdx.y, blk = blockIdx.x;
+  if (keep && keep[bg]) return;
   __shared__ float Ms[R], Ls[R];
   __shared__ uint32_t hist[2048];
   if (radix_hist)
@@ -495,7 +501,7 @@ hipError_t rows_t(hipStream_t s, const void* q_imp, const void* kimp, float* sco
 template <typename T, int DP>
 hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scores, int B,
                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
-                 int causal, uint32_t* hist) {
+                 int causal, uint32_t* hist, const int32_t* keep) {
   constexpr int LPT = DP / Vec16<T>::N;
   // a tile is what one block-wide step covers (kRawUnroll loads per thread); a workgroup
   // loops over enough tiles that a row has at most kRawRowWg workgroups -- this bounds the
@@ -507,13 +513,14 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
   dim3 grid((L + tpb - 1) / tpb, Lq, B * Hkv);
   hipLaunchKernelGGL((score_raw_kernel<T, DP>), grid, dim3(kRawThreads), 0, s, (const T*)q_imp,
                      (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal,
-                     tpb, hist);
+                     tpb, hist, keep);
   return hipGetLastError();
 }
 
 template <typename T, int D, int R>
 hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int B, int Hq,
-                int Hkv, int L, int L_cap, float scale, void* ws, uint32_t* hist) {
+                int Hkv, int L, int L_cap, float scale, void* ws, uint32_t* hist,
+                const int32_t* keep) {
   const int nblk = (L + kSvTokensPerBlock - 1) / kSvTokensPerBlock;
   float* logits = (float*)ws;
   float2* part = (float2*)(logits + (size_t)B * Hkv * R * L);
@@ -522,14 +529,14 @@ hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int 
   if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
     hipLaunchKernelGGL((softvote_logits_mfma_kernel<R>), grid, dim3(kSvThreads), 0, s,
                        (const bf16_t*)q, (const bf16_t*)k, logits, part, Hq, Hkv, L, L_cap,
-                       scale_log2, nblk);
+                       scale_log2, nblk, keep);
   } else {
     hipLaunchKernelGGL((softvote_logits_kernel<T, D, R>), grid, dim3(kSvThreads), 0, s,
                        (const T*)q, (const T*)k, logits, part, Hq, Hkv, L, L_cap, scale_log2,
-                       nblk);
+                       nblk, keep);
   }
   hipLaunchKernelGGL((softvote_combine_kernel<R>), grid, dim3(kSvThreads), 0, s, logits, part,
-                     scores, L, nblk, hist);
+                     scores, L, nblk, hist, keep);
   return hipGetLastError();
 }
 
@@ -539,18 +546,19 @@ bool R_ok(int Hq, int Hkv) { return Hq % Hkv == 0 && Hq / Hkv <= 8; }
 
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
-                            int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist) {
+                            int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist,
+                            const int32_t* keep) {
   if (dtype == 1 && Lq > 1 && R_ok(Hq, Hkv)) {
     // several query rows: the matrix-core kernel (it builds no first-digit histogram)
     if (dp == 32) return rows_t<32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
     if (dp == 16) return rows_t<16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
   }
   if (dtype == 1) {
-    if (dp == 32) return raw_t<bf16_t, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);
-    if (dp == 16) return raw_t<bf16_t, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);
+    if (dp == 32) return raw_t<bf16_t, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
+    if (dp == 16) return raw_t<bf16_t, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
   } else {
-    if (dp == 32) return raw_t<float, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);
-    if (dp == 16) return raw_t<float, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist);
+    if (dp == 32) return raw_t<float, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
+    if (dp == 16) return raw_t<float, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
   }
   return hipErrorInvalidValue;
 }
@@ -563,10 +571,11 @@ size_t softvote_workspace(int B, int Hq, int Hkv, int L) {
 
 hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const void* k,
                                  float* scores, int B, int Hq, int Hkv, int L, int L_cap,
-                                 int D, float scale, void* ws, uint32_t* hist) {
+                                 int D, float scale, void* ws, uint32_t* hist,
+                                 const int32_t* keep) {
   const int R = Hq / Hkv;
 #define BUTLER_SV(T, DD, RR)                                                       \
-  if (D == DD && R == RR) return sv_t<T, DD, RR>(s, q, k, scores, B, Hq, Hkv, L, L_cap, scale, ws, hist);
+  if (D == DD && R == RR) return sv_t<T, DD, RR>(s, q, k, scores, B, Hq, Hkv, L, L_cap, scale, ws, hist, keep);
   if (dtype == 1) {
     BUTLER_SV(bf16_t, 128, 1) BUTLER_SV(bf16_t, 128, 2) BUTLER_SV(bf16_t, 128, 4) BUTLER_SV(bf16_t, 128, 8)
     BUTLER_SV(bf16_t, 64, 1) BUTLER_SV(bf16_t, 64, 2) BUTLER_SV(bf16_t, 64, 4) BUTLER_SV(bf16_t, 64, 8)

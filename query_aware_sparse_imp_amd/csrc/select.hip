@@ -130,10 +130,12 @@ template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void select_row_kernel(
     const float* __restrict__ scores, int num, int den, int n_sink, int n_window,
     int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask, int32_t* __restrict__ count,
-    int Lq, int L, int cap, int q_pos0, int causal, uint32_t* __restrict__ ghist) {
+    int Lq, int L, int cap, int q_pos0, int causal, uint32_t* __restrict__ ghist,
+    const int32_t* __restrict__ keep) {
   constexpr int NW = NT / 64;
   constexpr int MAXW = NT * KPT / 64;
   const long long row = blockIdx.x;
+  if (keep && keep[row]) return;   // single-row calls: the cached selection stands
   const int i = (int)(row % Lq);
   const int L_r = causal ? min(q_pos0 + i + 1, L) : L;
   int k;
@@ -359,8 +361,10 @@ __device__ __forceinline__ int load_keys(const float* s, int t0, int L, uint32_t
 template <int KPT>
 __global__ __launch_bounds__(kMbThreads) void mb_hist1_kernel(const float* __restrict__ scores,
                                                               int num, int den, int L, int rows,
-                                                              uint32_t* __restrict__ ghist) {
+                                                              uint32_t* __restrict__ ghist,
+                                                              const int32_t* __restrict__ keep) {
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
+  if (keep && keep[row]) return;
   int k;
   if (row_mode(L, num, den, k) != kModeNormal) return;
   __shared__ uint32_t h[2048];
@@ -576,8 +580,10 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
                                                              int num, int den, int n_sink,
                                                              int n_window, int L, int rows,
                                                              const uint32_t* __restrict__ ghist,
-                                                             MbWs w) {
+                                                             MbWs w,
+                                                             const int32_t* __restrict__ keep) {
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
+  if (keep && keep[row]) return;
   const int nchunk = gridDim.x / rows;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int k;
@@ -676,10 +682,12 @@ template <int KPT>
 __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
     const float* __restrict__ scores, int num, int den, int n_sink, int n_window, int L,
     int rows, int cap, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask,
-    int32_t* __restrict__ count, uint32_t* __restrict__ ghist, MbWs w) {
+    int32_t* __restrict__ count, uint32_t* __restrict__ ghist, MbWs w,
+    const int32_t* __restrict__ keep) {
   constexpr int NWD = kMbWaves * KPT;   // 64-token words per chunk
   static_assert(NWD <= 128, "two words per lane in the prefix scan");
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
+  if (keep && keep[row]) return;   // the cached selection stands
   const int nchunk = gridDim.x / rows;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int k;
@@ -844,7 +852,7 @@ size_t select_workspace(int rows, int L, int Lq, int causal) {
 hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
                          int n_window, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
-                         uint32_t* hist, void* ws) {
+                         uint32_t* hist, const int32_t* keep, void* ws) {
   const long long rows = (long long)B * Hkv * Lq;
   if (use_chunked(Lq, L, causal)) {
     const MbWs w = carve(ws, rows, L);
@@ -855,11 +863,11 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
       constexpr int KPT = decltype(kpt_c)::value;
       if (!hist)
         hipLaunchKernelGGL(mb_hist1_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
-                           L, (int)rows, gh);
+                           L, (int)rows, gh, keep);
       hipLaunchKernelGGL(mb_cand_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
-                         n_sink, n_window, L, (int)rows, (const uint32_t*)gh, w);
+                         n_sink, n_window, L, (int)rows, (const uint32_t*)gh, w, keep);
       hipLaunchKernelGGL(mb_finish_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
-                         n_sink, n_window, L, (int)rows, cap, idx, bitmask, count, gh, w);
+                         n_sink, n_window, L, (int)rows, cap, idx, bitmask, count, gh, w, keep);
     };
     switch (kpt_for(L)) {
       case 8: run(std::integral_constant<int, 8>()); break;
@@ -872,7 +880,7 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
 #define BUTLER_SR(NT, KPT)                                                                 \
   hipLaunchKernelGGL((select_row_kernel<NT, KPT>), dim3((unsigned)rows), dim3(NT), 0, s,   \
                      scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,   \
-                     q_pos0, causal, hist)
+                     q_pos0, causal, hist, keep)
   if (L <= 1024) BUTLER_SR(64, 16);
   else if (L <= 2048) BUTLER_SR(128, 16);
   else if (L <= 4096) BUTLER_SR(256, 16);

@@ -20,7 +20,8 @@ MIS = 0x10004           # misaligned
 def test_every_declared_symbol_is_exported():
     names = qa.declared_symbols()
     assert {"butler_project_keys", "butler_produce_queries", "butler_score",
-            "butler_select_topk", "butler_sparse_decode_attn"} <= set(names)
+            "butler_select_topk", "butler_sparse_decode_attn",
+            "butler_selection_cache"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", qa.LIB_PATH], capture_output=True,
@@ -30,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert qa.butler_abi_version() == 1
+    assert qa.butler_abi_version() == 2
     assert qa.butler_status_string(0) == "BUTLER_OK"
     assert qa.butler_status_string(-3) == "BUTLER_ERR_WORKSPACE"
     assert qa.butler_status_string(123) == "BUTLER_ERR_UNKNOWN"
@@ -49,8 +50,8 @@ def test_project_keys_validation():
 
 def _score(mode=0, dtype=1, q=FAKE, keys=FAKE, scores=FAKE, B=1, Hq=32, Hkv=8, G=1, slot=0,
            Lq=1, Lk=1000, L_cap=1000, dk=32, q_pos0=0, causal=0, scale=0.1, ws=None, n=None):
-    return L.butler_score(None, mode, dtype, q, keys, scores, None, B, Hq, Hkv, G, slot, Lq, Lk,
-                          L_cap, dk, q_pos0, causal, scale, ws, n)
+    return L.butler_score(None, mode, dtype, q, keys, scores, None, None, B, Hq, Hkv, G, slot,
+                          Lq, Lk, L_cap, dk, q_pos0, causal, scale, ws, n)
 
 
 def test_score_validation_and_workspace_query():
@@ -72,13 +73,13 @@ def test_score_validation_and_workspace_query():
 def test_select_validation():
     f = L.butler_select_topk
     # cap smaller than min(L, x + sink + window)
-    assert f(None, FAKE, None, 1, 2, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 567, 0, 0, None,
+    assert f(None, FAKE, None, None, 1, 2, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 567, 0, 0, None,
              None) == INV
-    assert f(None, FAKE, None, 1, 0, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
+    assert f(None, FAKE, None, None, 1, 0, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
              None) == INV                                                  # den = 0
-    assert f(None, FAKE, None, 1, 2, -1, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
+    assert f(None, FAKE, None, None, 1, 2, -1, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
              None) == INV                                                  # negative sink
-    assert f(None, FAKE, None, 1, 2, 4, 64, None, None, FAKE, 1, 8, 1, 1000, 0, 0, 0, None,
+    assert f(None, FAKE, None, None, 1, 2, 4, 64, None, None, FAKE, 1, 8, 1, 1000, 0, 0, 0, None,
              None) == INV                                                  # no output
 
 
@@ -87,8 +88,9 @@ def test_attention_validation_and_workspace_query():
     n = ctypes.c_size_t(0)
     assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 128, 1, 32768, 32768,
              16452, 0, 0.088, None, ctypes.byref(n)) == OK
-    nsplit = (16452 + 255) // 256
-    assert n.value >= 8 * nsplit * 4 * 130 * 4
+    # one (max, sum, acc[D]) partial per (row, split, head): a whole number of splits >= 1
+    per_split = 8 * 4 * (128 + 4) * 4
+    assert n.value >= per_split and n.value % per_split == 0
     assert f(None, 1, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, 32, 8, 128, 1, 32768, 32768,
              16452, 0, 0.088, None, None) == INV                            # idx without count
     assert f(None, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1, 32, 8, 128, 4, 20000, 20000,
@@ -109,3 +111,14 @@ def test_produce_validation_and_workspace_query():
              ctypes.byref(n)) == UNS                                        # fp32 producer
     assert f(None, 1, FAKE, FAKE, FAKE, FAKE, 1, 1, 4000, 1024, 32, 4, 32, 1e-5, None,
              ctypes.byref(n)) == UNS                                        # E % 64
+
+
+def test_selection_cache_validation():
+    f = L.butler_selection_cache
+    assert f(None, 1, None, FAKE, FAKE, 16, 32, 8, 128, 0.98) == INV         # null q
+    assert f(None, 1, FAKE, FAKE, MIS, 16, 32, 8, 128, 0.98) == INV          # misaligned keep
+    assert f(None, 1, FAKE, FAKE, FAKE, 16, 30, 8, 128, 0.98) == INV         # Hq % Hkv
+    assert f(None, 1, FAKE, FAKE, FAKE, 16, 32, 8, 96, 0.98) == UNS          # D
+    assert f(None, 5, FAKE, FAKE, FAKE, 16, 32, 8, 128, 0.98) == UNS         # dtype
+    assert f(None, 1, FAKE, FAKE, FAKE, 16, 32, 8, 128, float("nan")) == INV  # threshold
+

@@ -1,0 +1,91 @@
+"""GPU parity of the selection cache (TokenSelect README, highlights, Selection Cache).
+
+Soft-voting batched decode (B=2, 32/8 heads, D=128, 30% + 4 + 64) over the first steps
+of the query walk, at a short row (per-row selection) and a long one (chunked
+selection).  Every step: butler_selection_cache decides per (b, KV head) whether the
+cached selection stands, then score and select skip the kept rows and attention runs
+over the current index lists.  Gates:
+  flags     equal to the oracle's float64 decision, except where the oracle's cosine lies
+            within 1e-5 of the threshold (the device sums in float32);
+  reference q_ref rows refreshed exactly where the flag is 0, bit-exact copies;
+  kept rows index lists, counts and scores identical to the previous step's;
+  selection bit-exact on the GPU's scores for every row (kept rows: the stored ones);
+  attention max-abs 2e-2 over the current index lists.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from parity import check_attend, check_select_exact, np64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("L", [3001, 9001])
+def test_selection_cache_softvote_walk(L):
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[3].replace(B=2, L=L)
+    threshold, steps = 0.9975, 6
+    print(f"[cache] B={w.B} L={L} threshold={threshold} steps={steps}", flush=True)
+    cache = synthetic.softvote_cache(w)
+    qs = synthetic.softvote_queries(w, steps)
+    dev = "cuda"
+    k, v = cache["k_cache"].to(dev), cache["v_cache"].to(dev)
+    q_ref = torch.zeros_like(qs[0], device=dev)
+    keep = torch.zeros(w.B, w.Hkv, dtype=torch.int32, device=dev)
+    cap = w.cap(L)
+    scores = torch.zeros(w.B, w.Hkv, 1, L, dtype=torch.float32, device=dev)
+    hist = torch.zeros(w.B, w.Hkv, 1, 2048, dtype=torch.int32, device=dev)
+    idx = torch.zeros(w.B, w.Hkv, 1, cap, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(w.B, w.Hkv, 1, dtype=torch.int32, device=dev)
+    out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=dev)
+    ref_np = np.zeros((w.B, w.Hq, w.D))
+    prev = None
+    kept_total = 0
+    for s in range(steps):
+        q = qs[s].to(dev)
+        qa.butler_selection_cache(q, q_ref, keep, Hkv=w.Hkv, threshold=threshold)
+        qa.butler_score(qa.BUTLER_SCORE_SOFTVOTE, q, k, scores, Hkv=w.Hkv, L=L,
+                        softmax_scale=w.scale, radix_hist=hist, keep=keep)
+        qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink, w.n_window, cnt,
+                              idx=idx, radix_hist=hist, keep=keep)
+        qa.butler_sparse_decode_attn(q, k, v, out, L=L, idx=idx, count=cnt,
+                                     softmax_scale=w.scale)
+        torch.cuda.synchronize()
+        qn = np64(qs[s])[:, :, 0]
+        okeep, _, cos = oracle.selection_cache(qn, ref_np, w.Hkv, threshold)
+        gkeep = keep.cpu().numpy().astype(bool)
+        band = np.abs(cos - threshold) <= 1e-5
+        assert ((gkeep == okeep) | band).all(), (s, cos[gkeep != okeep])
+        # the reference follows the device's decision
+        ref_np = np.where(gkeep.repeat(w.R, axis=1)[:, :, None], ref_np, qn)
+        assert np.array_equal(np64(q_ref)[:, :, 0], ref_np), s
+        assert int(hist.abs().sum()) == 0
+        cur = {"idx": idx.clone(), "cnt": cnt.clone(), "scores": scores.clone()}
+        if prev is not None:
+            for b in range(w.B):
+                for g in range(w.Hkv):
+                    if gkeep[b, g]:
+                        assert torch.equal(cur["cnt"][b, g], prev["cnt"][b, g])
+                        assert torch.equal(cur["idx"][b, g], prev["idx"][b, g])
+                        assert torch.equal(cur["scores"][b, g], prev["scores"][b, g])
+        else:
+            assert not gkeep.any()          # a zero reference refreshes every row
+        kept_total += int(gkeep.sum())
+        check_select_exact(idx, cnt, np64(scores), w.budget_num, w.budget_den, w.n_sink,
+                           w.n_window)
+        ic, cc = idx.cpu().numpy(), cnt.cpu().numpy()
+        check_attend(out, qs[s], cache["k_cache"], cache["v_cache"],
+                     lambda b, g, i: ic[b, g, i, :cc[b, g, i]], w.scale, w.dtype)
+        print(f"  step {s}: kept {int(gkeep.sum())} of {gkeep.size}, "
+              f"cos in [{cos.min():.5f}, {cos.max():.5f}]", flush=True)
+        prev = cur
+    assert 0 < kept_total < steps * w.B * w.Hkv

@@ -477,3 +477,39 @@ def test_mutations_are_caught(monkeypatch):
     _pins_fail(monkeypatch, "producer_of", lambda layer, G: G * ((layer - 1) // G) if layer else 0,
                test_slot_map_golden)
     monkeypatch.setattr(ref, "producer_of", good_prod)
+
+
+def test_selection_cache_pins():
+    """Selection cache: exact cosines of hand-built vectors, the stacking of the group's
+    heads into one vector, the zero-vector rule, scale invariance and the reference
+    refresh.  (3,4).(4,3) / 25 = 24/25 exactly; a per-head mean of cosines would give a
+    different value for heads of unequal norm, and that reading fails here."""
+    # B=1, Hkv=1, R=2, D=2: heads h0, h1
+    q = np.array([[[3.0, 4.0], [0.0, 0.0]]])
+    ref = np.array([[[4.0, 3.0], [0.0, 0.0]]])
+    keep, new_ref, cos = oracle.selection_cache(q, ref, 1, 0.96)
+    assert cos[0, 0] == 24.0 / 25.0 and keep[0, 0] and np.array_equal(new_ref, ref)
+    keep, new_ref, _ = oracle.selection_cache(q, ref, 1, 0.97)
+    assert not keep[0, 0] and np.array_equal(new_ref, q)           # refreshed with q
+    # stacking: heads (1,0),(0,10) vs (1,0),(10,0): stacked cos = 1/101, not mean(1, 0)
+    q2 = np.array([[[1.0, 0.0], [0.0, 10.0]]])
+    r2 = np.array([[[1.0, 0.0], [10.0, 0.0]]])
+    _, _, c2 = oracle.selection_cache(q2, r2, 1, 0.5)
+    assert abs(c2[0, 0] - 1.0 / 101.0) < 1e-15
+    # zero vector: cos 0, always refreshed at a positive threshold
+    z = np.zeros((1, 2, 2))
+    keep, new_ref, cz = oracle.selection_cache(q, z, 1, 0.0001)
+    assert cz[0, 0] == 0.0 and not keep[0, 0] and np.array_equal(new_ref, q)
+    # scale invariance, opposite vectors, two KV heads handled independently
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((2, 4, 8))
+    b = rng.standard_normal((2, 4, 8))
+    _, _, c_ab = oracle.selection_cache(a, b, 2, 0.0)
+    _, _, c_sc = oracle.selection_cache(3.0 * a, 0.5 * b, 2, 0.0)
+    assert np.allclose(c_ab, c_sc, rtol=0, atol=1e-15)
+    _, _, c_neg = oracle.selection_cache(a, -a, 2, 0.0)
+    assert np.allclose(c_neg, -1.0, atol=1e-15)
+    want = np.array([[np.dot(a[bb, 2 * g:2 * g + 2].ravel(), b[bb, 2 * g:2 * g + 2].ravel()) /
+                      (np.linalg.norm(a[bb, 2 * g:2 * g + 2]) * np.linalg.norm(b[bb, 2 * g:2 * g + 2]))
+                      for g in range(2)] for bb in range(2)])
+    assert np.allclose(c_ab, want, rtol=0, atol=1e-15)
