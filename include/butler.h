@@ -92,7 +92,7 @@ int butler_project_keys(void* stream, int dtype, const void* k_cache, const void
  *   w1     [E, F]             bf16
  *   w2     [F, Hq*G*d']       bf16
  *   q_imp  [B, Hq, G, Lq, d'] bf16 (written)
- * dtype must be BUTLER_BF16.  E, F multiples of 64; Hq*G*d' a multiple of 64.
+ * dtype must be BUTLER_BF16.  E, F multiples of 64, E <= 8192; Hq*G*d' a multiple of 64.
  * workspace: normalised rows and hidden activations, split-K partial sums.
  */
 int butler_produce_queries(void* stream, int dtype, const void* h, const void* w1,

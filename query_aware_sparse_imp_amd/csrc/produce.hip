@@ -24,24 +24,56 @@ constexpr int kLnThreads = 256;
 constexpr int kTM = 32, kTN = 64, kTK = 32;
 constexpr int kGemmThreads = 256;
 
+// One row per workgroup: the row is held in VGPRs (16-byte pieces, all requested before
+// the first reduction), mean and variance from block sums, then the bf16 x_hat.
 __global__ __launch_bounds__(kLnThreads) void ln_rows_kernel(const bf16_t* __restrict__ h,
                                                              bf16_t* __restrict__ xhat, int E,
                                                              float eps) {
+  constexpr int kPieces = 4;   // rows up to 256 * 8 * 4 = 8192 elements
   const long long row = blockIdx.x;
   const bf16_t* hr = h + row * E;
   __shared__ float tmp[kLnThreads / 64];
+  float hv[kPieces][8];
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u) {
+    const int e0 = (threadIdx.x + kLnThreads * u) * 8;
+    if (e0 < E) {
+      Vec16<bf16_t>::load(hr + e0, hv[u]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[u][e] = 0.f;
+    }
+  }
   float s = 0.f;
-  for (int j = threadIdx.x; j < E; j += kLnThreads) s += bf2f(hr[j]);
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += hv[u][e];
   const float mean = block_sum_f<kLnThreads>(s, tmp) / (float)E;
   float v = 0.f;
-  for (int j = threadIdx.x; j < E; j += kLnThreads) {
-    const float d = bf2f(hr[j]) - mean;
-    v = fmaf(d, d, v);
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u) {
+    if ((threadIdx.x + kLnThreads * u) * 8 >= E) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = hv[u][e] - mean;
+      v = fmaf(d, d, v);
+    }
   }
   const float var = block_sum_f<kLnThreads>(v, tmp) / (float)E;
   const float rstd = 1.0f / sqrtf(var + eps);
-  for (int j = threadIdx.x; j < E; j += kLnThreads)
-    xhat[row * E + j] = f2bf((bf2f(hr[j]) - mean) * rstd);
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u) {
+    const int e0 = (threadIdx.x + kLnThreads * u) * 8;
+    if (e0 >= E) continue;
+    uint4 o;
+    uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ow[e] = (uint32_t)f2bf((hv[u][2 * e] - mean) * rstd) |
+              ((uint32_t)f2bf((hv[u][2 * e + 1] - mean) * rstd) << 16);
+    *reinterpret_cast<uint4*>(xhat + row * E + e0) = o;
+  }
 }
 
 // Output placement of GEMM results.
