@@ -2,22 +2,22 @@
 // the full KV cache is kept, each step attends to the selected subset).
 //
 // Decode (index lists) -- split-K flash decoding.  The selected list of one (b, KV head,
-// query row) is cut into splits; a split is a 512-thread workgroup that takes 256 list
-// positions per round.  The split's indices are staged once in LDS; each wave owns 32
-// positions and D/8 lanes cover one key row (16 bytes each), so every lane issues the
-// loads of 8 rows' K and V slices back to back before any arithmetic -- 32 KiB of
-// gathers in flight per wave, straight into VGPRs.  All R query heads of the GQA group
-// use the same gathered rows.  Logits (DPP row reductions), the base-2 online softmax and
-// P.V run in float32.  A wave's lane groups merge by shuffles, the waves through LDS, and
-// each split writes (max, sum, acc[D]) per head.  A second kernel merges the splits of
-// every (row, head, 32-wide slice of D) in split order: its 256 threads load all the
-// partials of the slice at once (8 split groups x 32 columns), so the merge costs one
-// memory round trip.  (Workgroups do not hand work to each other inside a kernel: the
+// query row) is cut into splits sized so the grid is about what stays resident.  bf16 at
+// D = 128 runs on the matrix cores (attn_mfma_kernel, described with it below); the
+// other shapes take the VALU kernel: a 512-thread workgroup takes 256 list positions per
+// round, each wave owns 32 and D/8 lanes cover one key row, every lane issuing the loads
+// of 8 rows' K and V slices before any arithmetic.  All R query heads of the GQA group
+// use the same gathered rows; the base-2 online softmax and P.V run in float32.  Each
+// split writes (max, sum, acc[D]) per head, and a second kernel merges the splits of
+// every (row, head, 32-wide slice of D) in split order with all of its loads in one
+// round trip.  (Workgroups do not hand work to each other inside a kernel: the
 // device-wide release that would need writes back the XCD's L2.)
 //
-// Prefill (bitmask rows) -- one workgroup per query row walks the row's bitmask 2048
-// tokens at a time, compacts the set bits into an LDS index list and runs the same wave
-// routine over it.
+// Prefill (bitmask rows) -- bf16, D = 128, R = 4: the matrix-core kernel
+// attn_prefill_mfma_kernel (32 query rows per workgroup, one wave per head, dense causal
+// tiles masked by the rows' bitmask words; described with it below).  Other shapes: one
+// workgroup per query row compacts the set bits of its bitmask into an LDS index list and
+// runs the VALU wave routine over it.
 #include <type_traits>
 
 #include "common.h"

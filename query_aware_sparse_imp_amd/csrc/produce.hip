@@ -7,7 +7,8 @@
 //
 // Two GEMM kernels.  Blocks of rows (prefill: M = B*Lq >= 64) run on the matrix cores:
 // a 128 x 128 tile per workgroup, 64 x 64 per wave as 2 x 2 v_mfma_f32_32x32x16_bf16
-// tiles, K staged through LDS 32 at a time and double-buffered.  The MFMA wants eight
+// tiles, K staged through LDS 32 at a time, double-buffered, with a ring of four
+// register stages so three K tiles are in flight from memory.  The MFMA wants eight
 // consecutive K values per lane for both operands; the activations are K-contiguous, the
 // weights [K, N] are N-contiguous, so the weight tile is transposed on its way into LDS:
 // two K rows are packed into one 32-bit word per column.  A few rows (decode: one

@@ -1,23 +1,28 @@
 // Importance scores of every cached token.
 //
 // RAW (TokenButler model card, Method): score(t) = (sum of the group's Q_imp) . K_imp[t].
-//   The K_imp stream is read with 16-byte loads, DP/8 lanes per token (4 lanes at
-//   d' = 32, so one wave instruction covers 16 consecutive 64-byte rows = 1 KiB);
-//   products and sums run in float64, where every partial sum of bf16 products is
-//   exact, and the result is rounded once to float32 -- the score is the exactly
-//   rounded dot product whatever the reduction order.
+//   Decode rows: the K_imp stream is read with 16-byte loads, DP/8 lanes per token (4 at
+//   d' = 32, so one wave instruction covers 16 consecutive 64-byte rows), two batches of
+//   8 rows in flight per thread; products and sums run in float64, where every partial
+//   sum of bf16 products is exact, and the result is rounded once to float32 -- the
+//   score is the exactly rounded dot product whatever the reduction order.  Multi-row
+//   calls (prefill chunks): the same exact contraction on the matrix cores in float64
+//   (score_rows_mfma_kernel, described with it below).
 //
-// Both scorers can also add each score's first radix digit (the top 11 bits of the
+// Single-row calls can also add each score's first radix digit (the top 11 bits of the
 // order-preserving key that the selection uses) into a per-row global histogram, counted
 // in LDS per workgroup and flushed with atomics, so the selection that follows starts from
-// it instead of reading every score once more.
+// it instead of reading every score once more.  With selection-cache flags, the rows of a
+// kept (b, KV head) are skipped.
 //
 // SOFTVOTE (TokenSelect README, highlights): per-head logits z_h(t) = scale * q_h . k_t,
 //   a softmax over t for every head, summed over the heads of the GQA group.
-//   Pass 1 streams the keys once (D/8 lanes per 256-byte key row), writes the
-//   base-2 logits of the R heads and a per-block (max, sum of exp2) pair per head.
-//   Pass 2 merges the block pairs in block order (every block computes the same
-//   merge) and turns the stored logits into the summed probabilities.
+//   Pass 1 streams the keys once (bf16, D = 128: matrix cores, 16 key rows x the group's
+//   heads per MFMA; otherwise D/8 lanes per key row), writes the base-2 logits of the R
+//   heads and a per-block (max, sum of exp2) pair per head.  Pass 2 merges the block
+//   pairs (every block computes the same deterministic merge) and turns the stored
+//   logits into the summed probabilities.
+
 #include <type_traits>
 
 #include "common.h"

@@ -28,11 +28,15 @@
 //      and emits its bitmask words and indices through 64-token ballot words; the chunk-0
 //      workgroup writes the row count and clears the histogram.
 //
-// Other rows (short decode rows, every causal prefill row): one workgroup per row holds
-//   the row's keys in VGPRs (up to 64 per thread, strided so that a wave's ballot covers
-//   64 consecutive tokens), builds the digit histograms in LDS (the first from the
-//   scorer's histogram when given), and emits through 64-token ballot words with two
-//   block-wide scans over the words (tie ranks, then output positions).
+// Other rows (short decode rows, every causal prefill row): one workgroup per row, 64 to
+//   1024 threads sized to the row, holds the row's keys in VGPRs (16 to 64 per thread,
+//   strided so that a wave's ballot covers 64 consecutive tokens), builds the digit
+//   histograms in LDS (the first from the scorer's histogram when given), and emits
+//   through 64-token ballot words with two block-wide scans over the words (tie ranks,
+//   then output positions).
+//
+// Single-row calls with selection-cache flags skip the rows of kept (b, KV heads) in
+// every kernel, so their outputs and the workspace state stay as they were.
 #include "common.h"
 #include "kernels.h"
 
