@@ -14,7 +14,7 @@
 // device-wide release that would need writes back the XCD's L2.)
 //
 // Prefill (bitmask rows) -- bf16, D = 128, R = 4: the matrix-core kernel
-// attn_prefill_mfma_kernel (32 query rows per workgroup, one wave per head, dense causal
+// attn_prefill_mfma_kernel (64 query rows per workgroup, a wave per head and 32 rows, dense causal
 // tiles masked by the rows' bitmask words; described with it below).  Other shapes: one
 // workgroup per query row compacts the set bits of its bitmask into an LDS index list and
 // runs the VALU wave routine over it.
@@ -715,8 +715,8 @@ hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
 
 
 // ---------------------------------------------------------------------------
-// Prefill on the matrix cores (bf16, D = 128, R = 4): one workgroup per (b, KV head, 32
-// query rows), one wave per query head of the group.  Key tiles of 32 tokens run from 0
+// Prefill on the matrix cores (bf16, D = 128, R = 4): one workgroup per (b, KV head, 64
+// query rows), one wave per query head of the group and 32-row group.  Key tiles of 32 tokens run from 0
 // to the block's causal end; each tile is staged in LDS once for the four heads -- K as
 // [token][d], V transposed to [d][token] (two tokens packed per 32-bit word).
 //   S^T = K . Q^T        A = K rows (tokens), B = the wave's 32 queries (kept in VGPRs)
@@ -736,17 +736,18 @@ constexpr int kPfThreads = 256;
 constexpr int kPfKS = 128 + 8;   // LDS row stride (bf16) of the K tile
 constexpr int kPfVS = 32 + 4;    // LDS row stride (bf16) of the transposed V tile
 
-__global__ __launch_bounds__(kPfThreads) void attn_prefill_mfma_kernel(
+template <int RG>   // row groups of 32 queries per workgroup (one wave per head and group)
+__global__ __launch_bounds__(kPfThreads * RG) void attn_prefill_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const uint32_t* __restrict__ bitmask, float* __restrict__ out, int Hq, int Hkv, int Lq,
     int L, int L_cap, int q_pos0, float scale_log2) {
   constexpr int D = 128, R = 4;
-  const int nrb = (Lq + 31) / 32;
+  const int nrb = (Lq + 32 * RG - 1) / (32 * RG);
   const int rb = blockIdx.x % nrb, bg = blockIdx.x / nrb;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int h = g * R + wid;
-  const int i0 = rb * 32;
+  const int h = g * R + (wid & 3);
+  const int i0 = rb * 32 * RG + 32 * (wid >> 2);
   const int ql = lane & 31, hi = lane >> 5;
   const int qi = min(i0 + ql, Lq - 1);
   const bool qvalid = i0 + ql < Lq;
@@ -762,22 +763,30 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_mfma_kernel(
   const bf16_t* kb = k + (long long)bg * L_cap * D;
   const bf16_t* vb = v + (long long)bg * L_cap * D;
   // causal end of the block: its last row sees tokens < q_pos0 + last + 1
-  const int t_end = min(L, q_pos0 + min(i0 + 32, Lq));
+  const int t_end = min(L, q_pos0 + min(rb * 32 * RG + 32 * RG, Lq));
   __shared__ __align__(16) bf16_t Ks[32 * kPfKS];
   __shared__ __align__(16) bf16_t Vt[D * kPfVS];
-  // staging roles: K chunks c = tid, tid + 256 (token c/16, d 8*(c%16)); V token pair
-  // tp = tid/16 (tokens 2tp, 2tp+1), d group dg = tid%16 (d 8dg .. 8dg+7)
-  const int kc0 = tid, kc1 = tid + kPfThreads;
-  const int tp = tid >> 4, dg = tid & 15;
+  // staging roles.  One row group: every thread stages K chunks c = tid, tid + 256 (token
+  // c/16, d 8*(c%16)) and a V token pair tp = tid/16 (tokens 2tp, 2tp+1) at d group
+  // dg = tid%16.  Two row groups: the first 256 threads stage V, the others K.
+  const int kt = (RG == 2) ? tid - kPfThreads : tid;
+  const bool do_k = (RG == 1) || tid >= kPfThreads;
+  const bool do_v = (RG == 1) || tid < kPfThreads;
+  const int kc0 = max(kt, 0), kc1 = max(kt, 0) + kPfThreads;
+  const int tp = (tid & (kPfThreads - 1)) >> 4, dg = tid & 15;
   uint4 rk0, rk1, rv0, rv1;
   uint32_t wd_next;
   auto gload = [&](int t0) {
-    const int a0 = min(t0 + (kc0 >> 4), L - 1), a1 = min(t0 + (kc1 >> 4), L - 1);
-    rk0 = *reinterpret_cast<const uint4*>(kb + (long long)a0 * D + (kc0 & 15) * 8);
-    rk1 = *reinterpret_cast<const uint4*>(kb + (long long)a1 * D + (kc1 & 15) * 8);
-    const int v0 = min(t0 + 2 * tp, L - 1), v1 = min(t0 + 2 * tp + 1, L - 1);
-    rv0 = *reinterpret_cast<const uint4*>(vb + (long long)v0 * D + dg * 8);
-    rv1 = *reinterpret_cast<const uint4*>(vb + (long long)v1 * D + dg * 8);
+    if (do_k) {
+      const int a0 = min(t0 + (kc0 >> 4), L - 1), a1 = min(t0 + (kc1 >> 4), L - 1);
+      rk0 = *reinterpret_cast<const uint4*>(kb + (long long)a0 * D + (kc0 & 15) * 8);
+      rk1 = *reinterpret_cast<const uint4*>(kb + (long long)a1 * D + (kc1 & 15) * 8);
+    }
+    if (do_v) {
+      const int v0 = min(t0 + 2 * tp, L - 1), v1 = min(t0 + 2 * tp + 1, L - 1);
+      rv0 = *reinterpret_cast<const uint4*>(vb + (long long)v0 * D + dg * 8);
+      rv1 = *reinterpret_cast<const uint4*>(vb + (long long)v1 * D + dg * 8);
+    }
     wd_next = brow[min(t0 >> 5, nwords - 1)];
   };
   float m = neg_inf(), l = 0.f;
@@ -790,9 +799,11 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_mfma_kernel(
   for (int t0 = 0; t0 < t_end; t0 += 32) {
     const uint32_t wd = qvalid ? wd_next : 0u;
     __syncthreads();   // the previous tile's readers are done
-    *reinterpret_cast<uint4*>(&Ks[(kc0 >> 4) * kPfKS + (kc0 & 15) * 8]) = rk0;
-    *reinterpret_cast<uint4*>(&Ks[(kc1 >> 4) * kPfKS + (kc1 & 15) * 8]) = rk1;
-    {
+    if (do_k) {
+      *reinterpret_cast<uint4*>(&Ks[(kc0 >> 4) * kPfKS + (kc0 & 15) * 8]) = rk0;
+      *reinterpret_cast<uint4*>(&Ks[(kc1 >> 4) * kPfKS + (kc1 & 15) * 8]) = rk1;
+    }
+    if (do_v) {
       uint32_t* vw = reinterpret_cast<uint32_t*>(Vt);
       const uint32_t x0[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
       const uint32_t x1[4] = {rv1.x, rv1.y, rv1.z, rv1.w};
@@ -880,10 +891,12 @@ hipError_t bm_t(hipStream_t s, const void* q, const void* k, const void* v,
   const long long rows = (long long)B * Hkv * Lq;
   if constexpr (std::is_same<T, bf16_t>::value && D == 128 && R == 4) {
     if (Lq >= 32) {
-      const long long blocks = (long long)B * Hkv * ((Lq + 31) / 32);
-      hipLaunchKernelGGL(attn_prefill_mfma_kernel, dim3((unsigned)blocks), dim3(kPfThreads), 0, s,
-                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, bitmask, out, Hq,
-                         Hkv, Lq, L, L_cap, q_pos0, scale * 1.4426950408889634f);
+      // 64 query rows per workgroup: each staged K/V tile serves eight waves
+      const long long blocks = (long long)B * Hkv * ((Lq + 63) / 64);
+      hipLaunchKernelGGL(attn_prefill_mfma_kernel<2>, dim3((unsigned)blocks),
+                         dim3(2 * kPfThreads), 0, s, (const bf16_t*)q, (const bf16_t*)k,
+                         (const bf16_t*)v, bitmask, out, Hq, Hkv, Lq, L, L_cap, q_pos0,
+                         scale * 1.4426950408889634f);
       return hipGetLastError();
     }
   }
