@@ -333,6 +333,48 @@ def run_softvote(device, cache_threshold=None):
     return res
 
 
+def run_interval(w, L, interval, width, device, reps=8):
+    """The layer decode with TokenButler's prediction interval and neighbour fetching (arXiv
+    abstract; interval and width are not on the pages): the predictor scores and selects
+    once every `interval` steps of a layer, and the steps in between reuse that selection
+    widened by `width` neighbours per side and the window.  K_imp is still appended every
+    step, so the next predictor run sees every token.  8 layer replicas as the headline;
+    one graph holds `reps` intervals of every replica."""
+    import torch
+    import query_aware_sparse_imp_amd as qa
+    layers = [Layer(w, r, L, device) for r in range(8)]
+    B, Hkv = w.B, w.Hkv
+    for lay in layers:
+        lay.cap2 = min(L, lay.cap * (2 * width + 1) + w.n_window)
+        lay.idx2 = torch.empty(B, Hkv, 1, lay.cap2, dtype=torch.int32, device=device)
+        lay.count2 = torch.empty(B, Hkv, 1, dtype=torch.int32, device=device)
+
+    def reuse_calls(lay):
+        return [
+            lambda: qa.butler_project_keys(lay.k, lay.wk, lay.kimp, L - 1, 1),
+            lambda: qa.butler_expand_neighbors(
+                lay.idx.view(B, Hkv, lay.cap), lay.count.view(B, Hkv),
+                lay.idx2.view(B, Hkv, lay.cap2), lay.count2.view(B, Hkv), L=L, width=width,
+                n_window=w.n_window),
+            lambda: qa.butler_sparse_decode_attn(lay.q, lay.k, lay.v, lay.out, L=L,
+                                                 idx=lay.idx2, count=lay.count2,
+                                                 softmax_scale=w.scale)]
+    fns = []
+    for i in range(interval):
+        for lay in layers:
+            fns += [f for _, f in lay.calls()] if i == 0 else reuse_calls(lay)
+    sec = graph_time(fns, reps) / (interval * len(layers))
+    expand_only = graph_time([reuse_calls(lay)[1] for lay in layers], reps) / len(layers)
+    widened = sum(int(lay.count2.sum()) for lay in layers) / len(layers)
+    for lay in layers:
+        lay.free()
+        lay.idx2 = lay.count2 = None
+    return {"workload": f"{w.name}, prediction interval {interval}, neighbours +-{width}",
+            "L": L, "interval": interval, "width": width, "steps_per_s": 1.0 / sec,
+            "ms_per_step": sec * 1e3, "expand_us": round(expand_only * 1e6, 2),
+            "widened_per_step": widened}
+
+
 def _rope_t(x, base=500000.0):
     """Rotate-half RoPE over the last dim of x [..., T, D] (positions 0..T-1), float32."""
     import torch
@@ -511,8 +553,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--L", type=int, default=None)
-    ap.add_argument("--configs", default="3,4,5",
-                    help="other workloads to measure: 3 soft-voting, 4 full depth, 5 prefill")
+    ap.add_argument("--configs", default="2i,3,4,5",
+                    help="other workloads to measure: 2i prediction interval, 3 soft-voting, "
+                         "4 full depth, 5 prefill")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run a 256 MiB device copy first (HBM counter calibration)")
     a = ap.parse_args(argv)
@@ -563,7 +606,9 @@ def main(argv=None) -> int:
     for c in [x for x in a.configs.split(",") if x]:
         torch.cuda.empty_cache()
         log(f"[bench] workload {c}")
-        if c == "3":
+        if c == "2i":
+            others["layer_decode_prediction_interval"] = run_interval(w, L, 4, 1, dev)
+        elif c == "3":
             others["softvote_decode"] = run_softvote(dev)
             others["softvote_decode_selection_cache"] = run_softvote(dev, cache_threshold=0.98)
         elif c == "4":

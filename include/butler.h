@@ -232,6 +232,27 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
 int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, int32_t* keep,
                            int B, int Hq, int Hkv, int D, float threshold);
 
+/*
+ * butler_expand_neighbors -- neighbour fetching for the prediction interval.
+ * TokenButler arXiv abstract: the predictor can run once per prediction interval, the
+ * selection made at its last run being reused in between and widened with the tokens'
+ * neighbours (neighbor fetching).  Per (b, KV head) decode row:
+ *   S' = { u : |u - t| <= width for some t in S }  U  [max(0, L - n_window), L),  0 <= u < L
+ * where S is the first min(count, cap_in) entries of idx (a selection made at an earlier,
+ * shorter length) and the window is taken at the current length L, so the tokens appended
+ * since are attended.  Indices outside [0, L) in S are ignored.  idx_out holds S' in
+ * ascending order in its first count_out entries (entries beyond cap_out are dropped;
+ * count_out is |S'|).
+ *
+ *   idx       [B, Hkv, cap_in]    int32 (read), count [B, Hkv] int32 (read)
+ *   idx_out   [B, Hkv, cap_out]   int32 (written), count_out [B, Hkv] int32 (written)
+ * 0 <= width <= 31; L <= 2^23; cap_out >= min(L, cap_in * (2*width + 1) + n_window); the
+ * output buffers must not alias the inputs.  No workspace.
+ */
+int butler_expand_neighbors(void* stream, const int32_t* idx, const int32_t* count,
+                            int32_t* idx_out, int32_t* count_out, int B, int Hkv, int L,
+                            int cap_in, int cap_out, int width, int n_window);
+
 #ifdef __cplusplus
 }
 #endif

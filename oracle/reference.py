@@ -19,6 +19,9 @@ even, into its storage type.  Sources, cited by page title and section:
   ``min_sparse_index`` (sink) and ``sliding_window`` (window).
 * "TokenButler: Token Importance is Predictable" (arXiv abstract page):
   selection is per token under a fixed budget, the full KV cache is kept.
+* "TokenButler: Token Importance is Predictable" (arXiv abstract page):
+  prediction interval with neighbor fetching -- the predictor's selection is
+  reused between its runs, widened with the selected tokens' neighbours.
 * TokenSelect README, first highlights: per-head Q.K criticality, per-head
   softmax, summed over heads ("soft voting"); Selection Cache: consecutive
   similar queries share one token selection.
@@ -367,6 +370,24 @@ def selection_cache(q, q_ref, Hkv: int, threshold: float):
     new_ref = np.where(keep[:, :, None, None], c.reshape(B, Hkv, R, D),
                        a.reshape(B, Hkv, R, D)).reshape(B, Hq, D)
     return keep, new_ref, cos
+
+
+def expand_neighbors(sel, L: int, width: int, n_window: int) -> np.ndarray:
+    """Neighbour fetching for the prediction interval (TokenButler arXiv abstract page:
+    prediction interval with neighbor fetching).  The abstract only names the method; the
+    reading taken here: between predictor runs the last selection ``sel`` (token indices of
+    one row, any order) is reused at the current length L, every reused token brings the
+    tokens within ``width`` positions of it, and the recent window [L - n_window, L) is
+    added so tokens appended since the selection are attended.  Indices outside [0, L) are
+    dropped.  Returns the ascending int64 set."""
+    out = set()
+    for t in np.asarray(sel, np.int64).tolist():
+        if 0 <= t < L:
+            for u in range(t - width, t + width + 1):
+                if 0 <= u < L:
+                    out.add(u)
+    out.update(range(max(0, L - n_window), L))
+    return np.array(sorted(out), dtype=np.int64)
 
 
 def ulps_bf16(a, b) -> np.ndarray:

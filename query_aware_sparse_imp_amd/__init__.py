@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "BUTLER_OK", "BUTLER_SCORE_RAW", "BUTLER_SCORE_SOFTVOTE", "ButlerError", "lib", "LIB_PATH",
     "butler_project_keys", "butler_produce_queries", "butler_score", "butler_select_topk",
-    "butler_sparse_decode_attn", "butler_selection_cache", "butler_status_string",
+    "butler_sparse_decode_attn", "butler_selection_cache", "butler_expand_neighbors",
+    "butler_status_string",
     "butler_abi_version", "declared_symbols", "workspace_bytes",
 ]
 
@@ -47,6 +48,7 @@ _SIGS = {
     "butler_select_topk": ([_vp, _vp, _vp, _vp] + [_i] * 4 + [_vp, _vp, _vp] + [_i] * 7 +
                            [_vp, _sz], _i),
     "butler_selection_cache": ([_vp, _i, _vp, _vp, _vp] + [_i] * 4 + [_f], _i),
+    "butler_expand_neighbors": ([_vp] * 5 + [_i] * 7, _i),
     "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 9 + [_f, _vp, _sz], _i),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -279,3 +281,22 @@ def butler_selection_cache(q: torch.Tensor, q_ref: torch.Tensor, keep: torch.Ten
     _check("butler_selection_cache", lib.butler_selection_cache(
         _stream(stream), _dtype_code(q), _ptr(q), _ptr(q_ref), _ptr(keep), B, Hq, Hkv, D,
         float(threshold)))
+
+
+def butler_expand_neighbors(idx: torch.Tensor, count: torch.Tensor, idx_out: torch.Tensor,
+                            count_out: torch.Tensor, *, L: int, width: int, n_window: int,
+                            stream=None) -> None:
+    """Widens a reused selection with its tokens' neighbours and the window at length L
+    (see butler.h).  idx: int32 [B, Hkv, cap_in]; count: int32 [B, Hkv];
+    idx_out: int32 [B, Hkv, cap_out]; count_out: int32 [B, Hkv]."""
+    if idx.dim() != 3 or idx_out.dim() != 3 or idx.shape[:2] != idx_out.shape[:2]:
+        raise ValueError("shape mismatch")
+    B, Hkv, cap_in = idx.shape
+    for t in (idx, count, idx_out, count_out):
+        if t.dtype != torch.int32:
+            raise TypeError("int32 tensors expected")
+    if count.shape != (B, Hkv) or count_out.shape != (B, Hkv):
+        raise ValueError("count must be [B, Hkv]")
+    _check("butler_expand_neighbors", lib.butler_expand_neighbors(
+        _stream(stream), _ptr(idx), _ptr(count), _ptr(idx_out), _ptr(count_out), B, Hkv,
+        int(L), cap_in, idx_out.shape[2], int(width), int(n_window)))

@@ -225,4 +225,21 @@ int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, 
   return finish(s, launch_selection_cache(s, dtype, q, q_ref, keep, B, Hq, Hkv, D, threshold));
 }
 
+int butler_expand_neighbors(void* stream, const int32_t* idx, const int32_t* count,
+                            int32_t* idx_out, int32_t* count_out, int B, int Hkv, int L,
+                            int cap_in, int cap_out, int width, int n_window) {
+  if (B <= 0 || Hkv <= 0 || L <= 0 || cap_in <= 0 || cap_out <= 0) return BUTLER_ERR_INVALID_ARG;
+  if (width < 0 || width > 31 || n_window < 0) return BUTLER_ERR_INVALID_ARG;
+  if (L > expand_max_len() || (long long)B * Hkv > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
+  if (cap_out < L && (long long)cap_out < (long long)cap_in * (2 * width + 1) + n_window)
+    return BUTLER_ERR_INVALID_ARG;
+  if (!idx || !count || !idx_out || !count_out) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(idx) || !aligned16(count) || !aligned16(idx_out) || !aligned16(count_out))
+    return BUTLER_ERR_INVALID_ARG;
+  if (idx == idx_out || count == count_out) return BUTLER_ERR_INVALID_ARG;   // no aliasing
+  hipStream_t s = (hipStream_t)stream;
+  return finish(s, launch_expand_neighbors(s, idx, count, idx_out, count_out, B * Hkv, L, cap_in,
+                                           cap_out, width, n_window));
+}
+
 }  // extern "C"

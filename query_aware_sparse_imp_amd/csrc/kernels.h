@@ -50,4 +50,9 @@ hipError_t launch_attn_bitmask(hipStream_t s, int dtype, const void* q, const vo
 hipError_t launch_selection_cache(hipStream_t s, int dtype, const void* q, void* q_ref,
                                   int32_t* keep, int B, int Hq, int Hkv, int D, float threshold);
 
+hipError_t launch_expand_neighbors(hipStream_t s, const int32_t* idx, const int32_t* count,
+                                   int32_t* idx_out, int32_t* count_out, int rows, int L,
+                                   int cap_in, int cap_out, int width, int n_window);
+int expand_max_len();
+
 }  // namespace butler

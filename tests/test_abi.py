@@ -21,7 +21,7 @@ def test_every_declared_symbol_is_exported():
     names = qa.declared_symbols()
     assert {"butler_project_keys", "butler_produce_queries", "butler_score",
             "butler_select_topk", "butler_sparse_decode_attn",
-            "butler_selection_cache"} <= set(names)
+            "butler_selection_cache", "butler_expand_neighbors"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", qa.LIB_PATH], capture_output=True,
@@ -122,3 +122,18 @@ def test_selection_cache_validation():
     assert f(None, 5, FAKE, FAKE, FAKE, 16, 32, 8, 128, 0.98) == UNS         # dtype
     assert f(None, 1, FAKE, FAKE, FAKE, 16, 32, 8, 128, float("nan")) == INV  # threshold
 
+
+
+def test_expand_neighbors_validation():
+    f = L.butler_expand_neighbors
+    A, B2, C, D = FAKE, FAKE + 256, FAKE + 512, FAKE + 768
+    # idx, count, idx_out, count_out, B, Hkv, L, cap_in, cap_out, width, n_window
+    assert f(None, A, B2, A, D, 1, 8, 4096, 64, 512, 1, 16) == INV        # idx_out aliases idx
+    assert f(None, A, B2, C, B2, 1, 8, 4096, 64, 512, 1, 16) == INV       # count_out aliases
+    assert f(None, None, B2, C, D, 1, 8, 4096, 64, 512, 1, 16) == INV     # null idx
+    assert f(None, MIS, B2, C, D, 1, 8, 4096, 64, 512, 1, 16) == INV      # misaligned
+    assert f(None, A, B2, C, D, 1, 8, 4096, 64, 512, 32, 16) == INV       # width > 31
+    assert f(None, A, B2, C, D, 1, 8, 4096, 64, 512, -1, 16) == INV       # negative width
+    assert f(None, A, B2, C, D, 1, 8, 4096, 64, 100, 1, 16) == INV        # cap_out too small
+    assert f(None, A, B2, C, D, 1, 8, (1 << 23) + 1, 64, 1 << 24, 1, 16) == UNS   # L
+    assert f(None, A, B2, C, D, 0, 8, 4096, 64, 512, 1, 16) == INV        # B

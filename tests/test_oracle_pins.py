@@ -513,3 +513,34 @@ def test_selection_cache_pins():
                       (np.linalg.norm(a[bb, 2 * g:2 * g + 2]) * np.linalg.norm(b[bb, 2 * g:2 * g + 2]))
                       for g in range(2)] for bb in range(2)])
     assert np.allclose(c_ab, want, rtol=0, atol=1e-15)
+
+
+def test_expand_neighbors_pins():
+    """Neighbour fetching: hand-worked sets (edges clipped, overlaps merged, the window at
+    the current length, width 0, unordered and out-of-range input), then random rows
+    against a morphological dilation of the selection's indicator vector (a convolution
+    with a box of 2*width+1 ones), which forms the set by another route."""
+    E = oracle.expand_neighbors
+    assert E([4], 10, 1, 0).tolist() == [3, 4, 5]
+    assert E([0], 10, 2, 0).tolist() == [0, 1, 2]                    # clipped at 0
+    assert E([9], 10, 2, 0).tolist() == [7, 8, 9]                    # clipped at L - 1
+    assert E([2, 4], 10, 1, 0).tolist() == [1, 2, 3, 4, 5]           # overlap merged once
+    assert E([1], 10, 0, 3).tolist() == [1, 7, 8, 9]                 # window [L-3, L)
+    assert E([1], 4, 0, 9).tolist() == [0, 1, 2, 3]                  # window wider than L
+    assert E([5, 1, 5], 10, 0, 0).tolist() == [1, 5]                 # unordered, repeated
+    assert E([-1, 12], 10, 3, 0).tolist() == []                      # outside [0, L) dropped
+    assert E([], 10, 3, 2).tolist() == [8, 9]
+    # a selection made at a shorter length, reused after the cache grew: the window moves
+    assert E([0, 1, 2, 5, 6], 12, 1, 2).tolist() == [0, 1, 2, 3, 4, 5, 6, 7, 10, 11]
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        L = int(rng.integers(1, 400)) if trial % 3 else int(rng.integers(1, 8))
+        w = int(rng.integers(0, 6))
+        nw = int(rng.integers(0, 20))
+        sel = rng.choice(L + 10, size=int(rng.integers(0, L + 1)), replace=True) - 5
+        ind = np.zeros(L)
+        inr = sel[(sel >= 0) & (sel < L)]
+        ind[inr] = 1.0
+        dil = np.convolve(ind, np.ones(2 * w + 1), mode="full")[w:w + L] > 0.5
+        dil[max(0, L - nw):] = True
+        assert np.array_equal(E(sel, L, w, nw), np.flatnonzero(dil))
