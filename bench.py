@@ -80,10 +80,10 @@ class Layer:
     def calls(self):
         qa, w, L = self.qa, self.w, self.L
         return [
-            ("project", lambda: qa.butler_project_keys(self.k, self.wk, self.kimp, L - 1, 1)),
-            ("score", lambda: qa.butler_score(qa.BUTLER_SCORE_RAW, self.qi, self.kimp,
-                                              self.scores, Hkv=w.Hkv, L=L,
-                                              radix_hist=self.hist)),
+            # the appended token's K_imp row is projected inside the scoring launch
+            ("project+score", lambda: qa.butler_project_and_score(
+                self.qi, self.k, self.wk, self.kimp, self.scores, Hkv=w.Hkv, L=L,
+                radix_hist=self.hist)),
             ("select", lambda: qa.butler_select_topk(self.scores, w.budget_num, w.budget_den,
                                                      w.n_sink, w.n_window, self.count,
                                                      idx=self.idx, radix_hist=self.hist)),
@@ -163,7 +163,7 @@ def run_config(w, L, replicas, steps, warmup, device):
         # Events around a graph of `steps` back-to-back calls of one kind.  The scorer and
         # the selection share the first-digit histogram (the scorer fills it, the selection
         # empties it), so they are timed together as one pair.
-        groups = {"project": ["project"], "score+select": ["score", "select"], "attn": ["attn"]}
+        groups = {"project+score+select": ["project+score", "select"], "attn": ["attn"]}
         for gname, members in groups.items():
             gk = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gk):
@@ -333,46 +333,54 @@ def run_softvote(device, cache_threshold=None):
     return res
 
 
-def run_interval(w, L, interval, width, device, reps=8):
+def run_interval(w, L, interval, widths, device, reps=8):
     """The layer decode with TokenButler's prediction interval and neighbour fetching (arXiv
     abstract; interval and width are not on the pages): the predictor scores and selects
     once every `interval` steps of a layer, and the steps in between reuse that selection
     widened by `width` neighbours per side and the window.  K_imp is still appended every
     step, so the next predictor run sees every token.  8 layer replicas as the headline;
-    one graph holds `reps` intervals of every replica."""
+    one graph holds `reps` intervals of every replica; one result per width."""
     import torch
     import query_aware_sparse_imp_amd as qa
     layers = [Layer(w, r, L, device) for r in range(8)]
     B, Hkv = w.B, w.Hkv
-    for lay in layers:
-        lay.cap2 = min(L, lay.cap * (2 * width + 1) + w.n_window)
-        lay.idx2 = torch.empty(B, Hkv, 1, lay.cap2, dtype=torch.int32, device=device)
-        lay.count2 = torch.empty(B, Hkv, 1, dtype=torch.int32, device=device)
-
-    def reuse_calls(lay):
-        return [
-            lambda: qa.butler_project_keys(lay.k, lay.wk, lay.kimp, L - 1, 1),
-            lambda: qa.butler_expand_neighbors(
-                lay.idx.view(B, Hkv, lay.cap), lay.count.view(B, Hkv),
-                lay.idx2.view(B, Hkv, lay.cap2), lay.count2.view(B, Hkv), L=L, width=width,
-                n_window=w.n_window),
-            lambda: qa.butler_sparse_decode_attn(lay.q, lay.k, lay.v, lay.out, L=L,
-                                                 idx=lay.idx2, count=lay.count2,
-                                                 softmax_scale=w.scale)]
-    fns = []
-    for i in range(interval):
+    res = []
+    for width in widths:
         for lay in layers:
-            fns += [f for _, f in lay.calls()] if i == 0 else reuse_calls(lay)
-    sec = graph_time(fns, reps) / (interval * len(layers))
-    expand_only = graph_time([reuse_calls(lay)[1] for lay in layers], reps) / len(layers)
-    widened = sum(int(lay.count2.sum()) for lay in layers) / len(layers)
+            lay.cap2 = min(L, lay.cap * (2 * width + 1) + w.n_window)
+            lay.idx2 = torch.empty(B, Hkv, 1, lay.cap2, dtype=torch.int32, device=device)
+            lay.count2 = torch.empty(B, Hkv, 1, dtype=torch.int32, device=device)
+
+        def reuse_calls(lay, width=width):
+            return [
+                lambda: qa.butler_project_keys(lay.k, lay.wk, lay.kimp, L - 1, 1),
+                lambda: qa.butler_expand_neighbors(
+                    lay.idx.view(B, Hkv, lay.cap), lay.count.view(B, Hkv),
+                    lay.idx2.view(B, Hkv, lay.cap2), lay.count2.view(B, Hkv), L=L,
+                    width=width, n_window=w.n_window),
+                lambda: qa.butler_sparse_decode_attn(lay.q, lay.k, lay.v, lay.out, L=L,
+                                                     idx=lay.idx2, count=lay.count2,
+                                                     softmax_scale=w.scale)]
+        fns = []
+        for i in range(interval):
+            for lay in layers:
+                fns += [f for _, f in lay.calls()] if i == 0 else reuse_calls(lay)
+        sec = graph_time(fns, reps) / (interval * len(layers))
+        expand_only = graph_time([reuse_calls(lay)[1] for lay in layers], reps) / len(layers)
+        widened = sum(int(lay.count2.sum()) for lay in layers) / len(layers)
+        selected = sum(int(lay.count.sum()) for lay in layers) / len(layers)
+        res.append({"workload": f"{w.name}, prediction interval {interval}, "
+                                f"neighbours +-{width}",
+                    "L": L, "interval": interval, "width": width,
+                    "steps_per_s": 1.0 / sec, "ms_per_step": sec * 1e3,
+                    "expand_us": round(expand_only * 1e6, 2),
+                    "selected_per_predictor_step": selected,
+                    "attended_per_reuse_step": widened})
+        for lay in layers:
+            lay.idx2 = lay.count2 = None
     for lay in layers:
         lay.free()
-        lay.idx2 = lay.count2 = None
-    return {"workload": f"{w.name}, prediction interval {interval}, neighbours +-{width}",
-            "L": L, "interval": interval, "width": width, "steps_per_s": 1.0 / sec,
-            "ms_per_step": sec * 1e3, "expand_us": round(expand_only * 1e6, 2),
-            "widened_per_step": widened}
+    return res
 
 
 def _rope_t(x, base=500000.0):
@@ -434,7 +442,8 @@ def run_full_depth(steps, device):
     cnt = torch.empty(w.B, w.Hkv, 1, dtype=torch.int32, device=device)
     out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
     fns = []
-    groups = {"produce": [], "project": [], "dense layer 0": [], "score+select": [], "attn": []}
+    groups = {"produce": [], "project": [], "dense layer 0": [], "project+score+select": [],
+              "attn": []}
 
     def add(group, *fs):
         fns.extend(fs)
@@ -442,8 +451,9 @@ def run_full_depth(steps, device):
     for l, d in enumerate(lay):
         if l % w.G == 0:
             add("produce", lambda d=d: qa.butler_produce_queries(d["h"], d["w1"], d["w2"], d["qimp"]))
-        add("project", lambda d=d: qa.butler_project_keys(d["k"], d["wk"], d["kimp"], L - 1, 1))
         if l == 0:   # dense layer: the budget takes every token
+            add("project", lambda d=d: qa.butler_project_keys(d["k"], d["wk"], d["kimp"],
+                                                               L - 1, 1))
             add("dense layer 0",
                 lambda: qa.butler_select_topk(scores, 1, 1, w.n_sink, w.n_window, cnt,
                                               idx=idx_dense),
@@ -453,10 +463,10 @@ def run_full_depth(steps, device):
             continue
         prod = lay[w.G * (l // w.G)]
         slot = (l - 1) % w.G
-        add("score+select",
-            lambda d=d, prod=prod, slot=slot: qa.butler_score(
-                qa.BUTLER_SCORE_RAW, prod["qimp"], d["kimp"], scores, Hkv=w.Hkv, L=L,
-                slot=slot, radix_hist=hist),
+        add("project+score+select",
+            lambda d=d, prod=prod, slot=slot: qa.butler_project_and_score(
+                prod["qimp"], d["k"], d["wk"], d["kimp"], scores, Hkv=w.Hkv, L=L, slot=slot,
+                radix_hist=hist),
             lambda: qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink,
                                           w.n_window, cnt, idx=idx, radix_hist=hist))
         add("attn", lambda d=d: qa.butler_sparse_decode_attn(d["q"], d["k"], d["v"], out, L=L,
@@ -607,7 +617,7 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
         log(f"[bench] workload {c}")
         if c == "2i":
-            others["layer_decode_prediction_interval"] = run_interval(w, L, 4, 1, dev)
+            others["layer_decode_prediction_interval"] = run_interval(w, L, 4, (0, 1), dev)
         elif c == "3":
             others["softvote_decode"] = run_softvote(dev)
             others["softvote_decode_selection_cache"] = run_softvote(dev, cache_threshold=0.98)

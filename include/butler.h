@@ -59,14 +59,14 @@ enum butler_score_mode { BUTLER_SCORE_RAW = 0, BUTLER_SCORE_SOFTVOTE = 1 };
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* butler_status_string(int status);
 
-/* ABI version, currently 1. */
+/* ABI version, currently 2. */
 int butler_abi_version(void);
 
 /*
  * butler_project_keys -- K_imp = K . W_K for the tokens [pos0, pos0 + n_new).
- * Model card, Method: "the real (post-RoPE) cached keys are projected into the same
- * d'-dimensional space via a learned matrix W_K of shape D x d'", appended once per
- * generated token (n_new = 1 in decode, n_new = L when a prompt is first cached).
+ * Model card, Method: every cached key (after RoPE) is mapped to the d'-dimensional
+ * importance space by a learned D x d' matrix W_K; one row is added per generated token
+ * (n_new = 1 in decode, n_new = L when a prompt is first cached).
  *
  *   k_cache [B, Hkv, L_cap, D]      dtype   cached keys (read)
  *   w_k     [D, d']                 dtype   projection of this layer, shared by all KV heads
@@ -143,6 +143,28 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
                  void* workspace, size_t* ws_bytes);
 
 /*
+ * butler_project_and_score -- one decode step's projection and raw scoring in one launch:
+ * the same results as butler_project_keys(pos0 = L - 1, n_new = 1) followed by
+ * butler_score(BUTLER_SCORE_RAW, Lq = 1, non-causal) with the same arguments.  Model card,
+ * Method: the key row of the token just appended is projected to K_imp, then every cached
+ * token (this one included) is scored against the consumer's slot of Q_imp.
+ *
+ *   q_imp      [B, Hq, G, 1, d']    dtype (read), slot `slot` is used
+ *   k_cache    [B, Hkv, L_cap, D]   dtype (read): row L - 1 is projected
+ *   w_k        [D, d']              dtype (read)
+ *   kimp       [B, Hkv, L_cap, d']  dtype: row L - 1 written (even for kept rows), rows
+ *                                   0 .. L-2 read
+ *   scores     [B, Hkv, 1, L]       float32 (written)
+ *   radix_hist, keep                as in butler_score (single-row call)
+ * D in {64, 128}; d' in {16, 32}; R in {1, 2, 4, 8}; B * Hkv <= 65535; kimp must not alias
+ * k_cache or w_k.  No workspace.
+ */
+int butler_project_and_score(void* stream, int dtype, const void* q_imp, const void* k_cache,
+                             const void* w_k, void* kimp, float* scores, uint32_t* radix_hist,
+                             const int32_t* keep, int B, int Hq, int Hkv, int G, int slot,
+                             int L, int L_cap, int D, int dprime);
+
+/*
  * butler_select_topk -- fixed-budget top-x + sink + window, per KV head and query row.
  * Model card, Method and Memory requirements: keep the top-x tokens under a fixed
  * budget (fixed_<N>pc keeps (100-N)% of the tokens), augmented by a sink prefix of
@@ -190,8 +212,8 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
  * with float32 logits, float32 online softmax and float32 accumulation.
  *
  * Lq == 1 (decode): S comes from idx [B, Hkv, 1, cap] / count [B, Hkv, 1] as written by
- *   butler_select_topk; split over the selected list, partial results merged in a fixed
- *   order by the last block of each KV head.
+ *   butler_select_topk (or butler_expand_neighbors); the list is split over workgroups
+ *   and a second kernel merges the partial results in a fixed order.
  * Lq > 1 (chunked prefill): S of row i comes from bitmask [B, Hkv, Lq, ceil(L/32)];
  *   query row i sits at absolute position q_pos0 + i; only tokens t <= q_pos0 + i may
  *   be selected.
@@ -202,7 +224,7 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
  *   out     [B, Hq, Lq, D]      float32 (written)
  * An empty selected set is an error of the caller (the window always holds the newest
  * token); its output row is written as zeros.  Selected indices must be < L <= L_cap.
- * workspace: per-block softmax partials and merge tickets.
+ * workspace: per-split softmax partials (decode).
  */
 int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* idx, const int32_t* count,

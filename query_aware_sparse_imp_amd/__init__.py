@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "BUTLER_OK", "BUTLER_SCORE_RAW", "BUTLER_SCORE_SOFTVOTE", "ButlerError", "lib", "LIB_PATH",
-    "butler_project_keys", "butler_produce_queries", "butler_score", "butler_select_topk",
+    "butler_project_keys", "butler_produce_queries", "butler_score", "butler_project_and_score",
+    "butler_select_topk",
     "butler_sparse_decode_attn", "butler_selection_cache", "butler_expand_neighbors",
     "butler_status_string",
     "butler_abi_version", "declared_symbols", "workspace_bytes",
@@ -45,6 +46,7 @@ _SIGS = {
     "butler_project_keys": ([_vp, _i, _vp, _vp, _vp] + [_i] * 7, _i),
     "butler_produce_queries": ([_vp, _i, _vp, _vp, _vp, _vp] + [_i] * 7 + [_f, _vp, _sz], _i),
     "butler_score": ([_vp, _i, _i, _vp, _vp, _vp, _vp, _vp] + [_i] * 11 + [_f, _vp, _sz], _i),
+    "butler_project_and_score": ([_vp, _i] + [_vp] * 7 + [_i] * 9, _i),
     "butler_select_topk": ([_vp, _vp, _vp, _vp] + [_i] * 4 + [_vp, _vp, _vp] + [_i] * 7 +
                            [_vp, _sz], _i),
     "butler_selection_cache": ([_vp, _i, _vp, _vp, _vp] + [_i] * 4 + [_f], _i),
@@ -212,6 +214,30 @@ def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.T
     need = workspace_bytes(lambda ws, n: lib.butler_score(_stream(stream), *args, ws, n))
     ws, n = _workspace("score", need, q.device, tuple(args[7:]))
     _check("butler_score", lib.butler_score(_stream(stream), *args, ws, _byref(n)))
+
+
+def butler_project_and_score(q_imp: torch.Tensor, k_cache: torch.Tensor, w_k: torch.Tensor,
+                             kimp: torch.Tensor, scores: torch.Tensor, *, Hkv: int, L: int,
+                             slot: int = 0, radix_hist: Optional[torch.Tensor] = None,
+                             keep: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Projects key row L - 1 into kimp and scores tokens [0, L) in one launch: the same as
+    butler_project_keys(pos0=L-1, n_new=1) then butler_score(RAW) (see butler.h).
+    q_imp [B, Hq, G, 1, d'], k_cache [B, Hkv, L_cap, D], w_k [D, d'],
+    kimp [B, Hkv, L_cap, d'], scores [B, Hkv, 1, L]."""
+    B, Hq, G, Lq, dp = q_imp.shape
+    Bk, Hk, L_cap, D = k_cache.shape
+    if Lq != 1 or (Bk, Hk) != (B, Hkv) or w_k.shape != (D, dp):
+        raise ValueError("shape mismatch")
+    if kimp.shape != (B, Hkv, L_cap, dp) or scores.shape != (B, Hkv, 1, L):
+        raise ValueError("shape mismatch")
+    if not (q_imp.dtype == k_cache.dtype == w_k.dtype == kimp.dtype) or \
+            scores.dtype != torch.float32:
+        raise TypeError("dtype mismatch")
+    _check_hist(radix_hist, (B, Hkv, 1))
+    _check_keep(keep, (B, Hkv))
+    _check("butler_project_and_score", lib.butler_project_and_score(
+        _stream(stream), _dtype_code(q_imp), _ptr(q_imp), _ptr(k_cache), _ptr(w_k), _ptr(kimp),
+        _ptr(scores), _ptr(radix_hist), _ptr(keep), B, Hq, Hkv, G, slot, L, L_cap, D, dp))
 
 
 def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n_sink: int,

@@ -144,6 +144,27 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
                                          softmax_scale, workspace, hist, kp));
 }
 
+int butler_project_and_score(void* stream, int dtype, const void* q_imp, const void* k_cache,
+                             const void* w_k, void* kimp, float* scores, uint32_t* radix_hist,
+                             const int32_t* keep, int B, int Hq, int Hkv, int G, int slot,
+                             int L, int L_cap, int D, int dprime) {
+  if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || L_cap < L) return BUTLER_ERR_INVALID_ARG;
+  if (Hq % Hkv || G <= 0 || slot < 0 || slot >= G) return BUTLER_ERR_INVALID_ARG;
+  if (!pow2_group(Hq / Hkv)) return BUTLER_ERR_UNSUPPORTED;
+  if (!(D == 64 || D == 128) || !(dprime == 16 || dprime == 32)) return BUTLER_ERR_UNSUPPORTED;
+  if ((long long)B * Hkv > 65535) return BUTLER_ERR_UNSUPPORTED;
+  if (!q_imp || !k_cache || !w_k || !kimp || !scores) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(q_imp) || !aligned16(k_cache) || !aligned16(w_k) || !aligned16(kimp) ||
+      !aligned16(scores))
+    return BUTLER_ERR_INVALID_ARG;
+  if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
+  if (kimp == k_cache || kimp == w_k) return BUTLER_ERR_INVALID_ARG;   // no aliasing
+  hipStream_t s = (hipStream_t)stream;
+  return finish(s, launch_project_score(s, dtype, q_imp, k_cache, w_k, kimp, scores, B, Hq, Hkv,
+                                        G, slot, L, L_cap, D, dprime, radix_hist, keep));
+}
+
 int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
                        const int32_t* keep, int budget_num,
                        int budget_den,

@@ -19,6 +19,10 @@ hipError_t launch_produce(hipStream_t s, const void* h, const void* w1, const vo
                           float eps, void* ws);
 
 // ---- scoring --------------------------------------------------------------
+hipError_t launch_project_score(hipStream_t s, int dtype, const void* q_imp,
+                                const void* k_cache, const void* w_k, void* kimp,
+                                float* scores, int B, int Hq, int Hkv, int G, int slot, int L,
+                                int L_cap, int D, int dp, uint32_t* hist, const int32_t* keep);
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
                             int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist,

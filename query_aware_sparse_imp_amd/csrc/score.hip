@@ -47,17 +47,27 @@ struct RawBatch {
   uint4 v[U];
 };
 
-template <typename T, int DP>
+__device__ __forceinline__ bf16_t round_to(double v, bf16_t*) { return d2bf(v); }
+__device__ __forceinline__ float round_to(double v, float*) { return (float)v; }
+
+// DA > 0: the decode step's key row L - 1 (D = DA) is projected first, K_imp[L-1] =
+// K[L-1] . W_K, by the workgroup that holds token L - 1 -- with the summation order of
+// project_keys_kernel, so the row is the one butler_project_keys writes -- stored to
+// kimp_w, and scored from LDS.  Rows of kept (b, KV head) still get their K_imp row.
+template <typename T, int DP, int DA>
 __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
     const T* __restrict__ q_imp, const T* __restrict__ kimp, float* __restrict__ scores,
     int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal,
-    int tpb, uint32_t* __restrict__ radix_hist, const int32_t* __restrict__ keep) {
+    int tpb, uint32_t* __restrict__ radix_hist, const int32_t* __restrict__ keep,
+    const T* __restrict__ k_cache, const T* __restrict__ w_k, T* kimp_w) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPT = DP / EPL;           // lanes per token
   constexpr int TPI = kRawThreads / LPT;  // tokens per block-wide step
   constexpr int U = kRawUnroll;
   const int bg = blockIdx.z, i = blockIdx.y;
-  if (keep && keep[bg]) return;   // the cached selection stands (single-row calls)
+  const bool proj = DA > 0 && blockIdx.x == gridDim.x - 1;   // holds token L - 1
+  const bool skip = keep && keep[bg];
+  if (skip && !proj) return;   // the cached selection stands (single-row calls)
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int R = Hq / Hkv;
   const int part = threadIdx.x % LPT, sub = threadIdx.x / LPT;
@@ -77,6 +87,52 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   };
   __shared__ double qbar[DP];
   __shared__ uint32_t hist[2048];
+  constexpr int DW = DA > 0 ? DA : 1;
+  __shared__ float wsh[DW * DP];                  // W_K of the projection, as float
+  __shared__ float ksh[DW];                       // key row L - 1, as float
+  __shared__ __align__(16) T knew[DA > 0 ? DP : EPL];   // its K_imp row, storage type
+  if (proj) {
+    // W_K and the key row in 16-byte pieces, requested before anything else
+    constexpr int NPIECE = DW * DP / EPL;
+    constexpr int PER = (NPIECE + kRawThreads - 1) / kRawThreads;
+    float wv[PER][EPL], kv[EPL];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int pc = threadIdx.x + u * kRawThreads;
+      if (pc < NPIECE) Vec16<T>::load(w_k + pc * EPL, wv[u]);
+    }
+    const T* krow = k_cache + ((size_t)bg * L_cap + (L - 1)) * DW;
+    if (threadIdx.x < DW / EPL) Vec16<T>::load(krow + threadIdx.x * EPL, kv);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int pc = threadIdx.x + u * kRawThreads;
+      if (pc < NPIECE) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) wsh[pc * EPL + e] = wv[u][e];
+      }
+    }
+    if (threadIdx.x < DW / EPL) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ksh[threadIdx.x * EPL + e] = kv[e];
+    }
+    __syncthreads();
+    if (threadIdx.x < DP) {
+      const int j = threadIdx.x;
+      double acc4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int c = 0; c < DW / EPL; ++c) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          acc4[c & 3] = fma((double)ksh[c * EPL + e], (double)wsh[(c * EPL + e) * DP + j],
+                            acc4[c & 3]);
+      }
+      const T r = round_to((acc4[0] + acc4[1]) + (acc4[2] + acc4[3]), (T*)nullptr);
+      kimp_w[((size_t)bg * L_cap + (L - 1)) * DP + j] = r;
+      knew[j] = r;
+    }
+    __syncthreads();
+    if (skip) return;
+  }
   RawBatch<U> ba, bb;
   int t = t0 + sub;
   // the first two batches of K_imp rows are requested before the group query is summed
@@ -104,15 +160,16 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   auto consume = [&](const RawBatch<U>& rb, int tb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int tu = tb + u * TPI;
       Raw16 r16;
       r16.v = rb.v[u];
+      if (DA > 0 && proj && tu == L - 1) r16.v = reinterpret_cast<const uint4*>(knew)[part];
       float kf[EPL];
       unpack16<T>(r16, kf);
       double acc = 0.0;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc = fma(qv[e], (double)kf[e], acc);
       acc = quad_sum_d<LPT>(acc);
-      const int tu = tb + u * TPI;
       if (part == 0 && tu < t1) {
         const float sc = (tu < L_r) ? (float)acc : neg_inf();
         srow[tu] = sc;
@@ -503,10 +560,11 @@ hipError_t rows_t(hipStream_t s, const void* q_imp, const void* kimp, float* sco
   return hipGetLastError();
 }
 
-template <typename T, int DP>
+template <typename T, int DP, int DA = 0>
 hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scores, int B,
                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
-                 int causal, uint32_t* hist, const int32_t* keep) {
+                 int causal, uint32_t* hist, const int32_t* keep, const void* k_cache = nullptr,
+                 const void* w_k = nullptr) {
   constexpr int LPT = DP / Vec16<T>::N;
   // a tile is what one block-wide step covers (kRawUnroll loads per thread); a workgroup
   // loops over enough tiles that a row has at most kRawRowWg workgroups -- this bounds the
@@ -516,9 +574,10 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
   const int per = (tiles + kRawRowWg - 1) / kRawRowWg;
   const int tpb = tile * per;
   dim3 grid((L + tpb - 1) / tpb, Lq, B * Hkv);
-  hipLaunchKernelGGL((score_raw_kernel<T, DP>), grid, dim3(kRawThreads), 0, s, (const T*)q_imp,
-                     (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal,
-                     tpb, hist, keep);
+  hipLaunchKernelGGL((score_raw_kernel<T, DP, DA>), grid, dim3(kRawThreads), 0, s,
+                     (const T*)q_imp, (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap,
+                     q_pos0, causal, tpb, hist, keep, (const T*)k_cache, (const T*)w_k,
+                     (T*)const_cast<void*>(kimp));
   return hipGetLastError();
 }
 
@@ -565,6 +624,23 @@ hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const v
     if (dp == 32) return raw_t<float, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
     if (dp == 16) return raw_t<float, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_project_score(hipStream_t s, int dtype, const void* q_imp,
+                                const void* k_cache, const void* w_k, void* kimp,
+                                float* scores, int B, int Hq, int Hkv, int G, int slot, int L,
+                                int L_cap, int D, int dp, uint32_t* hist, const int32_t* keep) {
+#define BUTLER_PS(T, DP, DD)                                                                 \
+  if (dp == DP && D == DD)                                                                 \
+    return raw_t<T, DP, DD>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, 1, L, L_cap, 0, 0,  \
+                            hist, keep, k_cache, w_k);
+  if (dtype == 1) {
+    BUTLER_PS(bf16_t, 32, 128) BUTLER_PS(bf16_t, 16, 128) BUTLER_PS(bf16_t, 32, 64) BUTLER_PS(bf16_t, 16, 64)
+  } else {
+    BUTLER_PS(float, 32, 128) BUTLER_PS(float, 16, 128) BUTLER_PS(float, 32, 64) BUTLER_PS(float, 16, 64)
+  }
+#undef BUTLER_PS
   return hipErrorInvalidValue;
 }
 

@@ -137,3 +137,24 @@ def test_expand_neighbors_validation():
     assert f(None, A, B2, C, D, 1, 8, 4096, 64, 100, 1, 16) == INV        # cap_out too small
     assert f(None, A, B2, C, D, 1, 8, (1 << 23) + 1, 64, 1 << 24, 1, 16) == UNS   # L
     assert f(None, A, B2, C, D, 0, 8, 4096, 64, 512, 1, 16) == INV        # B
+
+
+def test_project_and_score_validation():
+    f = L.butler_project_and_score
+    P = [FAKE + 256 * i for i in range(5)]      # q_imp, k_cache, w_k, kimp, scores
+
+    def call(*, dtype=1, ptrs=P, hist=None, B=1, Hq=32, Hkv=8, G=1, slot=0, Lr=100, L_cap=100,
+             D=128, dp=32):
+        return f(None, dtype, *ptrs, hist, None, B, Hq, Hkv, G, slot, Lr, L_cap, D, dp)
+    assert call(dtype=7) == UNS
+    assert call(Lr=101) == INV                                   # L > L_cap
+    assert call(slot=1) == INV                                   # slot >= G
+    assert call(Hq=30) == INV                                    # Hq % Hkv
+    assert call(Hq=24) == UNS                                    # R = 3
+    assert call(D=96) == UNS
+    assert call(dp=8) == UNS
+    assert call(ptrs=[P[0], P[1], P[2], P[1], P[4]]) == INV      # kimp aliases k_cache
+    assert call(ptrs=[P[0], MIS, P[2], P[3], P[4]]) == INV       # misaligned
+    assert call(ptrs=[P[0], None, P[2], P[3], P[4]]) == INV
+    assert call(hist=MIS) == INV
+    assert call(B=9000) == UNS                                   # B * Hkv > 65535

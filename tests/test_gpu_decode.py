@@ -162,3 +162,47 @@ def test_scorer_histogram_matches_selection_without_it():
             assert torch.equal(a[key], b[key]), (L, key)
         check_select_exact(a["idx"], a["count"], np64(a["scores"]), w.budget_num, w.budget_den,
                            w.n_sink, w.n_window)
+
+
+@pytest.mark.parametrize("cfg,L", [(1, 256), (1, 1), (2, 1), (2, 5001), (2, 32768)])
+def test_project_and_score_matches_separate_calls(cfg, L):
+    """butler_project_and_score == butler_project_keys(L-1, 1) + butler_score(RAW): the
+    K_imp row, every score and the first-digit histogram bit for bit, whatever stale value
+    row L-1 of kimp held; with selection-cache flags the kept rows keep their scores and
+    histogram but still get their K_imp row.  The K_imp row is also checked against the
+    oracle's correctly rounded projection."""
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[cfg]
+    print(f"[project+score] cfg={cfg} L={L}", flush=True)
+    inp = to_device(synthetic.decode_layer(w, 0, L=L))
+    dev = "cuda"
+    k, wk, qi = inp["k_cache_d"], inp["w_k_d"], inp["q_imp_d"]
+    kimp_a = torch.zeros(w.B, w.Hkv, L, w.dprime, dtype=w.dtype, device=dev)
+    if L > 1:
+        qa.butler_project_keys(k, wk, kimp_a, 0, L - 1)
+    kimp_b = kimp_a.clone()
+    kimp_b[:, :, L - 1] = 7.0                                   # stale row, overwritten
+    sa = torch.empty(w.B, w.Hkv, 1, L, dtype=torch.float32, device=dev)
+    sb = torch.empty_like(sa)
+    ha = torch.zeros(w.B, w.Hkv, 1, 2048, dtype=torch.int32, device=dev)
+    hb = torch.zeros_like(ha)
+    qa.butler_project_keys(k, wk, kimp_a, L - 1, 1)
+    qa.butler_score(qa.BUTLER_SCORE_RAW, qi, kimp_a, sa, Hkv=w.Hkv, L=L, radix_hist=ha)
+    qa.butler_project_and_score(qi, k, wk, kimp_b, sb, Hkv=w.Hkv, L=L, radix_hist=hb)
+    torch.cuda.synchronize()
+    assert torch.equal(kimp_a, kimp_b)
+    assert torch.equal(sa, sb)
+    assert torch.equal(ha, hb) and int(ha.sum()) == w.B * w.Hkv * L
+    check_project(kimp_b, inp["k_cache"], inp["w_k"], L - 1, L)
+    # selection-cache flags: every other (b, KV head) kept
+    keep = (torch.arange(w.B * w.Hkv, dtype=torch.int32, device=dev) % 2).view(w.B, w.Hkv)
+    kimp_c = kimp_b.clone()
+    kimp_c[:, :, L - 1] = -3.0
+    sc = torch.full_like(sa, -5.0)
+    hc = torch.zeros_like(ha)
+    qa.butler_project_and_score(qi, k, wk, kimp_c, sc, Hkv=w.Hkv, L=L, radix_hist=hc, keep=keep)
+    torch.cuda.synchronize()
+    assert torch.equal(kimp_c, kimp_a)                          # written for kept rows too
+    kept = keep.bool()
+    assert (sc[kept] == -5.0).all() and int(hc[kept].abs().sum()) == 0
+    assert torch.equal(sc[~kept], sa[~kept]) and torch.equal(hc[~kept], ha[~kept])
