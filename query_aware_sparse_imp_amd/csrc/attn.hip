@@ -446,12 +446,18 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
                                             kk * 32 + 8 * quad);
     qf[kk] = as_bf16x8(raw);
   }
-  const int n = min(count[row], cap);
   const int p_begin = split * split_len;
+  const int32_t* irow = idx + (long long)row * cap;
+  // the first stage of indices is requested together with the count: its positions are
+  // clamped to the row's capacity, not to its count, so the two round trips overlap
+  constexpr int U = kMfStage / kMfThreads;
+  int iv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) iv[u] = irow[min(p_begin + (int)threadIdx.x + u * kMfThreads, cap - 1)];
+  const int n = min(count[row], cap);
   const int p_end = min(p_begin + split_len, n);
   const bf16_t* kb = k + (long long)bg * L_cap * D;
   const bf16_t* vb = v + (long long)bg * L_cap * D;
-  const int32_t* irow = idx + (long long)row * cap;
 
   float m = neg_inf(), l = 0.f;   // softmax state of head pe for this row's stream
   float acc[R][8];
@@ -464,18 +470,18 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
     const int len = min(kMfStage, p_end - cs);
     const int nr = (len + kMfRound - 1) / kMfRound;
     __syncthreads();
-    // the whole stage of indices is requested at once; positions past its end repeat its
-    // last entry, and indices outside [0, L_cap) are clamped so a bad list never reads
-    // past the cache
-    constexpr int U = kMfStage / kMfThreads;
-    const int last = (int)min((unsigned)irow[cs + len - 1], (unsigned)(L_cap - 1));
-    int iv[U];
+    if (cs != p_begin) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) iv[u] = irow[cs + min((int)threadIdx.x + u * kMfThreads, len - 1)];
+      for (int u = 0; u < U; ++u) iv[u] = irow[min(cs + (int)threadIdx.x + u * kMfThreads, cap - 1)];
+    }
+    // indices outside [0, L_cap) are clamped so a bad list never reads past the cache;
+    // positions past the stage's end then repeat its last entry (a row already loaded)
 #pragma unroll
     for (int u = 0; u < U; ++u)
       s_list[threadIdx.x + u * kMfThreads] = (int)min((unsigned)iv[u], (unsigned)(L_cap - 1));
-    for (int j = threadIdx.x; j < kMfPad; j += kMfThreads) s_list[kMfStage + j] = last;
+    __syncthreads();
+    const int last = s_list[len - 1];
+    for (int j = len + (int)threadIdx.x; j < kMfStage + kMfPad; j += kMfThreads) s_list[j] = last;
     __syncthreads();
     // a ring of kMfBuf tiles per wave: kMfBuf - 1 tiles are in flight during each compute.
     // Round rho lives in t[rho % kMfBuf]; the main loop has no branch, so every wait is for

@@ -843,8 +843,11 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
 
 
 
+#ifndef BUTLER_SEL_CHUNKED_ABOVE
+#define BUTLER_SEL_CHUNKED_ABOVE 4096
+#endif
 bool use_chunked(int Lq, int L, int causal) {
-  return !causal && Lq == 1 && L > 4096;
+  return !causal && Lq == 1 && L > BUTLER_SEL_CHUNKED_ABOVE;
 }
 
 }  // namespace
