@@ -427,8 +427,9 @@ def run_full_depth(steps, device):
         qa.butler_project_keys(d["k"], d["wk"], d["kimp"], 0, L)
         if l % w.G == 0:
             d["h"] = rn(w.B, 1, w.E).to(dt)
-            d["w1"] = rn(w.E, w.F, std=0.02).to(dt)
-            d["w2"] = rn(w.F, w.Hq * w.G * w.dprime, std=0.02).to(dt)
+            # [out, in] (PyTorch Linear) layout
+            d["w1"] = rn(w.F, w.E, std=0.02).to(dt)
+            d["w2"] = rn(w.Hq * w.G * w.dprime, w.F, std=0.02).to(dt)
             d["qimp"] = torch.empty(w.B, w.Hq, w.G, 1, w.dprime, dtype=dt, device=device)
         lay.append(d)
     torch.cuda.synchronize()
@@ -519,7 +520,8 @@ def run_prefill(device):
     Qc = [proj["q"][:, :, c * C:(c + 1) * C].contiguous() for c in range(nc)]
     Hc = [H[:, c * C:(c + 1) * C].contiguous() for c in range(nc)]
     del proj, H
-    w1, w2 = rn(w.E, w.F, std=0.02).to(dt), rn(w.F, w.Hq * w.G * w.dprime, std=0.02).to(dt)
+    # [out, in] (PyTorch Linear) layout
+    w1, w2 = rn(w.F, w.E, std=0.02).to(dt), rn(w.Hq * w.G * w.dprime, w.F, std=0.02).to(dt)
     wk = rn(w.D, w.dprime, std=0.02).to(dt)
     kimp = torch.empty(w.B, w.Hkv, L, w.dprime, dtype=dt, device=device)
     qimp = [torch.empty(w.B, w.Hq, w.G, C, w.dprime, dtype=dt, device=device) for _ in range(nc)]

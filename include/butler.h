@@ -59,7 +59,7 @@ enum butler_score_mode { BUTLER_SCORE_RAW = 0, BUTLER_SCORE_SOFTVOTE = 1 };
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* butler_status_string(int status);
 
-/* ABI version, currently 2. */
+/* ABI version, currently 3. */
 int butler_abi_version(void);
 
 /*
@@ -83,17 +83,19 @@ int butler_project_keys(void* stream, int dtype, const void* k_cache, const void
  * butler_produce_queries -- Q_imp = f_theta(LN(H)) at a producer layer.
  * Model card, Method: a producer reads the hidden states H [B, Lq, E] and predicts
  * importance queries for itself and the next G-1 layers, (B*Hq) x G x Lq x d'.
- * f_theta is the two-layer MLP  y = relu(LN(h) . W1) . W2  without biases; LN is a
+ * f_theta is the two-layer MLP  y = relu(LN(h) . W1^T) . W2^T  without biases; LN is a
  * LayerNorm without affine parameters (biased variance, ln_eps).  The normalised row,
  * the hidden activation and y are stored as bf16 between the steps.  Column
- * (head*G + slot)*d' + i of y is Q_imp[b, head, slot, t, i].
+ * (head*G + slot)*d' + i of y is Q_imp[b, head, slot, t, i].  The weights are in the
+ * [out_features, in_features] layout of a PyTorch Linear (K-contiguous rows).
  *
  *   h      [B, Lq, E]         bf16
- *   w1     [E, F]             bf16
- *   w2     [F, Hq*G*d']       bf16
+ *   w1     [F, E]             bf16
+ *   w2     [Hq*G*d', F]       bf16
  *   q_imp  [B, Hq, G, Lq, d'] bf16 (written)
  * dtype must be BUTLER_BF16.  E, F multiples of 64, E <= 8192; Hq*G*d' a multiple of 64.
- * workspace: normalised rows and hidden activations, split-K partial sums.
+ * workspace: normalised rows and hidden activations, split-K partial sums (at most 4
+ * rows: the hidden activations only).
  */
 int butler_produce_queries(void* stream, int dtype, const void* h, const void* w1,
                            const void* w2, void* q_imp, int B, int Lq, int E, int F, int Hq,

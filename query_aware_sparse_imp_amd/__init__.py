@@ -169,11 +169,12 @@ def butler_project_keys(k_cache: torch.Tensor, w_k: torch.Tensor, kimp: torch.Te
 
 def butler_produce_queries(h: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
                            q_imp: torch.Tensor, ln_eps: float = 1e-5, stream=None) -> None:
-    """q_imp [B, Hq, G, Lq, d'] = reshape(relu(LN(h) @ w1) @ w2) (see butler.h)."""
+    """q_imp [B, Hq, G, Lq, d'] = reshape(relu(LN(h) @ w1.T) @ w2.T) (see butler.h).
+    w1 [F, E] and w2 [Hq*G*d', F] are in the [out, in] layout of a PyTorch Linear."""
     B, Lq, E = h.shape
-    F = w1.shape[1]
+    F = w1.shape[0]
     _, Hq, G, Lq2, dp = q_imp.shape
-    if w1.shape != (E, F) or w2.shape != (F, Hq * G * dp) or Lq2 != Lq or q_imp.shape[0] != B:
+    if w1.shape != (F, E) or w2.shape != (Hq * G * dp, F) or Lq2 != Lq or q_imp.shape[0] != B:
         raise ValueError("shape mismatch")
     dt = _dtype_code(h)
     args = (dt, _ptr(h), _ptr(w1), _ptr(w2), _ptr(q_imp), B, Lq, E, F, Hq, G, dp, ln_eps)

@@ -64,7 +64,7 @@ const char* butler_status_string(int status) {
   }
 }
 
-int butler_abi_version(void) { return 2; }
+int butler_abi_version(void) { return 3; }
 
 int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
                         void* kimp, int B, int Hkv, int L_cap, int D, int dprime, int pos0,

@@ -1,20 +1,21 @@
 // Producer f_theta at a producer layer (TokenButler model card, Method):
-//   Q_imp = relu(LN(H) . W1) . W2, reshaped to [B, Hq, G, Lq, d'].
-// Steps: (1) LN rows -> bf16 x_hat; (2) GEMM x_hat . W1 split over K into float32
+//   Q_imp = relu(LN(H) . W1^T) . W2^T, reshaped to [B, Hq, G, Lq, d'].
+// The weights come in the [out, in] layout of a PyTorch Linear (W1 [F, E], W2 [N2, F]),
+// K-contiguous like the activations, so both MFMA operands read eight consecutive K
+// values per lane straight from the same kind of LDS tile, and a GEMV reads whole weight
+// rows with 16-byte loads.
+// Steps: (1) LN rows -> bf16 x_hat; (2) GEMM x_hat . W1^T split over K into float32
 // partial sums; (3) fixed-order reduction of the partials + ReLU -> bf16 a;
-// (4) GEMM a . W2; (5) reduction + bf16 store scattered into the Q_imp layout.
+// (4) GEMM a . W2^T; (5) reduction + bf16 store scattered into the Q_imp layout.
 // With one split the epilogue runs inside the GEMM.
 //
 // Two GEMM kernels.  Blocks of rows (prefill: M = B*Lq >= 64) run on the matrix cores:
 // a 128 x 128 tile per workgroup, 64 x 64 per wave as 2 x 2 v_mfma_f32_32x32x16_bf16
 // tiles, K staged through LDS 32 at a time, double-buffered, with a ring of four
-// register stages so three K tiles are in flight from memory.  The MFMA wants eight
-// consecutive K values per lane for both operands; the activations are K-contiguous, the
-// weights [K, N] are N-contiguous, so the weight tile is transposed on its way into LDS:
-// two K rows are packed into one 32-bit word per column.  A few rows (decode: one
-// hidden state per sequence) take the VALU kernel -- 32 rows x 64 columns per workgroup,
-// a thread owns 1 row x 8 columns -- since there the weights stream once from HBM and
-// the matrix cores would idle.  Up to 4 rows take a weight-streaming GEMV instead (below).
+// register stages so three K tiles are in flight from memory.  Other shapes with more
+// than 4 rows take the VALU kernel -- 32 rows x 64 columns per workgroup, a thread owns
+// 1 row x 8 columns.  Up to 4 rows (decode: one hidden state per sequence) take a
+// weight-streaming GEMV instead (below).
 #include "common.h"
 #include "kernels.h"
 
@@ -116,19 +117,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
       const int gm = m0 + ar, gk = kk + ac;
       As[ar][ac] = (gm < M && gk < k1) ? bf2f(A[(long long)gm * K + gk]) : 0.f;
     }
-    // B tile: 32 x 64, 8 elements (16 bytes) per thread
+    // B tile: 32 K x 64 columns from the [N, K] weights, 8 K values (16 bytes) per thread
     {
-      const int br = threadIdx.x / 8, bc = (threadIdx.x % 8) * 8;
-      const int gk = kk + br;
+      const int bn = threadIdx.x / 4, bk = (threadIdx.x % 4) * 8;
+      const int gk = kk + bk;
       float tmp[8];
-      if (gk < k1) {
-        Vec16<bf16_t>::load(Bm + (long long)gk * N + n0 + bc, tmp);
+      if (gk + 8 <= k1) {
+        Vec16<bf16_t>::load(Bm + (long long)(n0 + bn) * K + gk, tmp);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) tmp[j] = 0.f;
+        for (int j = 0; j < 8; ++j)
+          tmp[j] = (gk + j < k1) ? bf2f(Bm[(long long)(n0 + bn) * K + gk + j]) : 0.f;
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) Bs[br][bc + j] = tmp[j];
+      for (int j = 0; j < 8; ++j) Bs[bk + j][bn] = tmp[j];
     }
     __syncthreads();
 #pragma unroll 8
@@ -162,7 +164,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16v_t;
 constexpr int kMM = 128, kMN = 128, kMK = 32;
 constexpr int kMThreads = 256;
 constexpr int kMPf = 4;        // register stages of the K loop (even: LDS buffers alternate)
-constexpr int kAS = kMK + 8;   // LDS row stride in bf16 of the A tile and the transposed B tile
+constexpr int kAS = kMK + 8;   // LDS row stride in bf16 of the A and B tiles
 
 __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm, void* out, int M, int N, int K,
@@ -170,16 +172,16 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
   const int n0 = blockIdx.x * kMN, m0 = blockIdx.y * kMM, split = blockIdx.z;
   const int k0 = split * k_per_split, k1 = min(K, k0 + k_per_split);
   __shared__ __align__(16) bf16_t As[2][kMM * kAS];
-  __shared__ __align__(16) bf16_t Bt[2][kMN * kAS];
+  __shared__ __align__(16) bf16_t Bs[2][kMN * kAS];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  // staging roles: A chunks c = tid, tid + 256 are row c/4, K columns 8*(c%4) .. +8; for B
-  // the thread takes K rows 2p, 2p+1 and columns 8g .. 8g+7 of the tile
-  const int p = tid & 15, g = tid >> 4;
+  // staging roles, the same for both operands: chunks c = tid, tid + 256 are tile row c/4,
+  // K columns 8*(c%4) .. +8
   const int c0 = tid, c1 = tid + kMThreads;
   const bf16_t* a0 = A + (long long)min(m0 + (c0 >> 2), M - 1) * K + (c0 & 3) * 8;
   const bf16_t* a1 = A + (long long)min(m0 + (c1 >> 2), M - 1) * K + (c1 & 3) * 8;  // rows past M: computed, never stored
-  const bf16_t* bp = Bm + (long long)(2 * p) * N + n0 + 8 * g;
+  const bf16_t* b0 = Bm + (long long)(n0 + (c0 >> 2)) * K + (c0 & 3) * 8;
+  const bf16_t* b1 = Bm + (long long)(n0 + (c1 >> 2)) * K + (c1 & 3) * 8;
   const int as0 = (c0 >> 2) * kAS + (c0 & 3) * 8, as1 = (c1 >> 2) * kAS + (c1 & 3) * 8;
   // a ring of kMPf = 4 register stages: tiles t+1 .. t+3 are in flight from memory while
   // tile t is multiplied; every load is unconditional (the ring runs past the last tile on
@@ -190,22 +192,15 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
   do {                                                                           \
     ra0_##st = *reinterpret_cast<const uint4*>(a0 + (kk));                      \
     ra1_##st = *reinterpret_cast<const uint4*>(a1 + (kk));                      \
-    rb0_##st = *reinterpret_cast<const uint4*>(bp + (long long)(kk) * N);       \
-    rb1_##st = *reinterpret_cast<const uint4*>(bp + (long long)(kk) * N + N);   \
+    rb0_##st = *reinterpret_cast<const uint4*>(b0 + (kk));                      \
+    rb1_##st = *reinterpret_cast<const uint4*>(b1 + (kk));                      \
   } while (0)
-  // column 8g+2q gets the low halves of both K rows, column 8g+2q+1 the high halves
-#define BUTLER_PACK(q, x0, x1)                                                   \
-  bw[(8 * g + 2 * (q)) * (kAS / 2) + p] = ((x0) & 0xffffu) | ((x1) << 16);      \
-  bw[(8 * g + 2 * (q) + 1) * (kAS / 2) + p] = ((x0) >> 16) | ((x1) & 0xffff0000u)
 #define BUTLER_LSTORE(st, buf)                                                   \
   do {                                                                           \
     *reinterpret_cast<uint4*>(&As[buf][as0]) = ra0_##st;                        \
     *reinterpret_cast<uint4*>(&As[buf][as1]) = ra1_##st;                        \
-    uint32_t* bw = reinterpret_cast<uint32_t*>(Bt[buf]);                        \
-    BUTLER_PACK(0, rb0_##st.x, rb1_##st.x);                                      \
-    BUTLER_PACK(1, rb0_##st.y, rb1_##st.y);                                      \
-    BUTLER_PACK(2, rb0_##st.z, rb1_##st.z);                                      \
-    BUTLER_PACK(3, rb0_##st.w, rb1_##st.w);                                      \
+    *reinterpret_cast<uint4*>(&Bs[buf][as0]) = rb0_##st;                        \
+    *reinterpret_cast<uint4*>(&Bs[buf][as1]) = rb1_##st;                        \
   } while (0)
   f32x16v_t acc[2][2];
 #pragma unroll
@@ -231,7 +226,7 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
         a[i] = *reinterpret_cast<const bf16x8v_t*>(&As[buf][(wm * 64 + i * 32 + lr) * kAS + ks * 16 + lk]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8v_t*>(&Bt[buf][(wn * 64 + j * 32 + lr) * kAS + ks * 16 + lk]);
+        b[j] = *reinterpret_cast<const bf16x8v_t*>(&Bs[buf][(wn * 64 + j * 32 + lr) * kAS + ks * 16 + lk]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -256,7 +251,6 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
   }
 #undef BUTLER_STEP
 #undef BUTLER_GLOAD
-#undef BUTLER_PACK
 #undef BUTLER_LSTORE
   // accumulator r of tile (i, j): row 8(r/4) + 4(lane/32) + r%4, column lane%32
 #pragma unroll
@@ -333,35 +327,43 @@ hipError_t gemm(hipStream_t st, const bf16_t* A, const bf16_t* Bm, void* out, fl
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // ---------------------------------------------------------------------------
-// decode rows (M <= 4): weight-streaming GEMV in three kernels
+// decode rows (M <= 4): weight-streaming GEMV in two kernels
 // ---------------------------------------------------------------------------
-//   1  every workgroup normalises the M rows itself (LN statistics over E, then the bf16
-//      x_hat of its 64-row K slice), multiplies its slice of W1 (64 K rows x 256 columns,
-//      16-byte loads, all issued first) and writes float32 partial sums per K slice;
-//   2  every workgroup sums the first layer's partials of its K slice in slice order,
-//      applies ReLU and the bf16 rounding, and multiplies its slice of W2 the same way;
-//   3  the second layer's partials are summed in slice order, rounded to bf16 and
-//      scattered into the Q_imp layout.
-// The weights stream from HBM once; everything else is small and stays in L2.
+//   1  every workgroup normalises the M rows itself (LN statistics over E, then bf16
+//      x_hat into LDS) while its weight rows are in flight; a wave owns one row n of W1
+//      (K-contiguous: lane l reads K values 8l + 512j .. +8 with 16-byte loads, all issued
+//      first), dots it with the M rows, reduces across the wave, applies ReLU and writes
+//      the bf16 activation a[m][n];
+//   2  the same for W2 over the activations, the results rounded to bf16 and scattered
+//      into the Q_imp layout.
+// The weights stream from HBM once and no partial sums leave a wave.
 
-constexpr int kGvThreads = 256;
-constexpr int kGvCols = 256;      // columns per workgroup: 32 groups of 8
-constexpr int kGvK = 64;          // K rows per workgroup: 8 per thread row
+constexpr int kGvThreads = 256;     // 4 waves, one weight row each
+constexpr int kGvRows = kGvThreads / 64;
 constexpr int kGvMaxM = 4;
+constexpr int kGvMaxK = 8192;
 
-// x (float, the M rows of this K slice, in LDS) times W[k0 .. k0+64, n0 .. n0+256):
-// float32 partials to part[slice][m][n].
-__device__ __forceinline__ void gemv_slice(const float (*xs)[kGvK], const uint4 (&wv)[kGvK / 8],
-                                           float* __restrict__ part, int M, int N, int n0,
-                                           int slice, float* red) {
-  const int cg = threadIdx.x & 31, kr = threadIdx.x >> 5;
-  float acc[kGvMaxM][8];
+// Loads of weight row n (K-contiguous), NL 16-byte pieces per lane; pieces past K read
+// the row's last piece and are dropped in gv_dot.
+template <int NL>
+__device__ __forceinline__ void gv_load(uint4 (&wv)[NL], const bf16_t* __restrict__ W, int n,
+                                        int K, int lane) {
+  const bf16_t* wr = W + (long long)n * K;
 #pragma unroll
-  for (int m = 0; m < kGvMaxM; ++m)
+  for (int j = 0; j < NL; ++j) wv[j] = *reinterpret_cast<const uint4*>(wr + min(8 * lane + 512 * j, K - 8));
+}
+
+// The M dot products of the held weight row with the bf16 rows xs[m][0..K) in LDS, summed
+// across the wave (every lane gets the sums).
+template <int NL>
+__device__ __forceinline__ void gv_dot(const uint4 (&wv)[NL], const bf16_t* xs, int M, int K,
+                                       int lane, float (&acc)[kGvMaxM]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
+  for (int m = 0; m < kGvMaxM; ++m) acc[m] = 0.f;
 #pragma unroll
-  for (int j = 0; j < kGvK / 8; ++j) {
+  for (int j = 0; j < NL; ++j) {
+    const int k = 8 * lane + 512 * j;
+    if (k >= K) continue;
     Raw16 r;
     r.v = wv[j];
     float wf[8];
@@ -369,41 +371,35 @@ __device__ __forceinline__ void gemv_slice(const float (*xs)[kGvK], const uint4 
 #pragma unroll
     for (int m = 0; m < kGvMaxM; ++m) {
       if (m >= M) break;
-      const float x = xs[m][kr + 8 * j];
+      Raw16 xr;
+      xr.v = *reinterpret_cast<const uint4*>(xs + m * K + k);
+      float xf[8];
+      unpack16<bf16_t>(xr, xf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[m][e] = fmaf(x, wf[e], acc[m][e]);
+      for (int e = 0; e < 8; ++e) acc[m] = fmaf(xf[e], wf[e], acc[m]);
     }
   }
-  // the 8 thread rows meet in LDS, summed in row order
-  for (int m = 0; m < M; ++m) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[kr * kGvCols + cg * 8 + e] = acc[m][e];
-    __syncthreads();
-    float s = 0.f;
+  for (int m = 0; m < kGvMaxM; ++m)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) s += red[q * kGvCols + threadIdx.x];
-    part[((long long)slice * M + m) * N + n0 + threadIdx.x] = s;
-    __syncthreads();
-  }
+    for (int o = 32; o > 0; o >>= 1) acc[m] += __shfl_xor(acc[m], o, 64);
 }
 
+template <int NL>
 __global__ __launch_bounds__(kGvThreads) void gemv_ln_w1_kernel(const bf16_t* __restrict__ h,
                                                                  const bf16_t* __restrict__ W,
-                                                                 float* __restrict__ part, int M,
+                                                                 bf16_t* __restrict__ act, int M,
                                                                  int K, int N, float eps) {
-  const int n0 = blockIdx.x * kGvCols, slice = blockIdx.y, k0 = slice * kGvK;
-  const int cg = threadIdx.x & 31, kr = threadIdx.x >> 5;
-  uint4 wv[kGvK / 8];
-#pragma unroll
-  for (int j = 0; j < kGvK / 8; ++j)
-    wv[j] = *reinterpret_cast<const uint4*>(W + (long long)(k0 + kr + 8 * j) * N + n0 + 8 * cg);
-  __shared__ float xs[kGvMaxM][kGvK];
-  __shared__ float red[8 * kGvCols];
+  extern __shared__ __align__(16) bf16_t xs[];   // [M][K]
   __shared__ float tmp[kGvThreads / 64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n = min(blockIdx.x * kGvRows + wid, N - 1);
+  uint4 wv[NL];
+  gv_load<NL>(wv, W, n, K, lane);
   for (int m = 0; m < M; ++m) {
     // the row is held in registers: 16-byte pieces, all requested before the reductions
     const bf16_t* hr = h + (long long)m * K;
-    constexpr int kPieces = 4;   // rows up to 256 * 8 * 4 = 8192 elements
+    constexpr int kPieces = kGvMaxK / (kGvThreads * 8);
     float hv[kPieces][8];
 #pragma unroll
     for (int u = 0; u < kPieces; ++u) {
@@ -432,70 +428,70 @@ __global__ __launch_bounds__(kGvThreads) void gemv_ln_w1_kernel(const bf16_t* __
       }
     }
     const float rstd = 1.0f / sqrtf(block_sum_f<kGvThreads>(v, tmp) / (float)K + eps);
-    if (threadIdx.x < kGvK) xs[m][threadIdx.x] = bf2f(f2bf((bf2f(hr[k0 + threadIdx.x]) - mean) * rstd));
-  }
-  __syncthreads();
-  gemv_slice(xs, wv, part, M, N, n0, slice, red);
-}
-
-__global__ __launch_bounds__(kGvThreads) void gemv_relu_w2_kernel(const float* __restrict__ part1,
-                                                                   int nslice1,
-                                                                   const bf16_t* __restrict__ W,
-                                                                   float* __restrict__ part, int M,
-                                                                   int K, int N) {
-  const int n0 = blockIdx.x * kGvCols, slice = blockIdx.y, k0 = slice * kGvK;
-  const int cg = threadIdx.x & 31, kr = threadIdx.x >> 5;
-  uint4 wv[kGvK / 8];
 #pragma unroll
-  for (int j = 0; j < kGvK / 8; ++j)
-    wv[j] = *reinterpret_cast<const uint4*>(W + (long long)(k0 + kr + 8 * j) * N + n0 + 8 * cg);
-  __shared__ float xs[kGvMaxM][kGvK];
-  __shared__ float red[8 * kGvCols];
-  // first-layer activations of this K slice: partials summed in slice order, ReLU, bf16
-  const int m = threadIdx.x / kGvK, kk = threadIdx.x % kGvK;
-  if (m < M) {
-    float a = 0.f;
-    for (int s0 = 0; s0 < nslice1; s0 += 16) {
-      float pv[16];   // sixteen slices requested at once, summed in slice order
+    for (int u = 0; u < kPieces; ++u) {
+      const int e0 = (threadIdx.x + kGvThreads * u) * 8;
+      if (e0 >= K) continue;
+      uint4 o;
+      uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        pv[u] = part1[((long long)min(s0 + u, nslice1 - 1) * M + m) * K + k0 + kk];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) a += (s0 + u < nslice1) ? pv[u] : 0.f;
+      for (int e = 0; e < 4; ++e)
+        ow[e] = (uint32_t)f2bf((hv[u][2 * e] - mean) * rstd) |
+                ((uint32_t)f2bf((hv[u][2 * e + 1] - mean) * rstd) << 16);
+      *reinterpret_cast<uint4*>(xs + m * K + e0) = o;
     }
-    xs[m][kk] = bf2f(f2bf(fmaxf(a, 0.f)));
   }
   __syncthreads();
-  gemv_slice(xs, wv, part, M, N, n0, slice, red);
+  float acc[kGvMaxM];
+  gv_dot<NL>(wv, xs, M, K, lane, acc);
+  const int nn = blockIdx.x * kGvRows + wid;
+  if (lane < M && nn < N) {
+    float a = acc[0];
+#pragma unroll
+    for (int m = 1; m < kGvMaxM; ++m) a = (lane == m) ? acc[m] : a;
+    act[(long long)lane * N + nn] = f2bf(fmaxf(a, 0.f));
+  }
 }
 
-__global__ void gemv_out_kernel(const float* __restrict__ part2, int nslice2, bf16_t* q_imp,
-                                int M, int N, Epilogue ep) {
-  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (long long)M * N) return;
-  const int m = (int)(e / N), n = (int)(e % N);
-  float a = 0.f;
-  for (int s0 = 0; s0 < nslice2; s0 += 16) {
-    float pv[16];
+template <int NL>
+__global__ __launch_bounds__(kGvThreads) void gemv_w2_kernel(const bf16_t* __restrict__ act,
+                                                             const bf16_t* __restrict__ W,
+                                                             bf16_t* q_imp, int M, int K, int N,
+                                                             Epilogue ep) {
+  extern __shared__ __align__(16) bf16_t xs[];   // [M][K]
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n = min(blockIdx.x * kGvRows + wid, N - 1);
+  uint4 wv[NL];
+  gv_load<NL>(wv, W, n, K, lane);
+  for (int e0 = threadIdx.x * 8; e0 < M * K; e0 += kGvThreads * 8)
+    *reinterpret_cast<uint4*>(xs + e0) = *reinterpret_cast<const uint4*>(act + e0);
+  __syncthreads();
+  float acc[kGvMaxM];
+  gv_dot<NL>(wv, xs, M, K, lane, acc);
+  const int nn = blockIdx.x * kGvRows + wid;
+  if (lane < M && nn < N) {
+    float a = acc[0];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) pv[u] = part2[((long long)min(s0 + u, nslice2 - 1) * M + m) * N + n];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) a += (s0 + u < nslice2) ? pv[u] : 0.f;
+    for (int m = 1; m < kGvMaxM; ++m) a = (lane == m) ? acc[m] : a;
+    store_out(ep, q_imp, M, N, lane, nn, a);
   }
-  store_out(ep, q_imp, M, N, m, n, a);
 }
 
 bool use_gemv(int M, int E, int F, int N2) {
-  return M <= kGvMaxM && E <= kGvThreads * 8 * 4 && E % 8 == 0 && E % kGvK == 0 && F % kGvK == 0 && F % kGvCols == 0 &&
-         N2 % kGvCols == 0;
+  (void)N2;
+  return M <= kGvMaxM && E <= kGvMaxK && F <= kGvMaxK && E % 8 == 0 && F % 8 == 0;
 }
 
+// 16-byte pieces per lane for a row of K elements, rounded up to a launched instance
+int gv_loads(int K) {
+  const int nl = (K + 511) / 512;
+  return nl <= 2 ? 2 : nl <= 4 ? 4 : nl <= 8 ? 8 : 16;
+}
 
 }  // namespace
 
 size_t produce_workspace(int M, int E, int F, int N2) {
-  if (use_gemv(M, E, F, N2))
-    return align256((size_t)(E / kGvK) * M * F * 4) + align256((size_t)(F / kGvK) * M * N2 * 4);
+  if (use_gemv(M, E, F, N2)) return align256((size_t)M * F * 2);
   const size_t xs = align256((size_t)M * E * 2);
   const size_t as = align256((size_t)M * F * 2);
   const size_t p1 = (size_t)splits_for(M, F, E) * M * F * 4;
@@ -510,16 +506,29 @@ hipError_t launch_produce(hipStream_t s, const void* h, const void* w1, const vo
                           float eps, void* ws) {
   const int M = B * Lq, N2 = Hq * G * dp;
   if (use_gemv(M, E, F, N2)) {
-    float* p1 = (float*)ws;
-    float* p2 = (float*)((char*)ws + align256((size_t)(E / kGvK) * M * F * 4));
-    hipLaunchKernelGGL(gemv_ln_w1_kernel, dim3(F / kGvCols, E / kGvK), dim3(kGvThreads), 0, s,
-                       (const bf16_t*)h, (const bf16_t*)w1, p1, M, E, F, eps);
-    hipLaunchKernelGGL(gemv_relu_w2_kernel, dim3(N2 / kGvCols, F / kGvK), dim3(kGvThreads), 0, s,
-                       (const float*)p1, E / kGvK, (const bf16_t*)w2, p2, M, F, N2);
-    const long long tot = (long long)M * N2;
-    hipLaunchKernelGGL(gemv_out_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s,
-                       (const float*)p2, F / kGvK, (bf16_t*)q_imp, M, N2,
-                       Epilogue{2, Lq, Hq, G, dp});
+    bf16_t* act = (bf16_t*)ws;
+    const Epilogue e2{2, Lq, Hq, G, dp};
+#define BUTLER_GV1(NL)                                                                       \
+  hipLaunchKernelGGL(gemv_ln_w1_kernel<NL>, dim3((F + kGvRows - 1) / kGvRows), dim3(kGvThreads), \
+                     (size_t)M * E * 2, s, (const bf16_t*)h, (const bf16_t*)w1, act, M, E, F, eps)
+#define BUTLER_GV2(NL)                                                                       \
+  hipLaunchKernelGGL(gemv_w2_kernel<NL>, dim3((N2 + kGvRows - 1) / kGvRows), dim3(kGvThreads), \
+                     (size_t)M * F * 2, s, (const bf16_t*)act, (const bf16_t*)w2, (bf16_t*)q_imp, M, F, \
+                     N2, e2)
+    switch (gv_loads(E)) {
+      case 2: BUTLER_GV1(2); break;
+      case 4: BUTLER_GV1(4); break;
+      case 8: BUTLER_GV1(8); break;
+      default: BUTLER_GV1(16); break;
+    }
+    switch (gv_loads(F)) {
+      case 2: BUTLER_GV2(2); break;
+      case 4: BUTLER_GV2(4); break;
+      case 8: BUTLER_GV2(8); break;
+      default: BUTLER_GV2(16); break;
+    }
+#undef BUTLER_GV1
+#undef BUTLER_GV2
     return hipGetLastError();
   }
   bf16_t* xhat = (bf16_t*)ws;

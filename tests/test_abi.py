@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert qa.butler_abi_version() == 2
+    assert qa.butler_abi_version() == 3
     assert qa.butler_status_string(0) == "BUTLER_OK"
     assert qa.butler_status_string(-3) == "BUTLER_ERR_WORKSPACE"
     assert qa.butler_status_string(123) == "BUTLER_ERR_UNKNOWN"
@@ -106,7 +106,10 @@ def test_produce_validation_and_workspace_query():
     n = ctypes.c_size_t(0)
     assert f(None, 1, FAKE, FAKE, FAKE, FAKE, 1, 1, 4096, 1024, 32, 4, 32, 1e-5, None,
              ctypes.byref(n)) == OK
-    assert n.value >= 4096 * 2 + 1024 * 2
+    assert n.value >= 1024 * 2                        # one decode row: the hidden activation
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, 2, 1024, 4096, 1024, 32, 4, 32, 1e-5, None,
+             ctypes.byref(n)) == OK
+    assert n.value >= 2048 * (4096 + 1024) * 2        # prefill rows: x_hat and activations
     assert f(None, 0, FAKE, FAKE, FAKE, FAKE, 1, 1, 4096, 1024, 32, 4, 32, 1e-5, None,
              ctypes.byref(n)) == UNS                                        # fp32 producer
     assert f(None, 1, FAKE, FAKE, FAKE, FAKE, 1, 1, 4000, 1024, 32, 4, 32, 1e-5, None,

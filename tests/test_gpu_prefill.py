@@ -33,7 +33,9 @@ def _producer_case(w, rows, layer):
     h = synthetic.producer_hidden(w, layer, rows)
     wts = synthetic.producer_weights(w, layer)
     q_imp = torch.empty(w.B, w.Hq, w.G, rows, w.dprime, dtype=torch.bfloat16, device="cuda")
-    qa.butler_produce_queries(h.cuda(), wts["w1"].cuda(), wts["w2"].cuda(), q_imp)
+    # the library takes the weights in the [out, in] layout of a PyTorch Linear
+    qa.butler_produce_queries(h.cuda(), wts["w1"].t().contiguous().cuda(),
+                              wts["w2"].t().contiguous().cuda(), q_imp)
     torch.cuda.synchronize()
     want = oracle.produce_queries(np64(h), np64(wts["w1"]), np64(wts["w2"]), w.Hq, w.G,
                                   w.dprime, 1e-5)
@@ -49,6 +51,20 @@ def _producer_case(w, rows, layer):
 def test_producer_decode_row():
     w = synthetic.WORKLOADS[4]
     _producer_case(w, 1, layer=4)
+
+
+@pytest.mark.parametrize("B,E,F", [(4, 4096, 1024), (3, 576, 320), (2, 8192, 512)])
+def test_producer_decode_rows_gemv_shapes(B, E, F):
+    """Up to four decode rows take the GEMV: the largest batch, a ragged small shape (K not
+    a multiple of 512) and the longest hidden row."""
+    w = synthetic.WORKLOADS[4].replace(B=B, E=E, F=F)
+    _producer_case(w, 1, layer=2)
+
+
+def test_producer_few_rows_valu_gemm():
+    """13 rows: more than the GEMV takes, fewer than the matrix-core tiles want."""
+    w = synthetic.WORKLOADS[5].replace(B=1)
+    _producer_case(w, 13, layer=3)
 
 
 def test_producer_prefill_rows():
@@ -68,7 +84,8 @@ def _prefill_case(w, L, chunk):
     inp = synthetic.prefill_inputs(w, L=L)
     dev = "cuda"
     q_imp = torch.empty(w.B, w.Hq, w.G, L, w.dprime, dtype=torch.bfloat16, device=dev)
-    qa.butler_produce_queries(inp["h"].cuda(), inp["w1"].cuda(), inp["w2"].cuda(), q_imp)
+    qa.butler_produce_queries(inp["h"].cuda(), inp["w1"].t().contiguous().cuda(),
+                              inp["w2"].t().contiguous().cuda(), q_imp)
     k_d, v_d, q_d = inp["k_cache"].cuda(), inp["v_cache"].cuda(), inp["q"].cuda()
     kimp = torch.empty(w.B, w.Hkv, L, w.dprime, dtype=torch.bfloat16, device=dev)
     qa.butler_project_keys(k_d, inp["w_k"].cuda(), kimp, 0, L)
