@@ -84,17 +84,19 @@ class Layer:
             ("project+score", lambda: qa.butler_project_and_score(
                 self.qi, self.k, self.wk, self.kimp, self.scores, Hkv=w.Hkv, L=L,
                 radix_hist=self.hist)),
-            ("select", lambda: qa.butler_select_topk(self.scores, w.budget_num, w.budget_den,
-                                                     w.n_sink, w.n_window, self.count,
-                                                     idx=self.idx, radix_hist=self.hist)),
-            ("attn", lambda: qa.butler_sparse_decode_attn(self.q, self.k, self.v, self.out,
-                                                          L=L, idx=self.idx, count=self.count,
-                                                          softmax_scale=w.scale)),
+            # selection and attention in one call: the selection's finishing pass attends to
+            # its own chunk of the row, a merge kernel combines the chunks
+            ("select+attend", lambda: qa.butler_select_attend(
+                self.scores, w.budget_num, w.budget_den, w.n_sink, w.n_window, self.count,
+                self.idx, self.q, self.k, self.v, self.out, L=L, softmax_scale=w.scale,
+                radix_hist=self.hist)),
         ]
 
     def algorithmic_bytes(self):
         """Bytes a step must move: the K_imp stream, the new key row and its K_imp row,
-        the selected K and V rows, the index list written and read back, q and out."""
+        the selected K and V rows, the index list written and read back, q and out.  The
+        select+attend call's share: the scores read once, the selected K and V rows, the
+        index list written, q and out."""
         w = self.w
         n_sel = int(self.count.sum().item())
         elt = 2 if w.dtype.itemsize == 2 else 4
@@ -103,8 +105,8 @@ class Layer:
         gather = n_sel * 2 * w.D * elt
         idx = n_sel * 4 * 2
         qo = w.B * w.Hq * w.D * (elt + 4)
-        attn = gather + n_sel * 4 + qo
-        return {"step": kimp + proj + gather + idx + qo, "attn": attn, "n_sel": n_sel}
+        call = w.B * w.Hkv * self.L * 4 + gather + n_sel * 4 + qo
+        return {"step": kimp + proj + gather + idx + qo, "call": call, "n_sel": n_sel}
 
 
 def run_config(w, L, replicas, steps, warmup, device):
@@ -116,36 +118,18 @@ def run_config(w, L, replicas, steps, warmup, device):
             fn()
     torch.cuda.synchronize()
 
-    names = [n for n, _ in layers[0].calls()]
-
-    def capture(nsteps, with_events):
+    def graph_of(nsteps, members):
         g = torch.cuda.CUDAGraph()
-        evs = []
         with torch.cuda.graph(g):
-            for s in range(nsteps):
-                lay = layers[s % replicas]
-                for name, fn in lay.calls():
-                    if with_events:
-                        e0 = torch.cuda.Event(enable_timing=True, external=True)
-                        e1 = torch.cuda.Event(enable_timing=True, external=True)
-                        e0.record()
-                        fn()
-                        e1.record()
-                        evs.append((name, e0, e1))
-                    else:
-                        fn()
-        return g, evs
+            for st in range(nsteps):
+                calls = dict(layers[st % replicas].calls())
+                for m in members:
+                    calls[m]()
+        return g
 
-    method = "graph-events"
-    try:
-        g_warm, _ = capture(max(warmup, 1), False)
-        g_timed, evs = capture(steps, True)
-    except Exception as exc:  # event nodes not capturable: time kernels by further graphs
-        log(f"  external events in capture failed ({exc}); timing kernels per graph")
-        method = "per-call-graphs"
-        g_warm, _ = capture(max(warmup, 1), False)
-        g_timed, evs = capture(steps, False)
-
+    names = [n for n, _ in layers[0].calls()]
+    g_warm = graph_of(max(warmup, 1), names)
+    g_timed = graph_of(steps, names)
     g_warm.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -155,52 +139,56 @@ def run_config(w, L, replicas, steps, warmup, device):
     elapsed = t1 - t0
     ab = [lay.algorithmic_bytes() for lay in layers]   # counts of the last timed steps
 
-    per_kernel = {}
-    if method == "graph-events":
-        for name, e0, e1 in evs:
-            per_kernel.setdefault(name, []).append(e0.elapsed_time(e1) * 1e3)   # us
-    else:
-        # Events around a graph of `steps` back-to-back calls of one kind.  The scorer and
-        # the selection share the first-digit histogram (the scorer fills it, the selection
-        # empties it), so they are timed together as one pair.
-        groups = {"project+score+select": ["project+score", "select"], "attn": ["attn"]}
-        for gname, members in groups.items():
-            gk = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gk):
-                for s in range(steps):
-                    calls = dict(layers[s % replicas].calls())
-                    for m in members:
-                        calls[m]()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            gk.replay()
-            b.record()
-            torch.cuda.synchronize()
-            per_kernel[gname] = [a.elapsed_time(b) * 1e3 / steps]
-    avg_us = {k: sum(v) / len(v) for k, v in per_kernel.items()}
+    # Per-call times on the launch stream: events around the timed graph, and around a graph
+    # of the scoring call alone (events cannot be captured inside a graph on ROCm).  The
+    # scorer fills the first-digit histogram that select+attend empties, so select+attend
+    # is timed as the step minus the scoring call; the histograms are cleared afterwards.
+    def ev_time(g):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+    step_us = ev_time(g_timed)
+    score_us = ev_time(graph_of(steps, ["project+score"]))
+    for lay in layers:
+        lay.hist.zero_()
+    torch.cuda.synchronize()
+    avg_us = {"project+score": score_us, "select+attend": step_us - score_us, "step": step_us}
     step_bytes = sum(a["step"] for a in ab) / len(ab)
-    attn_bytes = sum(a["attn"] for a in ab) / len(ab)
+    call_bytes = sum(a["call"] for a in ab) / len(ab)
     n_sel = sum(a["n_sel"] for a in ab) / len(ab)
     ms = elapsed * 1e3 / steps
     return {
         "L": L, "replicas": replicas, "steps": steps, "ms_per_step": ms,
-        "steps_per_s": steps / elapsed, "timing": method,
+        "steps_per_s": steps / elapsed, "timing": "graph events, select+attend = step - score",
         "kernel_us": {k: round(v, 3) for k, v in avg_us.items()},
-        "step_bytes": step_bytes, "attn_bytes": attn_bytes, "selected_per_step": n_sel,
+        "step_bytes": step_bytes, "call_bytes": call_bytes, "selected_per_step": n_sel,
         "step_GBps": step_bytes / (ms * 1e-3) / 1e9,
-        "attn_GBps": attn_bytes / (avg_us["attn"] * 1e-6) / 1e9,
+        "call_GBps": call_bytes / (avg_us["select+attend"] * 1e-6) / 1e9,
     }, layers
 
 
-def traffic_record(kernel_file: str, name: str):
-    """rocprof FETCH_SIZE + WRITE_SIZE per launch recorded for the current source of the
-    kernel, scaled by the copy-kernel calibration; None when absent or stale."""
+# sources of the kernels in the roofline call (their digest keys the traffic record)
+TRAFFIC_SOURCES = ("select.hip", "attn.hip", "attn_tile.h", "common.h")
+
+
+def sources_sha256(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "query_aware_sparse_imp_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_record(kernel_files, name: str):
+    """rocprof FETCH_SIZE + WRITE_SIZE per launch recorded for the current sources of the
+    kernels, scaled by the copy-kernel calibration; None when absent or stale."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "query_aware_sparse_imp_amd", "csrc", kernel_file), "rb").read()
-    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("source_sha256") != sources_sha256(kernel_files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -443,8 +431,7 @@ def run_full_depth(steps, device):
     cnt = torch.empty(w.B, w.Hkv, 1, dtype=torch.int32, device=device)
     out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
     fns = []
-    groups = {"produce": [], "project": [], "dense layer 0": [], "project+score+select": [],
-              "attn": []}
+    groups = {"produce": [], "dense layer 0": [], "consumer layers": []}
 
     def add(group, *fs):
         fns.extend(fs)
@@ -453,30 +440,24 @@ def run_full_depth(steps, device):
         if l % w.G == 0:
             add("produce", lambda d=d: qa.butler_produce_queries(d["h"], d["w1"], d["w2"], d["qimp"]))
         if l == 0:   # dense layer: the budget takes every token
-            add("project", lambda d=d: qa.butler_project_keys(d["k"], d["wk"], d["kimp"],
-                                                               L - 1, 1))
             add("dense layer 0",
-                lambda: qa.butler_select_topk(scores, 1, 1, w.n_sink, w.n_window, cnt,
-                                              idx=idx_dense),
-                lambda d=d: qa.butler_sparse_decode_attn(d["q"], d["k"], d["v"], out, L=L,
-                                                         idx=idx_dense, count=cnt,
-                                                         softmax_scale=w.scale))
+                lambda d=d: qa.butler_project_keys(d["k"], d["wk"], d["kimp"], L - 1, 1),
+                lambda d=d: qa.butler_select_attend(scores, 1, 1, w.n_sink, w.n_window, cnt,
+                                                    idx_dense, d["q"], d["k"], d["v"], out,
+                                                    L=L, softmax_scale=w.scale))
             continue
         prod = lay[w.G * (l // w.G)]
         slot = (l - 1) % w.G
-        add("project+score+select",
+        add("consumer layers",
             lambda d=d, prod=prod, slot=slot: qa.butler_project_and_score(
                 prod["qimp"], d["k"], d["wk"], d["kimp"], scores, Hkv=w.Hkv, L=L, slot=slot,
                 radix_hist=hist),
-            lambda: qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink,
-                                          w.n_window, cnt, idx=idx, radix_hist=hist))
-        add("attn", lambda d=d: qa.butler_sparse_decode_attn(d["q"], d["k"], d["v"], out, L=L,
-                                                             idx=idx, count=cnt,
-                                                             softmax_scale=w.scale))
+            lambda d=d: qa.butler_select_attend(scores, w.budget_num, w.budget_den, w.n_sink,
+                                                w.n_window, cnt, idx, d["q"], d["k"], d["v"],
+                                                out, L=L, softmax_scale=w.scale,
+                                                radix_hist=hist))
     sec = graph_time(fns, steps)
-    phase = {name: graph_time(fs, 1) * 1e6 for name, fs in groups.items() if name != "attn"}
-    # the consumer attention reads the last consumer layer's index list in this timing
-    phase["attn"] = graph_time(groups["attn"], 1) * 1e6
+    phase = {name: graph_time(fs, 1) * 1e6 for name, fs in groups.items()}
     n_sel = int(cnt.sum())              # last consumer layer's selection
     elt = 2
     consumer = w.B * w.Hkv * (L * w.dprime * elt + n_sel // w.Hkv * (2 * w.D * elt + 8))
@@ -607,7 +588,7 @@ def main(argv=None) -> int:
             log(f"[bench] sweep L={Ls}")
             r, layers = run_config(w, Ls, 2, max(a.steps // 4, 20), max(a.warmup // 4, 4), dev)
             sweep.append({k: r[k] for k in ("L", "steps_per_s", "ms_per_step", "step_GBps",
-                                            "attn_GBps", "kernel_us", "timing")})
+                                            "call_GBps", "kernel_us", "timing")})
             sweep[-1]["step_frac_of_hbm_peak"] = r["step_GBps"] / HBM_PEAK_GBS
             log(f"[bench] sweep result: {json.dumps(sweep[-1])}")
         for lay in layers:
@@ -635,9 +616,9 @@ def main(argv=None) -> int:
         cpu = cpu_baseline(host0)
         log(f"[bench] cpu baseline: {json.dumps(cpu)}")
 
-    attn_us = head["kernel_us"]["attn"]
-    achieved = head["attn_bytes"] / (attn_us * 1e-6) / 1e9
-    traffic = traffic_record("attn.hip", "attn_decode_L32768")
+    call_us = head["kernel_us"]["select+attend"]
+    achieved = head["call_bytes"] / (call_us * 1e-6) / 1e9
+    traffic = traffic_record(TRAFFIC_SOURCES, "select_attend_decode_L32768")
     line = {
         "metric": METRIC,
         "value": head["steps_per_s"],
@@ -656,11 +637,13 @@ def main(argv=None) -> int:
                    "L": L, "scorer": "raw", "budget": f"{w.budget_num}/{w.budget_den}",
                    "sink": w.n_sink, "window": w.n_window, "layer_replicas": 8,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "sparse decode attention call: attn_mfma_kernel + attn_merge_kernel",
+        "roofline": {"bound": "hbm",
+                     "kernel": "select+attend call: mb_cand_kernel, mb_finish_kernel (the "
+                               "finishing pass attends to its chunk), attn_merge_kernel",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": head["attn_bytes"],
-                     "avg_launch_us": attn_us, "timing": head["timing"]},
+                     "algorithmic_bytes_per_launch": head["call_bytes"],
+                     "avg_launch_us": call_us, "timing": head["timing"]},
         "step_hbm": {"algorithmic_bytes": head["step_bytes"], "GB/s": head["step_GBps"],
                      "frac": head["step_GBps"] / HBM_PEAK_GBS},
         "kernel_us": head["kernel_us"],

@@ -235,6 +235,29 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
                               float softmax_scale, void* workspace, size_t* ws_bytes);
 
 /*
+ * butler_select_attend -- one decode step's selection and sparse attention in one call:
+ * the same results as butler_select_topk (Lq = 1, non-causal, idx output, no keep flags)
+ * followed by butler_sparse_decode_attn over that idx / count, with the same arguments.
+ * Model card, Method: the step keeps the top-x tokens plus sink and window, then attends
+ * only to them.  For bf16, D = 128 and rows longer than 4096 tokens the selection's
+ * finishing pass attends to its own chunk of the row while the chunk's indices are still
+ * on chip, and a merge kernel combines the chunks; other shapes run the two calls' kernels.
+ * The attention output equals the separate calls' up to float32 rounding order; idx and
+ * count are identical.
+ *
+ *   scores [B, Hkv, 1, L] float32, radix_hist [B, Hkv, 1, 2048] optional (as in
+ *   butler_select_topk), idx [B, Hkv, 1, cap] int32 and count [B, Hkv, 1] int32 (written),
+ *   q [B, Hq, 1, D], k_cache / v_cache [B, Hkv, L_cap, D] (dtype), out [B, Hq, 1, D] float32.
+ * Limits as in the two calls; L <= 2^23.  workspace: the selection's state and candidate
+ * ring, and one softmax partial per chunk (or the two calls' workspaces).
+ */
+int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t* radix_hist,
+                         int budget_num, int budget_den, int n_sink, int n_window, int32_t* idx,
+                         int32_t* count, const void* q, const void* k_cache, const void* v_cache,
+                         float* out, int B, int Hq, int Hkv, int D, int L, int L_cap, int cap,
+                         float softmax_scale, void* workspace, size_t* ws_bytes);
+
+/*
  * butler_selection_cache -- TokenSelect README, highlights, Selection Cache: consecutive
  * similar queries share one token selection, so selection runs less often.  For every
  * (b, KV head) of a decode step, the cosine similarity between the group's current query

@@ -20,7 +20,8 @@ __all__ = [
     "BUTLER_OK", "BUTLER_SCORE_RAW", "BUTLER_SCORE_SOFTVOTE", "ButlerError", "lib", "LIB_PATH",
     "butler_project_keys", "butler_produce_queries", "butler_score", "butler_project_and_score",
     "butler_select_topk",
-    "butler_sparse_decode_attn", "butler_selection_cache", "butler_expand_neighbors",
+    "butler_sparse_decode_attn", "butler_select_attend", "butler_selection_cache",
+    "butler_expand_neighbors",
     "butler_status_string",
     "butler_abi_version", "declared_symbols", "workspace_bytes",
 ]
@@ -50,6 +51,8 @@ _SIGS = {
     "butler_select_topk": ([_vp, _vp, _vp, _vp] + [_i] * 4 + [_vp, _vp, _vp] + [_i] * 7 +
                            [_vp, _sz], _i),
     "butler_selection_cache": ([_vp, _i, _vp, _vp, _vp] + [_i] * 4 + [_f], _i),
+    "butler_select_attend": ([_vp, _i, _vp, _vp] + [_i] * 4 + [_vp] * 6 + [_i] * 7 +
+                             [_f, _vp, _sz], _i),
     "butler_expand_neighbors": ([_vp] * 5 + [_i] * 7, _i),
     "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 9 + [_f, _vp, _sz], _i),
 }
@@ -294,6 +297,36 @@ def butler_sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     ws, n = _workspace("attn", need, q.device, tuple(args[8:]))
     _check("butler_sparse_decode_attn",
            lib.butler_sparse_decode_attn(_stream(stream), *args, ws, _byref(n)))
+
+
+def butler_select_attend(scores: torch.Tensor, budget_num: int, budget_den: int, n_sink: int,
+                         n_window: int, count: torch.Tensor, idx: torch.Tensor, q: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, out: torch.Tensor, *,
+                         L: int, softmax_scale: float,
+                         radix_hist: Optional[torch.Tensor] = None, stream=None) -> None:
+    """butler_select_topk then butler_sparse_decode_attn for one decode step (see butler.h).
+    scores [B, Hkv, 1, L]; idx [B, Hkv, 1, cap], count [B, Hkv, 1] (written);
+    q [B, Hq, 1, D]; caches [B, Hkv, L_cap, D]; out [B, Hq, 1, D] float32."""
+    B, Hkv, Lq, Ls = scores.shape
+    Bq, Hq, Lq2, D = q.shape
+    Bk, Hk, L_cap, D2 = k_cache.shape
+    if Lq != 1 or Lq2 != 1 or Ls != L or (Bq, Bk, Hk, D2) != (B, B, Hkv, D):
+        raise ValueError("shape mismatch")
+    if v_cache.shape != k_cache.shape or out.shape != (B, Hq, 1, D):
+        raise ValueError("shape mismatch")
+    if idx.shape[:3] != (B, Hkv, 1) or count.shape != (B, Hkv, 1):
+        raise ValueError("idx [B, Hkv, 1, cap] and count [B, Hkv, 1] required")
+    if scores.dtype != torch.float32 or out.dtype != torch.float32 or \
+            not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    _check_hist(radix_hist, (B, Hkv, 1))
+    args = (_dtype_code(q), _ptr(scores), _ptr(radix_hist), budget_num, budget_den, n_sink,
+            n_window, _ptr(idx), _ptr(count), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+            B, Hq, Hkv, D, L, L_cap, idx.shape[3], float(softmax_scale))
+    need = workspace_bytes(lambda ws, n: lib.butler_select_attend(_stream(stream), *args, ws, n))
+    ws, n = _workspace("select_attend", need, q.device, tuple(args[3:7]) + tuple(args[13:]))
+    _check("butler_select_attend",
+           lib.butler_select_attend(_stream(stream), *args, ws, _byref(n)))
 
 
 def butler_selection_cache(q: torch.Tensor, q_ref: torch.Tensor, keep: torch.Tensor, *,

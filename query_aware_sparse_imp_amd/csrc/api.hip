@@ -233,6 +233,50 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
                                        D, Lq, L, L_cap, q_pos0, softmax_scale, workspace));
 }
 
+int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t* radix_hist,
+                         int budget_num, int budget_den, int n_sink, int n_window, int32_t* idx,
+                         int32_t* count, const void* q, const void* k_cache, const void* v_cache,
+                         float* out, int B, int Hq, int Hkv, int D, int L, int L_cap, int cap,
+                         float softmax_scale, void* workspace, size_t* ws_bytes) {
+  if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || L_cap < L) return BUTLER_ERR_INVALID_ARG;
+  if (budget_num < 0 || budget_den <= 0 || n_sink < 0 || n_window < 0) return BUTLER_ERR_INVALID_ARG;
+  if (Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
+  if (!pow2_group(Hq / Hkv) || !(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.f)) return BUTLER_ERR_INVALID_ARG;
+  const long long rows = (long long)B * Hkv;
+  if (rows > 0x7fffffffLL || L > 8388608) return BUTLER_ERR_UNSUPPORTED;
+  {
+    const long long x = (long long)L * budget_num / budget_den;
+    long long need_cap = x + n_sink + n_window;
+    if (need_cap > L) need_cap = L;
+    if (cap < need_cap) return BUTLER_ERR_INVALID_ARG;
+  }
+  if (rows * ((cap + 255) / 256) > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
+  const bool fused = select_attend_fusable(dtype, D, Hq, Hkv, L);
+  // unfused: the selection's workspace, then the attention's
+  const size_t sel_ws = (select_workspace((int)rows, L, 1, 0) + 255) / 256 * 256;
+  const size_t need = fused ? select_attend_workspace((int)rows, Hq, Hkv, L)
+                            : sel_ws + attn_workspace(dtype, B, Hq, Hkv, D, 1, L, cap);
+  int rc;
+  if (workspace_phase(workspace, ws_bytes, need, &rc)) return rc;
+  if (!scores || !idx || !count || !q || !k_cache || !v_cache || !out) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(scores) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(out))
+    return BUTLER_ERR_INVALID_ARG;
+  if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (fused)
+    return finish(s, launch_select_attend(s, scores, budget_num, budget_den, n_sink, n_window,
+                                          idx, count, B, Hq, Hkv, L, cap, radix_hist, q, k_cache,
+                                          v_cache, out, L_cap, softmax_scale, workspace));
+  hipError_t e = launch_select(s, scores, budget_num, budget_den, n_sink, n_window, idx, nullptr,
+                               count, B, Hkv, 1, L, cap, 0, 0, radix_hist, nullptr, workspace);
+  if (e != hipSuccess) return finish(s, e);
+  return finish(s, launch_attn_idx(s, dtype, q, k_cache, v_cache, idx, count, out, B, Hq, Hkv, D,
+                                   1, L_cap, cap, softmax_scale, (char*)workspace + sel_ws));
+}
+
 int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, int32_t* keep,
                            int B, int Hq, int Hkv, int D, float threshold) {
   if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;

@@ -20,6 +20,7 @@
 // runs the VALU wave routine over it.
 #include <type_traits>
 
+#include "attn_tile.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -31,29 +32,6 @@ constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr int kRoundTokens = 256;     // list positions per workgroup round (32 per wave)
 constexpr int kMaxSplits = 512;          // splits per row (more -> several rounds per split)
 constexpr int kBmChunkWords = 64;     // bitmask words compacted per prefill round
-
-template <typename T, int D, int R>
-struct Geo {
-  static constexpr int EPL = Vec16<T>::N;          // elements per lane
-  static constexpr int LPR = D / EPL;              // lanes per key row
-  static constexpr int TPW = 64 / LPR;             // rows per wave step
-  static constexpr int STEPS = 32 / TPW;           // steps per wave per round
-  static constexpr int UB = STEPS < 8 ? STEPS : 8; // rows per lane group per batch
-};
-
-template <int R, int EPL>
-struct SoftState {
-  float m[R], l[R], acc[R][EPL];
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      m[r] = neg_inf();
-      l[r] = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[r][e] = 0.f;
-    }
-  }
-};
 
 // One batch: this lane group attends to rows toks[0..UB) (-1 = no row).
 template <typename T, int D, int R>
@@ -124,87 +102,6 @@ __device__ __forceinline__ void attend_batch(const T* __restrict__ kb, const T* 
 }
 
 // lo <- merge(lo, hi) for one head
-template <int EPL>
-__device__ __forceinline__ void merge_pair(float& m, float& l, float* acc, float m2, float l2,
-                                           const float* a2) {
-  if (m2 == neg_inf()) return;
-  if (m == neg_inf()) {
-    m = m2; l = l2;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = a2[e];
-    return;
-  }
-  const float mn = fmaxf(m, m2);
-  const float fa = fast_exp2(m - mn), fb = fast_exp2(m2 - mn);
-  l = l * fa + l2 * fb;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * fa + a2[e] * fb;
-  m = mn;
-}
-
-// Merges the lane groups of each wave (fixed order, identical in both lanes of a pair),
-// then the waves through LDS.  On return, red_m/red_l [R] and red_acc [R*D] hold the
-// workgroup's state; all threads have synchronised.
-template <typename T, int D, int R, int NT = kAttnThreads>
-__device__ __forceinline__ void block_reduce(SoftState<R, Geo<T, D, R>::EPL>& st, float* s_m,
-                                             float* s_l, float* s_acc, float* red_m,
-                                             float* red_l, float* red_acc) {
-  using G = Geo<T, D, R>;
-  constexpr int EPL = G::EPL, LPR = G::LPR;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int pe = lane % LPR;
-#pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) {
-    const bool low = (lane & o) == 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float m2 = __shfl_xor(st.m[r], o, 64);
-      const float l2 = __shfl_xor(st.l[r], o, 64);
-      float a2[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(st.acc[r][e], o, 64);
-      if (low) {
-        merge_pair<EPL>(st.m[r], st.l[r], st.acc[r], m2, l2, a2);
-      } else {
-        float m = m2, l = l2, acc[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = a2[e];
-        merge_pair<EPL>(m, l, acc, st.m[r], st.l[r], st.acc[r]);
-        st.m[r] = m; st.l[r] = l;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) st.acc[r][e] = acc[e];
-      }
-    }
-  }
-  if (lane < LPR) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (pe == 0) { s_m[wid * R + r] = st.m[r]; s_l[wid * R + r] = st.l[r]; }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[(wid * R + r) * D + pe * EPL + e] = st.acc[r][e];
-    }
-  }
-  __syncthreads();
-  constexpr int NWV = NT / 64;
-  for (int j = threadIdx.x; j < R * D; j += NT) {
-    const int r = j / D, d = j - r * D;
-    float M = neg_inf();
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_m[w * R + r]);
-    float lsum = 0.f, a = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      const float mw = s_m[w * R + r];
-      const float f = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
-      lsum += s_l[w * R + r] * f;
-      a += s_acc[(w * R + r) * D + d] * f;
-    }
-    red_acc[j] = a;
-    if (d == 0) { red_m[r] = M; red_l[r] = lsum; }
-  }
-  __syncthreads();
-}
-
 template <typename T, int D, int R>
 __device__ __forceinline__ void load_q(const T* q, long long head0, long long head_stride,
                                        int pe, float scale_log2,
@@ -278,7 +175,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_idx_kernel(
     __syncthreads();
     wave_round<T, D, R>(kb, vb, s_list, qr, st);
   }
-  block_reduce<T, D, R>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
+  block_reduce<T, D, R, kAttnThreads>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
   float* my = part + ((long long)row * nsplit + split) * R * PS;
   for (int j = threadIdx.x; j < R * D; j += kAttnThreads) my[(j / D) * PS + 4 + j % D] = red_acc[j];
   if (threadIdx.x < R) {
@@ -303,29 +200,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_idx_kernel(
 // heads.  Each wave takes 2 tiles per round with all 16 row loads in flight; rows and
 // waves merge with the same reduction as the VALU kernel.
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
-template <int H>
-__device__ __forceinline__ float row_bcast(float x) { return dpp_f<0x150 + H>(x); }
-
-__device__ __forceinline__ float row_bcast_rt(float x, int h) {
-  switch (h) {
-    case 0: return row_bcast<0>(x);
-    case 1: return row_bcast<1>(x);
-    case 2: return row_bcast<2>(x);
-    case 3: return row_bcast<3>(x);
-    case 4: return row_bcast<4>(x);
-    case 5: return row_bcast<5>(x);
-    case 6: return row_bcast<6>(x);
-    default: return row_bcast<7>(x);
-  }
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
 #ifndef BUTLER_MF_THREADS
 #define BUTLER_MF_THREADS 512
 #endif
@@ -346,75 +220,6 @@ constexpr int kMfStage = BUTLER_MF_STAGE;  // list positions staged in LDS at a 
 constexpr int kMfPad = (2 * kMfBuf - 2) * kMfRound;  // ring prefetch past the stage end
 constexpr int kMfTargetBlocks = BUTLER_MF_TARGET_BLOCKS;  // grid size aimed at (2 per CU)
 static_assert(kMfStage % kMfThreads == 0, "stage is a whole number of block-wide loads");
-
-struct MfTile {
-  uint4 k[4], v[4];
-};
-
-// Rows of the tile at list positions base .. base+15: lane (quad, pe) takes K columns
-// kk*32 + 8*quad of row pe, and V columns 8*pe of rows 4*quad + r.  Every position of the
-// staged list holds a valid cache row (past the end: a selected row, masked out of the
-// softmax), so the loads need no guard and the compiler can count them exactly.
-__device__ __forceinline__ void mf_load(MfTile& tl, const int* s_list, int base,
-                                        const bf16_t* kb, const bf16_t* vb, int quad, int pe) {
-  constexpr int D = 128;
-  const int tk = s_list[base + pe];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    tl.k[kk] = *reinterpret_cast<const uint4*>(kb + (long long)tk * D + kk * 32 + 8 * quad);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int tv = s_list[base + 4 * quad + r];
-    tl.v[r] = *reinterpret_cast<const uint4*>(vb + (long long)tv * D + 8 * pe);
-  }
-}
-
-// lim = how many of rows 4*quad .. 4*quad+3 of the tile are real list entries
-template <int R>
-__device__ __forceinline__ void mf_compute(const MfTile& tl, const bf16x8_t (&qf)[4], int lim,
-                                           float scale_log2, float& m, float& l,
-                                           float (&acc)[R][8]) {
-  f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[kk]), qf[kk], c, 0, 0, 0);
-  // lane (quad, pe): logits of rows 4*quad + r for head pe
-  float z[4], mt = neg_inf();
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    z[r] = (r < lim) ? c[r] * scale_log2 : neg_inf();
-    mt = fmaxf(mt, z[r]);
-  }
-  const float mn = fmaxf(m, mt);
-  const float alpha = (mn == neg_inf()) ? 1.f : fast_exp2(m - mn);
-  float pz[4], ps = 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    pz[r] = (r < lim) ? fast_exp2(z[r] - mn) : 0.f;
-    ps += pz[r];
-  }
-  l = l * alpha + ps;
-  m = mn;
-  float vv[4][8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    Raw16 rv;
-    rv.v = tl.v[r];
-    unpack16<bf16_t>(rv, vv[r]);
-  }
-#pragma unroll
-  for (int h = 0; h < R; ++h) {
-    const float a = row_bcast_rt(alpha, h);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] *= a;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = row_bcast_rt(pz[r], h);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vv[r][e], acc[h][e]);
-    }
-  }
-}
 
 template <int R>
 __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
@@ -642,7 +447,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bitmask_kernel(
       wave_round<T, D, R>(kb, vb, s_list + p0, qr, st);
     }
   }
-  block_reduce<T, D, R>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
+  block_reduce<T, D, R, kAttnThreads>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
   for (int j = threadIdx.x; j < R * D; j += kAttnThreads) {
     const int r = j / D, d = j - r * D;
     out[(((long long)b * Hq + g * R + r) * Lq + i) * D + d] =
@@ -681,6 +486,27 @@ SplitPlan plan_for(int cap) {
   return {(cap + per - 1) / per, rounds};
 }
 
+// splits per thread of the merge: the smallest power of two >= nsplit / 8
+template <int D, int R>
+hipError_t merge_t(hipStream_t s, const float* part, float* out, long long rows, int Hq, int Hkv,
+                   int Lq, int nsplit) {
+  const dim3 mgrid((unsigned)(rows * R * (D / 32)));
+  const int per = (nsplit + kMergeGroups - 1) / kMergeGroups;
+  if (per <= 4)
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 4>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  else if (per <= 8)
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 8>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  else if (per <= 16)
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 16>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  else if (per <= 32)
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 32>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  else if (per <= 64)
+    hipLaunchKernelGGL((attn_merge_kernel<D, R, 64>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 template <typename T, int D, int R>
 hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
                  const int32_t* idx, const int32_t* count, float* out, int B, int Hq, int Hkv,
@@ -703,20 +529,7 @@ hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
                        count, part, Hq, Hkv, Lq, L_cap, cap, scale * 1.4426950408889634f,
                        sp.nsplit, sp.rounds, (int)rows);
   }
-  // splits per thread of the merge: the smallest power of two >= nsplit / 8
-  const dim3 mgrid((unsigned)(rows * R * (D / 32)));
-  const int per = (nsplit + kMergeGroups - 1) / kMergeGroups;
-  if (per <= 4)
-    hipLaunchKernelGGL((attn_merge_kernel<D, R, 4>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
-  else if (per <= 8)
-    hipLaunchKernelGGL((attn_merge_kernel<D, R, 8>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
-  else if (per <= 16)
-    hipLaunchKernelGGL((attn_merge_kernel<D, R, 16>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
-  else if (per <= 32)
-    hipLaunchKernelGGL((attn_merge_kernel<D, R, 32>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
-  else
-    hipLaunchKernelGGL((attn_merge_kernel<D, R, 64>), mgrid, dim3(kMergeThreads), 0, s, part, out, Hq, Hkv, Lq, nsplit);
-  return hipGetLastError();
+  return merge_t<D, R>(s, part, out, rows, Hq, Hkv, Lq, nsplit);
 }
 
 
@@ -958,6 +771,17 @@ hipError_t launch_attn_idx(hipStream_t s, int dtype, const void* q, const void* 
                            float* out, int B, int Hq, int Hkv, int D, int Lq, int L_cap,
                            int cap, float scale, void* ws) {
   BUTLER_ATTN_DISPATCH(idx_t, s, q, k, v, idx, count, out, B, Hq, Hkv, Lq, L_cap, cap, scale, ws);
+}
+
+hipError_t launch_attn_merge(hipStream_t s, const float* part, float* out, long long rows, int Hq,
+                             int Hkv, int Lq, int D, int nsplit) {
+  const int R = Hq / Hkv;
+#define BUTLER_MG(DD, RR) \
+  if (D == DD && R == RR) return merge_t<DD, RR>(s, part, out, rows, Hq, Hkv, Lq, nsplit);
+  BUTLER_MG(128, 1) BUTLER_MG(128, 2) BUTLER_MG(128, 4) BUTLER_MG(128, 8)
+  BUTLER_MG(64, 1) BUTLER_MG(64, 2) BUTLER_MG(64, 4) BUTLER_MG(64, 8)
+#undef BUTLER_MG
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_bitmask(hipStream_t s, int dtype, const void* q, const void* k,

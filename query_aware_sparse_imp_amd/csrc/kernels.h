@@ -51,6 +51,15 @@ hipError_t launch_attn_bitmask(hipStream_t s, int dtype, const void* q, const vo
                                int Hq, int Hkv, int D, int Lq, int L, int L_cap, int q_pos0,
                                float scale, void* ws);
 
+hipError_t launch_attn_merge(hipStream_t s, const float* part, float* out, long long rows, int Hq,
+                             int Hkv, int Lq, int D, int nsplit);
+bool select_attend_fusable(int dtype, int D, int Hq, int Hkv, int L);
+size_t select_attend_workspace(int rows, int Hq, int Hkv, int L);
+hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int den,
+                                int n_sink, int n_window, int32_t* idx, int32_t* count, int B,
+                                int Hq, int Hkv, int L, int cap, uint32_t* hist, const void* q,
+                                const void* k, const void* v, float* out, int L_cap,
+                                float scale, void* ws);
 hipError_t launch_selection_cache(hipStream_t s, int dtype, const void* q, void* q_ref,
                                   int32_t* keep, int B, int Hq, int Hkv, int D, float threshold);
 

@@ -37,6 +37,7 @@
 //
 // Single-row calls with selection-cache flags skip the rows of kept (b, KV heads) in
 // every kernel, so their outputs and the workspace state stay as they were.
+#include "attn_tile.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -309,20 +310,24 @@ struct MbWs {
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
-long long nchunk_for(int L) {
-  const int chunk = kMbThreads * kpt_for(L);
+long long nchunk_k(int L, int kpt) {
+  const int chunk = kMbThreads * kpt;
   return (L + chunk - 1) / chunk;
 }
 
-size_t mb_bytes(long long rows, int L) {
-  const long long nchunk = nchunk_for(L);
+long long nchunk_for(int L) { return nchunk_k(L, kpt_for(L)); }
+
+size_t mb_bytes_k(long long rows, int L, int kpt) {
+  const long long nchunk = nchunk_k(L, kpt);
   return al256(rows * 2048 * 4) + al256(rows * 8) + al256(rows * sizeof(RowState)) +
          2 * al256(rows * nchunk * 4) + al256(rows * 4) + al256(2 * rows * 2048 * 4) +
          al256((size_t)rows * L * sizeof(uint2));
 }
 
-MbWs carve(void* ws, long long rows, int L) {
-  const long long nchunk = nchunk_for(L);
+size_t mb_bytes(long long rows, int L) { return mb_bytes_k(rows, L, kpt_for(L)); }
+
+MbWs carve_k(void* ws, long long rows, int L, int kpt) {
+  const long long nchunk = nchunk_k(L, kpt);
   char* p = (char*)ws;
   MbWs w;
   w.hist1 = (uint32_t*)p;                 p += al256(rows * 2048 * sizeof(uint32_t));
@@ -335,6 +340,8 @@ MbWs carve(void* ws, long long rows, int L) {
   w.cand = (uint2*)p;
   return w;
 }
+
+MbWs carve(void* ws, long long rows, int L) { return carve_k(ws, rows, L, kpt_for(L)); }
 
 // The KPT keys of tokens t0 .. t0+KPT-1 (all requested at once); returns how many exist.
 template <int KPT>
@@ -682,18 +689,45 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
 // prefix-summed once through LDS, and each wave writes its words' indices coalesced and
 // their bitmask words.  The chunk-0 workgroup writes the row count and clears the row's
 // histogram (nothing in this kernel reads it).
-template <int KPT>
+// Attention operands of the fused finishing pass (R > 0): bf16, D = 128, one query row.
+struct MbAttn {
+  const bf16_t* q;      // [B, Hq, 1, 128]
+  const bf16_t* k;      // [B, Hkv, L_cap, 128]
+  const bf16_t* v;
+  float* part;          // [rows][nchunk][R][128 + 4]: (max, sum, -, -, acc[128]) per head
+  int Hq, Hkv, L_cap;
+  float scale_log2;
+};
+
+constexpr int kMaRound = kMbWaves * 16;   // list positions per workgroup round (a tile per wave)
+constexpr int kMaPad = 2 * kMaRound;      // ring prefetch past the list end
+
+template <int KPT, int R>
 __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
     const float* __restrict__ scores, int num, int den, int n_sink, int n_window, int L,
     int rows, int cap, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask,
     int32_t* __restrict__ count, uint32_t* __restrict__ ghist, MbWs w,
-    const int32_t* __restrict__ keep) {
+    const int32_t* __restrict__ keep, MbAttn at) {
   constexpr int NWD = kMbWaves * KPT;   // 64-token words per chunk
   static_assert(NWD <= 128, "two words per lane in the prefix scan");
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
-  if (keep && keep[row]) return;   // the cached selection stands
+  if (R == 0 && keep && keep[row]) return;   // the cached selection stands
   const int nchunk = gridDim.x / rows;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // fused attention: the group's query heads as the MFMA B operand, requested first
+  bf16x8_t qf[4];
+  if constexpr (R > 0) {
+    const int b = row / at.Hkv, g = row - b * at.Hkv;
+    const int quad = lane >> 4, pe = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (pe < R)
+        raw = *reinterpret_cast<const uint4*>(at.q + ((long long)b * at.Hq + g * R + pe) * 128 +
+                                              kk * 32 + 8 * quad);
+      qf[kk] = as_bf16x8(raw);
+    }
+  }
   int k;
   const int mode = row_mode(L, num, den, k);
   __shared__ uint32_t h[2048];
@@ -824,19 +858,77 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
   const int out0 = def_before + sel_before;
   const unsigned long long lt = (1ull << lane) - 1ull;
   const int nwords = (L + 31) / 32;
+  // the chunk's selected tokens, ascending, for the fused attention
+  __shared__ int s_list[(R > 0) ? kMbThreads * KPT + kMaPad + kMaRound : 1];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int u = j * kMbWaves + wid;
     const int pe = __shfl(ex, u >> 1), pv = __shfl(v0, u >> 1);
     const int pref = pe + ((u & 1) ? pv : 0);
     const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
-    if (idx && ((sm[j] >> lane) & 1ull)) {
-      const int pos = out0 + pref + __popcll(sm[j] & lt);
-      if (pos < cap) idx[(long long)row * cap + pos] = t;
+    if ((sm[j] >> lane) & 1ull) {
+      const int lpos = pref + __popcll(sm[j] & lt);
+      if (idx) {
+        const int pos = out0 + lpos;
+        if (pos < cap) idx[(long long)row * cap + pos] = t;
+      }
+      if constexpr (R > 0) s_list[lpos] = t;
     }
     if (bitmask && lane < 2) {
       const int wd = (c_lo + kMbThreads * j + 64 * wid) / 32 + lane;
       if (wd < nwords) bitmask[(long long)row * nwords + wd] = (uint32_t)(sm[j] >> (32 * lane));
+    }
+  }
+  if constexpr (R > 0) {
+    // attention over the chunk's selected tokens: a ring of two 16-token tiles per wave;
+    // list positions past the end repeat the last selected token and are masked out
+    const int nsel = __shfl(ex + v0 + v1, 63);   // the chunk's count (inclusive scan total)
+    __syncthreads();
+    const int last = nsel > 0 ? s_list[nsel - 1] : 0;
+    for (int j = nsel + (int)threadIdx.x; j < kMbThreads * KPT + kMaPad + kMaRound; j += kMbThreads)
+      s_list[j] = last;
+    __syncthreads();
+    const int quad = lane >> 4, pe = lane & 15;
+    const bf16_t* kb = at.k + (long long)row * at.L_cap * 128;
+    const bf16_t* vb = at.v + (long long)row * at.L_cap * 128;
+    float m = neg_inf(), l = 0.f;
+    float acc[R][8];
+#pragma unroll
+    for (int h = 0; h < R; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    const int nr = (nsel + kMaRound - 1) / kMaRound;
+    const int w0 = wid * 16;
+    const int lim0 = nsel - w0 - 4 * quad;
+    MfTile t0, t1;
+    if (nr > 0) mf_load(t0, s_list, w0, kb, vb, quad, pe);
+    int r = 0;
+    for (; r + 2 <= nr; r += 2) {
+      mf_load(t1, s_list, (r + 1) * kMaRound + w0, kb, vb, quad, pe);
+      mf_compute<R>(t0, qf, lim0 - r * kMaRound, at.scale_log2, m, l, acc);
+      mf_load(t0, s_list, (r + 2) * kMaRound + w0, kb, vb, quad, pe);
+      mf_compute<R>(t1, qf, lim0 - (r + 1) * kMaRound, at.scale_log2, m, l, acc);
+    }
+    if (r < nr) mf_compute<R>(t0, qf, lim0 - r * kMaRound, at.scale_log2, m, l, acc);
+    // every lane of a 16-lane row needs the (m, l) of each head, held by lane h of the row
+    SoftState<R, 8> st;
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      st.m[h] = row_bcast_rt(m, h);
+      st.l[h] = row_bcast_rt(l, h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[h][e] = acc[h][e];
+    }
+    __shared__ float s_m[kMbWaves * (R > 0 ? R : 1)], s_l[kMbWaves * (R > 0 ? R : 1)];
+    __shared__ float red_m[R > 0 ? R : 1], red_l[R > 0 ? R : 1];
+    __shared__ float s_acc[kMbWaves * (R > 0 ? R : 1) * 128], red_acc[(R > 0 ? R : 1) * 128];
+    block_reduce<bf16_t, 128, R, kMbThreads>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
+    constexpr int PS = 128 + 4;
+    float* my = at.part + ((long long)row * nchunk + chunk) * R * PS;
+    for (int j = threadIdx.x; j < R * 128; j += kMbThreads) my[(j / 128) * PS + 4 + j % 128] = red_acc[j];
+    if (threadIdx.x < R) {
+      my[threadIdx.x * PS] = red_m[threadIdx.x];
+      my[threadIdx.x * PS + 1] = red_l[threadIdx.x];
     }
   }
 }
@@ -850,7 +942,79 @@ bool use_chunked(int Lq, int L, int causal) {
   return !causal && Lq == 1 && L > BUTLER_SEL_CHUNKED_ABOVE;
 }
 
+// Fused finishing pass + attention: chunks small enough that a short row still spreads
+// over the chip, few enough that the merge takes every chunk's partial at once.
+#ifndef BUTLER_SA_KPT_SHORT
+#define BUTLER_SA_KPT_SHORT 4    // rows up to 64K tokens
+#endif
+#ifndef BUTLER_SA_KPT_MID
+#define BUTLER_SA_KPT_MID 16     // rows up to 512K tokens
+#endif
+int kpt_attend(int L) {
+  return L <= 65536 ? BUTLER_SA_KPT_SHORT : L <= 524288 ? BUTLER_SA_KPT_MID : L <= 2097152 ? 16 : 32;
+}
+constexpr int kMaMaxChunks = 512;
+
 }  // namespace
+
+bool select_attend_fusable(int dtype, int D, int Hq, int Hkv, int L) {
+  const int R = Hq / Hkv;
+  return dtype == 1 && D == 128 && (R == 1 || R == 2 || R == 4 || R == 8) &&
+         use_chunked(1, L, 0) && nchunk_k(L, kpt_attend(L)) <= kMaMaxChunks;
+}
+
+size_t select_attend_workspace(int rows, int Hq, int Hkv, int L) {
+  const int kpt = kpt_attend(L);
+  return mb_bytes_k(rows, L, kpt) +
+         al256((size_t)rows * nchunk_k(L, kpt) * (Hq / Hkv) * (128 + 4) * sizeof(float));
+}
+
+hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int den,
+                                int n_sink, int n_window, int32_t* idx, int32_t* count, int B,
+                                int Hq, int Hkv, int L, int cap, uint32_t* hist, const void* q,
+                                const void* k, const void* v, float* out, int L_cap,
+                                float scale, void* ws) {
+  const long long rows = (long long)B * Hkv;
+  const int kpt = kpt_attend(L);
+  const int nchunk = (int)nchunk_k(L, kpt);
+  const MbWs w = carve_k(ws, rows, L, kpt);
+  float* part = (float*)((char*)ws + mb_bytes_k(rows, L, kpt));
+  const MbAttn at{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, part, Hq, Hkv, L_cap,
+                  scale * 1.4426950408889634f};
+  const dim3 grid((unsigned)(rows * nchunk));
+  uint32_t* gh = hist ? hist : w.hist1;
+  const int R = Hq / Hkv;
+  auto run = [&](auto kpt_c, auto r_c) {
+    constexpr int KPT = decltype(kpt_c)::value;
+    constexpr int RR = decltype(r_c)::value;
+    if (!hist)
+      hipLaunchKernelGGL(mb_hist1_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
+                         L, (int)rows, gh, (const int32_t*)nullptr);
+    hipLaunchKernelGGL(mb_cand_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
+                       n_sink, n_window, L, (int)rows, (const uint32_t*)gh, w,
+                       (const int32_t*)nullptr);
+    hipLaunchKernelGGL((mb_finish_kernel<KPT, RR>), grid, dim3(kMbThreads), 0, s, scores, num,
+                       den, n_sink, n_window, L, (int)rows, cap, idx, (uint32_t*)nullptr, count,
+                       gh, w, (const int32_t*)nullptr, at);
+  };
+  auto by_r = [&](auto kpt_c) {
+    switch (R) {
+      case 1: run(kpt_c, std::integral_constant<int, 1>()); break;
+      case 2: run(kpt_c, std::integral_constant<int, 2>()); break;
+      case 4: run(kpt_c, std::integral_constant<int, 4>()); break;
+      default: run(kpt_c, std::integral_constant<int, 8>()); break;
+    }
+  };
+  switch (kpt) {
+    case 4: by_r(std::integral_constant<int, 4>()); break;
+    case 8: by_r(std::integral_constant<int, 8>()); break;
+    case 16: by_r(std::integral_constant<int, 16>()); break;
+    default: by_r(std::integral_constant<int, 32>()); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attn_merge(s, part, out, rows, Hq, Hkv, 1, 128, nchunk);
+}
 
 size_t select_workspace(int rows, int L, int Lq, int causal) {
   return use_chunked(Lq, L, causal) ? mb_bytes(rows, L) : 0;
@@ -873,8 +1037,9 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
                            L, (int)rows, gh, keep);
       hipLaunchKernelGGL(mb_cand_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
                          n_sink, n_window, L, (int)rows, (const uint32_t*)gh, w, keep);
-      hipLaunchKernelGGL(mb_finish_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
-                         n_sink, n_window, L, (int)rows, cap, idx, bitmask, count, gh, w, keep);
+      hipLaunchKernelGGL((mb_finish_kernel<KPT, 0>), grid, dim3(kMbThreads), 0, s, scores, num,
+                         den, n_sink, n_window, L, (int)rows, cap, idx, bitmask, count, gh, w, keep,
+                         MbAttn{});
     };
     switch (kpt_for(L)) {
       case 8: run(std::integral_constant<int, 8>()); break;

@@ -161,3 +161,29 @@ def test_project_and_score_validation():
     assert call(ptrs=[P[0], None, P[2], P[3], P[4]]) == INV
     assert call(hist=MIS) == INV
     assert call(B=9000) == UNS                                   # B * Hkv > 65535
+
+
+def test_select_attend_validation_and_workspace_query():
+    f = L.butler_select_attend
+    P = [FAKE + 256 * i for i in range(7)]      # scores, idx, count, q, k, v, out
+
+    def call(*, dtype=1, num=1, den=2, ptrs=P, B=1, Hq=32, Hkv=8, D=128, Lr=32768,
+             L_cap=32768, cap=16452, scale=0.088, ws=FAKE, n=None):
+        n = n if n is not None else ctypes.c_size_t(1 << 40)
+        return f(None, dtype, ptrs[0], None, num, den, 4, 64, ptrs[1], ptrs[2], ptrs[3], ptrs[4],
+                 ptrs[5], ptrs[6], B, Hq, Hkv, D, Lr, L_cap, cap, scale, ws, ctypes.byref(n))
+    n = ctypes.c_size_t(0)
+    assert call(ws=None, n=n) == OK and n.value > 0                       # size query (fused)
+    fused = n.value
+    assert call(ws=None, n=n, Lr=3001, L_cap=3001, cap=1568) == OK and n.value > 0   # unfused
+    assert fused >= 8 * 32 * 4 * 132 * 4                                  # one partial per chunk
+    assert call(cap=16451) == INV                                        # cap too small
+    assert call(den=0) == INV
+    assert call(Hq=30) == INV
+    assert call(D=96) == UNS
+    assert call(dtype=3) == UNS
+    assert call(scale=0.0) == INV
+    assert call(Lr=32769) == INV                                         # L > L_cap
+    assert call(ptrs=[P[0], None] + P[2:]) == INV                        # idx required
+    assert call(ptrs=[P[0], P[1], P[2], MIS] + P[4:]) == INV             # misaligned q
+    assert call(ws=FAKE, n=ctypes.c_size_t(16)) == WSE                   # workspace too small

@@ -206,3 +206,68 @@ def test_project_and_score_matches_separate_calls(cfg, L):
     kept = keep.bool()
     assert (sc[kept] == -5.0).all() and int(hc[kept].abs().sum()) == 0
     assert torch.equal(sc[~kept], sa[~kept]) and torch.equal(hc[~kept], ha[~kept])
+
+
+@pytest.mark.parametrize("L,Hq,num,den,use_hist", [
+    (3001, 32, 1, 2, True),      # short row: the two calls' kernels
+    (5001, 32, 1, 2, True),      # fused, ragged last chunk
+    (32768, 32, 1, 2, True),     # fused, the layer workload's length
+    (70001, 32, 1, 16, False),   # fused with 8 keys per thread, no scorer histogram
+    (9000, 8, 3, 10, True),      # R = 1
+    (9000, 64, 1, 2, True),      # R = 8
+    (9000, 32, 1, 1, True),      # budget takes every token
+    (9000, 32, 0, 1, True),      # budget 0: sink and window only
+])
+def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
+    """butler_select_attend == butler_select_topk + butler_sparse_decode_attn: idx and count
+    bit for bit, the output within float32 rounding of the separate attention and within
+    the bf16 bound of the oracle's attention over the same sets; three calls in a row (the
+    selection's workspace state carries over between calls)."""
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[2].replace(Hq=Hq)
+    print(f"[select+attend] L={L} Hq={Hq} budget={num}/{den} hist={use_hist}", flush=True)
+    inp = to_device(synthetic.decode_layer(w, 0, L=L, with_qimp=False))
+    dev = "cuda"
+    k, v, q = inp["k_cache_d"], inp["v_cache_d"], inp["q_d"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(L + Hq)
+    scores = torch.randn(w.B, w.Hkv, 1, L, generator=gen, device=dev) * 10.0
+    cap = min(L, (L * num) // den + w.n_sink + w.n_window)
+
+    def hist_of():
+        """The first-digit histogram butler_score documents, counted from the scores (the
+        order-preserving key: -0 as +0, sign set -> all bits flipped, else sign bit set)."""
+        if not use_hist:
+            return None
+        bits = scores.view(torch.int32).to(torch.int64) & 0xffffffff
+        bits = torch.where(bits == 0x80000000, torch.zeros_like(bits), bits)
+        key = torch.where(bits >= 0x80000000, (~bits) & 0xffffffff, bits | 0x80000000)
+        b = (key >> 21).view(w.B * w.Hkv, L)
+        h = torch.zeros(w.B * w.Hkv, 2048, dtype=torch.int32, device=dev)
+        h.scatter_add_(1, b, torch.ones_like(b, dtype=torch.int32))
+        return h.view(w.B, w.Hkv, 1, 2048)
+    idx_a = torch.full((w.B, w.Hkv, 1, cap), -1, dtype=torch.int32, device=dev)
+    cnt_a = torch.zeros(w.B, w.Hkv, 1, dtype=torch.int32, device=dev)
+    out_a = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=dev)
+    qa.butler_select_topk(scores, num, den, w.n_sink, w.n_window, cnt_a, idx=idx_a,
+                          radix_hist=hist_of())
+    qa.butler_sparse_decode_attn(q, k, v, out_a, L=L, idx=idx_a, count=cnt_a,
+                                 softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        idx_b = torch.full_like(idx_a, -1)
+        cnt_b = torch.zeros_like(cnt_a)
+        out_b = torch.full_like(out_a, float("nan"))
+        qa.butler_select_attend(scores, num, den, w.n_sink, w.n_window, cnt_b, idx_b, q, k, v,
+                                out_b, L=L, softmax_scale=w.scale, radix_hist=hist_of())
+        torch.cuda.synchronize()
+        assert torch.equal(cnt_a, cnt_b), rep
+        assert torch.equal(idx_a, idx_b), rep
+        d = float((out_a - out_b).abs().max())
+        assert d <= 1e-4, (rep, d)
+    check_select_exact(idx_b, cnt_b, np64(scores), num, den, w.n_sink, w.n_window)
+    ic, cc = idx_b.cpu().numpy(), cnt_b.cpu().numpy()
+    err = check_attend(out_b, inp["q"], inp["k_cache"], inp["v_cache"],
+                       lambda b, g, i: ic[b, g, i, :cc[b, g, i]], w.scale, w.dtype)
+    print(f"  selected {int(cc.sum())}, fused vs separate max-abs {d:.2e}, vs oracle {err:.2e}",
+          flush=True)
