@@ -93,7 +93,8 @@ int butler_project_keys(void* stream, int dtype, const void* k_cache, const void
  *   w1     [F, E]             bf16
  *   w2     [Hq*G*d', F]       bf16
  *   q_imp  [B, Hq, G, Lq, d'] bf16 (written)
- * dtype must be BUTLER_BF16.  E, F multiples of 64, E <= 8192; Hq*G*d' a multiple of 64.
+ * dtype must be BUTLER_BF16.  E, F multiples of 64, E <= 8192; Hq*G*d' a multiple of 64;
+ * d' a multiple of 8.
  * workspace: normalised rows and hidden activations, split-K partial sums (at most 4
  * rows: the hidden activations only).
  */

@@ -89,7 +89,7 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
     return BUTLER_ERR_INVALID_ARG;
   if (!(ln_eps > 0.f)) return BUTLER_ERR_INVALID_ARG;
   const long long N2 = (long long)Hq * G * dprime;
-  if (E % 64 || F % 64 || N2 % 64 || N2 > (1 << 24)) return BUTLER_ERR_UNSUPPORTED;
+  if (E % 64 || F % 64 || N2 % 64 || N2 > (1 << 24) || dprime % 8) return BUTLER_ERR_UNSUPPORTED;
   if (E > 8192) return BUTLER_ERR_UNSUPPORTED;   // LN holds a row in registers
   if ((long long)B * Lq > (1 << 24)) return BUTLER_ERR_UNSUPPORTED;
   int rc;

@@ -11,11 +11,12 @@
 //
 // Two GEMM kernels.  Blocks of rows (prefill: M = B*Lq >= 64) run on the matrix cores:
 // a 128 x 128 tile per workgroup, 64 x 64 per wave as 2 x 2 v_mfma_f32_32x32x16_bf16
-// tiles, K staged through LDS 32 at a time, double-buffered, with a ring of four
-// register stages so three K tiles are in flight from memory.  Other shapes with more
-// than 4 rows take the VALU kernel -- 32 rows x 64 columns per workgroup, a thread owns
-// 1 row x 8 columns.  Up to 4 rows (decode: one hidden state per sequence) take a
-// weight-streaming GEMV instead (below).
+// tiles, K staged through LDS 64 at a time, double-buffered, with two register stages
+// so the next K tile is in flight from memory; bf16 results leave through an LDS stage
+// as 16-byte row chunks (contiguous in both the row-major activation and the Q_imp
+// layout).  Other shapes with more than 4 rows take the VALU kernel -- 32 rows x 64
+// columns per workgroup, a thread owns 1 row x 8 columns.  Up to 4 rows (decode: one
+// hidden state per sequence) take a weight-streaming GEMV instead (below).
 #include "common.h"
 #include "kernels.h"
 
@@ -161,46 +162,60 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8v_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16v_t;
 
-constexpr int kMM = 128, kMN = 128, kMK = 32;
+constexpr int kMM = 128, kMN = 128;
 constexpr int kMThreads = 256;
-constexpr int kMPf = 4;        // register stages of the K loop (even: LDS buffers alternate)
-constexpr int kAS = kMK + 8;   // LDS row stride in bf16 of the A and B tiles
+
+// 128 x 128 tiles, 64 x 64 per wave as 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.  K is staged
+// through LDS 64 at a time, double-buffered, with two register stages so the next tile
+// is in flight from memory while one is multiplied (16 MFMAs per wave between barriers).
+// LDS rows of 72 bf16 (144 B) keep the 16-byte operand reads of 16 consecutive rows on
+// distinct banks.  bf16 results leave through an LDS stage in 16-byte row chunks.
+constexpr int kM2K = 64;
+constexpr int kA2S = kM2K + 8;
 
 __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm, void* out, int M, int N, int K,
     int k_per_split, Epilogue ep) {
   const int n0 = blockIdx.x * kMN, m0 = blockIdx.y * kMM, split = blockIdx.z;
   const int k0 = split * k_per_split, k1 = min(K, k0 + k_per_split);
-  __shared__ __align__(16) bf16_t As[2][kMM * kAS];
-  __shared__ __align__(16) bf16_t Bs[2][kMN * kAS];
+  __shared__ __align__(16) bf16_t As[2][kMM * kA2S];
+  __shared__ __align__(16) bf16_t Bs[2][kMN * kA2S];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  // staging roles, the same for both operands: chunks c = tid, tid + 256 are tile row c/4,
-  // K columns 8*(c%4) .. +8
-  const int c0 = tid, c1 = tid + kMThreads;
-  const bf16_t* a0 = A + (long long)min(m0 + (c0 >> 2), M - 1) * K + (c0 & 3) * 8;
-  const bf16_t* a1 = A + (long long)min(m0 + (c1 >> 2), M - 1) * K + (c1 & 3) * 8;  // rows past M: computed, never stored
-  const bf16_t* b0 = Bm + (long long)(n0 + (c0 >> 2)) * K + (c0 & 3) * 8;
-  const bf16_t* b1 = Bm + (long long)(n0 + (c1 >> 2)) * K + (c1 & 3) * 8;
-  const int as0 = (c0 >> 2) * kAS + (c0 & 3) * 8, as1 = (c1 >> 2) * kAS + (c1 & 3) * 8;
-  // a ring of kMPf = 4 register stages: tiles t+1 .. t+3 are in flight from memory while
-  // tile t is multiplied; every load is unconditional (the ring runs past the last tile on
-  // clamped addresses), so each wait is for exactly one stage
-  uint4 ra0_0, ra1_0, rb0_0, rb1_0, ra0_1, ra1_1, rb0_1, rb1_1;
-  uint4 ra0_2, ra1_2, rb0_2, rb1_2, ra0_3, ra1_3, rb0_3, rb1_3;
+  // staging roles, the same for both operands: chunk c = tid + 256 i (i < 4) is tile row
+  // c / 8, K columns 8 (c % 8) .. +8
+  const int r0 = tid >> 3, kc = (tid & 7) * 8;   // rows r0 + 32 i
+  // rows past M: computed on clamped addresses, never stored
+  const bf16_t* ap = A + (long long)min(m0 + r0, M - 1) * K + kc;
+  const bf16_t* ap1 = A + (long long)min(m0 + r0 + 32, M - 1) * K + kc;
+  const bf16_t* ap2 = A + (long long)min(m0 + r0 + 64, M - 1) * K + kc;
+  const bf16_t* ap3 = A + (long long)min(m0 + r0 + 96, M - 1) * K + kc;
+  const bf16_t* bp = Bm + (long long)(n0 + r0) * K + kc;
+  const long long b_step = (long long)32 * K;
+  const int lo = r0 * kA2S + kc, lo_step = 32 * kA2S;
+  uint4 ra0_0, ra1_0, ra2_0, ra3_0, rb0_0, rb1_0, rb2_0, rb3_0;
+  uint4 ra0_1, ra1_1, ra2_1, ra3_1, rb0_1, rb1_1, rb2_1, rb3_1;
 #define BUTLER_GLOAD(st, kk)                                                     \
   do {                                                                           \
-    ra0_##st = *reinterpret_cast<const uint4*>(a0 + (kk));                      \
-    ra1_##st = *reinterpret_cast<const uint4*>(a1 + (kk));                      \
-    rb0_##st = *reinterpret_cast<const uint4*>(b0 + (kk));                      \
-    rb1_##st = *reinterpret_cast<const uint4*>(b1 + (kk));                      \
+    ra0_##st = *reinterpret_cast<const uint4*>(ap + (kk));                      \
+    ra1_##st = *reinterpret_cast<const uint4*>(ap1 + (kk));                     \
+    ra2_##st = *reinterpret_cast<const uint4*>(ap2 + (kk));                     \
+    ra3_##st = *reinterpret_cast<const uint4*>(ap3 + (kk));                     \
+    rb0_##st = *reinterpret_cast<const uint4*>(bp + (kk));                      \
+    rb1_##st = *reinterpret_cast<const uint4*>(bp + b_step + (kk));             \
+    rb2_##st = *reinterpret_cast<const uint4*>(bp + 2 * b_step + (kk));         \
+    rb3_##st = *reinterpret_cast<const uint4*>(bp + 3 * b_step + (kk));         \
   } while (0)
 #define BUTLER_LSTORE(st, buf)                                                   \
   do {                                                                           \
-    *reinterpret_cast<uint4*>(&As[buf][as0]) = ra0_##st;                        \
-    *reinterpret_cast<uint4*>(&As[buf][as1]) = ra1_##st;                        \
-    *reinterpret_cast<uint4*>(&Bs[buf][as0]) = rb0_##st;                        \
-    *reinterpret_cast<uint4*>(&Bs[buf][as1]) = rb1_##st;                        \
+    *reinterpret_cast<uint4*>(&As[buf][lo]) = ra0_##st;                         \
+    *reinterpret_cast<uint4*>(&As[buf][lo + lo_step]) = ra1_##st;               \
+    *reinterpret_cast<uint4*>(&As[buf][lo + 2 * lo_step]) = ra2_##st;           \
+    *reinterpret_cast<uint4*>(&As[buf][lo + 3 * lo_step]) = ra3_##st;           \
+    *reinterpret_cast<uint4*>(&Bs[buf][lo]) = rb0_##st;                         \
+    *reinterpret_cast<uint4*>(&Bs[buf][lo + lo_step]) = rb1_##st;               \
+    *reinterpret_cast<uint4*>(&Bs[buf][lo + 2 * lo_step]) = rb2_##st;           \
+    *reinterpret_cast<uint4*>(&Bs[buf][lo + 3 * lo_step]) = rb3_##st;           \
   } while (0)
   f32x16v_t acc[2][2];
 #pragma unroll
@@ -209,72 +224,104 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int T = (k1 - k0) / kMK;   // a multiple of kMPf (checked on the host)
+  const int T = (k1 - k0) / kM2K;   // even (checked on the host)
   BUTLER_GLOAD(0, k0);
-  BUTLER_GLOAD(1, k0 + min(1, T - 1) * kMK);
-  BUTLER_GLOAD(2, k0 + min(2, T - 1) * kMK);
-  BUTLER_GLOAD(3, k0 + min(3, T - 1) * kMK);
+  BUTLER_GLOAD(1, k0 + min(1, T - 1) * kM2K);
   BUTLER_LSTORE(0, 0);
   __syncthreads();
   const int lr = lane & 31, lk = 8 * (lane >> 5);
-  auto mma = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < kMK / 16; ++ks) {
-      bf16x8v_t a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8v_t*>(&As[buf][(wm * 64 + i * 32 + lr) * kAS + ks * 16 + lk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8v_t*>(&Bs[buf][(wn * 64 + j * 32 + lr) * kAS + ks * 16 + lk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  };
-  // tile t: multiply from LDS buffer t % 2, store tile t+1 (register stage (t+1) % 4) into
-  // the other buffer (past the end: written, never read), refill stage t % 4 with tile t+4
-#define BUTLER_STEP(st, nx)                                                       \
-  do {                                                                            \
-    mma((st) & 1);                                                                \
-    BUTLER_LSTORE(nx, ((st) & 1) ^ 1);                                            \
-    BUTLER_GLOAD(st, k0 + min(t0 + (st) + kMPf, T - 1) * kMK);                    \
-    __syncthreads();                                                              \
+#define BUTLER_MMA(buf)                                                                      \
+  do {                                                                                       \
+    _Pragma("unroll") for (int ks = 0; ks < kM2K / 16; ++ks) {                               \
+      bf16x8v_t a[2], b[2];                                                                  \
+      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                          \
+        a[i] = *reinterpret_cast<const bf16x8v_t*>(&As[buf][(wm * 64 + i * 32 + lr) * kA2S + ks * 16 + lk]); \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                          \
+        b[j] = *reinterpret_cast<const bf16x8v_t*>(&Bs[buf][(wn * 64 + j * 32 + lr) * kA2S + ks * 16 + lk]); \
+      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                          \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j)                                        \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0); \
+    }                                                                                        \
   } while (0)
-  for (int t0 = 0; t0 < T; t0 += kMPf) {
-    BUTLER_STEP(0, 1);
-    BUTLER_STEP(1, 2);
-    BUTLER_STEP(2, 3);
-    BUTLER_STEP(3, 0);
+  // tile t: multiply from LDS buffer t % 2, store tile t+1 (register stage (t+1) % 2) into
+  // the other buffer (past the end: written, never read), refill stage t % 2 with tile t+2
+  for (int t0 = 0; t0 < T; t0 += 2) {
+    BUTLER_MMA(0);
+    BUTLER_LSTORE(1, 1);
+    BUTLER_GLOAD(0, k0 + min(t0 + 2, T - 1) * kM2K);
+    __syncthreads();
+    BUTLER_MMA(1);
+    BUTLER_LSTORE(0, 0);
+    BUTLER_GLOAD(1, k0 + min(t0 + 3, T - 1) * kM2K);
+    __syncthreads();
   }
-#undef BUTLER_STEP
+#undef BUTLER_MMA
 #undef BUTLER_GLOAD
 #undef BUTLER_LSTORE
   // accumulator r of tile (i, j): row 8(r/4) + 4(lane/32) + r%4, column lane%32
+  if (ep.mode == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int n = n0 + wn * 64 + j * 32 + lr;
+          if (m < M) ((float*)out)[((long long)split * M + m) * N + n] = acc[i][j][r];
+        }
+    return;
+  }
+  // bf16 results go through LDS so every lane stores 16 contiguous bytes: the tile in
+  // [128][136] bf16 over the (now idle) A buffers, then 8 consecutive columns per chunk,
+  // which stay inside one (head, slot) run of d' values in the Q_imp layout
+  constexpr int CS = kMN + 8;
+  bf16_t* Cs = &As[0][0];
+  static_assert(kMM * CS <= 2 * kMM * kA2S, "output stage fits the A buffers");
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int n = n0 + wn * 64 + j * 32 + lr;
-        if (m >= M) continue;
-        if (ep.mode == 0) ((float*)out)[((long long)split * M + m) * N + n] = acc[i][j][r];
-        else store_out(ep, out, M, N, m, n, acc[i][j][r]);
+        const int rr = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const float v = (ep.mode == 1) ? fmaxf(acc[i][j][r], 0.f) : acc[i][j][r];
+        Cs[rr * CS + wn * 64 + j * 32 + lr] = f2bf(v);
       }
+  __syncthreads();
+  const int cc = tid & 15;   // 16-byte chunk of the row: columns 8 cc .. 8 cc + 7
+#pragma unroll
+  for (int i = 0; i < kMM / 16; ++i) {
+    const int rr = (tid >> 4) + 16 * i;
+    const int m = m0 + rr;
+    if (m >= M) continue;
+    const uint4 val = *reinterpret_cast<const uint4*>(&Cs[rr * CS + 8 * cc]);
+    const int n = n0 + 8 * cc;
+    bf16_t* dst;
+    if (ep.mode == 1) {
+      dst = (bf16_t*)out + (long long)m * N + n;
+    } else {
+      // column n = (head*G + slot)*dp + i, row m = b*Lq + t
+      const int b = m / ep.Lq, t = m - b * ep.Lq;
+      const int head = n / (ep.G * ep.dp);
+      const int rem = n - head * ep.G * ep.dp;
+      const int slot = rem / ep.dp, i0 = rem - slot * ep.dp;
+      dst = (bf16_t*)out + ((((long long)b * ep.Hq + head) * ep.G + slot) * ep.Lq + t) * ep.dp + i0;
+    }
+    *reinterpret_cast<uint4*>(dst) = val;
+  }
 }
 
+constexpr int kMGran = 2 * kM2K;   // K granule of a split
+
 bool use_mfma(int M, int N, int K) {
-  return M >= 64 && N % kMN == 0 && K % (kMK * kMPf) == 0;
+  return M >= 64 && N % kMN == 0 && K % kMGran == 0;
 }
 
 int mfma_splits(int M, int N, int K) {
   const int tiles = ((M + kMM - 1) / kMM) * (N / kMN);
   int s = 1;
-  while (tiles * s < 256 && K / (s * 2) >= 512 && (K / (s * 2)) % (kMK * kMPf) == 0) s *= 2;
+  while (tiles * s < 256 && K / (s * 2) >= 512 && (K / (s * 2)) % kMGran == 0) s *= 2;
   return s;
 }
 
@@ -302,7 +349,7 @@ hipError_t gemm(hipStream_t st, const bf16_t* A, const bf16_t* Bm, void* out, fl
                 int M, int N, int K, Epilogue ep) {
   const bool mf = use_mfma(M, N, K);
   const int ns = splits_for(M, N, K);
-  const int kt = mf ? kMK : kTK;
+  const int kt = mf ? kMGran : kTK;
   const int kps = ((K / ns) + kt - 1) / kt * kt;
   Epilogue pe = ep;
   if (ns > 1) pe.mode = 0;
