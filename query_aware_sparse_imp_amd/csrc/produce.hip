@@ -11,8 +11,8 @@
 //
 // Two GEMM kernels.  Blocks of rows (prefill: M = B*Lq >= 64) run on the matrix cores:
 // a 128 x 128 tile per workgroup, 64 x 64 per wave as 2 x 2 v_mfma_f32_32x32x16_bf16
-// tiles, K staged through LDS 64 at a time, double-buffered, with two register stages
-// so the next K tile is in flight from memory; bf16 results leave through an LDS stage
+// tiles, K staged through LDS 64 at a time, double-buffered, with two register stages so
+// the next K tile is in flight from memory; bf16 results leave through an LDS stage
 // as 16-byte row chunks (contiguous in both the row-major activation and the Q_imp
 // layout).  Other shapes with more than 4 rows take the VALU kernel -- 32 rows x 64
 // columns per workgroup, a thread owns 1 row x 8 columns.  Up to 4 rows (decode: one
@@ -167,10 +167,16 @@ constexpr int kMThreads = 256;
 
 // 128 x 128 tiles, 64 x 64 per wave as 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.  K is staged
 // through LDS 64 at a time, double-buffered, with two register stages so the next tile
-// is in flight from memory while one is multiplied (16 MFMAs per wave between barriers).
+// is in flight from memory while one is multiplied (16 MFMAs per wave between barriers;
+// a ring of four stages measured slower).
 // LDS rows of 72 bf16 (144 B) keep the 16-byte operand reads of 16 consecutive rows on
 // distinct banks.  bf16 results leave through an LDS stage in 16-byte row chunks.
+#ifndef BUTLER_GEMM_STAGES
+#define BUTLER_GEMM_STAGES 2
+#endif
 constexpr int kM2K = 64;
+constexpr int kM2St = BUTLER_GEMM_STAGES;   // register stages of the K loop (2 or 4)
+static_assert(kM2St == 2 || kM2St == 4, "stage ring");
 constexpr int kA2S = kM2K + 8;
 
 __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
@@ -195,6 +201,8 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
   const int lo = r0 * kA2S + kc, lo_step = 32 * kA2S;
   uint4 ra0_0, ra1_0, ra2_0, ra3_0, rb0_0, rb1_0, rb2_0, rb3_0;
   uint4 ra0_1, ra1_1, ra2_1, ra3_1, rb0_1, rb1_1, rb2_1, rb3_1;
+  uint4 ra0_2, ra1_2, ra2_2, ra3_2, rb0_2, rb1_2, rb2_2, rb3_2;
+  uint4 ra0_3, ra1_3, ra2_3, ra3_3, rb0_3, rb1_3, rb2_3, rb3_3;
 #define BUTLER_GLOAD(st, kk)                                                     \
   do {                                                                           \
     ra0_##st = *reinterpret_cast<const uint4*>(ap + (kk));                      \
@@ -224,9 +232,13 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int T = (k1 - k0) / kM2K;   // even (checked on the host)
+  const int T = (k1 - k0) / kM2K;   // a multiple of kM2St (checked on the host)
   BUTLER_GLOAD(0, k0);
   BUTLER_GLOAD(1, k0 + min(1, T - 1) * kM2K);
+  if constexpr (kM2St == 4) {
+    BUTLER_GLOAD(2, k0 + min(2, T - 1) * kM2K);
+    BUTLER_GLOAD(3, k0 + min(3, T - 1) * kM2K);
+  }
   BUTLER_LSTORE(0, 0);
   __syncthreads();
   const int lr = lane & 31, lk = 8 * (lane >> 5);
@@ -243,18 +255,28 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0); \
     }                                                                                        \
   } while (0)
-  // tile t: multiply from LDS buffer t % 2, store tile t+1 (register stage (t+1) % 2) into
-  // the other buffer (past the end: written, never read), refill stage t % 2 with tile t+2
-  for (int t0 = 0; t0 < T; t0 += 2) {
-    BUTLER_MMA(0);
-    BUTLER_LSTORE(1, 1);
-    BUTLER_GLOAD(0, k0 + min(t0 + 2, T - 1) * kM2K);
-    __syncthreads();
-    BUTLER_MMA(1);
-    BUTLER_LSTORE(0, 0);
-    BUTLER_GLOAD(1, k0 + min(t0 + 3, T - 1) * kM2K);
-    __syncthreads();
+  // tile t: multiply from LDS buffer t % 2, store tile t+1 (register stage (t+1) % kM2St)
+  // into the other buffer (past the end: written, never read), refill stage t % kM2St with
+  // tile t + kM2St
+#define BUTLER_STEP(st, nx)                                                       \
+  do {                                                                            \
+    BUTLER_MMA((st) & 1);                                                         \
+    BUTLER_LSTORE(nx, ((st) & 1) ^ 1);                                            \
+    BUTLER_GLOAD(st, k0 + min(t0 + (st) + kM2St, T - 1) * kM2K);                  \
+    __syncthreads();                                                              \
+  } while (0)
+  for (int t0 = 0; t0 < T; t0 += kM2St) {
+    if constexpr (kM2St == 4) {
+      BUTLER_STEP(0, 1);
+      BUTLER_STEP(1, 2);
+      BUTLER_STEP(2, 3);
+      BUTLER_STEP(3, 0);
+    } else {
+      BUTLER_STEP(0, 1);
+      BUTLER_STEP(1, 0);
+    }
   }
+#undef BUTLER_STEP
 #undef BUTLER_MMA
 #undef BUTLER_GLOAD
 #undef BUTLER_LSTORE
@@ -312,7 +334,7 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
   }
 }
 
-constexpr int kMGran = 2 * kM2K;   // K granule of a split
+constexpr int kMGran = kM2St * kM2K;   // K granule of a split
 
 bool use_mfma(int M, int N, int K) {
   return M >= 64 && N % kMN == 0 && K % kMGran == 0;
