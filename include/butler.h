@@ -59,7 +59,7 @@ enum butler_score_mode { BUTLER_SCORE_RAW = 0, BUTLER_SCORE_SOFTVOTE = 1 };
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* butler_status_string(int status);
 
-/* ABI version, currently 3. */
+/* ABI version, currently 4. */
 int butler_abi_version(void);
 
 /*
@@ -174,9 +174,13 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
  * n_sink tokens (min_sparse_index) and a recent window of n_window tokens
  * (sliding_window).  For a row of length L_r (L, or q_pos0+i+1 for causal row i):
  *   x   = floor(L_r * budget_num / budget_den)
- *   T   = the first min(x, L_r) tokens ordered by (score descending, index ascending);
- *         -0 equals +0, NaN ranks as -inf
- *   S   = T  U  [0, min(n_sink, L_r))  U  [max(0, L_r - n_window), L_r)
+ *   F   = [0, min(n_sink, L_r))  U  [max(0, L_r - n_window), L_r)   (the forced tokens)
+ *   P   = every token of the row, or, with budget_excludes_forced != 0, the tokens not in F
+ *   T   = the first min(x, |P|) tokens of P ordered by (score descending, index
+ *         ascending); -0 equals +0, NaN ranks as -inf
+ *   S   = T  U  F
+ * (budget_excludes_forced is the reading where the budget counts only the tokens outside
+ * the sink and the window, so |S| = min(x, |P|) + |F|; the default ranks every token.)
  * Output: `idx` (when non-NULL) holds S in ascending order in the first count[row]
  * entries of its row, entries beyond that are left as they were; `bitmask` (when
  * non-NULL) holds bit (t % 32) of word t / 32 set iff t in S, for every word of the row;
@@ -190,7 +194,8 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
  *                                    exactly these scores (see butler_score); it is used
  *                                    instead of a counting pass and zero-filled again.  NULL:
  *                                    the selection counts by itself.  Multi-row (Lq > 1)
- *                                    calls ignore it, as butler_score does.
+ *                                    calls ignore it, as butler_score does.  It must be NULL
+ *                                    when budget_excludes_forced is set (BUTLER_ERR_INVALID_ARG).
  *   idx     [B, Hkv, Lq, cap]        int32   (written) -- cap >= min(L, x + n_sink + n_window)
  *   bitmask [B, Hkv, Lq, ceil(L/32)] uint32  (written)
  *   count   [B, Hkv, Lq]             int32   (written)
@@ -201,11 +206,10 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
  * per row).
  */
 int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
-                       const int32_t* keep, int budget_num,
-                       int budget_den,
-                       int n_sink, int n_window, int32_t* idx, uint32_t* bitmask,
-                       int32_t* count, int B, int Hkv, int Lq, int L, int cap, int q_pos0,
-                       int causal, void* workspace, size_t* ws_bytes);
+                       const int32_t* keep, int budget_num, int budget_den, int n_sink,
+                       int n_window, int budget_excludes_forced, int32_t* idx,
+                       uint32_t* bitmask, int32_t* count, int B, int Hkv, int Lq, int L,
+                       int cap, int q_pos0, int causal, void* workspace, size_t* ws_bytes);
 
 /*
  * butler_sparse_decode_attn -- attention over the selected tokens only.
@@ -253,10 +257,11 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
  * ring, and one softmax partial per chunk (or the two calls' workspaces).
  */
 int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t* radix_hist,
-                         int budget_num, int budget_den, int n_sink, int n_window, int32_t* idx,
-                         int32_t* count, const void* q, const void* k_cache, const void* v_cache,
-                         float* out, int B, int Hq, int Hkv, int D, int L, int L_cap, int cap,
-                         float softmax_scale, void* workspace, size_t* ws_bytes);
+                         int budget_num, int budget_den, int n_sink, int n_window,
+                         int budget_excludes_forced, int32_t* idx, int32_t* count, const void* q,
+                         const void* k_cache, const void* v_cache, float* out, int B, int Hq,
+                         int Hkv, int D, int L, int L_cap, int cap, float softmax_scale,
+                         void* workspace, size_t* ws_bytes);
 
 /*
  * butler_selection_cache -- TokenSelect README, highlights, Selection Cache: consecutive

@@ -213,26 +213,36 @@ def fixed_pc_fraction(policy: str):
     return (100 - n, 100)
 
 
-def select(scores_row, x: int, n_sink: int, n_window: int) -> np.ndarray:
+def select(scores_row, x: int, n_sink: int, n_window: int,
+           exclude_forced: bool = False) -> np.ndarray:
     """Selected token set of one row, ascending int64.
 
     Top-x tokens by (score descending, index ascending) over the row's L_r
     tokens, unioned with the sink [0, n_sink) and the window
     [L_r - n_window, L_r).  -0 is +0 and NaN is -inf for the ordering.
+    With exclude_forced (the other reading of the model card's Method and
+    Memory requirements: the budget counts only the tokens that are neither
+    sink nor window), the top-x is taken among those middle tokens only.
     """
     s = np.array(scores_row, dtype=np.float64)
     s[np.isnan(s)] = -np.inf
     s[s == 0.0] = 0.0
     L_r = s.shape[0]
-    order = np.lexsort((np.arange(L_r), -s))       # last key is primary
-    top = order[:min(max(x, 0), L_r)]
     sink = np.arange(min(n_sink, L_r))
     window = np.arange(max(0, L_r - n_window), L_r)
+    pool = np.arange(L_r)
+    if exclude_forced:
+        forced = np.zeros(L_r, bool)
+        forced[sink] = True
+        forced[window] = True
+        pool = pool[~forced]
+    order = pool[np.lexsort((pool, -s[pool]))]     # last key is primary
+    top = order[:min(max(x, 0), pool.shape[0])]
     return np.unique(np.concatenate([top, sink, window]).astype(np.int64))
 
 
 def select_rows(scores, num: int, den: int, n_sink: int, n_window: int,
-                causal: bool = False, q_pos0: int = 0):
+                causal: bool = False, q_pos0: int = 0, exclude_forced: bool = False):
     """Apply ``select`` to every row of scores [B, Hkv, Lq, L]; returns a
     nested list [B][Hkv][Lq] of index arrays."""
     B, Hkv, Lq, L = scores.shape
@@ -245,7 +255,7 @@ def select_rows(scores, num: int, den: int, n_sink: int, n_window: int,
             for i in range(Lq):
                 L_r = int(lens[i])
                 rows_g.append(select(scores[b, g, i, :L_r], budget(L_r, num, den),
-                                     n_sink, n_window))
+                                     n_sink, n_window, exclude_forced))
             rows_b.append(rows_g)
         out.append(rows_b)
     return out

@@ -48,10 +48,10 @@ _SIGS = {
     "butler_produce_queries": ([_vp, _i, _vp, _vp, _vp, _vp] + [_i] * 7 + [_f, _vp, _sz], _i),
     "butler_score": ([_vp, _i, _i, _vp, _vp, _vp, _vp, _vp] + [_i] * 11 + [_f, _vp, _sz], _i),
     "butler_project_and_score": ([_vp, _i] + [_vp] * 7 + [_i] * 9, _i),
-    "butler_select_topk": ([_vp, _vp, _vp, _vp] + [_i] * 4 + [_vp, _vp, _vp] + [_i] * 7 +
+    "butler_select_topk": ([_vp, _vp, _vp, _vp] + [_i] * 5 + [_vp, _vp, _vp] + [_i] * 7 +
                            [_vp, _sz], _i),
     "butler_selection_cache": ([_vp, _i, _vp, _vp, _vp] + [_i] * 4 + [_f], _i),
-    "butler_select_attend": ([_vp, _i, _vp, _vp] + [_i] * 4 + [_vp] * 6 + [_i] * 7 +
+    "butler_select_attend": ([_vp, _i, _vp, _vp] + [_i] * 5 + [_vp] * 6 + [_i] * 7 +
                              [_f, _vp, _sz], _i),
     "butler_expand_neighbors": ([_vp] * 5 + [_i] * 7, _i),
     "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 9 + [_f, _vp, _sz], _i),
@@ -248,9 +248,11 @@ def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n
                        n_window: int, count: torch.Tensor, idx: Optional[torch.Tensor] = None,
                        bitmask: Optional[torch.Tensor] = None, *, q_pos0: int = 0,
                        causal: bool = False, radix_hist: Optional[torch.Tensor] = None,
-                       keep: Optional[torch.Tensor] = None, stream=None) -> None:
+                       keep: Optional[torch.Tensor] = None,
+                       budget_excludes_forced: bool = False, stream=None) -> None:
     """Top-x + sink + window per row of scores [B, Hkv, Lq, L] (see butler.h).  keep: as in
-    butler_score; kept rows leave idx, bitmask and count as they were."""
+    butler_score; kept rows leave idx, bitmask and count as they were.
+    budget_excludes_forced: the top-x ranks only the tokens outside the sink and the window."""
     B, Hkv, Lq, L = scores.shape
     cap = 0
     if idx is not None:
@@ -265,8 +267,8 @@ def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n
     _check_hist(radix_hist, (B, Hkv, Lq))
     _check_keep(keep, (B, Hkv))
     args = (_ptr(scores), _ptr(radix_hist), _ptr(keep), budget_num, budget_den, n_sink, n_window,
-            _ptr(idx),
-            _ptr(bitmask), _ptr(count), B, Hkv, Lq, L, cap, q_pos0, int(causal))
+            int(bool(budget_excludes_forced)), _ptr(idx), _ptr(bitmask), _ptr(count), B, Hkv, Lq,
+            L, cap, q_pos0, int(causal))
     need = workspace_bytes(lambda ws, n: lib.butler_select_topk(_stream(stream), *args, ws, n))
     ws, n = _workspace("select", need, scores.device, (budget_num, budget_den, B, Hkv, Lq, L, cap, q_pos0, int(causal)))
     _check("butler_select_topk",
@@ -303,7 +305,8 @@ def butler_select_attend(scores: torch.Tensor, budget_num: int, budget_den: int,
                          n_window: int, count: torch.Tensor, idx: torch.Tensor, q: torch.Tensor,
                          k_cache: torch.Tensor, v_cache: torch.Tensor, out: torch.Tensor, *,
                          L: int, softmax_scale: float,
-                         radix_hist: Optional[torch.Tensor] = None, stream=None) -> None:
+                         radix_hist: Optional[torch.Tensor] = None,
+                         budget_excludes_forced: bool = False, stream=None) -> None:
     """butler_select_topk then butler_sparse_decode_attn for one decode step (see butler.h).
     scores [B, Hkv, 1, L]; idx [B, Hkv, 1, cap], count [B, Hkv, 1] (written);
     q [B, Hq, 1, D]; caches [B, Hkv, L_cap, D]; out [B, Hq, 1, D] float32."""
@@ -321,10 +324,11 @@ def butler_select_attend(scores: torch.Tensor, budget_num: int, budget_den: int,
         raise TypeError("dtype mismatch")
     _check_hist(radix_hist, (B, Hkv, 1))
     args = (_dtype_code(q), _ptr(scores), _ptr(radix_hist), budget_num, budget_den, n_sink,
-            n_window, _ptr(idx), _ptr(count), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
-            B, Hq, Hkv, D, L, L_cap, idx.shape[3], float(softmax_scale))
+            n_window, int(bool(budget_excludes_forced)), _ptr(idx), _ptr(count), _ptr(q),
+            _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Hq, Hkv, D, L, L_cap, idx.shape[3],
+            float(softmax_scale))
     need = workspace_bytes(lambda ws, n: lib.butler_select_attend(_stream(stream), *args, ws, n))
-    ws, n = _workspace("select_attend", need, q.device, tuple(args[3:7]) + tuple(args[13:]))
+    ws, n = _workspace("select_attend", need, q.device, tuple(args[3:8]) + tuple(args[14:]))
     _check("butler_select_attend",
            lib.butler_select_attend(_stream(stream), *args, ws, _byref(n)))
 

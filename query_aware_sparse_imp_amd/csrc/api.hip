@@ -64,7 +64,7 @@ const char* butler_status_string(int status) {
   }
 }
 
-int butler_abi_version(void) { return 3; }
+int butler_abi_version(void) { return 4; }
 
 int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
                         void* kimp, int B, int Hkv, int L_cap, int D, int dprime, int pos0,
@@ -166,14 +166,16 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
 }
 
 int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
-                       const int32_t* keep, int budget_num,
-                       int budget_den,
-                       int n_sink, int n_window, int32_t* idx, uint32_t* bitmask,
-                       int32_t* count, int B, int Hkv, int Lq, int L, int cap, int q_pos0,
-                       int causal, void* workspace, size_t* ws_bytes) {
+                       const int32_t* keep, int budget_num, int budget_den, int n_sink,
+                       int n_window, int budget_excludes_forced, int32_t* idx,
+                       uint32_t* bitmask, int32_t* count, int B, int Hkv, int Lq, int L,
+                       int cap, int q_pos0, int causal, void* workspace, size_t* ws_bytes) {
   if (B <= 0 || Hkv <= 0 || Lq <= 0 || L <= 0 || q_pos0 < 0) return BUTLER_ERR_INVALID_ARG;
   if (budget_num < 0 || budget_den <= 0 || n_sink < 0 || n_window < 0)
     return BUTLER_ERR_INVALID_ARG;
+  const int fo = budget_excludes_forced ? 1 : 0;
+  // the scorer's histogram counts every token's key; the forced tokens then rank below all
+  if (fo && radix_hist && Lq == 1) return BUTLER_ERR_INVALID_ARG;
   const long long rows = (long long)B * Hkv * Lq;
   if (rows > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
   // one workgroup per row holds at most 64K keys; long rows use the chunked decode
@@ -194,7 +196,7 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
   hipStream_t s = (hipStream_t)stream;
   uint32_t* hist = (Lq > 1) ? nullptr : radix_hist;   // see butler_score
   const int32_t* kp = (Lq > 1) ? nullptr : keep;
-  return finish(s, launch_select(s, scores, budget_num, budget_den, n_sink, n_window, idx,
+  return finish(s, launch_select(s, scores, budget_num, budget_den, n_sink, n_window, fo, idx,
                                  bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, hist, kp,
                                  workspace));
 }
@@ -234,13 +236,16 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
 }
 
 int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t* radix_hist,
-                         int budget_num, int budget_den, int n_sink, int n_window, int32_t* idx,
-                         int32_t* count, const void* q, const void* k_cache, const void* v_cache,
-                         float* out, int B, int Hq, int Hkv, int D, int L, int L_cap, int cap,
-                         float softmax_scale, void* workspace, size_t* ws_bytes) {
+                         int budget_num, int budget_den, int n_sink, int n_window,
+                         int budget_excludes_forced, int32_t* idx, int32_t* count, const void* q,
+                         const void* k_cache, const void* v_cache, float* out, int B, int Hq,
+                         int Hkv, int D, int L, int L_cap, int cap, float softmax_scale,
+                         void* workspace, size_t* ws_bytes) {
   if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || L_cap < L) return BUTLER_ERR_INVALID_ARG;
   if (budget_num < 0 || budget_den <= 0 || n_sink < 0 || n_window < 0) return BUTLER_ERR_INVALID_ARG;
+  const int fo = budget_excludes_forced ? 1 : 0;
+  if (fo && radix_hist) return BUTLER_ERR_INVALID_ARG;   // see butler_select_topk
   if (Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
   if (!pow2_group(Hq / Hkv) || !(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
   if (!(softmax_scale > 0.f)) return BUTLER_ERR_INVALID_ARG;
@@ -268,9 +273,9 @@ int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t*
   hipStream_t s = (hipStream_t)stream;
   if (fused)
     return finish(s, launch_select_attend(s, scores, budget_num, budget_den, n_sink, n_window,
-                                          idx, count, B, Hq, Hkv, L, cap, radix_hist, q, k_cache,
+                                          fo, idx, count, B, Hq, Hkv, L, cap, radix_hist, q, k_cache,
                                           v_cache, out, L_cap, softmax_scale, workspace));
-  hipError_t e = launch_select(s, scores, budget_num, budget_den, n_sink, n_window, idx, nullptr,
+  hipError_t e = launch_select(s, scores, budget_num, budget_den, n_sink, n_window, fo, idx, nullptr,
                                count, B, Hkv, 1, L, cap, 0, 0, radix_hist, nullptr, workspace);
   if (e != hipSuccess) return finish(s, e);
   return finish(s, launch_attn_idx(s, dtype, q, k_cache, v_cache, idx, count, out, B, Hq, Hkv, D,

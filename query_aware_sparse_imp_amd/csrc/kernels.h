@@ -36,7 +36,7 @@ hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const 
 // ---- selection ------------------------------------------------------------
 size_t select_workspace(int rows, int L, int Lq, int causal);
 hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
-                         int n_window, int32_t* idx, uint32_t* bitmask, int32_t* count,
+                         int n_window, int fo, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
                          uint32_t* hist, const int32_t* keep, void* ws);
 
@@ -56,7 +56,7 @@ hipError_t launch_attn_merge(hipStream_t s, const float* part, float* out, long 
 bool select_attend_fusable(int dtype, int D, int Hq, int Hkv, int L);
 size_t select_attend_workspace(int rows, int Hq, int Hkv, int L);
 hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int den,
-                                int n_sink, int n_window, int32_t* idx, int32_t* count, int B,
+                                int n_sink, int n_window, int fo, int32_t* idx, int32_t* count, int B,
                                 int Hq, int Hkv, int L, int cap, uint32_t* hist, const void* q,
                                 const void* k, const void* v, float* out, int L_cap,
                                 float scale, void* ws);

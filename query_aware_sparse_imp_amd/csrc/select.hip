@@ -48,10 +48,24 @@ namespace {
 
 enum { kModeNormal = 0, kModeNone = 1, kModeAll = 2 };
 
-__device__ __forceinline__ int row_mode(int L_r, int num, int den, int& k) {
+// x = floor(L_r * num / den) ranked over every token (fo == 0), or over the tokens that
+// are neither sink nor window (fo != 0: the budget excludes the forced tokens).
+__device__ __forceinline__ int row_mode(int L_r, int num, int den, int n_sink, int n_window,
+                                        int fo, int& k) {
   const long long x = (long long)L_r * num / den;
-  k = (int)min<long long>(x, (long long)L_r);
-  return k <= 0 ? kModeNone : (k >= L_r ? kModeAll : kModeNormal);
+  int pool = L_r;
+  if (fo) {
+    const int s = min(n_sink, L_r), w_lo = max(0, L_r - n_window);
+    pool = L_r - (s + (L_r - max(w_lo, s)));   // tokens outside [0, s) U [w_lo, L_r)
+  }
+  k = (int)min<long long>(x, (long long)pool);
+  return k <= 0 ? kModeNone : (k >= pool ? kModeAll : kModeNormal);
+}
+
+// Ranking key of token t: the order-preserving score key, or 0 -- below every score's key
+// (NaN and -inf rank at 0x007fffff) -- for a forced token when the budget excludes them.
+__device__ __forceinline__ uint32_t rank_key(float f, int t, int n_sink, int w_lo, int fo) {
+  return (fo && (t < n_sink || t >= w_lo)) ? 0u : score_key(f);
 }
 
 // Among hist[0..nbins), scanned from the top bin down, the bin that holds the need-th
@@ -136,7 +150,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
     const float* __restrict__ scores, int num, int den, int n_sink, int n_window,
     int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask, int32_t* __restrict__ count,
     int Lq, int L, int cap, int q_pos0, int causal, uint32_t* __restrict__ ghist,
-    const int32_t* __restrict__ keep) {
+    const int32_t* __restrict__ keep, int fo) {
   constexpr int NW = NT / 64;
   constexpr int MAXW = NT * KPT / 64;
   const long long row = blockIdx.x;
@@ -144,7 +158,8 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
   const int i = (int)(row % Lq);
   const int L_r = causal ? min(q_pos0 + i + 1, L) : L;
   int k;
-  const int mode = row_mode(L_r, num, den, k);
+  const int mode = row_mode(L_r, num, den, n_sink, n_window, fo, k);
+  const int w_lo = max(0, L_r - n_window);
   const float* s = scores + row * (long long)L;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
@@ -158,7 +173,9 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
   // all loads at once, from clamped addresses (no control flow around them)
   uint32_t key[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = score_key(s[min((int)threadIdx.x + NT * j, L_r - 1)]);
+  for (int j = 0; j < KPT; ++j)
+    key[j] = rank_key(s[min((int)threadIdx.x + NT * j, L_r - 1)], (int)threadIdx.x + NT * j,
+                      n_sink, w_lo, fo);
   auto valid = [&](int j) { return (int)threadIdx.x + NT * j < L_r; };
 
   uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;
@@ -198,7 +215,6 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
   }
 
   // ---- emit in index order -------------------------------------------------------
-  const int w_lo = max(0, L_r - n_window);
   // rank of every key equal to tau among the row's equal keys, in index order
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -371,22 +387,27 @@ __device__ __forceinline__ int load_keys(const float* s, int t0, int L, uint32_t
 // first-digit histogram, when the scorer did not produce it
 template <int KPT>
 __global__ __launch_bounds__(kMbThreads) void mb_hist1_kernel(const float* __restrict__ scores,
-                                                              int num, int den, int L, int rows,
+                                                              int num, int den, int n_sink,
+                                                              int n_window, int fo, int L,
+                                                              int rows,
                                                               uint32_t* __restrict__ ghist,
                                                               const int32_t* __restrict__ keep) {
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
   if (keep && keep[row]) return;
   int k;
-  if (row_mode(L, num, den, k) != kModeNormal) return;
+  if (row_mode(L, num, den, n_sink, n_window, fo, k) != kModeNormal) return;
   __shared__ uint32_t h[2048];
   for (int j = threadIdx.x; j < 2048; j += kMbThreads) h[j] = 0u;
   __syncthreads();
   uint32_t key[KPT];
-  const int nv = load_keys<KPT>(scores + (long long)row * L,
-                                (chunk * kMbThreads + threadIdx.x) * KPT, L, key);
+  const int t0 = (chunk * kMbThreads + threadIdx.x) * KPT;
+  const int nv = load_keys<KPT>(scores + (long long)row * L, t0, L, key);
+  const int w_lo = max(0, L - n_window);
 #pragma unroll
-  for (int j = 0; j < KPT; ++j)
+  for (int j = 0; j < KPT; ++j) {
+    if (fo && (t0 + j < n_sink || t0 + j >= w_lo)) key[j] = 0u;   // forced: below every score
     if (j < nv) atomicAdd(&h[key[j] >> 21], 1u);
+  }
   __syncthreads();
   uint32_t* gh = ghist + (long long)row * 2048;
   for (int j = threadIdx.x; j < 2048; j += kMbThreads)
@@ -592,13 +613,14 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
                                                              int n_window, int L, int rows,
                                                              const uint32_t* __restrict__ ghist,
                                                              MbWs w,
-                                                             const int32_t* __restrict__ keep) {
+                                                             const int32_t* __restrict__ keep,
+                                                             int fo) {
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
   if (keep && keep[row]) return;
   const int nchunk = gridDim.x / rows;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int k;
-  const int mode = row_mode(L, num, den, k);
+  const int mode = row_mode(L, num, den, n_sink, n_window, fo, k);
   const int c_lo = chunk * kMbThreads * KPT;
   const float* srow = scores + (long long)row * L;
   float f[KPT];
@@ -619,7 +641,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
-    key[j] = score_key(f[j]);
+    key[j] = rank_key(f[j], t, n_sink, w_lo, fo);
     const bool valid = t < L;
     const bool forced = t < n_sink || t >= w_lo;
     bool def, cand;
@@ -707,7 +729,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
     const float* __restrict__ scores, int num, int den, int n_sink, int n_window, int L,
     int rows, int cap, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask,
     int32_t* __restrict__ count, uint32_t* __restrict__ ghist, MbWs w,
-    const int32_t* __restrict__ keep, MbAttn at) {
+    const int32_t* __restrict__ keep, MbAttn at, int fo) {
   constexpr int NWD = kMbWaves * KPT;   // 64-token words per chunk
   static_assert(NWD <= 128, "two words per lane in the prefix scan");
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
@@ -729,7 +751,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
     }
   }
   int k;
-  const int mode = row_mode(L, num, den, k);
+  const int mode = row_mode(L, num, den, n_sink, n_window, fo, k);
   __shared__ uint32_t h[2048];
   __shared__ int tmp[kMbWaves];
   __shared__ int3 tmp3[kMbWaves];
@@ -843,7 +865,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
-    const uint32_t key = score_key(f[j]);
+    const uint32_t key = rank_key(f[j], t, n_sink, w_lo, fo);
     bool s = t < n_sink || t >= w_lo || mode == kModeAll;
     if (mode == kModeNormal) s = s || key > tau || (key == tau && t <= tie_cut);
     sm[j] = __ballot(s && t < L);
@@ -970,7 +992,7 @@ size_t select_attend_workspace(int rows, int Hq, int Hkv, int L) {
 }
 
 hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int den,
-                                int n_sink, int n_window, int32_t* idx, int32_t* count, int B,
+                                int n_sink, int n_window, int fo, int32_t* idx, int32_t* count, int B,
                                 int Hq, int Hkv, int L, int cap, uint32_t* hist, const void* q,
                                 const void* k, const void* v, float* out, int L_cap,
                                 float scale, void* ws) {
@@ -989,13 +1011,13 @@ hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int
     constexpr int RR = decltype(r_c)::value;
     if (!hist)
       hipLaunchKernelGGL(mb_hist1_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
-                         L, (int)rows, gh, (const int32_t*)nullptr);
+                         n_sink, n_window, fo, L, (int)rows, gh, (const int32_t*)nullptr);
     hipLaunchKernelGGL(mb_cand_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
                        n_sink, n_window, L, (int)rows, (const uint32_t*)gh, w,
-                       (const int32_t*)nullptr);
+                       (const int32_t*)nullptr, fo);
     hipLaunchKernelGGL((mb_finish_kernel<KPT, RR>), grid, dim3(kMbThreads), 0, s, scores, num,
                        den, n_sink, n_window, L, (int)rows, cap, idx, (uint32_t*)nullptr, count,
-                       gh, w, (const int32_t*)nullptr, at);
+                       gh, w, (const int32_t*)nullptr, at, fo);
   };
   auto by_r = [&](auto kpt_c) {
     switch (R) {
@@ -1021,7 +1043,7 @@ size_t select_workspace(int rows, int L, int Lq, int causal) {
 }
 
 hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
-                         int n_window, int32_t* idx, uint32_t* bitmask, int32_t* count,
+                         int n_window, int fo, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
                          uint32_t* hist, const int32_t* keep, void* ws) {
   const long long rows = (long long)B * Hkv * Lq;
@@ -1034,12 +1056,12 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
       constexpr int KPT = decltype(kpt_c)::value;
       if (!hist)
         hipLaunchKernelGGL(mb_hist1_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
-                           L, (int)rows, gh, keep);
+                           n_sink, n_window, fo, L, (int)rows, gh, keep);
       hipLaunchKernelGGL(mb_cand_kernel<KPT>, grid, dim3(kMbThreads), 0, s, scores, num, den,
-                         n_sink, n_window, L, (int)rows, (const uint32_t*)gh, w, keep);
+                         n_sink, n_window, L, (int)rows, (const uint32_t*)gh, w, keep, fo);
       hipLaunchKernelGGL((mb_finish_kernel<KPT, 0>), grid, dim3(kMbThreads), 0, s, scores, num,
                          den, n_sink, n_window, L, (int)rows, cap, idx, bitmask, count, gh, w, keep,
-                         MbAttn{});
+                         MbAttn{}, fo);
     };
     switch (kpt_for(L)) {
       case 8: run(std::integral_constant<int, 8>()); break;
@@ -1052,7 +1074,7 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
 #define BUTLER_SR(NT, KPT)                                                                 \
   hipLaunchKernelGGL((select_row_kernel<NT, KPT>), dim3((unsigned)rows), dim3(NT), 0, s,   \
                      scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,   \
-                     q_pos0, causal, hist, keep)
+                     q_pos0, causal, hist, keep, fo)
   if (L <= 1024) BUTLER_SR(64, 16);
   else if (L <= 2048) BUTLER_SR(128, 16);
   else if (L <= 4096) BUTLER_SR(256, 16);

@@ -65,7 +65,7 @@ def threshold_band(scores_row: np.ndarray, x: int, mag_row: np.ndarray) -> np.nd
 
 
 def check_select_exact(idx_gpu, count_gpu, scores_gpu_np, num, den, n_sink, n_window,
-                       causal=False, q_pos0=0, rows=None) -> None:
+                       causal=False, q_pos0=0, rows=None, exclude_forced=False) -> None:
     """GPU selection == oracle selection on the GPU's own scores (bit-exact)."""
     B, Hkv, Lq, L = scores_gpu_np.shape
     cnt = count_gpu.cpu().numpy()
@@ -74,7 +74,7 @@ def check_select_exact(idx_gpu, count_gpu, scores_gpu_np, num, den, n_sink, n_wi
     for (b, g, i) in rows:
         L_r = min(q_pos0 + i + 1, L) if causal else L
         want = oracle.select(scores_gpu_np[b, g, i, :L_r], oracle.budget(L_r, num, den),
-                             n_sink, n_window)
+                             n_sink, n_window, exclude_forced)
         assert cnt[b, g, i] == len(want), f"count {cnt[b, g, i]} != {len(want)} at {(b, g, i)}"
         if idx is not None:
             got = idx[b, g, i, :cnt[b, g, i]]

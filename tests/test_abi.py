@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert qa.butler_abi_version() == 3
+    assert qa.butler_abi_version() == 4
     assert qa.butler_status_string(0) == "BUTLER_OK"
     assert qa.butler_status_string(-3) == "BUTLER_ERR_WORKSPACE"
     assert qa.butler_status_string(123) == "BUTLER_ERR_UNKNOWN"
@@ -72,15 +72,17 @@ def test_score_validation_and_workspace_query():
 
 def test_select_validation():
     f = L.butler_select_topk
-    # cap smaller than min(L, x + sink + window)
-    assert f(None, FAKE, None, None, 1, 2, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 567, 0, 0, None,
-             None) == INV
-    assert f(None, FAKE, None, None, 1, 0, 4, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
-             None) == INV                                                  # den = 0
-    assert f(None, FAKE, None, None, 1, 2, -1, 64, FAKE, None, FAKE, 1, 8, 1, 1000, 1000, 0, 0, None,
-             None) == INV                                                  # negative sink
-    assert f(None, FAKE, None, None, 1, 2, 4, 64, None, None, FAKE, 1, 8, 1, 1000, 0, 0, 0, None,
-             None) == INV                                                  # no output
+
+    def call(*, hist=None, num=1, den=2, sink=4, fo=0, idx=FAKE, cap=1000, Lr=1000, Lq=1):
+        # stream, scores, radix_hist, keep, num, den, sink, window, excludes_forced, idx,
+        # bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, ws, ws_bytes
+        return f(None, FAKE, hist, None, num, den, sink, 64, fo, idx, None, FAKE, 1, 8, Lq, Lr,
+                 cap, 0, 0, None, None)
+    assert call(cap=567) == INV                    # cap smaller than min(L, x + sink + window)
+    assert call(den=0) == INV
+    assert call(sink=-1) == INV                    # negative sink
+    assert call(idx=None, cap=0) == INV            # no output
+    assert call(hist=FAKE, fo=1) == INV            # the scorer's histogram with forced tokens out
 
 
 def test_attention_validation_and_workspace_query():
@@ -170,8 +172,9 @@ def test_select_attend_validation_and_workspace_query():
     def call(*, dtype=1, num=1, den=2, ptrs=P, B=1, Hq=32, Hkv=8, D=128, Lr=32768,
              L_cap=32768, cap=16452, scale=0.088, ws=FAKE, n=None):
         n = n if n is not None else ctypes.c_size_t(1 << 40)
-        return f(None, dtype, ptrs[0], None, num, den, 4, 64, ptrs[1], ptrs[2], ptrs[3], ptrs[4],
-                 ptrs[5], ptrs[6], B, Hq, Hkv, D, Lr, L_cap, cap, scale, ws, ctypes.byref(n))
+        return f(None, dtype, ptrs[0], None, num, den, 4, 64, 0, ptrs[1], ptrs[2], ptrs[3],
+                 ptrs[4], ptrs[5], ptrs[6], B, Hq, Hkv, D, Lr, L_cap, cap, scale, ws,
+                 ctypes.byref(n))
     n = ctypes.c_size_t(0)
     assert call(ws=None, n=n) == OK and n.value > 0                       # size query (fused)
     fused = n.value

@@ -217,6 +217,8 @@ def test_project_and_score_matches_separate_calls(cfg, L):
     (9000, 64, 1, 2, True),      # R = 8
     (9000, 32, 1, 1, True),      # budget takes every token
     (9000, 32, 0, 1, True),      # budget 0: sink and window only
+    (32768, 32, 1, 2, "fo"),     # the budget excludes the sink and the window
+    (3001, 32, 1, 2, "fo"),
 ])
 def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
     """butler_select_attend == butler_select_topk + butler_sparse_decode_attn: idx and count
@@ -225,7 +227,10 @@ def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
     selection's workspace state carries over between calls)."""
     import query_aware_sparse_imp_amd as qa
     w = synthetic.WORKLOADS[2].replace(Hq=Hq)
-    print(f"[select+attend] L={L} Hq={Hq} budget={num}/{den} hist={use_hist}", flush=True)
+    fo = use_hist == "fo"
+    use_hist = use_hist is True
+    print(f"[select+attend] L={L} Hq={Hq} budget={num}/{den} hist={use_hist} "
+          f"budget_excludes_forced={fo}", flush=True)
     inp = to_device(synthetic.decode_layer(w, 0, L=L, with_qimp=False))
     dev = "cuda"
     k, v, q = inp["k_cache_d"], inp["v_cache_d"], inp["q_d"]
@@ -250,7 +255,7 @@ def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
     cnt_a = torch.zeros(w.B, w.Hkv, 1, dtype=torch.int32, device=dev)
     out_a = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=dev)
     qa.butler_select_topk(scores, num, den, w.n_sink, w.n_window, cnt_a, idx=idx_a,
-                          radix_hist=hist_of())
+                          radix_hist=hist_of(), budget_excludes_forced=fo)
     qa.butler_sparse_decode_attn(q, k, v, out_a, L=L, idx=idx_a, count=cnt_a,
                                  softmax_scale=w.scale)
     torch.cuda.synchronize()
@@ -259,13 +264,15 @@ def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
         cnt_b = torch.zeros_like(cnt_a)
         out_b = torch.full_like(out_a, float("nan"))
         qa.butler_select_attend(scores, num, den, w.n_sink, w.n_window, cnt_b, idx_b, q, k, v,
-                                out_b, L=L, softmax_scale=w.scale, radix_hist=hist_of())
+                                out_b, L=L, softmax_scale=w.scale, radix_hist=hist_of(),
+                                budget_excludes_forced=fo)
         torch.cuda.synchronize()
         assert torch.equal(cnt_a, cnt_b), rep
         assert torch.equal(idx_a, idx_b), rep
         d = float((out_a - out_b).abs().max())
         assert d <= 1e-4, (rep, d)
-    check_select_exact(idx_b, cnt_b, np64(scores), num, den, w.n_sink, w.n_window)
+    check_select_exact(idx_b, cnt_b, np64(scores), num, den, w.n_sink, w.n_window,
+                       exclude_forced=fo)
     ic, cc = idx_b.cpu().numpy(), cnt_b.cpu().numpy()
     err = check_attend(out_b, inp["q"], inp["k_cache"], inp["v_cache"],
                        lambda b, g, i: ic[b, g, i, :cc[b, g, i]], w.scale, w.dtype)

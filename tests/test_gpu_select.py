@@ -2,7 +2,9 @@
 
 Covers ties (small-integer scores), -0 versus +0, NaN, +-inf, ragged lengths, budgets of
 0, of exactly L and above L, sinks and windows longer than the row, and causal rows whose
-length grows with the query position, with both index-list and bitmask outputs.
+length grows with the query position, with both index-list and bitmask outputs; under
+both readings of the budget (over every token, or over the tokens outside the sink and
+the window).
 """
 import numpy as np
 import pytest
@@ -38,7 +40,7 @@ def _scores(rng, shape, kind):
     raise ValueError(kind)
 
 
-def _run(scores_np, num, den, ns, nw, causal=False, q_pos0=0):
+def _run(scores_np, num, den, ns, nw, causal=False, q_pos0=0, fo=False):
     import query_aware_sparse_imp_amd as qa
     B, Hkv, Lq, L = scores_np.shape
     x = (L * num) // den
@@ -48,7 +50,7 @@ def _run(scores_np, num, den, ns, nw, causal=False, q_pos0=0):
     bm = torch.zeros((B, Hkv, Lq, (L + 31) // 32), dtype=torch.int32, device="cuda")
     cnt = torch.zeros((B, Hkv, Lq), dtype=torch.int32, device="cuda")
     qa.butler_select_topk(s, num, den, ns, nw, cnt, idx=idx, bitmask=bm, q_pos0=q_pos0,
-                          causal=causal)
+                          causal=causal, budget_excludes_forced=fo)
     torch.cuda.synchronize()
     sets = bitmask_to_sets(bm, L)
     cnt_np, idx_np = cnt.cpu().numpy(), idx.cpu().numpy()
@@ -57,7 +59,7 @@ def _run(scores_np, num, den, ns, nw, causal=False, q_pos0=0):
             for i in range(Lq):
                 L_r = min(q_pos0 + i + 1, L) if causal else L
                 want = oracle.select(scores_np[b, g, i, :L_r].astype(np.float64),
-                                     oracle.budget(L_r, num, den), ns, nw)
+                                     oracle.budget(L_r, num, den), ns, nw, exclude_forced=fo)
                 got = idx_np[b, g, i, :cnt_np[b, g, i]]
                 assert cnt_np[b, g, i] == len(want), (L, num, den, ns, nw, b, g, i)
                 assert np.array_equal(got, want), (L, num, den, ns, nw, b, g, i)
@@ -83,3 +85,25 @@ def test_select_causal_rows():
         print(f"[select-causal] Lq={Lq} q_pos0={q_pos0} L={L}", flush=True)
         _run(_scores(rng, (2, 2, Lq, L), "ties"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0)
         _run(_scores(rng, (1, 2, Lq, L), "normal"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "special", "equal"])
+def test_select_rows_excluding_forced_match_oracle(kind):
+    """The budget counts only the tokens outside the sink and the window (|S| = x + |F| when
+    the middle holds x tokens): the per-row kernel and the chunked schedule."""
+    rng = np.random.default_rng({"normal": 31, "ties": 32, "special": 33, "equal": 34}[kind])
+    cases = [(1, 1, 2, 4, 16), (31, 1, 2, 4, 16), (100, 0, 1, 3, 5), (257, 1, 1, 4, 16),
+             (300, 9, 10, 4, 64), (4096, 1, 2, 4, 64), (4097, 1, 2, 4, 64),
+             (20011, 1, 16, 4, 128), (40000, 3, 10, 64, 1000), (100003, 1, 2, 0, 0)]
+    for (L, num, den, ns, nw) in cases:
+        print(f"[select-excl] kind={kind} L={L} budget={num}/{den} sink={ns} window={nw}",
+              flush=True)
+        _run(_scores(rng, (1, 3, 1, L), kind), num, den, ns, nw, fo=True)
+
+
+def test_select_causal_rows_excluding_forced():
+    rng = np.random.default_rng(35)
+    for (Lq, q_pos0, L) in ((37, 100, 137), (129, 1000, 1129)):
+        print(f"[select-causal-excl] Lq={Lq} q_pos0={q_pos0} L={L}", flush=True)
+        _run(_scores(rng, (1, 2, Lq, L), "ties"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0,
+             fo=True)

@@ -317,6 +317,44 @@ def test_select_invariants():
     assert ref.select(s * 3.5, 123, 4, 16).tolist() == ref.select(s, 123, 4, 16).tolist()
 
 
+def brute_select_excluding_forced(s, x, n_sink, n_window):
+    """Budget over the middle tokens only: the unique size-min(x, |M|) subset of the middle
+    tokens M whose members all dominate every other middle token, plus sink and window."""
+    L = len(s)
+    F = set(range(min(n_sink, L))) | set(range(max(0, L - n_window), L))
+    M = [t for t in range(L) if t not in F]
+    k = min(x, len(M))
+    winners = []
+    for T in itertools.combinations(M, k):
+        Ts = set(T)
+        if all(_dominates(s, t, u) for t in Ts for u in M if u not in Ts):
+            winners.append(Ts)
+    assert len(winners) == 1
+    return sorted(winners[0] | F)
+
+
+def test_select_excluding_forced_matches_brute_force_and_invariants():
+    """The other reading of the budget (the sink and the window are outside it): brute-force
+    enumeration over the middle tokens, |S| = min(x, |M|) + |F|, no sink or window means the
+    default reading, and a forced token that would have won a budget place frees it."""
+    rng = np.random.default_rng(23)
+    vals = np.array([-2.0, -1.0, -0.0, 0.0, 0.5, 1.0, 3.0, np.inf, -np.inf, np.nan])
+    for trial in range(250):
+        L = int(rng.integers(1, 12))
+        sc = vals[rng.integers(0, len(vals), L)] if trial % 2 else rng.standard_normal(L)
+        x = int(rng.integers(0, L + 2))
+        ns, nw = int(rng.integers(0, 4)), int(rng.integers(0, 4))
+        got = ref.select(sc, x, ns, nw, exclude_forced=True).tolist()
+        assert got == brute_select_excluding_forced(sc, x, ns, nw), (sc, x, ns, nw)
+        F = set(range(min(ns, L))) | set(range(max(0, L - nw), L))
+        assert len(got) == min(x, L - len(F)) + len(F)
+        assert ref.select(sc, x, 0, 0, exclude_forced=True).tolist() == ref.select(sc, x, 0, 0).tolist()
+    # the two readings differ exactly when forced tokens take budget places
+    sc = np.array([9.0, 8.0, 1.0, 2.0, 3.0, 4.0, 7.0])
+    assert ref.select(sc, 2, 1, 1).tolist() == [0, 1, 6]            # token 0 used a place
+    assert ref.select(sc, 2, 1, 1, exclude_forced=True).tolist() == [0, 1, 5, 6]
+
+
 # ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------
