@@ -48,11 +48,14 @@ def log(*a):
 class Layer:
     """Device buffers of one layer replica and the calls of one decode step."""
 
-    def __init__(self, w, layer: int, L: int, device: str):
+    def __init__(self, w, layer: int, L: int, device: str, excludes_forced: bool = False):
         import torch
         import synthetic
         import query_aware_sparse_imp_amd as qa
         self.qa, self.w, self.L = qa, w, L
+        # the budget reading where sink and window sit outside it: the scorer's first-digit
+        # histogram ranks every token, so the selection counts by itself
+        self.fo = excludes_forced
         t0 = time.time()
         inp = synthetic.decode_layer(w, layer, L=L)
         self.host = inp
@@ -83,13 +86,13 @@ class Layer:
             # the appended token's K_imp row is projected inside the scoring launch
             ("project+score", lambda: qa.butler_project_and_score(
                 self.qi, self.k, self.wk, self.kimp, self.scores, Hkv=w.Hkv, L=L,
-                radix_hist=self.hist)),
+                radix_hist=None if self.fo else self.hist)),
             # selection and attention in one call: the selection's finishing pass attends to
             # its own chunk of the row, a merge kernel combines the chunks
             ("select+attend", lambda: qa.butler_select_attend(
                 self.scores, w.budget_num, w.budget_den, w.n_sink, w.n_window, self.count,
                 self.idx, self.q, self.k, self.v, self.out, L=L, softmax_scale=w.scale,
-                radix_hist=self.hist)),
+                radix_hist=None if self.fo else self.hist, budget_excludes_forced=self.fo)),
         ]
 
     def algorithmic_bytes(self):
@@ -109,9 +112,9 @@ class Layer:
         return {"step": kimp + proj + gather + idx + qo, "call": call, "n_sel": n_sel}
 
 
-def run_config(w, L, replicas, steps, warmup, device):
+def run_config(w, L, replicas, steps, warmup, device, excludes_forced=False):
     import torch
-    layers = [Layer(w, r, L, device) for r in range(replicas)]
+    layers = [Layer(w, r, L, device, excludes_forced) for r in range(replicas)]
     # eager warm-up: allocates every workspace before capture
     for lay in layers:
         for _, fn in lay.calls():
@@ -546,9 +549,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--L", type=int, default=None)
-    ap.add_argument("--configs", default="2i,3,4,5",
-                    help="other workloads to measure: 2i prediction interval, 3 soft-voting, "
-                         "4 full depth, 5 prefill")
+    ap.add_argument("--configs", default="2i,2f,3,4,5",
+                    help="other workloads to measure: 2i prediction interval, 2f budget "
+                         "excluding sink and window, 3 soft-voting, 4 full depth, 5 prefill")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run a 256 MiB device copy first (HBM counter calibration)")
     a = ap.parse_args(argv)
@@ -601,6 +604,16 @@ def main(argv=None) -> int:
         log(f"[bench] workload {c}")
         if c == "2i":
             others["layer_decode_prediction_interval"] = run_interval(w, L, 4, (0, 1), dev)
+        elif c == "2f":
+            r, lays = run_config(w, L, 8, max(a.steps // 2, 20), max(a.warmup // 2, 4), dev,
+                                 excludes_forced=True)
+            for lay in lays:
+                lay.free()
+            others["layer_decode_budget_excludes_forced"] = {
+                "workload": f"{w.name}, the budget counts only the tokens outside the sink "
+                            f"and the window", **{k: r[k] for k in (
+                                "L", "steps_per_s", "ms_per_step", "kernel_us",
+                                "selected_per_step", "step_GBps")}}
         elif c == "3":
             others["softvote_decode"] = run_softvote(dev)
             others["softvote_decode_selection_cache"] = run_softvote(dev, cache_threshold=0.98)
