@@ -28,7 +28,10 @@ even, into its storage type.  Sources, cited by page title and section:
 
 Readings where the pages are silent (each listed in the design notes):
 GQA head h belongs to KV head h // R; the raw scorer of a GQA group is the
-group's summed Q_imp dotted with K_imp; LN is LayerNorm without affine,
+group's summed Q_imp dotted with K_imp (the model card gives Q_imp one
+vector per head but not whether a group shares its selection: ``sel_group``
+query heads share one selected set, by default all R of a KV head, and
+sel_group = 1 selects per query head); LN is LayerNorm without affine,
 eps given, biased variance; f_theta is Linear -> ReLU -> Linear without
 biases, output laid out head-major, then slot, then d'; ties in the top-x go
 to the lower token index; -0 counts as +0 and NaN as -inf; the budget is
@@ -143,20 +146,33 @@ def _causal_lengths(Lq: int, L: int, q_pos0: int, causal: bool) -> np.ndarray:
     return np.minimum(q_pos0 + np.arange(Lq) + 1, L)
 
 
-def score_raw(q_imp_slot, kimp, Hkv: int, causal: bool = False, q_pos0: int = 0) -> np.ndarray:
-    """Raw importance scores [B, Hkv, Lq, L], float32 values in float64.
+def selection_groups(Hq: int, Hkv: int, sel_group: int = 0):
+    """(Hs, gs): selection heads per batch entry and query heads per selection head.
+    Selection head j holds query heads [j*gs, (j+1)*gs) and reads KV head j*gs // R."""
+    R = Hq // Hkv
+    gs = R if not sel_group else sel_group
+    assert Hq % Hkv == 0 and R % gs == 0, "sel_group must divide Hq / Hkv"
+    return Hq // gs, gs
+
+
+def score_raw(q_imp_slot, kimp, Hkv: int, causal: bool = False, q_pos0: int = 0,
+              sel_group: int = 0) -> np.ndarray:
+    """Raw importance scores [B, Hs, Lq, L], float32 values in float64.
 
     q_imp_slot: [B, Hq, Lq, d'] (the consumer's slot); kimp: [B, Hkv, L, d'].
-    Score of token t for KV head g is (sum of Q_imp over g's query heads)
-    . K_imp[t], summed in float64 and rounded once to float32.  For a causal
-    row i (absolute position q_pos0 + i) tokens after it score -inf.
+    Score of token t for selection head j is (sum of Q_imp over j's query
+    heads) . K_imp[t] of their KV head, summed in float64 and rounded once to
+    float32.  By default j is a KV head and its query heads are its GQA group.
+    For a causal row i (absolute position q_pos0 + i) tokens after it score -inf.
     """
     q = np.asarray(q_imp_slot, np.float64)
     k = np.asarray(kimp, np.float64)
     B, Hq, Lq, dp = q.shape
+    Hs, gs = selection_groups(Hq, Hkv, sel_group)
     R = Hq // Hkv
-    qbar = q.reshape(B, Hkv, R, Lq, dp).sum(axis=2)            # [B, Hkv, Lq, d']
-    s = round_to_f32(np.einsum("bgqi,bgti->bgqt", qbar, k))
+    qbar = q.reshape(B, Hs, gs, Lq, dp).sum(axis=2)             # [B, Hs, Lq, d']
+    kv_of = np.arange(Hs) * gs // R                              # KV head of each selection head
+    s = round_to_f32(np.einsum("bgqi,bgti->bgqt", qbar, k[:, kv_of]))
     lens = _causal_lengths(Lq, k.shape[2], q_pos0, causal)
     t = np.arange(k.shape[2])
     s[:, :, t[None, :] >= lens[:, None]] = -np.inf
@@ -172,18 +188,20 @@ def softmax_last(z) -> np.ndarray:
 
 
 def score_softvote(q, k, Hkv: int, scale: float, causal: bool = False,
-                   q_pos0: int = 0) -> np.ndarray:
-    """Soft-voting scores [B, Hkv, Lq, L] (TokenSelect README, highlights).
+                   q_pos0: int = 0, sel_group: int = 0) -> np.ndarray:
+    """Soft-voting scores [B, Hs, Lq, L] (TokenSelect README, highlights).
 
     q: [B, Hq, Lq, D]; k: [B, Hkv, L, D].  For each query head h the
     criticality of token t is its logit q_h . k_t * scale; each head's
     criticalities are normalised by a softmax over all cached tokens (the
-    causal prefix for a causal row); the score of t for KV head g is the sum
-    of those probabilities over g's query heads, rounded to float32.
+    causal prefix for a causal row); the score of t for selection head j is
+    the sum of those probabilities over j's query heads (by default the GQA
+    group of a KV head), rounded to float32.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     B, Hq, Lq, D = q.shape
+    Hs, gs = selection_groups(Hq, Hkv, sel_group)
     R = Hq // Hkv
     L = k.shape[2]
     kk = np.repeat(k, R, axis=1)                                 # [B, Hq, L, D]
@@ -192,7 +210,7 @@ def score_softvote(q, k, Hkv: int, scale: float, causal: bool = False,
     t = np.arange(L)
     z[:, :, t[None, :] >= lens[:, None]] = -np.inf
     p = softmax_last(z)
-    s = round_to_f32(p.reshape(B, Hkv, R, Lq, L).sum(axis=2))
+    s = round_to_f32(p.reshape(B, Hs, gs, Lq, L).sum(axis=2))
     s[:, :, t[None, :] >= lens[:, None]] = -np.inf
     return s
 
@@ -278,43 +296,48 @@ def attend(q_heads, k_rows, v_rows, scale: float) -> np.ndarray:
     return p @ v
 
 
-def sparse_decode_attn(q, k_cache, v_cache, sel, scale: float) -> np.ndarray:
+def sparse_decode_attn(q, k_cache, v_cache, sel, scale: float,
+                       sel_group: int = 0) -> np.ndarray:
     """Decode attention [B, Hq, D] for one query token per head.
 
-    q: [B, Hq, D]; caches [B, Hkv, L_cap, D]; sel[b][g] is the ascending
-    selected index array of KV head g.  Query head h reads KV head h // R.
+    q: [B, Hq, D]; caches [B, Hkv, L_cap, D]; sel[b][j] is the ascending
+    selected index array of selection head j (by default KV head j).  Query
+    head h attends to the set of selection head h // sel_group over the rows
+    of KV head h // R.
     """
     q = np.asarray(q, np.float64)
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
     R = Hq // Hkv
+    Hs, gs = selection_groups(Hq, Hkv, sel_group)
     out = np.zeros((B, Hq, D))
     for b in range(B):
-        for g in range(Hkv):
-            idx = np.asarray(sel[b][g], np.int64)
-            out[b, g * R:(g + 1) * R] = attend(q[b, g * R:(g + 1) * R],
-                                               np.asarray(k_cache[b, g])[idx],
-                                               np.asarray(v_cache[b, g])[idx], scale)
+        for h in range(Hq):
+            idx = np.asarray(sel[b][h // gs], np.int64)
+            out[b, h] = attend(q[b, h][None, :], np.asarray(k_cache[b, h // R])[idx],
+                               np.asarray(v_cache[b, h // R])[idx], scale)[0]
     return out
 
 
 def masked_attention_rows(q, k_cache, v_cache, sel_rows, scale: float,
-                          rows: Optional[list] = None) -> dict:
+                          rows: Optional[list] = None, sel_group: int = 0) -> dict:
     """Prefill attention for selected query rows.
 
-    q: [B, Hq, Lq, D]; sel_rows[b][g][i] is row i's selected set.  Returns
-    {(b, h, i): o[D]} for every (b, h, i) in ``rows`` (all rows if None).
+    q: [B, Hq, Lq, D]; sel_rows[b][j][i] is row i's selected set of selection
+    head j (by default KV head j).  Returns {(b, h, i): o[D]} for every
+    (b, h, i) in ``rows`` (all rows if None).
     """
     q = np.asarray(q, np.float64)
     B, Hq, Lq, D = q.shape
     Hkv = k_cache.shape[1]
     R = Hq // Hkv
+    Hs, gs = selection_groups(Hq, Hkv, sel_group)
     if rows is None:
         rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(Lq)]
     out = {}
     for (b, h, i) in rows:
         g = h // R
-        idx = np.asarray(sel_rows[b][g][i], np.int64)
+        idx = np.asarray(sel_rows[b][h // gs][i], np.int64)
         out[(b, h, i)] = attend(q[b, h, i][None, :], np.asarray(k_cache[b, g])[idx],
                                 np.asarray(v_cache[b, g])[idx], scale)[0]
     return out
@@ -334,12 +357,13 @@ def dense_decode_attn(q, k_cache, v_cache, L: int, scale: float) -> np.ndarray:
 def decode_layer_step(*, q, k_cache, v_cache, L: int, num: int, den: int,
                       n_sink: int, n_window: int, scale: float, Hkv: int,
                       mode: str = "raw", q_imp_slot=None, kimp=None,
-                      dense: bool = False) -> dict:
+                      dense: bool = False, sel_group: int = 0) -> dict:
     """Score -> select -> attend for one decode layer at context L.
 
     q: [B, Hq, D]; raw mode needs q_imp_slot [B, Hq, d'] and kimp
     [B, Hkv, >=L, d']; softvote mode scores with q against the keys.
-    Returns scores [B, Hkv, L], the selected sets and the output [B, Hq, D].
+    Returns scores [B, Hs, L], the selected sets and the output [B, Hq, D]
+    (Hs selection heads of sel_group query heads each; see selection_groups).
     """
     q = np.asarray(q, np.float64)
     B, Hq, D = q.shape
@@ -351,34 +375,38 @@ def decode_layer_step(*, q, k_cache, v_cache, L: int, num: int, den: int,
                 "out": sparse_decode_attn(q, kc, vc, sel, scale)}
     if mode == "raw":
         s = score_raw(np.asarray(q_imp_slot, np.float64)[:, :, None, :],
-                      np.asarray(kimp, np.float64)[:, :, :L], Hkv)[:, :, 0]
+                      np.asarray(kimp, np.float64)[:, :, :L], Hkv,
+                      sel_group=sel_group)[:, :, 0]
     else:
-        s = score_softvote(q[:, :, None, :], kc, Hkv, scale)[:, :, 0]
+        s = score_softvote(q[:, :, None, :], kc, Hkv, scale, sel_group=sel_group)[:, :, 0]
     x = budget(L, num, den)
-    sel = [[select(s[b, g], x, n_sink, n_window) for g in range(Hkv)] for b in range(B)]
-    return {"scores": s, "sel": sel, "out": sparse_decode_attn(q, kc, vc, sel, scale)}
+    sel = [[select(s[b, j], x, n_sink, n_window) for j in range(s.shape[1])]
+           for b in range(B)]
+    return {"scores": s, "sel": sel,
+            "out": sparse_decode_attn(q, kc, vc, sel, scale, sel_group=sel_group)}
 
 
-def selection_cache(q, q_ref, Hkv: int, threshold: float):
+def selection_cache(q, q_ref, Hkv: int, threshold: float, sel_group: int = 0):
     """TokenSelect README, highlights, Selection Cache: consecutive similar queries share
-    one token selection.  q, q_ref: [B, Hq, D] (one decode step).  Per (b, KV head), the
-    cosine similarity of the group's R query heads stacked into one vector (float64; 0
-    when either vector is zero) with the reference the cached selection was made for.
-    Returns (keep [B, Hkv] bool: cos >= threshold, new q_ref: q where not kept, cos)."""
+    one token selection.  q, q_ref: [B, Hq, D] (one decode step).  Per (b, selection
+    head) -- by default a KV head and its R query heads -- the cosine similarity of the
+    head's query heads stacked into one vector (float64; 0 when either vector is zero)
+    with the reference the cached selection was made for.
+    Returns (keep [B, Hs] bool: cos >= threshold, new q_ref: q where not kept, cos)."""
     q = np.asarray(q, dtype=np.float64)
     ref = np.asarray(q_ref, dtype=np.float64)
     B, Hq, D = q.shape
-    R = Hq // Hkv
-    a = q.reshape(B, Hkv, R * D)
-    c = ref.reshape(B, Hkv, R * D)
+    Hs, gs = selection_groups(Hq, Hkv, sel_group)
+    a = q.reshape(B, Hs, gs * D)
+    c = ref.reshape(B, Hs, gs * D)
     na = np.sqrt((a * a).sum(-1))
     nc = np.sqrt((c * c).sum(-1))
     dot = (a * c).sum(-1)
     den = na * nc
     cos = np.where(den > 0, dot / np.where(den > 0, den, 1.0), 0.0)
     keep = cos >= threshold
-    new_ref = np.where(keep[:, :, None, None], c.reshape(B, Hkv, R, D),
-                       a.reshape(B, Hkv, R, D)).reshape(B, Hq, D)
+    new_ref = np.where(keep[:, :, None, None], c.reshape(B, Hs, gs, D),
+                       a.reshape(B, Hs, gs, D)).reshape(B, Hq, D)
     return keep, new_ref, cos
 
 

@@ -402,6 +402,125 @@ def test_gqa_head_to_kv_head_map():
 
 
 # ---------------------------------------------------------------------------
+# selection heads (sel_group query heads share one selected set)
+# ---------------------------------------------------------------------------
+
+def _sel_heads_by_hand(Hq, Hkv, gs):
+    """[(query heads, KV head)] of every selection head, listed one by one."""
+    R = Hq // Hkv
+    out = []
+    for j in range(Hq // gs):
+        heads = [j * gs + r for r in range(gs)]
+        kvs = {h // R for h in heads}
+        assert len(kvs) == 1                       # a selection head never spans KV heads
+        out.append((heads, kvs.pop()))
+    return out
+
+
+@pytest.mark.parametrize("Hq,Hkv,gs", [(6, 3, 1), (8, 2, 2), (8, 2, 1), (8, 2, 4)])
+def test_score_raw_per_selection_head_matches_exact_dots(Hq, Hkv, gs):
+    """Raw scores of each selection head: the exact dot product of its own query heads'
+    summed Q_imp with its KV head's K_imp (Fraction arithmetic, rounded once)."""
+    rng = np.random.default_rng(40 + gs)
+    B, Lq, L, dp = 2, 2, 7, 4
+    q = bf16_grid(rng, (B, Hq, Lq, dp))
+    k = bf16_grid(rng, (B, Hkv, L, dp))
+    got = ref.score_raw(q, k, Hkv, sel_group=gs)
+    groups = _sel_heads_by_hand(Hq, Hkv, gs)
+    assert got.shape == (B, len(groups), Lq, L)
+    for b in range(B):
+        for j, (heads, kv) in enumerate(groups):
+            for i in range(Lq):
+                for t in range(L):
+                    exact = sum(Fraction(float(q[b, h, i, c])) * Fraction(float(k[b, kv, t, c]))
+                                for h in heads for c in range(dp))
+                    assert got[b, j, i, t] == frac_rne(exact, 24), (b, j, i, t)
+    if gs == Hq // Hkv:
+        assert np.array_equal(got, ref.score_raw(q, k, Hkv))    # the default grouping
+
+
+def test_softvote_per_query_head_is_each_heads_softmax():
+    """sel_group = 1: the soft-voting score of query head h is h's own softmax over the
+    keys of KV head h // R (torch softmax), and it ranks tokens as h's logits do."""
+    rng = np.random.default_rng(44)
+    B, Hq, Hkv, L, D = 1, 4, 2, 30, 8
+    q = bf16_grid(rng, (B, Hq, 1, D))
+    k = bf16_grid(rng, (B, Hkv, L, D))
+    s = ref.score_softvote(q, k, Hkv, 0.35, sel_group=1)
+    assert s.shape == (B, Hq, 1, L)
+    for h in range(Hq):
+        z = torch.from_numpy(q[0, h, 0] @ k[0, h // 2].T * 0.35)
+        np.testing.assert_array_equal(s[0, h, 0], torch.softmax(z, -1).float().double().numpy())
+        order_s = np.lexsort((np.arange(L), -s[0, h, 0]))
+        order_z = np.lexsort((np.arange(L), -z.numpy()))
+        assert np.array_equal(order_s, order_z)
+    # two heads per set: the sum of the two softmaxes
+    s2 = ref.score_softvote(q, k, Hkv, 0.35, sel_group=2)
+    np.testing.assert_allclose(s2[0, :, 0].sum(-1), 2.0, atol=1e-6)
+
+
+def test_attention_per_selection_head_matches_masked_sdpa():
+    """Every query head attends over its own selection head's set: torch's
+    scaled_dot_product_attention with a per-head boolean mask gives the same output
+    (decode rows, and prefill rows through masked_attention_rows)."""
+    rng = np.random.default_rng(45)
+    B, Hq, Hkv, L, D = 2, 8, 2, 24, 8
+    k = rng.standard_normal((B, Hkv, L, D)); v = rng.standard_normal((B, Hkv, L, D))
+    q = rng.standard_normal((B, Hq, D))
+    for gs in (1, 2):
+        Hs = Hq // gs
+        sel = [[np.sort(rng.choice(L, size=int(rng.integers(1, L)), replace=False))
+                for _ in range(Hs)] for _ in range(B)]
+        got = ref.sparse_decode_attn(q, k, v, sel, 0.3, sel_group=gs)
+        mask = torch.zeros(B, Hq, 1, L, dtype=torch.bool)
+        for b in range(B):
+            for h in range(Hq):
+                mask[b, h, 0, sel[b][h // gs]] = True
+        K = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1))
+        V = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1))
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[:, :, None, :], K, V, attn_mask=mask, scale=0.3)[:, :, 0]
+        np.testing.assert_allclose(got, want.numpy(), rtol=0, atol=1e-12)
+        rows = ref.masked_attention_rows(q[:, :, None, :], k, v,
+                                         [[[sel[b][j]] for j in range(Hs)] for b in range(B)],
+                                         0.3, sel_group=gs)
+        for (b, h, i), o in rows.items():
+            np.testing.assert_allclose(o, want[b, h].numpy(), rtol=0, atol=1e-12)
+
+
+def test_selection_cache_per_query_head():
+    """sel_group = 1: one cosine per query head (numpy's norm and dot on each head)."""
+    rng = np.random.default_rng(46)
+    a = rng.standard_normal((2, 4, 8)); c = rng.standard_normal((2, 4, 8))
+    c[1, 2] = a[1, 2] * 2.0                         # this head is kept at any threshold <= 1
+    keep, new_ref, cos = oracle.selection_cache(a, c, 2, 0.999, sel_group=1)
+    want = np.array([[np.dot(a[b, h], c[b, h]) / (np.linalg.norm(a[b, h]) * np.linalg.norm(c[b, h]))
+                      for h in range(4)] for b in range(2)])
+    assert cos.shape == (2, 4) and np.allclose(cos, want, rtol=0, atol=1e-15)
+    assert keep[1, 2] and keep.sum() == 1
+    assert np.array_equal(new_ref[1, 2], c[1, 2]) and np.array_equal(new_ref[0], a[0])
+
+
+def test_decode_step_per_query_head_sets_differ_and_contain_forced():
+    """Per-query-head selection on a layer whose two heads of a group prefer different
+    tokens: the two sets differ, each holds its sink and window, and the group's shared
+    set (the default) is neither of them."""
+    d = _tiny_layer(seed=47, L=48)
+    d["qi"][0, 1] = -d["qi"][0, 0]                # head 1 ranks in the reverse order of head 0
+    kimp = ref.project_keys(d["k"], d["wk"], "bf16")
+    kw = dict(q=d["q"], k_cache=d["k"], v_cache=d["v"], L=48, num=1, den=4, n_sink=2,
+              n_window=3, scale=0.25, Hkv=d["Hkv"], mode="raw", q_imp_slot=d["qi"], kimp=kimp)
+    per = ref.decode_layer_step(sel_group=1, **kw)
+    grp = ref.decode_layer_step(**kw)
+    s0, s1 = set(per["sel"][0][0].tolist()), set(per["sel"][0][1].tolist())
+    assert s0 != s1
+    for S in (s0, s1):
+        assert {0, 1, 45, 46, 47} <= S and 12 <= len(S) <= 17
+    assert set(grp["sel"][0][0].tolist()) not in (s0, s1)
+    assert per["scores"].shape == (1, 4, 48) and grp["scores"].shape == (1, 2, 48)
+
+
+# ---------------------------------------------------------------------------
 # whole decode step: invariants the method's definition fixes
 # ---------------------------------------------------------------------------
 
@@ -499,6 +618,18 @@ def test_mutations_are_caught(monkeypatch):
         return good_sr(q[:, ::R].repeat(R, axis=1) / R, k, Hkv, causal, q_pos0)
     _pins_fail(monkeypatch, "score_raw", score_first_head_only,
                test_score_raw_matches_exact_group_sums_and_causal_mask)
+    monkeypatch.setattr(ref, "score_raw", good_sr)
+
+    def score_kv_by_selection_index(q, k, Hkv, causal=False, q_pos0=0, sel_group=0):
+        # a plausible slip: selection head j reads KV head j % Hkv instead of its own
+        q = np.asarray(q, np.float64)
+        Hq = q.shape[1]
+        gs = sel_group or Hq // Hkv
+        Hs = Hq // gs
+        kk = np.asarray(k, np.float64)[:, np.arange(Hs) % Hkv]
+        return good_sr(q, kk, Hs, causal, q_pos0)
+    _pins_fail(monkeypatch, "score_raw", score_kv_by_selection_index,
+               lambda: test_score_raw_per_selection_head_matches_exact_dots(8, 2, 1))
     monkeypatch.setattr(ref, "score_raw", good_sr)
 
     good_att = ref.attend
