@@ -33,6 +33,18 @@
  *     differently: give it its own buffer, or zero-fill the shared one first.  Two calls
  *     that share a workspace must not run concurrently.
  *   - Results are deterministic: the same inputs give bitwise identical outputs.
+ *   - Selection heads.  The model card (Method) gives Q_imp one d'-vector per attention
+ *     head, and does not say whether the heads of a GQA group share one selected set.
+ *     Calls that take `sel_group` let the caller choose: a selected set belongs to
+ *     sel_group consecutive query heads.  sel_group = 0 means the whole group of
+ *     R = Hq / Hkv query heads of a KV head (one set per (b, KV head), the default);
+ *     any divisor of R is accepted, and sel_group = 1 gives every query head its own set.
+ *     Hs = Hq / sel_group (Hkv when sel_group = 0) is the number of selection heads per
+ *     batch entry.  Selection head j covers query heads [j*sel_group, (j+1)*sel_group) and
+ *     reads KV head j*sel_group / R.  Scores, radix histograms, keep flags, index lists,
+ *     bitmasks and counts are laid out per selection head ([B, Hs, ...]); caches and K_imp
+ *     stay per KV head.  butler_select_topk and butler_expand_neighbors work per row and
+ *     take Hs directly.
  */
 #ifndef BUTLER_H
 #define BUTLER_H
@@ -59,7 +71,7 @@ enum butler_score_mode { BUTLER_SCORE_RAW = 0, BUTLER_SCORE_SOFTVOTE = 1 };
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* butler_status_string(int status);
 
-/* ABI version, currently 4. */
+/* ABI version, currently 5. */
 int butler_abi_version(void);
 
 /*
@@ -103,28 +115,29 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
                            int G, int dprime, float ln_eps, void* workspace, size_t* ws_bytes);
 
 /*
- * butler_score -- importance score of every cached token, per KV head and query row.
+ * butler_score -- importance score of every cached token, per selection head and query row.
  *
  * BUTLER_SCORE_RAW (model card, Method: the consumer scores every cached token with its
  * slot of Q_imp against K_imp):
  *   q     = q_imp [B, Hq, G, Lq, d'], the consumer reads slot `slot`
  *   keys  = kimp  [B, Hkv, L_cap, d']
- *   score[b, g, i, t] = (sum over the R = Hq/Hkv query heads h of group g of
- *                        Q_imp[b, h, slot, i, :]) . K_imp[b, g, t, :]
+ *   score[b, j, i, t] = (sum over the query heads h of selection head j of
+ *                        Q_imp[b, h, slot, i, :]) . K_imp[b, kv(j), t, :]
+ *   (kv(j) = j * sel_group / R, the KV head of those query heads)
  *   computed exactly (float64 products and sums of the stored values) and rounded once
  *   to float32.  dk = d'.
  * BUTLER_SCORE_SOFTVOTE (TokenSelect README, highlights: per-head Q.K criticality,
  * normalised by a softmax per head, summed over heads):
  *   q     = [B, Hq, Lq, D] attention queries, keys = k_cache [B, Hkv, L_cap, D]
- *   score[b, g, i, t] = sum_{h in g} softmax_t(softmax_scale * q_h . k_t)
+ *   score[b, j, i, t] = sum_{h in j} softmax_t(softmax_scale * q_h . k_t), k_t of KV head kv(j)
  *   float32 arithmetic; the softmax runs over all scored tokens of the row.  dk = D,
  *   G and slot are ignored.
  * Causal rows (causal != 0): query row i sits at absolute position q_pos0 + i and scores
  * only the tokens t <= q_pos0 + i; the others are written as -inf.  Non-causal rows score
  * tokens [0, L).
  *
- *   scores     [B, Hkv, Lq, L]     float32 (written)
- *   radix_hist [B, Hkv, Lq, 2048]  uint32, optional (NULL = none), used by single-row
+ *   scores     [B, Hs, Lq, L]      float32 (written)
+ *   radix_hist [B, Hs, Lq, 2048]   uint32, optional (NULL = none), used by single-row
  *              (Lq == 1) calls only; multi-row calls leave it untouched.  When used, the
  *              count of every written score (t < row length) is added to bin key >> 21,
  *              where key is the score's order-preserving 32-bit key (bits of the float
@@ -132,16 +145,17 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
  *              sign bit set).  The caller zero-fills it before its first use; passing it
  *              on to butler_select_topk spares the selection one pass over the scores, and
  *              butler_select_topk leaves it zero-filled again.
- *   keep       [B, Hkv]            int32, optional (NULL = none), single-row calls only:
- *              rows of a (b, KV head) with keep != 0 are skipped -- their scores (and
- *              radix_hist) are left as they were (see butler_selection_cache).
- * RAW: d' in {16, 32}; SOFTVOTE: D in {64, 128}, Lq == 1 (decode); R in {1, 2, 4, 8}.
+ *   keep       [B, Hs]             int32, optional (NULL = none), single-row calls only:
+ *              rows of a (b, selection head) with keep != 0 are skipped -- their scores
+ *              (and radix_hist) are left as they were (see butler_selection_cache).
+ * sel_group: query heads per selected set (see "Selection heads" above; 0 = R).
+ * RAW: d' in {16, 32}, B * Hs <= 65535; SOFTVOTE: D in {64, 128}, Lq == 1 (decode);
+ * R in {1, 2, 4, 8}.
  * workspace: SOFTVOTE keeps per-token logits and per-block softmax partials.
  */
 int butler_score(void* stream, int mode, int dtype, const void* q, const void* keys,
                  float* scores, uint32_t* radix_hist, const int32_t* keep, int B, int Hq,
-                 int Hkv, int G, int slot,
-                 int Lq, int L,
+                 int Hkv, int sel_group, int G, int slot, int Lq, int L,
                  int L_cap, int dk, int q_pos0, int causal, float softmax_scale,
                  void* workspace, size_t* ws_bytes);
 
@@ -157,18 +171,18 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
  *   w_k        [D, d']              dtype (read)
  *   kimp       [B, Hkv, L_cap, d']  dtype: row L - 1 written (even for kept rows), rows
  *                                   0 .. L-2 read
- *   scores     [B, Hkv, 1, L]       float32 (written)
- *   radix_hist, keep                as in butler_score (single-row call)
- * D in {64, 128}; d' in {16, 32}; R in {1, 2, 4, 8}; B * Hkv <= 65535; kimp must not alias
+ *   scores     [B, Hs, 1, L]        float32 (written)
+ *   radix_hist, keep, sel_group     as in butler_score (single-row call)
+ * D in {64, 128}; d' in {16, 32}; R in {1, 2, 4, 8}; B * Hs <= 65535; kimp must not alias
  * k_cache or w_k.  No workspace.
  */
 int butler_project_and_score(void* stream, int dtype, const void* q_imp, const void* k_cache,
                              const void* w_k, void* kimp, float* scores, uint32_t* radix_hist,
-                             const int32_t* keep, int B, int Hq, int Hkv, int G, int slot,
-                             int L, int L_cap, int D, int dprime);
+                             const int32_t* keep, int B, int Hq, int Hkv, int sel_group, int G,
+                             int slot, int L, int L_cap, int D, int dprime);
 
 /*
- * butler_select_topk -- fixed-budget top-x + sink + window, per KV head and query row.
+ * butler_select_topk -- fixed-budget top-x + sink + window, per selection head and query row.
  * Model card, Method and Memory requirements: keep the top-x tokens under a fixed
  * budget (fixed_<N>pc keeps (100-N)% of the tokens), augmented by a sink prefix of
  * n_sink tokens (min_sparse_index) and a recent window of n_window tokens
@@ -186,19 +200,20 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
  * non-NULL) holds bit (t % 32) of word t / 32 set iff t in S, for every word of the row;
  * count[row] = |S|.  At least one of idx, bitmask must be non-NULL.
  *
- *   scores  [B, Hkv, Lq, L]          float32 (read)
- *   keep    [B, Hkv]                 int32, optional (NULL = none), single-row calls only:
+ *   scores  [B, Hs, Lq, L]           float32 (read)
+ *   keep    [B, Hs]                  int32, optional (NULL = none), single-row calls only:
  *                                    rows with keep != 0 are skipped; their idx, bitmask
  *                                    and count keep the previous selection.
- *   radix_hist [B, Hkv, Lq, 2048]    uint32, optional: the histogram butler_score built for
+ *   radix_hist [B, Hs, Lq, 2048]     uint32, optional: the histogram butler_score built for
  *                                    exactly these scores (see butler_score); it is used
  *                                    instead of a counting pass and zero-filled again.  NULL:
  *                                    the selection counts by itself.  Multi-row (Lq > 1)
  *                                    calls ignore it, as butler_score does.  It must be NULL
  *                                    when budget_excludes_forced is set (BUTLER_ERR_INVALID_ARG).
- *   idx     [B, Hkv, Lq, cap]        int32   (written) -- cap >= min(L, x + n_sink + n_window)
- *   bitmask [B, Hkv, Lq, ceil(L/32)] uint32  (written)
- *   count   [B, Hkv, Lq]             int32   (written)
+ *   idx     [B, Hs, Lq, cap]         int32   (written) -- cap >= min(L, x + n_sink + n_window)
+ *   bitmask [B, Hs, Lq, ceil(L/32)]  uint32  (written)
+ *   count   [B, Hs, Lq]              int32   (written)
+ * Hs: selection heads per batch entry (Hkv, or Hq / sel_group; see "Selection heads").
  * 0 <= budget_num, 1 <= budget_den, n_sink >= 0, n_window >= 0.  Rows of a causal or
  * multi-row (Lq > 1) call hold at most 65536 tokens; single-row decode calls up to 2^23.
  * workspace: none for causal / multi-row calls and rows up to 4096 tokens; otherwise a
@@ -208,20 +223,21 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
 int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
                        const int32_t* keep, int budget_num, int budget_den, int n_sink,
                        int n_window, int budget_excludes_forced, int32_t* idx,
-                       uint32_t* bitmask, int32_t* count, int B, int Hkv, int Lq, int L,
+                       uint32_t* bitmask, int32_t* count, int B, int Hs, int Lq, int L,
                        int cap, int q_pos0, int causal, void* workspace, size_t* ws_bytes);
 
 /*
  * butler_sparse_decode_attn -- attention over the selected tokens only.
  * Model card, intro and Method: attention reads only the selected subset of the full
- * (never evicted) KV cache.  For query head h (KV head g = h / R) of row i:
+ * (never evicted) KV cache.  For query head h (selection head j = h / sel_group, KV head
+ * h / R) of row i:
  *   o[b, h, i, :] = sum_{t in S} softmax_t(softmax_scale * q . k_t) v_t
  * with float32 logits, float32 online softmax and float32 accumulation.
  *
- * Lq == 1 (decode): S comes from idx [B, Hkv, 1, cap] / count [B, Hkv, 1] as written by
+ * Lq == 1 (decode): S comes from idx [B, Hs, 1, cap] / count [B, Hs, 1] as written by
  *   butler_select_topk (or butler_expand_neighbors); the list is split over workgroups
  *   and a second kernel merges the partial results in a fixed order.
- * Lq > 1 (chunked prefill): S of row i comes from bitmask [B, Hkv, Lq, ceil(L/32)];
+ * Lq > 1 (chunked prefill): S of row i comes from bitmask [B, Hs, Lq, ceil(L/32)];
  *   query row i sits at absolute position q_pos0 + i; only tokens t <= q_pos0 + i may
  *   be selected.
  *
@@ -229,6 +245,7 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
  *   k_cache [B, Hkv, L_cap, D]  dtype
  *   v_cache [B, Hkv, L_cap, D]  dtype
  *   out     [B, Hq, Lq, D]      float32 (written)
+ * sel_group: query heads per selected set (see "Selection heads"; 0 = R).
  * An empty selected set is an error of the caller (the window always holds the newest
  * token); its output row is written as zeros.  Selected indices must be < L <= L_cap.
  * workspace: per-split softmax partials (decode).
@@ -236,8 +253,9 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
 int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* idx, const int32_t* count,
                               const uint32_t* bitmask, float* out, int B, int Hq, int Hkv,
-                              int D, int Lq, int L, int L_cap, int cap, int q_pos0,
-                              float softmax_scale, void* workspace, size_t* ws_bytes);
+                              int sel_group, int D, int Lq, int L, int L_cap, int cap,
+                              int q_pos0, float softmax_scale, void* workspace,
+                              size_t* ws_bytes);
 
 /*
  * butler_select_attend -- one decode step's selection and sparse attention in one call:
@@ -250,9 +268,10 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
  * The attention output equals the separate calls' up to float32 rounding order; idx and
  * count are identical.
  *
- *   scores [B, Hkv, 1, L] float32, radix_hist [B, Hkv, 1, 2048] optional (as in
- *   butler_select_topk), idx [B, Hkv, 1, cap] int32 and count [B, Hkv, 1] int32 (written),
- *   q [B, Hq, 1, D], k_cache / v_cache [B, Hkv, L_cap, D] (dtype), out [B, Hq, 1, D] float32.
+ *   scores [B, Hs, 1, L] float32, radix_hist [B, Hs, 1, 2048] optional (as in
+ *   butler_select_topk), idx [B, Hs, 1, cap] int32 and count [B, Hs, 1] int32 (written),
+ *   q [B, Hq, 1, D], k_cache / v_cache [B, Hkv, L_cap, D] (dtype), out [B, Hq, 1, D] float32;
+ *   sel_group as in butler_sparse_decode_attn.
  * Limits as in the two calls; L <= 2^23.  workspace: the selection's state and candidate
  * ring, and one softmax partial per chunk (or the two calls' workspaces).
  */
@@ -260,36 +279,36 @@ int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t*
                          int budget_num, int budget_den, int n_sink, int n_window,
                          int budget_excludes_forced, int32_t* idx, int32_t* count, const void* q,
                          const void* k_cache, const void* v_cache, float* out, int B, int Hq,
-                         int Hkv, int D, int L, int L_cap, int cap, float softmax_scale,
-                         void* workspace, size_t* ws_bytes);
+                         int Hkv, int sel_group, int D, int L, int L_cap, int cap,
+                         float softmax_scale, void* workspace, size_t* ws_bytes);
 
 /*
  * butler_selection_cache -- TokenSelect README, highlights, Selection Cache: consecutive
  * similar queries share one token selection, so selection runs less often.  For every
- * (b, KV head) of a decode step, the cosine similarity between the group's current query
- * (its R heads' D-vectors stacked into one vector of R*D) and the reference query the
+ * (b, selection head j) of a decode step, the cosine similarity between j's current query
+ * (the D-vectors of its query heads stacked into one vector) and the reference query the
  * cached selection was made for:
- *   cos >= threshold  ->  keep[b, g] = 1: score and select skip the (b, g) rows and the
+ *   cos >= threshold  ->  keep[b, j] = 1: score and select skip the (b, j) rows and the
  *                         previous index list / bitmask / count stand;
- *   otherwise         ->  keep[b, g] = 0 and q_ref[b, g] = q[b, g]: the next score and
- *                         select recompute the selection for this query.
+ *   otherwise         ->  keep[b, j] = 0 and q_ref takes q for j's heads: the next score
+ *                         and select recompute the selection for this query.
  * A zero vector on either side gives cos = 0.  The similarity is accumulated in float32
  * (products of the stored values, one sum per (b, g) in lane order, then a fixed tree).
  *
  *   q      [B, Hq, 1, D]   dtype (read)
  *   q_ref  [B, Hq, 1, D]   dtype (read, rows refreshed) -- caller-owned state; a first call
  *                          with threshold > 1 (or a zero-filled q_ref) refreshes every row
- *   keep   [B, Hkv]        int32 (written)
- * D in {64, 128}, R = Hq / Hkv in {1, 2, 4, 8}.  No workspace.
+ *   keep   [B, Hs]         int32 (written)
+ * sel_group as in butler_score.  D in {64, 128}, R = Hq / Hkv in {1, 2, 4, 8}.  No workspace.
  */
 int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, int32_t* keep,
-                           int B, int Hq, int Hkv, int D, float threshold);
+                           int B, int Hq, int Hkv, int sel_group, int D, float threshold);
 
 /*
  * butler_expand_neighbors -- neighbour fetching for the prediction interval.
  * TokenButler arXiv abstract: the predictor can run once per prediction interval, the
  * selection made at its last run being reused in between and widened with the tokens'
- * neighbours (neighbor fetching).  Per (b, KV head) decode row:
+ * neighbours (neighbor fetching).  Per (b, selection head) decode row:
  *   S' = { u : |u - t| <= width for some t in S }  U  [max(0, L - n_window), L),  0 <= u < L
  * where S is the first min(count, cap_in) entries of idx (a selection made at an earlier,
  * shorter length) and the window is taken at the current length L, so the tokens appended
@@ -297,13 +316,13 @@ int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, 
  * ascending order in its first count_out entries (entries beyond cap_out are dropped;
  * count_out is |S'|).
  *
- *   idx       [B, Hkv, cap_in]    int32 (read), count [B, Hkv] int32 (read)
- *   idx_out   [B, Hkv, cap_out]   int32 (written), count_out [B, Hkv] int32 (written)
+ *   idx       [B, Hs, cap_in]     int32 (read), count [B, Hs] int32 (read)
+ *   idx_out   [B, Hs, cap_out]    int32 (written), count_out [B, Hs] int32 (written)
  * 0 <= width <= 31; L <= 2^23; cap_out >= min(L, cap_in * (2*width + 1) + n_window); the
  * output buffers must not alias the inputs.  No workspace.
  */
 int butler_expand_neighbors(void* stream, const int32_t* idx, const int32_t* count,
-                            int32_t* idx_out, int32_t* count_out, int B, int Hkv, int L,
+                            int32_t* idx_out, int32_t* count_out, int B, int Hs, int L,
                             int cap_in, int cap_out, int width, int n_window);
 
 #ifdef __cplusplus

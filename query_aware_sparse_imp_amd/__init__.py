@@ -46,15 +46,15 @@ _SIGS = {
     "butler_abi_version": ([], _i),
     "butler_project_keys": ([_vp, _i, _vp, _vp, _vp] + [_i] * 7, _i),
     "butler_produce_queries": ([_vp, _i, _vp, _vp, _vp, _vp] + [_i] * 7 + [_f, _vp, _sz], _i),
-    "butler_score": ([_vp, _i, _i, _vp, _vp, _vp, _vp, _vp] + [_i] * 11 + [_f, _vp, _sz], _i),
-    "butler_project_and_score": ([_vp, _i] + [_vp] * 7 + [_i] * 9, _i),
+    "butler_score": ([_vp, _i, _i, _vp, _vp, _vp, _vp, _vp] + [_i] * 12 + [_f, _vp, _sz], _i),
+    "butler_project_and_score": ([_vp, _i] + [_vp] * 7 + [_i] * 10, _i),
     "butler_select_topk": ([_vp, _vp, _vp, _vp] + [_i] * 5 + [_vp, _vp, _vp] + [_i] * 7 +
                            [_vp, _sz], _i),
-    "butler_selection_cache": ([_vp, _i, _vp, _vp, _vp] + [_i] * 4 + [_f], _i),
-    "butler_select_attend": ([_vp, _i, _vp, _vp] + [_i] * 5 + [_vp] * 6 + [_i] * 7 +
+    "butler_selection_cache": ([_vp, _i, _vp, _vp, _vp] + [_i] * 5 + [_f], _i),
+    "butler_select_attend": ([_vp, _i, _vp, _vp] + [_i] * 5 + [_vp] * 6 + [_i] * 8 +
                              [_f, _vp, _sz], _i),
     "butler_expand_neighbors": ([_vp] * 5 + [_i] * 7, _i),
-    "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 9 + [_f, _vp, _sz], _i),
+    "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 10 + [_f, _vp, _sz], _i),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -84,12 +84,24 @@ def declared_symbols() -> list:
 
 def _check_hist(h: Optional[torch.Tensor], rows: tuple) -> None:
     if h is not None and (tuple(h.shape) != (*rows, 2048) or h.element_size() != 4):
-        raise ValueError("radix_hist must be 32-bit [B, Hkv, Lq, 2048]")
+        raise ValueError("radix_hist must be 32-bit [B, Hs, Lq, 2048]")
 
 
 def _check_keep(k: Optional[torch.Tensor], shape: tuple) -> None:
     if k is not None and (tuple(k.shape) != shape or k.dtype != torch.int32):
-        raise ValueError("keep must be int32 [B, Hkv]")
+        raise ValueError("keep must be int32 [B, Hs]")
+
+
+def selection_heads(Hq: int, Hkv: int, sel_group: int = 0) -> int:
+    """Hs, the selected sets per batch entry: sel_group query heads share one set (0: the
+    Hq // Hkv heads of a KV head; 1: one set per query head)."""
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    R = Hq // Hkv
+    g = R if sel_group == 0 else sel_group
+    if g <= 0 or R % g:
+        raise ValueError(f"sel_group must be 0 or a divisor of Hq / Hkv = {R}")
+    return Hq // g
 
 
 def _check(fn: str, status: int) -> None:
@@ -190,14 +202,16 @@ def butler_produce_queries(h: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
 def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.Tensor, *,
                  Hkv: int, L: int, slot: int = 0, q_pos0: int = 0, causal: bool = False,
                  softmax_scale: float = 1.0, radix_hist: Optional[torch.Tensor] = None,
-                 keep: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Importance scores [B, Hkv, Lq, L] (see butler.h).
+                 keep: Optional[torch.Tensor] = None, sel_group: int = 0, stream=None) -> None:
+    """Importance scores [B, Hs, Lq, L] (see butler.h).
 
     RAW: q = q_imp [B, Hq, G, Lq, d'], keys = kimp [B, Hkv, L_cap, d'].
     SOFTVOTE: q = [B, Hq, Lq, D], keys = k_cache [B, Hkv, L_cap, D].
-    radix_hist: optional zero-filled int32/uint32 [B, Hkv, Lq, 2048] that collects the
+    sel_group: query heads per selected set (0: all Hq // Hkv of a KV head, Hs = Hkv;
+    1: per query head, Hs = Hq).
+    radix_hist: optional zero-filled int32/uint32 [B, Hs, Lq, 2048] that collects the
     first radix digit of every score for butler_select_topk.
-    keep: optional int32 [B, Hkv] from butler_selection_cache; rows with keep != 0 are
+    keep: optional int32 [B, Hs] from butler_selection_cache; rows with keep != 0 are
     skipped (single-row calls).
     """
     if mode == BUTLER_SCORE_RAW:
@@ -206,14 +220,15 @@ def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.T
         B, Hq, Lq, dk = q.shape
         G = 1
     Bk, Hk, L_cap, dk2 = keys.shape
-    if (Bk, Hk, dk2) != (B, Hkv, dk) or scores.shape != (B, Hkv, Lq, L):
+    Hs = selection_heads(Hq, Hkv, sel_group)
+    if (Bk, Hk, dk2) != (B, Hkv, dk) or scores.shape != (B, Hs, Lq, L):
         raise ValueError("shape mismatch")
     if q.dtype != keys.dtype or scores.dtype != torch.float32:
         raise TypeError("dtype mismatch")
-    _check_hist(radix_hist, (B, Hkv, Lq))
-    _check_keep(keep, (B, Hkv))
+    _check_hist(radix_hist, (B, Hs, Lq))
+    _check_keep(keep, (B, Hs))
     args = (mode, _dtype_code(q), _ptr(q), _ptr(keys), _ptr(scores), _ptr(radix_hist),
-            _ptr(keep), B, Hq, Hkv, G, slot, Lq, L, L_cap, dk, q_pos0, int(causal),
+            _ptr(keep), B, Hq, Hkv, sel_group, G, slot, Lq, L, L_cap, dk, q_pos0, int(causal),
             softmax_scale)
     need = workspace_bytes(lambda ws, n: lib.butler_score(_stream(stream), *args, ws, n))
     ws, n = _workspace("score", need, q.device, tuple(args[7:]))
@@ -223,25 +238,28 @@ def butler_score(mode: int, q: torch.Tensor, keys: torch.Tensor, scores: torch.T
 def butler_project_and_score(q_imp: torch.Tensor, k_cache: torch.Tensor, w_k: torch.Tensor,
                              kimp: torch.Tensor, scores: torch.Tensor, *, Hkv: int, L: int,
                              slot: int = 0, radix_hist: Optional[torch.Tensor] = None,
-                             keep: Optional[torch.Tensor] = None, stream=None) -> None:
+                             keep: Optional[torch.Tensor] = None, sel_group: int = 0,
+                             stream=None) -> None:
     """Projects key row L - 1 into kimp and scores tokens [0, L) in one launch: the same as
     butler_project_keys(pos0=L-1, n_new=1) then butler_score(RAW) (see butler.h).
     q_imp [B, Hq, G, 1, d'], k_cache [B, Hkv, L_cap, D], w_k [D, d'],
-    kimp [B, Hkv, L_cap, d'], scores [B, Hkv, 1, L]."""
+    kimp [B, Hkv, L_cap, d'], scores [B, Hs, 1, L]; sel_group as in butler_score."""
     B, Hq, G, Lq, dp = q_imp.shape
     Bk, Hk, L_cap, D = k_cache.shape
+    Hs = selection_heads(Hq, Hkv, sel_group)
     if Lq != 1 or (Bk, Hk) != (B, Hkv) or w_k.shape != (D, dp):
         raise ValueError("shape mismatch")
-    if kimp.shape != (B, Hkv, L_cap, dp) or scores.shape != (B, Hkv, 1, L):
+    if kimp.shape != (B, Hkv, L_cap, dp) or scores.shape != (B, Hs, 1, L):
         raise ValueError("shape mismatch")
     if not (q_imp.dtype == k_cache.dtype == w_k.dtype == kimp.dtype) or \
             scores.dtype != torch.float32:
         raise TypeError("dtype mismatch")
-    _check_hist(radix_hist, (B, Hkv, 1))
-    _check_keep(keep, (B, Hkv))
+    _check_hist(radix_hist, (B, Hs, 1))
+    _check_keep(keep, (B, Hs))
     _check("butler_project_and_score", lib.butler_project_and_score(
         _stream(stream), _dtype_code(q_imp), _ptr(q_imp), _ptr(k_cache), _ptr(w_k), _ptr(kimp),
-        _ptr(scores), _ptr(radix_hist), _ptr(keep), B, Hq, Hkv, G, slot, L, L_cap, D, dp))
+        _ptr(scores), _ptr(radix_hist), _ptr(keep), B, Hq, Hkv, sel_group, G, slot, L, L_cap, D,
+        dp))
 
 
 def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n_sink: int,
@@ -250,7 +268,7 @@ def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n
                        causal: bool = False, radix_hist: Optional[torch.Tensor] = None,
                        keep: Optional[torch.Tensor] = None,
                        budget_excludes_forced: bool = False, stream=None) -> None:
-    """Top-x + sink + window per row of scores [B, Hkv, Lq, L] (see butler.h).  keep: as in
+    """Top-x + sink + window per row of scores [B, Hs, Lq, L] (see butler.h).  keep: as in
     butler_score; kept rows leave idx, bitmask and count as they were.
     budget_excludes_forced: the top-x ranks only the tokens outside the sink and the window."""
     B, Hkv, Lq, L = scores.shape
@@ -279,21 +297,27 @@ def butler_sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
                               out: torch.Tensor, *, L: int, idx: Optional[torch.Tensor] = None,
                               count: Optional[torch.Tensor] = None,
                               bitmask: Optional[torch.Tensor] = None, q_pos0: int = 0,
-                              softmax_scale: float, stream=None) -> None:
-    """Attention of q [B, Hq, Lq, D] over the selected tokens (see butler.h)."""
+                              softmax_scale: float, sel_group: int = 0, stream=None) -> None:
+    """Attention of q [B, Hq, Lq, D] over the selected tokens (see butler.h): idx
+    [B, Hs, Lq, cap] and count [B, Hs, Lq], or bitmask [B, Hs, Lq, ceil(L/32)];
+    sel_group as in butler_score."""
     B, Hq, Lq, D = q.shape
     Bk, Hkv, L_cap, D2 = k_cache.shape
     if (Bk, D2) != (B, D) or v_cache.shape != k_cache.shape or out.shape != (B, Hq, Lq, D):
         raise ValueError("shape mismatch")
     if out.dtype != torch.float32 or not (q.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("dtype mismatch")
+    Hs = selection_heads(Hq, Hkv, sel_group)
     cap = 0
     if idx is not None:
-        if idx.shape[:3] != (B, Hkv, Lq) or count is None or count.shape != (B, Hkv, Lq):
-            raise ValueError("idx [B, Hkv, Lq, cap] and count [B, Hkv, Lq] required")
+        if idx.shape[:3] != (B, Hs, Lq) or count is None or count.shape != (B, Hs, Lq):
+            raise ValueError("idx [B, Hs, Lq, cap] and count [B, Hs, Lq] required")
         cap = idx.shape[3]
+    if bitmask is not None and tuple(bitmask.shape) != (B, Hs, Lq, (L + 31) // 32):
+        raise ValueError("bitmask must be [B, Hs, Lq, ceil(L/32)]")
     args = (_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(idx), _ptr(count),
-            _ptr(bitmask), _ptr(out), B, Hq, Hkv, D, Lq, L, L_cap, cap, q_pos0, softmax_scale)
+            _ptr(bitmask), _ptr(out), B, Hq, Hkv, sel_group, D, Lq, L, L_cap, cap, q_pos0,
+            softmax_scale)
     need = workspace_bytes(
         lambda ws, n: lib.butler_sparse_decode_attn(_stream(stream), *args, ws, n))
     ws, n = _workspace("attn", need, q.device, tuple(args[8:]))
@@ -306,27 +330,31 @@ def butler_select_attend(scores: torch.Tensor, budget_num: int, budget_den: int,
                          k_cache: torch.Tensor, v_cache: torch.Tensor, out: torch.Tensor, *,
                          L: int, softmax_scale: float,
                          radix_hist: Optional[torch.Tensor] = None,
-                         budget_excludes_forced: bool = False, stream=None) -> None:
+                         budget_excludes_forced: bool = False, sel_group: int = 0,
+                         stream=None) -> None:
     """butler_select_topk then butler_sparse_decode_attn for one decode step (see butler.h).
-    scores [B, Hkv, 1, L]; idx [B, Hkv, 1, cap], count [B, Hkv, 1] (written);
-    q [B, Hq, 1, D]; caches [B, Hkv, L_cap, D]; out [B, Hq, 1, D] float32."""
-    B, Hkv, Lq, Ls = scores.shape
+    scores [B, Hs, 1, L]; idx [B, Hs, 1, cap], count [B, Hs, 1] (written);
+    q [B, Hq, 1, D]; caches [B, Hkv, L_cap, D]; out [B, Hq, 1, D] float32;
+    sel_group as in butler_score."""
+    B, Hs, Lq, Ls = scores.shape
     Bq, Hq, Lq2, D = q.shape
-    Bk, Hk, L_cap, D2 = k_cache.shape
-    if Lq != 1 or Lq2 != 1 or Ls != L or (Bq, Bk, Hk, D2) != (B, B, Hkv, D):
+    Bk, Hkv, L_cap, D2 = k_cache.shape
+    if Lq != 1 or Lq2 != 1 or Ls != L or (Bq, Bk, D2) != (B, B, D):
         raise ValueError("shape mismatch")
+    if Hs != selection_heads(Hq, Hkv, sel_group):
+        raise ValueError("scores must have Hs = Hq / sel_group selection heads")
     if v_cache.shape != k_cache.shape or out.shape != (B, Hq, 1, D):
         raise ValueError("shape mismatch")
-    if idx.shape[:3] != (B, Hkv, 1) or count.shape != (B, Hkv, 1):
-        raise ValueError("idx [B, Hkv, 1, cap] and count [B, Hkv, 1] required")
+    if idx.shape[:3] != (B, Hs, 1) or count.shape != (B, Hs, 1):
+        raise ValueError("idx [B, Hs, 1, cap] and count [B, Hs, 1] required")
     if scores.dtype != torch.float32 or out.dtype != torch.float32 or \
             not (q.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("dtype mismatch")
-    _check_hist(radix_hist, (B, Hkv, 1))
+    _check_hist(radix_hist, (B, Hs, 1))
     args = (_dtype_code(q), _ptr(scores), _ptr(radix_hist), budget_num, budget_den, n_sink,
             n_window, int(bool(budget_excludes_forced)), _ptr(idx), _ptr(count), _ptr(q),
-            _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Hq, Hkv, D, L, L_cap, idx.shape[3],
-            float(softmax_scale))
+            _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Hq, Hkv, sel_group, D, L, L_cap,
+            idx.shape[3], float(softmax_scale))
     need = workspace_bytes(lambda ws, n: lib.butler_select_attend(_stream(stream), *args, ws, n))
     ws, n = _workspace("select_attend", need, q.device, tuple(args[3:8]) + tuple(args[14:]))
     _check("butler_select_attend",
@@ -334,25 +362,27 @@ def butler_select_attend(scores: torch.Tensor, budget_num: int, budget_den: int,
 
 
 def butler_selection_cache(q: torch.Tensor, q_ref: torch.Tensor, keep: torch.Tensor, *,
-                           Hkv: int, threshold: float, stream=None) -> None:
-    """keep[b, g] = cos(q group, q_ref group) >= threshold; refreshes q_ref where not
-    (see butler.h).  q, q_ref: [B, Hq, 1, D]; keep: int32 [B, Hkv]."""
+                           Hkv: int, threshold: float, sel_group: int = 0, stream=None) -> None:
+    """keep[b, j] = cos(q of selection head j, q_ref of j) >= threshold; refreshes q_ref
+    where not (see butler.h).  q, q_ref: [B, Hq, 1, D]; keep: int32 [B, Hs]; sel_group as
+    in butler_score."""
     B, Hq, Lq, D = q.shape
-    if q_ref.shape != q.shape or Lq != 1 or keep.shape != (B, Hkv) or keep.dtype != torch.int32:
+    Hs = selection_heads(Hq, Hkv, sel_group)
+    if q_ref.shape != q.shape or Lq != 1 or keep.shape != (B, Hs) or keep.dtype != torch.int32:
         raise ValueError("shape mismatch")
     if q_ref.dtype != q.dtype:
         raise TypeError("dtype mismatch")
     _check("butler_selection_cache", lib.butler_selection_cache(
-        _stream(stream), _dtype_code(q), _ptr(q), _ptr(q_ref), _ptr(keep), B, Hq, Hkv, D,
-        float(threshold)))
+        _stream(stream), _dtype_code(q), _ptr(q), _ptr(q_ref), _ptr(keep), B, Hq, Hkv,
+        sel_group, D, float(threshold)))
 
 
 def butler_expand_neighbors(idx: torch.Tensor, count: torch.Tensor, idx_out: torch.Tensor,
                             count_out: torch.Tensor, *, L: int, width: int, n_window: int,
                             stream=None) -> None:
     """Widens a reused selection with its tokens' neighbours and the window at length L
-    (see butler.h).  idx: int32 [B, Hkv, cap_in]; count: int32 [B, Hkv];
-    idx_out: int32 [B, Hkv, cap_out]; count_out: int32 [B, Hkv]."""
+    (see butler.h).  idx: int32 [B, Hs, cap_in]; count: int32 [B, Hs];
+    idx_out: int32 [B, Hs, cap_out]; count_out: int32 [B, Hs]."""
     if idx.dim() != 3 or idx_out.dim() != 3 or idx.shape[:2] != idx_out.shape[:2]:
         raise ValueError("shape mismatch")
     B, Hkv, cap_in = idx.shape

@@ -49,6 +49,18 @@ inline int workspace_phase(void* ws, size_t* ws_bytes, size_t need, int* rc) {
 inline bool valid_dtype(int d) { return d == BUTLER_F32 || d == BUTLER_BF16; }
 inline bool pow2_group(int R) { return R == 1 || R == 2 || R == 4 || R == 8; }
 
+// Query heads per selected set: 0 is the KV head's whole group (Hq/Hkv), otherwise a
+// divisor of it.  Gives the selection heads per batch entry (Hs) and how many of them
+// share one KV head (kvdiv); false when sel_group is not such a divisor.
+inline bool sel_heads(int Hq, int Hkv, int sel_group, int* Hs, int* kvdiv) {
+  const int R = Hq / Hkv;
+  const int gs = sel_group == 0 ? R : sel_group;
+  if (gs <= 0 || R % gs) return false;
+  *Hs = Hq / gs;
+  *kvdiv = R / gs;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,7 +76,7 @@ const char* butler_status_string(int status) {
   }
 }
 
-int butler_abi_version(void) { return 4; }
+int butler_abi_version(void) { return 5; }
 
 int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
                         void* kimp, int B, int Hkv, int L_cap, int D, int dprime, int pos0,
@@ -105,7 +117,7 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
 
 int butler_score(void* stream, int mode, int dtype, const void* q, const void* keys,
                  float* scores, uint32_t* radix_hist, const int32_t* keep, int B, int Hq,
-                 int Hkv, int G, int slot,
+                 int Hkv, int sel_group, int G, int slot,
                  int Lq, int L,
                  int L_cap, int dk, int q_pos0, int causal, float softmax_scale,
                  void* workspace, size_t* ws_bytes) {
@@ -115,17 +127,19 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
     return BUTLER_ERR_INVALID_ARG;
   if (Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
   if (!pow2_group(Hq / Hkv)) return BUTLER_ERR_UNSUPPORTED;
-  if ((long long)B * Hkv * Lq > 65535LL * 65535LL) return BUTLER_ERR_UNSUPPORTED;
+  int Hs, kvdiv;
+  if (!sel_heads(Hq, Hkv, sel_group, &Hs, &kvdiv)) return BUTLER_ERR_INVALID_ARG;
+  if ((long long)B * Hs * Lq > 65535LL * 65535LL) return BUTLER_ERR_UNSUPPORTED;
   size_t need = 0;
   if (mode == BUTLER_SCORE_RAW) {
     if (G <= 0 || slot < 0 || slot >= G) return BUTLER_ERR_INVALID_ARG;
     if (!(dk == 16 || dk == 32)) return BUTLER_ERR_UNSUPPORTED;
-    if (Lq > 65535 || B * Hkv > 65535) return BUTLER_ERR_UNSUPPORTED;
+    if (Lq > 65535 || (long long)B * Hs > 65535) return BUTLER_ERR_UNSUPPORTED;
   } else {
     if (!(dk == 64 || dk == 128)) return BUTLER_ERR_UNSUPPORTED;
     if (Lq != 1 || causal) return BUTLER_ERR_UNSUPPORTED;
     if (!(softmax_scale > 0.f)) return BUTLER_ERR_INVALID_ARG;
-    need = softvote_workspace(B, Hq, Hkv, L);
+    need = softvote_workspace(B, Hq, Hs, L);
   }
   int rc;
   if (workspace_phase(workspace, ws_bytes, need, &rc)) return rc;
@@ -138,22 +152,24 @@ int butler_score(void* stream, int mode, int dtype, const void* q, const void* k
   uint32_t* hist = (Lq > 1) ? nullptr : radix_hist;
   const int32_t* kp = (Lq > 1) ? nullptr : keep;
   if (mode == BUTLER_SCORE_RAW)
-    return finish(s, launch_score_raw(s, dtype, q, keys, scores, B, Hq, Hkv, G, slot, Lq, L,
-                                      L_cap, dk, q_pos0, causal, hist, kp));
-  return finish(s, launch_score_softvote(s, dtype, q, keys, scores, B, Hq, Hkv, L, L_cap, dk,
-                                         softmax_scale, workspace, hist, kp));
+    return finish(s, launch_score_raw(s, dtype, q, keys, scores, B, Hq, Hs, G, slot, Lq, L,
+                                      L_cap, dk, q_pos0, causal, hist, kp, kvdiv));
+  return finish(s, launch_score_softvote(s, dtype, q, keys, scores, B, Hq, Hs, L, L_cap, dk,
+                                         softmax_scale, workspace, hist, kp, kvdiv));
 }
 
 int butler_project_and_score(void* stream, int dtype, const void* q_imp, const void* k_cache,
                              const void* w_k, void* kimp, float* scores, uint32_t* radix_hist,
-                             const int32_t* keep, int B, int Hq, int Hkv, int G, int slot,
-                             int L, int L_cap, int D, int dprime) {
+                             const int32_t* keep, int B, int Hq, int Hkv, int sel_group, int G,
+                             int slot, int L, int L_cap, int D, int dprime) {
   if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || L_cap < L) return BUTLER_ERR_INVALID_ARG;
   if (Hq % Hkv || G <= 0 || slot < 0 || slot >= G) return BUTLER_ERR_INVALID_ARG;
   if (!pow2_group(Hq / Hkv)) return BUTLER_ERR_UNSUPPORTED;
+  int Hs, kvdiv;
+  if (!sel_heads(Hq, Hkv, sel_group, &Hs, &kvdiv)) return BUTLER_ERR_INVALID_ARG;
   if (!(D == 64 || D == 128) || !(dprime == 16 || dprime == 32)) return BUTLER_ERR_UNSUPPORTED;
-  if ((long long)B * Hkv > 65535) return BUTLER_ERR_UNSUPPORTED;
+  if ((long long)B * Hs > 65535) return BUTLER_ERR_UNSUPPORTED;
   if (!q_imp || !k_cache || !w_k || !kimp || !scores) return BUTLER_ERR_INVALID_ARG;
   if (!aligned16(q_imp) || !aligned16(k_cache) || !aligned16(w_k) || !aligned16(kimp) ||
       !aligned16(scores))
@@ -161,22 +177,22 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
   if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
   if (kimp == k_cache || kimp == w_k) return BUTLER_ERR_INVALID_ARG;   // no aliasing
   hipStream_t s = (hipStream_t)stream;
-  return finish(s, launch_project_score(s, dtype, q_imp, k_cache, w_k, kimp, scores, B, Hq, Hkv,
-                                        G, slot, L, L_cap, D, dprime, radix_hist, keep));
+  return finish(s, launch_project_score(s, dtype, q_imp, k_cache, w_k, kimp, scores, B, Hq, Hs,
+                                        G, slot, L, L_cap, D, dprime, radix_hist, keep, kvdiv));
 }
 
 int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
                        const int32_t* keep, int budget_num, int budget_den, int n_sink,
                        int n_window, int budget_excludes_forced, int32_t* idx,
-                       uint32_t* bitmask, int32_t* count, int B, int Hkv, int Lq, int L,
+                       uint32_t* bitmask, int32_t* count, int B, int Hs, int Lq, int L,
                        int cap, int q_pos0, int causal, void* workspace, size_t* ws_bytes) {
-  if (B <= 0 || Hkv <= 0 || Lq <= 0 || L <= 0 || q_pos0 < 0) return BUTLER_ERR_INVALID_ARG;
+  if (B <= 0 || Hs <= 0 || Lq <= 0 || L <= 0 || q_pos0 < 0) return BUTLER_ERR_INVALID_ARG;
   if (budget_num < 0 || budget_den <= 0 || n_sink < 0 || n_window < 0)
     return BUTLER_ERR_INVALID_ARG;
   const int fo = budget_excludes_forced ? 1 : 0;
   // the scorer's histogram counts every token's key; the forced tokens then rank below all
   if (fo && radix_hist && Lq == 1) return BUTLER_ERR_INVALID_ARG;
-  const long long rows = (long long)B * Hkv * Lq;
+  const long long rows = (long long)B * Hs * Lq;
   if (rows > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
   // one workgroup per row holds at most 64K keys; long rows use the chunked decode
   // schedule (one query row per KV head, no causal mask), up to 8M tokens
@@ -197,31 +213,34 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
   uint32_t* hist = (Lq > 1) ? nullptr : radix_hist;   // see butler_score
   const int32_t* kp = (Lq > 1) ? nullptr : keep;
   return finish(s, launch_select(s, scores, budget_num, budget_den, n_sink, n_window, fo, idx,
-                                 bitmask, count, B, Hkv, Lq, L, cap, q_pos0, causal, hist, kp,
+                                 bitmask, count, B, Hs, Lq, L, cap, q_pos0, causal, hist, kp,
                                  workspace));
 }
 
 int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* idx, const int32_t* count,
                               const uint32_t* bitmask, float* out, int B, int Hq, int Hkv,
-                              int D, int Lq, int L, int L_cap, int cap, int q_pos0,
-                              float softmax_scale, void* workspace, size_t* ws_bytes) {
+                              int sel_group, int D, int Lq, int L, int L_cap, int cap,
+                              int q_pos0, float softmax_scale, void* workspace,
+                              size_t* ws_bytes) {
   if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || L <= 0 || L_cap < L || q_pos0 < 0)
     return BUTLER_ERR_INVALID_ARG;
   if (Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
   if (!pow2_group(Hq / Hkv) || !(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
+  int Hs, kvdiv;
+  if (!sel_heads(Hq, Hkv, sel_group, &Hs, &kvdiv)) return BUTLER_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f)) return BUTLER_ERR_INVALID_ARG;
   const bool use_idx = idx != nullptr;
   if (!use_idx && !bitmask) return BUTLER_ERR_INVALID_ARG;
-  const long long rows = (long long)B * Hkv * Lq;
+  const long long rows = (long long)B * Hs * Lq;
   if (use_idx) {
     if (cap <= 0 || !count) return BUTLER_ERR_INVALID_ARG;
     if (rows * ((cap + 255) / 256) > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
   } else {
     if (L > 16384 || rows > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
   }
-  const size_t need = use_idx ? attn_workspace(dtype, B, Hq, Hkv, D, Lq, L, cap) : 0;
+  const size_t need = use_idx ? attn_workspace(dtype, B, Hq, Hs, D, Lq, L, cap) : 0;
   int rc;
   if (workspace_phase(workspace, ws_bytes, need, &rc)) return rc;
   if (!q || !k_cache || !v_cache || !out) return BUTLER_ERR_INVALID_ARG;
@@ -229,18 +248,18 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
     return BUTLER_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (use_idx)
-    return finish(s, launch_attn_idx(s, dtype, q, k_cache, v_cache, idx, count, out, B, Hq, Hkv,
-                                     D, Lq, L_cap, cap, softmax_scale, workspace));
-  return finish(s, launch_attn_bitmask(s, dtype, q, k_cache, v_cache, bitmask, out, B, Hq, Hkv,
-                                       D, Lq, L, L_cap, q_pos0, softmax_scale, workspace));
+    return finish(s, launch_attn_idx(s, dtype, q, k_cache, v_cache, idx, count, out, B, Hq, Hs,
+                                     D, Lq, L_cap, cap, softmax_scale, workspace, kvdiv));
+  return finish(s, launch_attn_bitmask(s, dtype, q, k_cache, v_cache, bitmask, out, B, Hq, Hs,
+                                       D, Lq, L, L_cap, q_pos0, softmax_scale, workspace, kvdiv));
 }
 
 int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t* radix_hist,
                          int budget_num, int budget_den, int n_sink, int n_window,
                          int budget_excludes_forced, int32_t* idx, int32_t* count, const void* q,
                          const void* k_cache, const void* v_cache, float* out, int B, int Hq,
-                         int Hkv, int D, int L, int L_cap, int cap, float softmax_scale,
-                         void* workspace, size_t* ws_bytes) {
+                         int Hkv, int sel_group, int D, int L, int L_cap, int cap,
+                         float softmax_scale, void* workspace, size_t* ws_bytes) {
   if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || L_cap < L) return BUTLER_ERR_INVALID_ARG;
   if (budget_num < 0 || budget_den <= 0 || n_sink < 0 || n_window < 0) return BUTLER_ERR_INVALID_ARG;
@@ -248,8 +267,10 @@ int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t*
   if (fo && radix_hist) return BUTLER_ERR_INVALID_ARG;   // see butler_select_topk
   if (Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
   if (!pow2_group(Hq / Hkv) || !(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
+  int Hs, kvdiv;
+  if (!sel_heads(Hq, Hkv, sel_group, &Hs, &kvdiv)) return BUTLER_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f)) return BUTLER_ERR_INVALID_ARG;
-  const long long rows = (long long)B * Hkv;
+  const long long rows = (long long)B * Hs;
   if (rows > 0x7fffffffLL || L > 8388608) return BUTLER_ERR_UNSUPPORTED;
   {
     const long long x = (long long)L * budget_num / budget_den;
@@ -258,11 +279,11 @@ int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t*
     if (cap < need_cap) return BUTLER_ERR_INVALID_ARG;
   }
   if (rows * ((cap + 255) / 256) > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
-  const bool fused = select_attend_fusable(dtype, D, Hq, Hkv, L);
+  const bool fused = select_attend_fusable(dtype, D, Hq, Hs, L);
   // unfused: the selection's workspace, then the attention's
   const size_t sel_ws = (select_workspace((int)rows, L, 1, 0) + 255) / 256 * 256;
-  const size_t need = fused ? select_attend_workspace((int)rows, Hq, Hkv, L)
-                            : sel_ws + attn_workspace(dtype, B, Hq, Hkv, D, 1, L, cap);
+  const size_t need = fused ? select_attend_workspace((int)rows, Hq, Hs, L)
+                            : sel_ws + attn_workspace(dtype, B, Hq, Hs, D, 1, L, cap);
   int rc;
   if (workspace_phase(workspace, ws_bytes, need, &rc)) return rc;
   if (!scores || !idx || !count || !q || !k_cache || !v_cache || !out) return BUTLER_ERR_INVALID_ARG;
@@ -273,34 +294,38 @@ int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t*
   hipStream_t s = (hipStream_t)stream;
   if (fused)
     return finish(s, launch_select_attend(s, scores, budget_num, budget_den, n_sink, n_window,
-                                          fo, idx, count, B, Hq, Hkv, L, cap, radix_hist, q, k_cache,
-                                          v_cache, out, L_cap, softmax_scale, workspace));
+                                          fo, idx, count, B, Hq, Hs, L, cap, radix_hist, q, k_cache,
+                                          v_cache, out, L_cap, softmax_scale, workspace, kvdiv));
   hipError_t e = launch_select(s, scores, budget_num, budget_den, n_sink, n_window, fo, idx, nullptr,
-                               count, B, Hkv, 1, L, cap, 0, 0, radix_hist, nullptr, workspace);
+                               count, B, Hs, 1, L, cap, 0, 0, radix_hist, nullptr, workspace);
   if (e != hipSuccess) return finish(s, e);
-  return finish(s, launch_attn_idx(s, dtype, q, k_cache, v_cache, idx, count, out, B, Hq, Hkv, D,
-                                   1, L_cap, cap, softmax_scale, (char*)workspace + sel_ws));
+  return finish(s, launch_attn_idx(s, dtype, q, k_cache, v_cache, idx, count, out, B, Hq, Hs, D,
+                                   1, L_cap, cap, softmax_scale, (char*)workspace + sel_ws,
+                                   kvdiv));
 }
 
 int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, int32_t* keep,
-                           int B, int Hq, int Hkv, int D, float threshold) {
+                           int B, int Hq, int Hkv, int sel_group, int D, float threshold) {
   if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
   if (!pow2_group(Hq / Hkv) || !(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
-  if ((long long)B * Hkv > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
+  int Hs, kvdiv;
+  if (!sel_heads(Hq, Hkv, sel_group, &Hs, &kvdiv)) return BUTLER_ERR_INVALID_ARG;
+  if ((long long)B * Hs > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
   if (threshold != threshold) return BUTLER_ERR_INVALID_ARG;   // NaN
   if (!q || !q_ref || !keep) return BUTLER_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(q_ref) || !aligned16(keep)) return BUTLER_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  return finish(s, launch_selection_cache(s, dtype, q, q_ref, keep, B, Hq, Hkv, D, threshold));
+  // the cache compares the query heads of one selection head: its group of Hq / Hs
+  return finish(s, launch_selection_cache(s, dtype, q, q_ref, keep, B, Hq, Hs, D, threshold));
 }
 
 int butler_expand_neighbors(void* stream, const int32_t* idx, const int32_t* count,
-                            int32_t* idx_out, int32_t* count_out, int B, int Hkv, int L,
+                            int32_t* idx_out, int32_t* count_out, int B, int Hs, int L,
                             int cap_in, int cap_out, int width, int n_window) {
-  if (B <= 0 || Hkv <= 0 || L <= 0 || cap_in <= 0 || cap_out <= 0) return BUTLER_ERR_INVALID_ARG;
+  if (B <= 0 || Hs <= 0 || L <= 0 || cap_in <= 0 || cap_out <= 0) return BUTLER_ERR_INVALID_ARG;
   if (width < 0 || width > 31 || n_window < 0) return BUTLER_ERR_INVALID_ARG;
-  if (L > expand_max_len() || (long long)B * Hkv > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
+  if (L > expand_max_len() || (long long)B * Hs > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
   if (cap_out < L && (long long)cap_out < (long long)cap_in * (2 * width + 1) + n_window)
     return BUTLER_ERR_INVALID_ARG;
   if (!idx || !count || !idx_out || !count_out) return BUTLER_ERR_INVALID_ARG;
@@ -308,7 +333,7 @@ int butler_expand_neighbors(void* stream, const int32_t* idx, const int32_t* cou
     return BUTLER_ERR_INVALID_ARG;
   if (idx == idx_out || count == count_out) return BUTLER_ERR_INVALID_ARG;   // no aliasing
   hipStream_t s = (hipStream_t)stream;
-  return finish(s, launch_expand_neighbors(s, idx, count, idx_out, count_out, B * Hkv, L, cap_in,
+  return finish(s, launch_expand_neighbors(s, idx, count, idx_out, count_out, B * Hs, L, cap_in,
                                            cap_out, width, n_window));
 }
 

@@ -13,6 +13,10 @@
 // round trip.  (Workgroups do not hand work to each other inside a kernel: the
 // device-wide release that would need writes back the XCD's L2.)
 //
+// Heads: "Hkv" counts selection heads (Hq/Hkv query heads share one selected set), and
+// kvdiv consecutive selection heads read one physical KV head, cache row bg / kvdiv;
+// kvdiv = 1 is selection per KV head.
+//
 // Prefill (bitmask rows) -- bf16, D = 128, R = 4: the matrix-core kernel
 // attn_prefill_mfma_kernel (64 query rows per workgroup, a wave per head and 32 rows, dense causal
 // tiles masked by the rows' bitmask words; described with it below).  Other shapes: one
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_idx_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
     float* __restrict__ part, int Hq, int Hkv, int Lq, int L_cap, int cap, float scale_log2,
-    int nsplit, int rounds, int rows) {
+    int nsplit, int rounds, int rows, int kvdiv) {
   using G = Geo<T, D, R>;
   constexpr int EPL = G::EPL;
   constexpr int PS = D + 4;  // floats per (split, head) partial: m, l, pad, pad, acc[D]
@@ -160,8 +164,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_idx_kernel(
   const int p_split = split * kRoundTokens * rounds;
   SoftState<R, EPL> st;
   st.init();
-  const T* kb = k + (long long)bg * L_cap * D + pe * EPL;
-  const T* vb = v + (long long)bg * L_cap * D + pe * EPL;
+  const T* kb = k + (long long)(bg / kvdiv) * L_cap * D + pe * EPL;
+  const T* vb = v + (long long)(bg / kvdiv) * L_cap * D + pe * EPL;
   const int32_t* irow = idx + (long long)row * cap;
   for (int rd = 0; rd < rounds; ++rd) {
     const int p0 = p_split + rd * kRoundTokens;
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
     float* __restrict__ part, int Hq, int Hkv, int Lq, int L_cap, int cap, float scale_log2,
-    int nsplit, int split_len, int rows) {
+    int nsplit, int split_len, int rows, int kvdiv) {
   constexpr int D = 128;
   constexpr int PS = D + 4;
   static_assert(R <= 8, "at most 8 query heads per KV head");
@@ -261,8 +265,8 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
   for (int u = 0; u < U; ++u) iv[u] = irow[min(p_begin + (int)threadIdx.x + u * kMfThreads, cap - 1)];
   const int n = min(count[row], cap);
   const int p_end = min(p_begin + split_len, n);
-  const bf16_t* kb = k + (long long)bg * L_cap * D;
-  const bf16_t* vb = v + (long long)bg * L_cap * D;
+  const bf16_t* kb = k + (long long)(bg / kvdiv) * L_cap * D;
+  const bf16_t* vb = v + (long long)(bg / kvdiv) * L_cap * D;
 
   float m = neg_inf(), l = 0.f;   // softmax state of head pe for this row's stream
   float acc[R][8];
@@ -397,7 +401,7 @@ template <typename T, int D, int R>
 __global__ __launch_bounds__(kAttnThreads) void attn_bitmask_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const uint32_t* __restrict__ bitmask, float* __restrict__ out, int Hq, int Hkv, int Lq,
-    int L, int L_cap, int q_pos0, float scale_log2) {
+    int L, int L_cap, int q_pos0, float scale_log2, int kvdiv) {
   using G = Geo<T, D, R>;
   constexpr int EPL = G::EPL;
   const int row = blockIdx.x;
@@ -419,8 +423,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bitmask_kernel(
                   scale_log2, qr);
   SoftState<R, EPL> st;
   st.init();
-  const T* kb = k + (long long)bg * L_cap * D + pe * EPL;
-  const T* vb = v + (long long)bg * L_cap * D + pe * EPL;
+  const T* kb = k + (long long)(bg / kvdiv) * L_cap * D + pe * EPL;
+  const T* vb = v + (long long)(bg / kvdiv) * L_cap * D + pe * EPL;
   const uint32_t* brow = bitmask + (long long)row * nwords;
   for (int w0 = 0; w0 < nwords_act; w0 += kBmChunkWords) {
     __syncthreads();
@@ -510,7 +514,7 @@ hipError_t merge_t(hipStream_t s, const float* part, float* out, long long rows,
 template <typename T, int D, int R>
 hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
                  const int32_t* idx, const int32_t* count, float* out, int B, int Hq, int Hkv,
-                 int Lq, int L_cap, int cap, float scale, void* ws) {
+                 int Lq, int L_cap, int cap, float scale, void* ws, int kvdiv) {
   const long long rows = (long long)B * Hkv * Lq;
   float* part = (float*)ws;
   int nsplit;
@@ -520,14 +524,14 @@ hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
     hipLaunchKernelGGL((attn_mfma_kernel<R>), dim3((unsigned)(sp.nsplit * rows)),
                        dim3(kMfThreads), 0, s, (const bf16_t*)q, (const bf16_t*)k,
                        (const bf16_t*)v, idx, count, part, Hq, Hkv, Lq, L_cap, cap,
-                       scale * 1.4426950408889634f, sp.nsplit, sp.split_len, (int)rows);
+                       scale * 1.4426950408889634f, sp.nsplit, sp.split_len, (int)rows, kvdiv);
   } else {
     const SplitPlan sp = plan_for(cap);
     nsplit = sp.nsplit;
     hipLaunchKernelGGL((attn_idx_kernel<T, D, R>), dim3((unsigned)(sp.nsplit * rows)),
                        dim3(kAttnThreads), 0, s, (const T*)q, (const T*)k, (const T*)v, idx,
                        count, part, Hq, Hkv, Lq, L_cap, cap, scale * 1.4426950408889634f,
-                       sp.nsplit, sp.rounds, (int)rows);
+                       sp.nsplit, sp.rounds, (int)rows, kvdiv);
   }
   return merge_t<D, R>(s, part, out, rows, Hq, Hkv, Lq, nsplit);
 }
@@ -706,10 +710,10 @@ __global__ __launch_bounds__(kPfThreads * RG) void attn_prefill_mfma_kernel(
 template <typename T, int D, int R>
 hipError_t bm_t(hipStream_t s, const void* q, const void* k, const void* v,
                 const uint32_t* bitmask, float* out, int B, int Hq, int Hkv, int Lq, int L,
-                int L_cap, int q_pos0, float scale) {
+                int L_cap, int q_pos0, float scale, int kvdiv) {
   const long long rows = (long long)B * Hkv * Lq;
   if constexpr (std::is_same<T, bf16_t>::value && D == 128 && R == 4) {
-    if (Lq >= 32) {
+    if (Lq >= 32 && kvdiv == 1) {
       // 64 query rows per workgroup: each staged K/V tile serves eight waves
       const long long blocks = (long long)B * Hkv * ((Lq + 63) / 64);
       hipLaunchKernelGGL(attn_prefill_mfma_kernel<2>, dim3((unsigned)blocks),
@@ -721,7 +725,7 @@ hipError_t bm_t(hipStream_t s, const void* q, const void* k, const void* v,
   }
   hipLaunchKernelGGL((attn_bitmask_kernel<T, D, R>), dim3((unsigned)rows), dim3(kAttnThreads),
                      0, s, (const T*)q, (const T*)k, (const T*)v, bitmask, out, Hq, Hkv, Lq,
-                     L, L_cap, q_pos0, scale * 1.4426950408889634f);
+                     L, L_cap, q_pos0, scale * 1.4426950408889634f, kvdiv);
   return hipGetLastError();
 }
 
@@ -769,8 +773,9 @@ size_t attn_workspace(int dtype, int B, int Hq, int Hkv, int D, int Lq, int L, i
 hipError_t launch_attn_idx(hipStream_t s, int dtype, const void* q, const void* k,
                            const void* v, const int32_t* idx, const int32_t* count,
                            float* out, int B, int Hq, int Hkv, int D, int Lq, int L_cap,
-                           int cap, float scale, void* ws) {
-  BUTLER_ATTN_DISPATCH(idx_t, s, q, k, v, idx, count, out, B, Hq, Hkv, Lq, L_cap, cap, scale, ws);
+                           int cap, float scale, void* ws, int kvdiv) {
+  BUTLER_ATTN_DISPATCH(idx_t, s, q, k, v, idx, count, out, B, Hq, Hkv, Lq, L_cap, cap, scale, ws,
+                       kvdiv);
 }
 
 hipError_t launch_attn_merge(hipStream_t s, const float* part, float* out, long long rows, int Hq,
@@ -787,9 +792,10 @@ hipError_t launch_attn_merge(hipStream_t s, const float* part, float* out, long 
 hipError_t launch_attn_bitmask(hipStream_t s, int dtype, const void* q, const void* k,
                                const void* v, const uint32_t* bitmask, float* out, int B,
                                int Hq, int Hkv, int D, int Lq, int L, int L_cap, int q_pos0,
-                               float scale, void* ws) {
+                               float scale, void* ws, int kvdiv) {
   (void)ws;
-  BUTLER_ATTN_DISPATCH(bm_t, s, q, k, v, bitmask, out, B, Hq, Hkv, Lq, L, L_cap, q_pos0, scale);
+  BUTLER_ATTN_DISPATCH(bm_t, s, q, k, v, bitmask, out, B, Hq, Hkv, Lq, L, L_cap, q_pos0, scale,
+                       kvdiv);
 }
 
 }  // namespace butler

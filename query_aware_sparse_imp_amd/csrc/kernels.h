@@ -7,6 +7,11 @@
 
 namespace butler {
 
+// Head counts: in the scoring, selection and attention launchers "Hkv" is the number of
+// selection heads per batch entry (Hq/Hkv query heads share one selected set) and kvdiv
+// consecutive selection heads read one physical KV head (cache row = selection row /
+// kvdiv).  kvdiv = 1: one selection per KV head.
+
 // ---- key projection -------------------------------------------------------
 hipError_t launch_project_keys(hipStream_t s, int dtype, const void* k, const void* w,
                                void* kimp, int B, int Hkv, int L_cap, int D, int dp,
@@ -22,16 +27,17 @@ hipError_t launch_produce(hipStream_t s, const void* h, const void* w1, const vo
 hipError_t launch_project_score(hipStream_t s, int dtype, const void* q_imp,
                                 const void* k_cache, const void* w_k, void* kimp,
                                 float* scores, int B, int Hq, int Hkv, int G, int slot, int L,
-                                int L_cap, int D, int dp, uint32_t* hist, const int32_t* keep);
+                                int L_cap, int D, int dp, uint32_t* hist, const int32_t* keep,
+                                int kvdiv);
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
                             int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist,
-                            const int32_t* keep);
+                            const int32_t* keep, int kvdiv);
 size_t softvote_workspace(int B, int Hq, int Hkv, int L);
 hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const void* k,
                                  float* scores, int B, int Hq, int Hkv, int L, int L_cap,
                                  int D, float scale, void* ws, uint32_t* hist,
-                                 const int32_t* keep);
+                                 const int32_t* keep, int kvdiv);
 
 // ---- selection ------------------------------------------------------------
 size_t select_workspace(int rows, int L, int Lq, int causal);
@@ -45,11 +51,11 @@ size_t attn_workspace(int dtype, int B, int Hq, int Hkv, int D, int Lq, int L, i
 hipError_t launch_attn_idx(hipStream_t s, int dtype, const void* q, const void* k,
                            const void* v, const int32_t* idx, const int32_t* count,
                            float* out, int B, int Hq, int Hkv, int D, int Lq, int L_cap,
-                           int cap, float scale, void* ws);
+                           int cap, float scale, void* ws, int kvdiv);
 hipError_t launch_attn_bitmask(hipStream_t s, int dtype, const void* q, const void* k,
                                const void* v, const uint32_t* bitmask, float* out, int B,
                                int Hq, int Hkv, int D, int Lq, int L, int L_cap, int q_pos0,
-                               float scale, void* ws);
+                               float scale, void* ws, int kvdiv);
 
 hipError_t launch_attn_merge(hipStream_t s, const float* part, float* out, long long rows, int Hq,
                              int Hkv, int Lq, int D, int nsplit);
@@ -59,7 +65,7 @@ hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int
                                 int n_sink, int n_window, int fo, int32_t* idx, int32_t* count, int B,
                                 int Hq, int Hkv, int L, int cap, uint32_t* hist, const void* q,
                                 const void* k, const void* v, float* out, int L_cap,
-                                float scale, void* ws);
+                                float scale, void* ws, int kvdiv);
 hipError_t launch_selection_cache(hipStream_t s, int dtype, const void* q, void* q_ref,
                                   int32_t* keep, int B, int Hq, int Hkv, int D, float threshold);
 

@@ -9,6 +9,11 @@
 //   calls (prefill chunks): the same exact contraction on the matrix cores in float64
 //   (score_rows_mfma_kernel, described with it below).
 //
+// Selection heads: B*Hkv score rows, where "Hkv" counts selection heads -- each the sum of
+// Hq/Hkv consecutive query heads -- and kvdiv consecutive selection heads read one physical
+// KV head (cache row bg / kvdiv).  kvdiv = 1 is selection per KV head; with one query head
+// per selection head, every query head ranks the tokens on its own.
+//
 // Single-row calls can also add each score's first radix digit (the top 11 bits of the
 // order-preserving key that the selection uses) into a per-row global histogram, counted
 // in LDS per workgroup and flushed with atomics, so the selection that follows starts from
@@ -59,7 +64,7 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
     const T* __restrict__ q_imp, const T* __restrict__ kimp, float* __restrict__ scores,
     int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal,
     int tpb, uint32_t* __restrict__ radix_hist, const int32_t* __restrict__ keep,
-    const T* __restrict__ k_cache, const T* __restrict__ w_k, T* kimp_w) {
+    const T* __restrict__ k_cache, const T* __restrict__ w_k, T* kimp_w, int kvdiv) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPT = DP / EPL;           // lanes per token
   constexpr int TPI = kRawThreads / LPT;  // tokens per block-wide step
@@ -75,7 +80,8 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   const int t0 = blockIdx.x * tpb;
   const int t1 = min(t0 + tpb, L);
   const int tv = min(t1, L_r);
-  const T* kb = kimp + (size_t)bg * L_cap * DP + part * EPL;
+  const int bk = bg / kvdiv;   // physical KV head
+  const T* kb = kimp + (size_t)bk * L_cap * DP + part * EPL;
   float* srow = scores + ((size_t)bg * Lq + i) * L;
   // batch loads at clamped addresses: no control flow around them
   auto load_batch = [&](RawBatch<U>& rb, int t) {
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
       const int pc = threadIdx.x + u * kRawThreads;
       if (pc < NPIECE) Vec16<T>::load(w_k + pc * EPL, wv[u]);
     }
-    const T* krow = k_cache + ((size_t)bg * L_cap + (L - 1)) * DW;
+    const T* krow = k_cache + ((size_t)bk * L_cap + (L - 1)) * DW;
     if (threadIdx.x < DW / EPL) Vec16<T>::load(krow + threadIdx.x * EPL, kv);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -127,7 +133,8 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
                             acc4[c & 3]);
       }
       const T r = round_to((acc4[0] + acc4[1]) + (acc4[2] + acc4[3]), (T*)nullptr);
-      kimp_w[((size_t)bg * L_cap + (L - 1)) * DP + j] = r;
+      // the first selection head of a KV head stores the row (the others compute the same)
+      if (bg == bk * kvdiv) kimp_w[((size_t)bk * L_cap + (L - 1)) * DP + j] = r;
       knew[j] = r;
     }
     __syncthreads();
@@ -214,7 +221,7 @@ template <typename T, int D, int R>
 __global__ __launch_bounds__(kSvThreads) void softvote_logits_kernel(
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ logits,
     float2* __restrict__ part, int Hq, int Hkv, int L, int L_cap, float scale_log2,
-    int nblk, const int32_t* __restrict__ keep) {
+    int nblk, const int32_t* __restrict__ keep, int kvdiv) {
   if (keep && keep[blockIdx.y]) return;
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPR = D / EPL;
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(kSvThreads) void softvote_logits_kernel(
 #pragma unroll
   for (int r = 0; r < R; ++r) { m[r] = neg_inf(); l[r] = 0.f; }
   const int tbase = blk * kSvTokensPerBlock + wid * 64 + sub;
-  const T* kb = k + (size_t)bg * L_cap * D + pe * EPL;
+  const T* kb = k + (size_t)(bg / kvdiv) * L_cap * D + pe * EPL;
   float* zb = logits + (size_t)bg * R * L;
 #pragma unroll 4
   for (int it = 0; it < ITERS; ++it) {
@@ -297,7 +304,7 @@ template <int R>
 __global__ __launch_bounds__(kSvThreads) void softvote_logits_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, float* __restrict__ logits,
     float2* __restrict__ part, int Hq, int Hkv, int L, int L_cap, float scale_log2, int nblk,
-    const int32_t* __restrict__ keep) {
+    const int32_t* __restrict__ keep, int kvdiv) {
   if (keep && keep[blockIdx.y]) return;
   constexpr int D = 128;
   const int bg = blockIdx.y, blk = blockIdx.x;
@@ -305,7 +312,7 @@ __global__ __launch_bounds__(kSvThreads) void softvote_logits_mfma_kernel(
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int quad = lane >> 4, pe = lane & 15;
   const int tw = blk * kSvTokensPerBlock + wid * 64;
-  const bf16_t* kb = k + (size_t)bg * L_cap * D + 8 * quad;
+  const bf16_t* kb = k + (size_t)(bg / kvdiv) * L_cap * D + 8 * quad;
   uint4 kr[4][4];
 #pragma unroll
   for (int tile = 0; tile < 4; ++tile) {
@@ -459,7 +466,8 @@ typedef __attribute__((ext_vector_type(4))) double f64x4_t;
 template <int DP>
 __global__ __launch_bounds__(kCsThreads) void score_rows_mfma_kernel(
     const bf16_t* __restrict__ q_imp, const bf16_t* __restrict__ kimp, float* __restrict__ scores,
-    int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal) {
+    int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal,
+    int kvdiv) {
   constexpr int KG = DP / 4;   // d' values per lane group
   const int bg = blockIdx.z, i0 = blockIdx.y * kCsRows;
   const int b = bg / Hkv, g = bg - b * Hkv;
@@ -494,7 +502,7 @@ __global__ __launch_bounds__(kCsThreads) void score_rows_mfma_kernel(
       qa[qb][e] = a;
     }
   }
-  const bf16_t* kb = kimp + (long long)bg * L_cap * DP + KG * g4;
+  const bf16_t* kb = kimp + (long long)(bg / kvdiv) * L_cap * DP + KG * g4;
   float* srow0 = scores + ((long long)bg * Lq) * L;
   const int i_last = min(i0 + kCsRows, Lq) - 1;
   const int t_vis = causal ? min(L, q_pos0 + i_last + 1) : L;   // tokens any row sees
@@ -552,19 +560,19 @@ __global__ __launch_bounds__(kCsThreads) void score_rows_mfma_kernel(
 template <int DP>
 hipError_t rows_t(hipStream_t s, const void* q_imp, const void* kimp, float* scores, int B,
                   int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
-                  int causal) {
+                  int causal, int kvdiv) {
   dim3 grid((L + kCsTokBlk - 1) / kCsTokBlk, (Lq + kCsRows - 1) / kCsRows, B * Hkv);
   hipLaunchKernelGGL((score_rows_mfma_kernel<DP>), grid, dim3(kCsThreads), 0, s,
                      (const bf16_t*)q_imp, (const bf16_t*)kimp, scores, Hq, Hkv, G, slot, Lq, L,
-                     L_cap, q_pos0, causal);
+                     L_cap, q_pos0, causal, kvdiv);
   return hipGetLastError();
 }
 
 template <typename T, int DP, int DA = 0>
 hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scores, int B,
                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
-                 int causal, uint32_t* hist, const int32_t* keep, const void* k_cache = nullptr,
-                 const void* w_k = nullptr) {
+                 int causal, uint32_t* hist, const int32_t* keep, int kvdiv,
+                 const void* k_cache = nullptr, const void* w_k = nullptr) {
   constexpr int LPT = DP / Vec16<T>::N;
   // a tile is what one block-wide step covers (kRawUnroll loads per thread); a workgroup
   // loops over enough tiles that a row has at most kRawRowWg workgroups -- this bounds the
@@ -577,14 +585,14 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
   hipLaunchKernelGGL((score_raw_kernel<T, DP, DA>), grid, dim3(kRawThreads), 0, s,
                      (const T*)q_imp, (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap,
                      q_pos0, causal, tpb, hist, keep, (const T*)k_cache, (const T*)w_k,
-                     (T*)const_cast<void*>(kimp));
+                     (T*)const_cast<void*>(kimp), kvdiv);
   return hipGetLastError();
 }
 
 template <typename T, int D, int R>
 hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int B, int Hq,
                 int Hkv, int L, int L_cap, float scale, void* ws, uint32_t* hist,
-                const int32_t* keep) {
+                const int32_t* keep, int kvdiv) {
   const int nblk = (L + kSvTokensPerBlock - 1) / kSvTokensPerBlock;
   float* logits = (float*)ws;
   float2* part = (float2*)(logits + (size_t)B * Hkv * R * L);
@@ -593,11 +601,11 @@ hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int 
   if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
     hipLaunchKernelGGL((softvote_logits_mfma_kernel<R>), grid, dim3(kSvThreads), 0, s,
                        (const bf16_t*)q, (const bf16_t*)k, logits, part, Hq, Hkv, L, L_cap,
-                       scale_log2, nblk, keep);
+                       scale_log2, nblk, keep, kvdiv);
   } else {
     hipLaunchKernelGGL((softvote_logits_kernel<T, D, R>), grid, dim3(kSvThreads), 0, s,
                        (const T*)q, (const T*)k, logits, part, Hq, Hkv, L, L_cap, scale_log2,
-                       nblk, keep);
+                       nblk, keep, kvdiv);
   }
   hipLaunchKernelGGL((softvote_combine_kernel<R>), grid, dim3(kSvThreads), 0, s, logits, part,
                      scores, L, nblk, hist, keep);
@@ -611,18 +619,18 @@ bool R_ok(int Hq, int Hkv) { return Hq % Hkv == 0 && Hq / Hkv <= 8; }
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
                             int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist,
-                            const int32_t* keep) {
+                            const int32_t* keep, int kvdiv) {
   if (dtype == 1 && Lq > 1 && R_ok(Hq, Hkv)) {
     // several query rows: the matrix-core kernel (it builds no first-digit histogram)
-    if (dp == 32) return rows_t<32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
-    if (dp == 16) return rows_t<16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal);
+    if (dp == 32) return rows_t<32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, kvdiv);
+    if (dp == 16) return rows_t<16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, kvdiv);
   }
   if (dtype == 1) {
-    if (dp == 32) return raw_t<bf16_t, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
-    if (dp == 16) return raw_t<bf16_t, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
+    if (dp == 32) return raw_t<bf16_t, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep, kvdiv);
+    if (dp == 16) return raw_t<bf16_t, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep, kvdiv);
   } else {
-    if (dp == 32) return raw_t<float, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
-    if (dp == 16) return raw_t<float, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep);
+    if (dp == 32) return raw_t<float, 32>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep, kvdiv);
+    if (dp == 16) return raw_t<float, 16>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, Lq, L, L_cap, q_pos0, causal, hist, keep, kvdiv);
   }
   return hipErrorInvalidValue;
 }
@@ -630,11 +638,12 @@ hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const v
 hipError_t launch_project_score(hipStream_t s, int dtype, const void* q_imp,
                                 const void* k_cache, const void* w_k, void* kimp,
                                 float* scores, int B, int Hq, int Hkv, int G, int slot, int L,
-                                int L_cap, int D, int dp, uint32_t* hist, const int32_t* keep) {
+                                int L_cap, int D, int dp, uint32_t* hist, const int32_t* keep,
+                                int kvdiv) {
 #define BUTLER_PS(T, DP, DD)                                                                 \
   if (dp == DP && D == DD)                                                                 \
     return raw_t<T, DP, DD>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, 1, L, L_cap, 0, 0,  \
-                            hist, keep, k_cache, w_k);
+                            hist, keep, kvdiv, k_cache, w_k);
   if (dtype == 1) {
     BUTLER_PS(bf16_t, 32, 128) BUTLER_PS(bf16_t, 16, 128) BUTLER_PS(bf16_t, 32, 64) BUTLER_PS(bf16_t, 16, 64)
   } else {
@@ -653,10 +662,10 @@ size_t softvote_workspace(int B, int Hq, int Hkv, int L) {
 hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const void* k,
                                  float* scores, int B, int Hq, int Hkv, int L, int L_cap,
                                  int D, float scale, void* ws, uint32_t* hist,
-                                 const int32_t* keep) {
+                                 const int32_t* keep, int kvdiv) {
   const int R = Hq / Hkv;
 #define BUTLER_SV(T, DD, RR)                                                       \
-  if (D == DD && R == RR) return sv_t<T, DD, RR>(s, q, k, scores, B, Hq, Hkv, L, L_cap, scale, ws, hist, keep);
+  if (D == DD && R == RR) return sv_t<T, DD, RR>(s, q, k, scores, B, Hq, Hkv, L, L_cap, scale, ws, hist, keep, kvdiv);
   if (dtype == 1) {
     BUTLER_SV(bf16_t, 128, 1) BUTLER_SV(bf16_t, 128, 2) BUTLER_SV(bf16_t, 128, 4) BUTLER_SV(bf16_t, 128, 8)
     BUTLER_SV(bf16_t, 64, 1) BUTLER_SV(bf16_t, 64, 2) BUTLER_SV(bf16_t, 64, 4) BUTLER_SV(bf16_t, 64, 8)

@@ -717,8 +717,9 @@ struct MbAttn {
   const bf16_t* k;      // [B, Hkv, L_cap, 128]
   const bf16_t* v;
   float* part;          // [rows][nchunk][R][128 + 4]: (max, sum, -, -, acc[128]) per head
-  int Hq, Hkv, L_cap;
+  int Hq, Hkv, L_cap;   // Hkv: selection heads; kvdiv of them share a cache row
   float scale_log2;
+  int kvdiv;
 };
 
 constexpr int kMaRound = kMbWaves * 16;   // list positions per workgroup round (a tile per wave)
@@ -911,8 +912,8 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
       s_list[j] = last;
     __syncthreads();
     const int quad = lane >> 4, pe = lane & 15;
-    const bf16_t* kb = at.k + (long long)row * at.L_cap * 128;
-    const bf16_t* vb = at.v + (long long)row * at.L_cap * 128;
+    const bf16_t* kb = at.k + (long long)(row / at.kvdiv) * at.L_cap * 128;
+    const bf16_t* vb = at.v + (long long)(row / at.kvdiv) * at.L_cap * 128;
     float m = neg_inf(), l = 0.f;
     float acc[R][8];
 #pragma unroll
@@ -995,14 +996,14 @@ hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int
                                 int n_sink, int n_window, int fo, int32_t* idx, int32_t* count, int B,
                                 int Hq, int Hkv, int L, int cap, uint32_t* hist, const void* q,
                                 const void* k, const void* v, float* out, int L_cap,
-                                float scale, void* ws) {
+                                float scale, void* ws, int kvdiv) {
   const long long rows = (long long)B * Hkv;
   const int kpt = kpt_attend(L);
   const int nchunk = (int)nchunk_k(L, kpt);
   const MbWs w = carve_k(ws, rows, L, kpt);
   float* part = (float*)((char*)ws + mb_bytes_k(rows, L, kpt));
   const MbAttn at{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, part, Hq, Hkv, L_cap,
-                  scale * 1.4426950408889634f};
+                  scale * 1.4426950408889634f, kvdiv};
   const dim3 grid((unsigned)(rows * nchunk));
   uint32_t* gh = hist ? hist : w.hist1;
   const int R = Hq / Hkv;

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert qa.butler_abi_version() == 4
+    assert qa.butler_abi_version() == 5
     assert qa.butler_status_string(0) == "BUTLER_OK"
     assert qa.butler_status_string(-3) == "BUTLER_ERR_WORKSPACE"
     assert qa.butler_status_string(123) == "BUTLER_ERR_UNKNOWN"
@@ -48,10 +48,11 @@ def test_project_keys_validation():
     assert f(None, 1, FAKE, FAKE, FAKE, 0, 8, 100, 128, 32, 0, 1) == INV      # B
 
 
-def _score(mode=0, dtype=1, q=FAKE, keys=FAKE, scores=FAKE, B=1, Hq=32, Hkv=8, G=1, slot=0,
-           Lq=1, Lk=1000, L_cap=1000, dk=32, q_pos0=0, causal=0, scale=0.1, ws=None, n=None):
-    return L.butler_score(None, mode, dtype, q, keys, scores, None, None, B, Hq, Hkv, G, slot,
-                          Lq, Lk, L_cap, dk, q_pos0, causal, scale, ws, n)
+def _score(mode=0, dtype=1, q=FAKE, keys=FAKE, scores=FAKE, B=1, Hq=32, Hkv=8, sg=0, G=1,
+           slot=0, Lq=1, Lk=1000, L_cap=1000, dk=32, q_pos0=0, causal=0, scale=0.1, ws=None,
+           n=None):
+    return L.butler_score(None, mode, dtype, q, keys, scores, None, None, B, Hq, Hkv, sg, G,
+                          slot, Lq, Lk, L_cap, dk, q_pos0, causal, scale, ws, n)
 
 
 def test_score_validation_and_workspace_query():
@@ -68,6 +69,14 @@ def test_score_validation_and_workspace_query():
     small = ctypes.c_size_t(16)
     assert _score(mode=1, dk=128, ws=FAKE, n=ctypes.byref(small)) == WSE
     assert _score(q=None) == INV
+    # sel_group: 0 or a divisor of R = 4
+    assert _score(sg=3) == INV and _score(sg=8) == INV and _score(sg=-1) == INV
+    # per-query-head softvote: the same logits workspace, Hs = 32 rows of one head each
+    n1 = ctypes.c_size_t(0)
+    assert _score(mode=1, dk=128, sg=1, n=ctypes.byref(n1)) == OK
+    assert n1.value >= 32 * Lk * 4
+    assert _score(B=2100, sg=1) == UNS                  # B * Hs > 65535 (raw grid)
+    assert _score(B=2100, sg=0, q=None) == INV          # sizes pass, then the null q
 
 
 def test_select_validation():
@@ -88,18 +97,25 @@ def test_select_validation():
 def test_attention_validation_and_workspace_query():
     f = L.butler_sparse_decode_attn
     n = ctypes.c_size_t(0)
-    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 128, 1, 32768, 32768,
-             16452, 0, 0.088, None, ctypes.byref(n)) == OK
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 0, 128, 1, 32768,
+             32768, 16452, 0, 0.088, None, ctypes.byref(n)) == OK
     # one (max, sum, acc[D]) partial per (row, split, head): a whole number of splits >= 1
     per_split = 8 * 4 * (128 + 4) * 4
     assert n.value >= per_split and n.value % per_split == 0
-    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, 32, 8, 128, 1, 32768, 32768,
-             16452, 0, 0.088, None, None) == INV                            # idx without count
-    assert f(None, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1, 32, 8, 128, 4, 20000, 20000,
-             0, 0, 0.088, None, None) == UNS                                # bitmask L too long
-    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 96, 1, 100, 100,
+    # per query head: 32 rows of one head each, the same bytes per split
+    n1 = ctypes.c_size_t(0)
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 1, 128, 1, 32768,
+             32768, 16452, 0, 0.088, None, ctypes.byref(n1)) == OK
+    assert n1.value >= per_split and n1.value % (32 * (128 + 4) * 4) == 0
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 3, 128, 1, 32768,
+             32768, 16452, 0, 0.088, None, ctypes.byref(n1)) == INV         # sel_group 3
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, 32, 8, 0, 128, 1, 32768,
+             32768, 16452, 0, 0.088, None, None) == INV                     # idx without count
+    assert f(None, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1, 32, 8, 0, 128, 4, 20000,
+             20000, 0, 0, 0.088, None, None) == UNS                         # bitmask L too long
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 0, 96, 1, 100, 100,
              100, 0, 0.088, None, None) == UNS                              # D
-    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 128, 1, 100, 100,
+    assert f(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 32, 8, 0, 128, 1, 100, 100,
              100, 0, -1.0, None, None) == INV                               # scale
 
 
@@ -120,12 +136,13 @@ def test_produce_validation_and_workspace_query():
 
 def test_selection_cache_validation():
     f = L.butler_selection_cache
-    assert f(None, 1, None, FAKE, FAKE, 16, 32, 8, 128, 0.98) == INV         # null q
-    assert f(None, 1, FAKE, FAKE, MIS, 16, 32, 8, 128, 0.98) == INV          # misaligned keep
-    assert f(None, 1, FAKE, FAKE, FAKE, 16, 30, 8, 128, 0.98) == INV         # Hq % Hkv
-    assert f(None, 1, FAKE, FAKE, FAKE, 16, 32, 8, 96, 0.98) == UNS          # D
-    assert f(None, 5, FAKE, FAKE, FAKE, 16, 32, 8, 128, 0.98) == UNS         # dtype
-    assert f(None, 1, FAKE, FAKE, FAKE, 16, 32, 8, 128, float("nan")) == INV  # threshold
+    assert f(None, 1, None, FAKE, FAKE, 16, 32, 8, 0, 128, 0.98) == INV      # null q
+    assert f(None, 1, FAKE, FAKE, MIS, 16, 32, 8, 0, 128, 0.98) == INV       # misaligned keep
+    assert f(None, 1, FAKE, FAKE, FAKE, 16, 30, 8, 0, 128, 0.98) == INV      # Hq % Hkv
+    assert f(None, 1, FAKE, FAKE, FAKE, 16, 32, 8, 3, 128, 0.98) == INV      # sel_group 3
+    assert f(None, 1, FAKE, FAKE, FAKE, 16, 32, 8, 0, 96, 0.98) == UNS       # D
+    assert f(None, 5, FAKE, FAKE, FAKE, 16, 32, 8, 0, 128, 0.98) == UNS      # dtype
+    assert f(None, 1, FAKE, FAKE, FAKE, 16, 32, 8, 0, 128, float("nan")) == INV  # threshold
 
 
 
@@ -148,9 +165,9 @@ def test_project_and_score_validation():
     f = L.butler_project_and_score
     P = [FAKE + 256 * i for i in range(5)]      # q_imp, k_cache, w_k, kimp, scores
 
-    def call(*, dtype=1, ptrs=P, hist=None, B=1, Hq=32, Hkv=8, G=1, slot=0, Lr=100, L_cap=100,
-             D=128, dp=32):
-        return f(None, dtype, *ptrs, hist, None, B, Hq, Hkv, G, slot, Lr, L_cap, D, dp)
+    def call(*, dtype=1, ptrs=P, hist=None, B=1, Hq=32, Hkv=8, sg=0, G=1, slot=0, Lr=100,
+             L_cap=100, D=128, dp=32):
+        return f(None, dtype, *ptrs, hist, None, B, Hq, Hkv, sg, G, slot, Lr, L_cap, D, dp)
     assert call(dtype=7) == UNS
     assert call(Lr=101) == INV                                   # L > L_cap
     assert call(slot=1) == INV                                   # slot >= G
@@ -163,17 +180,19 @@ def test_project_and_score_validation():
     assert call(ptrs=[P[0], None, P[2], P[3], P[4]]) == INV
     assert call(hist=MIS) == INV
     assert call(B=9000) == UNS                                   # B * Hkv > 65535
+    assert call(B=2100, sg=1) == UNS                             # B * Hs > 65535
+    assert call(sg=3) == INV and call(sg=16) == INV              # not a divisor of R = 4
 
 
 def test_select_attend_validation_and_workspace_query():
     f = L.butler_select_attend
     P = [FAKE + 256 * i for i in range(7)]      # scores, idx, count, q, k, v, out
 
-    def call(*, dtype=1, num=1, den=2, ptrs=P, B=1, Hq=32, Hkv=8, D=128, Lr=32768,
+    def call(*, dtype=1, num=1, den=2, ptrs=P, B=1, Hq=32, Hkv=8, sg=0, D=128, Lr=32768,
              L_cap=32768, cap=16452, scale=0.088, ws=FAKE, n=None):
         n = n if n is not None else ctypes.c_size_t(1 << 40)
         return f(None, dtype, ptrs[0], None, num, den, 4, 64, 0, ptrs[1], ptrs[2], ptrs[3],
-                 ptrs[4], ptrs[5], ptrs[6], B, Hq, Hkv, D, Lr, L_cap, cap, scale, ws,
+                 ptrs[4], ptrs[5], ptrs[6], B, Hq, Hkv, sg, D, Lr, L_cap, cap, scale, ws,
                  ctypes.byref(n))
     n = ctypes.c_size_t(0)
     assert call(ws=None, n=n) == OK and n.value > 0                       # size query (fused)
@@ -190,3 +209,6 @@ def test_select_attend_validation_and_workspace_query():
     assert call(ptrs=[P[0], None] + P[2:]) == INV                        # idx required
     assert call(ptrs=[P[0], P[1], P[2], MIS] + P[4:]) == INV             # misaligned q
     assert call(ws=FAKE, n=ctypes.c_size_t(16)) == WSE                   # workspace too small
+    n1 = ctypes.c_size_t(0)
+    assert call(ws=None, n=n1, sg=1) == OK and n1.value > fused          # 32 selection rows
+    assert call(sg=3) == INV
