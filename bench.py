@@ -48,7 +48,8 @@ def log(*a):
 class Layer:
     """Device buffers of one layer replica and the calls of one decode step."""
 
-    def __init__(self, w, layer: int, L: int, device: str, excludes_forced: bool = False):
+    def __init__(self, w, layer: int, L: int, device: str, excludes_forced: bool = False,
+                 sel_group: int = 0):
         import torch
         import synthetic
         import query_aware_sparse_imp_amd as qa
@@ -56,6 +57,9 @@ class Layer:
         # the budget reading where sink and window sit outside it: the scorer's first-digit
         # histogram ranks every token, so the selection counts by itself
         self.fo = excludes_forced
+        # query heads per selected set: 0 = the KV head's group, 1 = every query head
+        self.sg = sel_group
+        self.Hs = qa.selection_heads(w.Hq, w.Hkv, sel_group)
         t0 = time.time()
         inp = synthetic.decode_layer(w, layer, L=L)
         self.host = inp
@@ -67,11 +71,11 @@ class Layer:
         self.kimp = torch.empty(w.B, w.Hkv, L, w.dprime, dtype=w.dtype, device=device)
         qa.butler_project_keys(self.k, self.wk, self.kimp, 0, L)      # setup, untimed
         self.cap = w.cap(L)
-        self.scores = torch.empty(w.B, w.Hkv, 1, L, dtype=torch.float32, device=device)
-        self.idx = torch.empty(w.B, w.Hkv, 1, self.cap, dtype=torch.int32, device=device)
-        self.count = torch.empty(w.B, w.Hkv, 1, dtype=torch.int32, device=device)
+        self.scores = torch.empty(w.B, self.Hs, 1, L, dtype=torch.float32, device=device)
+        self.idx = torch.empty(w.B, self.Hs, 1, self.cap, dtype=torch.int32, device=device)
+        self.count = torch.empty(w.B, self.Hs, 1, dtype=torch.int32, device=device)
         # first-digit histogram handed from the scorer to the selection (kept zeroed by it)
-        self.hist = torch.zeros(w.B, w.Hkv, 1, 2048, dtype=torch.int32, device=device)
+        self.hist = torch.zeros(w.B, self.Hs, 1, 2048, dtype=torch.int32, device=device)
         self.out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
         log(f"  layer replica {layer} at L={L} ready in {time.time() - t0:.1f}s")
 
@@ -86,20 +90,23 @@ class Layer:
             # the appended token's K_imp row is projected inside the scoring launch
             ("project+score", lambda: qa.butler_project_and_score(
                 self.qi, self.k, self.wk, self.kimp, self.scores, Hkv=w.Hkv, L=L,
-                radix_hist=None if self.fo else self.hist)),
+                radix_hist=None if self.fo else self.hist, sel_group=self.sg)),
             # selection and attention in one call: the selection's finishing pass attends to
             # its own chunk of the row, a merge kernel combines the chunks
             ("select+attend", lambda: qa.butler_select_attend(
                 self.scores, w.budget_num, w.budget_den, w.n_sink, w.n_window, self.count,
                 self.idx, self.q, self.k, self.v, self.out, L=L, softmax_scale=w.scale,
-                radix_hist=None if self.fo else self.hist, budget_excludes_forced=self.fo)),
+                radix_hist=None if self.fo else self.hist, budget_excludes_forced=self.fo,
+                sel_group=self.sg)),
         ]
 
     def algorithmic_bytes(self):
         """Bytes a step must move: the K_imp stream, the new key row and its K_imp row,
         the selected K and V rows, the index list written and read back, q and out.  The
         select+attend call's share: the scores read once, the selected K and V rows, the
-        index list written, q and out."""
+        index list written, q and out.  K_imp counts once per KV head whatever the
+        selection heads; the gather counts the rows of every selected set (a set per
+        selection head)."""
         w = self.w
         n_sel = int(self.count.sum().item())
         elt = 2 if w.dtype.itemsize == 2 else 4
@@ -108,13 +115,13 @@ class Layer:
         gather = n_sel * 2 * w.D * elt
         idx = n_sel * 4 * 2
         qo = w.B * w.Hq * w.D * (elt + 4)
-        call = w.B * w.Hkv * self.L * 4 + gather + n_sel * 4 + qo
+        call = w.B * self.Hs * self.L * 4 + gather + n_sel * 4 + qo
         return {"step": kimp + proj + gather + idx + qo, "call": call, "n_sel": n_sel}
 
 
-def run_config(w, L, replicas, steps, warmup, device, excludes_forced=False):
+def run_config(w, L, replicas, steps, warmup, device, excludes_forced=False, sel_group=0):
     import torch
-    layers = [Layer(w, r, L, device, excludes_forced) for r in range(replicas)]
+    layers = [Layer(w, r, L, device, excludes_forced, sel_group) for r in range(replicas)]
     # eager warm-up: allocates every workspace before capture
     for lay in layers:
         for _, fn in lay.calls():
@@ -549,9 +556,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--L", type=int, default=None)
-    ap.add_argument("--configs", default="2i,2f,3,4,5",
+    ap.add_argument("--configs", default="2i,2f,2h,3,4,5",
                     help="other workloads to measure: 2i prediction interval, 2f budget "
-                         "excluding sink and window, 3 soft-voting, 4 full depth, 5 prefill")
+                         "excluding sink and window, 2h a selected set per query head, "
+                         "3 soft-voting, 4 full depth, 5 prefill")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run a 256 MiB device copy first (HBM counter calibration)")
     a = ap.parse_args(argv)
@@ -614,6 +622,15 @@ def main(argv=None) -> int:
                             f"and the window", **{k: r[k] for k in (
                                 "L", "steps_per_s", "ms_per_step", "kernel_us",
                                 "selected_per_step", "step_GBps")}}
+        elif c == "2h":
+            r, lays = run_config(w, L, 8, max(a.steps // 2, 20), max(a.warmup // 2, 4), dev,
+                                 sel_group=1)
+            for lay in lays:
+                lay.free()
+            others["layer_decode_per_query_head_selection"] = {
+                "workload": f"{w.name}, a selected set per query head (32 sets per step)",
+                **{k: r[k] for k in ("L", "steps_per_s", "ms_per_step", "kernel_us",
+                                     "selected_per_step", "step_GBps", "call_GBps")}}
         elif c == "3":
             others["softvote_decode"] = run_softvote(dev)
             others["softvote_decode_selection_cache"] = run_softvote(dev, cache_threshold=0.98)
