@@ -410,6 +410,28 @@ def selection_cache(q, q_ref, Hkv: int, threshold: float, sel_group: int = 0):
     return keep, new_ref, cos
 
 
+def fetch_rows(k_cache, v_cache, sel, Hq: int, cap: int, sel_group: int = 0):
+    """Selected-row fetch from a KV cache kept off the GPU (TokenButler arXiv abstract:
+    latency against dense attention with the KV cache offloaded to the CPU).  Only the
+    rows of each selected set cross to the GPU, packed in set order: for selection head
+    j of batch b, k_sel[b, j, p] = k_cache[b, kv(j), sel[b][j][p]] for p < |S|; slots
+    p >= |S| stay zero here.  k_cache, v_cache: [B, Hkv, L, D]; returns (k_sel, v_sel),
+    each [B, Hs, cap, D] float64."""
+    k = np.asarray(k_cache, np.float64)
+    v = np.asarray(v_cache, np.float64)
+    B, Hkv, _, D = k.shape
+    Hs, gs = selection_groups(Hq, Hkv, sel_group)
+    R = Hq // Hkv
+    ks = np.zeros((B, Hs, cap, D))
+    vs = np.zeros((B, Hs, cap, D))
+    for b in range(B):
+        for j in range(Hs):
+            rows = np.asarray(sel[b][j], np.int64)[:cap]
+            ks[b, j, :len(rows)] = k[b, j * gs // R, rows]
+            vs[b, j, :len(rows)] = v[b, j * gs // R, rows]
+    return ks, vs
+
+
 def expand_neighbors(sel, L: int, width: int, n_window: int) -> np.ndarray:
     """Neighbour fetching for the prediction interval (TokenButler arXiv abstract page:
     prediction interval with neighbor fetching).  The abstract only names the method; the

@@ -684,6 +684,44 @@ def test_selection_cache_pins():
     assert np.allclose(c_ab, want, rtol=0, atol=1e-15)
 
 
+def test_fetch_rows_pins():
+    """Selected-row fetch: a hand-worked gather (rows in set order, the KV head of each
+    selection head, slots past the set left zero), and attention over the packed rows with
+    positions 0..|S|-1 equals attention over the cache with the set (torch SDPA with a
+    mask, per query head)."""
+    k = np.arange(2 * 6 * 3, dtype=np.float64).reshape(1, 2, 6, 3)
+    k = np.concatenate([k, k + 1000.0], axis=0)                  # B = 2
+    v = -k
+    sel = [[np.array([1, 4]), np.array([0]), np.array([5, 2, 3]), np.array([])],
+           [np.array([3]), np.array([0, 1]), np.array([2]), np.array([4, 5])]]
+    ks, vs = oracle.fetch_rows(k, v, sel, Hq=4, cap=3, sel_group=1)   # Hkv = 2, R = 2
+    assert ks.shape == (2, 4, 3, 3)
+    # selection head j reads KV head j // 2
+    assert np.array_equal(ks[0, 0, :2], k[0, 0, [1, 4]]) and not ks[0, 0, 2].any()
+    assert np.array_equal(ks[0, 1, :1], k[0, 0, [0]]) and not ks[0, 1, 1:].any()
+    assert np.array_equal(ks[0, 2], k[0, 1, [5, 2, 3]])
+    assert not ks[0, 3].any()
+    assert np.array_equal(vs[1, 3, :2], v[1, 1, [4, 5]])
+    # the default grouping: one set per KV head
+    ks2, _ = oracle.fetch_rows(k, v, [[np.array([2, 0]), np.array([1])]] * 2, Hq=4, cap=2)
+    assert np.array_equal(ks2[1, 0], k[1, 0, [2, 0]]) and np.array_equal(ks2[1, 1, :1], k[1, 1, [1]])
+    # attention over the packed rows == attention over the cache with the set
+    rng = np.random.default_rng(48)
+    B, Hq, Hkv, L, D = 1, 4, 2, 20, 8
+    kc = rng.standard_normal((B, Hkv, L, D)); vc = rng.standard_normal((B, Hkv, L, D))
+    q = rng.standard_normal((B, Hq, D))
+    sets = [[np.sort(rng.choice(L, 7, replace=False)) for _ in range(Hq)]]
+    kp, vp = oracle.fetch_rows(kc, vc, sets, Hq=Hq, cap=7, sel_group=1)
+    packed = oracle.sparse_decode_attn(q, kp, vp, [[np.arange(7)] * Hq], 0.4)
+    mask = torch.zeros(B, Hq, 1, L, dtype=torch.bool)
+    for h in range(Hq):
+        mask[0, h, 0, sets[0][h]] = True
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None, :], torch.from_numpy(np.repeat(kc, 2, axis=1)),
+        torch.from_numpy(np.repeat(vc, 2, axis=1)), attn_mask=mask, scale=0.4)[:, :, 0]
+    np.testing.assert_allclose(packed, want.numpy(), rtol=0, atol=1e-12)
+
+
 def test_expand_neighbors_pins():
     """Neighbour fetching: hand-worked sets (edges clipped, overlaps merged, the window at
     the current length, width 0, unordered and out-of-range input), then random rows
