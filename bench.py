@@ -331,6 +331,103 @@ def run_softvote(device, cache_threshold=None):
     return res
 
 
+def run_offload(w, L, device, steps=10):
+    """Decode of one layer whose K/V cache lives in pinned host memory (TokenButler arXiv
+    abstract: latency against dense attention with the KV cache offloaded to the CPU).
+    K_imp, the queries and the selection stay on the GPU.
+      sparse: score (raw) -> select -> butler_fetch_rows (the selected K and V rows read
+              across the host link into packed device buffers) -> attention on the packed
+              rows;
+      dense:  the whole K and V copied to the GPU (hipMemcpyAsync from pinned memory),
+              then attention over every token.
+    Inputs drawn on the GPU from a seeded torch generator (N(0,1) K, V, queries; Q_imp and
+    W_K as in the layer workload, no heavy hitters), K and V then copied to pinned host
+    memory.  Eager calls timed with events over `steps` steps after 2 warm-up steps."""
+    import torch
+    import query_aware_sparse_imp_amd as qa
+    g = torch.Generator(device=device)
+    g.manual_seed(L)
+    dt = w.dtype
+    rn = lambda *shape: torch.randn(*shape, generator=g, device=device)
+    t0 = time.time()
+    k_dev = rn(w.B, w.Hkv, L, w.D).to(dt)
+    v_dev = rn(w.B, w.Hkv, L, w.D).to(dt)
+    q = rn(w.B, w.Hq, 1, w.D).to(dt)
+    wk = (rn(w.D, w.dprime) / math.sqrt(w.D)).to(dt)
+    qi = (q.float()[:, :, 0] @ wk.float()).to(dt).reshape(w.B, w.Hq, 1, 1, w.dprime)
+    kimp = torch.empty(w.B, w.Hkv, L, w.dprime, dtype=dt, device=device)
+    qa.butler_project_keys(k_dev, wk, kimp, 0, L)
+    k_host = torch.empty(k_dev.shape, dtype=dt, pin_memory=True)
+    v_host = torch.empty(v_dev.shape, dtype=dt, pin_memory=True)
+    k_host.copy_(k_dev)
+    v_host.copy_(v_dev)
+    torch.cuda.synchronize()
+    log(f"  offload inputs at L={L} ready in {time.time() - t0:.1f}s")
+    cap = w.cap(L)
+    Hs = w.Hkv
+    scores = torch.empty(w.B, Hs, 1, L, dtype=torch.float32, device=device)
+    hist = torch.zeros(w.B, Hs, 1, 2048, dtype=torch.int32, device=device)
+    idx = torch.empty(w.B, Hs, 1, cap, dtype=torch.int32, device=device)
+    cnt = torch.empty(w.B, Hs, 1, dtype=torch.int32, device=device)
+    k_sel = torch.empty(w.B, Hs, cap, w.D, dtype=dt, device=device)
+    v_sel = torch.empty_like(k_sel)
+    iota = torch.arange(cap, dtype=torch.int32, device=device).expand(w.B, Hs, 1, cap).contiguous()
+    iota_L = torch.arange(L, dtype=torch.int32, device=device).expand(w.B, w.Hkv, 1, L).contiguous()
+    cnt_L = torch.full((w.B, w.Hkv, 1), L, dtype=torch.int32, device=device)
+    out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=device)
+    out_dense = torch.empty_like(out)
+    fetch = lambda: qa.butler_fetch_rows(idx, cnt, k_host, v_host, k_sel, v_sel, Hq=w.Hq)
+    sparse = [
+        lambda: qa.butler_score(qa.BUTLER_SCORE_RAW, qi, kimp, scores, Hkv=w.Hkv, L=L,
+                                radix_hist=hist),
+        lambda: qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink, w.n_window,
+                                      cnt, idx=idx, radix_hist=hist),
+        fetch,
+        lambda: qa.butler_sparse_decode_attn(q, k_sel, v_sel, out, L=cap, idx=iota, count=cnt,
+                                             softmax_scale=w.scale)]
+    dense = [
+        lambda: k_dev.copy_(k_host, non_blocking=True),
+        lambda: v_dev.copy_(v_host, non_blocking=True),
+        lambda: qa.butler_sparse_decode_attn(q, k_dev, v_dev, out_dense, L=L, idx=iota_L,
+                                             count=cnt_L, softmax_scale=w.scale)]
+
+    def ev_ms(fns):
+        for _ in range(2):
+            for f in fns:
+                f()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            for f in fns:
+                f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+    sparse_ms = ev_ms(sparse)
+    fetch_ms = ev_ms([fetch])
+    dense_ms = ev_ms(dense)
+    copy_ms = ev_ms(dense[:2])
+    n_sel = int(cnt.sum())
+    elt = 2 if dt == torch.bfloat16 else 4
+    fetched = n_sel * 2 * w.D * elt
+    whole = 2 * w.B * w.Hkv * L * w.D * elt
+    # the same step with the cache on the GPU, for reference (sparse attention on HBM)
+    res = {
+        "workload": f"{w.name.split(' ')[0]} layer decode, K/V in pinned host memory, L={L}, "
+                    f"budget {w.budget_num}/{w.budget_den} + {w.n_sink} + {w.n_window}",
+        "L": L, "steps": steps, "selected_rows": n_sel,
+        "sparse_fetch_ms": round(sparse_ms, 4), "dense_offload_ms": round(dense_ms, 4),
+        "latency_reduction": dense_ms / sparse_ms,
+        "fetch_ms": round(fetch_ms, 4), "fetch_bytes": fetched,
+        "fetch_GBps": fetched / (fetch_ms * 1e-3) / 1e9,
+        "h2d_copy_ms": round(copy_ms, 4), "h2d_copy_bytes": whole,
+        "h2d_copy_GBps": whole / (copy_ms * 1e-3) / 1e9,
+        "timing": "eager calls, events over the steps",
+    }
+    del k_dev, v_dev, k_host, v_host
+    return res
+
+
 def run_interval(w, L, interval, widths, device, reps=8):
     """The layer decode with TokenButler's prediction interval and neighbour fetching (arXiv
     abstract; interval and width are not on the pages): the predictor scores and selects
@@ -556,10 +653,11 @@ def main(argv=None) -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--L", type=int, default=None)
-    ap.add_argument("--configs", default="2i,2f,2h,3,4,5",
+    ap.add_argument("--configs", default="2i,2f,2h,2o,3,4,5",
                     help="other workloads to measure: 2i prediction interval, 2f budget "
                          "excluding sink and window, 2h a selected set per query head, "
-                         "3 soft-voting, 4 full depth, 5 prefill")
+                         "2o K/V cache in host memory (selected-row fetch against dense "
+                         "offload), 3 soft-voting, 4 full depth, 5 prefill")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run a 256 MiB device copy first (HBM counter calibration)")
     a = ap.parse_args(argv)
@@ -631,6 +729,10 @@ def main(argv=None) -> int:
                 "workload": f"{w.name}, a selected set per query head (32 sets per step)",
                 **{k: r[k] for k in ("L", "steps_per_s", "ms_per_step", "kernel_us",
                                      "selected_per_step", "step_GBps", "call_GBps")}}
+        elif c == "2o":
+            others["layer_decode_host_kv"] = [
+                run_offload(w, L, dev),
+                run_offload(w.replace(budget_den=16, n_window=128), 262144, dev, steps=4)]
         elif c == "3":
             others["softvote_decode"] = run_softvote(dev)
             others["softvote_decode_selection_cache"] = run_softvote(dev, cache_threshold=0.98)

@@ -11,7 +11,8 @@
  *   prefix and a recent window, and attends over that set only.
  *
  * Conventions shared by every entry point
- *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library never
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller (the one exception:
+ *     butler_fetch_rows also reads a cache in pinned host memory).  The library never
  *     allocates or frees device memory, keeps no pointer after returning and never
  *     synchronises: all work is enqueued on `stream` (a hipStream_t; NULL is the null
  *     stream).  Buffers must stay alive until the stream has passed the enqueued work.
@@ -71,7 +72,7 @@ enum butler_score_mode { BUTLER_SCORE_RAW = 0, BUTLER_SCORE_SOFTVOTE = 1 };
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* butler_status_string(int status);
 
-/* ABI version, currently 5. */
+/* ABI version, currently 6. */
 int butler_abi_version(void);
 
 /*
@@ -324,6 +325,34 @@ int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, 
 int butler_expand_neighbors(void* stream, const int32_t* idx, const int32_t* count,
                             int32_t* idx_out, int32_t* count_out, int B, int Hs, int L,
                             int cap_in, int cap_out, int width, int n_window);
+
+/*
+ * butler_fetch_rows -- selected-row fetch from a KV cache kept in host memory.
+ * TokenButler arXiv abstract: against dense attention with the KV cache offloaded to the
+ * CPU, selection cuts decode latency, because only the selected tokens' K and V rows
+ * have to cross to the GPU.  For selection head j of batch b (see "Selection heads") and
+ * p < min(count[b, j], cap):
+ *   k_sel[b, j, p, :] = k_cache[b, kv(j), idx[b, j, 0, p], :]   (and v_sel from v_cache)
+ * so the rows of each selected set arrive packed in set order.  Slots p >= count are left
+ * as they were.  butler_sparse_decode_attn then attends over them with k_sel / v_sel as
+ * its caches ([B, Hs, cap, D], Hkv = Hs, sel_group = 0), positions 0 .. count-1 as its
+ * index list (any ascending list of them) and the same count.
+ *
+ *   idx     [B, Hs, 1, cap]       int32 (device), count [B, Hs, 1] int32 (device), as
+ *                                 written by butler_select_topk
+ *   k_cache [B, Hkv, L_cap, D]    dtype, pinned host memory (hipHostMalloc) that the GPU
+ *   v_cache [B, Hkv, L_cap, D]    maps -- the rows are read across the host link, with no
+ *                                 staging copy -- or device memory
+ *   k_sel   [B, Hs, cap, D]       dtype, device memory (written)
+ *   v_sel   [B, Hs, cap, D]       dtype, device memory (written)
+ * D in {64, 128}; R = Hq / Hkv in {1, 2, 4, 8}; indices outside [0, L_cap) are clamped.
+ * The memory kind of every pointer is checked with hipPointerGetAttributes (this call's
+ * validation uses the HIP runtime): pageable host memory, which no kernel may read, and
+ * unknown pointers give BUTLER_ERR_INVALID_ARG.  No workspace.
+ */
+int butler_fetch_rows(void* stream, int dtype, const int32_t* idx, const int32_t* count,
+                      const void* k_cache, const void* v_cache, void* k_sel, void* v_sel, int B,
+                      int Hq, int Hkv, int sel_group, int D, int L_cap, int cap);
 
 #ifdef __cplusplus
 }

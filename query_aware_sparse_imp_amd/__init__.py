@@ -5,7 +5,7 @@ live on the GPU, checks their shapes, dtypes and contiguity, and calls the C ent
 point of the same name in ``libbutler.so`` with raw device pointers, sizes and the
 current HIP stream.  All compute happens in the library's HIP kernels; there is no
 fallback.  Importing this package fails loudly if the library has not been built
-(``python -m query_aware_sparse_imp_amd.csrc.build``).
+(``python query_aware_sparse_imp_amd/csrc/build.py``).
 """
 from __future__ import annotations
 
@@ -36,7 +36,7 @@ BUTLER_SCORE_RAW, BUTLER_SCORE_SOFTVOTE = 0, 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m query_aware_sparse_imp_amd.csrc.build`")
+                      "`python query_aware_sparse_imp_amd/csrc/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -55,6 +55,7 @@ _SIGS = {
                              [_f, _vp, _sz], _i),
     "butler_expand_neighbors": ([_vp] * 5 + [_i] * 7, _i),
     "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 10 + [_f, _vp, _sz], _i),
+    "butler_fetch_rows": ([_vp, _i] + [_vp] * 6 + [_i] * 7, _i),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -124,6 +125,15 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
         raise ValueError("tensor must live on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr_host_ok(t: torch.Tensor) -> int:
+    """A device tensor, or a pinned host tensor (which the GPU can map)."""
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError("tensor must live on the GPU or in pinned host memory")
     return t.data_ptr()
 
 
@@ -394,3 +404,26 @@ def butler_expand_neighbors(idx: torch.Tensor, count: torch.Tensor, idx_out: tor
     _check("butler_expand_neighbors", lib.butler_expand_neighbors(
         _stream(stream), _ptr(idx), _ptr(count), _ptr(idx_out), _ptr(count_out), B, Hkv,
         int(L), cap_in, idx_out.shape[2], int(width), int(n_window)))
+
+
+def butler_fetch_rows(idx: torch.Tensor, count: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, k_sel: torch.Tensor, v_sel: torch.Tensor, *,
+                      Hq: int, sel_group: int = 0, stream=None) -> None:
+    """Packs the selected K and V rows of each selected set into k_sel / v_sel (see
+    butler.h).  k_cache, v_cache: [B, Hkv, L_cap, D] on the GPU or in pinned host memory
+    (read across the host link); idx [B, Hs, 1, cap], count [B, Hs, 1] int32;
+    k_sel, v_sel [B, Hs, cap, D] on the GPU."""
+    B, Hkv, L_cap, D = k_cache.shape
+    Hs = selection_heads(Hq, Hkv, sel_group)
+    if v_cache.shape != k_cache.shape or idx.dim() != 4 or idx.shape[:3] != (B, Hs, 1):
+        raise ValueError("shape mismatch")
+    cap = idx.shape[3]
+    if count.shape != (B, Hs, 1) or k_sel.shape != (B, Hs, cap, D) or v_sel.shape != k_sel.shape:
+        raise ValueError("shape mismatch")
+    if idx.dtype != torch.int32 or count.dtype != torch.int32:
+        raise TypeError("idx and count must be int32")
+    if not (k_cache.dtype == v_cache.dtype == k_sel.dtype == v_sel.dtype):
+        raise TypeError("dtype mismatch")
+    _check("butler_fetch_rows", lib.butler_fetch_rows(
+        _stream(stream), _dtype_code(k_cache), _ptr(idx), _ptr(count), _ptr_host_ok(k_cache),
+        _ptr_host_ok(v_cache), _ptr(k_sel), _ptr(v_sel), B, Hq, Hkv, sel_group, D, L_cap, cap))

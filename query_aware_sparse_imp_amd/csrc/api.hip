@@ -49,6 +49,23 @@ inline int workspace_phase(void* ws, size_t* ws_bytes, size_t need, int* rc) {
 inline bool valid_dtype(int d) { return d == BUTLER_F32 || d == BUTLER_BF16; }
 inline bool pow2_group(int R) { return R == 1 || R == 2 || R == 4 || R == 8; }
 
+// The address the GPU reads p at: p itself for device memory, the mapped address for
+// pinned host memory.  False for memory HIP does not know (pageable host memory), which
+// no kernel may touch.  The only validation step that calls the HIP runtime.
+inline bool gpu_view(const void* p, const void** out, bool allow_host) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();   // the failed query must not surface as a launch error
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice) { *out = p; return true; }
+  if (allow_host && a.type == hipMemoryTypeHost && a.devicePointer) {
+    *out = a.devicePointer;
+    return true;
+  }
+  return false;
+}
+
 // Query heads per selected set: 0 is the KV head's whole group (Hq/Hkv), otherwise a
 // divisor of it.  Gives the selection heads per batch entry (Hs) and how many of them
 // share one KV head (kvdiv); false when sel_group is not such a divisor.
@@ -76,7 +93,7 @@ const char* butler_status_string(int status) {
   }
 }
 
-int butler_abi_version(void) { return 5; }
+int butler_abi_version(void) { return 6; }
 
 int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
                         void* kimp, int B, int Hkv, int L_cap, int D, int dprime, int pos0,
@@ -335,6 +352,34 @@ int butler_expand_neighbors(void* stream, const int32_t* idx, const int32_t* cou
   hipStream_t s = (hipStream_t)stream;
   return finish(s, launch_expand_neighbors(s, idx, count, idx_out, count_out, B * Hs, L, cap_in,
                                            cap_out, width, n_window));
+}
+
+int butler_fetch_rows(void* stream, int dtype, const int32_t* idx, const int32_t* count,
+                      const void* k_cache, const void* v_cache, void* k_sel, void* v_sel, int B,
+                      int Hq, int Hkv, int sel_group, int D, int L_cap, int cap) {
+  if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L_cap <= 0 || cap <= 0 || Hq % Hkv)
+    return BUTLER_ERR_INVALID_ARG;
+  if (!pow2_group(Hq / Hkv) || !(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
+  int Hs, kvdiv;
+  if (!sel_heads(Hq, Hkv, sel_group, &Hs, &kvdiv)) return BUTLER_ERR_INVALID_ARG;
+  const long long rows = (long long)B * Hs;
+  const int row_bytes = D * (dtype == BUTLER_BF16 ? 2 : 4);
+  if (rows > 0x7fffffffLL || fetch_rows_blocks(rows, cap, row_bytes) > 0x7fffffffLL)
+    return BUTLER_ERR_UNSUPPORTED;
+  if (!idx || !count || !k_cache || !v_cache || !k_sel || !v_sel) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(idx) || !aligned16(count) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(k_sel) || !aligned16(v_sel))
+    return BUTLER_ERR_INVALID_ARG;
+  if (k_sel == v_sel || k_sel == k_cache || v_sel == v_cache) return BUTLER_ERR_INVALID_ARG;
+  const void *kd, *vd, *ksd, *vsd, *id, *cd;
+  if (!gpu_view(k_cache, &kd, true) || !gpu_view(v_cache, &vd, true)) return BUTLER_ERR_INVALID_ARG;
+  if (!gpu_view(k_sel, &ksd, false) || !gpu_view(v_sel, &vsd, false) ||
+      !gpu_view(idx, &id, false) || !gpu_view(count, &cd, false))
+    return BUTLER_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(s, launch_fetch_rows(s, idx, count, kd, vd, k_sel, v_sel, (int)rows, kvdiv,
+                                     row_bytes, L_cap, cap));
 }
 
 }  // extern "C"

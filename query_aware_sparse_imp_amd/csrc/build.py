@@ -1,6 +1,6 @@
 """Build libbutler.so for gfx950 in-tree with hipcc.
 
-    python -m query_aware_sparse_imp_amd.csrc.build [--jobs N]
+    python query_aware_sparse_imp_amd/csrc/build.py [--jobs N]
 
 Every .hip file in this directory is compiled to an object under ``_build/`` at the
 repository root and linked into ``query_aware_sparse_imp_amd/libbutler.so``.  It

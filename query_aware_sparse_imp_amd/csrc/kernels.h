@@ -74,4 +74,10 @@ hipError_t launch_expand_neighbors(hipStream_t s, const int32_t* idx, const int3
                                    int cap_in, int cap_out, int width, int n_window);
 int expand_max_len();
 
+// ---- selected-row fetch ------------------------------------------------------
+long long fetch_rows_blocks(long long rows, int cap, int row_bytes);
+hipError_t launch_fetch_rows(hipStream_t s, const int32_t* idx, const int32_t* count,
+                             const void* k, const void* v, void* k_sel, void* v_sel, int rows,
+                             int kvdiv, int row_bytes, int L_cap, int cap);
+
 }  // namespace butler

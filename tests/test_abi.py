@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert qa.butler_abi_version() == 5
+    assert qa.butler_abi_version() == 6
     assert qa.butler_status_string(0) == "BUTLER_OK"
     assert qa.butler_status_string(-3) == "BUTLER_ERR_WORKSPACE"
     assert qa.butler_status_string(123) == "BUTLER_ERR_UNKNOWN"
@@ -212,3 +212,26 @@ def test_select_attend_validation_and_workspace_query():
     n1 = ctypes.c_size_t(0)
     assert call(ws=None, n=n1, sg=1) == OK and n1.value > fused          # 32 selection rows
     assert call(sg=3) == INV
+
+
+def test_fetch_rows_validation():
+    """Size and pointer checks; pointers HIP does not know (here every one of them, GPU or
+    not) are rejected before any launch, so pageable host memory never reaches a kernel."""
+    f = L.butler_fetch_rows
+    P = [FAKE + 256 * i for i in range(6)]      # idx, count, k_cache, v_cache, k_sel, v_sel
+
+    def call(*, dtype=1, ptrs=P, B=1, Hq=32, Hkv=8, sg=0, D=128, L_cap=32768, cap=16452):
+        return f(None, dtype, *ptrs, B, Hq, Hkv, sg, D, L_cap, cap)
+    assert call(dtype=4) == UNS
+    assert call(D=96) == UNS
+    assert call(Hq=24) == UNS                                   # R = 3
+    assert call(Hq=30) == INV                                   # Hq % Hkv
+    assert call(sg=3) == INV                                    # not a divisor of R
+    assert call(cap=0) == INV
+    assert call(B=0) == INV
+    assert call(ptrs=[None] + P[1:]) == INV
+    assert call(ptrs=P[:4] + [MIS, P[5]]) == INV                # misaligned k_sel
+    assert call(ptrs=P[:4] + [P[4], P[4]]) == INV               # k_sel aliases v_sel
+    assert call(ptrs=P[:4] + [P[2], P[5]]) == INV               # k_sel aliases k_cache
+    assert call() == INV                                        # memory unknown to HIP
+    assert call(sg=1) == INV
