@@ -196,13 +196,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_idx_kernel(
 // S[t][h] = sum_d K[t][d] q[h][d] for the 16 rows (A operand: lane l holds 8 consecutive
 // d of row l%16, so 4 loads of 16 bytes per lane bring the tile's 16 key rows) and up to
 // 16 query-head columns (B operand: the group's R heads, zero beyond).  Four MFMAs cover
-// D = 128.  The result leaves the logits of rows 4q..4q+3 and head h in lane 16q + h:
-// every 16-lane row q runs its own online softmax for its 4 rows per tile, one lane per
-// head, and broadcasts the rescale factor and the 4 probabilities of each head across the
-// row with DPP row_newbcast.  P.V stays on the VALU in float32: lane p of row q owns
-// columns 8p..8p+7 of D and accumulates its row's 4 value rows (16-byte loads) for the R
-// heads.  Each wave takes 2 tiles per round with all 16 row loads in flight; rows and
-// waves merge with the same reduction as the VALU kernel.
+// D = 128.  The result leaves the logits of rows 4q..4q+3 and head h in lane 16q + h;
+// the wave keeps one online softmax per head (the max taken over the four 16-lane rows).
+// P.V runs on the matrix cores too: the probabilities, rounded to bf16, are already laid
+// out as the B operand of v_mfma_f32_16x16x16_bf16, and V^T comes from the lanes' value
+// rows (16-byte loads of 8 columns of D) by byte permutes -- eight MFMAs per tile, no
+// per-head VALU loop (PvStream).  Each wave keeps a ring of tiles with all 16 row loads
+// in flight; the waves merge through LDS in a fixed order.
 
 #ifndef BUTLER_MF_THREADS
 #define BUTLER_MF_THREADS 512
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
 
   __shared__ int s_list[kMfStage + kMfPad];
   __shared__ float s_m[kMfWaves * R], s_l[kMfWaves * R], red_m[R], red_l[R];
-  __shared__ float s_acc[kMfWaves * R * D];
+  __shared__ __align__(16) float s_acc[kMfWaves * R * D];
   __shared__ float red_acc[R * D];
 
   // B operand: q[h = pe][kk*32 + 8*quad .. +8], zero for columns pe >= R
@@ -268,12 +268,8 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
   const bf16_t* kb = k + (long long)(bg / kvdiv) * L_cap * D;
   const bf16_t* vb = v + (long long)(bg / kvdiv) * L_cap * D;
 
-  float m = neg_inf(), l = 0.f;   // softmax state of head pe for this row's stream
-  float acc[R][8];
-#pragma unroll
-  for (int h = 0; h < R; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  PvStream ms;   // online-softmax state of the wave's heads
+  ms.init();
 
   for (int cs = p_begin; cs < p_end; cs += kMfStage) {
     const int len = min(kMfStage, p_end - cs);
@@ -306,24 +302,14 @@ __global__ __launch_bounds__(kMfThreads) void attn_mfma_kernel(
       for (int b = 0; b < kMfBuf; ++b) {
         mf_load(t[(b + kMfBuf - 1) % kMfBuf], s_list, (r + b + kMfBuf - 1) * kMfRound + w0, kb, vb,
                 quad, pe);
-        mf_compute<R>(t[b], qf, lim0 - (r + b) * kMfRound, scale_log2, m, l, acc);
+        ms.compute(t[b], qf, lim0 - (r + b) * kMfRound, scale_log2);
       }
     }
 #pragma unroll
     for (int b = 0; b < kMfBuf - 1; ++b)
-      if (nmain + b < nr) mf_compute<R>(t[b], qf, lim0 - (nmain + b) * kMfRound, scale_log2, m, l, acc);
+      if (nmain + b < nr) ms.compute(t[b], qf, lim0 - (nmain + b) * kMfRound, scale_log2);
   }
-  // hand the per-row streams to the shared reduction: every lane of a row needs the
-  // (m, l) of every head, which live in lane h of the row
-  SoftState<R, 8> st;
-#pragma unroll
-  for (int h = 0; h < R; ++h) {
-    st.m[h] = row_bcast_rt(m, h);
-    st.l[h] = row_bcast_rt(l, h);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[h][e] = acc[h][e];
-  }
-  block_reduce<bf16_t, D, R, kMfThreads>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
+  ms.template reduce<R, kMfThreads>(s_m, s_l, s_acc, red_m, red_l, red_acc);
   float* my = part + ((long long)row * nsplit + split) * R * PS;
   for (int j = threadIdx.x; j < R * D; j += kMfThreads) my[(j / D) * PS + 4 + j % D] = red_acc[j];
   if (threadIdx.x < R) {

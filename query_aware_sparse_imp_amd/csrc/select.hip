@@ -722,8 +722,12 @@ struct MbAttn {
   int kvdiv;
 };
 
+#ifndef BUTLER_SA_RING
+#define BUTLER_SA_RING 2
+#endif
 constexpr int kMaRound = kMbWaves * 16;   // list positions per workgroup round (a tile per wave)
-constexpr int kMaPad = 2 * kMaRound;      // ring prefetch past the list end
+constexpr int kMaRing = BUTLER_SA_RING;   // tiles per wave in the load ring
+constexpr int kMaPad = (kMaRing + 1) * kMaRound;   // ring prefetch past the list end
 
 template <int KPT, int R>
 __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
@@ -882,7 +886,7 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
   const unsigned long long lt = (1ull << lane) - 1ull;
   const int nwords = (L + 31) / 32;
   // the chunk's selected tokens, ascending, for the fused attention
-  __shared__ int s_list[(R > 0) ? kMbThreads * KPT + kMaPad + kMaRound : 1];
+  __shared__ int s_list[(R > 0) ? kMbThreads * KPT + kMaPad : 1];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int u = j * kMbWaves + wid;
@@ -908,44 +912,40 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
     const int nsel = __shfl(ex + v0 + v1, 63);   // the chunk's count (inclusive scan total)
     __syncthreads();
     const int last = nsel > 0 ? s_list[nsel - 1] : 0;
-    for (int j = nsel + (int)threadIdx.x; j < kMbThreads * KPT + kMaPad + kMaRound; j += kMbThreads)
+    for (int j = nsel + (int)threadIdx.x; j < kMbThreads * KPT + kMaPad; j += kMbThreads)
       s_list[j] = last;
     __syncthreads();
     const int quad = lane >> 4, pe = lane & 15;
     const bf16_t* kb = at.k + (long long)(row / at.kvdiv) * at.L_cap * 128;
     const bf16_t* vb = at.v + (long long)(row / at.kvdiv) * at.L_cap * 128;
-    float m = neg_inf(), l = 0.f;
-    float acc[R][8];
-#pragma unroll
-    for (int h = 0; h < R; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    PvStream ms;   // online-softmax state of the wave's heads
+    ms.init();
     const int nr = (nsel + kMaRound - 1) / kMaRound;
     const int w0 = wid * 16;
     const int lim0 = nsel - w0 - 4 * quad;
-    MfTile t0, t1;
-    if (nr > 0) mf_load(t0, s_list, w0, kb, vb, quad, pe);
-    int r = 0;
-    for (; r + 2 <= nr; r += 2) {
-      mf_load(t1, s_list, (r + 1) * kMaRound + w0, kb, vb, quad, pe);
-      mf_compute<R>(t0, qf, lim0 - r * kMaRound, at.scale_log2, m, l, acc);
-      mf_load(t0, s_list, (r + 2) * kMaRound + w0, kb, vb, quad, pe);
-      mf_compute<R>(t1, qf, lim0 - (r + 1) * kMaRound, at.scale_log2, m, l, acc);
-    }
-    if (r < nr) mf_compute<R>(t0, qf, lim0 - r * kMaRound, at.scale_log2, m, l, acc);
-    // every lane of a 16-lane row needs the (m, l) of each head, held by lane h of the row
-    SoftState<R, 8> st;
+    // round rho lives in t[rho % kMaRing]; kMaRing - 1 tiles are in flight during each
+    // compute, and the main loop has no branch, so every wait is for exactly one tile.
+    // The last round loaded is nr + kMaRing - 2: inside the padded list.
+    MfTile t[kMaRing];
 #pragma unroll
-    for (int h = 0; h < R; ++h) {
-      st.m[h] = row_bcast_rt(m, h);
-      st.l[h] = row_bcast_rt(l, h);
+    for (int b = 0; b < kMaRing - 1; ++b) mf_load(t[b], s_list, b * kMaRound + w0, kb, vb, quad, pe);
+    const int nmain = nr - nr % kMaRing;
+    for (int r = 0; r < nmain; r += kMaRing) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st.acc[h][e] = acc[h][e];
+      for (int b = 0; b < kMaRing; ++b) {
+        mf_load(t[(b + kMaRing - 1) % kMaRing], s_list, (r + b + kMaRing - 1) * kMaRound + w0,
+                kb, vb, quad, pe);
+        ms.compute(t[b], qf, lim0 - (r + b) * kMaRound, at.scale_log2);
+      }
     }
+#pragma unroll
+    for (int b = 0; b < kMaRing - 1; ++b)
+      if (nmain + b < nr) ms.compute(t[b], qf, lim0 - (nmain + b) * kMaRound, at.scale_log2);
     __shared__ float s_m[kMbWaves * (R > 0 ? R : 1)], s_l[kMbWaves * (R > 0 ? R : 1)];
     __shared__ float red_m[R > 0 ? R : 1], red_l[R > 0 ? R : 1];
-    __shared__ float s_acc[kMbWaves * (R > 0 ? R : 1) * 128], red_acc[(R > 0 ? R : 1) * 128];
-    block_reduce<bf16_t, 128, R, kMbThreads>(st, s_m, s_l, s_acc, red_m, red_l, red_acc);
+    __shared__ __align__(16) float s_acc[kMbWaves * (R > 0 ? R : 1) * 128];
+    __shared__ float red_acc[(R > 0 ? R : 1) * 128];
+    ms.template reduce<R, kMbThreads>(s_m, s_l, s_acc, red_m, red_l, red_acc);
     constexpr int PS = 128 + 4;
     float* my = at.part + ((long long)row * nchunk + chunk) * R * PS;
     for (int j = threadIdx.x; j < R * 128; j += kMbThreads) my[(j / 128) * PS + 4 + j % 128] = red_acc[j];

@@ -140,6 +140,15 @@ def decode_step_gpu(inp: dict, kimp: torch.Tensor, L: int, mode: int, q_imp=None
     return {"scores": scores, "idx": idx, "count": count, "out": out, "num": num, "den": den}
 
 
+def pv_rounding_bound(v_cache: torch.Tensor) -> float:
+    """Largest difference allowed between two GPU attention outputs over the same set that
+    split it differently.  The matrix-core P.V rounds every probability to bf16 (relative
+    error <= 2^-9) against the softmax sum of the unrounded ones, so each output lies
+    within 2^-9 * max|v| of the float32 result; two of them within 2^-8 * max|v|, plus
+    float32 reordering (1e-5)."""
+    return 2.0 ** -8 * float(v_cache.float().abs().max()) + 1e-5
+
+
 def to_device(inp: dict, device="cuda") -> dict:
     for key in ("k_cache", "v_cache", "q", "w_k", "q_imp"):
         if key in inp:

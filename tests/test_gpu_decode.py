@@ -13,7 +13,7 @@ import torch
 import oracle
 import synthetic
 from parity import (ATOL, check_attend, check_project, check_select_exact, decode_step_gpu,
-                    np64, to_device)
+                    np64, pv_rounding_bound, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -222,7 +222,8 @@ def test_project_and_score_matches_separate_calls(cfg, L):
 ])
 def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
     """butler_select_attend == butler_select_topk + butler_sparse_decode_attn: idx and count
-    bit for bit, the output within float32 rounding of the separate attention and within
+    bit for bit, the output within the bf16 probability rounding of the separate attention
+    (pv_rounding_bound: the two split the set differently) and within
     the bf16 bound of the oracle's attention over the same sets; three calls in a row (the
     selection's workspace state carries over between calls)."""
     import query_aware_sparse_imp_amd as qa
@@ -270,7 +271,7 @@ def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
         assert torch.equal(cnt_a, cnt_b), rep
         assert torch.equal(idx_a, idx_b), rep
         d = float((out_a - out_b).abs().max())
-        assert d <= 1e-4, (rep, d)
+        assert d <= pv_rounding_bound(v), (rep, d)
     check_select_exact(idx_b, cnt_b, np64(scores), num, den, w.n_sink, w.n_window,
                        exclude_forced=fo)
     ic, cc = idx_b.cpu().numpy(), cnt_b.cpu().numpy()
