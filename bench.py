@@ -161,6 +161,19 @@ def run_config(w, L, replicas, steps, warmup, device, excludes_forced=False, sel
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / steps
     step_us = ev_time(g_timed)
+    # spread of the step time: 50 replays of a graph that steps every replica once, each
+    # between its own pair of events on the launch stream
+    g_round = graph_of(replicas, names)
+    rounds = []
+    for _ in range(50):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g_round.replay()
+        b.record()
+        torch.cuda.synchronize()
+        rounds.append(a.elapsed_time(b) * 1e3 / replicas)
+    rounds.sort()
+    spread = {"p10": rounds[5], "p50": rounds[25], "p90": rounds[45], "replays": 50}
     score_us = ev_time(graph_of(steps, ["project+score"]))
     for lay in layers:
         lay.hist.zero_()
@@ -173,6 +186,7 @@ def run_config(w, L, replicas, steps, warmup, device, excludes_forced=False, sel
     return {
         "L": L, "replicas": replicas, "steps": steps, "ms_per_step": ms,
         "steps_per_s": steps / elapsed, "timing": "graph events, select+attend = step - score",
+        "step_us_spread": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in spread.items()},
         "kernel_us": {k: round(v, 3) for k, v in avg_us.items()},
         "step_bytes": step_bytes, "call_bytes": call_bytes, "selected_per_step": n_sel,
         "step_GBps": step_bytes / (ms * 1e-3) / 1e9,
@@ -203,9 +217,10 @@ def traffic_record(kernel_files, name: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(layer, budget_s: float = 12.0):
-    """The oracle's per-layer decode step on the host (one thread), on a bounded sample:
-    as many whole steps of the same layer as fit in ~budget_s seconds (at least 2)."""
+def cpu_baseline(layer, budget_s: float = 12.0, threads: int = 1):
+    """The oracle's per-layer decode step on the host (`threads` BLAS threads; None: every
+    core this process may run on), on a bounded sample: as many whole steps of the same
+    layer as fit in ~budget_s seconds (at least 2)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
@@ -215,7 +230,8 @@ def cpu_baseline(layer, budget_s: float = 12.0):
     q = f64(inp["q"])[:, :, 0]
     wk = f64(inp["w_k"])
     qi = f64(inp["q_imp"])[:, :, 0, 0]
-    with threadpool_limits(1):
+    cores = threads if threads else len(os.sched_getaffinity(0))
+    with threadpool_limits(cores):
         kimp = oracle.project_keys(k[:, :, :L - 1], wk, "bf16")
         n, t0 = 0, time.perf_counter()
         while True:
@@ -229,7 +245,7 @@ def cpu_baseline(layer, budget_s: float = 12.0):
             el = time.perf_counter() - t0
             if (el >= budget_s and n >= 2) or el > 3 * budget_s:
                 break
-    return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+    return {"value": n / el, "unit": "steps/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} whole per-layer decode steps (project new key, score, select, "
                       f"attend; 8 KV heads, L={L}) of one layer replica, numpy float64, "
                       f"{el:.1f} s"}
@@ -653,8 +669,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--L", type=int, default=None)
-    ap.add_argument("--configs", default="2i,2f,2h,2o,3,4,5",
-                    help="other workloads to measure: 2i prediction interval, 2f budget "
+    ap.add_argument("--configs", default="1,2i,2f,2h,2o,3,4,5",
+                    help="other workloads to measure: 1 the tiny fp32 parity step, "
+                         "2i prediction interval, 2f budget "
                          "excluding sink and window, 2h a selected set per query head, "
                          "2o K/V cache in host memory (selected-row fetch against dense "
                          "offload), 3 soft-voting, 4 full depth, 5 prefill")
@@ -708,7 +725,15 @@ def main(argv=None) -> int:
     for c in [x for x in a.configs.split(",") if x]:
         torch.cuda.empty_cache()
         log(f"[bench] workload {c}")
-        if c == "2i":
+        if c == "1":
+            w1 = synthetic.WORKLOADS[1]
+            r, lays = run_config(w1, w1.L, 8, a.steps, a.warmup, dev)
+            for lay in lays:
+                lay.free()
+            others["tiny_fp32_decode"] = {
+                "workload": w1.name, "note": "parity configuration: launch-bound, microseconds only",
+                **{k: r[k] for k in ("L", "ms_per_step", "kernel_us", "step_us_spread")}}
+        elif c == "2i":
             others["layer_decode_prediction_interval"] = run_interval(w, L, 4, (0, 1), dev)
         elif c == "2f":
             r, lays = run_config(w, L, 8, max(a.steps // 2, 20), max(a.warmup // 2, 4), dev,
@@ -742,11 +767,13 @@ def main(argv=None) -> int:
             others["chunked_prefill"] = run_prefill(dev)
         log(f"[bench] workload {c}: {json.dumps(others)}")
 
-    cpu = None
+    cpu = cpu_all = None
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline(host0)
         log(f"[bench] cpu baseline: {json.dumps(cpu)}")
+        cpu_all = cpu_baseline(host0, budget_s=6.0, threads=None)
+        log(f"[bench] cpu baseline, all cores: {json.dumps(cpu_all)}")
 
     call_us = head["kernel_us"]["select+attend"]
     achieved = head["call_bytes"] / (call_us * 1e-6) / 1e9
@@ -779,9 +806,11 @@ def main(argv=None) -> int:
         "step_hbm": {"algorithmic_bytes": head["step_bytes"], "GB/s": head["step_GBps"],
                      "frac": head["step_GBps"] / HBM_PEAK_GBS},
         "kernel_us": head["kernel_us"],
+        "step_us_spread": head["step_us_spread"],
         "sweep": sweep,
         "configs": others,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
     }
     print(json.dumps(line), flush=True)
     return 0
