@@ -146,3 +146,31 @@ def test_pageable_host_memory_is_rejected():
                                   ks.data_ptr(), vs.data_ptr(), 1, 1, 1, 0, 64, 64, 8)
     assert rc == -1
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 64), (torch.float32, 128)])
+def test_fetch_rows_row_widths(dtype, D):
+    """The other row widths of the fetch (8 and 32 sixteen-byte pieces per row), from
+    pinned host memory, per query head (B = 1, 4 query heads on 2 KV heads)."""
+    import query_aware_sparse_imp_amd as qa
+    dev = "cuda"
+    B, Hq, Hkv, L_cap, cap = 1, 4, 2, 5000, 1500
+    g = torch.Generator().manual_seed(D)
+    k = torch.randn(B, Hkv, L_cap, D, generator=g).to(dtype)
+    v = torch.randn(B, Hkv, L_cap, D, generator=g).to(dtype)
+    idx = torch.stack([torch.sort(torch.randperm(L_cap, generator=g)[:cap])[0]
+                       for _ in range(Hq)]).to(torch.int32).reshape(B, Hq, 1, cap)
+    cnt = torch.tensor([[[cap], [1], [777], [0]]], dtype=torch.int32)
+    ks = torch.full((B, Hq, cap, D), 3.0, dtype=dtype, device=dev)
+    vs = torch.full_like(ks, 3.0)
+    qa.butler_fetch_rows(idx.to(dev), cnt.to(dev), _pinned(k), _pinned(v), ks, vs, Hq=Hq,
+                         sel_group=1)
+    torch.cuda.synchronize()
+    sets = [[idx[0, j, 0, :int(cnt[0, j, 0])].numpy() for j in range(Hq)]]
+    wk, wv = oracle.fetch_rows(np64(k), np64(v), sets, Hq, cap, sel_group=1)
+    gk, gv = np64(ks), np64(vs)
+    for j in range(Hq):
+        n = int(cnt[0, j, 0])
+        assert np.array_equal(gk[0, j, :n], wk[0, j, :n]) and np.array_equal(gv[0, j, :n], wv[0, j, :n])
+        assert (gk[0, j, n:] == 3.0).all() and (gv[0, j, n:] == 3.0).all()
+    print(f"  {dtype} D={D}: packed rows exact", flush=True)

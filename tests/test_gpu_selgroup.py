@@ -238,3 +238,61 @@ def test_selection_cache_per_query_head():
         ref_np = got_ref                                # the GPU's state carries on
         print(f"  step {s}: kept {int(got.sum())} of {got.size} heads "
               f"({int((~clear).sum())} within 1e-5 of the threshold)", flush=True)
+
+
+@pytest.mark.parametrize("dtype,D,dp", [(torch.float32, 64, 16), (torch.bfloat16, 64, 32)])
+def test_per_head_valu_paths(dtype, D, dp):
+    """sel_group = 1 on the shapes that take the VALU kernels: raw and soft-vote scoring,
+    the split attention of index lists (D = 64) and the unfused select+attend call (rows of
+    at most 4096 tokens); two KV heads of two query heads each, B = 2."""
+    import query_aware_sparse_imp_amd as qa
+    dev = "cuda"
+    B, Hq, Hkv, L = 2, 4, 2, 3001
+    print(f"[sel_group] VALU paths dtype={dtype} D={D} d'={dp} L={L}", flush=True)
+    g = torch.Generator().manual_seed(D + dp)
+    st = lambda *shape: torch.randn(*shape, generator=g).to(dtype)
+    k, v = st(B, Hkv, L, D), st(B, Hkv, L, D)
+    q = st(B, Hq, 1, D)
+    qi = st(B, Hq, 1, 1, dp)
+    kimp = st(B, Hkv, L, dp)
+    scale = 1.0 / D ** 0.5
+    kd, vd, qd, qid, kid = (t.to(dev) for t in (k, v, q, qi, kimp))
+    num, den, ns, nw = 1, 2, 4, 16
+    cap = min(L, L * num // den + ns + nw)
+    for mode in (qa.BUTLER_SCORE_RAW, qa.BUTLER_SCORE_SOFTVOTE):
+        scores = torch.empty(B, Hq, 1, L, dtype=torch.float32, device=dev)
+        if mode == qa.BUTLER_SCORE_RAW:
+            qa.butler_score(mode, qid, kid, scores, Hkv=Hkv, L=L, sel_group=1)
+        else:
+            qa.butler_score(mode, qd, kd, scores, Hkv=Hkv, L=L, softmax_scale=scale, sel_group=1)
+        idx = torch.full((B, Hq, 1, cap), -1, dtype=torch.int32, device=dev)
+        cnt = torch.zeros(B, Hq, 1, dtype=torch.int32, device=dev)
+        qa.butler_select_topk(scores, num, den, ns, nw, cnt, idx=idx)
+        out = torch.empty(B, Hq, 1, D, dtype=torch.float32, device=dev)
+        qa.butler_sparse_decode_attn(qd, kd, vd, out, L=L, idx=idx, count=cnt,
+                                     softmax_scale=scale, sel_group=1)
+        idx2 = torch.full_like(idx, -1)
+        cnt2 = torch.zeros_like(cnt)
+        out2 = torch.empty_like(out)
+        qa.butler_select_attend(scores, num, den, ns, nw, cnt2, idx2, qd, kd, vd, out2, L=L,
+                                softmax_scale=scale, sel_group=1)
+        torch.cuda.synchronize()
+        got = np64(scores)
+        if mode == qa.BUTLER_SCORE_RAW:
+            want = oracle.score_raw(np64(qi)[:, :, 0], np64(kimp), Hkv, sel_group=1)
+            if dtype == torch.bfloat16:
+                assert np.array_equal(got, want)
+            else:
+                mag = np.einsum("bhqi,bhti->bhqt", np.abs(np64(qi)[:, :, 0]),
+                                np.abs(np.repeat(np64(kimp), 2, axis=1)))
+                assert (np.abs(got - want) <= 1e-5 * mag).all()
+        else:
+            want = oracle.score_softvote(np64(q), np64(k), Hkv, scale, sel_group=1)
+            assert (np.abs(got - want) <= 1e-5 * np.abs(want) + 1e-30).all()
+        check_select_exact(idx, cnt, got, num, den, ns, nw)
+        assert torch.equal(idx2, idx) and torch.equal(cnt2, cnt)
+        assert float((out2 - out).abs().max()) <= 1e-5
+        ic, cc = idx.cpu().numpy(), cnt.cpu().numpy()
+        err = _check_attend_heads(out, q, k, v, lambda b, j, i: ic[b, j, i, :cc[b, j, i]],
+                                  scale, 1, Hq // Hkv, ATOL[dtype])
+        print(f"  mode {mode}: attention max-abs {err:.2e}", flush=True)
