@@ -18,13 +18,14 @@
 // Decode rows longer than 4096 tokens: kernels over chunks of 256 threads x 8 or 16 keys
 //   0  (only without the scorer's histogram) histogram of key bits 31..21
 //   1  every chunk derives the first-digit bin b1, counts its tokens that are surely
-//      selected (digit above b1, or a sink / window token) and appends the keys whose
-//      digit is b1 to the row's candidate ring -- for scores of any spread only a sliver
-//      of the row
+//      selected (digit above b1, or a sink / window token) and packs the keys whose
+//      digit is b1 into its own candidate region -- for scores of any spread only a
+//      sliver of the row
 //   2  every wave of every chunk resolves tau and the tie cut from the row's candidates
 //      on its own with ballot counts, bit by bit (the same work everywhere: cheaper than
-//      a kernel boundary while the candidates are few; past 2048 candidates the whole
-//      workgroup runs radix passes), derives its output offset from the per-chunk counts
+//      a kernel boundary while the candidates are few; beyond 256 candidates through the
+//      second digit, and past 2048 candidates of one second digit the whole workgroup
+//      runs radix passes), derives its output offset from the per-chunk counts
 //      and emits its bitmask words and indices through 64-token ballot words; the chunk-0
 //      workgroup writes the row count and clears the histogram.
 //
@@ -308,21 +309,35 @@ struct RowState {
   uint32_t b1;     // first-digit bin of the x-th largest key
   int need;        // rank of the x-th largest key inside that bin (1-based)
   uint32_t epoch;  // this call's number: which second-digit histogram is live
-  uint32_t pad;
+  int nb1;         // keys of the row in bin b1: the candidates
 };
+
+// Rows with more candidates than this sort each chunk's candidates by their coarse second
+// digit (key bits 20..15), so that the finishing pass reads only the coarse bin of tau.
+constexpr int kMbFew = 256;
 
 struct MbWs {
   uint32_t* hist1;               // [rows][2048]   first-digit counts, zero between calls
-  unsigned long long* ccount;    // [rows]         running candidate counter (never reset)
   RowState* state;               // [rows]
   int* defcnt;                   // [rows][nchunk] tokens of the chunk that are surely selected
   int* ncand;                    // [rows][nchunk] candidates the chunk appended
   uint32_t* epoch;               // [rows]         calls made so far (never reset)
-  uint32_t* hist2;               // [2][rows][2048] second-digit (key bits 20..10) counts of
-                                 //                the candidates; buffer epoch % 2 is filled,
-                                 //                the other one is zero
-  uint2* cand;                   // [rows][L]      ring of (key, index | sink/window flag << 31)
+  uint32_t* hist2;               // [2][rows][64]  coarse second-digit (key bits 20..15)
+                                 //                counts of the candidates of rows with many;
+                                 //                buffer epoch % 2 is filled, the other is zero
+  uint32_t* ctab;                // [rows][nchunk][64]  rows with many candidates: per chunk
+                                 //                and coarse bin c, the candidates in bins above
+                                 //                c (bits 0..15: where bin c starts in the
+                                 //                sorted region) and how many of them are not
+                                 //                sink / window tokens (bits 16..31)
+  uint2* cand;                   // [rows][nchunk][chunk tokens]  each chunk's candidates,
+                                 //                (key, index | sink/window flag << 31), packed
+                                 //                from the start of the chunk's own region
+                                 //                (by descending coarse bin in rows with many)
 };
+
+// Chunks of a row the finishing pass can index (L <= 8M tokens at 4096 tokens per chunk).
+constexpr int kMbMaxChunks = 2048;
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -335,9 +350,10 @@ long long nchunk_for(int L) { return nchunk_k(L, kpt_for(L)); }
 
 size_t mb_bytes_k(long long rows, int L, int kpt) {
   const long long nchunk = nchunk_k(L, kpt);
-  return al256(rows * 2048 * 4) + al256(rows * 8) + al256(rows * sizeof(RowState)) +
-         2 * al256(rows * nchunk * 4) + al256(rows * 4) + al256(2 * rows * 2048 * 4) +
-         al256((size_t)rows * L * sizeof(uint2));
+  return al256(rows * 2048 * 4) + al256(rows * sizeof(RowState)) +
+         2 * al256(rows * nchunk * 4) + al256(rows * 4) + al256(2 * rows * 64 * 4) +
+         al256((size_t)rows * nchunk * 64 * 4) +
+         al256((size_t)rows * nchunk * kMbThreads * kpt * sizeof(uint2));
 }
 
 size_t mb_bytes(long long rows, int L) { return mb_bytes_k(rows, L, kpt_for(L)); }
@@ -347,12 +363,12 @@ MbWs carve_k(void* ws, long long rows, int L, int kpt) {
   char* p = (char*)ws;
   MbWs w;
   w.hist1 = (uint32_t*)p;                 p += al256(rows * 2048 * sizeof(uint32_t));
-  w.ccount = (unsigned long long*)p;      p += al256(rows * 8);
   w.state = (RowState*)p;                 p += al256(rows * sizeof(RowState));
   w.defcnt = (int*)p;                     p += al256(rows * nchunk * sizeof(int));
   w.ncand = (int*)p;                      p += al256(rows * nchunk * sizeof(int));
   w.epoch = (uint32_t*)p;                 p += al256(rows * 4);
-  w.hist2 = (uint32_t*)p;                 p += al256(2 * rows * 2048 * 4);
+  w.hist2 = (uint32_t*)p;                 p += al256(2 * rows * 64 * 4);
+  w.ctab = (uint32_t*)p;                  p += al256((size_t)rows * nchunk * 64 * 4);
   w.cand = (uint2*)p;
   return w;
 }
@@ -428,7 +444,7 @@ __device__ __forceinline__ int ballot_count(bool p) { return __popcll(__ballot(p
 // key, and the rank left inside it.  Lane l sums bins [2048 - 32(l+1), 2048 - 32l), the
 // lanes scan from the top, and the lane whose range holds the rank walks its 32 bins.
 __device__ __forceinline__ void wave_find_top(const uint32_t* __restrict__ gh, int need,
-                                              uint32_t& bin, int& rest) {
+                                              uint32_t& bin, int& rest, int& count) {
   const int lane = threadIdx.x & 63;
   const int lo = 2048 - 32 * (lane + 1);
   uint32_t c[32];
@@ -448,43 +464,57 @@ __device__ __forceinline__ void wave_find_top(const uint32_t* __restrict__ gh, i
   const int excl = incl - local;
   const unsigned long long m = __ballot(excl < need && need <= incl);
   const int src = m ? (int)__ffsll((unsigned long long)m) - 1 : 0;
-  int above = excl, b = lo, r = 1;
+  int above = excl, b = lo, r = 1, cnt = 0;
   bool found = false;
 #pragma unroll
   for (int i = 31; i >= 0; --i) {
     if (!found && above + (int)c[i] >= need) {
       b = lo + i;
       r = need - above;
+      cnt = (int)c[i];
       found = true;
     }
     if (!found) above += (int)c[i];
   }
   bin = (uint32_t)__shfl(b, src);
   rest = __shfl(r, src);
+  count = __shfl(cnt, src);
+}
+
+// The same over a 64-bin histogram: the bin c holding the need-th largest key, how many
+// keys lie in the bins above it, and how many in it.
+__device__ __forceinline__ void wave_find_top64(const uint32_t* __restrict__ gh, int need,
+                                                uint32_t& bin, int& above, int& count) {
+  const int lane = threadIdx.x & 63;
+  const int v = (int)gh[63 - lane];
+  const int incl = wave_inclusive_sum(v);
+  const unsigned long long m = __ballot(incl - v < need && need <= incl);
+  const int src = m ? (int)__ffsll((unsigned long long)m) - 1 : 0;
+  bin = (uint32_t)(63 - src);
+  above = __shfl(incl - v, src);
+  count = __shfl(v, src);
 }
 
 // One wave resolves, from n <= 64*Q candidates (all share the key bits above top_bit,
 // given in prefix, and the need-th largest of them is the x-th largest key of the row;
-// crow[(base + j) mod L] is candidate j, in global memory or LDS), tau bit by bit from
+// load(j) gives candidate j, called by all 64 lanes at once), tau bit by bit from
 // top_bit down -- a ballot count of the candidates that carry the trial bit -- then, when
 // the budget splits the keys equal to tau, the tie cut bit by bit over their indices
 // (lowest indices first), and the counts of the selected candidates that are not sink /
 // window tokens: all of them, and those before index c_lo.
-template <int Q>
-__device__ void wave_resolve(const uint2* crow, int base, int n, int L, uint32_t prefix,
-                             int top_bit, int need, int c_lo, uint32_t& tau, int& tie_cut,
-                             int& sel_all, int& sel_before) {
+template <int Q, typename Load>
+__device__ void wave_resolve(const Load& load, int n, uint32_t prefix, int top_bit, int need,
+                             int c_lo, uint32_t& tau, int& tie_cut, int& sel_all,
+                             int& sel_before) {
   const int lane = threadIdx.x & 63;
   uint32_t ck[Q], ci[Q];
   bool cv[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     cv[q] = lane + 64 * q < n;
-    int p = base + min(lane + 64 * q, n - 1);
-    if (p >= L) p -= L;
-    const uint2 c = crow[p];
-    ck[q] = c.x;
-    ci[q] = c.y;
+    const uint2 e = load(min(lane + 64 * q, n - 1));
+    ck[q] = e.x;
+    ci[q] = e.y;
   }
   uint32_t P = prefix;
   int kk = need;
@@ -531,17 +561,32 @@ __device__ void wave_resolve(const uint2* crow, int base, int n, int L, uint32_t
   }
 }
 
+// Candidate j (0 <= j < n) of a row whose chunks packed their candidates into regions of
+// ch entries, taken from each region in turn: cp (LDS) holds the exclusive prefix of the
+// counts taken, so j lies in the last chunk whose prefix is <= j (chunks that give none
+// repeat the prefix).
+struct CandRow {
+  const uint2* base;   // the row's first region
+  const int* cp;       // [nchunk] exclusive prefix of the counts taken from each region
+  const int* off;      // [nchunk] where they start in the region (null: at its start)
+  int nchunk, ch;
+  __device__ __forceinline__ uint2 operator()(int j) const {
+    int lo = 0, hi = nchunk - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cp[mid] <= j) lo = mid;
+      else hi = mid - 1;
+    }
+    return base[(long long)lo * ch + min((off ? off[lo] : 0) + (j - cp[lo]), ch - 1)];
+  }
+};
+
 // The same for rows with many candidates, by the whole workgroup: radix passes over bits
-// 20..10 and 9..0 of the candidates (LDS histograms, read from the ring in memory), the
-// tie quota, the index radix of the ties, then the two counts.
-__device__ void block_resolve(const uint2* __restrict__ crow, int base, int n, int L,
-                              uint32_t b1, int need, int c_lo, uint32_t* h, int* tmp, int3* tmp3,
-                              int* sh, uint32_t& tau, int& tie_cut, int& sel_all,
-                              int& sel_before) {
-  auto at = [&](int j) {
-    const int p = base + j;
-    return crow[p >= L ? p - L : p];
-  };
+// 20..10 and 9..0 of the candidates (LDS histograms, read from the chunk regions), the tie
+// quota, the index radix of the ties, then the two counts.
+__device__ void block_resolve(const CandRow at, int n, uint32_t b1, int need, int c_lo,
+                              uint32_t* h, int* tmp, int3* tmp3, int* sh, uint32_t& tau,
+                              int& tie_cut, int& sel_all, int& sel_before) {
   uint32_t prefix = b1 << 21, pmask = 0xffe00000u;
   const int shifts[2] = {10, 0};
   const int bins[2] = {2048, 1024};
@@ -605,8 +650,11 @@ __device__ void block_resolve(const uint2* __restrict__ crow, int base, int n, i
 // Chunk pass.  Thread i of the workgroup holds tokens c_lo + i + 256 j (j < KPT), so a
 // wave's ballot covers 64 consecutive tokens.  Every wave derives the first-digit bin b1
 // from the row's histogram on its own, counts its tokens that are surely selected (digit
-// above b1, or sink / window) and appends the keys whose first digit is b1 to the row's
-// candidate ring, at positions the workgroup takes with one atomic.
+// above b1, or sink / window) and packs the keys whose first digit is b1 into the chunk's
+// own candidate region: no position is taken from a shared counter (64 workgroups of a
+// row serialised on one such atomic).  In rows with few candidates they go in wave order;
+// in rows with many, sorted by descending coarse second digit, with the chunk's table of
+// where each coarse bin starts and its counts added to the row's coarse histogram.
 template <int KPT>
 __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __restrict__ scores,
                                                              int num, int den, int n_sink,
@@ -627,13 +675,18 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
 #pragma unroll
   for (int j = 0; j < KPT; ++j) f[j] = srow[min(c_lo + (int)threadIdx.x + kMbThreads * j, L - 1)];
   uint32_t b1 = 0u;
-  int need = 0;
+  int need = 0, nb1 = 0;
   const uint32_t epoch = w.epoch[row];
   if (mode == kModeNormal) {
-    wave_find_top(ghist + (long long)row * 2048, k, b1, need);
-    if (chunk == 0 && threadIdx.x == 0) w.state[row] = RowState{b1, need, epoch, 0u};
+    wave_find_top(ghist + (long long)row * 2048, k, b1, need, nb1);
+    if (chunk == 0 && threadIdx.x == 0) w.state[row] = RowState{b1, need, epoch, nb1};
   }
-  uint32_t* h2 = w.hist2 + ((long long)(epoch & 1u) * rows + row) * 2048;
+  const bool sorted = nb1 > kMbFew;   // the same for every workgroup of the row
+  __shared__ int s_hc[64], s_hn[64], s_base[64];
+  if (sorted && threadIdx.x < 64) {
+    s_hc[threadIdx.x] = 0;
+    s_hn[threadIdx.x] = 0;
+  }
   const int w_lo = max(0, L - n_window);
   int ndef = 0, ncw = 0;
   unsigned long long cm[KPT];
@@ -656,12 +709,10 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
     ndef += def ? 1 : 0;
     cm[j] = __ballot(cand);
     ncw += __popcll(cm[j]);
-    if (cand) atomicAdd(&h2[(key[j] >> 10) & 2047u], 1u);
   }
   ndef = wave_sum_i(ndef);
   // one atomic per workgroup (same-address atomics serialise): the waves' counts meet in LDS
   __shared__ int s_n[kMbWaves], s_d[kMbWaves];
-  __shared__ int s_start;
   if (lane == 0) {
     s_n[wid] = ncw;
     s_d[wid] = ndef;
@@ -677,37 +728,65 @@ __global__ __launch_bounds__(kMbThreads) void mb_cand_kernel(const float* __rest
     const long long e = (long long)row * nchunk + chunk;
     w.defcnt[e] = td;
     w.ncand[e] = tn;
-    s_start = tn ? (int)(atomicAdd(&w.ccount[row], (unsigned long long)tn) % (unsigned long long)L)
-                 : 0;
+  }
+  uint2* crow = w.cand + ((long long)row * nchunk + chunk) * (kMbThreads * KPT);
+  if (!sorted) {
+    if (ncw) {
+      int pos = 0;
+#pragma unroll
+      for (int v = 0; v < kMbWaves; ++v) pos += (v < wid) ? s_n[v] : 0;
+      const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        if ((cm[j] >> lane) & 1ull) {
+          const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
+          const uint32_t flag = (t < n_sink || t >= w_lo) ? 0x80000000u : 0u;
+          crow[pos + __popcll(cm[j] & lt)] = make_uint2(key[j], (uint32_t)t | flag);
+        }
+        pos += __popcll(cm[j]);
+      }
+    }
+    return;
+  }
+  // many candidates in the row: a counting sort by coarse bin (the order inside a bin is
+  // immaterial, the finishing pass uses only the keys and indices)
+  int slot[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    slot[j] = 0;
+    if ((cm[j] >> lane) & 1ull) {
+      const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
+      const int cb = (int)((key[j] >> 15) & 63u);
+      slot[j] = atomicAdd(&s_hc[cb], 1);
+      if (!(t < n_sink || t >= w_lo)) atomicAdd(&s_hn[cb], 1);
+    }
   }
   __syncthreads();
-  int start = s_start;
+  if (wid == 0) {
+    // lane l takes bin 63 - l: the exclusive scan counts the candidates in the bins above
+    const int cb = 63 - lane;
+    const int hc = s_hc[cb], hn = s_hn[cb];
+    const int ac = wave_inclusive_sum(hc) - hc, an = wave_inclusive_sum(hn) - hn;
+    w.ctab[((long long)row * nchunk + chunk) * 64 + cb] = (uint32_t)ac | ((uint32_t)an << 16);
+    s_base[cb] = ac;
+    if (hc) atomicAdd(&w.hist2[((long long)(epoch & 1u) * rows + row) * 64 + cb], (uint32_t)hc);
+  }
+  __syncthreads();
 #pragma unroll
-  for (int v = 0; v < kMbWaves; ++v) start += (v < wid) ? s_n[v] : 0;
-  if (start >= L) start -= L;
-  if (ncw) {
-    uint2* crow = w.cand + (long long)row * L;
-    const unsigned long long lt = (1ull << lane) - 1ull;
-    int pos = start;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if ((cm[j] >> lane) & 1ull) {
-        int p = pos + __popcll(cm[j] & lt);
-        if (p >= L) p -= L;
-        const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
-        const uint32_t flag = (t < n_sink || t >= w_lo) ? 0x80000000u : 0u;
-        crow[p] = make_uint2(key[j], (uint32_t)t | flag);
-      }
-      pos += __popcll(cm[j]);
-      if (pos >= L) pos -= L;
+  for (int j = 0; j < KPT; ++j) {
+    if ((cm[j] >> lane) & 1ull) {
+      const int t = c_lo + (int)threadIdx.x + kMbThreads * j;
+      const uint32_t flag = (t < n_sink || t >= w_lo) ? 0x80000000u : 0u;
+      crow[s_base[(key[j] >> 15) & 63u] + slot[j]] = make_uint2(key[j], (uint32_t)t | flag);
     }
   }
 }
 
 // Finishing pass, one workgroup per chunk, tokens held as in the chunk pass.  Every wave
-// sums the row's per-chunk counts and resolves tau and the tie cut from the candidate ring
-// on its own (the whole workgroup only when the candidates exceed 2048), so nothing waits
-// on another wave until the output positions: the 64-token ballot words of the chunk are
+// sums the row's per-chunk counts; the workgroup indexes the chunks' candidate regions
+// (a prefix of their counts in LDS) and, while they are few, gathers the candidates into
+// LDS, where every wave resolves tau and the tie cut on its own (the whole workgroup only
+// for a flood of equal keys): the 64-token ballot words of the chunk are
 // prefix-summed once through LDS, and each wave writes its words' indices coalesced and
 // their bitmask words.  The chunk-0 workgroup writes the row count and clears the row's
 // histogram (nothing in this kernel reads it).
@@ -768,13 +847,9 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
   float f[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) f[j] = srow[min(c_lo + (int)threadIdx.x + kMbThreads * j, L - 1)];
-  // the row's state and candidate counter are requested with the per-wave counts
+  // the row's state is requested with the per-wave counts
   RowState st = {0u, 0};
-  unsigned long long end = 0ull;
-  if (mode == kModeNormal) {
-    st = w.state[row];
-    end = w.ccount[row];
-  }
+  if (mode == kModeNormal) st = w.state[row];
   const long long e0 = (long long)row * nchunk;
   int n = 0, def_all = 0, def_before = 0;
   for (int e = lane; e < nchunk; e += 64) {
@@ -783,81 +858,106 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
     def_before += (e < chunk) ? d : 0;
     n += w.ncand[e0 + e];
   }
-  n = wave_sum_i(n);
+  // with at most 64 chunks lane e holds chunk e's candidate count, and nc_incl its
+  // inclusive prefix over the chunks
+  const int nc_lane = n;
+  const int nc_incl = wave_inclusive_sum(nc_lane);
+  n = __shfl(nc_incl, 63);
   def_all = wave_sum_i(def_all);
   def_before = wave_sum_i(def_before);
   const uint32_t epoch = w.epoch[row];   // not advanced before this kernel ends
   if (chunk == 0) {
-    // clear the first-digit histogram and the second-digit one the next call fills
+    // clear the first-digit histogram and the coarse second-digit one the next call fills
     uint32_t* gh = ghist + (long long)row * 2048;
-    uint32_t* h2n = w.hist2 + ((long long)((epoch + 1u) & 1u) * rows + row) * 2048;
-    for (int j = threadIdx.x; j < 2048; j += kMbThreads) {
-      gh[j] = 0u;
-      h2n[j] = 0u;
-    }
+    for (int j = threadIdx.x; j < 2048; j += kMbThreads) gh[j] = 0u;
+    if (threadIdx.x < 64) w.hist2[((long long)((epoch + 1u) & 1u) * rows + row) * 64 + threadIdx.x] = 0u;
   }
   uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;
   int tie_cut = -1;
   int sel_all = 0, sel_before = 0;   // selected candidates that are not sink / window
-  if (mode == kModeNormal && n > 0) {
-    const int base = (int)((end - (unsigned long long)n) % (unsigned long long)L);
-    const uint2* crow = w.cand + (long long)row * L;
-#define BUTLER_RESOLVE(QQ, SRC, BASE, NN, LL, PRE, BIT, NEED, SA, SB) \
-  wave_resolve<QQ>(SRC, BASE, NN, LL, PRE, BIT, NEED, c_lo, tau, tie_cut, SA, SB)
-    if (n <= 256) {
+  if (mode == kModeNormal && n > 0) {   // uniform over the workgroup: n is the row's total
+    constexpr int CH = kMbThreads * KPT;
+    const uint2* rb = w.cand + (long long)row * nchunk * CH;
+    __shared__ int s_cp[kMbMaxChunks];
+    const auto lds = [&](int j) { return s_c[j]; };
+#define BUTLER_RESOLVE(QQ, LOAD, NN, PRE, BIT, NEED, SA, SB) \
+  wave_resolve<QQ>(LOAD, NN, PRE, BIT, NEED, c_lo, tau, tie_cut, SA, SB)
+    bool done = false;
+    if (n <= kMbFew && nchunk <= 64) {
+      // few candidates in few chunks: every wave reads them from the regions itself; the
+      // chunk of candidate j is the number of chunks whose inclusive count is <= j
+      const auto direct = [&](int j) {
+        int e = 0;
+#pragma unroll
+        for (int sft = 32; sft > 0; sft >>= 1) e += (__shfl(nc_incl, e + sft - 1) <= j) ? sft : 0;
+        return rb[(long long)e * CH + min(j - __shfl(nc_incl - nc_lane, e), CH - 1)];
+      };
       const uint32_t pre = st.b1 << 21;
-      if (n <= 64) BUTLER_RESOLVE(1, crow, base, n, L, pre, 20, st.need, sel_all, sel_before);
-      else if (n <= 128) BUTLER_RESOLVE(2, crow, base, n, L, pre, 20, st.need, sel_all, sel_before);
-      else BUTLER_RESOLVE(4, crow, base, n, L, pre, 20, st.need, sel_all, sel_before);
-    } else {
-      // many candidates: the second digit from the chunk pass's histogram, then one scan
-      // that counts the selected candidates above it and gathers the ones inside it
-      uint32_t b2;
-      int need2;
-      wave_find_top(w.hist2 + ((long long)(st.epoch & 1u) * rows + row) * 2048, st.need, b2,
-                    need2);
-      const uint32_t p22 = (st.b1 << 11) | b2;
-      if (threadIdx.x == 0) sh[0] = 0;
-      __syncthreads();
-      int a_all = 0, a_before = 0;
-      for (int j0 = 0; j0 < n; j0 += kMbThreads * 8) {
-        uint2 cc[8];   // eight candidates per thread requested at once
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int pj = base + min(j0 + (int)threadIdx.x + kMbThreads * u, n - 1);
-          cc[u] = crow[pj >= L ? pj - L : pj];
+      if (n <= 64) BUTLER_RESOLVE(1, direct, n, pre, 20, st.need, sel_all, sel_before);
+      else if (n <= 128) BUTLER_RESOLVE(2, direct, n, pre, 20, st.need, sel_all, sel_before);
+      else BUTLER_RESOLVE(4, direct, n, pre, 20, st.need, sel_all, sel_before);
+      done = true;
+    } else if (n > kMbFew && st.nb1 > kMbFew) {
+      // many candidates, sorted by coarse bin in every chunk: the coarse bin cb of tau from
+      // the row's coarse histogram; the candidates above cb are counted from the chunk
+      // tables, and only the ones inside cb are gathered and resolved
+      uint32_t cb;
+      int above, m;
+      wave_find_top64(w.hist2 + ((long long)(st.epoch & 1u) * rows + row) * 64, st.need, cb,
+                      above, m);
+      if (m <= kFinStage) {
+        int* s_st = reinterpret_cast<int*>(h);   // where cb starts in each chunk's region
+        int nf_all = 0, nf_before = 0;
+        for (int e = threadIdx.x; e < nchunk; e += kMbThreads) {
+          const uint32_t* te = w.ctab + (e0 + e) * 64;
+          const uint32_t v = te[cb];
+          const int end = cb ? (int)(te[cb - 1] & 0xffffu) : w.ncand[e0 + e];
+          s_st[e] = (int)(v & 0xffffu);
+          s_cp[e] = end - (int)(v & 0xffffu);
+          nf_all += (int)(v >> 16);
+          nf_before += (e < chunk) ? (int)(v >> 16) : 0;
         }
+        const int3 nf = block_sum3(nf_all, nf_before, 0, tmp3);
+        block_scan_array<kMbThreads>(s_cp, nchunk, tmp);
+        const CandRow part{rb, s_cp, s_st, nchunk, CH};
+        for (int j0 = 0; j0 < m; j0 += 2 * kMbThreads) {
+          uint2 g[2];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (j0 + (int)threadIdx.x + kMbThreads * u >= n) continue;
-          const uint2 c = cc[u];
-          const uint32_t k22 = c.x >> 10;
-          if (k22 > p22) {
-            if (!(c.y & 0x80000000u)) {
-              ++a_all;
-              a_before += ((int)c.y < c_lo) ? 1 : 0;
-            }
-          } else if (k22 == p22) {
-            const int slot = atomicAdd(&sh[0], 1);
-            if (slot < kFinStage) s_c[slot] = c;
-          }
+          for (int u = 0; u < 2; ++u) g[u] = part(min(j0 + (int)threadIdx.x + kMbThreads * u, m - 1));
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            if (j0 + (int)threadIdx.x + kMbThreads * u < m) s_c[j0 + threadIdx.x + kMbThreads * u] = g[u];
         }
-      }
-      const int3 ab = block_sum3(a_all, a_before, 0, tmp3);
-      const int m2 = sh[0];
-      if (m2 <= kFinStage) {
+        __syncthreads();
         int s2a = 0, s2b = 0;
-        const uint32_t pre = p22 << 10;
-        if (m2 <= 64) BUTLER_RESOLVE(1, s_c, 0, m2, kFinStage, pre, 9, need2, s2a, s2b);
-        else if (m2 <= 256) BUTLER_RESOLVE(4, s_c, 0, m2, kFinStage, pre, 9, need2, s2a, s2b);
-        else if (m2 <= 1024) BUTLER_RESOLVE(16, s_c, 0, m2, kFinStage, pre, 9, need2, s2a, s2b);
-        else BUTLER_RESOLVE(32, s_c, 0, m2, kFinStage, pre, 9, need2, s2a, s2b);
-        sel_all = ab.x + s2a;
-        sel_before = ab.y + s2b;
+        const uint32_t pre = (st.b1 << 21) | (cb << 15);
+        const int need2 = st.need - above;
+        if (m <= 64) BUTLER_RESOLVE(1, lds, m, pre, 14, need2, s2a, s2b);
+        else if (m <= 256) BUTLER_RESOLVE(4, lds, m, pre, 14, need2, s2a, s2b);
+        else if (m <= 1024) BUTLER_RESOLVE(16, lds, m, pre, 14, need2, s2a, s2b);
+        else BUTLER_RESOLVE(32, lds, m, pre, 14, need2, s2a, s2b);
+        sel_all = nf.x + s2a;
+        sel_before = nf.y + s2b;
+        done = true;
+      }
+    }
+    if (!done) {
+      // the rest (few candidates over many chunks, or a flood of keys in one coarse bin):
+      // the chunks' counts prefix-summed in LDS index every candidate of the row
+      for (int e = threadIdx.x; e < nchunk; e += kMbThreads) s_cp[e] = w.ncand[e0 + e];
+      __syncthreads();
+      block_scan_array<kMbThreads>(s_cp, nchunk, tmp);
+      const CandRow crow{rb, s_cp, nullptr, nchunk, CH};
+      if (n <= kMbFew) {
+        if ((int)threadIdx.x < n) s_c[threadIdx.x] = crow((int)threadIdx.x);
+        __syncthreads();
+        const uint32_t pre = st.b1 << 21;
+        if (n <= 64) BUTLER_RESOLVE(1, lds, n, pre, 20, st.need, sel_all, sel_before);
+        else if (n <= 128) BUTLER_RESOLVE(2, lds, n, pre, 20, st.need, sel_all, sel_before);
+        else BUTLER_RESOLVE(4, lds, n, pre, 20, st.need, sel_all, sel_before);
       } else {
-        // a flood of equal keys: the whole workgroup runs radix passes over the ring
-        block_resolve(crow, base, n, L, st.b1, st.need, c_lo, h, tmp, tmp3, sh, tau, tie_cut,
-                      sel_all, sel_before);
+        block_resolve(crow, n, st.b1, st.need, c_lo, h, tmp, tmp3, sh, tau, tie_cut, sel_all,
+                      sel_before);
       }
     }
 #undef BUTLER_RESOLVE
@@ -1000,6 +1100,7 @@ hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int
   const long long rows = (long long)B * Hkv;
   const int kpt = kpt_attend(L);
   const int nchunk = (int)nchunk_k(L, kpt);
+  if (nchunk > kMaMaxChunks) return hipErrorInvalidValue;
   const MbWs w = carve_k(ws, rows, L, kpt);
   float* part = (float*)((char*)ws + mb_bytes_k(rows, L, kpt));
   const MbAttn at{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, part, Hq, Hkv, L_cap,
@@ -1051,6 +1152,7 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
   if (use_chunked(Lq, L, causal)) {
     const MbWs w = carve(ws, rows, L);
     const int nchunk = (int)nchunk_for(L);
+    if (nchunk > kMbMaxChunks) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(rows * nchunk));
     uint32_t* gh = hist ? hist : w.hist1;
     auto run = [&](auto kpt_c) {

@@ -212,7 +212,8 @@ def test_project_and_score_matches_separate_calls(cfg, L):
     (3001, 32, 1, 2, True),      # short row: the two calls' kernels
     (5001, 32, 1, 2, True),      # fused, ragged last chunk
     (32768, 32, 1, 2, True),     # fused, the layer workload's length
-    (70001, 32, 1, 16, False),   # fused with 8 keys per thread, no scorer histogram
+    (70001, 32, 1, 16, False),   # fused with 16 keys per thread, no scorer histogram
+    (262144, 32, 1, 16, True),   # the long-context consumer layer: many candidates per row
     (9000, 8, 3, 10, True),      # R = 1
     (9000, 64, 1, 2, True),      # R = 8
     (9000, 32, 1, 1, True),      # budget takes every token

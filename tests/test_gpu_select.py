@@ -73,7 +73,10 @@ def test_select_rows_match_oracle(kind):
              (33, 1, 16, 4, 128), (100, 0, 1, 3, 5), (257, 1, 1, 4, 16), (1000, 5, 4, 0, 0),
              (4096, 1, 1, 4, 64), (4097, 1, 2, 4, 64), (8192, 0, 1, 4, 64),
              (12000, 5, 4, 4, 64), (20011, 1, 16, 4, 128), (40000, 3, 10, 4, 64),
-             (100003, 1, 2, 0, 0)]
+             (100003, 1, 2, 0, 0),
+             # more than 64 chunks of 4096 keys: few candidates indexed through LDS, and
+             # many candidates sorted by coarse bin
+             (600000, 1, 2, 4, 64), (300007, 1, 16, 4, 128)]
     for (L, num, den, ns, nw) in cases:
         print(f"[select] kind={kind} L={L} budget={num}/{den} sink={ns} window={nw}", flush=True)
         _run(_scores(rng, (1, 3, 1, L), kind), num, den, ns, nw)
