@@ -110,3 +110,44 @@ def test_select_causal_rows_excluding_forced():
         print(f"[select-causal-excl] Lq={Lq} q_pos0={q_pos0} L={L}", flush=True)
         _run(_scores(rng, (1, 2, Lq, L), "ties"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0,
              fo=True)
+
+
+def test_select_workspace_shared_across_budgets():
+    """One workspace, passed through the C entry point to calls of one shape with budgets
+    that alternate between few candidates per row (50%: chunk regions in wave order) and
+    many (1/16: regions sorted by coarse bin, with the double-buffered coarse histogram):
+    the per-row state the chunk kernels keep in the workspace carries over from call to
+    call, and every call's sets equal the oracle's."""
+    import ctypes
+    import query_aware_sparse_imp_amd as qa
+    rng = np.random.default_rng(77)
+    L, ns, nw = 300007, 4, 128
+    s_np = rng.standard_normal((1, 3, 1, L)).astype(np.float32)
+    s_np[0, 2, 0, ::7] = 1.5     # a flood of equal keys at the 1/16 threshold, ties cut by index
+    s = torch.from_numpy(s_np).cuda()
+    idx = torch.empty((1, 3, 1, L), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((1, 3, 1), dtype=torch.int32, device="cuda")
+    budgets = [(1, 2), (1, 16), (1, 16), (1, 2), (1, 16), (3, 10), (1, 2), (1, 16)]
+
+    def args(num, den):
+        return (qa._ptr(s), None, None, num, den, ns, nw, 0, qa._ptr(idx), None, qa._ptr(cnt),
+                1, 3, 1, L, L, 0, 0)
+    need = max(qa.workspace_bytes(
+        lambda ws, n, a=args(num, den): qa.lib.butler_select_topk(qa._stream(None), *a, ws, n))
+        for (num, den) in budgets)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    nbytes = ctypes.c_size_t(need)
+    for call, (num, den) in enumerate(budgets):
+        print(f"[select-shared-ws] call {call} budget {num}/{den} L={L}", flush=True)
+        idx.fill_(-7)
+        cnt.zero_()
+        rc = qa.lib.butler_select_topk(qa._stream(None), *args(num, den), ws.data_ptr(),
+                                       ctypes.byref(nbytes))
+        assert rc == 0, rc
+        torch.cuda.synchronize()
+        cnt_np, idx_np = cnt.cpu().numpy(), idx.cpu().numpy()
+        for g in range(3):
+            want = oracle.select(s_np[0, g, 0].astype(np.float64), oracle.budget(L, num, den),
+                                 ns, nw)
+            assert cnt_np[0, g, 0] == len(want), (call, num, den, g)
+            assert np.array_equal(idx_np[0, g, 0, :cnt_np[0, g, 0]], want), (call, num, den, g)
