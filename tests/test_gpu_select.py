@@ -151,3 +151,13 @@ def test_select_workspace_shared_across_budgets():
                                  ns, nw)
             assert cnt_np[0, g, 0] == len(want), (call, num, den, g)
             assert np.array_equal(idx_np[0, g, 0, :cnt_np[0, g, 0]], want), (call, num, den, g)
+
+
+@pytest.mark.parametrize("num,den", [(1, 2), (1, 16)])
+def test_select_longest_row(num, den):
+    """The longest decode row the chunked schedule takes (8388608 keys: 2048 chunks of 4096,
+    the most the finishing pass indexes), with few (50%) and many (1/16) candidates."""
+    rng = np.random.default_rng(8 + den)
+    L = 8388608
+    print(f"[select-longest] L={L} budget={num}/{den}", flush=True)
+    _run(rng.standard_normal((1, 1, 1, L)).astype(np.float32), num, den, 4, 128)
