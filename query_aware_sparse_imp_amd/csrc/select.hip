@@ -1181,7 +1181,7 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
   if (L <= 1024) BUTLER_SR(64, 16);
   else if (L <= 2048) BUTLER_SR(128, 16);
   else if (L <= 4096) BUTLER_SR(256, 16);
-  else if (L <= 8192) BUTLER_SR(256, 32);
+  else if (L <= 8192) BUTLER_SR(512, 16);   // 512 x 16 measured faster than 256 x 32 and 1024 x 8
   else if (L <= 16384) BUTLER_SR(512, 32);
   else if (L <= 32768) BUTLER_SR(1024, 32);
   else BUTLER_SR(1024, 64);

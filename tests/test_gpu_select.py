@@ -84,7 +84,10 @@ def test_select_rows_match_oracle(kind):
 
 def test_select_causal_rows():
     rng = np.random.default_rng(5)
-    for (Lq, q_pos0, L) in ((37, 100, 137), (64, 0, 64), (129, 1000, 1129)):
+    # row lengths in every per-row workgroup shape: up to 1024, 8192, 16384, 32768, 65536
+    for (Lq, q_pos0, L) in ((37, 100, 137), (64, 0, 64), (129, 1000, 1129), (64, 6000, 6064),
+                            (33, 8159, 8192), (9, 16000, 16009), (5, 30000, 30005),
+                            (3, 65533, 65536)):
         print(f"[select-causal] Lq={Lq} q_pos0={q_pos0} L={L}", flush=True)
         _run(_scores(rng, (2, 2, Lq, L), "ties"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0)
         _run(_scores(rng, (1, 2, Lq, L), "normal"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0)
