@@ -576,10 +576,14 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
   constexpr int LPT = DP / Vec16<T>::N;
   // a tile is what one block-wide step covers (kRawUnroll loads per thread); a workgroup
   // loops over enough tiles that a row has at most kRawRowWg workgroups -- this bounds the
-  // atomics that the workgroups' histograms send to the same hot bins of a row
+  // atomics that the workgroups' histograms send to the same hot bins of a row -- or twice
+  // that for rows of more than 4 kRawRowWg tiles, so that no workgroup streams more than
+  // 4 tiles while the row has under 2 kRawRowWg of them (measured: 4 tiles per workgroup
+  // beat 2 at 128K and 8 at 256K tokens)
   const int tile = (kRawThreads / LPT) * kRawUnroll;
   const int tiles = (L + tile - 1) / tile;
-  const int per = (tiles + kRawRowWg - 1) / kRawRowWg;
+  const int row_wg = tiles > 4 * kRawRowWg ? 2 * kRawRowWg : kRawRowWg;
+  const int per = (tiles + row_wg - 1) / row_wg;
   const int tpb = tile * per;
   dim3 grid((L + tpb - 1) / tpb, Lq, B * Hkv);
   hipLaunchKernelGGL((score_raw_kernel<T, DP, DA>), grid, dim3(kRawThreads), 0, s,

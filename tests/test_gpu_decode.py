@@ -150,7 +150,7 @@ def test_scorer_histogram_matches_selection_without_it():
     histogram as from its own counting pass, on short, mid and long rows."""
     import query_aware_sparse_imp_amd as qa
     w = synthetic.WORKLOADS[2]
-    for L in (3000, 9000, 70001):
+    for L in (3000, 9000, 70001, 300001):   # 300001: 128 scorer workgroups per row
         print(f"[hist] L={L}", flush=True)
         inp = to_device(synthetic.decode_layer(w, 5, L=L))
         kimp = torch.zeros(w.B, w.Hkv, L, w.dprime, dtype=w.dtype, device="cuda")
@@ -164,7 +164,8 @@ def test_scorer_histogram_matches_selection_without_it():
                            w.n_sink, w.n_window)
 
 
-@pytest.mark.parametrize("cfg,L", [(1, 256), (1, 1), (2, 1), (2, 5001), (2, 32768)])
+@pytest.mark.parametrize("cfg,L", [(1, 256), (1, 1), (2, 1), (2, 5001), (2, 32768),
+                                   (2, 300001)])
 def test_project_and_score_matches_separate_calls(cfg, L):
     """butler_project_and_score == butler_project_keys(L-1, 1) + butler_score(RAW): the
     K_imp row, every score and the first-digit histogram bit for bit, whatever stale value
