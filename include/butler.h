@@ -218,8 +218,9 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
  * 0 <= budget_num, 1 <= budget_den, n_sink >= 0, n_window >= 0.  Rows of a causal or
  * multi-row (Lq > 1) call hold at most 65536 tokens; single-row decode calls up to 2^23.
  * workspace: none for causal / multi-row calls and rows up to 4096 tokens; otherwise a
- * radix histogram, candidate keys, per-chunk counts and offsets (about 8 bytes per token
- * per row).
+ * radix histogram, each chunk's candidate keys, per-chunk counts and coarse-bin tables
+ * (about 8 bytes per token per row).  The state it carries between calls is valid for
+ * any budget, so calls of one shape may share a workspace whatever their budgets.
  */
 int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
                        const int32_t* keep, int budget_num, int budget_den, int n_sink,
@@ -273,8 +274,8 @@ int butler_sparse_decode_attn(void* stream, int dtype, const void* q, const void
  *   butler_select_topk), idx [B, Hs, 1, cap] int32 and count [B, Hs, 1] int32 (written),
  *   q [B, Hq, 1, D], k_cache / v_cache [B, Hkv, L_cap, D] (dtype), out [B, Hq, 1, D] float32;
  *   sel_group as in butler_sparse_decode_attn.
- * Limits as in the two calls; L <= 2^23.  workspace: the selection's state and candidate
- * ring, and one softmax partial per chunk (or the two calls' workspaces).
+ * Limits as in the two calls; L <= 2^23.  workspace: the selection's state and each
+ * chunk's candidates, and one softmax partial per chunk (or the two calls' workspaces).
  */
 int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t* radix_hist,
                          int budget_num, int budget_den, int n_sink, int n_window,
