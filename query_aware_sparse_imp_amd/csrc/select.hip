@@ -16,6 +16,7 @@
 // butler_score), which saves one pass over the scores.  Two schedules:
 //
 // Decode rows longer than 4096 tokens: kernels over chunks of 256 threads x 8 or 16 keys
+// (4 to 32 in the pass fused with attention, by row length)
 //   0  (only without the scorer's histogram) histogram of key bits 31..21
 //   1  every chunk derives the first-digit bin b1, counts its tokens that are surely
 //      selected (digit above b1, or a sink / window token) and packs the keys whose
