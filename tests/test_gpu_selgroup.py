@@ -45,14 +45,19 @@ def _check_attend_heads(out, q, k_cache, v_cache, sets, scale, gs, R, atol):
     return worst
 
 
-@pytest.mark.parametrize("L,gs", [(4133, 1), (9000, 2), (32768, 1)])
-def test_decode_chain_per_selection_head(L, gs):
+@pytest.mark.parametrize("L,gs,den", [(4133, 1, 2), (9000, 2, 2), (32768, 1, 2),
+                                      (150001, 1, 16)])
+def test_decode_chain_per_selection_head(L, gs, den):
     """project -> score -> select -> attend with sel_group = gs, then the fused
-    project_and_score and select_attend calls on the same step."""
+    project_and_score and select_attend calls on the same step.  The 1/16 budget (window
+    128) at 150001 tokens gives every selection row thousands of candidates: the chunks
+    sort them by coarse bin, in the fused pass too."""
     import query_aware_sparse_imp_amd as qa
     w = synthetic.WORKLOADS[2]
+    if den != 2:
+        w = w.replace(budget_den=den, n_window=128)
     Hs = w.Hq // gs
-    print(f"[sel_group] decode L={L} sel_group={gs} Hs={Hs}", flush=True)
+    print(f"[sel_group] decode L={L} sel_group={gs} Hs={Hs} budget 1/{den}", flush=True)
     inp = to_device(synthetic.decode_layer(w, 1, L=L))
     dev = "cuda"
     k, v, q = inp["k_cache_d"], inp["v_cache_d"], inp["q_d"]
