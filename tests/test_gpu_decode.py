@@ -221,6 +221,7 @@ def test_project_and_score_matches_separate_calls(cfg, L):
     (9000, 32, 0, 1, True),      # budget 0: sink and window only
     (32768, 32, 1, 2, "fo"),     # the budget excludes the sink and the window
     (3001, 32, 1, 2, "fo"),
+    (150001, 32, 1, 16, "fo"),   # ... with many candidates per row (sorted regions)
 ])
 def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
     """butler_select_attend == butler_select_topk + butler_sparse_decode_attn: idx and count
