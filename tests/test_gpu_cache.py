@@ -29,10 +29,14 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("L", [3001, 9001])
-def test_selection_cache_softvote_walk(L):
+@pytest.mark.parametrize("L,den", [(3001, 0), (9001, 0), (30001, 16)])
+def test_selection_cache_softvote_walk(L, den):
+    """den 16: the 1/16 budget, whose rows hold many candidates (chunk regions sorted by
+    coarse bin), so kept rows skip that path's kernels and leave its workspace state."""
     import query_aware_sparse_imp_amd as qa
     w = synthetic.WORKLOADS[3].replace(B=2, L=L)
+    if den:
+        w = w.replace(budget_num=1, budget_den=den)
     threshold, steps = 0.9975, 6
     print(f"[cache] B={w.B} L={L} threshold={threshold} steps={steps}", flush=True)
     cache = synthetic.softvote_cache(w)
