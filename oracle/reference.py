@@ -259,26 +259,6 @@ def select(scores_row, x: int, n_sink: int, n_window: int,
     return np.unique(np.concatenate([top, sink, window]).astype(np.int64))
 
 
-def select_rows(scores, num: int, den: int, n_sink: int, n_window: int,
-                causal: bool = False, q_pos0: int = 0, exclude_forced: bool = False):
-    """Apply ``select`` to every row of scores [B, Hkv, Lq, L]; returns a
-    nested list [B][Hkv][Lq] of index arrays."""
-    B, Hkv, Lq, L = scores.shape
-    lens = _causal_lengths(Lq, L, q_pos0, causal)
-    out = []
-    for b in range(B):
-        rows_b = []
-        for g in range(Hkv):
-            rows_g = []
-            for i in range(Lq):
-                L_r = int(lens[i])
-                rows_g.append(select(scores[b, g, i, :L_r], budget(L_r, num, den),
-                                     n_sink, n_window, exclude_forced))
-            rows_b.append(rows_g)
-        out.append(rows_b)
-    return out
-
-
 # ---------------------------------------------------------------------------
 # attention over the selected set (model card, intro and Method)
 # ---------------------------------------------------------------------------
@@ -450,17 +430,31 @@ def expand_neighbors(sel, L: int, width: int, n_window: int) -> np.ndarray:
     return np.array(sorted(out), dtype=np.int64)
 
 
+def cached_selection(sel_prev, L: int, n_window: int) -> np.ndarray:
+    """A kept row of the selection cache at the current length L (TokenSelect README,
+    highlights, Selection Cache: consecutive similar queries share one token selection;
+    model card, Method: the set always holds a recent window).  The reading taken: the
+    selection made for an earlier query (any earlier length) is reused, and the window is
+    re-taken at the current length, so every token appended since is attended:
+        S = (sel_prev restricted to [0, L))  U  [max(0, L - n_window), L)
+    Returns the ascending int64 set."""
+    prev = np.asarray(sel_prev, np.int64)
+    prev = prev[(prev >= 0) & (prev < L)]
+    window = np.arange(max(0, L - n_window), L, dtype=np.int64)
+    return np.union1d(prev, window).astype(np.int64)
+
+
 def ulps_bf16(a, b) -> np.ndarray:
-    """Distance in bf16 units in the last place between two bf16-valued arrays."""
+    """Distance between two bf16-valued arrays, counted in bf16 values: the number of
+    steps from one to the other along the ordered bf16 grid (-0 and +0 are one point;
+    the largest finite value and infinity are one step apart).  Each bf16 pattern maps
+    to an integer that grows with the value: the magnitude bits for a positive value,
+    their negation for a negative one."""
     def ordered(x):
         x = np.asarray(x, np.float64).astype(np.float32)
         u = x.view(np.uint32).astype(np.int64) >> 16
         return np.where(u & 0x8000, -(u & 0x7FFF), u)
     return np.abs(ordered(a) - ordered(b))
-
-
-def mean_abs(x) -> float:
-    return float(np.mean(np.abs(np.asarray(x, np.float64))))
 
 
 __all__ = [n for n in dir() if not n.startswith("_") and n not in ("math", "np", "Optional",

@@ -751,3 +751,106 @@ def test_expand_neighbors_pins():
         dil = np.convolve(ind, np.ones(2 * w + 1), mode="full")[w:w + L] > 0.5
         dil[max(0, L - nw):] = True
         assert np.array_equal(E(sel, L, w, nw), np.flatnonzero(dil))
+
+
+def test_ulps_bf16_pins():
+    """Distance along the bf16 grid: hand-worked pairs (equal values, -0 against +0,
+    neighbours, a binade edge, a sign crossing through zero, the largest finite value
+    against infinity), then every pair from a sample against the distance in an
+    enumeration of all finite bf16 values sorted by value (a different route: positions
+    in a sorted list, not bit arithmetic)."""
+    U = lambda a, b: int(oracle.ulps_bf16(np.array([a]), np.array([b]))[0])
+    tiny = 2.0 ** -133                               # smallest positive bf16 (subnormal)
+    big = float.fromhex("0x1.fep127")                # largest finite bf16 (0x7F7F)
+    assert U(1.0, 1.0) == 0 and U(0.0, -0.0) == 0
+    assert U(1.0, 1.0 + 2.0 ** -7) == 1 and U(1.0 + 2.0 ** -7, 1.0) == 1
+    assert U(2.0 - 2.0 ** -7, 2.0) == 1               # across a binade edge
+    assert U(1.0, 2.0) == 128                          # one binade holds 128 values
+    assert U(tiny, -tiny) == 2 and U(tiny, 0.0) == 1 and U(-tiny, -0.0) == 1
+    assert U(-1.0, 1.0) == 2 * 0x3F80                  # through zero: both magnitudes
+    assert U(big, np.inf) == 1 and U(-big, -np.inf) == 1
+    # all finite bf16 values, -0 merged with +0, sorted by value
+    pats = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    vals = pats.view(np.float32).astype(np.float64)
+    grid = np.unique(vals[np.isfinite(vals)])          # unique also merges -0 and +0
+    pos = {v: i for i, v in enumerate(grid.tolist())}
+    rng = np.random.default_rng(13)
+    a = grid[rng.integers(0, len(grid), 4000)]
+    b = np.where(rng.random(4000) < 0.5, grid[rng.integers(0, len(grid), 4000)],
+                 grid[np.clip(np.searchsorted(grid, a) + rng.integers(-3, 4, 4000), 0,
+                              len(grid) - 1)])
+    want = np.array([abs(pos[x] - pos[y]) for x, y in zip(a.tolist(), b.tolist())])
+    assert np.array_equal(oracle.ulps_bf16(a, b), want)
+
+
+def test_cached_selection_pins():
+    """A kept row of the selection cache at a grown length: hand-worked sets, then random
+    rows against the neighbour-fetching set with width 0 (another function, built as a
+    Python set) and the invariants: the previous set survives below the new window, the
+    window at the current length is always there, nothing at or past L."""
+    C = oracle.cached_selection
+    assert C([0, 1, 5, 9], 12, 3).tolist() == [0, 1, 5, 9, 10, 11]
+    assert C([0, 1, 5, 9], 10, 3).tolist() == [0, 1, 5, 7, 8, 9]      # same length
+    assert C([0, 3, 9, 11], 10, 2).tolist() == [0, 3, 8, 9]           # past L: dropped
+    assert C([], 5, 9).tolist() == [0, 1, 2, 3, 4]                     # window wider than L
+    assert C([2], 6, 0).tolist() == [2]
+    rng = np.random.default_rng(17)
+    for trial in range(80):
+        L = int(rng.integers(1, 300))
+        nw = int(rng.integers(0, 40))
+        Lp = int(rng.integers(1, L + 1))
+        prev = np.sort(rng.choice(Lp, size=int(rng.integers(0, Lp + 1)), replace=False))
+        got = C(prev, L, nw)
+        assert np.array_equal(got, oracle.expand_neighbors(prev, L, 0, nw))
+        assert np.all(np.diff(got) > 0) and (len(got) == 0 or got[-1] < L)
+        assert set(range(max(0, L - nw), L)) <= set(got.tolist())
+        assert set(prev[prev < L].tolist()) <= set(got.tolist())
+
+
+def test_masked_attention_rows_causal_prefill_matches_sdpa():
+    """Prefill rows (Lq > 1): row i of a chunk at q_pos0 attends over its own selected set
+    inside its causal prefix; torch SDPA with a per-(head, row) boolean mask gives the same
+    outputs for every row of several chunks, per KV head and per query head."""
+    rng = np.random.default_rng(49)
+    B, Hq, Hkv, D, Lq, q_pos0 = 2, 4, 2, 8, 6, 5
+    L = q_pos0 + Lq
+    k = rng.standard_normal((B, Hkv, L, D)); v = rng.standard_normal((B, Hkv, L, D))
+    q = rng.standard_normal((B, Hq, Lq, D))
+    for gs in (2, 1):
+        Hs = Hq // gs
+        sel = [[[np.sort(rng.choice(q_pos0 + i + 1, size=int(rng.integers(1, q_pos0 + i + 2)),
+                                    replace=False)) for i in range(Lq)]
+                for _ in range(Hs)] for _ in range(B)]
+        got = ref.masked_attention_rows(q, k, v, sel, 0.45, sel_group=gs)
+        assert len(got) == B * Hq * Lq
+        mask = torch.zeros(B, Hq, Lq, L, dtype=torch.bool)
+        for b in range(B):
+            for h in range(Hq):
+                for i in range(Lq):
+                    mask[b, h, i, sel[b][h // gs][i]] = True
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1)),
+            torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1)), attn_mask=mask, scale=0.45)
+        for (b, h, i), o in got.items():
+            np.testing.assert_allclose(o, want[b, h, i].numpy(), rtol=0, atol=1e-12)
+
+
+def test_ulps_and_cached_selection_mutations_are_caught(monkeypatch):
+    good_u = ref.ulps_bf16
+
+    def ulps_no_sign(a, b):                       # a dropped sign: magnitudes only
+        f = lambda x: np.asarray(x, np.float64).astype(np.float32).view(np.uint32).astype(np.int64) >> 16 & 0x7FFF
+        return np.abs(f(a) - f(b))
+    monkeypatch.setattr(oracle, "ulps_bf16", ulps_no_sign)
+    with pytest.raises(AssertionError):
+        test_ulps_bf16_pins()
+    monkeypatch.setattr(oracle, "ulps_bf16", good_u)
+
+    good_c = ref.cached_selection
+    # the window taken at the earlier length: no token appended since is attended
+    monkeypatch.setattr(oracle, "cached_selection",
+                        lambda prev, L, nw: good_c(prev, max(int(np.max(prev, initial=0)) + 1, 1), nw)
+                        if len(prev) else good_c(prev, L, nw))
+    with pytest.raises(AssertionError):
+        test_cached_selection_pins()
+    monkeypatch.setattr(oracle, "cached_selection", good_c)
