@@ -143,10 +143,11 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-# Workspaces: one zero-initialised buffer per (entry point, device, call shape).  The
-# library leaves the accumulators inside a workspace zero after every call, so a buffer is
-# reused by every later call of the same shape on one stream; a call of another shape may
-# lay the workspace out differently and gets its own buffer.
+# Workspaces: one zero-initialised buffer per (entry point, device, key).  The library
+# leaves the accumulators inside a workspace zero after every call, so a buffer is reused
+# by every later call with the same key on one stream.  The key is the call shape, except
+# for the selection calls, whose state between calls depends only on their rows: they key
+# by rows and grow the buffer (a new zeroed one) when a longer row needs more.
 _WS: Dict[tuple, torch.Tensor] = {}
 
 
@@ -298,7 +299,7 @@ def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n
             int(bool(budget_excludes_forced)), _ptr(idx), _ptr(bitmask), _ptr(count), B, Hkv, Lq,
             L, cap, q_pos0, int(causal))
     need = workspace_bytes(lambda ws, n: lib.butler_select_topk(_stream(stream), *args, ws, n))
-    ws, n = _workspace("select", need, scores.device, (budget_num, budget_den, B, Hkv, Lq, L, cap, q_pos0, int(causal)))
+    ws, n = _workspace("select", need, scores.device, (B * Hkv * Lq,))
     _check("butler_select_topk",
            lib.butler_select_topk(_stream(stream), *args, ws, _byref(n)))
 
@@ -366,7 +367,9 @@ def butler_select_attend(scores: torch.Tensor, budget_num: int, budget_den: int,
             _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Hq, Hkv, sel_group, D, L, L_cap,
             idx.shape[3], float(softmax_scale))
     need = workspace_bytes(lambda ws, n: lib.butler_select_attend(_stream(stream), *args, ws, n))
-    ws, n = _workspace("select_attend", need, q.device, tuple(args[3:8]) + tuple(args[14:]))
+    # the selection state comes first and depends on the rows only; the attention part
+    # behind it is rewritten by every call
+    ws, n = _workspace("select_attend", need, q.device, (B * Hs,))
     _check("butler_select_attend",
            lib.butler_select_attend(_stream(stream), *args, ws, _byref(n)))
 

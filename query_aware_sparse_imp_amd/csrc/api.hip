@@ -297,8 +297,12 @@ int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t*
   }
   if (rows * ((cap + 255) / 256) > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
   const bool fused = select_attend_fusable(dtype, D, Hq, Hs, L);
-  // unfused: the selection's workspace, then the attention's
-  const size_t sel_ws = (select_workspace((int)rows, L, 1, 0) + 255) / 256 * 256;
+  // unfused: the selection's workspace, then the attention's.  The selection part is at
+  // least the state region, so a buffer that also serves fused calls (longer rows) keeps
+  // that state when a short row takes this path.
+  size_t sel_ws = select_workspace((int)rows, L, 1, 0);
+  if (sel_ws < select_state_bytes((int)rows)) sel_ws = select_state_bytes((int)rows);
+  sel_ws = (sel_ws + 255) / 256 * 256;
   const size_t need = fused ? select_attend_workspace((int)rows, Hq, Hs, L)
                             : sel_ws + attn_workspace(dtype, B, Hq, Hs, D, 1, L, cap);
   int rc;

@@ -41,6 +41,9 @@ hipError_t launch_score_softvote(hipStream_t s, int dtype, const void* q, const 
 
 // ---- selection ------------------------------------------------------------
 size_t select_workspace(int rows, int L, int Lq, int causal);
+// The leading part of a chunked-selection workspace that carries state from one call to
+// the next; it depends only on the rows.
+size_t select_state_bytes(int rows);
 hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
                          int n_window, int fo, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,

@@ -37,8 +37,9 @@
 //   through 64-token ballot words with two block-wide scans over the words (tie ranks,
 //   then output positions).
 //
-// Single-row calls with selection-cache flags skip the rows of kept (b, KV heads) in
-// every kernel, so their outputs and the workspace state stay as they were.
+// Single-row calls with selection-cache flags skip the selection of kept (b, KV heads) in
+// every kernel, so the workspace state stays as it was; one workgroup of the row only
+// re-takes the recent window at the current length in the kept list (and bitmask).
 #include "attn_tile.h"
 #include "common.h"
 #include "kernels.h"
@@ -119,6 +120,46 @@ __device__ void find_bin_from_bottom(const uint32_t* hist, int nbins, int need, 
   __syncthreads();
 }
 
+// A row the selection cache keeps (keep != 0): its previous selection stands, but the
+// recent window is re-taken at the current length L, so tokens appended since the
+// selection was made are attended.  The list becomes its entries below
+// w_lo = max(0, L - n_window) followed by w_lo .. L-1 (at most cap entries), and the
+// bitmask gains the window's bits.  NT threads of one workgroup; the entries are counted
+// before any is overwritten.
+template <int NT>
+__device__ void refresh_kept_row(long long row, int L, int n_window, int cap,
+                                 int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask,
+                                 int32_t* __restrict__ count, int* tmp) {
+  const int w_lo = max(0, L - n_window);
+  if (idx) {
+    int32_t* irow = idx + row * (long long)cap;
+    const int n_old = min(max((int)count[row], 0), cap);
+    int below = 0;
+    for (int j = threadIdx.x; j < n_old; j += NT) below += (irow[j] < w_lo) ? 1 : 0;
+    int p;
+    block_exclusive_sum<NT>(below, p, tmp);   // p: the entries kept below the window
+    for (int j = threadIdx.x; j < L - w_lo && p + j < cap; j += NT) irow[p + j] = w_lo + j;
+    if (threadIdx.x == 0) count[row] = min(p + (L - w_lo), cap);
+  }
+  if (bitmask) {
+    const int nwords = (L + 31) / 32;
+    uint32_t* brow = bitmask + row * (long long)nwords;
+    int bits = 0;
+    for (int wd = threadIdx.x; wd < nwords; wd += NT) {
+      uint32_t v = brow[wd];
+      if (32 * wd + 32 > w_lo) {
+        const int lo = max(w_lo - 32 * wd, 0), hi = min(L - 32 * wd, 32);   // bits [lo, hi)
+        v |= (hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
+        brow[wd] = v;
+      }
+      bits += __popc(v);
+    }
+    int total;
+    block_exclusive_sum<NT>(bits, total, tmp);
+    if (!idx && threadIdx.x == 0) count[row] = total;   // without a list: the row's bits
+  }
+}
+
 // ---------------------------------------------------------------------------
 // one workgroup per row, keys in VGPRs
 // ---------------------------------------------------------------------------
@@ -156,7 +197,11 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
   constexpr int NW = NT / 64;
   constexpr int MAXW = NT * KPT / 64;
   const long long row = blockIdx.x;
-  if (keep && keep[row]) return;   // single-row calls: the cached selection stands
+  __shared__ int tmp[NW];
+  if (keep && keep[row]) {   // single-row calls: the cached selection stands, window refreshed
+    refresh_kept_row<NT>(row, L, n_window, cap, idx, bitmask, count, tmp);
+    return;
+  }
   const int i = (int)(row % Lq);
   const int L_r = causal ? min(q_pos0 + i + 1, L) : L;
   int k;
@@ -167,7 +212,6 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
   const uint64_t lt = (1ull << lane) - 1ull;
 
   __shared__ uint32_t hist[2048];
-  __shared__ int tmp[NW];
   __shared__ int sh_bin, sh_need;
   __shared__ int wtie[MAXW], wcnt[MAXW];
   __shared__ uint64_t wsel[MAXW];
@@ -349,10 +393,18 @@ long long nchunk_k(int L, int kpt) {
 
 long long nchunk_for(int L) { return nchunk_k(L, kpt_for(L)); }
 
+// The workspace starts with the state that lives from one call to the next (the
+// first-digit histogram, the call counters, the coarse histograms, the row states): its
+// layout depends only on the number of rows, so one buffer sized for the longest row
+// serves calls of any length.  The per-chunk arrays behind it are rewritten by every call.
+size_t mb_state_bytes(long long rows) {
+  return al256(rows * 2048 * 4) + al256(rows * 4) + al256(2 * rows * 64 * 4) +
+         al256(rows * sizeof(RowState));
+}
+
 size_t mb_bytes_k(long long rows, int L, int kpt) {
   const long long nchunk = nchunk_k(L, kpt);
-  return al256(rows * 2048 * 4) + al256(rows * sizeof(RowState)) +
-         2 * al256(rows * nchunk * 4) + al256(rows * 4) + al256(2 * rows * 64 * 4) +
+  return mb_state_bytes(rows) + 2 * al256(rows * nchunk * 4) +
          al256((size_t)rows * nchunk * 64 * 4) +
          al256((size_t)rows * nchunk * kMbThreads * kpt * sizeof(uint2));
 }
@@ -364,11 +416,11 @@ MbWs carve_k(void* ws, long long rows, int L, int kpt) {
   char* p = (char*)ws;
   MbWs w;
   w.hist1 = (uint32_t*)p;                 p += al256(rows * 2048 * sizeof(uint32_t));
+  w.epoch = (uint32_t*)p;                 p += al256(rows * 4);
+  w.hist2 = (uint32_t*)p;                 p += al256(2 * rows * 64 * 4);
   w.state = (RowState*)p;                 p += al256(rows * sizeof(RowState));
   w.defcnt = (int*)p;                     p += al256(rows * nchunk * sizeof(int));
   w.ncand = (int*)p;                      p += al256(rows * nchunk * sizeof(int));
-  w.epoch = (uint32_t*)p;                 p += al256(rows * 4);
-  w.hist2 = (uint32_t*)p;                 p += al256(2 * rows * 64 * 4);
   w.ctab = (uint32_t*)p;                  p += al256((size_t)rows * nchunk * 64 * 4);
   w.cand = (uint2*)p;
   return w;
@@ -818,7 +870,11 @@ __global__ __launch_bounds__(kMbThreads) void mb_finish_kernel(
   constexpr int NWD = kMbWaves * KPT;   // 64-token words per chunk
   static_assert(NWD <= 128, "two words per lane in the prefix scan");
   const int row = blockIdx.x % rows, chunk = blockIdx.x / rows;
-  if (R == 0 && keep && keep[row]) return;   // the cached selection stands
+  if (R == 0 && keep && keep[row]) {   // the cached selection stands, window refreshed
+    __shared__ int ktmp[kMbWaves];
+    if (chunk == 0) refresh_kept_row<kMbThreads>(row, L, n_window, cap, idx, bitmask, count, ktmp);
+    return;
+  }
   const int nchunk = gridDim.x / rows;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   // fused attention: the group's query heads as the MFMA B operand, requested first
@@ -1144,6 +1200,8 @@ hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int
 size_t select_workspace(int rows, int L, int Lq, int causal) {
   return use_chunked(Lq, L, causal) ? mb_bytes(rows, L) : 0;
 }
+
+size_t select_state_bytes(int rows) { return mb_state_bytes(rows); }
 
 hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, int n_sink,
                          int n_window, int fo, int32_t* idx, uint32_t* bitmask, int32_t* count,

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synthetic
 from parity import (ATOL, check_attend, check_project, check_select_exact, decode_step_gpu,
-                    np64, pv_rounding_bound, to_device)
+                    np64, pv_rounding_bound, check_pv_rounding, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -226,7 +226,7 @@ def test_project_and_score_matches_separate_calls(cfg, L):
 def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
     """butler_select_attend == butler_select_topk + butler_sparse_decode_attn: idx and count
     bit for bit, the output within the bf16 probability rounding of the separate attention
-    (pv_rounding_bound: the two split the set differently) and within
+    (per element, pv_rounding_bound: the two split the set differently) and within
     the bf16 bound of the oracle's attention over the same sets; three calls in a row (the
     selection's workspace state carries over between calls)."""
     import query_aware_sparse_imp_amd as qa
@@ -263,6 +263,9 @@ def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
     qa.butler_sparse_decode_attn(q, k, v, out_a, L=L, idx=idx_a, count=cnt_a,
                                  softmax_scale=w.scale)
     torch.cuda.synchronize()
+    ia, ca = idx_a.cpu().numpy(), cnt_a.cpu().numpy()
+    gate = pv_rounding_bound(inp["q"], inp["k_cache"], inp["v_cache"],
+                             lambda b, j, i: ia[b, j, i, :ca[b, j, i]], w.scale)
     for rep in range(3):
         idx_b = torch.full_like(idx_a, -1)
         cnt_b = torch.zeros_like(cnt_a)
@@ -273,8 +276,7 @@ def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
         torch.cuda.synchronize()
         assert torch.equal(cnt_a, cnt_b), rep
         assert torch.equal(idx_a, idx_b), rep
-        d = float((out_a - out_b).abs().max())
-        assert d <= pv_rounding_bound(v), (rep, d)
+        d = check_pv_rounding(out_a, out_b, gate)
     check_select_exact(idx_b, cnt_b, np64(scores), num, den, w.n_sink, w.n_window,
                        exclude_forced=fo)
     ic, cc = idx_b.cpu().numpy(), cnt_b.cpu().numpy()
@@ -282,3 +284,39 @@ def test_select_attend_matches_separate_calls(L, Hq, num, den, use_hist):
                        lambda b, g, i: ic[b, g, i, :cc[b, g, i]], w.scale, w.dtype)
     print(f"  selected {int(cc.sum())}, fused vs separate max-abs {d:.2e}, vs oracle {err:.2e}",
           flush=True)
+
+
+def test_select_attend_workspace_shared_across_lengths():
+    """One workspace (the binding keys the selection calls' buffers by rows) serves calls of
+    different lengths in turn: a long row (chunked selection fused with attention, whose
+    state lives at the start of the buffer), a short row (per-row selection, then the
+    separate attention, whose partials follow that state), the long row again, and a
+    length in between.  Every call must give the same idx, count and output as the first
+    call of its length on a fresh buffer (bitwise), and the sets the oracle's."""
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[2]
+    dev = "cuda"
+    lengths = [70001, 3001, 70001, 9000, 3001, 70001]
+    ins, ref = {}, {}
+    for L in sorted(set(lengths)):
+        inp = to_device(synthetic.decode_layer(w, 5, L=L, with_qimp=False))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(L)
+        ins[L] = (inp, torch.randn(w.B, w.Hkv, 1, L, generator=gen, device=dev))
+    for n, L in enumerate(lengths):
+        inp, scores = ins[L]
+        cap = w.cap(L)
+        idx = torch.full((w.B, w.Hkv, 1, cap), -1, dtype=torch.int32, device=dev)
+        cnt = torch.zeros(w.B, w.Hkv, 1, dtype=torch.int32, device=dev)
+        out = torch.empty(w.B, w.Hq, 1, w.D, dtype=torch.float32, device=dev)
+        print(f"[shared workspace] call {n}: L={L}", flush=True)
+        qa.butler_select_attend(scores, 1, 16, w.n_sink, w.n_window, cnt, idx, inp["q_d"],
+                                inp["k_cache_d"], inp["v_cache_d"], out, L=L,
+                                softmax_scale=w.scale)
+        torch.cuda.synchronize()
+        if L not in ref:
+            ref[L] = (idx.clone(), cnt.clone(), out.clone())
+            check_select_exact(idx, cnt, np64(scores), 1, 16, w.n_sink, w.n_window)
+        else:
+            assert torch.equal(idx, ref[L][0]) and torch.equal(cnt, ref[L][1]), (n, L)
+            assert torch.equal(out, ref[L][2]), (n, L)
