@@ -84,8 +84,10 @@ int butler_abi_version(void);
  *   k_cache [B, Hkv, L_cap, D]      dtype   cached keys (read)
  *   w_k     [D, d']                 dtype   projection of this layer, shared by all KV heads
  *   kimp    [B, Hkv, L_cap, d']     dtype   rows pos0 .. pos0+n_new-1 written, others untouched
- * Each output is the exact dot product (float64 accumulation) rounded once, to nearest
- * even, into dtype.
+ * Each output is the dot product accumulated in float64 and rounded once, to nearest
+ * even, into dtype.  For bf16 inputs the float64 sum is exact, so the result is the
+ * exactly rounded dot product; for float32 inputs the float64 sum may round (products
+ * take up to 48 bits), which in rare cases moves the result by one float32 ulp.
  * D in {64, 128}; d' in {16, 32}; 0 <= pos0, n_new >= 1, pos0 + n_new <= L_cap.
  */
 int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
@@ -125,8 +127,11 @@ int butler_produce_queries(void* stream, int dtype, const void* h, const void* w
  *   score[b, j, i, t] = (sum over the query heads h of selection head j of
  *                        Q_imp[b, h, slot, i, :]) . K_imp[b, kv(j), t, :]
  *   (kv(j) = j * sel_group / R, the KV head of those query heads)
- *   computed exactly (float64 products and sums of the stored values) and rounded once
- *   to float32.  dk = d'.
+ *   computed from float64 products and float64 sums of the stored values, rounded once
+ *   to float32.  For bf16 inputs every product and partial sum is exact in float64, so
+ *   the score is the exactly rounded dot product whatever the summation order.  For
+ *   float32 inputs a product takes up to 48 bits and the float64 sums may round, so in
+ *   rare cases the result differs from the exactly rounded value.  dk = d'.
  * BUTLER_SCORE_SOFTVOTE (TokenSelect README, highlights: per-head Q.K criticality,
  * normalised by a softmax per head, summed over heads):
  *   q     = [B, Hq, Lq, D] attention queries, keys = k_cache [B, Hkv, L_cap, D]
@@ -203,8 +208,17 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
  *
  *   scores  [B, Hs, Lq, L]           float32 (read)
  *   keep    [B, Hs]                  int32, optional (NULL = none), single-row calls only:
- *                                    rows with keep != 0 are skipped; their idx, bitmask
- *                                    and count keep the previous selection.
+ *                                    rows with keep != 0 are not selected again: they keep
+ *                                    the previous selection with the window re-taken at
+ *                                    the current L (the cache may have grown since), i.e.
+ *                                    S = {t in S_prev : t < max(0, L - n_window)}
+ *                                        U [max(0, L - n_window), L).
+ *                                    idx then holds the first min(|S|, cap) entries of S
+ *                                    and count = min(|S|, cap): a kept row grows by one
+ *                                    entry per token appended since its selection, so cap
+ *                                    must leave room for them.  bitmask (laid out for the
+ *                                    current L) gains the window's bits; with a bitmask and
+ *                                    no idx, count is the number of bits set in the row.
  *   radix_hist [B, Hs, Lq, 2048]     uint32, optional: the histogram butler_score built for
  *                                    exactly these scores (see butler_score); it is used
  *                                    instead of a counting pass and zero-filled again.  NULL:
@@ -219,8 +233,12 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
  * multi-row (Lq > 1) call hold at most 65536 tokens; single-row decode calls up to 2^23.
  * workspace: none for causal / multi-row calls and rows up to 4096 tokens; otherwise a
  * radix histogram, each chunk's candidate keys, per-chunk counts and coarse-bin tables
- * (about 8 bytes per token per row).  The state it carries between calls is valid for
- * any budget, so calls of one shape may share a workspace whatever their budgets.
+ * (about 8 bytes per token per row).  The state it carries between calls sits at the
+ * start of the buffer, depends only on the number of rows B * Hs * Lq and is valid for
+ * any budget and any L: one buffer sized for the longest row serves every call with the
+ * same rows, whatever their budgets and lengths (a decode loop whose cache grows by a
+ * token per step).  butler_select_attend lays out the same state the same way, so the
+ * two calls may share one buffer too.
  */
 int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
                        const int32_t* keep, int budget_num, int budget_den, int n_sink,
@@ -234,7 +252,14 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
  * (never evicted) KV cache.  For query head h (selection head j = h / sel_group, KV head
  * h / R) of row i:
  *   o[b, h, i, :] = sum_{t in S} softmax_t(softmax_scale * q . k_t) v_t
- * with float32 logits, float32 online softmax and float32 accumulation.
+ * with float32 logits, a float32 online softmax (running maximum m, normaliser
+ * l = sum of the float32 probabilities p_t = exp(z_t - m)) and float32 accumulation.
+ * Precision of P.V: with bf16 inputs and D = 128 (the matrix-core kernels: decode with
+ * R in {1, 2, 4, 8}, prefill with R = 4) the probabilities enter the product rounded to
+ * bf16 while l sums the unrounded ones.  Each p_t then carries a relative error of at
+ * most 2^-8, so an output element lies within 2^-8 * sum_t p_t |v_t| / sum_t p_t
+ * (<= 2^-8 * max |v|) of the float32 result.  The other kernels (float32 inputs, D = 64)
+ * multiply float32 probabilities.
  *
  * Lq == 1 (decode): S comes from idx [B, Hs, 1, cap] / count [B, Hs, 1] as written by
  *   butler_select_topk (or butler_expand_neighbors); the list is split over workgroups
@@ -290,8 +315,9 @@ int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t*
  * (b, selection head j) of a decode step, the cosine similarity between j's current query
  * (the D-vectors of its query heads stacked into one vector) and the reference query the
  * cached selection was made for:
- *   cos >= threshold  ->  keep[b, j] = 1: score and select skip the (b, j) rows and the
- *                         previous index list / bitmask / count stand;
+ *   cos >= threshold  ->  keep[b, j] = 1: score and select skip the (b, j) rows; the
+ *                         previous index list / bitmask stand, with the recent window
+ *                         re-taken at the current length (see butler_select_topk);
  *   otherwise         ->  keep[b, j] = 0 and q_ref takes q for j's heads: the next score
  *                         and select recompute the selection for this query.
  * A zero vector on either side gives cos = 0.  The similarity is accumulated in float32

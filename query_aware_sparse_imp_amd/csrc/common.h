@@ -157,11 +157,6 @@ template <> __device__ __forceinline__ void unpack16<float>(const Raw16& r, floa
   out[2] = __uint_as_float(r.v.z); out[3] = __uint_as_float(r.v.w);
 }
 
-// Atomic ticket at agent scope: returns the previous value.
-__device__ __forceinline__ int ticket_take(int* t) {
-  return __hip_atomic_fetch_add(t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Sum of a double over aligned groups of N lanes (N in {1, 2, 4, 8}): quad-permute DPP
 // moves of both 32-bit halves, then one xor-4 shuffle for N = 8; every lane of a group
 // ends with the same bits.

@@ -140,13 +140,48 @@ def decode_step_gpu(inp: dict, kimp: torch.Tensor, L: int, mode: int, q_imp=None
     return {"scores": scores, "idx": idx, "count": count, "out": out, "num": num, "den": den}
 
 
-def pv_rounding_bound(v_cache: torch.Tensor) -> float:
-    """Largest difference allowed between two GPU attention outputs over the same set that
-    split it differently.  The matrix-core P.V rounds every probability to bf16 (relative
-    error <= 2^-9) against the softmax sum of the unrounded ones, so each output lies
-    within 2^-9 * max|v| of the float32 result; two of them within 2^-8 * max|v|, plus
-    float32 reordering (1e-5)."""
-    return 2.0 ** -8 * float(v_cache.float().abs().max()) + 1e-5
+def pv_rounding_bound(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, sets,
+                      scale: float, sel_group: int = 0) -> np.ndarray:
+    """Per-element gate [B, Hq, D] for two GPU attention outputs over the same selected sets
+    that split them differently (the fused select+attend call against the separate calls).
+
+    The matrix-core P.V rounds every probability p_t = exp(z_t - m) to bf16 (8 significant
+    bits: a rounding error of at most 2^-8 p_t, uniform over +-half an ulp, so of standard
+    deviation at most 2^-8 p_t / sqrt(3)), while the normaliser sums the unrounded p_t.
+    The two outputs use different running maxima m, so their roundings are independent;
+    element d of head h differs by sum_t (e1_t - e2_t) v_td / sum_t p_t, whose standard
+    deviation is at most sqrt(2) * 2^-8 / sqrt(3) * sqrt(sum_t p_t^2 v_td^2) / sum_t p_t.
+    The gate is six of those (a chance below 2e-9 per element) plus 1e-5 for float32
+    summation order, computed from the row's own probabilities (float64, the oracle's
+    logits).  It never exceeds the worst case 2 * 2^-8 * sum_t p_t |v_td| / sum_t p_t.
+    sets(b, j, i) is the selected set of selection head j."""
+    qn, kn, vn = np64(q), np64(k_cache), np64(v_cache)
+    B, Hq, _, D = qn.shape
+    Hkv = kn.shape[1]
+    R = Hq // Hkv
+    gs = sel_group or R
+    sig = math.sqrt(2.0) * 2.0 ** -8 / math.sqrt(3.0)
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        for h in range(Hq):
+            sel = np.asarray(sets(b, h // gs, 0), np.int64)
+            kr, vr = kn[b, h // R, sel], vn[b, h // R, sel]
+            z = (kr @ qn[b, h, 0]) * scale
+            p = np.exp(z - z.max())
+            stat = 6.0 * sig * np.sqrt((p[:, None] ** 2 * vr ** 2).sum(0)) / p.sum()
+            worst = 2.0 * 2.0 ** -8 * (p[:, None] * np.abs(vr)).sum(0) / p.sum()
+            out[b, h] = np.minimum(stat, worst) + 1e-5
+    return out
+
+
+def check_pv_rounding(out_a: torch.Tensor, out_b: torch.Tensor, bound: np.ndarray) -> float:
+    """|out_a - out_b| within the per-element gate of pv_rounding_bound; returns the largest
+    difference."""
+    d = np.abs(out_a.cpu().double().numpy()[:, :, 0] - out_b.cpu().double().numpy()[:, :, 0])
+    bad = d > bound
+    assert not bad.any(), (f"fused vs separate: {int(bad.sum())} elements over the gate, "
+                           f"worst {float((d - bound).max()):.3e} above it")
+    return float(d.max())
 
 
 def to_device(inp: dict, device="cuda") -> dict:

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synthetic
-from parity import ATOL, pv_rounding_bound, bitmask_to_sets, check_project, check_select_exact, np64, to_device
+from parity import ATOL, pv_rounding_bound, check_pv_rounding, bitmask_to_sets, check_project, check_select_exact, np64, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -108,6 +108,8 @@ def test_decode_chain_per_selection_head(L, gs, den):
     assert torch.equal(hist2.sum(-1), torch.full_like(hist2.sum(-1), L))
 
     # fused selection + attention, twice (the workspace state carries over)
+    gate = pv_rounding_bound(inp["q"], inp["k_cache"], inp["v_cache"], sets, w.scale,
+                             sel_group=gs)
     for rep in range(2):
         idx_b = torch.full_like(idx, -1)
         cnt_b = torch.zeros_like(cnt)
@@ -117,8 +119,7 @@ def test_decode_chain_per_selection_head(L, gs, den):
                                 radix_hist=hist2 if rep == 0 else None, sel_group=gs)
         torch.cuda.synchronize()
         assert torch.equal(cnt_b, cnt) and torch.equal(idx_b, idx), rep
-        d = float((out_b - out).abs().max())
-        assert d <= pv_rounding_bound(v), (rep, d)
+        d = check_pv_rounding(out, out_b, gate)
     assert int(hist2.abs().sum()) == 0
     print(f"  fused calls: same K_imp row, scores, sets; output within {d:.2e}", flush=True)
 
