@@ -149,3 +149,111 @@ def test_prefill_small_chunks():
 def test_prefill_llama_shape_one_chunk_pair():
     w = synthetic.WORKLOADS[5].replace(B=2)
     _prefill_case(w, L=2048, chunk=1024)
+
+
+def _sample_rows(rng, B, Hkv, Lq, n):
+    """n (b, g, i) rows of a chunk: its first and last rows of the first and last heads,
+    the rest at random."""
+    fixed = [(0, 0, 0), (B - 1, Hkv - 1, Lq - 1), (0, Hkv - 1, Lq - 2), (B - 1, 0, Lq // 2)]
+    rnd = [(int(rng.integers(B)), int(rng.integers(Hkv)), int(rng.integers(Lq)))
+           for _ in range(n - len(fixed))]
+    return sorted(set(fixed + rnd))
+
+
+def test_prefill_full_size_all_chunks_sampled():
+    """The prefill workload at its stated size (B=2, L=8192, eight chunks of 1024 rows) in
+    the launch configuration the bench times: per chunk the producer on the chunk's hidden
+    rows (M = 2048), K_imp of the chunk's keys, causal raw scores against the prefix,
+    per-row top 50% + 4 + 64 into a bitmask, masked attention of every row.  K_imp is
+    compared whole; Q_imp, scores, sets and attention on sampled rows of every chunk
+    (including the last rows of the last chunk, whose prefix is the whole sequence)."""
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[5]
+    L, C = w.L, w.chunk
+    print(f"[prefill-full] B={w.B} L={L} chunk={C}", flush=True)
+    inp = synthetic.prefill_inputs(w, L=L)
+    dev = "cuda"
+    h_d = inp["h"].to(dev)
+    w1 = inp["w1"].t().contiguous().to(dev)
+    w2 = inp["w2"].t().contiguous().to(dev)
+    k_d, v_d, q_d = inp["k_cache"].to(dev), inp["v_cache"].to(dev), inp["q"].to(dev)
+    wk_d = inp["w_k"].to(dev)
+    kimp = torch.empty(w.B, w.Hkv, L, w.dprime, dtype=torch.bfloat16, device=dev)
+    hn, w1n, w2n = np64(inp["h"]), np64(inp["w1"]), np64(inp["w2"])
+    qn, kc, vc = np64(inp["q"]), np64(inp["k_cache"]), np64(inp["v_cache"])
+    rng = np.random.default_rng(5)
+    for c0 in range(0, L, C):
+        Lk = c0 + C
+        qimp = torch.empty(w.B, w.Hq, w.G, C, w.dprime, dtype=torch.bfloat16, device=dev)
+        qa.butler_produce_queries(h_d[:, c0:Lk].contiguous(), w1, w2, qimp)
+        qa.butler_project_keys(k_d, wk_d, kimp, c0, C)
+        scores = torch.empty(w.B, w.Hkv, C, Lk, dtype=torch.float32, device=dev)
+        hist = torch.zeros(w.B, w.Hkv, C, 2048, dtype=torch.int32, device=dev)
+        qa.butler_score(qa.BUTLER_SCORE_RAW, qimp, kimp, scores, Hkv=w.Hkv, L=Lk, slot=0,
+                        q_pos0=c0, causal=True, radix_hist=hist)
+        bm = torch.zeros(w.B, w.Hkv, C, (Lk + 31) // 32, dtype=torch.int32, device=dev)
+        cnt = torch.zeros(w.B, w.Hkv, C, dtype=torch.int32, device=dev)
+        qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink, w.n_window, cnt,
+                              bitmask=bm, q_pos0=c0, causal=True, radix_hist=hist)
+        out = torch.empty(w.B, w.Hq, C, w.D, dtype=torch.float32, device=dev)
+        qa.butler_sparse_decode_attn(q_d[:, :, c0:Lk].contiguous(), k_d, v_d, out, L=Lk,
+                                     bitmask=bm, q_pos0=c0, softmax_scale=w.scale)
+        torch.cuda.synchronize()
+        check_project(kimp, inp["k_cache"], inp["w_k"], c0, Lk)
+        rows = _sample_rows(rng, w.B, w.Hkv, C, 24)
+        # producer rows: every head and slot of the sampled token positions
+        ts = sorted({i for (_, _, i) in rows})
+        want_q = oracle.produce_queries(hn[:, [c0 + i for i in ts]], w1n, w2n, w.Hq, w.G,
+                                        w.dprime, 1e-5)
+        got_q = np64(qimp)[:, :, :, ts]
+        qerr = float(np.abs(got_q - want_q).max())
+        assert qerr <= 2e-2, (c0, qerr)
+        qi, kn = np64(qimp)[:, :, 0], np64(kimp)
+        sets = bitmask_to_sets(bm, Lk)
+        cn, o = cnt.cpu().numpy(), out.cpu().double().numpy()
+        worst = 0.0
+        for (b, g, i) in rows:
+            L_r = c0 + i + 1
+            want_s = oracle.score_raw(qi[b:b + 1, g * w.R:(g + 1) * w.R, i:i + 1],
+                                      kn[b:b + 1, g:g + 1, :Lk], 1, causal=True,
+                                      q_pos0=c0 + i)[0, 0, 0]
+            got_s = np64(scores[b, g, i])
+            assert np.array_equal(got_s, want_s), ("scores", c0, b, g, i)
+            want = oracle.select(got_s[:L_r], oracle.budget(L_r, w.budget_num, w.budget_den),
+                                 w.n_sink, w.n_window)
+            assert np.array_equal(np.nonzero(sets[b, g, i])[0], want), ("set", c0, b, g, i)
+            assert cn[b, g, i] == len(want)
+            for r in range(w.R):
+                hh = g * w.R + r
+                ref = oracle.attend(qn[b, hh, c0 + i][None], kc[b, g, want], vc[b, g, want],
+                                    w.scale)[0]
+                worst = max(worst, float(np.abs(o[b, hh, i] - ref).max()))
+        assert worst <= 2e-2, (c0, worst)
+        print(f"  chunk at {c0}: rows {len(rows)}, Q_imp max-abs {qerr:.2e}, "
+              f"attention max-abs {worst:.2e}", flush=True)
+
+
+def test_producer_whole_prompt_sampled():
+    """The producer over the whole prompt of both sequences at once (M = 16384 rows: the
+    matrix-core GEMM with one K split, its ReLU epilogue inside the GEMM), checked on
+    sampled token positions, every head and slot."""
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[5]
+    rows = w.L
+    print(f"[producer] B={w.B} rows={rows} (whole prompt)", flush=True)
+    h = synthetic.producer_hidden(w, 6, rows)
+    wts = synthetic.producer_weights(w, 6)
+    q_imp = torch.empty(w.B, w.Hq, w.G, rows, w.dprime, dtype=torch.bfloat16, device="cuda")
+    qa.butler_produce_queries(h.cuda(), wts["w1"].t().contiguous().cuda(),
+                              wts["w2"].t().contiguous().cuda(), q_imp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    ts = sorted(set([0, 1, 4095, 4096, rows - 1] + rng.integers(0, rows, 59).tolist()))
+    want = oracle.produce_queries(np64(h)[:, ts], np64(wts["w1"]), np64(wts["w2"]), w.Hq, w.G,
+                                  w.dprime, 1e-5)
+    got = np64(q_imp)[:, :, :, ts]
+    err = float(np.abs(got - want).max())
+    u = oracle.ulps_bf16(got, want)
+    print(f"  {len(ts)} positions: max-abs {err:.3e}, elements off by >=1 ulp: "
+          f"{(u > 0).mean():.4%}", flush=True)
+    assert err <= 2e-2
