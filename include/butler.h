@@ -72,7 +72,7 @@ enum butler_score_mode { BUTLER_SCORE_RAW = 0, BUTLER_SCORE_SOFTVOTE = 1 };
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* butler_status_string(int status);
 
-/* ABI version, currently 6. */
+/* ABI version, currently 7. */
 int butler_abi_version(void);
 
 /*
@@ -308,6 +308,30 @@ int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t*
                          const void* k_cache, const void* v_cache, float* out, int B, int Hq,
                          int Hkv, int sel_group, int D, int L, int L_cap, int cap,
                          float softmax_scale, void* workspace, size_t* ws_bytes);
+
+/*
+ * butler_select_attend_noalloc -- butler_select_attend without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture, and serving
+ * loops or harnesses that forbid hipMalloc.  The arguments, results, limits and error
+ * codes are those of butler_select_attend; idx, count and out are bitwise the same.  The
+ * call allocates nothing: its workspace is a fixed device array inside the library of
+ * BUTLER_NOALLOC_SCRATCH_BYTES bytes, one copy per GPU, held until the process ends.
+ * A call that needs more (the size butler_select_attend's workspace query reports; about
+ * 8 bytes per token per selection row, so up to ~7M tokens over all rows) returns
+ * BUTLER_ERR_WORKSPACE with nothing enqueued.  Every call on a GPU uses that GPU's one
+ * array: calls that may overlap on one GPU (other streams, other host threads) race and
+ * must be ordered by the caller.  Each call first clears, with a kernel on `stream`, the
+ * part of the array that must start at zero, so it depends on no earlier call.  The first
+ * call on a device looks up that device's copy (hipGetSymbolAddress) before enqueuing.
+ */
+#define BUTLER_NOALLOC_SCRATCH_BYTES (64u << 20)
+int butler_select_attend_noalloc(void* stream, int dtype, const float* scores,
+                                 uint32_t* radix_hist, int budget_num, int budget_den,
+                                 int n_sink, int n_window, int budget_excludes_forced,
+                                 int32_t* idx, int32_t* count, const void* q,
+                                 const void* k_cache, const void* v_cache, float* out, int B,
+                                 int Hq, int Hkv, int sel_group, int D, int L, int L_cap,
+                                 int cap, float softmax_scale);
 
 /*
  * butler_selection_cache -- TokenSelect README, highlights, Selection Cache: consecutive

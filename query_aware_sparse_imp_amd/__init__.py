@@ -20,7 +20,8 @@ __all__ = [
     "BUTLER_OK", "BUTLER_SCORE_RAW", "BUTLER_SCORE_SOFTVOTE", "ButlerError", "lib", "LIB_PATH",
     "butler_project_keys", "butler_produce_queries", "butler_score", "butler_project_and_score",
     "butler_select_topk",
-    "butler_sparse_decode_attn", "butler_select_attend", "butler_selection_cache",
+    "butler_sparse_decode_attn", "butler_select_attend", "butler_select_attend_noalloc",
+    "butler_selection_cache",
     "butler_expand_neighbors",
     "butler_status_string",
     "butler_abi_version", "declared_symbols", "workspace_bytes",
@@ -53,6 +54,8 @@ _SIGS = {
     "butler_selection_cache": ([_vp, _i, _vp, _vp, _vp] + [_i] * 5 + [_f], _i),
     "butler_select_attend": ([_vp, _i, _vp, _vp] + [_i] * 5 + [_vp] * 6 + [_i] * 8 +
                              [_f, _vp, _sz], _i),
+    "butler_select_attend_noalloc": ([_vp, _i, _vp, _vp] + [_i] * 5 + [_vp] * 6 + [_i] * 8 +
+                                     [_f], _i),
     "butler_expand_neighbors": ([_vp] * 5 + [_i] * 7, _i),
     "butler_sparse_decode_attn": ([_vp, _i] + [_vp] * 7 + [_i] * 10 + [_f, _vp, _sz], _i),
     "butler_fetch_rows": ([_vp, _i] + [_vp] * 6 + [_i] * 7, _i),
@@ -372,6 +375,37 @@ def butler_select_attend(scores: torch.Tensor, budget_num: int, budget_den: int,
     ws, n = _workspace("select_attend", need, q.device, (B * Hs,))
     _check("butler_select_attend",
            lib.butler_select_attend(_stream(stream), *args, ws, _byref(n)))
+
+
+def butler_select_attend_noalloc(scores: torch.Tensor, budget_num: int, budget_den: int,
+                                 n_sink: int, n_window: int, count: torch.Tensor,
+                                 idx: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                 v_cache: torch.Tensor, out: torch.Tensor, *, L: int,
+                                 softmax_scale: float, radix_hist: Optional[torch.Tensor] = None,
+                                 budget_excludes_forced: bool = False, sel_group: int = 0,
+                                 stream=None) -> None:
+    """butler_select_attend on the library's own fixed scratch array: no workspace is
+    passed or allocated (see butler.h).  Same arguments and results."""
+    B, Hs, Lq, Ls = scores.shape
+    Bq, Hq, Lq2, D = q.shape
+    Bk, Hkv, L_cap, D2 = k_cache.shape
+    if Lq != 1 or Lq2 != 1 or Ls != L or (Bq, Bk, D2) != (B, B, D):
+        raise ValueError("shape mismatch")
+    if Hs != selection_heads(Hq, Hkv, sel_group):
+        raise ValueError("scores must have Hs = Hq / sel_group selection heads")
+    if v_cache.shape != k_cache.shape or out.shape != (B, Hq, 1, D):
+        raise ValueError("shape mismatch")
+    if idx.shape[:3] != (B, Hs, 1) or count.shape != (B, Hs, 1):
+        raise ValueError("idx [B, Hs, 1, cap] and count [B, Hs, 1] required")
+    if scores.dtype != torch.float32 or out.dtype != torch.float32 or \
+            not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    _check_hist(radix_hist, (B, Hs, 1))
+    _check("butler_select_attend_noalloc", lib.butler_select_attend_noalloc(
+        _stream(stream), _dtype_code(q), _ptr(scores), _ptr(radix_hist), budget_num, budget_den,
+        n_sink, n_window, int(bool(budget_excludes_forced)), _ptr(idx), _ptr(count), _ptr(q),
+        _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Hq, Hkv, sel_group, D, L, L_cap,
+        idx.shape[3], float(softmax_scale)))
 
 
 def butler_selection_cache(q: torch.Tensor, q_ref: torch.Tensor, keep: torch.Tensor, *,

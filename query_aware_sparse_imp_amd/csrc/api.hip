@@ -80,6 +80,75 @@ inline bool sel_heads(int Hq, int Hkv, int sel_group, int* Hs, int* kvdiv) {
 
 }  // namespace
 
+namespace butler {
+
+// butler_select_attend, split so that its allocation-free variant (scratch.hip) runs the
+// same checks and launches on another buffer.
+int select_attend_plan(const SelectAttendArgs& a, SelectAttendPlan* plan) {
+  if (!valid_dtype(a.dtype)) return BUTLER_ERR_UNSUPPORTED;
+  if (a.B <= 0 || a.Hq <= 0 || a.Hkv <= 0 || a.L <= 0 || a.L_cap < a.L)
+    return BUTLER_ERR_INVALID_ARG;
+  if (a.budget_num < 0 || a.budget_den <= 0 || a.n_sink < 0 || a.n_window < 0)
+    return BUTLER_ERR_INVALID_ARG;
+  plan->fo = a.budget_excludes_forced ? 1 : 0;
+  if (plan->fo && a.radix_hist) return BUTLER_ERR_INVALID_ARG;   // see butler_select_topk
+  if (a.Hq % a.Hkv) return BUTLER_ERR_INVALID_ARG;
+  if (!pow2_group(a.Hq / a.Hkv) || !(a.D == 64 || a.D == 128)) return BUTLER_ERR_UNSUPPORTED;
+  if (!sel_heads(a.Hq, a.Hkv, a.sel_group, &plan->Hs, &plan->kvdiv)) return BUTLER_ERR_INVALID_ARG;
+  if (!(a.softmax_scale > 0.f)) return BUTLER_ERR_INVALID_ARG;
+  const long long rows = (long long)a.B * plan->Hs;
+  if (rows > 0x7fffffffLL || a.L > 8388608) return BUTLER_ERR_UNSUPPORTED;
+  {
+    const long long x = (long long)a.L * a.budget_num / a.budget_den;
+    long long need_cap = x + a.n_sink + a.n_window;
+    if (need_cap > a.L) need_cap = a.L;
+    if (a.cap < need_cap) return BUTLER_ERR_INVALID_ARG;
+  }
+  if (rows * ((a.cap + 255) / 256) > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
+  plan->rows = (int)rows;
+  plan->fused = select_attend_fusable(a.dtype, a.D, a.Hq, plan->Hs, a.L);
+  // unfused: the selection's workspace, then the attention's.  The selection part is at
+  // least the state region, so a buffer that also serves fused calls (longer rows) keeps
+  // that state when a short row takes this path.
+  size_t sel_ws = select_workspace(plan->rows, a.L, 1, 0);
+  if (sel_ws < select_state_bytes(plan->rows)) sel_ws = select_state_bytes(plan->rows);
+  plan->sel_ws = (sel_ws + 255) / 256 * 256;
+  plan->need = plan->fused
+                   ? select_attend_workspace(plan->rows, a.Hq, plan->Hs, a.L)
+                   : plan->sel_ws + attn_workspace(a.dtype, a.B, a.Hq, plan->Hs, a.D, 1, a.L, a.cap);
+  return BUTLER_OK;
+}
+
+int select_attend_check_pointers(const SelectAttendArgs& a) {
+  if (!a.scores || !a.idx || !a.count || !a.q || !a.k_cache || !a.v_cache || !a.out)
+    return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(a.scores) || !aligned16(a.q) || !aligned16(a.k_cache) || !aligned16(a.v_cache) ||
+      !aligned16(a.out))
+    return BUTLER_ERR_INVALID_ARG;
+  if (a.radix_hist && !aligned16(a.radix_hist)) return BUTLER_ERR_INVALID_ARG;
+  return BUTLER_OK;
+}
+
+hipError_t select_attend_launch(hipStream_t s, const SelectAttendArgs& a,
+                                const SelectAttendPlan& plan, void* ws) {
+  if (plan.fused)
+    return launch_select_attend(s, a.scores, a.budget_num, a.budget_den, a.n_sink, a.n_window,
+                                plan.fo, a.idx, a.count, a.B, a.Hq, plan.Hs, a.L, a.cap,
+                                a.radix_hist, a.q, a.k_cache, a.v_cache, a.out, a.L_cap,
+                                a.softmax_scale, ws, plan.kvdiv);
+  hipError_t e = launch_select(s, a.scores, a.budget_num, a.budget_den, a.n_sink, a.n_window,
+                               plan.fo, a.idx, nullptr, a.count, a.B, plan.Hs, 1, a.L, a.cap, 0,
+                               0, a.radix_hist, nullptr, ws);
+  if (e != hipSuccess) return e;
+  return launch_attn_idx(s, a.dtype, a.q, a.k_cache, a.v_cache, a.idx, a.count, a.out, a.B,
+                         a.Hq, plan.Hs, a.D, 1, a.L_cap, a.cap, a.softmax_scale,
+                         (char*)ws + plan.sel_ws, plan.kvdiv);
+}
+
+int finish_call(hipStream_t s, hipError_t e) { return finish(s, e); }
+
+}  // namespace butler
+
 extern "C" {
 
 const char* butler_status_string(int status) {
@@ -93,7 +162,7 @@ const char* butler_status_string(int status) {
   }
 }
 
-int butler_abi_version(void) { return 6; }
+int butler_abi_version(void) { return 7; }
 
 int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
                         void* kimp, int B, int Hkv, int L_cap, int D, int dprime, int pos0,
@@ -277,52 +346,17 @@ int butler_select_attend(void* stream, int dtype, const float* scores, uint32_t*
                          const void* k_cache, const void* v_cache, float* out, int B, int Hq,
                          int Hkv, int sel_group, int D, int L, int L_cap, int cap,
                          float softmax_scale, void* workspace, size_t* ws_bytes) {
-  if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || L_cap < L) return BUTLER_ERR_INVALID_ARG;
-  if (budget_num < 0 || budget_den <= 0 || n_sink < 0 || n_window < 0) return BUTLER_ERR_INVALID_ARG;
-  const int fo = budget_excludes_forced ? 1 : 0;
-  if (fo && radix_hist) return BUTLER_ERR_INVALID_ARG;   // see butler_select_topk
-  if (Hq % Hkv) return BUTLER_ERR_INVALID_ARG;
-  if (!pow2_group(Hq / Hkv) || !(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
-  int Hs, kvdiv;
-  if (!sel_heads(Hq, Hkv, sel_group, &Hs, &kvdiv)) return BUTLER_ERR_INVALID_ARG;
-  if (!(softmax_scale > 0.f)) return BUTLER_ERR_INVALID_ARG;
-  const long long rows = (long long)B * Hs;
-  if (rows > 0x7fffffffLL || L > 8388608) return BUTLER_ERR_UNSUPPORTED;
-  {
-    const long long x = (long long)L * budget_num / budget_den;
-    long long need_cap = x + n_sink + n_window;
-    if (need_cap > L) need_cap = L;
-    if (cap < need_cap) return BUTLER_ERR_INVALID_ARG;
-  }
-  if (rows * ((cap + 255) / 256) > 0x7fffffffLL) return BUTLER_ERR_UNSUPPORTED;
-  const bool fused = select_attend_fusable(dtype, D, Hq, Hs, L);
-  // unfused: the selection's workspace, then the attention's.  The selection part is at
-  // least the state region, so a buffer that also serves fused calls (longer rows) keeps
-  // that state when a short row takes this path.
-  size_t sel_ws = select_workspace((int)rows, L, 1, 0);
-  if (sel_ws < select_state_bytes((int)rows)) sel_ws = select_state_bytes((int)rows);
-  sel_ws = (sel_ws + 255) / 256 * 256;
-  const size_t need = fused ? select_attend_workspace((int)rows, Hq, Hs, L)
-                            : sel_ws + attn_workspace(dtype, B, Hq, Hs, D, 1, L, cap);
-  int rc;
-  if (workspace_phase(workspace, ws_bytes, need, &rc)) return rc;
-  if (!scores || !idx || !count || !q || !k_cache || !v_cache || !out) return BUTLER_ERR_INVALID_ARG;
-  if (!aligned16(scores) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(out))
-    return BUTLER_ERR_INVALID_ARG;
-  if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
+  SelectAttendArgs a{dtype, scores, radix_hist, budget_num, budget_den, n_sink, n_window,
+                     budget_excludes_forced, idx, count, q, k_cache, v_cache, out, B, Hq, Hkv,
+                     sel_group, D, L, L_cap, cap, softmax_scale};
+  SelectAttendPlan plan;
+  int rc = select_attend_plan(a, &plan);
+  if (rc != BUTLER_OK) return rc;
+  if (workspace_phase(workspace, ws_bytes, plan.need, &rc)) return rc;
+  rc = select_attend_check_pointers(a);
+  if (rc != BUTLER_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
-  if (fused)
-    return finish(s, launch_select_attend(s, scores, budget_num, budget_den, n_sink, n_window,
-                                          fo, idx, count, B, Hq, Hs, L, cap, radix_hist, q, k_cache,
-                                          v_cache, out, L_cap, softmax_scale, workspace, kvdiv));
-  hipError_t e = launch_select(s, scores, budget_num, budget_den, n_sink, n_window, fo, idx, nullptr,
-                               count, B, Hs, 1, L, cap, 0, 0, radix_hist, nullptr, workspace);
-  if (e != hipSuccess) return finish(s, e);
-  return finish(s, launch_attn_idx(s, dtype, q, k_cache, v_cache, idx, count, out, B, Hq, Hs, D,
-                                   1, L_cap, cap, softmax_scale, (char*)workspace + sel_ws,
-                                   kvdiv));
+  return finish(s, select_attend_launch(s, a, plan, workspace));
 }
 
 int butler_selection_cache(void* stream, int dtype, const void* q, void* q_ref, int32_t* keep,

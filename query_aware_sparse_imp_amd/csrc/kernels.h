@@ -69,6 +69,35 @@ hipError_t launch_select_attend(hipStream_t s, const float* scores, int num, int
                                 int Hq, int Hkv, int L, int cap, uint32_t* hist, const void* q,
                                 const void* k, const void* v, float* out, int L_cap,
                                 float scale, void* ws, int kvdiv);
+// Arguments of butler_select_attend, shared with its allocation-free variant.
+struct SelectAttendArgs {
+  int dtype;
+  const float* scores;
+  uint32_t* radix_hist;
+  int budget_num, budget_den, n_sink, n_window, budget_excludes_forced;
+  int32_t* idx;
+  int32_t* count;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  float* out;
+  int B, Hq, Hkv, sel_group, D, L, L_cap, cap;
+  float softmax_scale;
+};
+struct SelectAttendPlan {
+  int fo, Hs, kvdiv, rows;
+  bool fused;
+  size_t sel_ws;   // unfused: where the attention's part of the workspace starts
+  size_t need;     // workspace bytes
+};
+// Size checks (no pointer is looked at) and the workspace the call needs; a butler_status.
+int select_attend_plan(const SelectAttendArgs& a, SelectAttendPlan* plan);
+int select_attend_check_pointers(const SelectAttendArgs& a);
+hipError_t select_attend_launch(hipStream_t s, const SelectAttendArgs& a,
+                                const SelectAttendPlan& plan, void* ws);
+// The status of a finished launch sequence (BUTLER_DEBUG_SYNC=1 also synchronises).
+int finish_call(hipStream_t s, hipError_t e);
+
 hipError_t launch_selection_cache(hipStream_t s, int dtype, const void* q, void* q_ref,
                                   int32_t* keep, int B, int Hq, int Hkv, int D, float threshold);
 

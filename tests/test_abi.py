@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert qa.butler_abi_version() == 6
+    assert qa.butler_abi_version() == 7
     assert qa.butler_status_string(0) == "BUTLER_OK"
     assert qa.butler_status_string(-3) == "BUTLER_ERR_WORKSPACE"
     assert qa.butler_status_string(123) == "BUTLER_ERR_UNKNOWN"
@@ -235,3 +235,27 @@ def test_fetch_rows_validation():
     assert call(ptrs=P[:4] + [P[2], P[5]]) == INV               # k_sel aliases k_cache
     assert call() == INV                                        # memory unknown to HIP
     assert call(sg=1) == INV
+
+
+def test_select_attend_noalloc_validation_without_a_gpu():
+    """The allocation-free variant checks its arguments as butler_select_attend does, and
+    refuses a call whose workspace would not fit the library's fixed scratch array, before
+    it touches the HIP runtime (so these run without a GPU)."""
+    f = L.butler_select_attend_noalloc
+    P = [FAKE + 256 * i for i in range(7)]
+
+    def call(*, dtype=1, num=1, den=2, ptrs=P, B=1, Hq=32, Hkv=8, sg=0, D=128, Lr=32768,
+             L_cap=32768, cap=16452, scale=0.088):
+        return f(None, dtype, ptrs[0], None, num, den, 4, 64, 0, ptrs[1], ptrs[2], ptrs[3],
+                 ptrs[4], ptrs[5], ptrs[6], B, Hq, Hkv, sg, D, Lr, L_cap, cap, scale)
+    assert call(cap=16451) == INV
+    assert call(D=96) == UNS
+    assert call(ptrs=[P[0], None] + P[2:]) == INV
+    # the workspace butler_select_attend would ask for at this shape exceeds the array
+    big_L = 8388608
+    n = ctypes.c_size_t(0)
+    assert L.butler_select_attend(None, 1, P[0], None, 1, 16, 4, 128, 0, P[1], P[2], P[3], P[4],
+                                  P[5], P[6], 2, 32, 8, 0, 128, big_L, big_L, big_L, 0.088,
+                                  None, ctypes.byref(n)) == OK
+    assert n.value > (64 << 20)
+    assert call(B=2, num=1, den=16, Lr=big_L, L_cap=big_L, cap=big_L) == WSE
