@@ -559,18 +559,19 @@ def run_full_depth(steps, device):
     def add(group, *fs):
         fns.extend(fs)
         groups[group].extend(fs)
-    for l, d in enumerate(lay):
-        if l % w.G == 0:
+    from query_aware_sparse_imp_amd import control
+    for role, d in zip(control.layer_plan(w.layers, w.G), lay):
+        l = role.layer
+        if role.produces:
             add("produce", lambda d=d: qa.butler_produce_queries(d["h"], d["w1"], d["w2"], d["qimp"]))
-        if l == 0:   # dense layer: the budget takes every token
+        if role.dense:   # dense layer: the budget takes every token
             add("dense layer 0",
                 lambda d=d: qa.butler_project_keys(d["k"], d["wk"], d["kimp"], L - 1, 1),
                 lambda d=d: qa.butler_select_attend(scores, 1, 1, w.n_sink, w.n_window, cnt,
                                                     idx_dense, d["q"], d["k"], d["v"], out,
                                                     L=L, softmax_scale=w.scale))
             continue
-        prod = lay[w.G * (l // w.G)]
-        slot = (l - 1) % w.G
+        prod, slot = lay[role.producer], role.slot
         add("consumer layers",
             lambda d=d, prod=prod, slot=slot: qa.butler_project_and_score(
                 prod["qimp"], d["k"], d["wk"], d["kimp"], scores, Hkv=w.Hkv, L=L, slot=slot,
@@ -582,6 +583,7 @@ def run_full_depth(steps, device):
     sec = graph_time(fns, steps)
     phase = {name: graph_time(fs, 1) * 1e6 for name, fs in groups.items()}
     n_sel = int(cnt.sum())              # last consumer layer's selection
+
     elt = 2
     consumer = w.B * w.Hkv * (L * w.dprime * elt + n_sel // w.Hkv * (2 * w.D * elt + 8))
     dense = w.B * w.Hkv * L * 2 * w.D * elt
@@ -675,6 +677,9 @@ def main(argv=None) -> int:
                          "excluding sink and window, 2h a selected set per query head, "
                          "2o K/V cache in host memory (selected-row fetch against dense "
                          "offload), 3 soft-voting, 4 full depth, 5 prefill")
+    ap.add_argument("--skip-headline", action="store_true",
+                    help="profiling aid: run only the --configs workloads and print their "
+                         "results (no headline line)")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run a 256 MiB device copy first (HBM counter calibration)")
     a = ap.parse_args(argv)
@@ -698,13 +703,16 @@ def main(argv=None) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    log(f"[bench] {w.name}: L={L}, 8 replicas, steps={a.steps}, warmup={a.warmup}")
-    head, layers = run_config(w, L, 8, a.steps, a.warmup, dev)
-    host0 = layers[0]
-    log(f"[bench] headline: {json.dumps(head)}")
+    head = host0 = None
+    layers = []
+    if not a.skip_headline:
+        log(f"[bench] {w.name}: L={L}, 8 replicas, steps={a.steps}, warmup={a.warmup}")
+        head, layers = run_config(w, L, 8, a.steps, a.warmup, dev)
+        host0 = layers[0]
+        log(f"[bench] headline: {json.dumps(head)}")
 
     sweep = []
-    if not a.no_sweep:
+    if not a.no_sweep and not a.skip_headline:
         for Ls in (131072, 262144):
             for lay in layers:
                 if lay is not host0:
@@ -767,6 +775,9 @@ def main(argv=None) -> int:
             others["chunked_prefill"] = run_prefill(dev)
         log(f"[bench] workload {c}: {json.dumps(others)}")
 
+    if a.skip_headline:
+        print(json.dumps({"configs": others}), flush=True)
+        return 0
     cpu = cpu_all = None
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")

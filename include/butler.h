@@ -72,7 +72,7 @@ enum butler_score_mode { BUTLER_SCORE_RAW = 0, BUTLER_SCORE_SOFTVOTE = 1 };
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* butler_status_string(int status);
 
-/* ABI version, currently 7. */
+/* ABI version, currently 8. */
 int butler_abi_version(void);
 
 /*
@@ -186,6 +186,35 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
                              const void* w_k, void* kimp, float* scores, uint32_t* radix_hist,
                              const int32_t* keep, int B, int Hq, int Hkv, int sel_group, int G,
                              int slot, int L, int L_cap, int D, int dprime);
+
+/*
+ * butler_score_tokens -- raw scores of the tokens [t_begin, t_end) of single decode rows of
+ * length L, optionally with the appended key row projected in the same launch.  Model
+ * card, Method: a producer predicts the importance queries of itself and the next G - 1
+ * layers, so a consumer's scores of the tokens already cached depend only on its
+ * producer's Q_imp and on K_imp: they can be computed as soon as the producer has run,
+ * before the consumer layer's own input exists, and only the token that layer appends is
+ * left for its turn.  Scores and histogram counts are those of butler_score (RAW, Lq = 1,
+ * non-causal) for the same tokens; the other tokens of the rows are left as they were, so
+ * two calls over [0, L-1) and [L-1, L) give butler_score's or butler_project_and_score's
+ * result over [0, L).
+ *
+ *   q_imp      [B, Hq, G, 1, d']    dtype (read), slot `slot`
+ *   kimp       [B, Hkv, L_cap, d']  dtype: rows t_begin .. t_end-1 read
+ *   k_cache    [B, Hkv, L_cap, D]   dtype, w_k [D, d'] dtype: both NULL, or both given with
+ *                                   t_end == L, and row L - 1 of kimp is first projected
+ *                                   (written) as butler_project_and_score does
+ *   scores     [B, Hs, 1, L]        float32: entries t_begin .. t_end-1 of every row written
+ *   radix_hist, keep, sel_group     as in butler_score (single-row call): the counts of the
+ *                                   scored tokens are added
+ * 0 <= t_begin < t_end <= L; d' in {16, 32}; D in {64, 128} when projecting; R in
+ * {1, 2, 4, 8}; B * Hs <= 65535.  No workspace.
+ */
+int butler_score_tokens(void* stream, int dtype, const void* q_imp, void* kimp,
+                        const void* k_cache, const void* w_k, float* scores,
+                        uint32_t* radix_hist, const int32_t* keep, int B, int Hq, int Hkv,
+                        int sel_group, int G, int slot, int L, int L_cap, int D, int dprime,
+                        int t_begin, int t_end);
 
 /*
  * butler_select_topk -- fixed-budget top-x + sink + window, per selection head and query row.

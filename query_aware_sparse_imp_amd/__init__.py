@@ -19,6 +19,7 @@ import torch
 __all__ = [
     "BUTLER_OK", "BUTLER_SCORE_RAW", "BUTLER_SCORE_SOFTVOTE", "ButlerError", "lib", "LIB_PATH",
     "butler_project_keys", "butler_produce_queries", "butler_score", "butler_project_and_score",
+    "butler_score_tokens",
     "butler_select_topk",
     "butler_sparse_decode_attn", "butler_select_attend", "butler_select_attend_noalloc",
     "butler_selection_cache",
@@ -49,6 +50,7 @@ _SIGS = {
     "butler_produce_queries": ([_vp, _i, _vp, _vp, _vp, _vp] + [_i] * 7 + [_f, _vp, _sz], _i),
     "butler_score": ([_vp, _i, _i, _vp, _vp, _vp, _vp, _vp] + [_i] * 12 + [_f, _vp, _sz], _i),
     "butler_project_and_score": ([_vp, _i] + [_vp] * 7 + [_i] * 10, _i),
+    "butler_score_tokens": ([_vp, _i] + [_vp] * 7 + [_i] * 12, _i),
     "butler_select_topk": ([_vp, _vp, _vp, _vp] + [_i] * 5 + [_vp, _vp, _vp] + [_i] * 7 +
                            [_vp, _sz], _i),
     "butler_selection_cache": ([_vp, _i, _vp, _vp, _vp] + [_i] * 5 + [_f], _i),
@@ -274,6 +276,40 @@ def butler_project_and_score(q_imp: torch.Tensor, k_cache: torch.Tensor, w_k: to
         _stream(stream), _dtype_code(q_imp), _ptr(q_imp), _ptr(k_cache), _ptr(w_k), _ptr(kimp),
         _ptr(scores), _ptr(radix_hist), _ptr(keep), B, Hq, Hkv, sel_group, G, slot, L, L_cap, D,
         dp))
+
+
+def butler_score_tokens(q_imp: torch.Tensor, kimp: torch.Tensor, scores: torch.Tensor, *,
+                        Hkv: int, L: int, t_begin: int, t_end: int, slot: int = 0,
+                        k_cache: Optional[torch.Tensor] = None,
+                        w_k: Optional[torch.Tensor] = None,
+                        radix_hist: Optional[torch.Tensor] = None,
+                        keep: Optional[torch.Tensor] = None, sel_group: int = 0,
+                        stream=None) -> None:
+    """Raw scores of tokens [t_begin, t_end) of decode rows of length L (see butler.h);
+    with k_cache and w_k (t_end == L) row L - 1 of kimp is projected first.
+    q_imp [B, Hq, G, 1, d'], kimp [B, Hkv, L_cap, d'], scores [B, Hs, 1, L]."""
+    B, Hq, G, Lq, dp = q_imp.shape
+    Bk, Hk, L_cap, dp2 = kimp.shape
+    Hs = selection_heads(Hq, Hkv, sel_group)
+    if Lq != 1 or (Bk, Hk, dp2) != (B, Hkv, dp) or scores.shape != (B, Hs, 1, L):
+        raise ValueError("shape mismatch")
+    D = 0
+    if k_cache is not None or w_k is not None:
+        if k_cache is None or w_k is None:
+            raise ValueError("k_cache and w_k go together")
+        D = k_cache.shape[3]
+        if k_cache.shape != (B, Hkv, L_cap, D) or w_k.shape != (D, dp):
+            raise ValueError("shape mismatch")
+        if not (k_cache.dtype == w_k.dtype == kimp.dtype):
+            raise TypeError("dtype mismatch")
+    if q_imp.dtype != kimp.dtype or scores.dtype != torch.float32:
+        raise TypeError("dtype mismatch")
+    _check_hist(radix_hist, (B, Hs, 1))
+    _check_keep(keep, (B, Hs))
+    _check("butler_score_tokens", lib.butler_score_tokens(
+        _stream(stream), _dtype_code(q_imp), _ptr(q_imp), _ptr(kimp), _ptr(k_cache), _ptr(w_k),
+        _ptr(scores), _ptr(radix_hist), _ptr(keep), B, Hq, Hkv, sel_group, G, slot, L, L_cap, D,
+        dp, int(t_begin), int(t_end)))
 
 
 def butler_select_topk(scores: torch.Tensor, budget_num: int, budget_den: int, n_sink: int,

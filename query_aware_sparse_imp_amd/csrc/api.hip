@@ -162,7 +162,7 @@ const char* butler_status_string(int status) {
   }
 }
 
-int butler_abi_version(void) { return 7; }
+int butler_abi_version(void) { return 8; }
 
 int butler_project_keys(void* stream, int dtype, const void* k_cache, const void* w_k,
                         void* kimp, int B, int Hkv, int L_cap, int D, int dprime, int pos0,
@@ -264,7 +264,41 @@ int butler_project_and_score(void* stream, int dtype, const void* q_imp, const v
   if (kimp == k_cache || kimp == w_k) return BUTLER_ERR_INVALID_ARG;   // no aliasing
   hipStream_t s = (hipStream_t)stream;
   return finish(s, launch_project_score(s, dtype, q_imp, k_cache, w_k, kimp, scores, B, Hq, Hs,
-                                        G, slot, L, L_cap, D, dprime, radix_hist, keep, kvdiv));
+                                        G, slot, L, L_cap, D, dprime, radix_hist, keep, kvdiv,
+                                        0));
+}
+
+int butler_score_tokens(void* stream, int dtype, const void* q_imp, void* kimp,
+                        const void* k_cache, const void* w_k, float* scores,
+                        uint32_t* radix_hist, const int32_t* keep, int B, int Hq, int Hkv,
+                        int sel_group, int G, int slot, int L, int L_cap, int D, int dprime,
+                        int t_begin, int t_end) {
+  if (!valid_dtype(dtype)) return BUTLER_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || L_cap < L) return BUTLER_ERR_INVALID_ARG;
+  if (t_begin < 0 || t_end <= t_begin || t_end > L) return BUTLER_ERR_INVALID_ARG;
+  if (Hq % Hkv || G <= 0 || slot < 0 || slot >= G) return BUTLER_ERR_INVALID_ARG;
+  if (!pow2_group(Hq / Hkv)) return BUTLER_ERR_UNSUPPORTED;
+  int Hs, kvdiv;
+  if (!sel_heads(Hq, Hkv, sel_group, &Hs, &kvdiv)) return BUTLER_ERR_INVALID_ARG;
+  if (!(dprime == 16 || dprime == 32)) return BUTLER_ERR_UNSUPPORTED;
+  if ((long long)B * Hs > 65535) return BUTLER_ERR_UNSUPPORTED;
+  const bool project = k_cache != nullptr || w_k != nullptr;
+  if (project) {
+    if (!k_cache || !w_k || t_end != L) return BUTLER_ERR_INVALID_ARG;
+    if (!(D == 64 || D == 128)) return BUTLER_ERR_UNSUPPORTED;
+    if (!aligned16(k_cache) || !aligned16(w_k)) return BUTLER_ERR_INVALID_ARG;
+    if (kimp == k_cache || kimp == w_k) return BUTLER_ERR_INVALID_ARG;   // no aliasing
+  }
+  if (!q_imp || !kimp || !scores) return BUTLER_ERR_INVALID_ARG;
+  if (!aligned16(q_imp) || !aligned16(kimp) || !aligned16(scores)) return BUTLER_ERR_INVALID_ARG;
+  if (radix_hist && !aligned16(radix_hist)) return BUTLER_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (project)
+    return finish(s, launch_project_score(s, dtype, q_imp, k_cache, w_k, kimp, scores, B,
+                                          Hq, Hs, G, slot, L, L_cap, D, dprime, radix_hist, keep,
+                                          kvdiv, t_begin));
+  return finish(s, launch_score_tokens(s, dtype, q_imp, kimp, scores, B, Hq, Hs, G, slot, L,
+                                       L_cap, dprime, radix_hist, keep, kvdiv, t_begin, t_end));
 }
 
 int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,

@@ -3,8 +3,10 @@
     python query_aware_sparse_imp_amd/csrc/build.py [--jobs N]
 
 Every .hip file in this directory is compiled to an object under ``_build/`` at the
-repository root and linked into ``query_aware_sparse_imp_amd/libbutler.so``.  It
-always recompiles (a build is the "does it compile" check).
+repository root and linked into ``query_aware_sparse_imp_amd/libbutler.so``; the
+bandwidth-measurement kernels in ``measure/`` go into a library of their own,
+``query_aware_sparse_imp_amd/libbutler_measure.so``.  It always recompiles (a build is the
+"does it compile" check).
 """
 from __future__ import annotations
 
@@ -20,6 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libbutler.so")
+OUT_MEASURE = os.path.join(PKG, "libbutler_measure.so")
 BUILD = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -35,7 +38,9 @@ CFLAGS = [
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    sub = os.path.basename(os.path.dirname(src))
+    prefix = "" if os.path.dirname(src) == HERE else sub + "_"
+    obj = os.path.join(BUILD, prefix + os.path.basename(src)[:-4] + ".o")
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -43,19 +48,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(HERE, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, OUT)
+    shutil.move(tmp, out)
+
+
+def build(jobs: int = 8, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(HERE, "*.hip")))
+    msrcs = sorted(glob.glob(os.path.join(HERE, "measure", "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, srcs + msrcs))
+    _link(objs[:len(srcs)], OUT)
+    _link(objs[len(srcs):], OUT_MEASURE)
     if verbose:
-        print(f"built {OUT} from {len(srcs)} sources")
+        print(f"built {OUT} from {len(srcs)} sources and {OUT_MEASURE} from {len(msrcs)}")
     return OUT
 
 

@@ -28,7 +28,12 @@ hipError_t launch_project_score(hipStream_t s, int dtype, const void* q_imp,
                                 const void* k_cache, const void* w_k, void* kimp,
                                 float* scores, int B, int Hq, int Hkv, int G, int slot, int L,
                                 int L_cap, int D, int dp, uint32_t* hist, const int32_t* keep,
-                                int kvdiv);
+                                int kvdiv, int t_begin);
+// Raw scores of tokens [t_begin, t_end) of single decode rows of length L (row stride L).
+hipError_t launch_score_tokens(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
+                               float* scores, int B, int Hq, int Hkv, int G, int slot, int L,
+                               int L_cap, int dp, uint32_t* hist, const int32_t* keep,
+                               int kvdiv, int t_begin, int t_end);
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
                             int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist,

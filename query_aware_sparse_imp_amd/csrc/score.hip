@@ -64,21 +64,22 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
     const T* __restrict__ q_imp, const T* __restrict__ kimp, float* __restrict__ scores,
     int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal,
     int tpb, uint32_t* __restrict__ radix_hist, const int32_t* __restrict__ keep,
-    const T* __restrict__ k_cache, const T* __restrict__ w_k, T* kimp_w, int kvdiv) {
+    const T* __restrict__ k_cache, const T* __restrict__ w_k, T* kimp_w, int kvdiv,
+    int t_begin, int t_end) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPT = DP / EPL;           // lanes per token
   constexpr int TPI = kRawThreads / LPT;  // tokens per block-wide step
   constexpr int U = kRawUnroll;
   const int bg = blockIdx.z, i = blockIdx.y;
-  const bool proj = DA > 0 && blockIdx.x == gridDim.x - 1;   // holds token L - 1
+  const bool proj = DA > 0 && blockIdx.x == gridDim.x - 1;   // holds token L - 1 (t_end = L)
   const bool skip = keep && keep[bg];
   if (skip && !proj) return;   // the cached selection stands (single-row calls)
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int R = Hq / Hkv;
   const int part = threadIdx.x % LPT, sub = threadIdx.x / LPT;
   const int L_r = causal ? min(q_pos0 + i + 1, L) : L;
-  const int t0 = blockIdx.x * tpb;
-  const int t1 = min(t0 + tpb, L);
+  const int t0 = t_begin + blockIdx.x * tpb;   // this workgroup's tokens [t0, t1)
+  const int t1 = min(t0 + tpb, t_end);
   const int tv = min(t1, L_r);
   const int bk = bg / kvdiv;   // physical KV head
   const T* kb = kimp + (size_t)bk * L_cap * DP + part * EPL;
@@ -572,7 +573,10 @@ template <typename T, int DP, int DA = 0>
 hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scores, int B,
                  int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
                  int causal, uint32_t* hist, const int32_t* keep, int kvdiv,
-                 const void* k_cache = nullptr, const void* w_k = nullptr) {
+                 const void* k_cache = nullptr, const void* w_k = nullptr, int t_begin = 0,
+                 int t_end = -1) {
+  if (t_end < 0) t_end = L;
+  const int n = t_end - t_begin;   // tokens scored per row
   constexpr int LPT = DP / Vec16<T>::N;
   // a tile is what one block-wide step covers (kRawUnroll loads per thread); a workgroup
   // loops over enough tiles that a row has at most kRawRowWg workgroups -- this bounds the
@@ -581,15 +585,15 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
   // 4 tiles while the row has under 2 kRawRowWg of them (measured: 4 tiles per workgroup
   // beat 2 at 128K and 8 at 256K tokens)
   const int tile = (kRawThreads / LPT) * kRawUnroll;
-  const int tiles = (L + tile - 1) / tile;
+  const int tiles = (n + tile - 1) / tile;
   const int row_wg = tiles > 4 * kRawRowWg ? 2 * kRawRowWg : kRawRowWg;
   const int per = (tiles + row_wg - 1) / row_wg;
   const int tpb = tile * per;
-  dim3 grid((L + tpb - 1) / tpb, Lq, B * Hkv);
+  dim3 grid((n + tpb - 1) / tpb, Lq, B * Hkv);
   hipLaunchKernelGGL((score_raw_kernel<T, DP, DA>), grid, dim3(kRawThreads), 0, s,
                      (const T*)q_imp, (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap,
                      q_pos0, causal, tpb, hist, keep, (const T*)k_cache, (const T*)w_k,
-                     (T*)const_cast<void*>(kimp), kvdiv);
+                     (T*)const_cast<void*>(kimp), kvdiv, t_begin, t_end);
   return hipGetLastError();
 }
 
@@ -620,6 +624,23 @@ bool R_ok(int Hq, int Hkv) { return Hq % Hkv == 0 && Hq / Hkv <= 8; }
 
 }  // namespace
 
+hipError_t launch_score_tokens(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
+                               float* scores, int B, int Hq, int Hkv, int G, int slot, int L,
+                               int L_cap, int dp, uint32_t* hist, const int32_t* keep,
+                               int kvdiv, int t_begin, int t_end) {
+#define BUTLER_ST(T, DP)                                                                     \
+  if (dp == DP)                                                                            \
+    return raw_t<T, DP>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, 1, L, L_cap, 0, 0, hist, \
+                        keep, kvdiv, nullptr, nullptr, t_begin, t_end);
+  if (dtype == 1) {
+    BUTLER_ST(bf16_t, 32) BUTLER_ST(bf16_t, 16)
+  } else {
+    BUTLER_ST(float, 32) BUTLER_ST(float, 16)
+  }
+#undef BUTLER_ST
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_score_raw(hipStream_t s, int dtype, const void* q_imp, const void* kimp,
                             float* scores, int B, int Hq, int Hkv, int G, int slot, int Lq,
                             int L, int L_cap, int dp, int q_pos0, int causal, uint32_t* hist,
@@ -643,11 +664,11 @@ hipError_t launch_project_score(hipStream_t s, int dtype, const void* q_imp,
                                 const void* k_cache, const void* w_k, void* kimp,
                                 float* scores, int B, int Hq, int Hkv, int G, int slot, int L,
                                 int L_cap, int D, int dp, uint32_t* hist, const int32_t* keep,
-                                int kvdiv) {
+                                int kvdiv, int t_begin) {
 #define BUTLER_PS(T, DP, DD)                                                                 \
   if (dp == DP && D == DD)                                                                 \
     return raw_t<T, DP, DD>(s, q_imp, kimp, scores, B, Hq, Hkv, G, slot, 1, L, L_cap, 0, 0,  \
-                            hist, keep, kvdiv, k_cache, w_k);
+                            hist, keep, kvdiv, k_cache, w_k, t_begin, L);
   if (dtype == 1) {
     BUTLER_PS(bf16_t, 32, 128) BUTLER_PS(bf16_t, 16, 128) BUTLER_PS(bf16_t, 32, 64) BUTLER_PS(bf16_t, 16, 64)
   } else {

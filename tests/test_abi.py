@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert qa.butler_abi_version() == 7
+    assert qa.butler_abi_version() == 8
     assert qa.butler_status_string(0) == "BUTLER_OK"
     assert qa.butler_status_string(-3) == "BUTLER_ERR_WORKSPACE"
     assert qa.butler_status_string(123) == "BUTLER_ERR_UNKNOWN"
@@ -259,3 +259,20 @@ def test_select_attend_noalloc_validation_without_a_gpu():
                                   None, ctypes.byref(n)) == OK
     assert n.value > (64 << 20)
     assert call(B=2, num=1, den=16, Lr=big_L, L_cap=big_L, cap=big_L) == WSE
+
+
+def test_score_tokens_validation():
+    f = L.butler_score_tokens
+
+    def call(*, dtype=1, q=FAKE, kimp=FAKE + 256, k=None, wk=None, scores=FAKE + 512, B=1,
+             Hq=32, Hkv=8, sg=0, G=4, slot=1, Lr=1000, L_cap=1000, D=128, dp=32, tb=0, te=999):
+        return f(None, dtype, q, kimp, k, wk, scores, None, None, B, Hq, Hkv, sg, G, slot, Lr,
+                 L_cap, D, dp, tb, te)
+    assert call(tb=-1) == INV and call(te=0) == INV and call(te=1001) == INV
+    assert call(tb=5, te=5) == INV                                  # empty range
+    assert call(k=FAKE + 768) == INV                                # k_cache without w_k
+    assert call(k=FAKE + 768, wk=FAKE + 1024) == INV                # projecting needs t_end = L
+    assert call(k=FAKE + 768, wk=FAKE + 1024, te=1000, D=96) == UNS
+    assert call(k=FAKE, wk=FAKE + 1024, te=1000, kimp=FAKE) == INV  # kimp aliases k_cache
+    assert call(slot=4) == INV and call(dp=24) == UNS and call(Hq=24) == UNS
+    assert call(scores=MIS) == INV and call(q=None) == INV

@@ -320,3 +320,49 @@ def test_select_attend_workspace_shared_across_lengths():
         else:
             assert torch.equal(idx, ref[L][0]) and torch.equal(cnt, ref[L][1]), (n, L)
             assert torch.equal(out, ref[L][2]), (n, L)
+
+
+@pytest.mark.parametrize("cfg,L,sel_group", [(2, 5001, 0), (2, 300001, 0), (2, 32768, 1),
+                                             (1, 256, 0)])
+def test_score_tokens_split_equals_one_launch(cfg, L, sel_group):
+    """butler_score_tokens: the cached tokens [0, L-1) scored first without projection,
+    then the appended token with its K_imp row projected in the same launch, give bit for
+    bit what butler_project_and_score gives over [0, L): the K_imp row, every score, the
+    first-digit histogram.  A middle range [a, b) writes exactly entries a..b-1 (the
+    others keep a planted value) and adds exactly their counts."""
+    import query_aware_sparse_imp_amd as qa
+    w = synthetic.WORKLOADS[cfg]
+    print(f"[score tokens] cfg={cfg} L={L} sel_group={sel_group}", flush=True)
+    inp = to_device(synthetic.decode_layer(w, 4, L=L))
+    dev = "cuda"
+    k, wk, qi = inp["k_cache_d"], inp["w_k_d"], inp["q_imp_d"]
+    Hs = qa.selection_heads(w.Hq, w.Hkv, sel_group)
+    base = torch.zeros(w.B, w.Hkv, L, w.dprime, dtype=w.dtype, device=dev)
+    if L > 1:
+        qa.butler_project_keys(k, wk, base, 0, L - 1)
+    kimp_a, kimp_b = base.clone(), base.clone()
+    kimp_b[:, :, L - 1] = 5.0                                   # stale row, overwritten
+    sa = torch.empty(w.B, Hs, 1, L, dtype=torch.float32, device=dev)
+    sb = torch.full_like(sa, float("nan"))
+    ha = torch.zeros(w.B, Hs, 1, 2048, dtype=torch.int32, device=dev)
+    hb = torch.zeros_like(ha)
+    qa.butler_project_and_score(qi, k, wk, kimp_a, sa, Hkv=w.Hkv, L=L, radix_hist=ha,
+                                sel_group=sel_group)
+    qa.butler_score_tokens(qi, kimp_b, sb, Hkv=w.Hkv, L=L, t_begin=0, t_end=L - 1,
+                           radix_hist=hb, sel_group=sel_group)
+    qa.butler_score_tokens(qi, kimp_b, sb, Hkv=w.Hkv, L=L, t_begin=L - 1, t_end=L, k_cache=k,
+                           w_k=wk, radix_hist=hb, sel_group=sel_group)
+    torch.cuda.synchronize()
+    assert torch.equal(kimp_a, kimp_b)
+    assert torch.equal(sa, sb)
+    assert torch.equal(ha, hb) and int(hb.sum()) == w.B * Hs * L
+    # a middle range
+    a, b = L // 3, max(L // 3 + 1, (2 * L) // 3)
+    sc = torch.full_like(sa, -7.0)
+    hc = torch.zeros_like(ha)
+    qa.butler_score_tokens(qi, kimp_a, sc, Hkv=w.Hkv, L=L, t_begin=a, t_end=b, radix_hist=hc,
+                           sel_group=sel_group)
+    torch.cuda.synchronize()
+    assert torch.equal(sc[..., a:b], sa[..., a:b])
+    assert (sc[..., :a] == -7.0).all() and (sc[..., b:] == -7.0).all()
+    assert int(hc.sum()) == w.B * Hs * (b - a)
