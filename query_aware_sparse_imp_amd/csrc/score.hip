@@ -55,10 +55,11 @@ struct RawBatch {
 __device__ __forceinline__ bf16_t round_to(double v, bf16_t*) { return d2bf(v); }
 __device__ __forceinline__ float round_to(double v, float*) { return (float)v; }
 
-// DA > 0: the decode step's key row L - 1 (D = DA) is projected first, K_imp[L-1] =
-// K[L-1] . W_K, by the workgroup that holds token L - 1 -- with the summation order of
-// project_keys_kernel, so the row is the one butler_project_keys writes -- stored to
-// kimp_w, and scored from LDS.  Rows of kept (b, KV head) still get their K_imp row.
+// DA > 0: the decode step's key row L - 1 (D = DA) is projected, K_imp[L-1] =
+// K[L-1] . W_K, by one extra workgroup per row (the last in x) -- with the summation order
+// of project_keys_kernel, so the row is the one butler_project_keys writes -- stored to
+// kimp_w and scored from LDS, while the other workgroups stream tokens [t_begin, L - 1).
+// Rows of kept (b, KV head) still get their K_imp row.
 template <typename T, int DP, int DA>
 __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
     const T* __restrict__ q_imp, const T* __restrict__ kimp, float* __restrict__ scores,
@@ -71,15 +72,16 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   constexpr int TPI = kRawThreads / LPT;  // tokens per block-wide step
   constexpr int U = kRawUnroll;
   const int bg = blockIdx.z, i = blockIdx.y;
-  const bool proj = DA > 0 && blockIdx.x == gridDim.x - 1;   // holds token L - 1 (t_end = L)
+  const bool proj = DA > 0 && blockIdx.x == gridDim.x - 1;   // the appended token L - 1
   const bool skip = keep && keep[bg];
   if (skip && !proj) return;   // the cached selection stands (single-row calls)
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int R = Hq / Hkv;
   const int part = threadIdx.x % LPT, sub = threadIdx.x / LPT;
   const int L_r = causal ? min(q_pos0 + i + 1, L) : L;
-  const int t0 = t_begin + blockIdx.x * tpb;   // this workgroup's tokens [t0, t1)
-  const int t1 = min(t0 + tpb, t_end);
+  const int t_stream = DA > 0 ? L - 1 : t_end;   // the streaming workgroups' end
+  const int t0 = t_begin + blockIdx.x * tpb;     // this workgroup's tokens [t0, t1)
+  const int t1 = min(t0 + tpb, t_stream);
   const int tv = min(t1, L_r);
   const int bk = bg / kvdiv;   // physical KV head
   const T* kb = kimp + (size_t)bk * L_cap * DP + part * EPL;
@@ -94,52 +96,104 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   };
   __shared__ double qbar[DP];
   __shared__ uint32_t hist[2048];
-  constexpr int DW = DA > 0 ? DA : 1;
-  __shared__ float wsh[DW * DP];                  // W_K of the projection, as float
-  __shared__ float ksh[DW];                       // key row L - 1, as float
-  __shared__ __align__(16) T knew[DA > 0 ? DP : EPL];   // its K_imp row, storage type
-  if (proj) {
-    // W_K and the key row in 16-byte pieces, requested before anything else
-    constexpr int NPIECE = DW * DP / EPL;
-    constexpr int PER = (NPIECE + kRawThreads - 1) / kRawThreads;
-    float wv[PER][EPL], kv[EPL];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int pc = threadIdx.x + u * kRawThreads;
-      if (pc < NPIECE) Vec16<T>::load(w_k + pc * EPL, wv[u]);
-    }
-    const T* krow = k_cache + ((size_t)bk * L_cap + (L - 1)) * DW;
-    if (threadIdx.x < DW / EPL) Vec16<T>::load(krow + threadIdx.x * EPL, kv);
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int pc = threadIdx.x + u * kRawThreads;
-      if (pc < NPIECE) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) wsh[pc * EPL + e] = wv[u][e];
-      }
-    }
-    if (threadIdx.x < DW / EPL) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) ksh[threadIdx.x * EPL + e] = kv[e];
-    }
-    __syncthreads();
+  // the group's summed query: R <= 8 values loaded together, then summed in head order
+  auto sum_query = [&]() {
     if (threadIdx.x < DP) {
-      const int j = threadIdx.x;
-      double acc4[4] = {0.0, 0.0, 0.0, 0.0};
+      float qh[8];
 #pragma unroll
-      for (int c = 0; c < DW / EPL; ++c) {
+      for (int r = 0; r < 8; ++r)
+        qh[r] = (r < R) ? load_elem(q_imp + ((((size_t)b * Hq + g * R + min(r, R - 1)) * G + slot) *
+                                                 Lq + i) * DP + threadIdx.x)
+                        : 0.f;
+      double a = 0.0;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          acc4[c & 3] = fma((double)ksh[c * EPL + e], (double)wsh[(c * EPL + e) * DP + j],
-                            acc4[c & 3]);
-      }
-      const T r = round_to((acc4[0] + acc4[1]) + (acc4[2] + acc4[3]), (T*)nullptr);
-      // the first selection head of a KV head stores the row (the others compute the same)
-      if (bg == bk * kvdiv) kimp_w[((size_t)bk * L_cap + (L - 1)) * DP + j] = r;
-      knew[j] = r;
+      for (int r = 0; r < 8; ++r) a += (double)qh[r];
+      qbar[threadIdx.x] = a;
     }
-    __syncthreads();
-    if (skip) return;
+  };
+  // score of one token from its d' values kf (this lane's EPL of them), summed over the
+  // token's LPT lanes: the same arithmetic in the streaming and the appended-token paths
+  auto dot = [&](const float* kf, const double* qv) {
+    double acc = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = fma(qv[e], (double)kf[e], acc);
+    return quad_sum_d<LPT>(acc);
+  };
+  if constexpr (DA > 0) {
+    if (proj) {
+      constexpr int DW = DA;
+      __shared__ float wsh[DW * DP];                  // W_K of the projection, as float
+      __shared__ float ksh[DW];                       // key row L - 1, as float
+      __shared__ __align__(16) T knew[DP];            // its K_imp row, storage type
+      // W_K and the key row in 16-byte pieces, requested before anything else
+      constexpr int NPIECE = DW * DP / EPL;
+      constexpr int PER = (NPIECE + kRawThreads - 1) / kRawThreads;
+      float wv[PER][EPL], kv[EPL];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int pc = threadIdx.x + u * kRawThreads;
+        if (pc < NPIECE) Vec16<T>::load(w_k + pc * EPL, wv[u]);
+      }
+      const T* krow = k_cache + ((size_t)bk * L_cap + (L - 1)) * DW;
+      if (threadIdx.x < DW / EPL) Vec16<T>::load(krow + threadIdx.x * EPL, kv);
+      sum_query();
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int pc = threadIdx.x + u * kRawThreads;
+        if (pc < NPIECE) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) wsh[pc * EPL + e] = wv[u][e];
+        }
+      }
+      if (threadIdx.x < DW / EPL) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ksh[threadIdx.x * EPL + e] = kv[e];
+      }
+      __syncthreads();
+      // four lanes per output j, lane r keeping the chain of chunks c = r (mod 4): the
+      // four float64 partial sums of project_keys_kernel, combined in its order
+      if (threadIdx.x < 4 * DP) {
+        const int j = threadIdx.x >> 2, r = threadIdx.x & 3;
+        double acc = 0.0;
+#pragma unroll
+        for (int c = r; c < DW / EPL; c += 4) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            acc = fma((double)ksh[c * EPL + e], (double)wsh[(c * EPL + e) * DP + j], acc);
+        }
+        const int lo = __double2loint(acc), hi = __double2hiint(acc);
+        const double a1 = __hiloint2double(__shfl_xor(hi, 1), __shfl_xor(lo, 1));
+        const double s01 = (r & 1) ? a1 + acc : acc + a1;   // (acc0 + acc1), (acc2 + acc3)
+        const int lo2 = __double2loint(s01), hi2 = __double2hiint(s01);
+        const double s23 = __hiloint2double(__shfl_xor(hi2, 2), __shfl_xor(lo2, 2));
+        const double tot = (r & 2) ? s23 + s01 : s01 + s23;
+        if (r == 0) {
+          const T rv = round_to(tot, (T*)nullptr);
+          // the first selection head of a KV head stores the row (the others compute the same)
+          if (bg == bk * kvdiv) kimp_w[((size_t)bk * L_cap + (L - 1)) * DP + j] = rv;
+          knew[j] = rv;
+        }
+      }
+      __syncthreads();
+      if (skip || L - 1 < t_begin) return;
+      if (threadIdx.x < LPT) {
+        double qv[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[e] = qbar[part * EPL + e];
+        Raw16 r16;
+        r16.v = reinterpret_cast<const uint4*>(knew)[part];
+        float kf[EPL];
+        unpack16<T>(r16, kf);
+        const double acc = dot(kf, qv);
+        if (part == 0) {
+          const float sc = (L - 1 < L_r) ? (float)acc : neg_inf();
+          srow[L - 1] = sc;
+          if (radix_hist && L - 1 < L_r)
+            atomicAdd(&radix_hist[((size_t)bg * Lq + i) * 2048 + (score_key(sc) >> 21)], 1u);
+        }
+      }
+      return;
+    }
   }
   RawBatch<U> ba, bb;
   int t = t0 + sub;
@@ -148,19 +202,7 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   if (t + TPI * U < t1) load_batch(bb, t + TPI * U);
   if (radix_hist)
     for (int j = threadIdx.x; j < 2048; j += kRawThreads) hist[j] = 0u;
-  if (threadIdx.x < DP) {
-    // the group's R <= 8 values are loaded together, then summed in head order
-    float qh[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      qh[r] = (r < R) ? load_elem(q_imp + ((((size_t)b * Hq + g * R + min(r, R - 1)) * G + slot) *
-                                               Lq + i) * DP + threadIdx.x)
-                      : 0.f;
-    double a = 0.0;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) a += (double)qh[r];
-    qbar[threadIdx.x] = a;
-  }
+  sum_query();
   __syncthreads();
   double qv[EPL];
 #pragma unroll
@@ -171,13 +213,9 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
       const int tu = tb + u * TPI;
       Raw16 r16;
       r16.v = rb.v[u];
-      if (DA > 0 && proj && tu == L - 1) r16.v = reinterpret_cast<const uint4*>(knew)[part];
       float kf[EPL];
       unpack16<T>(r16, kf);
-      double acc = 0.0;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc = fma(qv[e], (double)kf[e], acc);
-      acc = quad_sum_d<LPT>(acc);
+      const double acc = dot(kf, qv);
       if (part == 0 && tu < t1) {
         const float sc = (tu < L_r) ? (float)acc : neg_inf();
         srow[tu] = sc;
@@ -576,7 +614,8 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
                  const void* k_cache = nullptr, const void* w_k = nullptr, int t_begin = 0,
                  int t_end = -1) {
   if (t_end < 0) t_end = L;
-  const int n = t_end - t_begin;   // tokens scored per row
+  // with the projection (DA > 0, t_end = L) the appended token gets a workgroup of its own
+  const int n = (DA > 0 ? t_end - 1 : t_end) - t_begin;   // tokens streamed per row
   constexpr int LPT = DP / Vec16<T>::N;
   // a tile is what one block-wide step covers (kRawUnroll loads per thread); a workgroup
   // loops over enough tiles that a row has at most kRawRowWg workgroups -- this bounds the
@@ -588,8 +627,9 @@ hipError_t raw_t(hipStream_t s, const void* q_imp, const void* kimp, float* scor
   const int tiles = (n + tile - 1) / tile;
   const int row_wg = tiles > 4 * kRawRowWg ? 2 * kRawRowWg : kRawRowWg;
   const int per = (tiles + row_wg - 1) / row_wg;
-  const int tpb = tile * per;
-  dim3 grid((n + tpb - 1) / tpb, Lq, B * Hkv);
+  const int tpb = tile * (per > 0 ? per : 1);
+  const int nstream = n > 0 ? (n + tpb - 1) / tpb : 0;   // none when only token L-1 is scored
+  dim3 grid(nstream + (DA > 0 ? 1 : 0), Lq, B * Hkv);
   hipLaunchKernelGGL((score_raw_kernel<T, DP, DA>), grid, dim3(kRawThreads), 0, s,
                      (const T*)q_imp, (const T*)kimp, scores, Hq, Hkv, G, slot, Lq, L, L_cap,
                      q_pos0, causal, tpb, hist, keep, (const T*)k_cache, (const T*)w_k,
