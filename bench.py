@@ -20,7 +20,9 @@ call (split kernel + merge kernel), the dominant one: it moves ~79% of a step's
 algorithmic bytes.
 
 Extra fields: the same step at L = 128K and 256K (2 replicas each), and the CPU oracle
-timed on a bounded sample of the same workload (one thread).  Inputs are seeded and
+timed on a bounded sample of the same workload (one thread).  Every HBM fraction is also
+given against this GPU's practical read ceiling, measured first with the repository's own
+stream kernel (libbutler_measure.so), as a secondary figure beside the 8 TB/s spec.  Inputs are seeded and
 synthetic; nothing is read from disk except profiles/traffic_*.json (rocprof counters
 recorded for the current kernel source, else traffic is null).
 """
@@ -255,6 +257,46 @@ def cpu_baseline(layer, budget_s: float = 12.0, threads: int = 1):
 # the other workloads: soft-voting batched decode, full-depth long-context decode,
 # chunked causal prefill (reported in "configs"; the headline stays the layer decode)
 # ---------------------------------------------------------------------------
+
+def stream_ceiling(device, gib: int = 1, reps: int = 10) -> dict:
+    """This GPU's practical HBM ceilings, measured with this repository's own stream
+    kernels (libbutler_measure.so): a read of every byte of a `gib` GiB buffer with
+    16-byte loads (4096 workgroups, 16 loads per lane in flight: the best shape of a
+    sweep), and a plain copy of the same size.  GB/s of bytes moved, best of `reps`."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "query_aware_sparse_imp_amd", "libbutler_measure.so")
+    lib = ctypes.CDLL(path)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.butler_measure_read.argtypes = [vp, vp, sz, vp, i, i]
+    lib.butler_measure_copy.argtypes = [vp, vp, vp, sz, i, i]
+    n = gib << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device=device)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4096, dtype=torch.int32, device=device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def best(f, nbytes):
+        if f() != 0:
+            raise RuntimeError("stream kernel launch failed")
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b) * 1e-3)
+        return nbytes / min(t) / 1e9
+    rd = best(lambda: lib.butler_measure_read(st, src.data_ptr(), n, sink.data_ptr(), 4096, 16), n)
+    cp = best(lambda: lib.butler_measure_copy(st, src.data_ptr(), dst.data_ptr(), n, 4096, 8),
+              2 * n)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"read_GBps": rd, "copy_GBps": cp, "bytes": n,
+            "kernels": "butler_measure_read / butler_measure_copy (16-byte loads)"}
+
 
 def graph_time(fns, reps):
     """Seconds per replay of a graph holding `reps` passes over `fns` (after one eager
@@ -703,6 +745,9 @@ def main(argv=None) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceiling = stream_ceiling(dev)
+    log(f"[bench] measured HBM ceilings: {json.dumps(ceiling)}")
+    rd_ceil = ceiling["read_GBps"]
     head = host0 = None
     layers = []
     if not a.skip_headline:
@@ -724,6 +769,7 @@ def main(argv=None) -> int:
             sweep.append({k: r[k] for k in ("L", "steps_per_s", "ms_per_step", "step_GBps",
                                             "call_GBps", "kernel_us", "timing")})
             sweep[-1]["step_frac_of_hbm_peak"] = r["step_GBps"] / HBM_PEAK_GBS
+            sweep[-1]["step_frac_of_measured_read_ceiling"] = r["step_GBps"] / rd_ceil
             log(f"[bench] sweep result: {json.dumps(sweep[-1])}")
         for lay in layers:
             lay.free()
@@ -768,9 +814,13 @@ def main(argv=None) -> int:
                 run_offload(w.replace(budget_den=16, n_window=128), 262144, dev, steps=4)]
         elif c == "3":
             others["softvote_decode"] = run_softvote(dev)
+            others["softvote_decode"]["frac_of_measured_read_ceiling"] = \
+                others["softvote_decode"]["GB/s"] / rd_ceil
             others["softvote_decode_selection_cache"] = run_softvote(dev, cache_threshold=0.98)
         elif c == "4":
             others["full_depth_decode"] = run_full_depth(max(a.steps // 40, 3), dev)
+            others["full_depth_decode"]["frac_of_measured_read_ceiling"] = \
+                others["full_depth_decode"]["GB/s"] / rd_ceil
         elif c == "5":
             others["chunked_prefill"] = run_prefill(dev)
         log(f"[bench] workload {c}: {json.dumps(others)}")
@@ -812,10 +862,14 @@ def main(argv=None) -> int:
                                "finishing pass attends to its chunk), attn_merge_kernel",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "measured_read_ceiling": rd_ceil,
+                     "frac_of_measured_read_ceiling": achieved / rd_ceil,
                      "algorithmic_bytes_per_launch": head["call_bytes"],
                      "avg_launch_us": call_us, "timing": head["timing"]},
         "step_hbm": {"algorithmic_bytes": head["step_bytes"], "GB/s": head["step_GBps"],
-                     "frac": head["step_GBps"] / HBM_PEAK_GBS},
+                     "frac": head["step_GBps"] / HBM_PEAK_GBS,
+                     "frac_of_measured_read_ceiling": head["step_GBps"] / rd_ceil},
+        "hbm_ceiling": ceiling,
         "kernel_us": head["kernel_us"],
         "step_us_spread": head["step_us_spread"],
         "sweep": sweep,
