@@ -152,6 +152,15 @@ template <> __device__ __forceinline__ void unpack16<bf16_t>(const Raw16& r, flo
     out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
   }
 }
+// Element e of 16 raw bytes as a float (e < 8 for bf16, e < 4 for float).
+template <typename T> __device__ __forceinline__ float elem16(const uint4& v, int e);
+template <> __device__ __forceinline__ float elem16<bf16_t>(const uint4& v, int e) {
+  const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+template <> __device__ __forceinline__ float elem16<float>(const uint4& v, int e) {
+  return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+}
 template <> __device__ __forceinline__ void unpack16<float>(const Raw16& r, float* out) {
   out[0] = __uint_as_float(r.v.x); out[1] = __uint_as_float(r.v.y);
   out[2] = __uint_as_float(r.v.z); out[3] = __uint_as_float(r.v.w);

@@ -56,7 +56,7 @@ __device__ __forceinline__ bf16_t round_to(double v, bf16_t*) { return d2bf(v); 
 __device__ __forceinline__ float round_to(double v, float*) { return (float)v; }
 
 // DA > 0: the decode step's key row L - 1 (D = DA) is projected, K_imp[L-1] =
-// K[L-1] . W_K, by one extra workgroup per row (the last in x) -- with the summation order
+// K[L-1] . W_K, by one extra workgroup per row (the first in x) -- with the summation order
 // of project_keys_kernel, so the row is the one butler_project_keys writes -- stored to
 // kimp_w and scored from LDS, while the other workgroups stream tokens [t_begin, L - 1).
 // Rows of kept (b, KV head) still get their K_imp row.
@@ -72,7 +72,8 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   constexpr int TPI = kRawThreads / LPT;  // tokens per block-wide step
   constexpr int U = kRawUnroll;
   const int bg = blockIdx.z, i = blockIdx.y;
-  const bool proj = DA > 0 && blockIdx.x == gridDim.x - 1;   // the appended token L - 1
+  // the appended token L - 1 has the first workgroup of the row (dispatched early)
+  const bool proj = DA > 0 && blockIdx.x == 0;
   const bool skip = keep && keep[bg];
   if (skip && !proj) return;   // the cached selection stands (single-row calls)
   const int b = bg / Hkv, g = bg - b * Hkv;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   const int part = threadIdx.x % LPT, sub = threadIdx.x / LPT;
   const int L_r = causal ? min(q_pos0 + i + 1, L) : L;
   const int t_stream = DA > 0 ? L - 1 : t_end;   // the streaming workgroups' end
-  const int t0 = t_begin + blockIdx.x * tpb;     // this workgroup's tokens [t0, t1)
+  const int t0 = t_begin + ((int)blockIdx.x - (DA > 0 ? 1 : 0)) * tpb;   // tokens [t0, t1)
   const int t1 = min(t0 + tpb, t_stream);
   const int tv = min(t1, L_r);
   const int bk = bg / kvdiv;   // physical KV head
@@ -96,18 +97,22 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   };
   __shared__ double qbar[DP];
   __shared__ uint32_t hist[2048];
-  // the group's summed query: R <= 8 values loaded together, then summed in head order
-  auto sum_query = [&]() {
-    if (threadIdx.x < DP) {
-      float qh[8];
+  // The group's summed query: its R <= 8 values (element threadIdx.x % DP of each head)
+  // are loaded together at clamped addresses -- no load behind a branch, which would make
+  // the compiler wait for every load in flight -- and summed in head order into LDS.
+  // Loads complete in issue order, so they are issued before the K_imp batches.
+  auto load_query = [&](float (&qh)[8]) {
+    const int d = threadIdx.x % DP;
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        qh[r] = (r < R) ? load_elem(q_imp + ((((size_t)b * Hq + g * R + min(r, R - 1)) * G + slot) *
-                                                 Lq + i) * DP + threadIdx.x)
-                        : 0.f;
+    for (int r = 0; r < 8; ++r)
+      qh[r] = load_elem(q_imp + ((((size_t)b * Hq + g * R + min(r, R - 1)) * G + slot) * Lq + i) *
+                                    DP + d);
+  };
+  auto sum_query = [&](const float (&qh)[8]) {
+    if (threadIdx.x < DP) {
       double a = 0.0;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) a += (double)qh[r];
+      for (int r = 0; r < 8; ++r) a += (r < R) ? (double)qh[r] : 0.0;
       qbar[threadIdx.x] = a;
     }
   };
@@ -122,29 +127,30 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
   if constexpr (DA > 0) {
     if (proj) {
       constexpr int DW = DA;
-      __shared__ float wsh[DW * DP];                  // W_K of the projection, as float
+      // W_K of the projection in its storage type: bf16 fits in the histogram's LDS, which
+      // this workgroup does not use, so the kernel's LDS stays that of the streaming ones
+      static_assert(sizeof(T) != 2 || DW * DP * 2 <= 2048 * 4, "W_K fits the histogram's LDS");
+      constexpr int WSH = sizeof(T) == 2 ? 1 : DW * DP;
+      __shared__ __align__(16) T wsh_own[WSH];
+      T* wsh = sizeof(T) == 2 ? reinterpret_cast<T*>(hist) : wsh_own;
       __shared__ float ksh[DW];                       // key row L - 1, as float
       __shared__ __align__(16) T knew[DP];            // its K_imp row, storage type
       // W_K and the key row in 16-byte pieces, requested before anything else
       constexpr int NPIECE = DW * DP / EPL;
       constexpr int PER = (NPIECE + kRawThreads - 1) / kRawThreads;
-      float wv[PER][EPL], kv[EPL];
+      // (the pieces go straight to LDS: a register array holding them would be placed in
+      // LDS by the compiler, doubling the kernel's LDS)
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         const int pc = threadIdx.x + u * kRawThreads;
-        if (pc < NPIECE) Vec16<T>::load(w_k + pc * EPL, wv[u]);
+        if (pc < NPIECE)
+          *reinterpret_cast<uint4*>(wsh + pc * EPL) = *reinterpret_cast<const uint4*>(w_k + pc * EPL);
       }
+      float kv[EPL], qh[8];
       const T* krow = k_cache + ((size_t)bk * L_cap + (L - 1)) * DW;
       if (threadIdx.x < DW / EPL) Vec16<T>::load(krow + threadIdx.x * EPL, kv);
-      sum_query();
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int pc = threadIdx.x + u * kRawThreads;
-        if (pc < NPIECE) {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) wsh[pc * EPL + e] = wv[u][e];
-        }
-      }
+      load_query(qh);
+      sum_query(qh);
       if (threadIdx.x < DW / EPL) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) ksh[threadIdx.x * EPL + e] = kv[e];
@@ -159,7 +165,8 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
         for (int c = r; c < DW / EPL; c += 4) {
 #pragma unroll
           for (int e = 0; e < EPL; ++e)
-            acc = fma((double)ksh[c * EPL + e], (double)wsh[(c * EPL + e) * DP + j], acc);
+            acc = fma((double)ksh[c * EPL + e], (double)load_elem(wsh + (c * EPL + e) * DP + j),
+                      acc);
         }
         const int lo = __double2loint(acc), hi = __double2hiint(acc);
         const double a1 = __hiloint2double(__shfl_xor(hi, 1), __shfl_xor(lo, 1));
@@ -196,43 +203,61 @@ __global__ __launch_bounds__(kRawThreads) void score_raw_kernel(
     }
   }
   RawBatch<U> ba, bb;
-  int t = t0 + sub;
-  // the first two batches of K_imp rows are requested before the group query is summed
-  if (t < t1) load_batch(ba, t);
-  if (t + TPI * U < t1) load_batch(bb, t + TPI * U);
+  const int t = t0 + sub;
+  constexpr int STEP = TPI * U;   // tokens of one batch
+  // batches of this workgroup: the same count for every lane
+  const int nb = t1 > t0 ? (t1 - t0 + STEP - 1) / STEP : 0;
+  // the query values first, then the first two batches of K_imp rows, all in flight while
+  // the group query is summed.  Every batch load is unconditional (past the end it reads
+  // the last token again, and consume() stores nothing for it), so the compiler counts
+  // the loads in flight exactly and each wait is for one batch only.
+  float qh[8];
+  load_query(qh);
+  load_batch(ba, t);
+  load_batch(bb, t + STEP);
   if (radix_hist)
     for (int j = threadIdx.x; j < 2048; j += kRawThreads) hist[j] = 0u;
-  sum_query();
+  sum_query(qh);
   __syncthreads();
   double qv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = qbar[part * EPL + e];
+  // The U tokens of a batch run as U independent chains -- each token's own sum in the
+  // order dot() takes (element e = 0, 1, ... then the lanes) -- interleaved so that the
+  // float64 latencies overlap; the stores and histogram counts come after all of them.
   auto consume = [&](const RawBatch<U>& rb, int tb) {
+    double acc[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tu = tb + u * TPI;
-      Raw16 r16;
-      r16.v = rb.v[u];
-      float kf[EPL];
-      unpack16<T>(r16, kf);
-      const double acc = dot(kf, qv);
-      if (part == 0 && tu < t1) {
-        const float sc = (tu < L_r) ? (float)acc : neg_inf();
-        srow[tu] = sc;
-        if (radix_hist && tu < L_r) atomicAdd(&hist[score_key(sc) >> 21], 1u);
+    for (int u = 0; u < U; ++u) acc[u] = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] = fma(qv[e], (double)elem16<T>(rb.v[u], e), acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = quad_sum_d<LPT>(acc[u]);
+    if (part == 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int tu = tb + u * TPI;
+        if (tu < t1) {
+          const float sc = (tu < L_r) ? (float)acc[u] : neg_inf();
+          srow[tu] = sc;
+          if (radix_hist && tu < L_r) atomicAdd(&hist[score_key(sc) >> 21], 1u);
+        }
       }
     }
   };
-  // two batches in flight: the one after next is requested before this one is consumed
-  while (t < t1) {
-    consume(ba, t);
-    t += TPI * U;
-    if (t + TPI * U < t1) load_batch(ba, t + TPI * U);
-    if (t >= t1) break;
-    consume(bb, t);
-    t += TPI * U;
-    if (t + TPI * U < t1) load_batch(bb, t + TPI * U);
+  // two batches in flight: the one after next is requested as soon as one is consumed
+  // (the last pair's requests may read past the end: the last token again, unused)
+  for (int pr = 0; pr < nb / 2; ++pr) {
+    const int tb = t + 2 * pr * STEP;
+    consume(ba, tb);
+    load_batch(ba, tb + 2 * STEP);
+    consume(bb, tb + STEP);
+    load_batch(bb, tb + 3 * STEP);
   }
+  if (nb & 1) consume(ba, t + (nb - 1) * STEP);
   if (radix_hist) {
     __syncthreads();
     uint32_t* gh = radix_hist + ((size_t)bg * Lq + i) * 2048;
