@@ -440,6 +440,12 @@ __global__ __launch_bounds__(kSvThreads) void softvote_logits_mfma_kernel(
   }
 }
 
+// Combine: 8 tokens per thread (2048 per workgroup), so the row's (max, sum) merge and the
+// histogram's set-up and flush are shared by more tokens; the block's logits are requested
+// first, at clamped addresses, all in flight together with the (max, sum) pairs.
+constexpr int kCbTpt = 8;
+constexpr int kCbTokens = kSvThreads * kCbTpt;
+
 template <int R>
 __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
     const float* __restrict__ logits, const float2* __restrict__ part,
@@ -447,6 +453,13 @@ __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
     const int32_t* __restrict__ keep) {
   const int bg = blockIdx.y, blk = blockIdx.x;
   if (keep && keep[bg]) return;
+  const float* zb = logits + (size_t)bg * R * L;
+  const int t0 = blk * kCbTokens + threadIdx.x;
+  float z[kCbTpt][R];
+#pragma unroll
+  for (int j = 0; j < kCbTpt; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) z[j][r] = zb[(size_t)r * L + min(t0 + kSvThreads * j, L - 1)];
   __shared__ float Ms[R], Ls[R];
   __shared__ uint32_t hist[2048];
   if (radix_hist)
@@ -487,14 +500,16 @@ __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
     }
   }
   __syncthreads();
-  const float* zb = logits + (size_t)bg * R * L;
-  const int t0 = blk * kSvTokensPerBlock;
-  for (int t = t0 + threadIdx.x; t < min(t0 + kSvTokensPerBlock, L); t += kSvThreads) {
+#pragma unroll
+  for (int j = 0; j < kCbTpt; ++j) {
+    const int t = t0 + kSvThreads * j;
     float s = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) s += fast_exp2(zb[(size_t)r * L + t] - Ms[r]) / Ls[r];
-    scores[(size_t)bg * L + t] = s;
-    if (radix_hist) atomicAdd(&hist[score_key(s) >> 21], 1u);
+    for (int r = 0; r < R; ++r) s += fast_exp2(z[j][r] - Ms[r]) / Ls[r];
+    if (t < L) {
+      scores[(size_t)bg * L + t] = s;
+      if (radix_hist) atomicAdd(&hist[score_key(s) >> 21], 1u);
+    }
   }
   if (radix_hist) {
     __syncthreads();
@@ -680,7 +695,8 @@ hipError_t sv_t(hipStream_t s, const void* q, const void* k, float* scores, int 
                        (const T*)q, (const T*)k, logits, part, Hq, Hkv, L, L_cap, scale_log2,
                        nblk, keep, kvdiv);
   }
-  hipLaunchKernelGGL((softvote_combine_kernel<R>), grid, dim3(kSvThreads), 0, s, logits, part,
+  const dim3 cgrid((L + kCbTokens - 1) / kCbTokens, B * Hkv);
+  hipLaunchKernelGGL((softvote_combine_kernel<R>), cgrid, dim3(kSvThreads), 0, s, logits, part,
                      scores, L, nblk, hist, keep);
   return hipGetLastError();
 }
