@@ -525,17 +525,25 @@ hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
 
 // ---------------------------------------------------------------------------
 // Prefill on the matrix cores (bf16, D = 128, R = 4): one workgroup per (b, KV head, 64
-// query rows), one wave per query head of the group and 32-row group.  Key tiles of 32 tokens run from 0
-// to the block's causal end; each tile is staged in LDS once for the four heads -- K as
-// [token][d], V transposed to [d][token] (two tokens packed per 32-bit word).
-//   S^T = K . Q^T        A = K rows (tokens), B = the wave's 32 queries (kept in VGPRs)
-//   O^T += V^T . P^T      A = V^T rows (d), B = P^T straight from the S^T accumulators
+// query rows), one wave per query head of the group and 32-row group.  Key tiles of 64
+// tokens run from 0 to the block's causal end; each tile is staged in LDS once for the
+// eight waves -- K as [token][d], V transposed to [d][token] (two tokens packed per 32-bit
+// word) -- into one of two buffers: the next tile's rows are requested before this tile's
+// products and written to the other buffer after them, so one barrier separates two tiles.
+//   S^T = K . Q^T        A = K rows (tokens), B = the wave's 32 queries (kept in VGPRs),
+//                        as two 32-token halves (two accumulator sets)
+//   O^T += V^T . P^T      A = V^T rows (d), B = P^T straight from the S^T accumulators,
+//                        four 16-token K steps
 // In the 32x32 accumulator layout lane l holds query l%32 and tokens 8(r/4) + 4(l/32) +
 // r%4: ordered by r, that is exactly the MFMA B operand of a 16-token K step if the K
 // order is permuted the same way on the V^T side (tokens {0-3, 8-11} for lanes 0-31,
 // {4-7, 12-15} for lanes 32-63: two 8-byte LDS reads).  The query is the lane in both
 // S^T and O^T, so the online softmax (max, rescale, sum) needs only the partner lane
-// l ^ 32.  Masking comes from the row's bitmask word of the tile.
+// l ^ 32.  Masking comes from the row's bitmask words of the tile.  The kernel is bound by
+// its vector work (the exponentials and the softmax around them), not by the matrix
+// cores: the logits are masked with one bitfield extract and one bit-select each, the
+// scale sits in the exponent's FMA, and the accumulators are rescaled only when some
+// query's max moved.
 // ---------------------------------------------------------------------------
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
@@ -543,14 +551,15 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 
 constexpr int kPfThreads = 256;
 constexpr int kPfKS = 128 + 8;   // LDS row stride (bf16) of the K tile
-constexpr int kPfVS = 32 + 4;    // LDS row stride (bf16) of the transposed V tile
 
-template <int RG>   // row groups of 32 queries per workgroup (one wave per head and group)
-__global__ __launch_bounds__(kPfThreads * RG) void attn_prefill_mfma_kernel(
+constexpr int kPfTok = 64;
+constexpr int kPfVS = kPfTok + 4;   // LDS row stride (bf16) of the transposed V tile
+
+__global__ __launch_bounds__(2 * kPfThreads) void attn_prefill_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const uint32_t* __restrict__ bitmask, float* __restrict__ out, int Hq, int Hkv, int Lq,
     int L, int L_cap, int q_pos0, float scale_log2) {
-  constexpr int D = 128, R = 4;
+  constexpr int D = 128, R = 4, RG = 2;
   const int nrb = (Lq + 32 * RG - 1) / (32 * RG);
   const int rb = blockIdx.x % nrb, bg = blockIdx.x / nrb;
   const int b = bg / Hkv, g = bg - b * Hkv;
@@ -561,7 +570,6 @@ __global__ __launch_bounds__(kPfThreads * RG) void attn_prefill_mfma_kernel(
   const int qi = min(i0 + ql, Lq - 1);
   const bool qvalid = i0 + ql < Lq;
   const int nwords = (L + 31) / 32;
-  // the wave's 32 queries as the B operand: lane l: query l%32, d = 16s + 8(l/32) .. +8
   bf16x8_t qf[8];
   {
     const bf16_t* qr = q + (((long long)b * Hq + h) * Lq + qi) * D + 8 * hi;
@@ -571,111 +579,142 @@ __global__ __launch_bounds__(kPfThreads * RG) void attn_prefill_mfma_kernel(
   const uint32_t* brow = bitmask + ((long long)bg * Lq + qi) * nwords;
   const bf16_t* kb = k + (long long)bg * L_cap * D;
   const bf16_t* vb = v + (long long)bg * L_cap * D;
-  // causal end of the block: its last row sees tokens < q_pos0 + last + 1
   const int t_end = min(L, q_pos0 + min(rb * 32 * RG + 32 * RG, Lq));
-  __shared__ __align__(16) bf16_t Ks[32 * kPfKS];
-  __shared__ __align__(16) bf16_t Vt[D * kPfVS];
-  // staging roles.  One row group: every thread stages K chunks c = tid, tid + 256 (token
-  // c/16, d 8*(c%16)) and a V token pair tp = tid/16 (tokens 2tp, 2tp+1) at d group
-  // dg = tid%16.  Two row groups: the first 256 threads stage V, the others K.
-  const int kt = (RG == 2) ? tid - kPfThreads : tid;
-  const bool do_k = (RG == 1) || tid >= kPfThreads;
-  const bool do_v = (RG == 1) || tid < kPfThreads;
-  const int kc0 = max(kt, 0), kc1 = max(kt, 0) + kPfThreads;
-  const int tp = (tid & (kPfThreads - 1)) >> 4, dg = tid & 15;
-  uint4 rk0, rk1, rv0, rv1;
-  uint32_t wd_next;
+  __shared__ __align__(16) bf16_t Ks[2][kPfTok * kPfKS];
+  __shared__ __align__(16) bf16_t Vt[2][D * kPfVS];
+  // staging roles: threads 256.. stage K (chunks c = kt + 256u: token c/16, d 8*(c%16)),
+  // threads ..255 stage V token pairs tp = (tid + 256u) / 16 at d group dg = tid % 16
+  const bool do_k = tid >= kPfThreads;
+  const int kt = do_k ? tid - kPfThreads : tid;
+  const int dg = tid & 15;
+  uint4 rs[4];        // K: 4 chunks; V: 2 pairs x 2 tokens
+  uint32_t wn0, wn1;  // bitmask words of the tile in flight
   auto gload = [&](int t0) {
     if (do_k) {
-      const int a0 = min(t0 + (kc0 >> 4), L - 1), a1 = min(t0 + (kc1 >> 4), L - 1);
-      rk0 = *reinterpret_cast<const uint4*>(kb + (long long)a0 * D + (kc0 & 15) * 8);
-      rk1 = *reinterpret_cast<const uint4*>(kb + (long long)a1 * D + (kc1 & 15) * 8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = kt + kPfThreads * u;
+        rs[u] = *reinterpret_cast<const uint4*>(kb + (long long)min(t0 + (c >> 4), L - 1) * D + (c & 15) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tp = (tid + kPfThreads * u) >> 4;
+        rs[2 * u] = *reinterpret_cast<const uint4*>(vb + (long long)min(t0 + 2 * tp, L - 1) * D + dg * 8);
+        rs[2 * u + 1] = *reinterpret_cast<const uint4*>(vb + (long long)min(t0 + 2 * tp + 1, L - 1) * D + dg * 8);
+      }
     }
-    if (do_v) {
-      const int v0 = min(t0 + 2 * tp, L - 1), v1 = min(t0 + 2 * tp + 1, L - 1);
-      rv0 = *reinterpret_cast<const uint4*>(vb + (long long)v0 * D + dg * 8);
-      rv1 = *reinterpret_cast<const uint4*>(vb + (long long)v1 * D + dg * 8);
-    }
-    wd_next = brow[min(t0 >> 5, nwords - 1)];
+    const int w0 = t0 >> 5;
+    wn0 = brow[min(w0, nwords - 1)];
+    const uint32_t w1 = brow[min(w0 + 1, nwords - 1)];
+    wn1 = (w0 + 1 < nwords) ? w1 : 0u;   // past the last word: no tokens
   };
-  float m = neg_inf(), l = 0.f;
+  auto stage = [&](int buf) {
+    if (do_k) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = kt + kPfThreads * u;
+        *reinterpret_cast<uint4*>(&Ks[buf][(c >> 4) * kPfKS + (c & 15) * 8]) = rs[u];
+      }
+    } else {
+      uint32_t* vw = reinterpret_cast<uint32_t*>(Vt[buf]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tp = (tid + kPfThreads * u) >> 4;
+        const uint32_t x0[4] = {rs[2 * u].x, rs[2 * u].y, rs[2 * u].z, rs[2 * u].w};
+        const uint32_t x1[4] = {rs[2 * u + 1].x, rs[2 * u + 1].y, rs[2 * u + 1].z, rs[2 * u + 1].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vw[(8 * dg + 2 * j) * (kPfVS / 2) + tp] = (x0[j] & 0xffffu) | (x1[j] << 16);
+          vw[(8 * dg + 2 * j + 1) * (kPfVS / 2) + tp] = (x0[j] >> 16) | (x1[j] & 0xffff0000u);
+        }
+      }
+    }
+  };
+  float m = neg_inf(), msc = 0.f, l = 0.f;
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   gload(0);
-  for (int t0 = 0; t0 < t_end; t0 += 32) {
-    const uint32_t wd = qvalid ? wd_next : 0u;
-    __syncthreads();   // the previous tile's readers are done
-    if (do_k) {
-      *reinterpret_cast<uint4*>(&Ks[(kc0 >> 4) * kPfKS + (kc0 & 15) * 8]) = rk0;
-      *reinterpret_cast<uint4*>(&Ks[(kc1 >> 4) * kPfKS + (kc1 & 15) * 8]) = rk1;
-    }
-    if (do_v) {
-      uint32_t* vw = reinterpret_cast<uint32_t*>(Vt);
-      const uint32_t x0[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
-      const uint32_t x1[4] = {rv1.x, rv1.y, rv1.z, rv1.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vw[(8 * dg + 2 * j) * (kPfVS / 2) + tp] = (x0[j] & 0xffffu) | (x1[j] << 16);
-        vw[(8 * dg + 2 * j + 1) * (kPfVS / 2) + tp] = (x0[j] >> 16) | (x1[j] & 0xffff0000u);
-      }
-    }
-    __syncthreads();
-    gload(min(t0 + 32, t_end - 1));   // next tile in flight during this one
-    // S^T tile: 32 tokens x 32 queries
-    f32x16_t c;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) c[r] = 0.f;
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[ql * kPfKS + 16 * s8 + 8 * hi]);
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s8], c, 0, 0, 0);
-    }
-    // mask, online softmax of query ql (partner lane l ^ 32 holds the other 16 tokens)
-    float z[16], mt = neg_inf();
+  stage(0);
+  __syncthreads();
+  int cur = 0;
+  for (int t0 = 0; t0 < t_end; t0 += kPfTok) {
+    const uint32_t wd0 = qvalid ? wn0 : 0u, wd1 = qvalid ? wn1 : 0u;
+    gload(t0 + kPfTok);   // the next tile (clamped addresses; unused past the end)
+    const bf16_t* Kc = Ks[cur];
+    f32x16_t c0, c1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int tt = 8 * (r >> 2) + 4 * hi + (r & 3);
-      z[r] = ((wd >> tt) & 1u) ? c[r] * scale_log2 : neg_inf();
-      mt = fmaxf(mt, z[r]);
+      c0[r] = 0.f;
+      c1[r] = 0.f;
+    }
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(&Kc[ql * kPfKS + 16 * s8 + 8 * hi]);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(&Kc[(32 + ql) * kPfKS + 16 * s8 + 8 * hi]);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s8], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s8], c1, 0, 0, 0);
+    }
+    // Raw logits of the selected tokens, -inf elsewhere: the token's bitmask bit,
+    // sign-extended into a 32-bit lane mask, picks between the logit and -inf.  The
+    // running max is kept raw (m) and scaled (msc); the scale goes into the exponent's FMA.
+    const uint32_t w0 = wd0 >> (4 * hi), w1 = wd1 >> (4 * hi);
+    float z[32], mt = neg_inf();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tt = 8 * (r >> 2) + (r & 3);
+      const uint32_t k0 = (uint32_t)((int)(w0 << (31 - tt)) >> 31);
+      const uint32_t k1 = (uint32_t)((int)(w1 << (31 - tt)) >> 31);
+      z[r] = __uint_as_float((__float_as_uint(c0[r]) & k0) | (0xff800000u & ~k0));
+      z[16 + r] = __uint_as_float((__float_as_uint(c1[r]) & k1) | (0xff800000u & ~k1));
+      mt = fmaxf(mt, fmaxf(z[r], z[16 + r]));
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float mn = fmaxf(m, mt);
-    const float alpha = (mn == neg_inf()) ? 1.f : fast_exp2(m - mn);
-    float pr[16], ps = 0.f;
+    const float ms = (mn == neg_inf()) ? 0.f : mn * scale_log2;
+    // nothing accumulated while m is -inf; an unchanged max rescales by exactly 1
+    const float alpha = (m == neg_inf()) ? 0.f : fast_exp2(msc - ms);
+    float pr[32], ps = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pr[r] = (z[r] == neg_inf()) ? 0.f : fast_exp2(z[r] - mn);
+    for (int r = 0; r < 32; ++r) {
+      pr[r] = fast_exp2(fmaf(z[r], scale_log2, -ms));   // exp2(-inf) = 0
       ps += pr[r];
     }
     ps += __shfl_xor(ps, 32);
     l = l * alpha + ps;
     m = mn;
+    msc = ms;
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    // P^T as the B operand of the two 16-token K steps
-    bf16x8_t pb[2];
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    bf16x8_t pb[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)pr[8 * ks + e];
+    const bf16_t* Vc = Vt[cur];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const bf16_t* vrow = &Vt[(db * 32 + ql) * kPfVS];
+      const bf16_t* vrow = &Vc[(db * 32 + ql) * kPfVS];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 4; ++ks) {
         const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * ks + 4 * hi);
         const bf16x4_t hi4 = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * ks + 8 + 4 * hi);
         const bf16x8_t a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[db], 0, 0, 0);
       }
     }
+    // the other buffer was last read before the previous barrier
+    stage(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
   }
-  // O^T: lane l holds query ql, d = 32 db + 8(r/4) + 4(l/32) + r%4
   if (qvalid) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     float* orow = out + (((long long)b * Hq + h) * Lq + i0 + ql) * D;
@@ -702,7 +741,7 @@ hipError_t bm_t(hipStream_t s, const void* q, const void* k, const void* v,
     if (Lq >= 32 && kvdiv == 1) {
       // 64 query rows per workgroup: each staged K/V tile serves eight waves
       const long long blocks = (long long)B * Hkv * ((Lq + 63) / 64);
-      hipLaunchKernelGGL(attn_prefill_mfma_kernel<2>, dim3((unsigned)blocks),
+      hipLaunchKernelGGL(attn_prefill_mfma_kernel, dim3((unsigned)blocks),
                          dim3(2 * kPfThreads), 0, s, (const bf16_t*)q, (const bf16_t*)k,
                          (const bf16_t*)v, bitmask, out, Hq, Hkv, Lq, L, L_cap, q_pos0,
                          scale * 1.4426950408889634f);
