@@ -1232,15 +1232,25 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
     }
     return hipGetLastError();
   }
-  // one workgroup per row, sized to the row: 16 or 32 keys per thread, 64 to 1024 threads
+  // one workgroup per row, sized to the row: 64 to 1024 threads, and keys per thread in
+  // steps that keep the slots past the row's end (idle work) to a quarter or less
 #define BUTLER_SR(NT, KPT)                                                                 \
   hipLaunchKernelGGL((select_row_kernel<NT, KPT>), dim3((unsigned)rows), dim3(NT), 0, s,   \
                      scores, num, den, n_sink, n_window, idx, bitmask, count, Lq, L, cap,   \
                      q_pos0, causal, hist, keep, fo)
-  if (L <= 1024) BUTLER_SR(64, 16);
+  if (L <= 256) BUTLER_SR(64, 4);
+  else if (L <= 512) BUTLER_SR(64, 8);
+  else if (L <= 768) BUTLER_SR(64, 12);
+  else if (L <= 1024) BUTLER_SR(64, 16);
+  else if (L <= 1536) BUTLER_SR(128, 12);
   else if (L <= 2048) BUTLER_SR(128, 16);
+  else if (L <= 3072) BUTLER_SR(256, 12);
   else if (L <= 4096) BUTLER_SR(256, 16);
-  else if (L <= 8192) BUTLER_SR(512, 16);   // 512 x 16 measured faster than 256 x 32 and 1024 x 8
+  // 512 threads: x 16 measured faster than 256 x 32 and 1024 x 8
+  else if (L <= 5120) BUTLER_SR(512, 10);
+  else if (L <= 6144) BUTLER_SR(512, 12);
+  else if (L <= 7168) BUTLER_SR(512, 14);
+  else if (L <= 8192) BUTLER_SR(512, 16);
   else if (L <= 16384) BUTLER_SR(512, 32);
   else if (L <= 32768) BUTLER_SR(1024, 32);
   else BUTLER_SR(1024, 64);

@@ -70,7 +70,8 @@ def _run(scores_np, num, den, ns, nw, causal=False, q_pos0=0, fo=False):
 def test_select_rows_match_oracle(kind):
     rng = np.random.default_rng({"normal": 1, "ties": 2, "special": 3, "equal": 4}[kind])
     cases = [(1, 1, 2, 0, 0), (2, 1, 2, 1, 1), (31, 1, 2, 4, 16), (32, 3, 10, 4, 64),
-             (33, 1, 16, 4, 128), (100, 0, 1, 3, 5), (257, 1, 1, 4, 16), (1000, 5, 4, 0, 0),
+             (33, 1, 16, 4, 128), (100, 0, 1, 3, 5), (257, 1, 1, 4, 16), (700, 1, 2, 4, 64),
+             (1000, 5, 4, 0, 0), (1500, 1, 16, 4, 128), (2500, 1, 2, 4, 64),
              (4096, 1, 1, 4, 64), (4097, 1, 2, 4, 64), (8192, 0, 1, 4, 64),
              (12000, 5, 4, 4, 64), (20011, 1, 16, 4, 128), (40000, 3, 10, 4, 64),
              (100003, 1, 2, 0, 0),
@@ -84,10 +85,11 @@ def test_select_rows_match_oracle(kind):
 
 def test_select_causal_rows():
     rng = np.random.default_rng(5)
-    # row lengths in every per-row workgroup shape: up to 1024, 8192, 16384, 32768, 65536
-    for (Lq, q_pos0, L) in ((37, 100, 137), (64, 0, 64), (129, 1000, 1129), (64, 6000, 6064),
-                            (33, 8159, 8192), (9, 16000, 16009), (5, 30000, 30005),
-                            (3, 65533, 65536)):
+    # row lengths in every per-row workgroup shape: 64 to 1024 threads, 4 to 64 keys each
+    for (Lq, q_pos0, L) in ((37, 100, 137), (64, 0, 64), (40, 500, 540), (129, 1000, 1129),
+                            (70, 2000, 2070), (40, 4500, 4540), (64, 6000, 6064),
+                            (30, 7000, 7030), (33, 8159, 8192), (9, 16000, 16009),
+                            (5, 30000, 30005), (3, 65533, 65536)):
         print(f"[select-causal] Lq={Lq} q_pos0={q_pos0} L={L}", flush=True)
         _run(_scores(rng, (2, 2, Lq, L), "ties"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0)
         _run(_scores(rng, (1, 2, Lq, L), "normal"), 1, 2, 4, 64, causal=True, q_pos0=q_pos0)
