@@ -533,8 +533,9 @@ __global__ __launch_bounds__(kSvThreads) void softvote_combine_kernel(
 // so that lane group g4 = l/16 feeds d' = KG*g4 + s at step s (KG = d'/4): each lane then
 // reads KG consecutive K_imp elements of its token with one load.
 // A workgroup holds 64 query rows (qbar in VGPRs, 16 x 16 tiles of 4 x 4 per wave) and
-// its 4 waves sweep 1024 tokens, 64 per wave step; tiles past every row's causal end are
-// written as -inf without arithmetic.
+// its 4 waves sweep 1024 tokens, 64 per wave step, each step's K_imp rows requested
+// before the previous step's products; tiles past every row's causal end are written as
+// -inf without arithmetic.
 
 constexpr int kCsThreads = 256;
 constexpr int kCsRows = 64;
@@ -543,7 +544,7 @@ constexpr int kCsTokBlk = 1024;
 typedef __attribute__((ext_vector_type(4))) double f64x4_t;
 
 template <int DP>
-__global__ __launch_bounds__(kCsThreads) void score_rows_mfma_kernel(
+__global__ __launch_bounds__(kCsThreads, 2) void score_rows_mfma_kernel(
     const bf16_t* __restrict__ q_imp, const bf16_t* __restrict__ kimp, float* __restrict__ scores,
     int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal,
     int kvdiv) {
@@ -585,42 +586,49 @@ __global__ __launch_bounds__(kCsThreads) void score_rows_mfma_kernel(
   float* srow0 = scores + ((long long)bg * Lq) * L;
   const int i_last = min(i0 + kCsRows, Lq) - 1;
   const int t_vis = causal ? min(L, q_pos0 + i_last + 1) : L;   // tokens any row sees
-  for (int it = 0; it < kCsTokBlk / (64 * 4); ++it) {
-    const int t0 = blockIdx.x * kCsTokBlk + (it * 4 + wid) * 64;
-    if (t0 >= L) break;
-    const bool live = t0 < t_vis;
-    f64x4_t acc[4][4];
+  // the wave's K_imp rows of a 64-token step, at clamped addresses
+  auto load_k = [&](float (&kv)[4][KG], int t0) {
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[qb][tb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-    if (live) {
-      float kv[4][KG];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const bf16_t* src = kb + (long long)min(t0 + 16 * tb + ql, L - 1) * DP;
-        if constexpr (KG == 8) {
-          Vec16<bf16_t>::load(src, kv[tb]);
-        } else {
-          const uint2 raw = *reinterpret_cast<const uint2*>(src);
-          kv[tb][0] = bf2f((bf16_t)(raw.x & 0xffffu));
-          kv[tb][1] = bf2f((bf16_t)(raw.x >> 16));
-          kv[tb][2] = bf2f((bf16_t)(raw.y & 0xffffu));
-          kv[tb][3] = bf2f((bf16_t)(raw.y >> 16));
-        }
+    for (int tb = 0; tb < 4; ++tb) {
+      const bf16_t* src = kb + (long long)min(t0 + 16 * tb + ql, L - 1) * DP;
+      if constexpr (KG == 8) {
+        Vec16<bf16_t>::load(src, kv[tb]);
+      } else {
+        const uint2 raw = *reinterpret_cast<const uint2*>(src);
+        kv[tb][0] = bf2f((bf16_t)(raw.x & 0xffffu));
+        kv[tb][1] = bf2f((bf16_t)(raw.x >> 16));
+        kv[tb][2] = bf2f((bf16_t)(raw.y & 0xffffu));
+        kv[tb][3] = bf2f((bf16_t)(raw.y >> 16));
       }
+    }
+  };
+  constexpr int kSteps = kCsTokBlk / (64 * 4);
+  const int tw = blockIdx.x * kCsTokBlk + wid * 64;   // this wave's first token
+  float kv[4][KG];
+  load_k(kv, tw);
+  for (int it = 0; it < kSteps; ++it) {
+    const int t0 = tw + it * 256;
+    if (t0 >= L) break;
+    // the next step's rows are requested before this step's products and stores
+    float kn[4][KG];
+    load_k(kn, min(t0 + 256, L - 1));
+    const bool live = t0 < t_vis;
+    // one 16-row block at a time (4 accumulator tiles live, not 16: two waves per SIMD),
+    // its four token tiles as independent chains; accumulator r of tile tb: row
+    // i0 + 16qb + 4r + g4, token t0 + 16tb + ql
 #pragma unroll
-      for (int s8 = 0; s8 < KG; ++s8)
+    for (int qb = 0; qb < 4; ++qb) {
+      f64x4_t acc[4];
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
+      for (int tb = 0; tb < 4; ++tb) acc[tb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+      if (live) {
+#pragma unroll
+        for (int s8 = 0; s8 < KG; ++s8)
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb)
-            acc[qb][tb] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[qb][s8], (double)kv[tb][s8],
-                                                               acc[qb][tb], 0, 0, 0);
-    }
-    // accumulator r of tile (qb, tb): row i0 + 16qb + 4r + g4, token t0 + 16tb + ql
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+            acc[tb] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[qb][s8], (double)kv[tb][s8],
+                                                           acc[tb], 0, 0, 0);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + 16 * qb + 4 * r + g4;
@@ -630,9 +638,14 @@ __global__ __launch_bounds__(kCsThreads) void score_rows_mfma_kernel(
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
           const int t = t0 + 16 * tb + ql;
-          if (t < L) srow[t] = (t < lim) ? (float)acc[qb][tb][r] : neg_inf();
+          if (t < L) srow[t] = (t < lim) ? (float)acc[tb][r] : neg_inf();
         }
       }
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int e = 0; e < KG; ++e) kv[tb][e] = kn[tb][e];
   }
 }
 
