@@ -675,7 +675,6 @@ def run_prefill(device):
     qimp = [torch.empty(w.B, w.Hq, w.G, C, w.dprime, dtype=dt, device=device) for _ in range(nc)]
     scores = [torch.empty(w.B, w.Hkv, C, (c + 1) * C, dtype=torch.float32, device=device)
               for c in range(nc)]
-    hist = [torch.zeros(w.B, w.Hkv, C, 2048, dtype=torch.int32, device=device) for _ in range(nc)]
     bms = [torch.empty(w.B, w.Hkv, C, ((c + 1) * C + 31) // 32, dtype=torch.int32, device=device)
            for c in range(nc)]
     cnt = torch.empty(w.B, w.Hkv, C, dtype=torch.int32, device=device)
@@ -687,10 +686,9 @@ def run_prefill(device):
         groups["project"].append(lambda c0=c0: qa.butler_project_keys(k, wk, kimp, c0, C))
         groups["score+select"].append(lambda c=c, c0=c0, Lc=Lc: (
             qa.butler_score(qa.BUTLER_SCORE_RAW, qimp[c], kimp, scores[c], Hkv=w.Hkv, L=Lc,
-                            slot=0, q_pos0=c0, causal=True, radix_hist=hist[c]),
+                            slot=0, q_pos0=c0, causal=True),
             qa.butler_select_topk(scores[c], w.budget_num, w.budget_den, w.n_sink, w.n_window,
-                                  cnt, bitmask=bms[c], q_pos0=c0, causal=True,
-                                  radix_hist=hist[c])))
+                                  cnt, bitmask=bms[c], q_pos0=c0, causal=True)))
         groups["attn"].append(lambda c=c, c0=c0, Lc=Lc: qa.butler_sparse_decode_attn(
             Qc[c], k, v, outs[c], L=Lc, bitmask=bms[c], q_pos0=c0, softmax_scale=w.scale))
     order = [f for c in range(nc) for f in (groups["produce"][c], groups["project"][c],
