@@ -543,7 +543,7 @@ constexpr int kCsTokBlk = 1024;
 
 typedef __attribute__((ext_vector_type(4))) double f64x4_t;
 
-template <int DP>
+template <int DP, int R>   // R: query heads per KV head (1, 2, 4 or 8)
 __global__ __launch_bounds__(kCsThreads, 2) void score_rows_mfma_kernel(
     const bf16_t* __restrict__ q_imp, const bf16_t* __restrict__ kimp, float* __restrict__ scores,
     int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0, int causal,
@@ -551,7 +551,6 @@ __global__ __launch_bounds__(kCsThreads, 2) void score_rows_mfma_kernel(
   constexpr int KG = DP / 4;   // d' values per lane group
   const int bg = blockIdx.z, i0 = blockIdx.y * kCsRows;
   const int b = bg / Hkv, g = bg - b * Hkv;
-  const int R = Hq / Hkv;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int ql = lane & 15, g4 = lane >> 4;
   // qbar[qb][s] = sum over the group's heads of Q_imp[row i0 + 16qb + ql][KG*g4 + s]
@@ -559,11 +558,10 @@ __global__ __launch_bounds__(kCsThreads, 2) void score_rows_mfma_kernel(
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
     const int i = min(i0 + 16 * qb + ql, Lq - 1);
-    float hv[8][KG];
+    float hv[R][KG];
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      const int hh = min(h, R - 1);
-      const bf16_t* src = q_imp + ((((long long)b * Hq + g * R + hh) * G + slot) * Lq + i) * DP + KG * g4;
+    for (int h = 0; h < R; ++h) {
+      const bf16_t* src = q_imp + ((((long long)b * Hq + g * R + h) * G + slot) * Lq + i) * DP + KG * g4;
       if constexpr (KG == 8) {
         Vec16<bf16_t>::load(src, hv[h]);
       } else {
@@ -578,7 +576,7 @@ __global__ __launch_bounds__(kCsThreads, 2) void score_rows_mfma_kernel(
     for (int e = 0; e < KG; ++e) {
       double a = 0.0;
 #pragma unroll
-      for (int h = 0; h < 8; ++h) a += (h < R) ? (double)hv[h][e] : 0.0;
+      for (int h = 0; h < R; ++h) a += (double)hv[h][e];
       qa[qb][e] = a;
     }
   }
@@ -654,9 +652,18 @@ hipError_t rows_t(hipStream_t s, const void* q_imp, const void* kimp, float* sco
                   int Hq, int Hkv, int G, int slot, int Lq, int L, int L_cap, int q_pos0,
                   int causal, int kvdiv) {
   dim3 grid((L + kCsTokBlk - 1) / kCsTokBlk, (Lq + kCsRows - 1) / kCsRows, B * Hkv);
-  hipLaunchKernelGGL((score_rows_mfma_kernel<DP>), grid, dim3(kCsThreads), 0, s,
-                     (const bf16_t*)q_imp, (const bf16_t*)kimp, scores, Hq, Hkv, G, slot, Lq, L,
-                     L_cap, q_pos0, causal, kvdiv);
+#define BUTLER_ROWS(R)                                                                    \
+  hipLaunchKernelGGL((score_rows_mfma_kernel<DP, R>), grid, dim3(kCsThreads), 0, s,       \
+                     (const bf16_t*)q_imp, (const bf16_t*)kimp, scores, Hq, Hkv, G, slot, Lq, \
+                     L, L_cap, q_pos0, causal, kvdiv)
+  switch (Hq / Hkv) {
+    case 1: BUTLER_ROWS(1); break;
+    case 2: BUTLER_ROWS(2); break;
+    case 4: BUTLER_ROWS(4); break;
+    case 8: BUTLER_ROWS(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef BUTLER_ROWS
   return hipGetLastError();
 }
 

@@ -146,6 +146,14 @@ def test_prefill_small_chunks():
     _prefill_case(w, L=300, chunk=128)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (4, 4), (4, 2)])
+def test_prefill_small_chunks_head_groups(Hq, Hkv):
+    """Groups of 8, 1 and 2 query heads per KV head: the causal scorer's instances for
+    R = 8, 1 and 2, and the bitmask attention off the R = 4 path."""
+    w = synthetic.WORKLOADS[5].replace(B=1, E=256, F=128, Hq=Hq, Hkv=Hkv)
+    _prefill_case(w, L=300, chunk=128)
+
+
 def test_prefill_llama_shape_one_chunk_pair():
     w = synthetic.WORKLOADS[5].replace(B=2)
     _prefill_case(w, L=2048, chunk=1024)
