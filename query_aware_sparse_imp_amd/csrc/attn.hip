@@ -552,6 +552,15 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 constexpr int kPfThreads = 256;
 constexpr int kPfKS = 128 + 8;   // LDS row stride (bf16) of the K tile
 
+// max of three floats that are finite or -inf.  fmaxf would first canonicalise each
+// operand built by bit operations (one more instruction per logit); v_max3_f32 needs no
+// canonical inputs for such values.
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 constexpr int kPfTok = 64;
 constexpr int kPfVS = kPfTok + 4;   // LDS row stride (bf16) of the transposed V tile
 
@@ -670,7 +679,15 @@ __global__ __launch_bounds__(2 * kPfThreads) void attn_prefill_mfma_kernel(
       const uint32_t k1 = (uint32_t)((int)(w1 << (31 - tt)) >> 31);
       z[r] = __uint_as_float((__float_as_uint(c0[r]) & k0) | (0xff800000u & ~k0));
       z[16 + r] = __uint_as_float((__float_as_uint(c1[r]) & k1) | (0xff800000u & ~k1));
-      mt = fmaxf(mt, fmaxf(z[r], z[16 + r]));
+    }
+    {
+      float ma = neg_inf(), mb = neg_inf();
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        ma = max3_f32(ma, z[r], z[16 + r]);
+        mb = max3_f32(mb, z[r + 1], z[17 + r]);
+      }
+      mt = fmaxf(ma, mb);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float mn = fmaxf(m, mt);
