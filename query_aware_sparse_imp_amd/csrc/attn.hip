@@ -528,8 +528,10 @@ hipError_t idx_t(hipStream_t s, const void* q, const void* k, const void* v,
 // query rows), one wave per query head of the group and 32-row group.  Key tiles of 64
 // tokens run from 0 to the block's causal end; each tile is staged in LDS once for the
 // eight waves -- K as [token][d], V transposed to [d][token] (two tokens packed per 32-bit
-// word) -- into one of two buffers: the next tile's rows are requested before this tile's
-// products and written to the other buffer after them, so one barrier separates two tiles.
+// word) -- in two buffers each, K one tile ahead of V: a wave takes the logits of the next
+// tile on the matrix cores beside the softmax of this one on the vector units (the two
+// waves of a SIMD would otherwise reach each phase together), and one barrier separates
+// two tiles.
 //   S^T = K . Q^T        A = K rows (tokens), B = the wave's 32 queries (kept in VGPRs),
 //                        as two 32-token halves (two accumulator sets)
 //   O^T += V^T . P^T      A = V^T rows (d), B = P^T straight from the S^T accumulators,
@@ -598,35 +600,39 @@ __global__ __launch_bounds__(2 * kPfThreads) void attn_prefill_mfma_kernel(
   const int dg = tid & 15;
   uint4 rs[4];        // K: 4 chunks; V: 2 pairs x 2 tokens
   uint32_t wn0, wn1;  // bitmask words of the tile in flight
-  auto gload = [&](int t0) {
+  // K rows of tile tk (K stagers) or V rows of tile tv (V stagers), clamped addresses
+  auto gload = [&](int tk, int tv) {
     if (do_k) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int c = kt + kPfThreads * u;
-        rs[u] = *reinterpret_cast<const uint4*>(kb + (long long)min(t0 + (c >> 4), L - 1) * D + (c & 15) * 8);
+        rs[u] = *reinterpret_cast<const uint4*>(kb + (long long)min(tk + (c >> 4), L - 1) * D + (c & 15) * 8);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int tp = (tid + kPfThreads * u) >> 4;
-        rs[2 * u] = *reinterpret_cast<const uint4*>(vb + (long long)min(t0 + 2 * tp, L - 1) * D + dg * 8);
-        rs[2 * u + 1] = *reinterpret_cast<const uint4*>(vb + (long long)min(t0 + 2 * tp + 1, L - 1) * D + dg * 8);
+        rs[2 * u] = *reinterpret_cast<const uint4*>(vb + (long long)min(tv + 2 * tp, L - 1) * D + dg * 8);
+        rs[2 * u + 1] = *reinterpret_cast<const uint4*>(vb + (long long)min(tv + 2 * tp + 1, L - 1) * D + dg * 8);
       }
     }
+  };
+  auto gload_words = [&](int t0) {
     const int w0 = t0 >> 5;
     wn0 = brow[min(w0, nwords - 1)];
     const uint32_t w1 = brow[min(w0 + 1, nwords - 1)];
     wn1 = (w0 + 1 < nwords) ? w1 : 0u;   // past the last word: no tokens
   };
-  auto stage = [&](int buf) {
+  // the held rows into K buffer kbuf (K stagers) or V buffer vbuf (V stagers)
+  auto stage = [&](int kbuf, int vbuf) {
     if (do_k) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int c = kt + kPfThreads * u;
-        *reinterpret_cast<uint4*>(&Ks[buf][(c >> 4) * kPfKS + (c & 15) * 8]) = rs[u];
+        *reinterpret_cast<uint4*>(&Ks[kbuf][(c >> 4) * kPfKS + (c & 15) * 8]) = rs[u];
       }
     } else {
-      uint32_t* vw = reinterpret_cast<uint32_t*>(Vt[buf]);
+      uint32_t* vw = reinterpret_cast<uint32_t*>(Vt[vbuf]);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int tp = (tid + kPfThreads * u) >> 4;
@@ -640,21 +646,9 @@ __global__ __launch_bounds__(2 * kPfThreads) void attn_prefill_mfma_kernel(
       }
     }
   };
-  float m = neg_inf(), msc = 0.f, l = 0.f;
-  f32x16_t o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  gload(0);
-  stage(0);
-  __syncthreads();
-  int cur = 0;
-  for (int t0 = 0; t0 < t_end; t0 += kPfTok) {
-    const uint32_t wd0 = qvalid ? wn0 : 0u, wd1 = qvalid ? wn1 : 0u;
-    gload(t0 + kPfTok);   // the next tile (clamped addresses; unused past the end)
-    const bf16_t* Kc = Ks[cur];
-    f32x16_t c0, c1;
+  // the logits S^T of the tile in K buffer kbuf: two 32-token halves
+  auto logits = [&](int kbuf, f32x16_t& c0, f32x16_t& c1) {
+    const bf16_t* Kc = Ks[kbuf];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       c0[r] = 0.f;
@@ -667,6 +661,34 @@ __global__ __launch_bounds__(2 * kPfThreads) void attn_prefill_mfma_kernel(
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s8], c0, 0, 0, 0);
       c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s8], c1, 0, 0, 0);
     }
+  };
+  float m = neg_inf(), msc = 0.f, l = 0.f;
+  f32x16_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  // K runs one tile ahead of V: iteration `it` takes the logits of tile it + 1 (matrix
+  // cores) beside the softmax of tile it (vector units), then P.V of tile it.  Iteration it
+  // reads K buffer (it+1)%2 and V buffer it%2 and refills K buffer it%2 with tile it + 2
+  // and V buffer (it+1)%2 with tile it + 1: one barrier per tile.
+  gload(0, 0);
+  gload_words(0);
+  stage(0, 0);
+  gload(kPfTok, 0);
+  stage(1, 0);   // V stagers store tile 0 again: the same values
+  __syncthreads();
+  f32x16_t s0, s1;   // logits of the current tile
+  logits(0, s0, s1);
+  __syncthreads();   // every wave is done with K buffer 0 before iteration 0 refills it
+  int it = 0;
+  for (int t0 = 0; t0 < t_end; t0 += kPfTok, ++it) {
+    const uint32_t wd0 = qvalid ? wn0 : 0u, wd1 = qvalid ? wn1 : 0u;
+    gload(t0 + 2 * kPfTok, t0 + kPfTok);   // past the end: clamped, never used
+    gload_words(t0 + kPfTok);
+    f32x16_t n0, n1;
+    logits((it + 1) & 1, n0, n1);
+    const f32x16_t c0 = s0, c1 = s1;
     // Raw logits of the selected tokens, -inf elsewhere: the token's bitmask bit,
     // sign-extended into a 32-bit lane mask, picks between the logit and -inf.  The
     // running max is kept raw (m) and scaled (msc); the scale goes into the exponent's FMA.
@@ -715,7 +737,7 @@ __global__ __launch_bounds__(2 * kPfThreads) void attn_prefill_mfma_kernel(
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)pr[8 * ks + e];
-    const bf16_t* Vc = Vt[cur];
+    const bf16_t* Vc = Vt[it & 1];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const bf16_t* vrow = &Vc[(db * 32 + ql) * kPfVS];
@@ -727,10 +749,11 @@ __global__ __launch_bounds__(2 * kPfThreads) void attn_prefill_mfma_kernel(
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[db], 0, 0, 0);
       }
     }
-    // the other buffer was last read before the previous barrier
-    stage(cur ^ 1);
+    // the buffers refilled here were last read before the previous barrier
+    stage(it & 1, (it + 1) & 1);
     __syncthreads();
-    cur ^= 1;
+    s0 = n0;
+    s1 = n1;
   }
   if (qvalid) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
