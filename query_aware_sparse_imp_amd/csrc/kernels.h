@@ -65,6 +65,10 @@ hipError_t launch_attn_bitmask(hipStream_t s, int dtype, const void* q, const vo
                                int Hq, int Hkv, int D, int Lq, int L, int L_cap, int q_pos0,
                                float scale, void* ws, int kvdiv);
 
+// bf16, D = 128, 4 query heads per KV head, Lq >= 32, one selection set per KV head
+hipError_t launch_prefill_mfma(hipStream_t s, const void* q, const void* k, const void* v,
+                               const uint32_t* bitmask, float* out, int B, int Hq, int Hkv,
+                               int Lq, int L, int L_cap, int q_pos0, float scale);
 hipError_t launch_attn_merge(hipStream_t s, const float* part, float* out, long long rows, int Hq,
                              int Hkv, int Lq, int D, int nsplit);
 bool select_attend_fusable(int dtype, int D, int Hq, int Hkv, int L);
