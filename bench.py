@@ -197,7 +197,7 @@ def run_config(w, L, replicas, steps, warmup, device, excludes_forced=False, sel
 
 
 # sources of the kernels in the roofline call (their digest keys the traffic record)
-TRAFFIC_SOURCES = ("select.hip", "attn.hip", "attn_tile.h", "common.h")
+TRAFFIC_SOURCES = ("select.hip", "select_rule.h", "attn.hip", "attn_tile.h", "common.h")
 
 
 def sources_sha256(files) -> str:

@@ -332,6 +332,9 @@ int butler_select_topk(void* stream, const float* scores, uint32_t* radix_hist,
   hipStream_t s = (hipStream_t)stream;
   uint32_t* hist = (Lq > 1) ? nullptr : radix_hist;   // see butler_score
   const int32_t* kp = (Lq > 1) ? nullptr : keep;
+  if (select_rows_fits(Lq, L))
+    return finish(s, launch_select_rows(s, scores, budget_num, budget_den, n_sink, n_window, fo,
+                                        idx, bitmask, count, B, Hs, Lq, L, cap, q_pos0, causal));
   return finish(s, launch_select(s, scores, budget_num, budget_den, n_sink, n_window, fo, idx,
                                  bitmask, count, B, Hs, Lq, L, cap, q_pos0, causal, hist, kp,
                                  workspace));

@@ -53,6 +53,13 @@ hipError_t launch_select(hipStream_t s, const float* scores, int num, int den, i
                          int n_window, int fo, int32_t* idx, uint32_t* bitmask, int32_t* count,
                          int B, int Hkv, int Lq, int L, int cap, int q_pos0, int causal,
                          uint32_t* hist, const int32_t* keep, void* ws);
+// Calls with several query rows per (b, head) and rows of at most 8192 tokens: one wave
+// per row (no scorer histogram, no selection-cache flags).
+bool select_rows_fits(int Lq, int L);
+hipError_t launch_select_rows(hipStream_t s, const float* scores, int num, int den, int n_sink,
+                              int n_window, int fo, int32_t* idx, uint32_t* bitmask,
+                              int32_t* count, int B, int Hs, int Lq, int L, int cap, int q_pos0,
+                              int causal);
 
 // ---- attention ------------------------------------------------------------
 size_t attn_workspace(int dtype, int B, int Hq, int Hkv, int D, int Lq, int L, int cap);

@@ -30,7 +30,8 @@
 //      and emits its bitmask words and indices through 64-token ballot words; the chunk-0
 //      workgroup writes the row count and clears the histogram.
 //
-// Other rows (short decode rows, every causal prefill row): one workgroup per row, 64 to
+// Other rows (short decode rows; calls with several query rows of more than 8192 tokens --
+//   those up to 8192 take one wave per row, in select_rows.hip): one workgroup per row, 64 to
 //   1024 threads sized to the row, holds the row's keys in VGPRs (16 to 64 per thread,
 //   strided so that a wave's ballot covers 64 consecutive tokens), builds the digit
 //   histograms in LDS (the first from the scorer's histogram when given), and emits
@@ -43,33 +44,12 @@
 #include "attn_tile.h"
 #include "common.h"
 #include "kernels.h"
+#include "select_rule.h"
 
 #include <type_traits>
 
 namespace butler {
 namespace {
-
-enum { kModeNormal = 0, kModeNone = 1, kModeAll = 2 };
-
-// x = floor(L_r * num / den) ranked over every token (fo == 0), or over the tokens that
-// are neither sink nor window (fo != 0: the budget excludes the forced tokens).
-__device__ __forceinline__ int row_mode(int L_r, int num, int den, int n_sink, int n_window,
-                                        int fo, int& k) {
-  const long long x = (long long)L_r * num / den;
-  int pool = L_r;
-  if (fo) {
-    const int s = min(n_sink, L_r), w_lo = max(0, L_r - n_window);
-    pool = L_r - (s + (L_r - max(w_lo, s)));   // tokens outside [0, s) U [w_lo, L_r)
-  }
-  k = (int)min<long long>(x, (long long)pool);
-  return k <= 0 ? kModeNone : (k >= pool ? kModeAll : kModeNormal);
-}
-
-// Ranking key of token t: the order-preserving score key, or 0 -- below every score's key
-// (NaN and -inf rank at 0x007fffff) -- for a forced token when the budget excludes them.
-__device__ __forceinline__ uint32_t rank_key(float f, int t, int n_sink, int w_lo, int fo) {
-  return (fo && (t < n_sink || t >= w_lo)) ? 0u : score_key(f);
-}
 
 // Among hist[0..nbins), scanned from the top bin down, the bin that holds the need-th
 // largest key, and the rank left inside it.  All NT threads call it.
@@ -216,12 +196,15 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
   __shared__ int wtie[MAXW], wcnt[MAXW];
   __shared__ uint64_t wsel[MAXW];
 
-  // all loads at once, from clamped addresses (no control flow around them)
+  // all loads at once, from clamped addresses, before any key is formed (a conversion
+  // next to each load would make the compiler wait for each load in turn)
+  float raw[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) raw[j] = s[min((int)threadIdx.x + NT * j, L_r - 1)];
   uint32_t key[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
-    key[j] = rank_key(s[min((int)threadIdx.x + NT * j, L_r - 1)], (int)threadIdx.x + NT * j,
-                      n_sink, w_lo, fo);
+    key[j] = rank_key(raw[j], (int)threadIdx.x + NT * j, n_sink, w_lo, fo);
   auto valid = [&](int j) { return (int)threadIdx.x + NT * j < L_r; };
 
   uint32_t tau = (mode == kModeAll) ? 0u : 0xffffffffu;

@@ -83,6 +83,24 @@ def test_select_rows_match_oracle(kind):
         _run(_scores(rng, (1, 3, 1, L), kind), num, den, ns, nw)
 
 
+@pytest.mark.parametrize("kind", ["normal", "ties", "special", "equal"])
+@pytest.mark.parametrize("fo", [False, True])
+def test_select_many_rows_match_oracle(kind, fo):
+    """Calls with several query rows of up to 8192 tokens (one wave per row): every row
+    length class, budgets of 0, below and at or above the pool, a row count that leaves a
+    workgroup part-filled, and rows whose bitmask ends inside a 64-word store."""
+    rng = np.random.default_rng({"normal": 41, "ties": 42, "special": 43, "equal": 44}[kind]
+                                + (10 if fo else 0))
+    cases = [(1, 1, 2, 0, 0), (31, 1, 2, 4, 16), (64, 3, 10, 4, 64), (65, 1, 16, 4, 128),
+             (1000, 0, 1, 3, 5), (1024, 1, 2, 4, 64), (1025, 1, 1, 4, 16),
+             (2048, 5, 4, 4, 64), (3000, 1, 2, 4, 64), (5000, 1, 16, 4, 128),
+             (6200, 9, 10, 64, 1000), (8191, 1, 2, 4, 64), (8192, 1, 2, 4, 64)]
+    for (L, num, den, ns, nw) in cases:
+        print(f"[select-rows] kind={kind} fo={fo} L={L} budget={num}/{den} sink={ns} "
+              f"window={nw}", flush=True)
+        _run(_scores(rng, (1, 2, 3, L), kind), num, den, ns, nw, fo=fo)
+
+
 def test_select_causal_rows():
     rng = np.random.default_rng(5)
     # row lengths in every per-row workgroup shape: 64 to 1024 threads, 4 to 64 keys each
