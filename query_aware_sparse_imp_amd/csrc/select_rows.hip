@@ -28,7 +28,7 @@ namespace butler {
 namespace {
 
 constexpr int kSwWaves = 4;      // rows per workgroup
-constexpr int kSwWords = 1024;   // 2048 bins, two 16-bit counts per word
+constexpr int kSwCand = 256;     // tau's first-digit bin resolved without more radix passes
 
 // Orders the wave's LDS accesses of one phase before those of the next: a wave's LDS
 // instructions run in issue order, so only the compiler has to be kept from moving them.
@@ -60,75 +60,112 @@ __device__ __forceinline__ int wave_exclusive_sum(int v, int lane) {
   return incl - v;
 }
 
-// Among the NB bins of hist (packed 16-bit counts), scanned from the top bin down, the bin
-// that holds the need-th largest key (1 <= need <= the total count), the rank left inside
-// it, and its count.  Lane l covers bins [NB - (l + 1) P, NB - l P), P = NB / 64.
-template <int NB>
+// Order-preserving key of a score, equal to score_key in five vector instructions: the
+// max with -inf turns NaN into -inf and adding +0 turns -0 into +0 (IEEE arithmetic, with
+// denormals kept), then a negative value has every bit flipped and a non-negative one its
+// sign bit set.
+__device__ __forceinline__ uint32_t fast_key(float f) {
+  const float g = fmaxf(f, -__builtin_inff()) + 0.0f;
+  const uint32_t u = __float_as_uint(g);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+// A wave's radix histogram: NB counts, 32-bit (8 KB for 2048 bins), or 16-bit packed two
+// to a word (PACKED: word w holds bins 2w and 2w + 1) for the short-row instances, whose
+// many resident waves would not fit 8 KB each in LDS.
+template <bool PACKED>
+constexpr int sw_words(int nb) { return PACKED ? nb / 2 : nb; }
+
+// Count of bin b in hist.
+template <bool PACKED>
+__device__ __forceinline__ int bin_count(const uint32_t* hist, int b) {
+  if constexpr (PACKED)
+    return (int)((hist[b >> 1] >> ((b & 1) << 4)) & 0xffffu);
+  else
+    return (int)hist[b];
+}
+
+// Among the NB bins of hist, scanned from the top bin down, the bin that holds the need-th
+// largest key (1 <= need <= the total count), the rank left inside it, and its count.
+// Lane l sums bins [NB - (l + 1) P, NB - l P), P = NB / 64; a prefix sum over the lanes
+// finds the lane f whose bins hold the rank, then lane m < P takes f's bin NB - f P - 1 - m
+// (from the top) and a second prefix sum finds the bin.
+template <int NB, bool PACKED>
 __device__ __forceinline__ void wave_find_bin(const uint32_t* hist, int need, int lane,
                                               int& bin, int& need_in, int& cnt) {
-  constexpr int P = NB / 64, WPL = P / 2;
-  const int base = NB / 2 - (lane + 1) * WPL;   // first word of this lane's bins
-  uint32_t w[WPL];
+  constexpr int P = NB / 64, WPL = PACKED ? P / 2 : P;
+  const int base = sw_words<PACKED>(NB) - (lane + 1) * WPL;   // first word of this lane's bins
+  uint32_t sum = 0;
 #pragma unroll
   for (int q = 0; q < WPL / 4; ++q) {
     const uint4 v = reinterpret_cast<const uint4*>(hist + base)[q];
-    w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+    sum += v.x + v.y + v.z + v.w;   // packed: the low halves stay below 2^16
   }
-  uint32_t sum = 0;
-#pragma unroll
-  for (int m = 0; m < WPL; ++m) sum += w[m];   // low halves stay below 2^16: no carry
-  const int local = (int)(sum & 0xffffu) + (int)(sum >> 16);
+  const int local = PACKED ? (int)(sum & 0xffffu) + (int)(sum >> 16) : (int)sum;
   const int above = wave_exclusive_sum(local, lane);
   const uint64_t hit = __ballot(above < need && need <= above + local);
   const int f = __builtin_amdgcn_readfirstlane((int)__ffsll((unsigned long long)hit) - 1);
-  int b_f = 0, n_f = 0, c_f = 0;
-  if (lane == f) {
-    int run = above;
-    bool done = false;
-#pragma unroll
-    for (int m = WPL - 1; m >= 0; --m) {
-#pragma unroll
-      for (int h = 1; h >= 0; --h) {
-        const int c = (int)((w[m] >> (16 * h)) & 0xffffu);
-        if (!done && run + c >= need) {
-          done = true;
-          b_f = 2 * (base + m) + h;
-          n_f = need - run;
-          c_f = c;
-        }
-        run += c;
-      }
-    }
-  }
-  bin = __builtin_amdgcn_readlane(b_f, f);
-  need_in = __builtin_amdgcn_readlane(n_f, f);
-  cnt = __builtin_amdgcn_readlane(c_f, f);
+  const int above_f = __builtin_amdgcn_readlane(above, f);
+  const int b = NB - f * P - 1 - lane;   // lane m < P: f's bins from the top down
+  const int c = lane < P ? bin_count<PACKED>(hist, b) : 0;
+  const int run = above_f + wave_exclusive_sum(c, lane);   // keys above bin b
+  const uint64_t hit2 = __ballot(lane < P && run < need && need <= run + c);
+  const int g = __builtin_amdgcn_readfirstlane((int)__ffsll((unsigned long long)hit2) - 1);
+  bin = __builtin_amdgcn_readlane(b, g);
+  need_in = need - __builtin_amdgcn_readlane(run, g);
+  cnt = __builtin_amdgcn_readlane(c, g);
 }
 
-// Histogram of digit (key >> SH) & (NB - 1) over the valid keys that share prefix under
-// pmask (every valid key when ALL), then the bin of the need-th largest.
-template <int KPT, int NB, int SH, bool ALL>
-__device__ __forceinline__ void wave_digit(const uint32_t (&key)[KPT], uint32_t* hist,
-                                           int lane, int L_r, uint32_t prefix, uint32_t pmask,
-                                           int need, int& bin, int& need_in, int& cnt) {
+template <int NB, bool PACKED>
+__device__ __forceinline__ void wave_clear(uint32_t* hist, int lane) {
   uint4* h4 = reinterpret_cast<uint4*>(hist);
 #pragma unroll
-  for (int q = 0; q < NB / 2 / 4 / 64; ++q) h4[lane + 64 * q] = make_uint4(0u, 0u, 0u, 0u);
+  for (int q = 0; q < sw_words<PACKED>(NB) / 4 / 64; ++q)
+    h4[lane + 64 * q] = make_uint4(0u, 0u, 0u, 0u);
   wave_lds_order();
-  const int ln = opaque_v(lane), lr = opaque_s(L_r);
+}
+
+template <bool PACKED>
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d) {
+  if constexpr (PACKED)
+    atomicAdd(&hist[d >> 1], 1u << ((d & 1u) << 4));
+  else
+    atomicAdd(&hist[d], 1u);
+}
+
+// First radix digit (key bits 31..21) of the row's L_r keys, then the bin of the need-th
+// largest.  Slots wholly inside the row add with every lane, the one slot that holds the
+// row's end with its valid lanes, and slots past the end not at all.
+template <int KPT, bool PACKED>
+__device__ __forceinline__ void wave_digit0(const uint32_t (&key)[KPT], uint32_t* hist,
+                                            int lane, int L_r, int need, int& bin,
+                                            int& need_in, int& cnt) {
+  wave_clear<2048, PACKED>(hist, lane);
+  const int lr = opaque_s(L_r);
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t d = (key[j] >> SH) & (NB - 1);
-    const uint32_t inc = 1u << ((d & 1u) << 4);
-    if constexpr (ALL) {
-      // every slot adds, past the row's end nothing (no branch around the atomic)
-      atomicAdd(&hist[d >> 1], ln + 64 * j < lr ? inc : 0u);
-    } else {
-      if (ln + 64 * j < lr && (key[j] & pmask) == prefix) atomicAdd(&hist[d >> 1], inc);
-    }
-  }
+  for (int j = 0; j < KPT; ++j)
+    if (64 * j < lr) hist_add<PACKED>(hist, key[j] >> 21);
   wave_lds_order();
-  wave_find_bin<NB>(hist, need, lane, bin, need_in, cnt);
+  // the slot that holds the row's end added its lanes past the end (keys of 0) to bin 0
+  if ((lr & 63) && lane == 0) hist[0] -= (uint32_t)(64 - (lr & 63));
+  wave_lds_order();
+  wave_find_bin<2048, PACKED>(hist, need, lane, bin, need_in, cnt);
+  wave_lds_order();
+}
+
+// A later digit (key >> SH) & (NB - 1) over the keys that share prefix under pmask (a key
+// zeroed as past the row's end or forced never does: prefix holds a first digit of 3 or
+// more), then the bin of the need-th largest.
+template <int KPT, int NB, int SH, bool PACKED>
+__device__ __forceinline__ void wave_digit(const uint32_t (&key)[KPT], uint32_t* hist,
+                                           int lane, uint32_t prefix, uint32_t pmask,
+                                           int need, int& bin, int& need_in, int& cnt) {
+  wave_clear<NB, PACKED>(hist, lane);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if ((key[j] & pmask) == prefix) hist_add<PACKED>(hist, (key[j] >> SH) & (NB - 1));
+  wave_lds_order();
+  wave_find_bin<NB, PACKED>(hist, need, lane, bin, need_in, cnt);
   wave_lds_order();
 }
 
@@ -140,7 +177,8 @@ __global__ __launch_bounds__(64 * kSwWaves, sw_waves_per_simd(KPT)) void select_
     const float* __restrict__ scores, int num, int den, int n_sink, int n_window, int fo,
     int32_t* __restrict__ idx, uint32_t* __restrict__ bitmask, int32_t* __restrict__ count,
     long long rows, int Lq, int L, int cap, int q_pos0, int causal) {
-  __shared__ __align__(16) uint32_t hist_all[kSwWaves][kSwWords];
+  constexpr bool PACKED = KPT < 48;
+  __shared__ __align__(16) uint32_t hist_all[kSwWaves][sw_words<PACKED>(2048)];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const long long row = (long long)blockIdx.x * kSwWaves + wid;
@@ -155,8 +193,8 @@ __global__ __launch_bounds__(64 * kSwWaves, sw_waves_per_simd(KPT)) void select_
 
   // every load at once, before any key is formed (a conversion next to each load would
   // make the compiler wait for each load in turn), through a buffer resource whose range
-  // is the row's L_r scores: slots past the end read 0 (masked below) instead of needing
-  // a clamped address each, and all loads share one offset register
+  // is the row's L_r scores: slots past the end read 0 instead of needing a clamped
+  // address each, and all loads share one offset register
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)s, (short)0, L_r * 4, 0x00020000);
   float raw[KPT];
@@ -165,28 +203,85 @@ __global__ __launch_bounds__(64 * kSwWaves, sw_waves_per_simd(KPT)) void select_
     raw[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (lane + 64 * j), 0, 0));
   uint32_t key[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = rank_key(raw[j], lane + 64 * j, n_sink, w_lo, fo);
+  for (int j = 0; j < KPT; ++j) key[j] = fast_key(raw[j]);
+  // keys that do not rank become 0, below every score's key (-inf's is 0x007fffff): the
+  // slots past the row's end, and the forced tokens when the budget excludes them; only
+  // the slots that hold such a token are touched
+  {
+    const int ln = opaque_v(lane), lr = opaque_s(L_r), ns = opaque_s(n_sink), wl = opaque_s(w_lo);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (64 * j + 64 > lr || (fo && (64 * j < ns || 64 * j + 64 > wl))) {
+        const int t = ln + 64 * j;
+        key[j] = ((t >= lr) | (fo && ((t < ns) | (t >= wl)))) ? 0u : key[j];
+      }
+    }
+  }
 
   // tau: the k-th largest key; need: how many keys equal to tau the budget takes
   uint32_t tau = 0;
   int need = 0, n_eq = 0;
   if (mode == kModeNormal) {
-    int b0, b1, b2, n0, n1;
-    wave_digit<KPT, 2048, 21, true>(key, hist, lane, L_r, 0u, 0u, k, b0, n0, n_eq);
+    int b0, b1, b2, n0, n1, c0;
+    wave_digit0<KPT, PACKED>(key, hist, lane, L_r, k, b0, n0, c0);
     const uint32_t p0 = (uint32_t)b0 << 21;
-    wave_digit<KPT, 2048, 10, false>(key, hist, lane, L_r, p0, 0xffe00000u, n0, b1, n1, n_eq);
-    const uint32_t p1 = p0 | ((uint32_t)b1 << 10);
-    wave_digit<KPT, 1024, 0, false>(key, hist, lane, L_r, p1, 0xfffffc00u, n1, b2, need, n_eq);
-    tau = p1 | (uint32_t)b2;
+    if (c0 <= kSwCand) {
+      // few keys share tau's first digit: gather them into LDS, four per lane at most,
+      // and find the n0-th largest of them bit by bit (21 ballot counts), no histogram
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool m = (key[j] >> 21) == (uint32_t)b0;
+        const uint64_t bm = __ballot(m);
+        if (bm) {
+          const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bm, base));
+          if (m & (pos < kSwCand)) hist[pos] = key[j];   // pos < c0: the same keys were counted
+          base = opaque_s(base + __popcll(bm));
+        }
+      }
+      wave_lds_order();
+      uint32_t c[kSwCand / 64];
+#pragma unroll
+      for (int q = 0; q < kSwCand / 64; ++q) c[q] = (lane + 64 * q < c0) ? hist[lane + 64 * q] : 0u;
+      wave_lds_order();
+      // the zero padding never counts: the n0-th largest candidate is a score's key (the
+      // budget takes fewer keys than there are non-forced tokens), at least -inf's
+      // 0x007fffff, so t > 0
+      uint32_t t = p0;
+#pragma unroll
+      for (int bit = 20; bit >= 0; --bit) {
+        const uint32_t trial = t | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < kSwCand / 64; ++q) n += __popcll(__ballot(c[q] >= trial));
+        t = n >= n0 ? trial : t;
+      }
+      int n_gt = 0;
+#pragma unroll
+      for (int q = 0; q < kSwCand / 64; ++q) {
+        n_gt += __popcll(__ballot(c[q] > t));
+        n_eq += __popcll(__ballot(c[q] == t));
+      }
+      tau = t;
+      need = n0 - n_gt;
+    } else {
+      wave_digit<KPT, 2048, 10, PACKED>(key, hist, lane, p0, 0xffe00000u, n0, b1, n1, n_eq);
+      const uint32_t p1 = p0 | ((uint32_t)b1 << 10);
+      wave_digit<KPT, 1024, 0, PACKED>(key, hist, lane, p1, 0xfffffc00u, n1, b2, need, n_eq);
+      tau = p1 | (uint32_t)b2;
+    }
   }
 
   // ---- emit in index order ----------------------------------------------------------
   const int nwords = (L + 31) / 32;   // <= 2 KPT: the instance covers the row stride L
   uint32_t* brow = bitmask ? bitmask + row * (long long)nwords : nullptr;
   int32_t* irow = idx ? idx + row * (long long)cap : nullptr;
-  // without a tie cut a key is taken iff key >= lo: 0 takes every key, and no key reaches
-  // 0xffffffff (the largest, +inf's, is 0xff800000)
-  const uint32_t lo = mode == kModeAll ? 0u : (mode == kModeNormal ? tau : 0xffffffffu);
+  const bool ties = mode == kModeNormal && n_eq > need;
+  // without a tie cut a token is taken iff it is forced or key >= lo: lo = 1 takes every
+  // score (0 is past the row's end), and no score's key reaches 0xffffffff (the largest,
+  // +inf's, is 0xff800000)
+  const uint32_t lo = mode == kModeAll ? 1u : (mode == kModeNormal ? tau : 0xffffffffu);
   const bool odd = lane & 1;
   const int pair = lane >> 1;
   int sel_base = 0;
@@ -195,30 +290,40 @@ __global__ __launch_bounds__(64 * kSwWaves, sw_waves_per_simd(KPT)) void select_
                    BM = decltype(bm_c)::value;
     int tie_base = 0;
     uint32_t wordv = 0;
-    const int ln = opaque_v(lane), lr = opaque_s(L_r);
+    const int ln = opaque_v(lane), lr = opaque_s(L_r), ns = opaque_s(n_sink),
+              wl = opaque_s(w_lo);
+    // slots [js, js + span) hold no forced token: one unsigned range test per slot
+    const int nsr = min(ns, lr);
+    const int js = (nsr + 63) >> 6, span = opaque_s(max((wl >> 6) - js, 0));
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      // bitwise rather than short-circuit logic: lane masks combined by scalar instructions
-      const int t = ln + 64 * j;
-      const bool v = t < lr;
-      const bool forced = (t < n_sink) | (t >= w_lo);
-      bool sel;
+      int rank = 0;
       if constexpr (TIES) {
-        // the budget takes the need lowest-index keys equal to tau
-        const bool eq = v & (key[j] == tau);
-        const uint64_t e = __ballot(eq);
-        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(e >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)e, tie_base));
+        // the budget takes the need lowest-index keys equal to tau (a zeroed key never is)
+        const uint64_t e = __ballot(key[j] == tau);
+        rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(e >> 32),
+                                         __builtin_amdgcn_mbcnt_lo((uint32_t)e, tie_base));
         tie_base += __popcll(e);
-        sel = v & (forced | (key[j] > tau) | (eq & (rank < need)));
-      } else {
-        sel = v & (forced | (key[j] >= lo));
       }
-      const uint64_t b = __ballot(sel);
+      uint64_t b;
+      if constexpr (TIES) {
+        const int t = ln + 64 * j;
+        const bool by_key = (key[j] > tau) | ((key[j] == tau) & (rank < need));
+        b = __ballot((t < lr) & ((t < ns) | (t >= wl) | by_key));
+      } else {
+        // a ballot in each branch keeps the branch (the forced test runs only where needed)
+        if ((unsigned)(j - js) >= (unsigned)span) {
+          const int t = ln + 64 * j;
+          b = __ballot((key[j] >= lo) | (t < nsr) | ((t >= wl) & (t < lr)));
+        } else {
+          b = __ballot(key[j] >= lo);
+        }
+      }
       if constexpr (IDX) {
+        const bool sel = (b >> ln) & 1ull;
         const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)b, sel_base));
-        if (sel && pos < cap) irow[pos] = t;
+        if (sel && pos < cap) irow[pos] = ln + 64 * j;
       }
       sel_base = opaque_s(sel_base + __popcll(b));   // counted now: b need not stay live
       if constexpr (BM) {
@@ -227,7 +332,7 @@ __global__ __launch_bounds__(64 * kSwWaves, sw_waves_per_simd(KPT)) void select_
         wordv = (uint32_t)opaque_v((int)((pair == (j & 31)) ? half : wordv));   // now, not
                                                                                    // at the store
         if ((j & 31) == 31 || j == KPT - 1) {
-          const int wd = 64 * (j >> 5) + lane;
+          const int wd = 64 * (j >> 5) + ln;
           if (wd < nwords) brow[wd] = wordv;
           wordv = 0;
         }
@@ -239,7 +344,6 @@ __global__ __launch_bounds__(64 * kSwWaves, sw_waves_per_simd(KPT)) void select_
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  const bool ties = mode == kModeNormal && n_eq > need;
   if (ties) {
     if (irow && brow) emit(T_(), T_(), T_());
     else if (irow) emit(T_(), T_(), F_());
