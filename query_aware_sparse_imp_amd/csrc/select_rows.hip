@@ -144,7 +144,7 @@ __device__ __forceinline__ void wave_digit0(const uint32_t (&key)[KPT], uint32_t
   const int lr = opaque_s(L_r);
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
-    if (64 * j < lr) hist_add<PACKED>(hist, key[j] >> 21);
+    if (__builtin_expect(64 * j < lr, 1)) hist_add<PACKED>(hist, key[j] >> 21);
   wave_lds_order();
   // the slot that holds the row's end added its lanes past the end (keys of 0) to bin 0
   if ((lr & 63) && lane == 0) hist[0] -= (uint32_t)(64 - (lr & 63));
