@@ -9,12 +9,15 @@
 // (4) GEMM a . W2^T; (5) reduction + bf16 store scattered into the Q_imp layout.
 // With one split the epilogue runs inside the GEMM.
 //
-// Two GEMM kernels.  Blocks of rows (prefill: M = B*Lq >= 64) run on the matrix cores:
-// a 128 x 128 tile per workgroup, 64 x 64 per wave as 2 x 2 v_mfma_f32_32x32x16_bf16
-// tiles, K staged through LDS 64 at a time, double-buffered, with two register stages so
-// the next K tile is in flight from memory; bf16 results leave through an LDS stage
-// as 16-byte row chunks (contiguous in both the row-major activation and the Q_imp
-// layout).  Other shapes with more than 4 rows take the VALU kernel -- 32 rows x 64
+// GEMM kernels.  Blocks of rows (prefill: M = B*Lq >= 64) run on the matrix cores: a
+// 128 x 128 tile per workgroup, 64 x 64 per wave as 2 x 2 v_mfma_f32_32x32x16_bf16 tiles,
+// K staged through LDS 64 at a time.  gemm_dma_kernel (every shape whose operands fit
+// 32-bit byte offsets) loads each stage straight into LDS with buffer loads, in a ring of
+// two stages (two workgroups per CU), takes its tile from an XCD-aware order, and keeps
+// the accumulators transposed so its epilogue packs four columns per LDS write;
+// gemm_mfma_kernel (the rest) stages through registers.  bf16 results leave through an
+// LDS stage as 16-byte row chunks (contiguous in both the row-major activation and the
+// Q_imp layout).  Other shapes with more than 4 rows take the VALU kernel -- 32 rows x 64
 // columns per workgroup, a thread owns 1 row x 8 columns.  Up to 4 rows (decode: one
 // hidden state per sequence) take a weight-streaming GEMV instead (below).
 #include "common.h"
@@ -77,6 +80,14 @@ __global__ __launch_bounds__(kLnThreads) void ln_rows_kernel(const bf16_t* __res
               ((uint32_t)f2bf((hv[u][2 * e + 1] - mean) * rstd) << 16);
     *reinterpret_cast<uint4*>(xhat + row * E + e0) = o;
   }
+}
+
+// Two floats -> two bf16 (rounded to nearest even) in one 32-bit word, low half first:
+// the hardware's packed conversion.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2v_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Output placement of GEMM results.
@@ -334,7 +345,247 @@ __global__ __launch_bounds__(kMThreads) void gemm_mfma_kernel(
   }
 }
 
+// The same tiles and wave layout fed by LDS-direct buffer loads: each stage of 64 K values
+// (16 KB of A, 16 KB of B) goes from memory straight into LDS (buffer_load_dwordx4 ... lds,
+// no VGPR staging, no LDS store instructions), S stages in a ring, so S - 1 stages are in
+// flight while one is multiplied; one barrier per stage.  A wave's load writes 1 KB of LDS
+// in lane order: eight tile rows of 128 bytes.  The lane picks which 16-byte chunk of its
+// row it fetches so that chunk c of tile row r sits in slot c ^ ((r >> 1) & 7): the
+// operand reads of 16 consecutive rows (one LDS cycle of a 16-byte read) then hit 16
+// distinct 16-byte bank groups.  Rows past M are read clamped and never stored.
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kDK = 64;                                 // K per stage
+constexpr int kDTile = kMM * kDK * 2;                   // bytes of one operand tile
+constexpr int kDLoads = kDTile / (kMThreads * 16);      // 16-byte loads per lane and operand
+
+// s_waitcnt bounding only the vector-memory counter (expcnt, lgkmcnt left at their maximum)
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// wait until at most n_left (0, 8 or 16: whole stages) of this wave's loads are in flight
+__device__ __forceinline__ void wait_vm(int n_left) {
+  if (n_left >= 16) wait_vm_n<16>();
+  else if (n_left >= 8) wait_vm_n<8>();
+  else wait_vm_n<0>();
+}
+
+// Which tile a workgroup takes.  Workgroup w runs on XCD w % 8, and each XCD has its own
+// L2: with xcd set, the XCDs split the (split, row block, column tile) space into 8
+// rectangles of xs x xm x xn, and XCD x takes every tile of rectangle x, so its L2 fetches
+// only those rows of A and of B (for the producer at 2048 rows: 6 MB per XCD instead of
+// nearly all 25 MB).
+struct TileMap {
+  int nm, nn, ns;    // row blocks, column tiles, K splits
+  int xm, xn, xs;    // how the 8 XCDs divide each (xcd != 0)
+  int xcd;
+};
+
+__device__ __forceinline__ void tile_of(const TileMap& t, int w, int& mb, int& nb, int& s) {
+  if (!t.xcd) {
+    nb = w % t.nn;
+    mb = (w / t.nn) % t.nm;
+    s = w / (t.nn * t.nm);
+    return;
+  }
+  const int x = w & 7, j = w >> 3;
+  const int rn = t.nn / t.xn, rm = t.nm / t.xm, rs = t.ns / t.xs;
+  nb = (x % t.xn) * rn + j % rn;
+  mb = ((x / t.xn) % t.xm) * rm + (j / rn) % rm;
+  s = (x / (t.xn * t.xm)) * rs + j / (rn * rm);
+}
+
+template <int S>
+__global__ __launch_bounds__(kMThreads) void gemm_dma_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm, void* out, int M, int N, int K,
+    int k_per_split, Epilogue ep, TileMap tm) {
+  static_assert(S >= 2 && S <= 4, "stage ring");
+  __shared__ __align__(16) unsigned char sm[S * 2 * kDTile];
+  int mb, nb, split;
+  tile_of(tm, blockIdx.x, mb, nb, split);
+  const int n0 = nb * kMN, m0 = mb * kMM;
+  const int k0 = split * k_per_split;
+  const int T = k_per_split / kDK;   // >= S - 1 (checked on the host)
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, M * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Bm, (short)0, N * K * 2, 0x00020000);
+  // load j of this lane: tile row 32 wid + 8 j + lane / 8, slot lane % 8
+  int va[kDLoads], vb[kDLoads];
+#pragma unroll
+  for (int j = 0; j < kDLoads; ++j) {
+    const int r = 32 * wid + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    va[j] = (min(m0 + r, M - 1) * K + 8 * c) * 2;
+    vb[j] = ((n0 + r) * K + 8 * c) * 2;
+  }
+  lds_void_t* lds = (lds_void_t*)sm;
+  const auto issue = [&](int t) {
+    const int so = (k0 + t * kDK) * 2;
+    unsigned char* base = sm + (t % S) * 2 * kDTile + wid * (kDLoads * 1024);
+#pragma unroll
+    for (int j = 0; j < kDLoads; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(base + j * 1024), 16, va[j], so, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kDLoads; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(base + kDTile + j * 1024), 16, vb[j], so, 0, 0);
+  };
+  (void)lds;
+  // operand reads: tile row (wm or wn) * 64 + 32 i + lane % 32, logical chunk 2 ks + lane / 32
+  const int f = (lane >> 1) & 7, h = lane >> 5;
+  int rowa[2], rowb[2], slot[kDK / 16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    rowa[i] = (wm * 64 + i * 32 + (lane & 31)) * 128;
+    rowb[i] = kDTile + (wn * 64 + i * 32 + (lane & 31)) * 128;
+  }
+#pragma unroll
+  for (int ks = 0; ks < kDK / 16; ++ks) slot[ks] = 16 * ((2 * ks + h) ^ f);
+  f32x16v_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+  for (int t = 0; t < T; ++t) {
+    // this wave's loads of stage t have landed once at most the later stages' are left
+    wait_vm(min(S - 2, T - 1 - t) * 2 * kDLoads);
+    // every wave's stage t is in LDS and every wave is done with stage t-1 (a bare barrier:
+    // __syncthreads would also wait for the later stages' loads)
+    __builtin_amdgcn_s_barrier();
+    if (t + S - 1 < T) issue(t + S - 1);
+    const unsigned char* st = sm + (t % S) * 2 * kDTile;
+#pragma unroll
+    for (int ks = 0; ks < kDK / 16; ++ks) {
+      bf16x8v_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8v_t*>(st + rowa[i] + slot[ks]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8v_t*>(st + rowb[j] + slot[ks]);
+      // weights as the first operand: the accumulators hold C^T, so a lane's four
+      // consecutive accumulators are four consecutive output columns of one row
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+  }
+  // accumulator r of tile (i, j): row m0 + 64 wm + 32 i + lane % 32, column
+  // n0 + 64 wn + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4
+  const int lr = lane & 31, h4 = 4 * (lane >> 5);
+  if (ep.mode == 0) {
+    float* P = (float*)out + (long long)split * M * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = m0 + wm * 64 + i * 32 + lr;
+      if (m >= M) continue;
+      float* prow = P + (long long)m * N + n0 + wn * 64 + h4;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(prow + j * 32 + 8 * g) =
+              make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                          acc[i][j][4 * g + 3]);
+    }
+    return;
+  }
+  // bf16 results through LDS ([128][136] over the ring, 8-byte writes of four columns),
+  // then 16-byte row chunks to memory
+  constexpr int CS = kMN + 8;
+  bf16_t* Cs = reinterpret_cast<bf16_t*>(sm);
+  static_assert(kMM * CS * 2 <= S * 2 * kDTile, "output stage fits the ring");
+  __syncthreads();   // every wave is done reading the last stage
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = (ep.mode == 1) ? fmaxf(acc[i][j][4 * g + e], 0.f) : acc[i][j][4 * g + e];
+        *reinterpret_cast<uint2*>(&Cs[(wm * 64 + i * 32 + lr) * CS + wn * 64 + j * 32 + 8 * g + h4]) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+  __syncthreads();
+  const int cc = tid & 15;   // this thread's 16-byte chunk: columns n0 + 8 cc .. + 7
+  const int r0 = tid >> 4;   // rows r0 + 16 i
+  const int n = n0 + 8 * cc;
+  if (ep.mode == 1) {
+#pragma unroll
+    for (int i = 0; i < kMM / 16; ++i) {
+      const int m = m0 + r0 + 16 * i;
+      if (m >= M) break;
+      *reinterpret_cast<uint4*>((bf16_t*)out + (long long)m * N + n) =
+          *reinterpret_cast<const uint4*>(&Cs[(r0 + 16 * i) * CS + 8 * cc]);
+    }
+    return;
+  }
+  // Q_imp layout: column n = (head G + slot) d' + i0, row m = b Lq + t; the chunk stays
+  // inside one (head, slot) run.  The column part is fixed per thread; (b, t) steps by 16
+  // rows at a time.
+  const int head = n / (ep.G * ep.dp);
+  const int rem = n - head * ep.G * ep.dp;
+  const int slot2 = rem / ep.dp, i0 = rem - slot2 * ep.dp;
+  int bb = (m0 + r0) / ep.Lq, tt = (m0 + r0) - bb * ep.Lq;
+#pragma unroll
+  for (int i = 0; i < kMM / 16; ++i) {
+    const int m = m0 + r0 + 16 * i;
+    if (m >= M) break;
+    bf16_t* dst = (bf16_t*)out +
+                  ((((long long)bb * ep.Hq + head) * ep.G + slot2) * ep.Lq + tt) * ep.dp + i0;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&Cs[(r0 + 16 * i) * CS + 8 * cc]);
+    tt += 16;
+    while (tt >= ep.Lq) {
+      tt -= ep.Lq;
+      ++bb;
+    }
+  }
+}
+
 constexpr int kMGran = kM2St * kM2K;   // K granule of a split
+
+#ifndef BUTLER_GEMM_DMA_STAGES
+#define BUTLER_GEMM_DMA_STAGES 2
+#endif
+constexpr int kDStages = BUTLER_GEMM_DMA_STAGES;   // 0: register-staged kernel only
+constexpr int kDRing = kDStages >= 2 ? kDStages : 2;   // the LDS-direct kernel's ring
+
+// The LDS-direct kernel addresses its operands with 32-bit byte offsets and needs at least
+// S - 1 stages of K in a split.
+bool use_dma(int M, int N, int K, int kps) {
+  return kDStages >= 2 && (long long)M * K * 2 < (1LL << 31) &&
+         (long long)N * K * 2 < (1LL << 31) && kps % kDK == 0 && kps / kDK >= kDStages - 1;
+}
+
+// The XCD split of the tiles with the least L2 fill: per XCD, its splits' share of K times
+// (row blocks + column tiles) of its rectangle.  Without a split into 8 equal rectangles,
+// the plain order.
+TileMap tile_map(int nm, int nn, int ns) {
+  TileMap best{nm, nn, ns, 1, 1, 1, 0};
+  long long best_cost = -1;
+  for (int xs = 1; xs <= 8; xs *= 2)
+    for (int xm = 1; xs * xm <= 8; xm *= 2) {
+      const int xn = 8 / (xs * xm);
+      if (ns % xs || nm % xm || nn % xn) continue;
+      const long long cost = (long long)(ns / xs) * (nm / xm + nn / xn);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best = TileMap{nm, nn, ns, xm, xn, xs, 1};
+      }
+    }
+  return best;
+}
 
 bool use_mfma(int M, int N, int K) {
   return M >= 64 && N % kMN == 0 && K % kMGran == 0;
@@ -354,6 +605,42 @@ __global__ void reduce_splits_kernel(const float* __restrict__ P, void* out, int
   float acc = 0.f;
   for (int s = 0; s < nsplit; ++s) acc += P[(long long)s * M * N + e];
   store_out(ep, out, M, N, (int)(e / N), (int)(e % N), acc);
+}
+
+// The same eight columns at a time (N and d' are multiples of 8, so the eight share a row
+// and a (head, slot) run of the Q_imp layout): 32-byte partial loads per split, summed in
+// the same order, and one 16-byte store.
+__global__ void reduce_splits8_kernel(const float* __restrict__ P, void* out, int M, int N,
+                                      int nsplit, Epilogue ep) {
+  const long long e = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (e >= (long long)M * N) return;
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* ps = P + (long long)s * M * N + e;
+    const float4 a = *reinterpret_cast<const float4*>(ps);
+    const float4 b = *reinterpret_cast<const float4*>(ps + 4);
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+  if (ep.mode == 1)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = fmaxf(acc[c], 0.f);
+  const uint4 o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  const int m = (int)(e / N), n = (int)(e - (long long)m * N);
+  bf16_t* dst;
+  if (ep.mode == 1) {
+    dst = (bf16_t*)out + e;
+  } else {
+    const int b = m / ep.Lq, t = m - b * ep.Lq;
+    const int head = n / (ep.G * ep.dp);
+    const int rem = n - head * ep.G * ep.dp;
+    const int slot = rem / ep.dp, i = rem - slot * ep.dp;
+    dst = (bf16_t*)out + ((((long long)b * ep.Hq + head) * ep.G + slot) * ep.Lq + t) * ep.dp + i;
+  }
+  *reinterpret_cast<uint4*>(dst) = o;
 }
 
 int valu_splits(int M, int N, int K) {
@@ -378,8 +665,14 @@ hipError_t gemm(hipStream_t st, const bf16_t* A, const bf16_t* Bm, void* out, fl
   void* dst = (ns > 1) ? (void*)partial : out;
   if (mf) {
     dim3 grid(N / kMN, (M + kMM - 1) / kMM, ns);
-    hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(kMThreads), 0, st, A, Bm, dst, M, N, K, kps,
-                       pe);
+    if (use_dma(M, N, K, kps)) {
+      const TileMap tm = tile_map((M + kMM - 1) / kMM, N / kMN, ns);
+      const unsigned nwg = (unsigned)grid.x * grid.y * grid.z;
+      hipLaunchKernelGGL(gemm_dma_kernel<kDRing>, dim3(nwg),
+                         dim3(kMThreads), 0, st, A, Bm, dst, M, N, K, kps, pe, tm);
+    } else
+      hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(kMThreads), 0, st, A, Bm, dst, M, N, K,
+                         kps, pe);
   } else {
     dim3 grid(N / kTN, (M + kTM - 1) / kTM, ns);
     hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(kGemmThreads), 0, st, A, Bm, dst, M, N, K,
@@ -387,8 +680,12 @@ hipError_t gemm(hipStream_t st, const bf16_t* A, const bf16_t* Bm, void* out, fl
   }
   if (ns > 1) {
     const long long tot = (long long)M * N;
-    hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,
-                       st, partial, out, M, N, ns, ep);
+    if (N % 8 == 0 && (ep.mode != 2 || ep.dp % 8 == 0))
+      hipLaunchKernelGGL(reduce_splits8_kernel, dim3((unsigned)((tot / 8 + 255) / 256)), dim3(256),
+                         0, st, partial, out, M, N, ns, ep);
+    else
+      hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,
+                         st, partial, out, M, N, ns, ep);
   }
   return hipGetLastError();
 }
