@@ -30,6 +30,14 @@ constexpr int kLnThreads = 256;
 constexpr int kTM = 32, kTN = 64, kTK = 32;
 constexpr int kGemmThreads = 256;
 
+// Two floats -> two bf16 (rounded to nearest even) in one 32-bit word, low half first:
+// the hardware's packed conversion.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2v_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // One row per workgroup: the row is held in VGPRs (16-byte pieces, all requested before
 // the first reduction), mean and variance from block sums, then the bf16 x_hat.
 __global__ __launch_bounds__(kLnThreads) void ln_rows_kernel(const bf16_t* __restrict__ h,
@@ -76,18 +84,9 @@ __global__ __launch_bounds__(kLnThreads) void ln_rows_kernel(const bf16_t* __res
     uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      ow[e] = (uint32_t)f2bf((hv[u][2 * e] - mean) * rstd) |
-              ((uint32_t)f2bf((hv[u][2 * e + 1] - mean) * rstd) << 16);
+      ow[e] = pack_bf16x2((hv[u][2 * e] - mean) * rstd, (hv[u][2 * e + 1] - mean) * rstd);
     *reinterpret_cast<uint4*>(xhat + row * E + e0) = o;
   }
-}
-
-// Two floats -> two bf16 (rounded to nearest even) in one 32-bit word, low half first:
-// the hardware's packed conversion.
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2v_t v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Output placement of GEMM results.
