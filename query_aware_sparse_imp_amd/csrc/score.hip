@@ -627,16 +627,25 @@ __global__ __launch_bounds__(kCsThreads, 2) void score_rows_mfma_kernel(
             acc[tb] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[qb][s8], (double)kv[tb][s8],
                                                            acc[tb], 0, 0, 0);
       }
+      // The block's 16 rows as one buffer range: a store of a row past Lq or of a token
+      // past L gets an offset beyond the range and is dropped by the hardware, so no
+      // store sits behind a branch; the causal mask is a select.
+      const int ib = i0 + 16 * qb;
+      if (ib < Lq) {
+        const int nrows = min(16, Lq - ib);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(srow0 + (long long)ib * L), (short)0, nrows * L * 4, 0x00020000);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 16 * qb + 4 * r + g4;
-        if (i >= Lq) continue;
-        const int lim = causal ? min(L, q_pos0 + i + 1) : L;
-        float* srow = srow0 + (long long)i * L;
+        for (int r = 0; r < 4; ++r) {
+          const int ir = 4 * r + g4;
+          const int lim = causal ? min(L, q_pos0 + ib + ir + 1) : L;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const int t = t0 + 16 * tb + ql;
-          if (t < L) srow[t] = (t < lim) ? (float)acc[tb][r] : neg_inf();
+          for (int tb = 0; tb < 4; ++tb) {
+            const int t = t0 + 16 * tb + ql;
+            const float v = (t < lim) ? (float)acc[tb][r] : neg_inf();
+            const int off = (t < L) ? (ir * L + t) * 4 : 0x7fffffff;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
+          }
         }
       }
     }
