@@ -364,6 +364,9 @@ __device__ __forceinline__ void wait_vm_n() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS accesses have completed
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // wait until at most n_left (0, 8 or 16: whole stages) of this wave's loads are in flight
 __device__ __forceinline__ void wait_vm(int n_left) {
   if (n_left >= 16) wait_vm_n<16>();
@@ -456,9 +459,14 @@ __global__ __launch_bounds__(kMThreads) void gemm_dma_kernel(
   for (int t = 0; t < T; ++t) {
     // this wave's loads of stage t have landed once at most the later stages' are left
     wait_vm(min(S - 2, T - 1 - t) * 2 * kDLoads);
-    // every wave's stage t is in LDS and every wave is done with stage t-1 (a bare barrier:
-    // __syncthreads would also wait for the later stages' loads)
+    // every wave's stage t is in LDS and every wave is done with stage t-1.  __syncthreads
+    // would also wait for the later stages' loads (its fence covers the LDS-direct writes),
+    // so: this wave's LDS reads completed, then the hardware barrier between two compiler
+    // barriers, so no LDS access moves across it.
+    wait_lds();
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     if (t + S - 1 < T) issue(t + S - 1);
     const unsigned char* st = sm + (t % S) * 2 * kDTile;
 #pragma unroll
