@@ -30,7 +30,7 @@ namespace {
 // its vector work (the exponentials and the softmax around them), not by the matrix
 // cores: the logits are masked with one bitfield extract and one bit-select each, the
 // scale sits in the exponent's FMA, and the accumulators are rescaled only when some
-// query's max moved.
+// query's reference max moved, which it does only by more than 2^8 in probability.
 // ---------------------------------------------------------------------------
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
@@ -197,7 +197,12 @@ __global__ __launch_bounds__(2 * kPfThreads) void attn_prefill_mfma_kernel(
       mt = fmaxf(ma, mb);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
+    // The reference max moves only when this tile's max passes it by more than 8 in the
+    // base-2 exponent: below that the probabilities stay under 2^8, which the float32 sums
+    // and the bf16 rounding of P hold as well as values under 1 (softmax does not depend
+    // on the shift), and the accumulators keep their scale (alpha is exactly 1).
+    const bool move = (m == neg_inf()) || (mt * scale_log2 > msc + 8.f);
+    const float mn = move ? fmaxf(m, mt) : m;
     const float ms = (mn == neg_inf()) ? 0.f : mn * scale_log2;
     // nothing accumulated while m is -inf; an unchanged max rescales by exactly 1
     const float alpha = (m == neg_inf()) ? 0.f : fast_exp2(msc - ms);
