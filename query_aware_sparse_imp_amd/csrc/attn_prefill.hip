@@ -228,17 +228,26 @@ __global__ __launch_bounds__(2 * kPfThreads) void attn_prefill_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)pr[8 * ks + e];
     const bf16_t* Vc = Vt[it & 1];
+    bf16x8_t va[16];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const bf16_t* vrow = &Vc[(db * 32 + ql) * kPfVS];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * ks + 4 * hi);
-        const bf16x4_t hi4 = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * ks + 8 + 4 * hi);
-        const bf16x8_t a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[db], 0, 0, 0);
-      }
+    for (int j = 0; j < 16; ++j) {
+      const bf16_t* vrow = &Vc[((j >> 2) * 32 + ql) * kPfVS + 16 * (j & 3)];
+      const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vrow + 4 * hi);
+      const bf16x4_t hi4 = *reinterpret_cast<const bf16x4_t*>(vrow + 8 + 4 * hi);
+      va[j] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      o[j >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb[j & 3], o[j >> 2], 0, 0, 0);
+    // V^T operands read two ahead of their products (the scheduler otherwise puts each
+    // read right before its MFMA and waits on it)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int j = 0; j < 14; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     // the buffers refilled here were last read before the previous barrier
     stage(it & 1, (it + 1) & 1);
     __syncthreads();
