@@ -484,6 +484,14 @@ __global__ __launch_bounds__(kMThreads) void gemm_dma_kernel(
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
+    // the next k-step's four operands read ahead of this k-step's four products
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int ks = 0; ks < kDK / 16 - 1; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   }
   // accumulator r of tile (i, j): row m0 + 64 wm + 32 i + lane % 32, column
   // n0 + 64 wn + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4
