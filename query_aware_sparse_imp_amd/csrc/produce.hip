@@ -356,6 +356,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kDK = 64;                                 // K per stage
 constexpr int kDTile = kMM * kDK * 2;                   // bytes of one operand tile
 constexpr int kDLoads = kDTile / (kMThreads * 16);      // 16-byte loads per lane and operand
+static_assert(2 * kDLoads == 8, "wait_vm counts a stage as eight loads per lane");
 
 // s_waitcnt bounding only the vector-memory counter (expcnt, lgkmcnt left at their maximum)
 template <int N>
