@@ -33,6 +33,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -298,9 +299,23 @@ def stream_ceiling(device, gib: int = 1, reps: int = 10) -> dict:
             "kernels": "butler_measure_read / butler_measure_copy (16-byte loads)"}
 
 
-def graph_time(fns, reps):
+def _timed_replays(g, replays):
+    """Median seconds of `replays` timed replays of graph g (after one warm-up replay)."""
+    import torch
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(replays):
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    return statistics.median(ts)
+
+
+def graph_time(fns, reps, replays=1):
     """Seconds per replay of a graph holding `reps` passes over `fns` (after one eager
-    pass and one warm-up replay)."""
+    pass and one warm-up replay; the median of `replays` timed replays)."""
     import torch
     for f in fns:
         f()
@@ -310,12 +325,34 @@ def graph_time(fns, reps):
         for _ in range(reps):
             for f in fns:
                 f()
-    g.replay()
+    return _timed_replays(g, replays) / reps
+
+
+def graph_time_two_streams(fronts, backs, replays=1):
+    """Seconds per replay of one graph in which fronts[c] run in order on the capturing
+    stream and backs[c] in order on a second stream, each back after its own front (the
+    streams forked and joined by events), after one eager pass and one warm-up replay; the
+    median of `replays` timed replays."""
+    import torch
+    side = torch.cuda.Stream()
+
+    def issue():
+        side.wait_stream(torch.cuda.current_stream())
+        for f, b in zip(fronts, backs):
+            f()
+            e = torch.cuda.Event()
+            e.record()
+            with torch.cuda.stream(side):
+                side.wait_event(e)
+                b()
+        torch.cuda.current_stream().wait_stream(side)
+
+    issue()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g.replay()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / reps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        issue()
+    return _timed_replays(g, replays)
 
 
 def run_softvote(device, cache_threshold=None):
@@ -641,7 +678,7 @@ def run_full_depth(steps, device):
             "inputs": "seeded torch generator on the GPU"}
 
 
-def run_prefill(device):
+def run_prefill(device, pipelined=True):
     """Chunked causal prefill: B=2, L=8192 in query chunks of 1024.  Per chunk: f_theta
     on the chunk's hidden rows (Q_imp, slot 0 scored), K_imp of the chunk's keys, causal
     raw scores of the chunk against its prefix, per-row top-50% + sink 4 + window 64 into
@@ -693,10 +730,43 @@ def run_prefill(device):
             Qc[c], k, v, outs[c], L=Lc, bitmask=bms[c], q_pos0=c0, softmax_scale=w.scale))
     order = [f for c in range(nc) for f in (groups["produce"][c], groups["project"][c],
                                            groups["score+select"][c], groups["attn"][c])]
-    sec = graph_time(order, 1)
+    sec_seq = graph_time(order, 1, replays=5)
+    sched = {"sequential_s": sec_seq}
+    sec = sec_seq
+    if pipelined:
+        # chunk c's selection and attention on a second stream, beside chunk c+1's producer,
+        # projection and scoring (they read nothing the other writes)
+        ref = [o.clone() for o in outs] + [m.clone() for m in bms]
+        for o in outs:
+            o.fill_(float("nan"))
+        for m in bms:
+            m.fill_(-1)
+
+        def front(c):
+            c0, Lc = c * C, (c + 1) * C
+            groups["produce"][c]()
+            groups["project"][c]()
+            qa.butler_score(qa.BUTLER_SCORE_RAW, qimp[c], kimp, scores[c], Hkv=w.Hkv, L=Lc,
+                            slot=0, q_pos0=c0, causal=True)
+
+        def back(c):
+            qa.butler_select_topk(scores[c], w.budget_num, w.budget_den, w.n_sink, w.n_window,
+                                  cnt, bitmask=bms[c], q_pos0=c * C, causal=True)
+            groups["attn"][c]()
+
+        sec2 = graph_time_two_streams([lambda c=c: front(c) for c in range(nc)],
+                                      [lambda c=c: back(c) for c in range(nc)], replays=5)
+        same = all(torch.equal(a, b) for a, b in zip(ref, outs + bms))
+        sched.update({"two_streams_s": sec2, "two_streams_bit_identical": same})
+        if same:
+            sec = sec2
+        else:
+            log("[bench] prefill: the two-stream schedule differs from the sequential one; "
+                "reporting the sequential time")
     part = {name: graph_time(fs, 1) * 1e6 for name, fs in groups.items()}
     prod_flops = 2.0 * w.B * L * (w.E * w.F + w.F * w.Hq * w.G * w.dprime)
     return {"workload": w.name, "prefill_s": sec, "tokens_per_s": w.B * L / sec,
+            "schedule": sched,
             "phase_us": {kk: round(vv, 1) for kk, vv in part.items()},
             "producer_TFLOPs": prod_flops / (part["produce"] * 1e-6) / 1e12,
             "producer_frac_of_bf16_mfma_peak": prod_flops / (part["produce"] * 1e-6) / 2.5e15,
