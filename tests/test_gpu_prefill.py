@@ -159,6 +159,77 @@ def test_prefill_llama_shape_one_chunk_pair():
     _prefill_case(w, L=2048, chunk=1024)
 
 
+def _chunked_prefill(w, inp, L, chunk, two_streams):
+    """Per chunk: producer on the chunk's hidden rows, K_imp of its keys, causal raw scores
+    (the front), then per-row selection and masked attention (the back).  With two_streams,
+    each chunk's back runs on a second stream after an event on its own front, beside the
+    next chunks' fronts.  Outputs and bitmasks start poisoned (NaN, -1)."""
+    import query_aware_sparse_imp_amd as qa
+    dev = "cuda"
+    h = inp["h"].cuda()
+    w1, w2 = inp["w1"].t().contiguous().cuda(), inp["w2"].t().contiguous().cuda()
+    k_d, v_d, q_d, wk = (inp["k_cache"].cuda(), inp["v_cache"].cuda(), inp["q"].cuda(),
+                         inp["w_k"].cuda())
+    kimp = torch.empty(w.B, w.Hkv, L, w.dprime, dtype=torch.bfloat16, device=dev)
+    starts = list(range(0, L, chunk))
+    outs, bms, cnts, keep = [], [], [], []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for c0 in starts:
+        Lq = min(chunk, L - c0)
+        Lk = c0 + Lq
+        qimp = torch.empty(w.B, w.Hq, w.G, Lq, w.dprime, dtype=torch.bfloat16, device=dev)
+        hc = h[:, c0:c0 + Lq].contiguous()
+        qc = q_d[:, :, c0:c0 + Lq].contiguous()
+        scores = torch.empty(w.B, w.Hkv, Lq, Lk, dtype=torch.float32, device=dev)
+        bm = torch.full((w.B, w.Hkv, Lq, (Lk + 31) // 32), -1, dtype=torch.int32, device=dev)
+        cnt = torch.full((w.B, w.Hkv, Lq), -1, dtype=torch.int32, device=dev)
+        out = torch.full((w.B, w.Hq, Lq, w.D), float("nan"), dtype=torch.float32, device=dev)
+        keep += [qimp, hc, qc, scores]
+        qa.butler_produce_queries(hc, w1, w2, qimp)
+        qa.butler_project_keys(k_d, wk, kimp, c0, Lq)
+        qa.butler_score(qa.BUTLER_SCORE_RAW, qimp, kimp, scores, Hkv=w.Hkv, L=Lk, slot=0,
+                        q_pos0=c0, causal=True)
+
+        def back(scores=scores, bm=bm, cnt=cnt, out=out, qc=qc, c0=c0, Lk=Lk):
+            qa.butler_select_topk(scores, w.budget_num, w.budget_den, w.n_sink, w.n_window,
+                                  cnt, bitmask=bm, q_pos0=c0, causal=True)
+            qa.butler_sparse_decode_attn(qc, k_d, v_d, out, L=Lk, bitmask=bm, q_pos0=c0,
+                                         softmax_scale=w.scale)
+
+        if two_streams:
+            e = torch.cuda.Event()
+            e.record()
+            with torch.cuda.stream(side):
+                side.wait_event(e)
+                back()
+        else:
+            back()
+        outs.append(out)
+        bms.append(bm)
+        cnts.append(cnt)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return outs, bms, cnts
+
+
+def test_prefill_two_streams_matches_one_stream():
+    """The bench's two-stream prefill schedule (chunk c's selection and attention on a
+    second stream beside chunk c+1's producer, projection and scores) gives the one-stream
+    schedule's outputs, bitmasks and counts bit for bit (the one-stream path's parity with
+    the oracle is checked by the tests above)."""
+    w = synthetic.WORKLOADS[5].replace(B=2)
+    L, chunk = 2048, 512
+    print(f"[prefill two streams] B={w.B} L={L} chunk={chunk}", flush=True)
+    inp = synthetic.prefill_inputs(w, L=L)
+    one = _chunked_prefill(w, inp, L, chunk, two_streams=False)
+    two = _chunked_prefill(w, inp, L, chunk, two_streams=True)
+    for name, a, b in zip(("out", "bitmask", "count"), one, two):
+        for c, (x, y) in enumerate(zip(a, b)):
+            assert not torch.isnan(x).any() if x.is_floating_point() else (x != -1).any()
+            assert torch.equal(x, y), f"{name} of chunk {c} differs between the schedules"
+
+
 def _sample_rows(rng, B, Hkv, Lq, n):
     """n (b, g, i) rows of a chunk: its first and last rows of the first and last heads,
     the rest at random."""
