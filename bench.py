@@ -328,24 +328,28 @@ def graph_time(fns, reps, replays=1):
     return _timed_replays(g, replays) / reps
 
 
-def graph_time_two_streams(fronts, backs, replays=1):
-    """Seconds per replay of one graph in which fronts[c] run in order on the capturing
-    stream and backs[c] in order on a second stream, each back after its own front (the
-    streams forked and joined by events), after one eager pass and one warm-up replay; the
-    median of `replays` timed replays."""
+def graph_time_streams(stages, replays=1):
+    """Seconds per replay of one graph in which stage s of every chunk, stages[c][s], runs
+    on stream s (stream 0 the capturing one), in chunk order on each stream, after stage
+    s - 1 of its own chunk (the streams forked and joined by events); after one eager pass
+    and one warm-up replay, the median of `replays` timed replays."""
     import torch
-    side = torch.cuda.Stream()
+    side = [torch.cuda.Stream() for _ in range(len(stages[0]) - 1)]
 
     def issue():
-        side.wait_stream(torch.cuda.current_stream())
-        for f, b in zip(fronts, backs):
-            f()
-            e = torch.cuda.Event()
-            e.record()
-            with torch.cuda.stream(side):
-                side.wait_event(e)
-                b()
-        torch.cuda.current_stream().wait_stream(side)
+        main = torch.cuda.current_stream()
+        for st in side:
+            st.wait_stream(main)
+        for chunk in stages:
+            chunk[0]()
+            for st, f in zip(side, chunk[1:]):
+                e = torch.cuda.Event()
+                e.record()
+                with torch.cuda.stream(st):
+                    st.wait_event(e)
+                    f()
+        for st in side:
+            main.wait_stream(st)
 
     issue()
     torch.cuda.synchronize()
@@ -678,7 +682,7 @@ def run_full_depth(steps, device):
             "inputs": "seeded torch generator on the GPU"}
 
 
-def run_prefill(device, pipelined=True):
+def run_prefill(device, streams=2):
     """Chunked causal prefill: B=2, L=8192 in query chunks of 1024.  Per chunk: f_theta
     on the chunk's hidden rows (Q_imp, slot 0 scored), K_imp of the chunk's keys, causal
     raw scores of the chunk against its prefix, per-row top-50% + sink 4 + window 64 into
@@ -733,9 +737,10 @@ def run_prefill(device, pipelined=True):
     sec_seq = graph_time(order, 1, replays=5)
     sched = {"sequential_s": sec_seq}
     sec = sec_seq
-    if pipelined:
-        # chunk c's selection and attention on a second stream, beside chunk c+1's producer,
-        # projection and scoring (they read nothing the other writes)
+    if streams > 1:
+        # chunk c's selection and attention on a second stream (with streams=3, the
+        # attention on a third), beside chunk c+1's producer, projection and scoring (they
+        # read nothing the other writes)
         ref = [o.clone() for o in outs] + [m.clone() for m in bms]
         for o in outs:
             o.fill_(float("nan"))
@@ -749,19 +754,26 @@ def run_prefill(device, pipelined=True):
             qa.butler_score(qa.BUTLER_SCORE_RAW, qimp[c], kimp, scores[c], Hkv=w.Hkv, L=Lc,
                             slot=0, q_pos0=c0, causal=True)
 
-        def back(c):
+        def select(c):
             qa.butler_select_topk(scores[c], w.budget_num, w.budget_den, w.n_sink, w.n_window,
                                   cnt, bitmask=bms[c], q_pos0=c * C, causal=True)
+
+        def back(c):
+            select(c)
             groups["attn"][c]()
 
-        sec2 = graph_time_two_streams([lambda c=c: front(c) for c in range(nc)],
-                                      [lambda c=c: back(c) for c in range(nc)], replays=5)
+        if streams == 2:
+            stages = [[lambda c=c: front(c), lambda c=c: back(c)] for c in range(nc)]
+        else:
+            stages = [[lambda c=c: front(c), lambda c=c: select(c), groups["attn"][c]]
+                      for c in range(nc)]
+        sec2 = graph_time_streams(stages, replays=5)
         same = all(torch.equal(a, b) for a, b in zip(ref, outs + bms))
-        sched.update({"two_streams_s": sec2, "two_streams_bit_identical": same})
+        sched.update({"streams": streams, "pipelined_s": sec2, "pipelined_bit_identical": same})
         if same:
             sec = sec2
         else:
-            log("[bench] prefill: the two-stream schedule differs from the sequential one; "
+            log("[bench] prefill: the pipelined schedule differs from the sequential one; "
                 "reporting the sequential time")
     part = {name: graph_time(fs, 1) * 1e6 for name, fs in groups.items()}
     prod_flops = 2.0 * w.B * L * (w.E * w.F + w.F * w.Hq * w.G * w.dprime)
