@@ -342,12 +342,14 @@ def graph_time_streams(stages, replays=1):
             st.wait_stream(main)
         for chunk in stages:
             chunk[0]()
+            prev = main
             for st, f in zip(side, chunk[1:]):
                 e = torch.cuda.Event()
-                e.record()
+                e.record(prev)   # after the previous stage of this chunk
                 with torch.cuda.stream(st):
                     st.wait_event(e)
                     f()
+                prev = st
         for st in side:
             main.wait_stream(st)
 
